@@ -1,0 +1,484 @@
+"""Pins of the CPU oracle against what the page and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine implemented independently (torch.nn.functional), a closed form, an
+exhaustive table built from the format definition, brute force on tiny
+inputs, or an identity of the method (k = K equals a dense recompute).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import polestar_oracle as O
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- KL drift
+def test_kl_nonnegative_and_zero_on_identical():
+    for _ in range(50):
+        n = int(RNG.integers(2, 64))
+        s = RNG.normal(size=(3, n)) * RNG.uniform(0.1, 5)
+        sp = RNG.normal(size=(3, n)) * RNG.uniform(0.1, 5)
+        kl = O.kl_logits(s, sp)
+        assert np.all(kl >= -1e-12)
+        assert np.all(O.kl_logits(s, s) == 0.0)
+
+
+def test_kl_two_key_closed_form():
+    # KL between Bernoulli(p) and Bernoulli(q) written from scratch.
+    for a, b, a2, b2 in RNG.normal(size=(40, 4)) * 2:
+        p = 1.0 / (1.0 + math.exp(-(a - b)))
+        q = 1.0 / (1.0 + math.exp(-(a2 - b2)))
+        want = p * math.log(p / q) + (1 - p) * math.log((1 - p) / (1 - q))
+        got = O.kl_logits(np.array([a, b]), np.array([a2, b2]))
+        assert abs(got - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_kl_pinsker_and_shift_invariance():
+    for _ in range(50):
+        n = int(RNG.integers(2, 200))
+        s = RNG.normal(size=n) * 2
+        sp = s + RNG.normal(size=n) * RNG.uniform(0.01, 2)
+        kl = float(O.kl_logits(s, sp))
+        p = np.exp(s - s.max()); p /= p.sum()
+        q = np.exp(sp - sp.max()); q /= q.sum()
+        assert np.abs(p - q).sum() <= math.sqrt(2 * kl) + 1e-12          # Prop. 2 (Pinsker)
+        c1, c2 = RNG.normal(size=2) * 10
+        assert abs(float(O.kl_logits(s + c1, sp + c2)) - kl) <= 1e-10 * max(1, kl)
+
+
+def test_head_summed_drift_clamps_and_sums():
+    s = RNG.normal(size=(4, 3, 17))
+    sp = RNG.normal(size=(4, 3, 17))
+    kl = O.kl_logits(s, sp)
+    assert np.allclose(O.head_summed_drift(s, sp), kl.sum(axis=1))
+
+
+# ---------------------------------------------------------------- layer pieces vs torch
+def test_rmsnorm_and_project_match_torch():
+    x = RNG.normal(size=(7, 48))
+    w = RNG.normal(size=(20, 48))
+    eps = 1e-6
+    tx = torch.tensor(x)
+    want_n = F.rms_norm(tx, (48,), eps=eps).numpy()
+    assert np.allclose(O.rmsnorm(x, eps), want_n, rtol=1e-13, atol=0)
+    want_p = F.linear(F.rms_norm(tx, (48,), eps=eps), torch.tensor(w)).numpy()
+    assert np.allclose(O.project(x, w, eps), want_p, rtol=1e-12, atol=1e-13)
+
+
+def test_silu_matches_torch():
+    x = RNG.normal(size=100) * 5
+    assert np.allclose(O.silu(x), F.silu(torch.tensor(x)).numpy(), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (28, 4)])
+def test_attention_matches_torch_sdpa(hq, hkv):
+    n, dh, R = 19, 16, 5
+    q = RNG.normal(size=(R, hq, dh))
+    k = RNG.normal(size=(n, hkv, dh))
+    v = RNG.normal(size=(n, hkv, dh))
+    out, logits = O.attention(q, k, v, hq, hkv)
+    tq = torch.tensor(q).permute(1, 0, 2)                       # [H, R, dh]
+    rep = hq // hkv
+    tk = torch.tensor(k).permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    tv = torch.tensor(v).permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    want = F.scaled_dot_product_attention(tq, tk, tv).permute(1, 0, 2).numpy()
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(logits, np.einsum("rhd,hnd->rhn", q, tk.numpy()) / math.sqrt(dh))
+
+
+def test_attention_single_key_and_permutations():
+    q = RNG.normal(size=(3, 2, 8))
+    k = RNG.normal(size=(1, 2, 8))
+    v = RNG.normal(size=(1, 2, 8))
+    out, _ = O.attention(q, k, v, 2, 2)
+    assert np.allclose(out, np.broadcast_to(v[0], out.shape))
+    k = RNG.normal(size=(9, 2, 8)); v = RNG.normal(size=(9, 2, 8))
+    out, _ = O.attention(q, k, v, 2, 2)
+    perm = RNG.permutation(9)
+    out2, _ = O.attention(q, k[perm], v[perm], 2, 2)
+    assert np.allclose(out, out2)
+    qp = RNG.permutation(3)
+    out3, _ = O.attention(q[qp], k, v, 2, 2)
+    assert np.allclose(out3, out[qp])
+
+
+def test_full_forward_one_layer_matches_torch_modules():
+    d, hq, hkv, dh, f, n = 32, 4, 2, 8, 48, 11
+    cfg = O.Cfg(d=d, n_heads=hq, n_kv_heads=hkv, head_dim=dh, ffn=f, n_pos=n, block=4,
+                win_prefix=4, win_suffix=2, n_clusters=2, top_k=1, dtype="f64")
+    W = {"wq": RNG.normal(size=(hq * dh, d)) / 6, "wk": RNG.normal(size=(hkv * dh, d)) / 6,
+         "wv": RNG.normal(size=(hkv * dh, d)) / 6, "wo": RNG.normal(size=(d, hq * dh)) / 6,
+         "wg": RNG.normal(size=(f, d)) / 6, "wu": RNG.normal(size=(f, d)) / 6, "wd": RNG.normal(size=(d, f)) / 6}
+    h0 = RNG.normal(size=(n, d))
+    Hs, Ks, Vs, _ = O.full_forward(h0, [W], cfg)
+    T = {k: torch.tensor(v) for k, v in W.items()}
+    x = torch.tensor(h0)
+    a = F.rms_norm(x, (d,), eps=1e-6)
+    q = F.linear(a, T["wq"]).view(n, hq, dh).permute(1, 0, 2)
+    k = F.linear(a, T["wk"]).view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    v = F.linear(a, T["wv"]).view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    o = F.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).reshape(n, hq * dh)
+    hp = x + F.linear(o, T["wo"])
+    b = F.rms_norm(hp, (d,), eps=1e-6)
+    out = hp + F.linear(F.silu(F.linear(b, T["wg"])) * F.linear(b, T["wu"]), T["wd"])
+    assert np.allclose(Hs[1], out.numpy(), rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------- rounding
+def test_round_bf16_matches_torch_on_fp32_values():
+    x = (RNG.normal(size=20000) * np.exp(RNG.uniform(-20, 20, size=20000))).astype(np.float32)
+    want = torch.tensor(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), want)
+
+
+def test_round_bf16_rounds_once_from_float64():
+    # 1 + 2^-8 is the exact bf16 midpoint between 1 and 1 + 2^-7: ties to even -> 1.
+    assert O.round_bf16(np.array([1 + 2 ** -8]))[0] == 1.0
+    # Slightly above the midpoint rounds up even though float32 rounding would land on it.
+    v = 1 + 2 ** -8 + 2 ** -40
+    assert O.round_bf16(np.array([v]))[0] == 1 + 2 ** -7
+    assert O.round_bf16(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6   # tie to even upward
+
+
+# ---------------------------------------------------------------- spherical k-means
+def _objective(x, z, m):
+    return float(np.sum(x * z[m]))
+
+
+def test_kmeans_unit_norm_monotone_and_fixed_point():
+    for trial in range(20):
+        nw, d, K = int(RNG.integers(9, 60)), int(RNG.integers(3, 40)), int(RNG.integers(2, 9))
+        h = RNG.normal(size=(nw, d))
+        init = RNG.permutation(nw)[: min(K, nw)]
+        z, m, trace = O.spherical_kmeans(h, K, init, iters=10)
+        kk = min(K, nw)
+        assert np.allclose(np.linalg.norm(z[:kk], axis=1), 1.0, atol=1e-12)
+        assert np.all(np.diff(trace) >= -1e-12)
+        # objective after an update equals sum of member-sum norms
+        x = O.unit_rows(h)
+        assert abs(trace[-1] - _objective(x, z, m)) < 1e-9
+        # one more assignment from the final centroids at the converged state
+        z2, m2, trace2 = O.spherical_kmeans(h, K, init, iters=60)
+        cos = x @ z2[:kk].T
+        assert np.array_equal(np.argmax(cos, axis=1), m2)
+
+
+def test_kmeans_recovers_planted_directions():
+    d, K, per = 64, 8, 12
+    dirs = np.linalg.qr(RNG.normal(size=(d, K)))[0].T          # orthonormal directions
+    labels = np.repeat(np.arange(K), per)
+    h = dirs[labels] * RNG.uniform(0.5, 3.0, size=(K * per, 1)) + 0.02 * RNG.normal(size=(K * per, d))
+    init = np.array([c * per for c in range(K)])
+    z, m, _ = O.spherical_kmeans(h, K, init, iters=10)
+    assert np.array_equal(m, labels)
+    assert np.all(np.sum(z * dirs, axis=1) > 0.99)
+
+
+def test_kmeans_bruteforce_tiny():
+    for trial in range(10):
+        nw = int(RNG.integers(4, 10))
+        h = RNG.normal(size=(nw, 3))
+        x = O.unit_rows(h)
+        best = -1.0
+        for lab in itertools.product(range(2), repeat=nw):
+            lab = np.asarray(lab)
+            val = sum(np.linalg.norm(x[lab == c].sum(axis=0)) for c in range(2) if (lab == c).any())
+            best = max(best, val)
+        z, m, trace = O.spherical_kmeans(h, 2, RNG.permutation(nw)[:2], iters=10)
+        assert trace[-1] <= best + 1e-12
+
+
+def test_kmeans_zero_row_and_empty_cluster():
+    h = np.zeros((5, 4)); h[1] = [1, 0, 0, 0]; h[2] = [0, 1, 0, 0]; h[3] = [1, 0.1, 0, 0]; h[4] = [1, 0.2, 0, 0]
+    z, m, _ = O.spherical_kmeans(h, 3, np.array([1, 2, 0]), iters=3)
+    assert m[0] == 0                                 # zero row -> lowest index
+    # cluster 2 starts at the zero row: it keeps its (zero) centroid when empty
+    assert np.all(z[2] == 0)
+
+
+def test_centroid_update_fixed_labels():
+    h = RNG.normal(size=(30, 16))
+    m = RNG.integers(0, 4, size=30)
+    m[m == 3] = 2                                    # cluster 3 empty
+    zold = RNG.normal(size=(4, 16))
+    z = O.centroid_update(h * RNG.uniform(0.1, 10, size=(30, 1)), m, zold)
+    x = h / np.linalg.norm(h, axis=1, keepdims=True)
+    for c in range(3):
+        s = x[m == c].sum(axis=0)
+        assert np.allclose(z[c], s / np.linalg.norm(s))
+    assert np.array_equal(z[3], zold[3])
+
+
+def test_kmeans_fewer_rows_than_clusters():
+    h = RNG.normal(size=(5, 8))
+    z, m, _ = O.spherical_kmeans(h, 8, np.array([4, 2, 0, 1, 3]), iters=4)
+    assert set(m.tolist()) <= set(range(5)) and np.all(z[5:] == 0)
+
+
+# ---------------------------------------------------------------- NVFP4
+def test_e2m1_table_from_bit_fields():
+    for code in range(16):
+        s, e, mt = code >> 3, (code >> 1) & 3, code & 1
+        mag = mt * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + mt / 2)
+        assert O.e2m1_value(code) == (-mag if s else mag)
+
+
+def test_e4m3_table_matches_torch_float8():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.tensor(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_value(codes)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_e4m3_encode_matches_torch_rne():
+    x = np.concatenate([np.abs(RNG.normal(size=20000)) * np.exp(RNG.uniform(-12, 6, size=20000)),
+                        O.e4m3_value(np.arange(0x7F)),
+                        (O.e4m3_value(np.arange(0x7E)) + O.e4m3_value(np.arange(1, 0x7F))) / 2])
+    x = x[x <= 448].astype(np.float32).astype(np.float64)
+    want = torch.tensor(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), want)
+    assert O.e4m3_encode(np.array([1e6]))[0] == 0x7E                    # saturates at 448
+
+
+def test_e2m1_encode_ties_to_even_and_saturation():
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for y, v in ties.items():
+        assert O.e2m1_value(O.e2m1_encode(np.array([y])))[0] == v
+        assert O.e2m1_value(O.e2m1_encode(np.array([-y])))[0] == -v
+    grid = O.E2M1_MAG
+    for a, b in zip(grid[:-1], grid[1:]):
+        mid = (a + b) / 2
+        assert O.e2m1_value(O.e2m1_encode(np.array([np.nextafter(mid, 0)])))[0] == a
+        assert O.e2m1_value(O.e2m1_encode(np.array([np.nextafter(mid, 10)])))[0] == b
+    assert O.e2m1_value(O.e2m1_encode(np.array([7.9, -100.0]))).tolist() == [6.0, -6.0]
+    assert O.e2m1_encode(np.array([-0.0, -0.1]))[0] == 0 and O.e2m1_encode(np.array([-0.1]))[0] == 0
+
+
+def test_nvfp4_exact_round_trip_on_representable_groups():
+    rows, d = 12, 128
+    grid = np.concatenate([O.E2M1_MAG, -O.E2M1_MAG[1:]])
+    vals = RNG.choice(grid, size=(rows, d))
+    vals[:, ::16] = RNG.choice([6.0, -6.0], size=(rows, d // 16))       # every group holds +-6
+    sc = RNG.integers(1, 0x7E, size=(rows, d // 16))
+    sv = O.e4m3_value(sc)
+    r = (vals.reshape(rows, d // 16, 16) * sv[..., None]).reshape(rows, d).astype(np.float32)
+    packed, scales = O.nvfp4_quantize(r)
+    assert np.array_equal(scales, sc.astype(np.uint8))
+    assert np.array_equal(O.nvfp4_dequantize(packed, scales), r)
+
+
+def test_nvfp4_error_bound_and_zero_group():
+    r = (RNG.normal(size=(16, 256)) * np.exp(RNG.uniform(-6, 4, size=(16, 1)))).astype(np.float32)
+    r[3, 32:48] = 0.0
+    packed, scales = O.nvfp4_quantize(r)
+    deq = O.nvfp4_dequantize(packed, scales)
+    sv = np.repeat(O.e4m3_value(scales), 16, axis=1)
+    y = np.abs(r.astype(np.float64)) / np.where(sv > 0, sv, 1)
+    step = np.select([y < 2, y < 4], [0.5, 1.0], 2.0)
+    err = np.abs(deq.astype(np.float64) - r)
+    ok = (err <= sv * step / 2 + 1e-30) | ((y > 6) & np.isclose(err, np.abs(r) - 6 * sv, rtol=1e-6))
+    assert ok.all()
+    assert np.all(packed[3, 16:24] == 0) and scales[3, 2] == 0
+
+
+def test_nvfp4_nibble_order():
+    r = np.zeros((1, 16), dtype=np.float32)
+    r[0, 0], r[0, 1] = 6.0, 0.5          # amax 6 -> s = 1 exactly
+    packed, scales = O.nvfp4_quantize(r)
+    assert O.e4m3_value(scales)[0, 0] == 1.0
+    assert packed[0, 0] == (0x7 | (0x1 << 4))
+
+
+# ---------------------------------------------------------------- selection
+def test_topk_bruteforce_and_ties():
+    for _ in range(200):
+        K = int(RNG.integers(1, 17))
+        k = int(RNG.integers(1, K + 1))
+        D = RNG.integers(0, 4, size=K).astype(np.float64)      # many exact ties
+        want = np.lexsort((np.arange(K), -D))[:k]
+        assert np.array_equal(O.topk_clusters(D, k), want)
+    D = RNG.normal(size=8)
+    assert sorted(O.topk_clusters(D, 8).tolist()) == list(range(8))
+    assert O.topk_clusters(np.zeros(8), 4).tolist() == [0, 1, 2, 3]
+    assert O.topk_clusters(np.array([5, 1, 9, 9.0]), 3, k_eff=3).tolist() == [2, 0, 1]
+
+
+def test_select_rows_bruteforce():
+    m = RNG.integers(0, 8, size=96)
+    top = np.array([6, 1, 3, 0])
+    want = np.nonzero(np.isin(m, top))[0]
+    assert np.array_equal(O.select_rows(m, top), want)
+
+
+def test_window_positions_bruteforce():
+    for n, s, B, pre, suf in [(320, 64, 32, 64, 32), (100, 0, 32, 64, 32), (96, 64, 32, 64, 32),
+                              (1024, 992, 32, 64, 32), (50, 30, 8, 16, 8)]:
+        want = [j for j in range(n) if s - pre <= j < s + B + suf and not (s <= j < s + B)]
+        assert O.window_positions(s, n, B, pre, suf).tolist() == want
+
+
+def test_trigger_truth_table():
+    assert [O.should_refresh(c, 3) for c in range(7)] == [False] * 4 + [True] * 3
+    assert not O.should_refresh(10**6, None)
+    assert O.should_refresh(1, 0) and not O.should_refresh(0, 0)
+
+
+# ---------------------------------------------------------------- commit
+def test_commit_threshold_limits_and_boundaries():
+    f = np.float32
+    tau_s, alpha = 0.9, 10.0
+    # tau_d = 0 at c = tau_s, and alpha * tau_s^2 at c = 0
+    _, _, taud, _, _ = O.commit_decide([0.0, 0.0], [f(tau_s), 0.0], [1, 1], np.zeros((2, 5)), [0, 0], 5, alpha, tau_s)
+    assert taud[0] == 0.0 and abs(taud[1] - alpha * tau_s ** 2) < 1e-5
+    # c exactly tau_s commits (c >= tau_s); spike exactly tau_d does not (strict >)
+    c = np.array([f(tau_s), f(0.5), f(0.5), f(0.95)])
+    td = f(f(alpha) * f(f(f(tau_s) - f(0.5)) ** 2))
+    delta = np.array([0.0, td, np.nextafter(td, np.float32(10)), 0.0], dtype=np.float32)
+    commit, spike, _, _, _ = O.commit_decide(delta, c, [1, 1, 1, 0], np.zeros((4, 5)), [0] * 4, 5, alpha, tau_s)
+    assert commit.tolist() == [1, 0, 1, 0]            # last one is not masked
+
+
+def test_commit_history_mean_and_ring():
+    hv = np.zeros((1, 3), dtype=np.float32)
+    hc = np.zeros(1, dtype=np.int32)
+    seq = [1.0, 2.0, 4.0, 8.0, 16.0]
+    spikes = []
+    for d in seq:
+        _, sp, _, hv, hc = O.commit_decide([d], [0.0], [1], hv, hc, 3, 10.0, 0.9)
+        spikes.append(float(sp[0]))
+    # history holds the previous <= 3 deltas; its mean is subtracted
+    assert np.allclose(spikes, [1.0, 1.0, 2.5, 8.0 - 7.0 / 3.0, 16.0 - 14.0 / 3.0], rtol=1e-6)
+    assert hv[0].tolist() == [4.0, 8.0, 16.0]
+    # h = 0: raw drift
+    _, sp, _, _, _ = O.commit_decide([3.5], [0.0], [1], np.zeros((1, 1)), [0], 0, 10.0, 0.9)
+    assert sp[0] == np.float32(3.5)
+
+
+def test_confidence_matches_torch_softmax():
+    V, d = 50, 16
+    x = RNG.normal(size=(6, d))
+    w = RNG.normal(size=(V, d))
+    x[2] = w[7] * 40                        # planted: id 7 dominates
+    c, yhat, _ = O.confidence(x, w, mask_id=V - 1, eps=1e-6)
+    p = torch.softmax(F.linear(F.rms_norm(torch.tensor(x), (d,), eps=1e-6), torch.tensor(w)), dim=1).numpy()
+    p[:, V - 1] = -1
+    assert np.allclose(c, p.max(axis=1), rtol=1e-12)
+    assert np.array_equal(yhat, p.argmax(axis=1))
+    assert yhat[2] == 7 and c[2] > 0.99
+    assert np.all(c >= 1.0 / V - 1e-12) and np.all(c <= 1.0)
+
+
+def test_suffix_commit_rule():
+    out = O.suffix_commit([0.95, 0.9, 0.5, 0.99], [1, 1, 1, 0], 0.9)
+    assert out.tolist() == [1, 1, 0, 0]
+
+
+# ---------------------------------------------------------------- the k = K identity
+def _tiny_stack(n_layers, d=32, hq=4, hkv=2, dh=8, f=48, seed=7):
+    rng = np.random.default_rng(seed)
+    s = 1 / math.sqrt(d)
+    return [{"wq": rng.normal(size=(hq * dh, d)) * s, "wk": rng.normal(size=(hkv * dh, d)) * s,
+             "wv": rng.normal(size=(hkv * dh, d)) * s, "wo": rng.normal(size=(d, hq * dh)) * s,
+             "wg": rng.normal(size=(f, d)) * s, "wu": rng.normal(size=(f, d)) * s,
+             "wd": rng.normal(size=(d, f)) * s} for _ in range(n_layers)]
+
+
+def _run_refresh_steps(cfg, layers, h0, blk_start, steps, tau_upd, rng, k_override=None):
+    """Oracle refresh loop over a stack; returns final per-layer states and h0."""
+    n_layers = len(layers)
+    Hs, Ks, Vs, _ = O.full_forward(h0, layers, cfg)
+    wpos = O.window_positions(blk_start, cfg.n, cfg.B, cfg.pre, cfg.suf)
+    states = []
+    for l in range(n_layers):
+        init = rng.permutation(len(wpos))[: min(cfg.K, len(wpos))]
+        states.append(O.block_entry_layer_state(Hs[l], Ks[l], Vs[l], layers[l]["wq"], cfg, blk_start, init))
+    h0 = h0.copy()
+    decoded = 0
+    for t in range(steps):
+        pos = blk_start + rng.choice(cfg.B, size=2, replace=False)
+        h0[pos] += rng.normal(size=(2, cfg.d)) * 0.3
+        decoded += 2
+        refresh = O.should_refresh(decoded, tau_upd)
+        if refresh:
+            decoded = 0
+        h_act = cfg.st(h0[blk_start: blk_start + cfg.B])
+        u_rows, u_idx = None, None
+        for l in range(n_layers):
+            ls = states[l]
+            if refresh:
+                cu = O.cluster_update(ls, cfg, u_rows, u_idx)
+                dr = O.drift_layer(ls, layers[l], cfg, blk_start, h_act, cu["h"], cu["patched"], True)
+                S = dr["S"]
+                rf = O.refresh_layer(layers[l], cfg, h_act, cu["h"], dr["o"], S)
+                u_rows, u_idx = rf["U"], S
+            else:
+                dr = O.drift_layer(ls, layers[l], cfg, blk_start, h_act, None, None, False)
+                rf = O.refresh_layer(layers[l], cfg, h_act, np.zeros((0, cfg.d)), dr["o"], np.zeros(0, int))
+            h_act = rf["h_act_out"]
+    return states, h0, h_act
+
+
+def test_refresh_with_k_equal_K_matches_dense_recompute():
+    # prompt 64 + gen 64, B = 32, block 0: the window covers every non-active position.
+    layers = _tiny_stack(3)
+    cfg = O.Cfg(d=32, n_heads=4, n_kv_heads=2, head_dim=8, ffn=48, n_pos=128, block=32, win_prefix=64,
+                win_suffix=32, n_clusters=8, top_k=8, dtype="f64")
+    rng = np.random.default_rng(3)
+    h0 = rng.normal(size=(128, 32))
+    states, h0_final, h_act = _run_refresh_steps(cfg, layers, h0, 64, steps=4, tau_upd=0, rng=rng)
+    Hs, Ks, Vs, _ = O.full_forward(h0_final, layers, cfg)
+    wpos = O.window_positions(64, 128, 32, 64, 32)
+    for l in range(3):
+        assert np.allclose(states[l]["K"], Ks[l], rtol=0, atol=1e-11)
+        assert np.allclose(states[l]["V"], Vs[l], rtol=0, atol=1e-11)
+        assert np.allclose(states[l]["H"], Hs[l][wpos], rtol=0, atol=1e-11)
+    assert np.allclose(h_act, Hs[3][64:96], atol=1e-11)
+
+
+def test_refresh_with_k_below_K_is_not_dense():
+    # sanity: the identity above is not vacuous; k < K leaves stale rows behind.
+    layers = _tiny_stack(3)
+    cfg = O.Cfg(d=32, n_heads=4, n_kv_heads=2, head_dim=8, ffn=48, n_pos=128, block=32, win_prefix=64,
+                win_suffix=32, n_clusters=8, top_k=2, dtype="f64")
+    rng = np.random.default_rng(3)
+    h0 = rng.normal(size=(128, 32))
+    states, h0_final, _ = _run_refresh_steps(cfg, layers, h0, 64, steps=4, tau_upd=0, rng=rng)
+    Hs, Ks, _, _ = O.full_forward(h0_final, layers, cfg)
+    assert not np.allclose(states[2]["K"], Ks[2], atol=1e-6)
+
+
+def test_no_refresh_leaves_window_caches_untouched():
+    layers = _tiny_stack(2)
+    cfg = O.Cfg(d=32, n_heads=4, n_kv_heads=2, head_dim=8, ffn=48, n_pos=128, block=32, win_prefix=64,
+                win_suffix=32, n_clusters=8, top_k=4, dtype="bf16")
+    rng = np.random.default_rng(5)
+    h0 = rng.normal(size=(128, 32))
+    Hs, Ks, Vs, _ = O.full_forward(h0, layers, cfg)
+    rng2 = np.random.default_rng(5)
+    rng2.normal(size=(128, 32))
+    states, _, _ = _run_refresh_steps(cfg, layers, h0, 64, steps=3, tau_upd=None, rng=rng2)
+    jb = np.arange(64, 96)
+    other = np.setdiff1d(np.arange(128), jb)
+    for l in range(2):
+        assert np.array_equal(states[l]["K"][other], Ks[l][other])
+        assert np.array_equal(states[l]["V"][other], Vs[l][other])
+        assert np.array_equal(states[l]["H"], Hs[l][O.window_positions(64, 128, 32, 64, 32)])
+
+
+def test_kv_rows_follow_fresh_packet():
+    cfg = O.Cfg(d=32, n_heads=4, n_kv_heads=2, head_dim=8, ffn=48, n_pos=128, block=32, win_prefix=64,
+                win_suffix=32, n_clusters=8, top_k=4, dtype="bf16")
+    u = O.round_bf16(RNG.normal(size=(5, 32)))
+    wk, wv = RNG.normal(size=(16, 32)), RNG.normal(size=(16, 32))
+    k, v = O.kv_rows(u, wk, wv, cfg)
+    want = F.linear(F.rms_norm(torch.tensor(u), (32,), eps=1e-6), torch.tensor(wk)).to(torch.float32)
+    # every stored value is a bf16 number within half a bf16 ulp of the exact projection
+    assert np.array_equal(O.round_bf16(k.reshape(5, 16)), k.reshape(5, 16))
+    assert np.allclose(k.reshape(5, 16), want.numpy(), rtol=2 ** -8, atol=1e-6)
