@@ -1,0 +1,206 @@
+"""ctypes binding of libpolestar.so (include/polestar.h): argument marshalling only.
+
+Every refresh-path step runs in the library's HIP kernels; this module converts
+Python/torch arguments into the C structs and pointers the library takes.  It
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpolestar.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_ALIGN, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, BF16 = 0, 1
+RESID_RAW, RESID_NVFP4 = 0, 1
+CLUSTER_ENTRY, CLUSTER_UPDATE = 0, 1
+DRIFT_REFRESH, DRIFT_ACTIVE_ONLY = 0, 1
+W_QKV, W_O, W_GU, W_DOWN, W_KV, W_LM = 0, 1, 2, 3, 4, 5
+
+EXPORTED = [
+    "polestar_create", "polestar_destroy", "polestar_strerror", "polestar_workspace_size",
+    "polestar_set_check", "polestar_weight_packed_size", "polestar_pack_weight", "polestar_cluster",
+    "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
+    "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host",
+]
+
+
+class Dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "d", "n_heads", "n_kv_heads", "head_dim", "ffn", "n_pos", "batch", "block", "win_prefix",
+        "win_suffix", "n_clusters", "top_k", "vocab", "dtype", "resid_fmt")]
+
+
+class Params(C.Structure):
+    _fields_ = [("rms_eps", C.c_float), ("tau_s", C.c_float), ("tau_suf", C.c_float), ("alpha", C.c_float),
+                ("hist", C.c_int32), ("mask_id", C.c_int32), ("kmeans_iters", C.c_int32)]
+
+
+class Layer(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gu", C.c_void_p), ("w_down", C.c_void_p),
+                ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("win_h", C.c_void_p),
+                ("win_codes", C.c_void_p), ("win_scales", C.c_void_p), ("win_z", C.c_void_p),
+                ("win_m", C.c_void_p), ("proxy_logits", C.c_void_p)]
+
+
+class Packet(C.Structure):
+    _fields_ = [("rows", C.c_void_p), ("idx", C.c_void_p), ("count", C.c_void_p)]
+
+
+class Check(C.Structure):
+    _fields_ = [("qkv", C.c_void_p), ("attn_out", C.c_void_p), ("hp", C.c_void_p), ("out", C.c_void_p),
+                ("kv_next", C.c_void_p)]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+class PolestarError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m drift_driven_sparse_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.polestar_create.argtypes = [C.POINTER(Dims), C.POINTER(Params), C.POINTER(vp)]
+        L.polestar_destroy.argtypes = [vp]
+        L.polestar_destroy.restype = None
+        L.polestar_strerror.argtypes = [C.c_int]
+        L.polestar_strerror.restype = C.c_char_p
+        L.polestar_workspace_size.argtypes = [vp, C.POINTER(sz)]
+        L.polestar_set_check.argtypes = [vp, C.POINTER(Check)]
+        L.polestar_weight_packed_size.argtypes = [vp, C.c_int, C.POINTER(sz)]
+        L.polestar_pack_weight.argtypes = [vp, C.c_int, vp, vp, vp]
+        L.polestar_cluster.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, C.POINTER(Packet), vp, vp, vp, vp, sz, vp]
+        L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
+                                     C.POINTER(Packet), vp, vp, vp, sz, vp]
+        L.polestar_refresh.argtypes = [vp, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp, vp, vp, vp, vp, sz, vp]
+        L.polestar_commit.argtypes = [vp, i32, vp, vp, C.POINTER(Packet), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+        L.polestar_should_refresh.argtypes = [i32, i32]
+        L.polestar_nvfp4_pack.argtypes = [vp, i64, i32, vp, vp, vp]
+        L.polestar_nvfp4_unpack.argtypes = [vp, vp, i64, i32, vp, vp]
+        L.polestar_nvfp4_pack_host.argtypes = [vp, i64, i32, vp, vp]
+        for name in EXPORTED:
+            f = getattr(L, name)
+            if name not in ("polestar_destroy", "polestar_strerror"):
+                f.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().polestar_strerror(code).decode()
+
+
+def _ck(code: int, where: str) -> None:
+    if code != OK:
+        raise PolestarError(code, where)
+
+
+def ptr(t) -> Optional[int]:
+    """Device/host address of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def stream_ptr(stream=None) -> Optional[int]:
+    import torch
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ---- thin wrappers with the C names ------------------------------------------------------
+def polestar_create(dims: Dims, params: Params) -> int:
+    h = C.c_void_p()
+    _ck(lib().polestar_create(C.byref(dims), C.byref(params), C.byref(h)), "polestar_create")
+    return h.value
+
+
+def polestar_destroy(h: int) -> None:
+    lib().polestar_destroy(h)
+
+
+def polestar_workspace_size(h: int) -> int:
+    n = C.c_size_t()
+    _ck(lib().polestar_workspace_size(h, C.byref(n)), "polestar_workspace_size")
+    return n.value
+
+
+def polestar_set_check(h: int, chk: Optional[Check]) -> None:
+    _ck(lib().polestar_set_check(h, C.byref(chk) if chk is not None else None), "polestar_set_check")
+
+
+def polestar_weight_packed_size(h: int, which: int) -> int:
+    n = C.c_size_t()
+    _ck(lib().polestar_weight_packed_size(h, which, C.byref(n)), "polestar_weight_packed_size")
+    return n.value
+
+
+def polestar_pack_weight(h: int, which: int, src, dst, stream=None) -> None:
+    _ck(lib().polestar_pack_weight(h, which, ptr(src), ptr(dst), stream_ptr(stream)), "polestar_pack_weight")
+
+
+def _pk(p: Optional[Packet]):
+    return C.byref(p) if p is not None else None
+
+
+def polestar_cluster(h, mode, layer: Layer, blk_start, u_in: Optional[Packet], init_idx, entry_h, objective,
+                     ws, ws_bytes, stream=None) -> None:
+    _ck(lib().polestar_cluster(h, mode, C.byref(layer), blk_start, _pk(u_in), ptr(init_idx), ptr(entry_h),
+                               ptr(objective), ptr(ws), ws_bytes, stream_ptr(stream)), "polestar_cluster")
+
+
+def polestar_drift(h, mode, layer: Layer, blk_start, h_active, u_in: Optional[Packet], D, topk, sel: Packet,
+                   act_logits, delta, ws, ws_bytes, stream=None) -> None:
+    _ck(lib().polestar_drift(h, mode, C.byref(layer), blk_start, ptr(h_active), _pk(u_in), ptr(D), ptr(topk),
+                             C.byref(sel), ptr(act_logits), ptr(delta), ptr(ws), ws_bytes, stream_ptr(stream)),
+        "polestar_drift")
+
+
+def polestar_refresh(h, layer: Layer, blk_start, h_active, sel: Packet, w_kv_next, k_next, v_next, h_active_out,
+                     u_rows, ws, ws_bytes, stream=None) -> None:
+    _ck(lib().polestar_refresh(h, C.byref(layer), blk_start, ptr(h_active), C.byref(sel), ptr(w_kv_next),
+                               ptr(k_next), ptr(v_next), ptr(h_active_out), ptr(u_rows), ptr(ws), ws_bytes,
+                               stream_ptr(stream)), "polestar_refresh")
+
+
+def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,
+                    hist_vals, hist_cnt, commit_active, commit_suffix, conf_active, yhat_active, spike, conf_suffix,
+                    ws, ws_bytes, stream=None) -> None:
+    _ck(lib().polestar_commit(h, blk_start, ptr(w_lm), ptr(h_final), _pk(u_final), ptr(delta), ptr(active_masked),
+                              ptr(suffix_masked), ptr(hist_vals), ptr(hist_cnt), ptr(commit_active),
+                              ptr(commit_suffix), ptr(conf_active), ptr(yhat_active), ptr(spike), ptr(conf_suffix),
+                              ptr(ws), ws_bytes, stream_ptr(stream)), "polestar_commit")
+
+
+def polestar_should_refresh(decoded_since_refresh: int, tau_upd: int) -> bool:
+    return bool(lib().polestar_should_refresh(decoded_since_refresh, tau_upd))
+
+
+def polestar_nvfp4_pack(x, rows, d, codes, scales, stream=None) -> None:
+    _ck(lib().polestar_nvfp4_pack(ptr(x), rows, d, ptr(codes), ptr(scales), stream_ptr(stream)), "polestar_nvfp4_pack")
+
+
+def polestar_nvfp4_unpack(codes, scales, rows, d, x, stream=None) -> None:
+    _ck(lib().polestar_nvfp4_unpack(ptr(codes), ptr(scales), rows, d, ptr(x), stream_ptr(stream)),
+        "polestar_nvfp4_unpack")
+
+
+def polestar_nvfp4_pack_host(x, rows, d, codes, scales) -> None:
+    _ck(lib().polestar_nvfp4_pack_host(ptr(x), rows, d, ptr(codes), ptr(scales)), "polestar_nvfp4_pack_host")

@@ -1,0 +1,687 @@
+// C ABI of the Polestar refresh library: host-side validation, workspace layout
+// and the launch sequence of each call.  Every argument is checked before the
+// first launch, so a call that returns an error has enqueued nothing.
+#include <new>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxRows = 144;   // rows of one projection tile column
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elt(const polestar_handle* h) { return h->dm.dtype == POLESTAR_BF16 ? 2 : 4; }
+
+void layout(polestar_handle* h) {
+  const polestar_dims& d = h->dm;
+  const size_t T = elt(h), Bt = d.batch;
+  WsLayout& w = h->ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += ps_align256(bytes); return o; };
+  w.win_rows = take(Bt * h->win_max * d.d * T);
+  w.flags = take(Bt * h->win_max * 4);
+  w.a_qkv = take(Bt * h->mq * d.d * T);
+  w.inv_qkv = take(Bt * h->mq * 4);
+  w.q = take(Bt * h->mq * (size_t)h->nq * 4);
+  w.o = take(Bt * h->mt * (size_t)h->nq * 4);
+  w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
+  w.akl = take(Bt * d.block * d.n_heads * 4);
+  w.part = take((size_t)h->ksplit * Bt * h->mt * d.d * 4);
+  w.hp = take(Bt * h->mt * d.d * 4);
+  w.inv_hp = take(Bt * h->mt * 4);
+  w.act = take(Bt * h->mt * (size_t)d.ffn * 4);
+  w.inv_out = take(Bt * h->mt * 4);
+  w.xhat = take(Bt * h->win_max * d.d * 8);
+  w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
+  const size_t lm_rows = d.block + d.win_suffix;
+  if (d.vocab > 0) {
+    w.lm_a = take(Bt * lm_rows * d.d * T);
+    w.lm_inv = take(Bt * lm_rows * 4);
+    w.lm_stats = take(Bt * lm_rows * (size_t)h->lm_tiles * 4 * 4);
+    w.lm_meta = take(Bt * 2 * 4);
+  } else {
+    w.lm_a = w.lm_inv = w.lm_stats = w.lm_meta = 0;
+  }
+  w.total = off;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
+
+int check_ws(const polestar_handle* h, const void* ws, size_t ws_bytes) {
+  if (!ws) return POLESTAR_E_NULL;
+  if (((uintptr_t)ws & 255u) != 0) return POLESTAR_E_ALIGN;
+  if (ws_bytes < h->ws.total) return POLESTAR_E_WORKSPACE;
+  return POLESTAR_OK;
+}
+
+int check_blk(const polestar_handle* h, int32_t blk_start) {
+  if (blk_start < 0 || blk_start + h->dm.block > h->dm.n_pos) return POLESTAR_E_ARG;
+  return POLESTAR_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? POLESTAR_OK : POLESTAR_E_HIP; }
+
+WinGeom geom_of(const polestar_handle* h, int32_t blk_start) {
+  return make_geom(blk_start, h->dm.n_pos, h->dm.block, h->dm.win_prefix, h->dm.win_suffix);
+}
+
+template <typename T>
+int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+               const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, double* objective,
+               void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  ClusterArgs a;
+  memset(&a, 0, sizeof(a));
+  a.mode = mode;
+  a.batch = d.batch;
+  a.d = d.d;
+  a.K = d.n_clusters;
+  a.win_max = h->win_max;
+  a.block = d.block;
+  a.n_pos = d.n_pos;
+  a.iters = h->pr.kmeans_iters;
+  a.geom = geom_of(h, blk_start);
+  a.win_h = L->win_h;
+  a.codes = L->win_codes;
+  a.scales = L->win_scales;
+  a.win_z = L->win_z;
+  a.win_m = L->win_m;
+  a.entry_h = entry_h;
+  a.init_idx = init_idx;
+  a.objective = objective;
+  if (u_in) {
+    a.u_rows = u_in->rows;
+    a.u_idx = u_in->idx;
+    a.u_count = u_in->count;
+  }
+  a.ws_rows = at<char>(ws, h->ws.win_rows);
+  a.flags = at<int32_t>(ws, h->ws.flags);
+  a.xhat = at<double>(ws, h->ws.xhat);
+  a.z64 = at<double>(ws, h->ws.z64);
+  a.nvfp4 = d.resid_fmt == POLESTAR_RESID_NVFP4;
+  if (a.geom.n_win == 0) return POLESTAR_OK;
+  return hip_status(launch_cluster<T>(a, s));
+}
+
+template <typename T>
+int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
+             const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
+             float* delta, void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const int refresh = mode == POLESTAR_DRIFT_REFRESH && g.n_win > 0;
+  (void)u_in;
+  // 1. QKV rows
+  PrepArgs p;
+  memset(&p, 0, sizeof(p));
+  p.batch = d.batch;
+  p.d = d.d;
+  p.block = d.block;
+  p.win_max = h->win_max;
+  p.n_win = g.n_win;
+  p.K = d.n_clusters;
+  p.mq = h->mq;
+  p.refresh = refresh;
+  p.h_act = h_active;
+  p.ws_rows = at<char>(ws, h->ws.win_rows);
+  p.win_z = L->win_z;
+  p.a_qkv = at<char>(ws, h->ws.a_qkv);
+  p.inv = at<float>(ws, h->ws.inv_qkv);
+  p.eps = h->pr.rms_eps;
+  hipError_t e = launch_prep_qkv<T>(p, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 2. projections; K/V of the active block and of the packet rows go to the cache
+  const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
+  GemmArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.A.base = p.a_qkv;
+  ga.A.bstride = (int64_t)h->mq * d.d;
+  ga.A.lda = d.d;
+  ga.A.rows_static = rows;
+  ga.W = L->w_qkv;
+  ga.N = h->nq + 2 * h->nkv;
+  ga.K = d.d;
+  ga.batch = d.batch;
+  ga.ksplit = 1;
+  EpiParams ep;
+  memset(&ep, 0, sizeof(ep));
+  ep.kind = EPI_QKV;
+  ep.inv_rms = p.inv;
+  ep.inv_bstride = h->mq;
+  ep.q = at<float>(ws, h->ws.q);
+  ep.q_rows = h->mq;
+  ep.kc = L->k_cache;
+  ep.vc = L->v_cache;
+  ep.flags = at<int32_t>(ws, h->ws.flags);
+  ep.nq = h->nq;
+  ep.nkv = h->nkv;
+  ep.block = d.block;
+  ep.win_max = h->win_max;
+  ep.n_pos = d.n_pos;
+  ep.geom = g;
+  ep.chk = h->chk.qkv;
+  ep.chk_rows = h->mq;
+  ep.chk_ld = ga.N;
+  e = launch_gemm<T>(ga, ep, rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 3. attention, proxy attention and drift
+  AttnArgs at_;
+  memset(&at_, 0, sizeof(at_));
+  at_.batch = d.batch;
+  at_.n_pos = d.n_pos;
+  at_.hq = d.n_heads;
+  at_.hkv = d.n_kv_heads;
+  at_.dh = d.head_dim;
+  at_.mq = h->mq;
+  at_.mt = h->mt;
+  at_.n_tok = refresh ? d.block + g.n_win : d.block;
+  at_.n_proxy = refresh ? d.n_clusters : 0;
+  at_.block = d.block;
+  at_.q = ep.q;
+  at_.kc = L->k_cache;
+  at_.vc = L->v_cache;
+  at_.o = at<char>(ws, h->ws.o);
+  at_.proxy_logits = L->proxy_logits;
+  at_.kl = at<float>(ws, h->ws.kl);
+  at_.act_logits = act_logits;
+  at_.act_kl = delta != nullptr;
+  at_.akl = at<float>(ws, h->ws.akl);
+  at_.chk = h->chk.attn_out;
+  at_.chk_rows = h->mt;
+  e = launch_attention<T>(at_, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 4. top-k clusters and the selected rows
+  TopkArgs tk;
+  memset(&tk, 0, sizeof(tk));
+  tk.batch = d.batch;
+  tk.K = d.n_clusters;
+  tk.k = d.top_k;
+  tk.hq = d.n_heads;
+  tk.block = d.block;
+  tk.win_max = h->win_max;
+  tk.n_win = g.n_win;
+  tk.kl = at_.kl;
+  tk.win_m = L->win_m;
+  tk.D = D;
+  tk.topk = topk;
+  tk.sel_idx = sel->idx;
+  tk.sel_count = sel->count;
+  tk.akl = at_.akl;
+  tk.delta = (act_logits && delta) ? delta : nullptr;
+  tk.refresh = refresh;
+  return hip_status(launch_topk(tk, s));
+}
+
+template <typename T>
+int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
+               const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
+               void* u_rows, void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const int max_rows = d.block + g.n_win;
+  float* part = at<float>(ws, h->ws.part);
+  // 1. h' = h + o W_O^T over rows [active; S]
+  GemmArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.A.base = at<char>(ws, h->ws.o);
+  ga.A.f32 = 1;
+  ga.A.bstride = (int64_t)h->mt * h->nq;
+  ga.A.lda = h->nq;
+  ga.A.rowmap = sel->idx;
+  ga.A.map_bstride = h->win_max;
+  ga.A.map_from = d.block;
+  ga.A.map_off = d.block;
+  ga.A.rows_dev = sel->count;
+  ga.A.rows_add = d.block;
+  ga.A.rows_max = max_rows;
+  ga.W = L->w_o;
+  ga.N = d.d;
+  ga.K = h->nq;
+  ga.batch = d.batch;
+  ga.ksplit = h->ksplit;
+  ga.part = part;
+  ga.part_rows = h->mt;
+  EpiParams ep;
+  memset(&ep, 0, sizeof(ep));
+  ep.kind = EPI_PARTIAL;
+  hipError_t e = launch_gemm<T>(ga, ep, max_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  RowReduceArgs rr;
+  memset(&rr, 0, sizeof(rr));
+  rr.part = part;
+  rr.ksplit = h->ksplit;
+  rr.part_rows = h->mt;
+  rr.batch = d.batch;
+  rr.d = d.d;
+  rr.count = sel->count;
+  rr.block = d.block;
+  rr.win_max = h->win_max;
+  rr.res_a = h_active;
+  rr.res_a_bstride = (int64_t)d.block * d.d;
+  rr.res_split = d.block;
+  rr.res_b = at<char>(ws, h->ws.win_rows);
+  rr.res_b_bstride = (int64_t)h->win_max * d.d;
+  rr.sel_idx = sel->idx;
+  rr.out_a = at<char>(ws, h->ws.hp);
+  rr.out_a_bstride = (int64_t)h->mt * d.d;
+  rr.out_split = h->mt;
+  rr.out_f32 = 1;
+  rr.inv_rms = at<float>(ws, h->ws.inv_hp);
+  rr.inv_bstride = h->mt;
+  rr.eps = h->pr.rms_eps;
+  rr.chk = h->chk.hp;
+  rr.chk_rows = h->mt;
+  e = launch_row_reduce<T>(rr, max_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 2. act = silu(g) * u with g, u the projections of RMSNorm(h')
+  memset(&ga, 0, sizeof(ga));
+  ga.A.base = rr.out_a;
+  ga.A.f32 = 1;
+  ga.A.bstride = (int64_t)h->mt * d.d;
+  ga.A.lda = d.d;
+  ga.A.rows_dev = sel->count;
+  ga.A.rows_add = d.block;
+  ga.A.rows_max = max_rows;
+  ga.W = L->w_gu;
+  ga.N = 2 * d.ffn;
+  ga.K = d.d;
+  ga.batch = d.batch;
+  ga.ksplit = 1;
+  memset(&ep, 0, sizeof(ep));
+  ep.kind = EPI_SWIGLU;
+  ep.inv_rms = rr.inv_rms;
+  ep.inv_bstride = h->mt;
+  ep.act = at<char>(ws, h->ws.act);
+  ep.act_rows = h->mt;
+  ep.ffn = d.ffn;
+  e = launch_gemm<T>(ga, ep, max_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 3. out = h' + act W_down^T -> next active rows and the update packet
+  memset(&ga, 0, sizeof(ga));
+  ga.A.base = ep.act;
+  ga.A.f32 = 1;
+  ga.A.bstride = (int64_t)h->mt * d.ffn;
+  ga.A.lda = d.ffn;
+  ga.A.rows_dev = sel->count;
+  ga.A.rows_add = d.block;
+  ga.A.rows_max = max_rows;
+  ga.W = L->w_down;
+  ga.N = d.d;
+  ga.K = d.ffn;
+  ga.batch = d.batch;
+  ga.ksplit = h->ksplit;
+  ga.part = part;
+  ga.part_rows = h->mt;
+  memset(&ep, 0, sizeof(ep));
+  ep.kind = EPI_PARTIAL;
+  e = launch_gemm<T>(ga, ep, max_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // the residual stream continues from the unrounded h'
+  RowReduceArgs r2 = rr;
+  r2.res_a = rr.out_a;
+  r2.res_a_f32 = 1;
+  r2.res_a_bstride = (int64_t)h->mt * d.d;
+  r2.res_split = h->mt;
+  r2.out_f32 = 0;
+  r2.res_b = nullptr;
+  r2.out_a = h_active_out;
+  r2.out_a_bstride = (int64_t)d.block * d.d;
+  r2.out_split = d.block;
+  r2.out_b = u_rows;
+  r2.out_b_bstride = (int64_t)h->win_max * d.d;
+  r2.inv_rms = at<float>(ws, h->ws.inv_out);
+  r2.chk = h->chk.out;
+  e = launch_row_reduce<T>(r2, max_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 4. K/V of layer l+1 for the packet rows
+  if (w_kv_next && g.n_win > 0) {
+    memset(&ga, 0, sizeof(ga));
+    ga.A.base = u_rows;
+    ga.A.bstride = (int64_t)h->win_max * d.d;
+    ga.A.lda = d.d;
+    ga.A.rows_dev = sel->count;
+    ga.A.rows_max = g.n_win;
+    ga.W = w_kv_next;
+    ga.N = 2 * h->nkv;
+    ga.K = d.d;
+    ga.batch = d.batch;
+    ga.ksplit = 1;
+    memset(&ep, 0, sizeof(ep));
+    ep.kind = EPI_KV;
+    ep.inv_rms = r2.inv_rms;
+    ep.inv_bstride = h->mt;
+    ep.inv_off = d.block;
+    ep.kc = k_next;
+    ep.vc = v_next;
+    ep.nkv = h->nkv;
+    ep.win_max = h->win_max;
+    ep.n_pos = d.n_pos;
+    ep.geom = g;
+    ep.sel_idx = sel->idx;
+    ep.chk = h->chk.kv_next;
+    ep.chk_rows = h->win_max;
+    ep.chk_ld = 2 * h->nkv;
+    e = launch_gemm<T>(ga, ep, g.n_win, s);
+    if (e != hipSuccess) return POLESTAR_E_HIP;
+  }
+  return POLESTAR_OK;
+}
+
+template <typename T>
+int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,
+              const polestar_packet* u_final, const float* delta, const uint8_t* active_masked,
+              const uint8_t* suffix_masked, float* hist_vals, int32_t* hist_cnt, uint8_t* commit_active,
+              uint8_t* commit_suffix, float* conf_active, int32_t* yhat_active, float* spike, float* conf_suffix,
+              void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const int lm_rows = d.block + d.win_suffix;
+  LmPrepArgs lp;
+  memset(&lp, 0, sizeof(lp));
+  lp.batch = d.batch;
+  lp.d = d.d;
+  lp.block = d.block;
+  lp.win_max = h->win_max;
+  lp.win_suffix = d.win_suffix;
+  lp.n_pre = g.n_pre;
+  lp.lm_rows = lm_rows;
+  lp.h_final = h_final;
+  if (u_final) {
+    lp.u_rows = u_final->rows;
+    lp.u_idx = u_final->idx;
+    lp.u_count = u_final->count;
+  }
+  lp.a_lm = at<char>(ws, h->ws.lm_a);
+  lp.inv = at<float>(ws, h->ws.lm_inv);
+  lp.meta = at<int32_t>(ws, h->ws.lm_meta);
+  lp.eps = h->pr.rms_eps;
+  hipError_t e = launch_lm_prep<T>(lp, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  GemmArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.A.base = lp.a_lm;
+  ga.A.bstride = (int64_t)lm_rows * d.d;
+  ga.A.lda = d.d;
+  ga.A.rows_dev = lp.meta;
+  ga.A.rows_max = lm_rows;
+  ga.W = w_lm;
+  ga.N = d.vocab;
+  ga.K = d.d;
+  ga.batch = d.batch;
+  ga.ksplit = 1;
+  EpiParams ep;
+  memset(&ep, 0, sizeof(ep));
+  ep.kind = EPI_LMSTAT;
+  ep.inv_rms = lp.inv;
+  ep.inv_bstride = lm_rows;
+  ep.lm_stats = at<float>(ws, h->ws.lm_stats);
+  ep.lm_rows = lm_rows;
+  ep.lm_tiles = h->lm_tiles;
+  ep.vocab = d.vocab;
+  ep.mask_id = h->pr.mask_id;
+  e = launch_gemm<T>(ga, ep, lm_rows, s);
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  DecideArgs da;
+  memset(&da, 0, sizeof(da));
+  da.batch = d.batch;
+  da.block = d.block;
+  da.win_suffix = d.win_suffix;
+  da.win_max = h->win_max;
+  da.n_pre = g.n_pre;
+  da.lm_rows = lm_rows;
+  da.lm_tiles = h->lm_tiles;
+  da.hist = h->pr.hist;
+  da.mask_id = h->pr.mask_id;
+  da.tau_s = h->pr.tau_s;
+  da.tau_suf = h->pr.tau_suf;
+  da.alpha = h->pr.alpha;
+  da.lm_stats = ep.lm_stats;
+  da.meta = lp.meta;
+  da.u_idx = lp.u_idx;
+  da.delta = delta;
+  da.active_masked = active_masked;
+  da.suffix_masked = suffix_masked;
+  da.hist_vals = hist_vals;
+  da.hist_cnt = hist_cnt;
+  da.commit_active = commit_active;
+  da.commit_suffix = commit_suffix;
+  da.conf_active = conf_active;
+  da.yhat_active = yhat_active;
+  da.spike = spike;
+  da.conf_suffix = conf_suffix;
+  return hip_status(launch_decide(da, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* polestar_strerror(int code) {
+  switch (code) {
+    case POLESTAR_OK: return "ok";
+    case POLESTAR_E_NULL: return "required pointer is NULL";
+    case POLESTAR_E_SHAPE: return "inconsistent or out-of-range dimension";
+    case POLESTAR_E_DTYPE: return "unknown dtype or residual format";
+    case POLESTAR_E_UNSUPPORTED: return "configuration not supported";
+    case POLESTAR_E_WORKSPACE: return "workspace too small";
+    case POLESTAR_E_ALIGN: return "device pointer misaligned";
+    case POLESTAR_E_HIP: return "HIP runtime error while enqueueing";
+    case POLESTAR_E_ARG: return "invalid mode or scalar argument";
+  }
+  return "unknown error";
+}
+
+int polestar_create(const polestar_dims* dims, const polestar_params* params, polestar_handle** out) {
+  if (!dims || !params || !out) return POLESTAR_E_NULL;
+  *out = nullptr;
+  const polestar_dims& d = *dims;
+  if (d.dtype != POLESTAR_F32 && d.dtype != POLESTAR_BF16) return POLESTAR_E_DTYPE;
+  if (d.resid_fmt != POLESTAR_RESID_RAW && d.resid_fmt != POLESTAR_RESID_NVFP4) return POLESTAR_E_DTYPE;
+  if (d.d <= 0 || d.n_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 || d.ffn <= 0 || d.n_pos <= 0 ||
+      d.batch <= 0 || d.block <= 0 || d.win_prefix < 0 || d.win_suffix < 0 || d.n_clusters <= 0 ||
+      d.top_k <= 0 || d.vocab < 0)
+    return POLESTAR_E_SHAPE;
+  if (d.n_heads % d.n_kv_heads != 0) return POLESTAR_E_SHAPE;
+  if (d.n_pos < d.block) return POLESTAR_E_SHAPE;
+  if (d.n_clusters > 16 || d.top_k > d.n_clusters) return POLESTAR_E_UNSUPPORTED;
+  if (d.head_dim != 64 && d.head_dim != 128) return POLESTAR_E_UNSUPPORTED;
+  if (d.block > 64 || d.win_prefix + d.win_suffix > 256) return POLESTAR_E_UNSUPPORTED;
+  if (d.block + d.win_prefix + d.win_suffix + d.n_clusters > kMaxRows) return POLESTAR_E_UNSUPPORTED;
+  if (d.n_pos > 1024) return POLESTAR_E_UNSUPPORTED;
+  if (d.d % 16 != 0) return POLESTAR_E_UNSUPPORTED;
+  if (d.dtype == POLESTAR_BF16) {
+    if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16) return POLESTAR_E_UNSUPPORTED;
+  } else {
+    if (d.ffn % 4 || d.d % 4) return POLESTAR_E_UNSUPPORTED;
+  }
+  if (d.resid_fmt == POLESTAR_RESID_NVFP4 && d.dtype != POLESTAR_BF16) return POLESTAR_E_UNSUPPORTED;
+  const polestar_params& p = *params;
+  if (!(p.rms_eps >= 0.f) || p.hist < 0 || p.hist > 16 || p.kmeans_iters < 0 || p.kmeans_iters > 1000)
+    return POLESTAR_E_ARG;
+  if (d.vocab > 0 && (p.mask_id < -1 || p.mask_id >= d.vocab)) return POLESTAR_E_ARG;
+  polestar_handle* h = new (std::nothrow) polestar_handle;
+  if (!h) return POLESTAR_E_SHAPE;
+  memset(h, 0, sizeof(*h));
+  h->dm = d;
+  h->pr = p;
+  h->win_max = d.win_prefix + d.win_suffix;
+  h->mq = d.block + h->win_max + d.n_clusters;
+  h->mt = d.block + h->win_max;
+  h->nq = d.n_heads * d.head_dim;
+  h->nkv = d.n_kv_heads * d.head_dim;
+  const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
+  int ks = PS_CEIL_DIV(256, ntiles);
+  h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
+  h->lm_tiles = PS_CEIL_DIV(d.vocab, 64);
+  layout(h);
+  *out = h;
+  return POLESTAR_OK;
+}
+
+void polestar_destroy(polestar_handle* h) { delete h; }
+
+int polestar_workspace_size(const polestar_handle* h, size_t* bytes) {
+  if (!h || !bytes) return POLESTAR_E_NULL;
+  *bytes = h->ws.total;
+  return POLESTAR_OK;
+}
+
+int polestar_set_check(polestar_handle* h, const polestar_check* chk) {
+  if (!h) return POLESTAR_E_NULL;
+  if (chk) h->chk = *chk;
+  else memset(&h->chk, 0, sizeof(h->chk));
+  return POLESTAR_OK;
+}
+
+static int weight_shape(const polestar_handle* h, int which, int* N, int* K) {
+  const polestar_dims& d = h->dm;
+  switch (which) {
+    case POLESTAR_W_QKV: *N = h->nq + 2 * h->nkv; *K = d.d; break;
+    case POLESTAR_W_O: *N = d.d; *K = h->nq; break;
+    case POLESTAR_W_GU: *N = 2 * d.ffn; *K = d.d; break;
+    case POLESTAR_W_DOWN: *N = d.d; *K = d.ffn; break;
+    case POLESTAR_W_KV: *N = 2 * h->nkv; *K = d.d; break;
+    case POLESTAR_W_LM:
+      if (d.vocab <= 0) return POLESTAR_E_SHAPE;
+      *N = d.vocab; *K = d.d; break;
+    default: return POLESTAR_E_ARG;
+  }
+  return POLESTAR_OK;
+}
+
+int polestar_weight_packed_size(const polestar_handle* h, int which, size_t* bytes) {
+  if (!h || !bytes) return POLESTAR_E_NULL;
+  int N, K;
+  int rc = weight_shape(h, which, &N, &K);
+  if (rc) return rc;
+  *bytes = packed_elems(N, K) * elt(h);
+  return POLESTAR_OK;
+}
+
+int polestar_pack_weight(const polestar_handle* h, int which, const void* src, void* dst, void* stream) {
+  if (!h || !src || !dst) return POLESTAR_E_NULL;
+  int N, K;
+  int rc = weight_shape(h, which, &N, &K);
+  if (rc) return rc;
+  if (!aligned16(src) || !aligned16(dst)) return POLESTAR_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = h->dm.dtype == POLESTAR_BF16 ? launch_pack<bf16_t>(which, src, dst, N, K, h->dm.ffn, s)
+                                              : launch_pack<float>(which, src, dst, N, K, h->dm.ffn, s);
+  return hip_status(e);
+}
+
+int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                     const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, double* objective,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !L) return POLESTAR_E_NULL;
+  if (mode != POLESTAR_CLUSTER_ENTRY && mode != POLESTAR_CLUSTER_UPDATE) return POLESTAR_E_ARG;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  const bool nv = h->dm.resid_fmt == POLESTAR_RESID_NVFP4;
+  if (!L->win_z || !L->win_m) return POLESTAR_E_NULL;
+  if (nv ? (!L->win_codes || !L->win_scales) : !L->win_h) return POLESTAR_E_NULL;
+  if (mode == POLESTAR_CLUSTER_ENTRY && (!init_idx || !entry_h)) return POLESTAR_E_NULL;
+  if (u_in && (!u_in->rows || !u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  return h->dm.dtype == POLESTAR_BF16
+             ? do_cluster<bf16_t>(h, mode, L, blk_start, u_in, init_idx, entry_h, objective, ws, s)
+             : do_cluster<float>(h, mode, L, blk_start, u_in, init_idx, entry_h, objective, ws, s);
+}
+
+int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                   const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
+                   float* delta, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !L || !h_active || !sel || !sel->idx || !sel->count) return POLESTAR_E_NULL;
+  if (mode != POLESTAR_DRIFT_REFRESH && mode != POLESTAR_DRIFT_ACTIVE_ONLY) return POLESTAR_E_ARG;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  if (!L->w_qkv || !L->k_cache || !L->v_cache) return POLESTAR_E_NULL;
+  if (mode == POLESTAR_DRIFT_REFRESH && (!L->win_z || !L->win_m || !L->proxy_logits)) return POLESTAR_E_NULL;
+  if (!aligned16(L->w_qkv) || !aligned16(h_active)) return POLESTAR_E_ALIGN;
+  if (delta && !act_logits) return POLESTAR_E_NULL;
+  if (u_in && (!u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  return h->dm.dtype == POLESTAR_BF16
+             ? do_drift<bf16_t>(h, mode, L, blk_start, h_active, u_in, D, topk, sel, act_logits, delta, ws, s)
+             : do_drift<float>(h, mode, L, blk_start, h_active, u_in, D, topk, sel, act_logits, delta, ws, s);
+}
+
+int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                     const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
+                     void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !L || !h_active || !sel || !sel->idx || !sel->count || !h_active_out || !u_rows) return POLESTAR_E_NULL;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  if (!L->w_o || !L->w_gu || !L->w_down) return POLESTAR_E_NULL;
+  if (w_kv_next && (!k_next || !v_next)) return POLESTAR_E_NULL;
+  if (!aligned16(L->w_o) || !aligned16(L->w_gu) || !aligned16(L->w_down) || !aligned16(h_active) ||
+      !aligned16(u_rows) || (w_kv_next && !aligned16(w_kv_next)))
+    return POLESTAR_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  return h->dm.dtype == POLESTAR_BF16
+             ? do_refresh<bf16_t>(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s)
+             : do_refresh<float>(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s);
+}
+
+int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,
+                    const polestar_packet* u_final, const float* delta, const uint8_t* active_masked,
+                    const uint8_t* suffix_masked, float* hist_vals, int32_t* hist_cnt, uint8_t* commit_active,
+                    uint8_t* commit_suffix, float* conf_active, int32_t* yhat_active, float* spike,
+                    float* conf_suffix, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !w_lm || !h_final || !delta || !active_masked || !suffix_masked || !hist_vals || !hist_cnt ||
+      !commit_active || !commit_suffix || !conf_active || !yhat_active || !spike || !conf_suffix)
+    return POLESTAR_E_NULL;
+  if (h->dm.vocab <= 0) return POLESTAR_E_SHAPE;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  if (u_final && (!u_final->rows || !u_final->idx || !u_final->count)) return POLESTAR_E_NULL;
+  if (!aligned16(w_lm) || !aligned16(h_final)) return POLESTAR_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  return h->dm.dtype == POLESTAR_BF16
+             ? do_commit<bf16_t>(h, blk_start, w_lm, h_final, u_final, delta, active_masked, suffix_masked,
+                                 hist_vals, hist_cnt, commit_active, commit_suffix, conf_active, yhat_active, spike,
+                                 conf_suffix, ws, s)
+             : do_commit<float>(h, blk_start, w_lm, h_final, u_final, delta, active_masked, suffix_masked,
+                                hist_vals, hist_cnt, commit_active, commit_suffix, conf_active, yhat_active, spike,
+                                conf_suffix, ws, s);
+}
+
+int polestar_should_refresh(int32_t decoded_since_refresh, int32_t tau_upd) {
+  if (tau_upd < 0) return 0;
+  return decoded_since_refresh > tau_upd ? 1 : 0;
+}
+
+int polestar_nvfp4_pack(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales) return POLESTAR_E_NULL;
+  if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;
+  if (!aligned16(x)) return POLESTAR_E_ALIGN;
+  return hip_status(launch_nvfp4_pack(x, rows, d, codes, scales, (hipStream_t)stream));
+}
+
+int polestar_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                          void* stream) {
+  if (!x || !codes || !scales) return POLESTAR_E_NULL;
+  if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;
+  return hip_status(launch_nvfp4_unpack(codes, scales, rows, d, x, (hipStream_t)stream));
+}
+
+int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales) {
+  if (!x || !codes || !scales) return POLESTAR_E_NULL;
+  if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;
+  const int64_t groups = rows * (d / 16);
+  for (int64_t g = 0; g < groups; ++g) {
+    uint32_t c[16];
+    scales[g] = (uint8_t)nvfp4_group(x + g * 16, c);
+    for (int e = 0; e < 8; ++e) codes[g * 8 + e] = (uint8_t)(c[2 * e] | (c[2 * e + 1] << 4));
+  }
+  return POLESTAR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+// Window clustering kernels: spherical k-means at block entry, the per-step
+// window update (dequantise, patch from the update packet, fixed-label centroid
+// refresh, NVFP4 re-quantisation), the QKV row staging, and the NVFP4 codec
+// test hooks.  Cosines and centroid sums are accumulated in float64 so that the
+// integer decisions (labels) do not depend on the summation order.
+#include "kernels.h"
+
+namespace {
+
+// Row reduction in float64 over a whole workgroup (fixed order).
+PS_DEV double block_sum_d(double v, double* red) { return block_sum<double>(v, red); }
+
+// ---- block entry: spherical k-means ---------------------------------------------------
+// One workgroup per sequence.  xhat/z64/s64 are float64 workspace rows.
+template <typename T>
+__global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, double* s64) {
+  __shared__ double red[16];
+  __shared__ int lab[256];
+  __shared__ double best[256];
+  __shared__ double snorm_sh;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int d = a.d, nwin = a.geom.n_win, K = a.K;
+  const int keff = min(K, nwin);
+  const T* src = (const T*)a.entry_h + (int64_t)b * a.win_max * d;
+  double* xh = a.xhat + (int64_t)b * a.win_max * d;
+  double* z = a.z64 + (int64_t)b * K * d;
+  double* sb = s64 + (int64_t)b * d;
+
+  // unit rows (a zero row stays zero); raw storage copies the rows into the window
+  for (int w = 0; w < nwin; ++w) {
+    double ss = 0.0;
+    for (int n = tid; n < d; n += blockDim.x) {
+      const double x = St<T>::load(src, (int64_t)w * d + n);
+      ss += x * x;
+    }
+    ss = block_sum_d(ss, red);
+    const double nr = sqrt(ss);
+    for (int n = tid; n < d; n += blockDim.x) {
+      const float x = St<T>::load(src, (int64_t)w * d + n);
+      xh[(int64_t)w * d + n] = nr > 0.0 ? (double)x / nr : 0.0;
+      if (!a.nvfp4 && a.win_h != a.entry_h)
+        ((T*)a.win_h)[((int64_t)b * a.win_max + w) * d + n] = ((const T*)src)[(int64_t)w * d + n];
+    }
+  }
+  __syncthreads();
+  for (int c = 0; c < K; ++c) {
+    int r = c < keff ? a.init_idx[(int64_t)b * K + c] : -1;
+    if (r < 0 || r >= nwin) r = -1;
+    for (int n = tid; n < d; n += blockDim.x) z[(int64_t)c * d + n] = (c < keff && r >= 0) ? xh[(int64_t)r * d + n] : 0.0;
+  }
+  __syncthreads();
+  for (int it = 0; it < a.iters; ++it) {
+    // assignment: largest cosine, lowest index on ties
+    for (int w = wave; w < nwin; w += nw) {
+      int bc = 0;
+      double bv = -INFINITY;
+      for (int c = 0; c < keff; ++c) {
+        double t = 0.0;
+        for (int n = lane; n < d; n += 64) t += xh[(int64_t)w * d + n] * z[(int64_t)c * d + n];
+        t = wave_sum(t);
+        if (t > bv) { bv = t; bc = c; }
+      }
+      if (lane == 0) { lab[w] = bc; best[w] = bv; }
+    }
+    __syncthreads();
+    if (tid == 0 && a.objective) {
+      double J = 0.0;
+      for (int w = 0; w < nwin; ++w) J += best[w];
+      a.objective[(int64_t)b * 2 * a.iters + 2 * it] = J;
+    }
+    // update: normalised member sum; empty clusters (or a zero sum) keep their centroid
+    double Jup = 0.0;
+    for (int c = 0; c < keff; ++c) {
+      int cnt = 0;
+      for (int w = 0; w < nwin; ++w) cnt += lab[w] == c;
+      if (cnt == 0) continue;
+      double ss = 0.0;
+      for (int n = tid; n < d; n += blockDim.x) {
+        double s = 0.0;
+        for (int w = 0; w < nwin; ++w)
+          if (lab[w] == c) s += xh[(int64_t)w * d + n];
+        sb[n] = s;
+        ss += s * s;
+      }
+      ss = block_sum_d(ss, red);
+      const double ns = sqrt(ss);
+      if (tid == 0) snorm_sh = ns;
+      Jup += ns;
+      if (ns > 0.0)
+        for (int n = tid; n < d; n += blockDim.x) z[(int64_t)c * d + n] = sb[n] / ns;
+      __syncthreads();
+    }
+    if (tid == 0 && a.objective) a.objective[(int64_t)b * 2 * a.iters + 2 * it + 1] = Jup;
+    __syncthreads();
+  }
+  // outputs: labels, centroids (rounded once), NVFP4 residual codes
+  for (int w = tid; w < a.win_max; w += blockDim.x)
+    a.win_m[(int64_t)b * a.win_max + w] = w < nwin ? (a.iters > 0 ? lab[w] : 0) : 0;
+  for (int i = tid; i < K * d; i += blockDim.x)
+    St<T>::store_d((T*)a.win_z + (int64_t)b * K * d, i, z[i]);
+  __syncthreads();
+  if (a.nvfp4) {
+    const int ng = d / 16;
+    for (int i = tid; i < nwin * ng; i += blockDim.x) {
+      const int w = i / ng, gi = i % ng;
+      const int c = a.iters > 0 ? lab[w] : 0;
+      float r[16];
+      uint32_t codes[16];
+      for (int e = 0; e < 16; ++e) {
+        const float h = St<T>::load(src, (int64_t)w * d + gi * 16 + e);
+        const float zz = St<T>::load((const T*)a.win_z + ((int64_t)b * K + c) * d, gi * 16 + e);
+        r[e] = h - zz;
+      }
+      const uint32_t sc = nvfp4_group(r, codes);
+      const int64_t row = (int64_t)b * a.win_max + w;
+      a.scales[row * ng + gi] = (uint8_t)sc;
+      for (int e = 0; e < 8; ++e) a.codes[row * (d / 2) + gi * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
+    }
+  }
+}
+
+// ---- per refresh step: window update ---------------------------------------------------------
+// One workgroup per (cluster, sequence) handles exactly the window rows labelled with
+// that cluster, so every row and centroid has a single writer.
+template <typename T>
+__global__ __launch_bounds__(256) void window_update_kernel(ClusterArgs a) {
+  __shared__ double red[4];
+  __shared__ int plist[256];      // packet row of each window row, -1 if none
+  __shared__ int mem[256];
+  __shared__ double nrm[256];
+  __shared__ int nmem_sh;
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = a.d, nwin = a.geom.n_win;
+  const int64_t wbase = (int64_t)b * a.win_max;
+  int cnt = a.u_count ? a.u_count[b] : 0;
+  cnt = cnt < 0 ? 0 : (cnt > a.win_max ? a.win_max : cnt);
+  for (int w = tid; w < a.win_max; w += blockDim.x) plist[w] = -1;
+  __syncthreads();
+  for (int r = tid; r < cnt; r += blockDim.x) {
+    const int w = a.u_idx[wbase + r];
+    if (w >= 0 && w < nwin) plist[w] = r;
+  }
+  if (tid == 0) {
+    int m = 0;
+    for (int w = 0; w < nwin; ++w)
+      if (a.win_m[wbase + w] == c) mem[m++] = w;
+    nmem_sh = m;
+  }
+  __syncthreads();
+  const int nmem = nmem_sh;
+  if (nmem == 0) return;
+  T* rows = (T*)a.ws_rows;
+  const T* zc = (const T*)a.win_z + ((int64_t)b * a.K + c) * d;
+  // 1. current rows: packet row, else raw window row or centroid + dequantised residual
+  for (int m = 0; m < nmem; ++m) {
+    const int w = mem[m];
+    const int pr = plist[w];
+    const int64_t dst = (wbase + w) * d;
+    double ss = 0.0;
+    for (int n = tid; n < d; n += blockDim.x) {
+      float x;
+      if (pr >= 0) {
+        x = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n);
+      } else if (a.nvfp4) {
+        const uint8_t byte = a.codes[(wbase + w) * (d / 2) + n / 2];
+        const uint32_t code = (n & 1) ? (byte >> 4) : (byte & 15u);
+        const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n / 16]);
+        x = St<T>::round(St<T>::load(zc, n) + sv * e2m1_value(code));
+      } else {
+        x = St<T>::load((const T*)a.win_h, dst + n);
+      }
+      St<T>::store(rows, dst + n, x);
+      if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n, x);
+      ss += (double)x * (double)x;
+    }
+    ss = block_sum_d(ss, red);
+    if (tid == 0) {
+      nrm[m] = sqrt(ss);
+      a.flags[wbase + w] = pr >= 0;
+    }
+  }
+  __syncthreads();
+  // 2. normalised member sum (float64)
+  double* s = a.z64 + ((int64_t)b * a.K + c) * d;
+  double ss = 0.0;
+  for (int n = tid; n < d; n += blockDim.x) {
+    double acc = 0.0;
+    for (int m = 0; m < nmem; ++m) {
+      const double nr = nrm[m];
+      if (nr > 0.0) acc += (double)St<T>::load(rows, (wbase + mem[m]) * d + n) / nr;
+    }
+    s[n] = acc;
+    ss += acc * acc;
+  }
+  ss = block_sum_d(ss, red);
+  const double ns = sqrt(ss);
+  // 3. centroid (kept when the sum vanishes)
+  if (ns > 0.0)
+    for (int n = tid; n < d; n += blockDim.x) St<T>::store_d((T*)zc, n, s[n] / ns);
+  __syncthreads();
+  // 4. NVFP4: residual to the new centroid
+  if (a.nvfp4) {
+    const int ng = d / 16;
+    for (int i = tid; i < nmem * ng; i += blockDim.x) {
+      const int w = mem[i / ng], gi = i % ng;
+      float r[16];
+      uint32_t codes[16];
+      for (int e = 0; e < 16; ++e)
+        r[e] = St<T>::load(rows, (wbase + w) * d + gi * 16 + e) - St<T>::load(zc, gi * 16 + e);
+      const uint32_t sc = nvfp4_group(r, codes);
+      a.scales[(wbase + w) * ng + gi] = (uint8_t)sc;
+      for (int e = 0; e < 8; ++e)
+        a.codes[(wbase + w) * (d / 2) + gi * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
+    }
+  }
+}
+
+// ---- QKV rows: [active; window; centroids] + 1/rms ---------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int d = a.d;
+  const T* src;
+  if (r < a.block) src = (const T*)a.h_act + ((int64_t)b * a.block + r) * d;
+  else if (r < a.block + a.n_win) src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + (r - a.block)) * d;
+  else src = (const T*)a.win_z + ((int64_t)b * a.K + (r - a.block - a.n_win)) * d;
+  T* dst = (T*)a.a_qkv + ((int64_t)b * a.mq + r) * d;
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < d; n += blockDim.x) {
+    const T v = src[n];
+    dst[n] = v;
+    const float x = St<T>::load(&v, 0);
+    ss += x * x;
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) a.inv[(int64_t)b * a.mq + r] = 1.f / sqrtf(ss / (float)d + a.eps);
+}
+
+// ---- NVFP4 test hooks ---------------------------------------------------------------------------
+__global__ void nvfp4_pack_kernel(const float* x, int64_t groups, int32_t d, uint8_t* codes, uint8_t* scales) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= groups) return;
+  float r[16];
+  uint32_t c[16];
+  for (int e = 0; e < 16; ++e) r[e] = x[g * 16 + e];
+  scales[g] = (uint8_t)nvfp4_group(r, c);
+  for (int e = 0; e < 8; ++e) codes[g * 8 + e] = (uint8_t)(c[2 * e] | (c[2 * e + 1] << 4));
+}
+
+__global__ void nvfp4_unpack_kernel(const uint8_t* codes, const uint8_t* scales, int64_t groups, float* x) {
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= groups) return;
+  const float sv = e4m3_value(scales[g]);
+  for (int e = 0; e < 8; ++e) {
+    const uint8_t byte = codes[g * 8 + e];
+    x[g * 16 + 2 * e] = sv * e2m1_value(byte & 15u);
+    x[g * 16 + 2 * e + 1] = sv * e2m1_value(byte >> 4);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
+  if (a.mode == POLESTAR_CLUSTER_ENTRY) {
+    double* s64 = a.z64 + (int64_t)a.batch * a.K * a.d;   // scratch row per sequence after the centroids
+    hipLaunchKernelGGL(kmeans_entry_kernel<T>, dim3(a.batch), dim3(1024), 0, s, a, s64);
+  } else {
+    hipLaunchKernelGGL(window_update_kernel<T>, dim3(a.K, a.batch), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prep_qkv(const PrepArgs& a, hipStream_t s) {
+  const int rows = a.refresh ? a.block + a.n_win + a.K : a.block;
+  hipLaunchKernelGGL(prep_qkv_kernel<T>, dim3(rows, a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_pack(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s) {
+  const int64_t groups = rows * (d / 16);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(nvfp4_pack_kernel, dim3((unsigned)PS_CEIL_DIV(groups, 256)), dim3(256), 0, s, x, groups, d,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                               hipStream_t s) {
+  const int64_t groups = rows * (d / 16);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(nvfp4_unpack_kernel, dim3((unsigned)PS_CEIL_DIV(groups, 256)), dim3(256), 0, s, codes, scales,
+                     groups, x);
+  return hipGetLastError();
+}
+
+template hipError_t launch_cluster<float>(const ClusterArgs&, hipStream_t);
+template hipError_t launch_cluster<bf16_t>(const ClusterArgs&, hipStream_t);
+template hipError_t launch_prep_qkv<float>(const PrepArgs&, hipStream_t);
+template hipError_t launch_prep_qkv<bf16_t>(const PrepArgs&, hipStream_t);

@@ -1,0 +1,186 @@
+// Shared device/host helpers of the Polestar refresh kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/polestar.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+#define PS_DEV __device__ __forceinline__
+#define PS_HD __host__ __device__ __forceinline__
+
+// ---- storage dtype helpers ------------------------------------------------
+// bfloat16 is carried as raw uint16 bit patterns.
+struct bf16_t {
+  uint16_t bits;
+};
+
+PS_HD float bf16_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = ((uint32_t)b) << 16;
+  return v.f;
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (finite inputs).
+PS_HD uint16_t f32_to_bf16(float f) {
+  union { uint32_t u; float f; } v;
+  v.f = f;
+  uint32_t u = v.u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// float64 -> bfloat16 rounded once (to 8 significant bits, ties to even), for
+// values in the normal float range.
+PS_HD uint16_t f64_to_bf16(double x) {
+  union { uint64_t u; double d; } v;
+  v.d = x;
+  uint64_t u = v.u;
+  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
+  u &= ~0x00001FFFFFFFFFFFull;
+  v.u = u;
+  const float f = (float)v.d;           // exact: at most 8 significant bits
+  union { uint32_t u; float f; } w;
+  w.f = f;
+  return (uint16_t)(w.u >> 16);
+}
+
+template <typename T> struct St;
+template <> struct St<float> {
+  static PS_DEV float load(const float* p, int64_t i) { return p[i]; }
+  static PS_DEV void store(float* p, int64_t i, float v) { p[i] = v; }
+  static PS_DEV float round(float v) { return v; }
+  static PS_DEV void store_d(float* p, int64_t i, double v) { p[i] = (float)v; }
+};
+template <> struct St<bf16_t> {
+  static PS_DEV float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
+  static PS_DEV void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+  static PS_DEV float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  static PS_DEV void store_d(bf16_t* p, int64_t i, double v) { p[i].bits = f64_to_bf16(v); }
+};
+
+// ---- reductions -------------------------------------------------------------
+template <typename V>
+PS_DEV V wave_sum(V v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+PS_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum with a fixed combination order (deterministic).  `red` must
+// hold one slot per wave.  All threads get the result.
+template <typename V>
+PS_DEV V block_sum(V v, V* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  V s = 0;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+
+// ---- window geometry -------------------------------------------------------
+// Window row w -> sequence position: first the prefix rows, then the suffix rows.
+struct WinGeom {
+  int32_t blk_start, block, n_pre, n_win;   // n_pre prefix rows, n_win total
+  PS_HD int32_t pos(int32_t w) const {
+    return w < n_pre ? blk_start - n_pre + w : blk_start + block + (w - n_pre);
+  }
+};
+
+PS_HD WinGeom make_geom(int32_t blk_start, int32_t n_pos, int32_t block, int32_t pre, int32_t suf) {
+  WinGeom g;
+  g.blk_start = blk_start;
+  g.block = block;
+  int32_t p0 = blk_start - pre;
+  if (p0 < 0) p0 = 0;
+  g.n_pre = blk_start - p0;
+  int32_t s1 = blk_start + block + suf;
+  if (s1 > n_pos) s1 = n_pos;
+  int32_t n_suf = s1 - (blk_start + block);
+  if (n_suf < 0) n_suf = 0;
+  g.n_win = g.n_pre + n_suf;
+  return g;
+}
+
+// ---- NVFP4 (E2M1 values, E4M3FN scale per 16) -------------------------------
+PS_HD float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  float v = (m == 0) ? 0.f : (m == 1) ? 0.5f : (m == 2) ? 1.f : (m == 3) ? 1.5f
+          : (m == 4) ? 2.f : (m == 5) ? 3.f : (m == 6) ? 4.f : 6.f;
+  return (c & 8u) ? -v : v;
+}
+
+PS_HD float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;   // m * 2^-9
+  } else {
+    union { uint32_t u; float f; } v;
+    v.u = ((e - 7u + 127u) << 23) | (m << 20);
+    mag = v.f;
+  }
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Non-negative finite float -> E4M3FN byte, round to nearest even, saturate at 448.
+PS_HD uint32_t e4m3_encode(float s) {
+  if (!(s > 0.f)) return 0u;
+  if (s >= 448.f) return 0x7Eu;
+  if (s < 0.015625f) {                      // below 2^-6: subnormal grid step 2^-9
+    float q = rintf(s * 512.f);             // exact scaling, then round half even
+    return (uint32_t)q;                     // q == 8 encodes 2^-6 (e=1, m=0)
+  }
+  union { uint32_t u; float f; } v;
+  v.f = s;
+  int32_t ex = (int32_t)((v.u >> 23) & 0xFFu) - 127;
+  uint32_t man = v.u & 0x7FFFFFu;
+  uint32_t m3 = man >> 20, rem = man & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+  if (m3 == 8u) { m3 = 0u; ++ex; }
+  uint32_t code = ((uint32_t)(ex + 7) << 3) | m3;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// float -> E2M1 nibble, round to nearest with ties to the even code, saturate at 6.
+PS_HD uint32_t e2m1_encode(float y) {
+  float a = fabsf(y);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.f) c = 6;
+  else c = 7;
+  if (y < 0.f && c != 0) c |= 8u;
+  return c;
+}
+
+// Quantise one group of 16 float32 values.  Returns the scale byte; codes[i] nibbles.
+PS_HD uint32_t nvfp4_group(const float* r, uint32_t* codes) {
+  float amax = 0.f;
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(r[i]));
+  const float s = amax / 6.f;               // correctly rounded float32 division
+  const uint32_t sc = e4m3_encode(s);
+  const float sv = e4m3_value(sc);
+  for (int i = 0; i < 16; ++i) codes[i] = (sv == 0.f) ? 0u : e2m1_encode(r[i] / sv);
+  return sc;
+}
+
+// ---- misc -------------------------------------------------------------------
+#define PS_CEIL_DIV(a, b) (((a) + (b) - 1) / (b))
+
+inline size_t ps_align256(size_t x) { return (x + 255) & ~(size_t)255; }

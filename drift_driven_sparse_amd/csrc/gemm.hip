@@ -1,0 +1,399 @@
+// Projection kernels for the gathered rows of a refresh step.
+//
+// The rows the method needs per layer and sequence are few (active block,
+// window rows, centroids: <= 144) while the weights are large, so every
+// projection here is a skinny GEMM that streams the weight once from HBM.
+//
+// bf16 path: weights are repacked once into MFMA 16x16x32 B-operand fragments
+// stored in lane order, so every wave load is one contiguous 1 KiB from HBM.
+// A workgroup (4 waves) owns 64 output columns (4 fragments) of one sequence
+// and a range of K; its waves split that range and stream their A rows
+// (activations, L2-resident) straight into registers.  Wave partial sums are
+// combined in LDS in a fixed order, then a fused epilogue writes the result.
+// N = d projections use a split-K grid whose partial sums are reduced (in a
+// fixed order) by a row kernel that also adds the residual.
+//
+// float32 path (small models): the same grid and epilogues with a plain FMA
+// inner product.
+#include "kernels.h"
+
+namespace {
+
+constexpr int kNT = 64;          // output columns per workgroup
+constexpr int kLDT = kNT + 4;    // LDS tile row stride (floats)
+
+PS_HD int64_t gu_src_row(int64_t p, int ffn) {
+  const int64_t sub = p >> 4, i = sub >> 1;
+  return (sub & 1) * (int64_t)ffn + i * 16 + (p & 15);
+}
+
+// ---- weight packing -----------------------------------------------------------------
+// bf16: dst[((n16*(K/32) + k32)*64 + lane)*8 + e] = W'[n16*16 + lane%16][k32*32 + (lane/16)*8 + e]
+// f32:  dst[n][k] = W'[n][k]
+// W' = W with rows permuted for the gate/up weight (gate and up 16-row groups interleaved).
+__global__ void pack_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K,
+                                 int is_gu, int ffn) {
+  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // one 8-element chunk
+  const int64_t k32n = K >> 5;
+  const int64_t total = (int64_t)N * K / 8;
+  if (c >= total) return;
+  const int lane = (int)(c & 63);
+  const int64_t blk = c >> 6;
+  const int64_t n16 = blk / k32n, k32 = blk % k32n;
+  const int64_t n = n16 * 16 + (lane & 15);
+  const int64_t k = k32 * 32 + (lane >> 4) * 8;
+  const int64_t row = is_gu ? gu_src_row(n, ffn) : n;
+  *(uint4*)(dst + c * 8) = *(const uint4*)(src + row * K + k);
+}
+
+__global__ void pack_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int N, int K, int is_gu,
+                                int ffn) {
+  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // one element
+  if (c >= (int64_t)N * K) return;
+  const int64_t n = c / K, k = c % K;
+  const int64_t row = is_gu ? gu_src_row(n, ffn) : n;
+  dst[c] = src[row * K + k];
+}
+
+// ---- epilogues ------------------------------------------------------------------------
+template <typename T, int KIND>
+PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, int n0, int nt,
+                     const float* tile) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  if constexpr (KIND == EPI_PARTIAL) {
+    float* out = g.part + (((int64_t)blockIdx.z * g.batch + b) * g.part_rows) * g.N;
+    for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
+      const int r = idx / kNT, c = idx % kNT, n = n0 + c;
+      if (n < g.N) out[(int64_t)r * g.N + n] = tile[r * kLDT + c];
+    }
+  } else if constexpr (KIND == EPI_QKV) {
+    for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
+      const int r = idx / kNT, c = idx % kNT, n = n0 + c;
+      if (n >= g.N) continue;
+      const float v = tile[r * kLDT + c] * e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
+      if (n < e.nq) {
+        e.q[((int64_t)b * e.q_rows + r) * e.nq + n] = v;
+      } else {
+        const int kv = n - e.nq;
+        const int which = kv >= e.nkv;
+        const int col = kv - which * e.nkv;
+        int pos = -1;
+        if (r < e.block) {
+          pos = e.geom.blk_start + r;
+        } else {
+          const int w = r - e.block;
+          if (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) pos = e.geom.pos(w);
+        }
+        if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), ((int64_t)b * e.n_pos + pos) * e.nkv + col, v);
+      }
+    }
+  } else if constexpr (KIND == EPI_SWIGLU) {
+    // tile columns: [gate 16 | up 16] x 2 pairs -> 32 output columns starting at n0/2
+    for (int idx = tid; idx < rows_b * (kNT / 2); idx += nthr) {
+      const int r = idx / (kNT / 2), j = idx % (kNT / 2);
+      const int p = j >> 4, jj = j & 15;
+      const int oc = (n0 >> 1) + j;
+      if (oc >= e.ffn) continue;
+      const float s = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      const float gv = tile[r * kLDT + (2 * p) * 16 + jj] * s;
+      const float uv = tile[r * kLDT + (2 * p + 1) * 16 + jj] * s;
+      const float a = gv / (1.f + expf(-gv)) * uv;
+      ((float*)e.act)[((int64_t)b * e.act_rows + r) * e.ffn + oc] = a;
+    }
+  } else if constexpr (KIND == EPI_KV) {
+    for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
+      const int r = idx / kNT, c = idx % kNT, n = n0 + c;
+      if (n >= g.N) continue;
+      const float v = tile[r * kLDT + c] * e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
+      const int which = n >= e.nkv;
+      const int col = n - which * e.nkv;
+      const int w = e.sel_idx[(int64_t)b * e.win_max + r];
+      if (w < 0 || w >= e.geom.n_win) continue;
+      const int pos = e.geom.pos(w);
+      St<T>::store((T*)(which ? e.vc : e.kc), ((int64_t)b * e.n_pos + pos) * e.nkv + col, v);
+    }
+  } else if constexpr (KIND == EPI_LMSTAT) {
+    // Per row, over this tile's vocabulary ids: max logit, sum exp(logit - max), and the
+    // largest logit among ids != mask_id with its id (lowest id on ties).
+    const int lane = tid & 63, wave = tid >> 6, nwave = nthr >> 6;
+    for (int r = wave; r < rows_b; r += nwave) {
+      const int n = n0 + lane;
+      const bool valid = n < e.vocab;
+      const float s = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      const float l = valid ? tile[r * kLDT + lane] * s : -INFINITY;
+      const float m = wave_max(l);
+      const float se = wave_sum(valid ? expf(l - m) : 0.f);
+      const float lb = (valid && n != e.mask_id) ? l : -INFINITY;
+      const float bm = wave_max(lb);
+      const unsigned long long hit = __ballot(lb == bm && bm > -INFINITY);
+      const int bid = hit ? n0 + __ffsll((long long)hit) - 1 : -1;
+      if (lane == 0) {
+        float* st = e.lm_stats + (((int64_t)b * e.lm_rows + r) * e.lm_tiles + nt) * 4;
+        st[0] = m;
+        st[1] = se;
+        st[2] = bm;
+        st[3] = __int_as_float(bid);
+      }
+    }
+  }
+}
+
+// ---- bf16 MFMA main loop -----------------------------------------------------------------
+// bf16 x bf16 -> f32 MFMA of one 16x16 tile step
+PS_DEV floatx4_t mfma(uint4 a, uint4 w, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, w), c,
+                                                 0, 0, 0);
+}
+
+// Split 8 float32 values into bf16 hi (round to nearest) and lo = bf16(x - hi):
+// hi + lo reproduces x to 2^-18 relative.
+PS_DEV void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
+  const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = f32_to_bf16(xs[2 * i]), h1 = f32_to_bf16(xs[2 * i + 1]);
+    const uint16_t l0 = f32_to_bf16(xs[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(xs[2 * i + 1] - bf16_to_f32(h1));
+    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <typename T, int RT, int KIND, int AF32>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e) {
+  constexpr int NSUB = kNT / 16;
+  __shared__ float tile[RT * 16 * kLDT];
+  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  int rows_b = g.A.rows(b);
+  if (rows_b > RT * 16) rows_b = RT * 16;
+  if (rows_b <= 0) return;
+  const int nrt = (rows_b + 15) >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ksteps = g.K >> 7;
+  const int s0 = (int)((int64_t)ksteps * sp / g.ksplit), s1 = (int)((int64_t)ksteps * (sp + 1) / g.ksplit);
+  const int w0 = s0 + (s1 - s0) * wave / 4, w1 = s0 + (s1 - s0) * (wave + 1) / 4;
+
+  typedef typename std::conditional<AF32 != 0, float, uint16_t>::type AE;
+  const AE* Ab = (const AE*)g.A.base + (int64_t)b * g.A.bstride;
+  const AE* arow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int r = rt * 16 + (lane & 15);
+    if (r >= rows_b) r = 0;
+    arow[rt] = Ab + g.A.src_row(b, r) * g.A.lda + 8 * (lane >> 4);
+  }
+  const int64_t k32n = g.K >> 5;
+  const int n16_total = g.N >> 4;
+  // per-subtile fragment stream; subtiles past N re-read the first one (their columns are never stored)
+  const uint4* Wsub[NSUB];
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    int n16 = nt * NSUB + sb;
+    if (n16 >= n16_total) n16 = nt * NSUB;
+    Wsub[sb] = (const uint4*)g.W + ((int64_t)n16 * k32n) * 64 + lane;
+  }
+
+  floatx4_t acc[RT][NSUB];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks = w0; ks < w1; ++ks) {
+    uint4 wf[NSUB][4];
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[sb][j] = Wsub[sb][((int64_t)ks * 4 + j) * 64];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (rt < nrt) {
+        if constexpr (AF32 != 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4* ap = (const float4*)(arow[rt] + ks * 128 + 32 * j);
+            uint4 hi, lo;
+            split8(ap[0], ap[1], hi, lo);
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) {
+              acc[rt][sb] = mfma(hi, wf[sb][j], acc[rt][sb]);
+              acc[rt][sb] = mfma(lo, wf[sb][j], acc[rt][sb]);
+            }
+          }
+        } else {
+          uint4 af[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = *(const uint4*)(arow[rt] + ks * 128 + 32 * j);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(af[j], wf[sb][j], acc[rt][sb]);
+        }
+      }
+    }
+  }
+  // Combine the four waves' partial sums in LDS, wave 0 first.
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt < nrt) {
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float* t = &tile[(rt * 16 + 4 * (lane >> 4) + i) * kLDT + sb * 16 + (lane & 15)];
+              *t = (w == 0 ? 0.f : *t) + acc[rt][sb][i];
+            }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  epilogue<T, KIND>(g, e, b, rows_b, nt * kNT, nt, tile);
+}
+
+// ---- float32 main loop ----------------------------------------------------------------------
+template <int RT, int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) {
+  __shared__ float tile[RT * 16 * kLDT];
+  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  int rows_b = g.A.rows(b);
+  if (rows_b > RT * 16) rows_b = RT * 16;
+  if (rows_b <= 0) return;
+  const int kc = g.K >> 2;
+  const int c0 = (int)((int64_t)kc * sp / g.ksplit), c1 = (int)((int64_t)kc * (sp + 1) / g.ksplit);
+  const float* Ab = (const float*)g.A.base + (int64_t)b * g.A.bstride;
+  const float* W = (const float*)g.W;
+  const int n0 = nt * kNT;
+  for (int idx = threadIdx.x; idx < rows_b * kNT; idx += blockDim.x) {
+    const int r = idx / kNT, c = idx % kNT, n = n0 + c;
+    float acc = 0.f;
+    if (n < g.N) {
+      const float4* a4 = (const float4*)(Ab + g.A.src_row(b, r) * g.A.lda);
+      const float4* w4 = (const float4*)(W + (int64_t)n * g.K);
+      for (int k = c0; k < c1; ++k) {
+        const float4 x = a4[k], y = w4[k];
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+      }
+    }
+    tile[r * kLDT + c] = acc;
+  }
+  __syncthreads();
+  epilogue<float, KIND>(g, e, b, rows_b, n0, nt, tile);
+}
+
+template <typename T, int RT, int KIND>
+hipError_t launch_one(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
+  dim3 grid(PS_CEIL_DIV(g.N, kNT), g.batch, g.ksplit);
+  if constexpr (std::is_same<T, float>::value) {
+    hipLaunchKernelGGL((gemm_f32_kernel<RT, KIND>), grid, dim3(256), 0, s, g, e);
+  } else {
+    if (g.A.f32) hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND, 1>), grid, dim3(256), 0, s, g, e);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND, 0>), grid, dim3(256), 0, s, g, e);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int RT>
+hipError_t dispatch_kind(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
+  switch (e.kind) {
+    case EPI_PARTIAL: return launch_one<T, RT, EPI_PARTIAL>(g, e, s);
+    case EPI_QKV: return launch_one<T, RT, EPI_QKV>(g, e, s);
+    case EPI_SWIGLU: return launch_one<T, RT, EPI_SWIGLU>(g, e, s);
+    case EPI_KV: return launch_one<T, RT, EPI_KV>(g, e, s);
+    case EPI_LMSTAT: return launch_one<T, RT, EPI_LMSTAT>(g, e, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---- split-K row reduction ------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, b = blockIdx.y;
+  int rows_b = a.block + (a.count ? a.count[b] : 0);
+  if (rows_b > (int)gridDim.x) rows_b = gridDim.x;
+  if (r >= rows_b) return;
+  const T* res = nullptr;
+  const float* res32 = nullptr;
+  if (r < a.res_split) {
+    if (a.res_a_f32) res32 = (const float*)a.res_a + (int64_t)b * a.res_a_bstride + (int64_t)r * a.d;
+    else res = (const T*)a.res_a + (int64_t)b * a.res_a_bstride + (int64_t)r * a.d;
+  } else {
+    int src = a.sel_idx[(int64_t)b * a.win_max + r - a.res_split];
+    src = (src < 0 || src >= a.win_max) ? 0 : src;
+    res = (const T*)a.res_b + (int64_t)b * a.res_b_bstride + (int64_t)src * a.d;
+  }
+  const int64_t ooff = (r < a.out_split) ? (int64_t)b * a.out_a_bstride + (int64_t)r * a.d
+                                         : (int64_t)b * a.out_b_bstride + (int64_t)(r - a.out_split) * a.d;
+  void* obase = (r < a.out_split) ? a.out_a : a.out_b;
+  const int64_t pstride = (int64_t)a.batch * a.part_rows * a.d;
+  const float* p = a.part + ((int64_t)b * a.part_rows + r) * a.d;
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < a.d; n += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < a.ksplit; ++s) v += p[s * pstride + n];
+    v += res32 ? res32[n] : St<T>::load(res, n);
+    if (a.chk) a.chk[((int64_t)b * a.chk_rows + r) * a.d + n] = v;
+    float q;
+    if (a.out_f32) {
+      q = v;
+      ((float*)obase)[ooff + n] = v;
+    } else {
+      q = St<T>::round(v);
+      St<T>::store((T*)obase, ooff + n, v);
+    }
+    ss += q * q;
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0 && a.inv_rms) a.inv_rms[(int64_t)b * a.inv_bstride + r] = 1.f / sqrtf(ss / (float)a.d + a.eps);
+}
+
+}  // namespace
+
+size_t packed_elems(int N, int K) { return (size_t)N * (size_t)K; }
+
+template <typename T>
+hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s) {
+  const int is_gu = kind == POLESTAR_W_GU;
+  if constexpr (std::is_same<T, float>::value) {
+    const int64_t total = (int64_t)N * K;
+    hipLaunchKernelGGL(pack_f32_kernel, dim3((unsigned)PS_CEIL_DIV(total, 256)), dim3(256), 0, s,
+                       (const float*)src, (float*)dst, N, K, is_gu, ffn);
+  } else {
+    const int64_t total = (int64_t)N * K / 8;
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)PS_CEIL_DIV(total, 256)), dim3(256), 0, s,
+                       (const uint16_t*)src, (uint16_t*)dst, N, K, is_gu, ffn);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s) {
+  if (max_rows <= 32) return dispatch_kind<T, 2>(g, e, s);
+  if (max_rows <= 64) return dispatch_kind<T, 4>(g, e, s);
+  if (max_rows <= 144) return dispatch_kind<T, 9>(g, e, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_pack<float>(int, const void*, void*, int, int, int, hipStream_t);
+template hipError_t launch_pack<bf16_t>(int, const void*, void*, int, int, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmArgs&, const EpiParams&, int, hipStream_t);
+template hipError_t launch_gemm<bf16_t>(const GemmArgs&, const EpiParams&, int, hipStream_t);
+template hipError_t launch_row_reduce<float>(const RowReduceArgs&, int, hipStream_t);
+template hipError_t launch_row_reduce<bf16_t>(const RowReduceArgs&, int, hipStream_t);

@@ -1,0 +1,192 @@
+// Launch interfaces between the C ABI layer and the HIP kernels.
+#pragma once
+#include "common.h"
+
+// Handle contents (host only).
+struct WsLayout {
+  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, part, hp, inv_hp, act, inv_out, xhat, z64,
+      lm_a, lm_inv, lm_stats, lm_meta, total;
+};
+
+struct polestar_handle {
+  polestar_dims dm;
+  polestar_params pr;
+  int32_t win_max;   // win_prefix + win_suffix
+  int32_t mq;        // QKV rows per sequence: B + win_max + K
+  int32_t mt;        // token rows per sequence: B + win_max
+  int32_t nq, nkv;   // Hq*dh, Hkv*dh
+  int32_t ksplit;    // split-K factor of the N = d projections
+  int32_t lm_tiles;  // vocab / 64 rounded up
+  WsLayout ws;
+  polestar_check chk;
+};
+
+// ---- GEMM ---------------------------------------------------------------------
+// A operand: rows of M-block b (one sequence).  Row r reads source row
+//   r                                  when rowmap == nullptr or r < map_from
+//   map_off + rowmap[b*map_bstride + r - map_from]   otherwise.
+struct GemmA {
+  const void* base;
+  int32_t f32;           // rows are float32 (bf16 path: fed to MFMA as a hi + lo bf16 pair)
+  int64_t bstride;       // elements between sequences
+  int32_t lda;           // elements between rows
+  const int32_t* rowmap;
+  int32_t map_bstride, map_from, map_off;
+  const int32_t* rows_dev;   // rows of block b = min(rows_dev[b] + rows_add, rows_max), or rows_static
+  int32_t rows_add, rows_static, rows_max;
+  PS_DEV int rows(int b) const {
+    if (!rows_dev) return rows_static;
+    int r = rows_dev[b] + rows_add;
+    r = r < rows_add ? rows_add : r;
+    return r > rows_max ? rows_max : r;
+  }
+  PS_DEV int64_t src_row(int b, int r) const {
+    if (rowmap != nullptr && r >= map_from) {
+      int m = rowmap[b * map_bstride + r - map_from];
+      m = (m < 0 || m >= map_bstride) ? 0 : m;
+      return (int64_t)map_off + m;
+    }
+    return r;
+  }
+};
+
+struct GemmArgs {
+  GemmA A;
+  const void* W;       // packed weight
+  int32_t N, K;
+  int32_t batch;
+  int32_t ksplit;
+  float* part;         // when set: raw sums to part[((s*batch + b)*part_rows + r)*N + n]
+  int32_t part_rows;
+};
+
+enum EpiKind { EPI_PARTIAL = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_KV = 3, EPI_LMSTAT = 4 };
+
+struct EpiParams {
+  int kind;
+  // row scale (RMSNorm as an output scale): inv_rms[b*inv_bstride + inv_off + r]
+  const float* inv_rms;
+  int32_t inv_bstride, inv_off;
+  // QKV
+  float* q; int32_t q_rows;     // q[(b*q_rows + r)*nq + n]
+  void* kc; void* vc;           // caches (storage dtype)
+  const int32_t* flags;         // patched flags [batch][win_max]
+  int32_t nq, nkv, block, win_max, n_pos;
+  WinGeom geom;
+  float* chk; int32_t chk_rows, chk_ld;   // chk[(b*chk_rows + r)*chk_ld + n]
+  // SwiGLU
+  void* act; int32_t act_rows, ffn;
+  // KV scatter of packet rows: dest pos = geom.pos(sel_idx[b*win_max + r])
+  const int32_t* sel_idx;
+  // LM statistics
+  float* lm_stats; int32_t lm_rows, lm_tiles, vocab, mask_id;
+};
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s);
+template <typename T>
+hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s);
+size_t packed_elems(int N, int K);
+
+// Row reductions after split-K projections: out = round(sum of partials + residual),
+// one row per workgroup, plus 1/rms of the stored row (RMSNorm of the next projection).
+struct RowReduceArgs {
+  const float* part; int32_t ksplit, part_rows, batch, d;
+  const int32_t* count;   // rows of seq b = block + count[b]
+  int32_t block, win_max;
+  // residual row r: r < res_split -> res_a[b][r]; else res_b[b][sel_idx[b*win_max + r - res_split]]
+  const void* res_a; int64_t res_a_bstride; int32_t res_split;
+  int32_t res_a_f32;            // res_a holds float32 rows (else storage dtype)
+  const void* res_b; int64_t res_b_bstride;
+  const int32_t* sel_idx;
+  // output row r: r < out_split -> out_a[b][r]; else out_b[b][r - out_split]
+  void* out_a; int64_t out_a_bstride; int32_t out_split;
+  void* out_b; int64_t out_b_bstride;
+  int32_t out_f32;              // outputs are float32 rows (else storage dtype)
+  float* inv_rms; int32_t inv_bstride;
+  float eps;
+  float* chk; int32_t chk_rows;
+};
+template <typename T>
+hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s);
+
+// ---- window / clustering ----------------------------------------------------------
+struct ClusterArgs {
+  int mode;
+  int32_t batch, d, K, win_max, block, n_pos, iters;
+  WinGeom geom;
+  void* win_h; uint8_t* codes; uint8_t* scales; void* win_z; int32_t* win_m;
+  const void* entry_h;
+  const int32_t* init_idx;
+  double* objective;
+  const void* u_rows; const int32_t* u_idx; const int32_t* u_count;
+  void* ws_rows;            // patched window rows [batch][win_max][d] (storage dtype)
+  int32_t* flags;           // [batch][win_max]
+  double* xhat; double* z64;
+  int nvfp4;
+};
+template <typename T>
+hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
+
+// Active rows, window rows and centroids -> contiguous QKV A rows + 1/rms.
+struct PrepArgs {
+  int32_t batch, d, block, win_max, n_win, K, mq, refresh;
+  const void* h_act; const void* ws_rows; const void* win_z;
+  void* a_qkv; float* inv; float eps;
+};
+template <typename T>
+hipError_t launch_prep_qkv(const PrepArgs& a, hipStream_t s);
+
+// ---- attention / drift ------------------------------------------------------------
+struct AttnArgs {
+  int32_t batch, n_pos, hq, hkv, dh, mq, mt;
+  int32_t n_tok;          // token query rows per sequence (block + n_win, or block)
+  int32_t n_proxy;        // centroid query rows (K or 0)
+  int32_t block;
+  const float* q;         // [batch][mq][hq*dh]
+  const void* kc; const void* vc;
+  void* o;                // [batch][mt][hq*dh] float32
+  float* proxy_logits;    // [batch][K][hq][n]
+  float* kl;              // [batch][K][hq]
+  float* act_logits;      // [batch][block][hq][n] or null
+  int32_t act_kl;         // compute active-row KL against act_logits before overwrite
+  float* akl;             // [batch][block][hq]
+  float* chk; int32_t chk_rows;
+};
+template <typename T>
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  int32_t batch, K, k, hq, block, win_max, n_win;
+  const float* kl; const int32_t* win_m;
+  float* D; int32_t* topk; int32_t* sel_idx; int32_t* sel_count;
+  const float* akl; float* delta;
+  int32_t refresh;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// ---- commit ---------------------------------------------------------------------
+struct LmPrepArgs {
+  int32_t batch, d, block, win_max, win_suffix, n_pre, lm_rows;
+  const void* h_final; const void* u_rows; const int32_t* u_idx; const int32_t* u_count;
+  void* a_lm; float* inv; int32_t* meta; float eps;   // meta[b*? ]: [n_rows, suffix start in packet]
+};
+template <typename T>
+hipError_t launch_lm_prep(const LmPrepArgs& a, hipStream_t s);
+
+struct DecideArgs {
+  int32_t batch, block, win_suffix, win_max, n_pre, lm_rows, lm_tiles, hist, mask_id;
+  float tau_s, tau_suf, alpha;
+  const float* lm_stats; const int32_t* meta; const int32_t* u_idx;
+  const float* delta; const uint8_t* active_masked; const uint8_t* suffix_masked;
+  float* hist_vals; int32_t* hist_cnt;
+  uint8_t* commit_active; uint8_t* commit_suffix; float* conf_active; int32_t* yhat_active;
+  float* spike; float* conf_suffix;
+};
+hipError_t launch_decide(const DecideArgs& a, hipStream_t s);
+
+// ---- NVFP4 test hooks -------------------------------------------------------------
+hipError_t launch_nvfp4_pack(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s);
+hipError_t launch_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                               hipStream_t s);

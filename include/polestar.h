@@ -1,0 +1,284 @@
+/*
+ * polestar.h — C ABI of the drift-scored sparse KV refresh for masked-diffusion
+ * LLMs (Polestar-Cache) and its drift-aware commit rule (Polestar-Commit),
+ * implemented as HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "Polestar: Drift-Aware Cache Calibration and Token
+ * Commitment for Efficient Inference of Diffusion LLMs" (arXiv 2607.14107);
+ * each call below names the section, equation, table or Algorithm 1 step
+ * group it implements.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers: every tensor pointer is a DEVICE pointer unless documented as
+ *   host.  The caller allocates and owns all memory (weights, caches, window
+ *   state, packets, outputs and the workspace); the library never allocates
+ *   device memory and keeps only host-side dimensions in the handle.
+ * Storage dtype: dims.dtype selects float32 (POLESTAR_F32) or bfloat16
+ *   (POLESTAR_BF16, stored as raw uint16 bit patterns) for weights, KV caches,
+ *   hidden rows and centroids.  Drift logits, drift values, confidences and
+ *   spikes are always float32.
+ * Layouts (row-major, batch outermost):
+ *   hidden rows          [batch, rows, d]
+ *   KV cache (per layer) [batch, n_pos, n_kv_heads, head_dim]
+ *   window rows          [batch, win_max, d], win_max = win_prefix + win_suffix;
+ *                        window row w is the w-th position, ascending, of
+ *                        [blk_start - win_prefix, blk_start) U
+ *                        [blk_start + block, blk_start + block + win_suffix),
+ *                        clipped to [0, n_pos); n_win <= win_max rows are used.
+ *   NVFP4 window codes   [batch, win_max, d/2] u8 (element 2j low nibble,
+ *                        2j+1 high nibble), scales [batch, win_max, d/16] u8
+ *                        (OCP E4M3FN bytes)
+ *   centroids            [batch, n_clusters, d]; labels [batch, win_max] i32
+ *   proxy logits         [batch, n_clusters, n_heads, n_pos] f32
+ *   active-block logits  [batch, block, n_heads, n_pos] f32
+ *   packed weights       produced by polestar_pack_weight (opaque layout)
+ * Streams: every call enqueues asynchronously on the given hipStream_t
+ *   (passed as void*; NULL = the null stream) and never synchronises.
+ *   Outputs are valid once the caller synchronises that stream.  A handle is
+ *   used by one stream at a time.
+ * Workspace: calls take a caller-allocated device workspace of at least
+ *   polestar_workspace_size() bytes (256-byte aligned).  The calls for one
+ *   layer of one refresh step must run in the order cluster -> drift ->
+ *   refresh on the same workspace: cluster leaves the patched window rows in
+ *   it, drift leaves the attention outputs in it.
+ * Errors: every int-returning call returns POLESTAR_OK (0) or a negative
+ *   code.  Arguments are validated on the host before anything is enqueued,
+ *   so a failed call has launched nothing.  POLESTAR_E_HIP reports a launch
+ *   error (hipGetLastError); faults inside kernels surface at the caller's
+ *   synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef POLESTAR_H
+#define POLESTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  POLESTAR_OK = 0,
+  POLESTAR_E_NULL = -1,        /* required pointer is NULL */
+  POLESTAR_E_SHAPE = -2,       /* inconsistent or out-of-range dimension */
+  POLESTAR_E_DTYPE = -3,       /* unknown dtype / residual format */
+  POLESTAR_E_UNSUPPORTED = -4, /* valid but not implemented (K > 16, k > K, ...) */
+  POLESTAR_E_WORKSPACE = -5,   /* workspace smaller than polestar_workspace_size */
+  POLESTAR_E_ALIGN = -6,       /* device pointer not 16-byte aligned */
+  POLESTAR_E_HIP = -7,         /* HIP runtime error while enqueueing */
+  POLESTAR_E_ARG = -8          /* invalid mode or scalar argument */
+};
+
+enum { POLESTAR_F32 = 0, POLESTAR_BF16 = 1 };
+enum { POLESTAR_RESID_RAW = 0, POLESTAR_RESID_NVFP4 = 1 };
+enum { POLESTAR_CLUSTER_ENTRY = 0, POLESTAR_CLUSTER_UPDATE = 1 };
+enum { POLESTAR_DRIFT_REFRESH = 0, POLESTAR_DRIFT_ACTIVE_ONLY = 1 };
+enum {
+  POLESTAR_W_QKV = 0,  /* src [(n_heads + 2 n_kv_heads) head_dim, d] = rows of W_Q, W_K, W_V */
+  POLESTAR_W_O = 1,    /* src [d, n_heads head_dim] */
+  POLESTAR_W_GU = 2,   /* src [2 ffn, d] = rows of W_gate then W_up */
+  POLESTAR_W_DOWN = 3, /* src [d, ffn] */
+  POLESTAR_W_KV = 4,   /* src [2 n_kv_heads head_dim, d] = rows of W_K then W_V */
+  POLESTAR_W_LM = 5    /* src [vocab, d] */
+};
+
+/* Model and method dimensions (host struct, copied into the handle). */
+typedef struct polestar_dims {
+  int32_t d;          /* hidden size */
+  int32_t n_heads;    /* query heads */
+  int32_t n_kv_heads; /* key/value heads; n_heads % n_kv_heads == 0 */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t ffn;        /* SwiGLU width */
+  int32_t n_pos;      /* positions per sequence (prompt + generation) */
+  int32_t batch;      /* independent sequences processed together */
+  int32_t block;      /* active block size B (<= 64) */
+  int32_t win_prefix; /* |Omega_p| */
+  int32_t win_suffix; /* |Omega_s| */
+  int32_t n_clusters; /* K (1..16) */
+  int32_t top_k;      /* k (1..K) */
+  int32_t vocab;      /* LM-head rows, 0 when polestar_commit is not used */
+  int32_t dtype;      /* POLESTAR_F32 | POLESTAR_BF16 */
+  int32_t resid_fmt;  /* POLESTAR_RESID_RAW | POLESTAR_RESID_NVFP4 (bf16 only) */
+} polestar_dims;
+
+/* Scalar hyper-parameters [Polestar §5.1 and Table 5]. */
+typedef struct polestar_params {
+  float rms_eps;        /* RMSNorm epsilon (unit gain) */
+  float tau_s;          /* static confidence threshold (0.9) */
+  float tau_suf;        /* suffix commit confidence (0.9) */
+  float alpha;          /* drift-gate coefficient (10) */
+  int32_t hist;         /* drift history length h (5), 0..16 */
+  int32_t mask_id;      /* vocabulary id excluded from the confidence max */
+  int32_t kmeans_iters; /* Lloyd iterations at block entry (10) */
+} polestar_params;
+
+typedef struct polestar_handle polestar_handle;
+
+/* Per-layer device buffers.  Weights are packed (polestar_pack_weight). */
+typedef struct polestar_layer {
+  const void* w_qkv;    /* packed POLESTAR_W_QKV */
+  const void* w_o;      /* packed POLESTAR_W_O */
+  const void* w_gu;     /* packed POLESTAR_W_GU */
+  const void* w_down;   /* packed POLESTAR_W_DOWN */
+  void* k_cache;        /* [batch, n_pos, n_kv_heads, head_dim], in/out */
+  void* v_cache;        /* same */
+  void* win_h;          /* RAW: window rows [batch, win_max, d], in/out */
+  uint8_t* win_codes;   /* NVFP4: [batch, win_max, d/2], in/out */
+  uint8_t* win_scales;  /* NVFP4: [batch, win_max, d/16], in/out */
+  void* win_z;          /* centroids [batch, n_clusters, d], in/out */
+  int32_t* win_m;       /* cluster labels [batch, win_max], in/out */
+  float* proxy_logits;  /* previous proxy-attention logits [batch, K, n_heads, n_pos], in/out */
+} polestar_layer;
+
+/* Update packet U(t,l): rows of selected window positions.  Row r of
+ * sequence b holds window row idx[b*win_max + r]; count[b] rows are valid,
+ * ascending.  count lives on the device and is never read by the host. */
+typedef struct polestar_packet {
+  void* rows;      /* [batch, win_max, d] storage dtype */
+  int32_t* idx;    /* [batch, win_max] */
+  int32_t* count;  /* [batch] */
+} polestar_packet;
+
+/* Optional float32 side outputs of values before their storage rounding,
+ * for numerical checks.  Any pointer may be NULL.  Set with
+ * polestar_set_check; they stay in effect until replaced. */
+typedef struct polestar_check {
+  float* qkv;      /* [batch, B + win_max + K, (Hq + 2 Hkv) dh] projections of the QKV rows */
+  float* attn_out; /* [batch, B + win_max, Hq dh] attention outputs of token rows */
+  float* hp;       /* [batch, B + win_max, d] h' = h + o W_O^T rows [active; S] */
+  float* out;      /* [batch, B + win_max, d] layer outputs of rows [active; S] */
+  float* kv_next;  /* [batch, win_max, 2 Hkv dh] next-layer K/V of packet rows */
+} polestar_check;
+
+/* ---- handle ------------------------------------------------------------ */
+/* Validates dims/params (host only, no HIP call) and creates a handle.
+ * Returns E_NULL, E_SHAPE, E_DTYPE or E_UNSUPPORTED on bad input. */
+int polestar_create(const polestar_dims* dims, const polestar_params* params, polestar_handle** out);
+void polestar_destroy(polestar_handle* h);
+const char* polestar_strerror(int code);
+/* Bytes of device workspace every call needs. */
+int polestar_workspace_size(const polestar_handle* h, size_t* bytes);
+int polestar_set_check(polestar_handle* h, const polestar_check* chk /* NULL clears */);
+
+/* ---- weights ----------------------------------------------------------- */
+/* Bytes of a packed weight of the given kind. */
+int polestar_weight_packed_size(const polestar_handle* h, int which, size_t* bytes);
+/* Repack a weight from [out, in] row-major (storage dtype, device) into the
+ * layout the projection kernels stream (device, caller-allocated). */
+int polestar_pack_weight(const polestar_handle* h, int which, const void* src, void* dst, void* stream);
+
+/* ---- the four refresh-path calls ---------------------------------------- */
+/*
+ * polestar_cluster — window clustering [§4.1 "Cluster and Quantize Hidden
+ * States"; Algorithm 1: SphericalKMeans, ResidualQuantization at block entry,
+ * Dequantize, Patch, ResidualQuantization inside the layer loop].
+ *  ENTRY:  spherical k-means of the window rows entry_h ([batch, win_max, d],
+ *          storage dtype; may alias L->win_h) with min(K, n_win) initial
+ *          centroids at rows init_idx [batch, K] (i32, device), then
+ *          kmeans_iters Lloyd iterations (assign by largest cosine, lowest
+ *          index on ties; empty clusters keep their centroid).  Writes win_z,
+ *          win_m, and win_h (RAW) or the NVFP4 residual codes (h - z_M(i)).
+ *          objective (nullable, device f64 [batch, 2*kmeans_iters]) receives
+ *          the objective after every assignment and every update.
+ *  UPDATE: per refresh step.  Rebuilds the window rows (RAW: win_h; NVFP4:
+ *          z_M(i) + dequantised residual, stored as bf16), overwrites rows
+ *          named by the packet u_in (nullable = no packet), recomputes every
+ *          non-empty centroid from its members with the labels fixed (§4.1
+ *          incremental centroid update), and re-quantises (NVFP4).  The
+ *          patched rows stay in the workspace for polestar_drift/refresh.
+ */
+int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                     const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h,
+                     double* objective, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * polestar_drift — main attention of the active block and drift scoring
+ * [§2 Eq. 3; Eq. 4; §4.1 "Measuring Drift and Layer-wise KV Updates";
+ * Algorithm 1 forward of the active block, ProxyAttn, KL, TopK, S = M[K]].
+ *  REFRESH: projects [active rows h_active [batch, B, d]; window rows; the
+ *    centroids] with W_Q/W_K/W_V (RMSNorm with unit gain), writes the active
+ *    block's K/V and the K/V of the packet rows u_in into the layer's cache,
+ *    runs softmax attention of the active and window rows over all n_pos
+ *    keys, runs proxy attention of the centroid queries over the same keys,
+ *    scores each cluster by D_c = sum over heads of max(0, KL(P_t || P_prev))
+ *    against L->proxy_logits (then overwritten with P_t's logits), picks the
+ *    top-k clusters (largest D, lowest index on ties) and writes the selected
+ *    window rows S (ascending) to sel->idx / sel->count.  D [batch, K] and
+ *    topk [batch, k] (-1 past min(k, n_win)) are nullable outputs.
+ *  ACTIVE_ONLY: the active rows only (a step without a refresh, §4.1
+ *    "Update Schedule"); sel->count is set to 0.
+ *  act_logits (nullable, in/out [batch, B, Hq, n_pos]): the active block's
+ *    main-attention logits of the previous step; when delta is non-NULL the
+ *    per-row drift delta_j = sum_h max(0, KL(A_t || A_prev)) (f32 [batch, B])
+ *    is written, then act_logits is overwritten with this step's logits
+ *    (§4.2 "Current Block Commit"; Algorithm 1 main-attention drift of the
+ *    last layer).
+ */
+int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                   const void* h_active, const polestar_packet* u_in, float* D, int32_t* topk,
+                   polestar_packet* sel, float* act_logits, float* delta,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * polestar_refresh — gathered sparse layer forward producing the update
+ * packet [§4.1: forward over the selected clusters' rows only, giving
+ * U(t, l+1); Algorithm 1 sparse forward].  Rows are [active block; the
+ * sel->count rows S]: h' = h + o W_O^T, out = h' + (silu(g) * u) W_down^T with
+ * g, u the gate/up projections of RMSNorm(h').  Writes h_active_out
+ * [batch, B, d] (the next layer's active input) and u_rows [batch, win_max, d]
+ * (row r = output of window row sel->idx[r]).  When w_kv_next (packed
+ * POLESTAR_W_KV of layer l+1) is given, the K/V rows of layer l+1 for S are
+ * computed from the fresh U and scattered into k_next/v_next
+ * ([batch, n_pos, n_kv_heads, head_dim]).
+ */
+int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                     const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
+                     void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * polestar_commit — Polestar-Commit [§4.2 "Current Block Commit" and
+ * "Suffix Block Commit"; Table 5: tau_s, h, alpha, suffix confidence].
+ *  Confidence c = max over ids != mask_id of softmax(RMSNorm(x) W_lm^T),
+ *  yhat its argmax, for the active rows x = h_final [batch, B, d] and for the
+ *  suffix packet rows (u_final rows whose sel_final window row is in the
+ *  suffix window).  Current block: with the history hist_vals
+ *  [batch, B, max(hist,1)] f32 / hist_cnt [batch, B] i32 (in/out; reset to 0
+ *  at block entry), spike = delta - mean(history) (0 mean when empty), then
+ *  delta is pushed; tau_d = alpha (tau_s - c)^2; commit when masked and
+ *  (c >= tau_s or spike > tau_d).  Suffix: commit when the row is in S,
+ *  masked (suffix_masked [batch, win_suffix] u8) and c >= tau_suf.
+ *  Outputs: commit_active [batch, B] u8, commit_suffix [batch, win_suffix] u8,
+ *  conf_active / spike [batch, B] f32, yhat_active [batch, B] i32,
+ *  conf_suffix [batch, win_suffix] f32 (0 where not a packet row).
+ *  delta comes from polestar_drift of the last layer.  W_lm is packed
+ *  POLESTAR_W_LM.  active_masked [batch, B] u8.
+ */
+int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,
+                    const polestar_packet* u_final, const float* delta, const uint8_t* active_masked,
+                    const uint8_t* suffix_masked, float* hist_vals, int32_t* hist_cnt,
+                    uint8_t* commit_active, uint8_t* commit_suffix, float* conf_active,
+                    int32_t* yhat_active, float* spike, float* conf_suffix,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---- update schedule (host) --------------------------------------------- */
+/* 1 when the tokens decoded since the last refresh exceed tau_upd (a refresh
+ * step), else 0; tau_upd < 0 means never [§4.1 "Update Schedule"]. */
+int polestar_should_refresh(int32_t decoded_since_refresh, int32_t tau_upd);
+
+/* ---- NVFP4 codec [App. C.3] ---------------------------------------------- */
+/* Quantise float32 rows x [rows, d] (device) to codes [rows, d/2] and scales
+ * [rows, d/16]: per 16 channels s = amax/6, scale = E4M3(s) (round to
+ * nearest even, saturating at 448), code = E2M1(x / scale) (nearest even,
+ * saturating at 6; 0 when the scale is 0). */
+int polestar_nvfp4_pack(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales, void* stream);
+/* Exact dequantisation scale * value(code) into float32 x [rows, d]. */
+int polestar_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                          void* stream);
+/* Host evaluation of the same encoders (host pointers), for checks without a GPU. */
+int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POLESTAR_H */

@@ -13,11 +13,12 @@ the oracle follows its steps in the page's order.  It emulates the storage
 precision of the GPU path at exactly these points (``st`` = round to the
 storage dtype, identity for "f64"):
   * projections: RMSNorm (unit gain, eps) is applied as a per-row scale of the
-    projection output, ``y = (x @ W.T) / rms(x)``; token Q/K/V are stored
-    (``st``); centroid (proxy) queries are kept unrounded;
-  * attention output ``o`` and the SwiGLU product are stored before their
-    projections; the residual states ``h' = st(h + o Wo^T)`` and
-    ``out = st(h' + act Wd^T)`` are stored;
+    projection output, ``y = (x @ W.T) / rms(x)``; K and V are stored
+    (``st``); queries (token and centroid rows) are never stored and stay
+    unrounded;
+  * values that live only inside one call (attention output ``o``,
+    ``h' = h + o Wo^T``, the SwiGLU product ``act``) stay unrounded; the layer
+    output ``out = st(h' + act Wd^T)`` is stored;
   * centroids are stored after normalisation; attention logits that are kept
     as the next step's reference are stored as float32;
   * the NVFP4 codec and the commit rule are evaluated in float32, the
@@ -125,12 +126,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int, n_kv: i
     R, hq, dh = q.shape
     assert hq == n_heads
     g = (np.arange(n_heads) * n_kv) // n_heads
-    kk = k[:, g, :]                                   # [n, Hq, dh]
-    vv = v[:, g, :]
-    logits = np.einsum("rhd,nhd->rhn", q, kk) / math.sqrt(dh)
+    kk = np.asarray(k, dtype=np.float64)[:, g, :].transpose(1, 2, 0)      # [Hq, dh, n]
+    vv = np.asarray(v, dtype=np.float64)[:, g, :].transpose(1, 0, 2)      # [Hq, n, dh]
+    qh = np.asarray(q, dtype=np.float64).transpose(1, 0, 2)               # [Hq, R, dh]
+    logits = np.matmul(qh, kk) / math.sqrt(dh)                            # [Hq, R, n]
     p = np.exp(logits - logsumexp(logits)[..., None])
-    out = np.einsum("rhn,nhd->rhd", p, vv)
-    return out, logits
+    out = np.matmul(p, vv)                                                # [Hq, R, dh]
+    return out.transpose(1, 0, 2), logits.transpose(1, 0, 2)
 
 
 # ---------------------------------------------------------------------------
@@ -434,7 +436,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     nw = len(wpos)
     hq, hkv, dh = cfg.hq, cfg.hkv, cfg.dh
     toks = np.concatenate([h_act, h_win], axis=0) if refresh else np.asarray(h_act)
-    q = st(project(toks, W["wq"], eps)).reshape(-1, hq, dh)
+    q = project(toks, W["wq"], eps).reshape(-1, hq, dh)
     kr = st(project(toks, W["wk"], eps)).reshape(-1, hkv, dh)
     vr = st(project(toks, W["wv"], eps)).reshape(-1, hkv, dh)
     K, V = ls["K"], ls["V"]
@@ -444,7 +446,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
         K[wpos[rows]] = kr[cfg.B + rows]
         V[wpos[rows]] = vr[cfg.B + rows]
     out, logits = attention(q, K, V, hq, hkv)
-    res = {"o": st(out.reshape(out.shape[0], hq * dh)), "o_pre": out.reshape(out.shape[0], hq * dh),
+    res = {"o": out.reshape(out.shape[0], hq * dh),
            "act_logits": round_f32(logits[: cfg.B])}
     if commit_prev is not None:
         res["delta"] = head_summed_drift(logits[: cfg.B], commit_prev)
@@ -474,14 +476,13 @@ def refresh_layer(W: Dict, cfg: Cfg, h_act: np.ndarray, h_win: np.ndarray, o_tok
     S = np.asarray(S, dtype=np.int64)
     x = np.concatenate([h_act, h_win[S]], axis=0)
     o = np.concatenate([o_tok[:B], o_tok[B + S]], axis=0)
-    hp_pre = x + o @ np.asarray(W["wo"], dtype=np.float64).T
-    hp = st(hp_pre)
+    hp = x + o @ np.asarray(W["wo"], dtype=np.float64).T
     g = project(hp, W["wg"], eps)
     u = project(hp, W["wu"], eps)
-    act = st(silu(g) * u)
+    act = silu(g) * u
     out_pre = hp + act @ np.asarray(W["wd"], dtype=np.float64).T
     out = st(out_pre)
-    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp, "hp_pre": hp_pre, "act": act}
+    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp, "act": act}
 
 
 def kv_rows(u: np.ndarray, wk: np.ndarray, wv: np.ndarray, cfg: Cfg):
@@ -574,13 +575,13 @@ def full_forward(h0: np.ndarray, layers: List[Dict], cfg: Cfg):
     Hs, Ks, Vs = [h], [], []
     logits = None
     for W in layers:
-        q = st(project(h, W["wq"], eps)).reshape(-1, cfg.hq, cfg.dh)
+        q = project(h, W["wq"], eps).reshape(-1, cfg.hq, cfg.dh)
         k = st(project(h, W["wk"], eps)).reshape(-1, cfg.hkv, cfg.dh)
         v = st(project(h, W["wv"], eps)).reshape(-1, cfg.hkv, cfg.dh)
         out, logits = attention(q, k, v, cfg.hq, cfg.hkv)
-        o = st(out.reshape(out.shape[0], -1))
-        hp = st(h + o @ np.asarray(W["wo"], dtype=np.float64).T)
-        act = st(silu(project(hp, W["wg"], eps)) * project(hp, W["wu"], eps))
+        o = out.reshape(out.shape[0], -1)
+        hp = h + o @ np.asarray(W["wo"], dtype=np.float64).T
+        act = silu(project(hp, W["wg"], eps)) * project(hp, W["wu"], eps)
         h = st(hp + act @ np.asarray(W["wd"], dtype=np.float64).T)
         Hs.append(h)
         Ks.append(k)

@@ -1,0 +1,307 @@
+"""Per-call parity of one layer's refresh step: HIP path vs the CPU oracle on the
+same seeded inputs.
+
+Each case builds synthetic layer state (KV caches, window rows, an update
+packet, the previous logits), runs on the GPU
+  cluster(ENTRY) -> cluster(UPDATE, packet) -> drift(REFRESH) -> refresh(+ next-layer K/V)
+  -> cluster(UPDATE) of layer l+1 with the new packet,
+and after every call compares against the oracle run on the identical inputs.
+Discrete outputs (labels, top-k, S, NVFP4 codes) must match exactly; floating
+point values before their storage rounding must match within 2e-3 relative;
+stored bf16 values may differ from the oracle's rounding by at most one ulp at
+isolated near-midpoints.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from drift_driven_sparse_amd import binding as B
+from oracle import polestar_oracle as O
+from tests.harness import (Dev, assert_close, assert_stored, layer_struct, log, np64, oracle_weights,
+                           packed_layer, packet, to_dev, topk_margin, weights)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, batch, overrides)
+    "tiny_fp32": (synth.WORKLOADS[1], 1, {}),
+    "tiny_fp32_k8": (synth.WORKLOADS[1], 1, {"top_k": 8}),
+    "llada_layer_bf16": (synth.WORKLOADS[2], 1, {}),
+    "llada_layer_n1024": (synth.WORKLOADS[3], 1, {}),
+    "dream_gqa_layer": (synth.WORKLOADS[4], 1, {}),
+    "llada_nvfp4_batch2": (synth.WORKLOADS[5], 2, {}),
+    "tiny_bf16_window_tail": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=64, gen=64), 1,
+                              {"blk_start": 96}),
+    "tiny_bf16_small_window": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=4, gen=64), 1,
+                               {"blk_start": 4}),
+}
+
+
+def _state(w, dev, seq, nw, run=0):
+    d, n, hkv, dh, hq = w.d, w.n_pos, w.n_kv_heads, w.head_dim, w.n_heads
+    t = lambda tag, shape, std=1.0, dtype=w.dtype: synth.tensor(w, (seq,) + tag, shape, std, run, "cuda", dtype)
+    s = {
+        "K": t((10,), (n, hkv, dh)), "V": t((11,), (n, hkv, dh)),
+        "K1": t((12,), (n, hkv, dh)), "V1": t((13,), (n, hkv, dh)),
+        "H": t((14,), (nw, d)), "H1": t((15,), (nw, d)),
+        "h_act": t((16,), (w.block, d)),
+        "act_prev": t((17,), (w.block, hq, n), 1.0, "f32"),
+    }
+    rng = np.random.default_rng([w.seed(run), 99, seq])
+    n_patch = min(nw, max(1, nw // 4))
+    s["u_idx"] = np.sort(rng.choice(nw, size=n_patch, replace=False)).astype(np.int32)
+    s["u_rows"] = t((18,), (n_patch, d))
+    s["init"] = synth.kmeans_init(w, nw, 0, 0, run, seq)
+    s["init1"] = synth.kmeans_init(w, nw, 1, 0, run, seq)
+    return s
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_layer_step_parity(case):
+    w, batch, over = CASES[case]
+    top_k = over.get("top_k")
+    if top_k:
+        w = synth.shrink(w, top_k=top_k)
+    log(f"[layer-parity] case={case} d={w.d} n={w.n_pos} heads={w.n_heads}/{w.n_kv_heads} batch={batch} "
+        f"dtype={w.dtype} resid={w.resid}")
+    torch.manual_seed(0)
+    dev = Dev(w, batch=batch, vocab=0)
+    cfg = O.Cfg.from_workload(w, top_k=w.top_k)
+    st = cfg.st
+    n, d, hq, hkv, dh, Bk = w.n_pos, w.d, w.n_heads, w.n_kv_heads, w.head_dim, w.block
+    blk_start = over.get("blk_start", w.prompt)
+    wpos = O.window_positions(blk_start, n, Bk, w.win_prefix, w.win_suffix)
+    nw, WM, K = len(wpos), dev.win_max, w.n_clusters
+    keff = min(K, nw)
+    nv = w.resid == "nvfp4"
+    W0, W1 = weights(w, 0), weights(w, 1)
+    P0 = packed_layer(dev, W0)
+    wkv1 = dev.pack(B.W_KV, torch.cat([W1["wk"], W1["wv"]], 0))
+    Wo = oracle_weights(W0)
+    wk1, wv1 = np64(W1["wk"]), np64(W1["wv"])
+    del W1
+
+    S = [_state(w, dev, b, nw) for b in range(batch)]
+    # ---- device buffers
+    kc = torch.stack([s["K"] for s in S]).contiguous()
+    vc = torch.stack([s["V"] for s in S]).contiguous()
+    kc1 = torch.stack([s["K1"] for s in S]).contiguous()
+    vc1 = torch.stack([s["V1"] for s in S]).contiguous()
+    win = dev.zeros(batch, WM, d)
+    win1 = dev.zeros(batch, WM, d)
+    for b, s in enumerate(S):
+        win[b, :nw] = s["H"]
+        win1[b, :nw] = s["H1"]
+    codes = torch.zeros(batch, WM, d // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(batch, WM, d // 16, dtype=torch.uint8, device="cuda")
+    codes1, scales1 = codes.clone(), scales.clone()
+    z = dev.zeros(batch, K, d)
+    z1 = dev.zeros(batch, K, d)
+    m = torch.zeros(batch, WM, dtype=torch.int32, device="cuda")
+    m1 = m.clone()
+    plog = torch.zeros(batch, K, hq, n, dtype=torch.float32, device="cuda")
+    init = torch.zeros(batch, K, dtype=torch.int32, device="cuda")
+    init1 = init.clone()
+    for b, s in enumerate(S):
+        init[b, :keff] = torch.tensor(s["init"])
+        init1[b, :keff] = torch.tensor(s["init1"])
+    obj = torch.zeros(batch, 2 * w.kmeans_iters, dtype=torch.float64, device="cuda")
+    L0 = dict(P0, k_cache=kc, v_cache=vc, win_z=z, win_m=m, proxy_logits=plog)
+    L1 = dict(k_cache=kc1, v_cache=vc1, win_z=z1, win_m=m1)
+    if nv:
+        L0.update(win_codes=codes, win_scales=scales)
+        L1.update(win_codes=codes1, win_scales=scales1)
+    else:
+        L0.update(win_h=win)
+        L1.update(win_h=win1)
+    Ls0, Ls1 = layer_struct(L0), layer_struct(L1)
+
+    # ---- 1. block-entry clustering of layers l and l+1
+    B.polestar_cluster(dev.h, B.CLUSTER_ENTRY, Ls0, blk_start, None, init, win, obj, dev.ws, dev.ws_bytes)
+    B.polestar_cluster(dev.h, B.CLUSTER_ENTRY, Ls1, blk_start, None, init1, win1, None, dev.ws, dev.ws_bytes)
+    torch.cuda.synchronize()
+    OL, OL1 = [], []
+    for b, s in enumerate(S):
+        Hb = np64(s["H"])
+        zo, mo, tr = O.spherical_kmeans(Hb, K, s["init"], w.kmeans_iters)
+        assert np.array_equal(m[b, :nw].cpu().numpy(), mo), "k-means labels differ"
+        assert_stored(np64(z[b]), st(zo), w.dtype, "entry centroids")
+        assert np.allclose(obj[b].cpu().numpy(), tr, rtol=1e-12, atol=0), "k-means objective trace"
+        zo1, mo1, _ = O.spherical_kmeans(np64(s["H1"]), K, s["init1"], w.kmeans_iters)
+        assert np.array_equal(m1[b, :nw].cpu().numpy(), mo1)
+        ls = {"K": np64(s["K"]), "V": np64(s["V"]), "Z": st(zo), "M": mo}
+        ls1 = {"K": np64(s["K1"]), "V": np64(s["V1"]), "Z": st(zo1), "M": mo1}
+        if nv:
+            ls["codes"], ls["scales"] = O.residual_quantize(Hb, ls["Z"], mo)
+            ls1["codes"], ls1["scales"] = O.residual_quantize(np64(s["H1"]), ls1["Z"], mo1)
+            assert np.array_equal(codes[b, :nw].cpu().numpy(), ls["codes"]), "entry NVFP4 codes differ"
+            assert np.array_equal(scales[b, :nw].cpu().numpy(), ls["scales"])
+        else:
+            ls["H"] = Hb
+            ls1["H"] = np64(s["H1"])
+        # first drift reference: proxy logits of the entry centroids (oracle -> device)
+        zq = O.project(ls["Z"], Wo["wq"], cfg.eps).reshape(K, hq, dh)
+        _, pl = O.attention(zq, ls["K"], ls["V"], hq, hkv)
+        ls["P"] = O.round_f32(pl)
+        plog[b] = torch.tensor(ls["P"], dtype=torch.float32)
+        # keep both sides on identical state: device gets the oracle's centroids
+        z[b] = to_dev(ls["Z"], w.dtype)
+        z1[b] = to_dev(ls1["Z"], w.dtype)
+        OL.append(ls)
+        OL1.append(ls1)
+    log("[layer-parity] entry ok")
+
+    # ---- 2. window update with an incoming packet
+    u_rows = dev.zeros(batch, WM, d)
+    u_idx = torch.zeros(batch, WM, dtype=torch.int32, device="cuda")
+    u_cnt = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    for b, s in enumerate(S):
+        c = len(s["u_idx"])
+        u_rows[b, :c] = s["u_rows"]
+        u_idx[b, :c] = torch.tensor(s["u_idx"])
+        u_cnt[b] = c
+    pin = packet(u_rows, u_idx, u_cnt)
+    B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls0, blk_start, pin, None, None, None, dev.ws, dev.ws_bytes)
+    torch.cuda.synchronize()
+    CU = []
+    for b, s in enumerate(S):
+        cu = O.cluster_update(OL[b], cfg, np64(s["u_rows"]), s["u_idx"])
+        CU.append(cu)
+        assert_stored(np64(z[b]), OL[b]["Z"], w.dtype, "updated centroids")
+        if nv:
+            assert np.array_equal(codes[b, :nw].cpu().numpy(), OL[b]["codes"]), "re-quantised codes differ"
+            assert np.array_equal(scales[b, :nw].cpu().numpy(), OL[b]["scales"])
+        else:
+            assert np.array_equal(np64(win[b, :nw]), OL[b]["H"]), "patched window rows differ"
+        z[b] = to_dev(OL[b]["Z"], w.dtype)
+    log("[layer-parity] window update ok")
+
+    # ---- 3. drift
+    chk_qkv = torch.zeros(batch, dev.win_max + Bk + K, (hq + 2 * hkv) * dh, dtype=torch.float32, device="cuda")
+    chk_att = torch.zeros(batch, Bk + WM, hq * dh, dtype=torch.float32, device="cuda")
+    chk_hp = torch.zeros(batch, Bk + WM, d, dtype=torch.float32, device="cuda")
+    chk_out = torch.zeros(batch, Bk + WM, d, dtype=torch.float32, device="cuda")
+    chk_kv = torch.zeros(batch, WM, 2 * hkv * dh, dtype=torch.float32, device="cuda")
+    chk = B.Check(qkv=chk_qkv.data_ptr(), attn_out=chk_att.data_ptr(), hp=chk_hp.data_ptr(), out=chk_out.data_ptr(),
+                  kv_next=chk_kv.data_ptr())
+    B.polestar_set_check(dev.h, chk)
+    h_act = torch.stack([s["h_act"] for s in S]).contiguous()
+    act_logits = torch.stack([s["act_prev"] for s in S]).contiguous()
+    D = torch.zeros(batch, K, dtype=torch.float32, device="cuda")
+    topk = torch.zeros(batch, w.top_k, dtype=torch.int32, device="cuda")
+    sel_idx = torch.zeros(batch, WM, dtype=torch.int32, device="cuda")
+    sel_cnt = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    delta = torch.zeros(batch, Bk, dtype=torch.float32, device="cuda")
+    sel = packet(None, sel_idx, sel_cnt)
+    kc_before = kc.clone()
+    B.polestar_drift(dev.h, B.DRIFT_REFRESH, Ls0, blk_start, h_act, pin, D, topk, sel, act_logits, delta, dev.ws,
+                     dev.ws_bytes)
+    torch.cuda.synchronize()
+    DR = []
+    for b, s in enumerate(S):
+        ha = np64(s["h_act"])
+        dr = O.drift_layer(OL[b], Wo, cfg, blk_start, ha, CU[b]["h"], CU[b]["patched"], True,
+                           commit_prev=np64(s["act_prev"]))
+        DR.append(dr)
+        toks = np.concatenate([ha, CU[b]["h"]], 0)
+        proj = np.concatenate([O.project(toks, np.concatenate([Wo["wq"], Wo["wk"], Wo["wv"]], 0), cfg.eps),
+                               O.project(OL[b]["Z"], np.concatenate([Wo["wq"], Wo["wk"], Wo["wv"]], 0), cfg.eps)], 0)
+        assert_close(chk_qkv[b, : Bk + nw + K].cpu().numpy(), proj, "QKV projections", dtype=w.dtype)
+        # caches: active rows and patched rows rewritten, every other row bit-identical
+        assert_stored(np64(kc[b]).reshape(n, -1), OL[b]["K"].reshape(n, -1), w.dtype, "K cache")
+        assert_stored(np64(vc[b]).reshape(n, -1), OL[b]["V"].reshape(n, -1), w.dtype, "V cache")
+        untouched = np.setdiff1d(np.arange(n), np.concatenate([np.arange(blk_start, blk_start + Bk),
+                                                              wpos[s["u_idx"]]]))
+        assert torch.equal(kc[b, untouched], kc_before[b, untouched])
+        assert_close(chk_att[b, : Bk + nw].cpu().numpy(), dr["o"], "attention outputs", dtype=w.dtype)
+        assert_close(plog[b].cpu().numpy(), dr["proxy_logits"], "proxy logits", dtype=w.dtype)
+        assert_close(act_logits[b].cpu().numpy(), dr["act_logits"], "active logits", dtype=w.dtype)
+        assert_close(delta[b].cpu().numpy(), dr["delta"], "active drift delta")
+        Dg = D[b].cpu().numpy()
+        assert_close(Dg, dr["D"], "cluster drift D")
+        tg = topk[b].cpu().numpy()
+        assert np.array_equal(tg[: min(w.top_k, keff)], O.topk_clusters(Dg, w.top_k, keff)), "top-k rule"
+        if not np.array_equal(tg[: min(w.top_k, keff)], dr["topk"]):
+            mg = topk_margin(dr["D"], dr["topk"], keff)
+            pytest.fail(f"top-k differs from the oracle (oracle margin {mg:.2e})")
+        cnt = int(sel_cnt[b])
+        assert np.array_equal(sel_idx[b, :cnt].cpu().numpy(), dr["S"]), "selected rows S differ"
+        log(f"[layer-parity] seq {b}: D={np.round(Dg, 5).tolist()} topk={tg.tolist()} nS={cnt}")
+    log("[layer-parity] drift ok")
+
+    # ---- 4. sparse forward + next-layer K/V
+    h_out = dev.zeros(batch, Bk, d)
+    u_new = dev.zeros(batch, WM, d)
+    B.polestar_refresh(dev.h, Ls0, blk_start, h_act, sel, wkv1, kc1, vc1, h_out, u_new, dev.ws, dev.ws_bytes)
+    torch.cuda.synchronize()
+    RF = []
+    for b, s in enumerate(S):
+        Sb = DR[b]["S"]
+        rf = O.refresh_layer(Wo, cfg, np64(s["h_act"]), CU[b]["h"], DR[b]["o"], Sb)
+        RF.append(rf)
+        rows = Bk + len(Sb)
+        assert_close(chk_hp[b, :rows].cpu().numpy(), rf["hp"], "h' = h + o W_O", dtype=w.dtype)
+        assert_close(chk_out[b, :rows].cpu().numpy(), rf["out_pre"], "layer outputs", dtype=w.dtype)
+        assert_stored(np64(h_out[b]), rf["h_act_out"], w.dtype, "active outputs")
+        assert_stored(np64(u_new[b, : len(Sb)]), rf["U"], w.dtype, "update packet U")
+        k1, v1 = O.kv_rows(rf["U"], wk1, wv1, cfg)
+        pre = np.concatenate([O.project(rf["U"], wk1, cfg.eps), O.project(rf["U"], wv1, cfg.eps)], 1)
+        assert_close(chk_kv[b, : len(Sb)].cpu().numpy(), pre, "next-layer K/V projections", dtype=w.dtype)
+        pos = wpos[Sb]
+        assert_stored(np64(kc1[b, pos]).reshape(len(pos), -1), k1.reshape(len(pos), -1), w.dtype, "next-layer K rows")
+        assert_stored(np64(vc1[b, pos]).reshape(len(pos), -1), v1.reshape(len(pos), -1), w.dtype, "next-layer V rows")
+        others = np.setdiff1d(np.arange(n), pos)
+        assert torch.equal(kc1[b, others], S[b]["K1"][others])
+    log("[layer-parity] refresh ok")
+
+    # ---- 5. layer l+1 takes the packet: window rows patched, centroids refreshed
+    pout = packet(u_new, sel_idx, sel_cnt)
+    B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls1, blk_start, pout, None, None, None, dev.ws, dev.ws_bytes)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        O.cluster_update(OL1[b], cfg, RF[b]["U"], DR[b]["S"])
+        assert_stored(np64(z1[b]), OL1[b]["Z"], w.dtype, "layer l+1 centroids")
+        if not nv:
+            assert_stored(np64(win1[b, :nw]), OL1[b]["H"], w.dtype, "layer l+1 window rows")
+    B.polestar_set_check(dev.h, None)
+    dev.close()
+    log(f"[layer-parity] case={case} passed")
+
+
+def test_drift_is_deterministic():
+    """Identical inputs give bit-identical outputs across two runs."""
+    w = synth.WORKLOADS[2]
+    dev = Dev(w, batch=1, vocab=0)
+    n, d, hq, hkv, dh, Bk = w.n_pos, w.d, w.n_heads, w.n_kv_heads, w.head_dim, w.block
+    wpos = O.window_positions(w.prompt, n, Bk, w.win_prefix, w.win_suffix)
+    nw, WM, K = len(wpos), dev.win_max, w.n_clusters
+    P0 = packed_layer(dev, weights(w, 0))
+    s = _state(w, dev, 0, nw)
+    outs = []
+    for rep in range(2):
+        kc, vc = s["K"][None].clone(), s["V"][None].clone()
+        win = dev.zeros(1, WM, d)
+        win[0, :nw] = s["H"]
+        z, m = dev.zeros(1, K, d), torch.zeros(1, WM, dtype=torch.int32, device="cuda")
+        plog = synth.tensor(w, (0, 40), (1, K, hq, n), 1.0, 0, "cuda", "f32")
+        init = torch.tensor(s["init"], dtype=torch.int32, device="cuda")[None]
+        Ls = layer_struct(dict(P0, k_cache=kc, v_cache=vc, win_h=win, win_z=z, win_m=m, proxy_logits=plog))
+        B.polestar_cluster(dev.h, B.CLUSTER_ENTRY, Ls, w.prompt, None, init, win, None, dev.ws, dev.ws_bytes)
+        B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls, w.prompt, None, None, None, None, dev.ws, dev.ws_bytes)
+        D = torch.zeros(1, K, dtype=torch.float32, device="cuda")
+        sel_idx = torch.zeros(1, WM, dtype=torch.int32, device="cuda")
+        sel_cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+        sel = packet(None, sel_idx, sel_cnt)
+        h_act = s["h_act"][None].contiguous()
+        B.polestar_drift(dev.h, B.DRIFT_REFRESH, Ls, w.prompt, h_act, None, D, None, sel, None, None, dev.ws,
+                         dev.ws_bytes)
+        h_out, u_new = dev.zeros(1, Bk, d), dev.zeros(1, WM, d)
+        B.polestar_refresh(dev.h, Ls, w.prompt, h_act, sel, None, None, None, h_out, u_new, dev.ws, dev.ws_bytes)
+        torch.cuda.synchronize()
+        outs.append((D.clone(), sel_idx.clone(), h_out.clone(), u_new.clone(), kc.clone(), plog.clone(), z.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    dev.close()
