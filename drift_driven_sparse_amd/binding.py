@@ -24,8 +24,11 @@ EXPORTED = [
     "polestar_create", "polestar_destroy", "polestar_strerror", "polestar_workspace_size",
     "polestar_set_check", "polestar_weight_packed_size", "polestar_pack_weight", "polestar_cluster",
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
-    "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host",
+    "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
+    "polestar_profile_read",
 ]
+KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
+           "lmprep", "lmhead", "decide"]
 
 
 class Dims(C.Structure):
@@ -90,6 +93,8 @@ def lib() -> C.CDLL:
         L.polestar_nvfp4_pack.argtypes = [vp, i64, i32, vp, vp, vp]
         L.polestar_nvfp4_unpack.argtypes = [vp, vp, i64, i32, vp, vp]
         L.polestar_nvfp4_pack_host.argtypes = [vp, i64, i32, vp, vp]
+        L.polestar_profile.argtypes = [vp, C.c_int]
+        L.polestar_profile_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32)]
         for name in EXPORTED:
             f = getattr(L, name)
             if name not in ("polestar_destroy", "polestar_strerror"):
@@ -204,3 +209,16 @@ def polestar_nvfp4_unpack(codes, scales, rows, d, x, stream=None) -> None:
 
 def polestar_nvfp4_pack_host(x, rows, d, codes, scales) -> None:
     _ck(lib().polestar_nvfp4_pack_host(ptr(x), rows, d, ptr(codes), ptr(scales)), "polestar_nvfp4_pack_host")
+
+
+def polestar_profile(h: int, enable: bool) -> None:
+    _ck(lib().polestar_profile(h, 1 if enable else 0), "polestar_profile")
+
+
+def polestar_profile_read(h: int):
+    """{kernel name: (total ms, launches)} of the recorded launches."""
+    n = len(KERNELS)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int32 * n)()
+    _ck(lib().polestar_profile_read(h, ms, cnt), "polestar_profile_read")
+    return {KERNELS[i]: (ms[i], cnt[i]) for i in range(n)}

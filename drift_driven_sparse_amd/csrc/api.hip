@@ -3,10 +3,51 @@
 // first launch, so a call that returns an error has enqueued nothing.
 #include <new>
 #include <string.h>
+#include <vector>
 
 #include "kernels.h"
 
+struct ProfState {
+  struct Rec { int id; hipEvent_t a, b; };
+  bool on = false;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t take() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  void clear() { recs.clear(); used = 0; }
+  ~ProfState() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
 namespace {
+
+// Brackets one kernel launch with profiling events when profiling is on.
+struct ProfScope {
+  ProfState* p;
+  hipStream_t s;
+  ProfState::Rec r;
+  ProfScope(polestar_handle* h, hipStream_t s_, int id) : p(h->prof && h->prof->on ? h->prof : nullptr), s(s_) {
+    if (!p) return;
+    r.id = id;
+    r.a = p->take();
+    r.b = p->take();
+    if (r.a && r.b) (void)hipEventRecord(r.a, s);
+  }
+  ~ProfScope() {
+    if (!p || !r.a || !r.b) return;
+    (void)hipEventRecord(r.b, s);
+    p->recs.push_back(r);
+  }
+};
+#define PROF(id) ProfScope _prof_##__LINE__(h, s, id)
 
 constexpr int kMaxRows = 144;   // rows of one projection tile column
 
@@ -103,6 +144,7 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.z64 = at<double>(ws, h->ws.z64);
   a.nvfp4 = d.resid_fmt == POLESTAR_RESID_NVFP4;
   if (a.geom.n_win == 0) return POLESTAR_OK;
+  PROF(POLESTAR_K_CLUSTER);
   return hip_status(launch_cluster<T>(a, s));
 }
 
@@ -131,7 +173,11 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.a_qkv = at<char>(ws, h->ws.a_qkv);
   p.inv = at<float>(ws, h->ws.inv_qkv);
   p.eps = h->pr.rms_eps;
-  hipError_t e = launch_prep_qkv<T>(p, s);
+  hipError_t e;
+  {
+    PROF(POLESTAR_K_PREP);
+    e = launch_prep_qkv<T>(p, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 2. projections; K/V of the active block and of the packet rows go to the cache
   const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
@@ -165,7 +211,10 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   ep.chk = h->chk.qkv;
   ep.chk_rows = h->mq;
   ep.chk_ld = ga.N;
-  e = launch_gemm<T>(ga, ep, rows, s);
+  {
+    PROF(POLESTAR_K_QKV);
+    e = launch_gemm<T>(ga, ep, rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 3. attention, proxy attention and drift
   AttnArgs at_;
@@ -191,7 +240,10 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.akl = at<float>(ws, h->ws.akl);
   at_.chk = h->chk.attn_out;
   at_.chk_rows = h->mt;
-  e = launch_attention<T>(at_, s);
+  {
+    PROF(POLESTAR_K_ATTN);
+    e = launch_attention<T>(at_, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 4. top-k clusters and the selected rows
   TopkArgs tk;
@@ -212,6 +264,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   tk.akl = at_.akl;
   tk.delta = (act_logits && delta) ? delta : nullptr;
   tk.refresh = refresh;
+  PROF(POLESTAR_K_TOPK);
   return hip_status(launch_topk(tk, s));
 }
 
@@ -247,7 +300,11 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   EpiParams ep;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_PARTIAL;
-  hipError_t e = launch_gemm<T>(ga, ep, max_rows, s);
+  hipError_t e;
+  {
+    PROF(POLESTAR_K_OPROJ);
+    e = launch_gemm<T>(ga, ep, max_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   RowReduceArgs rr;
   memset(&rr, 0, sizeof(rr));
@@ -274,7 +331,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.eps = h->pr.rms_eps;
   rr.chk = h->chk.hp;
   rr.chk_rows = h->mt;
-  e = launch_row_reduce<T>(rr, max_rows, s);
+  {
+    PROF(POLESTAR_K_OREDUCE);
+    e = launch_row_reduce<T>(rr, max_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 2. act = silu(g) * u with g, u the projections of RMSNorm(h')
   memset(&ga, 0, sizeof(ga));
@@ -297,7 +357,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ep.act = at<char>(ws, h->ws.act);
   ep.act_rows = h->mt;
   ep.ffn = d.ffn;
-  e = launch_gemm<T>(ga, ep, max_rows, s);
+  {
+    PROF(POLESTAR_K_GU);
+    e = launch_gemm<T>(ga, ep, max_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&ga, 0, sizeof(ga));
@@ -317,7 +380,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.part_rows = h->mt;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_PARTIAL;
-  e = launch_gemm<T>(ga, ep, max_rows, s);
+  {
+    PROF(POLESTAR_K_DOWN);
+    e = launch_gemm<T>(ga, ep, max_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // the residual stream continues from the unrounded h'
   RowReduceArgs r2 = rr;
@@ -334,7 +400,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
   r2.inv_rms = at<float>(ws, h->ws.inv_out);
   r2.chk = h->chk.out;
-  e = launch_row_reduce<T>(r2, max_rows, s);
+  {
+    PROF(POLESTAR_K_DREDUCE);
+    e = launch_row_reduce<T>(r2, max_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 4. K/V of layer l+1 for the packet rows
   if (w_kv_next && g.n_win > 0) {
@@ -364,6 +433,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     ep.chk = h->chk.kv_next;
     ep.chk_rows = h->win_max;
     ep.chk_ld = 2 * h->nkv;
+    PROF(POLESTAR_K_KVNEXT);
     e = launch_gemm<T>(ga, ep, g.n_win, s);
     if (e != hipSuccess) return POLESTAR_E_HIP;
   }
@@ -398,7 +468,11 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   lp.inv = at<float>(ws, h->ws.lm_inv);
   lp.meta = at<int32_t>(ws, h->ws.lm_meta);
   lp.eps = h->pr.rms_eps;
-  hipError_t e = launch_lm_prep<T>(lp, s);
+  hipError_t e;
+  {
+    PROF(POLESTAR_K_LMPREP);
+    e = launch_lm_prep<T>(lp, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   GemmArgs ga;
   memset(&ga, 0, sizeof(ga));
@@ -422,7 +496,10 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   ep.lm_tiles = h->lm_tiles;
   ep.vocab = d.vocab;
   ep.mask_id = h->pr.mask_id;
-  e = launch_gemm<T>(ga, ep, lm_rows, s);
+  {
+    PROF(POLESTAR_K_LMHEAD);
+    e = launch_gemm<T>(ga, ep, lm_rows, s);
+  }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   DecideArgs da;
   memset(&da, 0, sizeof(da));
@@ -452,6 +529,7 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   da.yhat_active = yhat_active;
   da.spike = spike;
   da.conf_suffix = conf_suffix;
+  PROF(POLESTAR_K_DECIDE);
   return hip_status(launch_decide(da, s));
 }
 
@@ -505,6 +583,11 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   polestar_handle* h = new (std::nothrow) polestar_handle;
   if (!h) return POLESTAR_E_SHAPE;
   memset(h, 0, sizeof(*h));
+  h->prof = new (std::nothrow) ProfState;
+  if (!h->prof) {
+    delete h;
+    return POLESTAR_E_SHAPE;
+  }
   h->dm = d;
   h->pr = p;
   h->win_max = d.win_prefix + d.win_suffix;
@@ -521,7 +604,36 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   return POLESTAR_OK;
 }
 
-void polestar_destroy(polestar_handle* h) { delete h; }
+void polestar_destroy(polestar_handle* h) {
+  if (!h) return;
+  delete h->prof;
+  delete h;
+}
+
+int polestar_profile(polestar_handle* h, int enable) {
+  if (!h) return POLESTAR_E_NULL;
+  h->prof->clear();
+  h->prof->on = enable != 0;
+  return POLESTAR_OK;
+}
+
+int polestar_profile_read(polestar_handle* h, double* total_ms, int32_t* launches) {
+  if (!h || !total_ms || !launches) return POLESTAR_E_NULL;
+  for (int i = 0; i < POLESTAR_K_COUNT; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (const ProfState::Rec& r : h->prof->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return POLESTAR_E_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return POLESTAR_E_HIP;
+    if (r.id >= 0 && r.id < POLESTAR_K_COUNT) {
+      total_ms[r.id] += ms;
+      launches[r.id] += 1;
+    }
+  }
+  return POLESTAR_OK;
+}
 
 int polestar_workspace_size(const polestar_handle* h, size_t* bytes) {
   if (!h || !bytes) return POLESTAR_E_NULL;

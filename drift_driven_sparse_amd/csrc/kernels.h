@@ -8,7 +8,10 @@ struct WsLayout {
       lm_a, lm_inv, lm_stats, lm_meta, total;
 };
 
+struct ProfState;   // per-kernel event records (api.hip)
+
 struct polestar_handle {
+  ProfState* prof;
   polestar_dims dm;
   polestar_params pr;
   int32_t win_max;   // win_prefix + win_suffix

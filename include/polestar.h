@@ -261,6 +261,24 @@ int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, con
                     int32_t* yhat_active, float* spike, float* conf_suffix,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- per-kernel timing (diagnostics) ------------------------------------ */
+enum {
+  POLESTAR_K_CLUSTER = 0, POLESTAR_K_PREP, POLESTAR_K_QKV, POLESTAR_K_ATTN, POLESTAR_K_TOPK,
+  POLESTAR_K_OPROJ, POLESTAR_K_OREDUCE, POLESTAR_K_GU, POLESTAR_K_DOWN, POLESTAR_K_DREDUCE,
+  POLESTAR_K_KVNEXT, POLESTAR_K_LMPREP, POLESTAR_K_LMHEAD, POLESTAR_K_DECIDE, POLESTAR_K_COUNT
+};
+/* enable != 0: from now on every kernel this handle enqueues is bracketed by
+ * a pair of hipEvents on its stream (events recorded during stream capture
+ * become graph nodes and are re-recorded by every replay); enable == 0 stops.
+ * Either way the previous records are dropped.  Host-side only; no device
+ * memory is allocated. */
+int polestar_profile(polestar_handle* h, int enable);
+/* Waits for the recorded events and returns, per kernel kind (POLESTAR_K_*),
+ * the summed duration in ms (total_ms[POLESTAR_K_COUNT]) and the number of
+ * launches (launches[POLESTAR_K_COUNT]) of the recorded launches; the records
+ * stay (a graph replay re-records them).  E_HIP if an event query fails. */
+int polestar_profile_read(polestar_handle* h, double* total_ms, int32_t* launches);
+
 /* ---- update schedule (host) --------------------------------------------- */
 /* 1 when the tokens decoded since the last refresh exceed tau_upd (a refresh
  * step), else 0; tau_upd < 0 means never [§4.1 "Update Schedule"]. */
