@@ -28,7 +28,7 @@ EXPORTED = [
     "polestar_profile_read",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
-           "lmprep", "lmhead", "decide"]
+           "lmprep", "lmhead", "decide", "kl"]
 
 
 class Dims(C.Structure):

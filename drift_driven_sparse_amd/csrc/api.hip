@@ -69,6 +69,7 @@ void layout(polestar_handle* h) {
   w.o = take(Bt * h->mt * (size_t)h->nq * 4);
   w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
   w.akl = take(Bt * d.block * d.n_heads * 4);
+  w.lg = take(Bt * (size_t)(d.n_clusters + d.block) * d.n_heads * d.n_pos * 4);
   w.part = take((size_t)h->ksplit * Bt * h->mt * d.d * 4);
   w.hp = take(Bt * h->mt * d.d * 4);
   w.inv_hp = take(Bt * h->mt * 4);
@@ -204,6 +205,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   ep.flags = at<int32_t>(ws, h->ws.flags);
   ep.nq = h->nq;
   ep.nkv = h->nkv;
+  ep.dh = d.head_dim;
   ep.block = d.block;
   ep.win_max = h->win_max;
   ep.n_pos = d.n_pos;
@@ -238,11 +240,17 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.act_logits = act_logits;
   at_.act_kl = delta != nullptr;
   at_.akl = at<float>(ws, h->ws.akl);
+  at_.lg_stage = at<float>(ws, h->ws.lg);
   at_.chk = h->chk.attn_out;
   at_.chk_rows = h->mt;
   {
     PROF(POLESTAR_K_ATTN);
     e = launch_attention<T>(at_, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  {
+    PROF(POLESTAR_K_KL);
+    e = launch_kl(at_, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 4. top-k clusters and the selected rows
@@ -426,6 +434,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     ep.kc = k_next;
     ep.vc = v_next;
     ep.nkv = h->nkv;
+    ep.dh = d.head_dim;
     ep.win_max = h->win_max;
     ep.n_pos = d.n_pos;
     ep.geom = g;
@@ -571,7 +580,8 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   if (d.n_pos > 1024) return POLESTAR_E_UNSUPPORTED;
   if (d.d % 16 != 0) return POLESTAR_E_UNSUPPORTED;
   if (d.dtype == POLESTAR_BF16) {
-    if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16) return POLESTAR_E_UNSUPPORTED;
+    if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16 || d.n_pos % 4)
+      return POLESTAR_E_UNSUPPORTED;
   } else {
     if (d.ffn % 4 || d.d % 4) return POLESTAR_E_UNSUPPORTED;
   }

@@ -56,6 +56,13 @@ __global__ void pack_f32_kernel(const float* __restrict__ src, float* __restrict
 }
 
 // ---- epilogues ------------------------------------------------------------------------
+// Cache element of position pos, K/V column col (= kv head * dh + d):
+// K token-major [b][n][Hkv][dh]; V transposed [b][Hkv][dh][n].
+PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
+  if (!is_v) return ((int64_t)b * e.n_pos + pos) * e.nkv + col;
+  return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
+}
+
 template <typename T, int KIND>
 PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, int n0, int nt,
                      const float* tile) {
@@ -85,7 +92,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
           const int w = r - e.block;
           if (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) pos = e.geom.pos(w);
         }
-        if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), ((int64_t)b * e.n_pos + pos) * e.nkv + col, v);
+        if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
       }
     }
   } else if constexpr (KIND == EPI_SWIGLU) {
@@ -112,7 +119,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
       const int w = e.sel_idx[(int64_t)b * e.win_max + r];
       if (w < 0 || w >= e.geom.n_win) continue;
       const int pos = e.geom.pos(w);
-      St<T>::store((T*)(which ? e.vc : e.kc), ((int64_t)b * e.n_pos + pos) * e.nkv + col, v);
+      St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
     }
   } else if constexpr (KIND == EPI_LMSTAT) {
     // Per row, over this tile's vocabulary ids: max logit, sum exp(logit - max), and the

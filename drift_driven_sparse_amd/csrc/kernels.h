@@ -4,7 +4,7 @@
 
 // Handle contents (host only).
 struct WsLayout {
-  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, part, hp, inv_hp, act, inv_out, xhat, z64,
+  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64,
       lm_a, lm_inv, lm_stats, lm_meta, total;
 };
 
@@ -74,7 +74,7 @@ struct EpiParams {
   float* q; int32_t q_rows;     // q[(b*q_rows + r)*nq + n]
   void* kc; void* vc;           // caches (storage dtype)
   const int32_t* flags;         // patched flags [batch][win_max]
-  int32_t nq, nkv, block, win_max, n_pos;
+  int32_t nq, nkv, block, win_max, n_pos, dh;
   WinGeom geom;
   float* chk; int32_t chk_rows, chk_ld;   // chk[(b*chk_rows + r)*chk_ld + n]
   // SwiGLU
@@ -152,12 +152,14 @@ struct AttnArgs {
   float* proxy_logits;    // [batch][K][hq][n]
   float* kl;              // [batch][K][hq]
   float* act_logits;      // [batch][block][hq][n] or null
+  float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
   int32_t act_kl;         // compute active-row KL against act_logits before overwrite
   float* akl;             // [batch][block][hq]
   float* chk; int32_t chk_rows;
 };
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_kl(const AttnArgs& a, hipStream_t s);
 
 struct TopkArgs {
   int32_t batch, K, k, hq, block, win_max, n_win;

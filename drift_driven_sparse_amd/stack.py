@@ -38,7 +38,7 @@ class RefreshStack:
         for _ in range(n_layers):
             L = {
                 "k_cache": torch.zeros(bt, n, dims.n_kv_heads, dims.head_dim, dtype=self.tdt, device=device),
-                "v_cache": torch.zeros(bt, n, dims.n_kv_heads, dims.head_dim, dtype=self.tdt, device=device),
+                "v_cache": torch.zeros(bt, dims.n_kv_heads, dims.head_dim, n, dtype=self.tdt, device=device),
                 "win_z": torch.zeros(bt, dims.n_clusters, d, dtype=self.tdt, device=device),
                 "win_m": torch.zeros(bt, self.win_max, dtype=torch.int32, device=device),
                 "proxy_logits": torch.zeros(bt, dims.n_clusters, dims.n_heads, n, dtype=torch.float32, device=device),

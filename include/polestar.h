@@ -20,7 +20,9 @@
  *   spikes are always float32.
  * Layouts (row-major, batch outermost):
  *   hidden rows          [batch, rows, d]
- *   KV cache (per layer) [batch, n_pos, n_kv_heads, head_dim]
+ *   K cache (per layer)  [batch, n_pos, n_kv_heads, head_dim]   (token-major)
+ *   V cache (per layer)  [batch, n_kv_heads, head_dim, n_pos]   (transposed:
+ *                        keys contiguous, the layout the attention streams)
  *   window rows          [batch, win_max, d], win_max = win_prefix + win_suffix;
  *                        window row w is the w-th position, ascending, of
  *                        [blk_start - win_prefix, blk_start) U
@@ -90,7 +92,7 @@ typedef struct polestar_dims {
   int32_t n_kv_heads; /* key/value heads; n_heads % n_kv_heads == 0 */
   int32_t head_dim;   /* 64 or 128 */
   int32_t ffn;        /* SwiGLU width */
-  int32_t n_pos;      /* positions per sequence (prompt + generation) */
+  int32_t n_pos;      /* positions per sequence (prompt + generation); bf16: multiple of 4 */
   int32_t batch;      /* independent sequences processed together */
   int32_t block;      /* active block size B (<= 64) */
   int32_t win_prefix; /* |Omega_p| */
@@ -122,7 +124,7 @@ typedef struct polestar_layer {
   const void* w_gu;     /* packed POLESTAR_W_GU */
   const void* w_down;   /* packed POLESTAR_W_DOWN */
   void* k_cache;        /* [batch, n_pos, n_kv_heads, head_dim], in/out */
-  void* v_cache;        /* same */
+  void* v_cache;        /* [batch, n_kv_heads, head_dim, n_pos], in/out */
   void* win_h;          /* RAW: window rows [batch, win_max, d], in/out */
   uint8_t* win_codes;   /* NVFP4: [batch, win_max, d/2], in/out */
   uint8_t* win_scales;  /* NVFP4: [batch, win_max, d/16], in/out */
@@ -230,7 +232,7 @@ int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_
  * (row r = output of window row sel->idx[r]).  When w_kv_next (packed
  * POLESTAR_W_KV of layer l+1) is given, the K/V rows of layer l+1 for S are
  * computed from the fresh U and scattered into k_next/v_next
- * ([batch, n_pos, n_kv_heads, head_dim]).
+ * (K and V caches of layer l+1, layouts as above).
  */
 int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
                      const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
@@ -265,7 +267,7 @@ int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, con
 enum {
   POLESTAR_K_CLUSTER = 0, POLESTAR_K_PREP, POLESTAR_K_QKV, POLESTAR_K_ATTN, POLESTAR_K_TOPK,
   POLESTAR_K_OPROJ, POLESTAR_K_OREDUCE, POLESTAR_K_GU, POLESTAR_K_DOWN, POLESTAR_K_DREDUCE,
-  POLESTAR_K_KVNEXT, POLESTAR_K_LMPREP, POLESTAR_K_LMHEAD, POLESTAR_K_DECIDE, POLESTAR_K_COUNT
+  POLESTAR_K_KVNEXT, POLESTAR_K_LMPREP, POLESTAR_K_LMHEAD, POLESTAR_K_DECIDE, POLESTAR_K_KL, POLESTAR_K_COUNT
 };
 /* enable != 0: from now on every kernel this handle enqueues is bracketed by
  * a pair of hipEvents on its stream (events recorded during stream capture

@@ -87,9 +87,9 @@ def test_layer_step_parity(case):
     S = [_state(w, dev, b, nw) for b in range(batch)]
     # ---- device buffers
     kc = torch.stack([s["K"] for s in S]).contiguous()
-    vc = torch.stack([s["V"] for s in S]).contiguous()
+    vc = torch.stack([s["V"].permute(1, 2, 0) for s in S]).contiguous()      # V cache: [Hkv, dh, n]
     kc1 = torch.stack([s["K1"] for s in S]).contiguous()
-    vc1 = torch.stack([s["V1"] for s in S]).contiguous()
+    vc1 = torch.stack([s["V1"].permute(1, 2, 0) for s in S]).contiguous()
     win = dev.zeros(batch, WM, d)
     win1 = dev.zeros(batch, WM, d)
     for b, s in enumerate(S):
@@ -212,7 +212,7 @@ def test_layer_step_parity(case):
         assert_close(chk_qkv[b, : Bk + nw + K].cpu().numpy(), proj, "QKV projections", dtype=w.dtype)
         # caches: active rows and patched rows rewritten, every other row bit-identical
         assert_stored(np64(kc[b]).reshape(n, -1), OL[b]["K"].reshape(n, -1), w.dtype, "K cache")
-        assert_stored(np64(vc[b]).reshape(n, -1), OL[b]["V"].reshape(n, -1), w.dtype, "V cache")
+        assert_stored(np64(vc[b].permute(2, 0, 1)).reshape(n, -1), OL[b]["V"].reshape(n, -1), w.dtype, "V cache")
         untouched = np.setdiff1d(np.arange(n), np.concatenate([np.arange(blk_start, blk_start + Bk),
                                                               wpos[s["u_idx"]]]))
         assert torch.equal(kc[b, untouched], kc_before[b, untouched])
@@ -252,7 +252,8 @@ def test_layer_step_parity(case):
         assert_close(chk_kv[b, : len(Sb)].cpu().numpy(), pre, "next-layer K/V projections", dtype=w.dtype)
         pos = wpos[Sb]
         assert_stored(np64(kc1[b, pos]).reshape(len(pos), -1), k1.reshape(len(pos), -1), w.dtype, "next-layer K rows")
-        assert_stored(np64(vc1[b, pos]).reshape(len(pos), -1), v1.reshape(len(pos), -1), w.dtype, "next-layer V rows")
+        assert_stored(np64(vc1[b].permute(2, 0, 1)[pos]).reshape(len(pos), -1), v1.reshape(len(pos), -1), w.dtype,
+                      "next-layer V rows")
         others = np.setdiff1d(np.arange(n), pos)
         assert torch.equal(kc1[b, others], S[b]["K1"][others])
     log("[layer-parity] refresh ok")
@@ -282,7 +283,7 @@ def test_drift_is_deterministic():
     s = _state(w, dev, 0, nw)
     outs = []
     for rep in range(2):
-        kc, vc = s["K"][None].clone(), s["V"][None].clone()
+        kc, vc = s["K"][None].clone(), s["V"].permute(1, 2, 0)[None].contiguous()
         win = dev.zeros(1, WM, d)
         win[0, :nw] = s["H"]
         z, m = dev.zeros(1, K, d), torch.zeros(1, WM, dtype=torch.int32, device="cuda")
