@@ -77,6 +77,7 @@ void layout(polestar_handle* h) {
   w.inv_out = take(Bt * h->mt * 4);
   w.xhat = take(Bt * h->win_max * d.d * 8);
   w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
+  w.wstat = take(Bt * (h->win_max + (size_t)d.n_clusters * PS_CEIL_DIV(d.d, 256)) * 8);
   const size_t lm_rows = d.block + d.win_suffix;
   if (d.vocab > 0) {
     w.lm_a = take(Bt * lm_rows * d.d * T);
@@ -143,6 +144,9 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.flags = at<int32_t>(ws, h->ws.flags);
   a.xhat = at<double>(ws, h->ws.xhat);
   a.z64 = at<double>(ws, h->ws.z64);
+  a.wnorm = at<double>(ws, h->ws.wstat);
+  a.nchunk = PS_CEIL_DIV(d.d, 256);
+  a.cpart = a.wnorm + (size_t)d.batch * h->win_max;
   a.nvfp4 = d.resid_fmt == POLESTAR_RESID_NVFP4;
   if (a.geom.n_win == 0) return POLESTAR_OK;
   PROF(POLESTAR_K_CLUSTER);

@@ -120,98 +120,138 @@ __global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, doubl
 }
 
 // ---- per refresh step: window update ---------------------------------------------------------
-// One workgroup per (cluster, sequence) handles exactly the window rows labelled with
-// that cluster, so every row and centroid has a single writer.
+// Three passes, each spread over the whole chip:
+//   rows:    one workgroup per window row -> current row (packet row, else the stored row or
+//            centroid + dequantised residual), patch flag, float64 norm;
+//   sum:     one workgroup per (256-column chunk, cluster, sequence) -> float64 normalised
+//            member sum of its columns and the chunk's sum of squares;
+//   finish:  same grid -> the norm of the whole sum (chunk partials added in chunk order),
+//            the new centroid columns and, for NVFP4 storage, the members' re-quantised groups.
+constexpr int kChunk = 256;
+
+// Window rows of sequence b labelled c, ascending, into mem[] (with their norms when nr != null).
+// Returns the member count; every thread of the 256-thread workgroup gets it.
+PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* nr, int* wcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t wbase = (int64_t)b * a.win_max;
+  const bool in = tid < a.geom.n_win && a.win_m[wbase + tid] == c;
+  const unsigned long long m = __ballot(in);
+  if (lane == 0) wcnt[wave] = __popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? wcnt[w] : 0;
+    tot += wcnt[w];
+  }
+  if (in) {
+    const int pos = off + __popcll(m & ((1ull << lane) - 1ull));
+    mem[pos] = tid;
+    if (nr) nr[pos] = a.wnorm[wbase + tid];
+  }
+  __syncthreads();
+  return tot;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void window_update_kernel(ClusterArgs a) {
+__global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
   __shared__ double red[4];
-  __shared__ int plist[256];      // packet row of each window row, -1 if none
-  __shared__ int mem[256];
-  __shared__ double nrm[256];
-  __shared__ int nmem_sh;
-  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int d = a.d, nwin = a.geom.n_win;
+  __shared__ int pr_sh;
+  const int w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = a.d;
   const int64_t wbase = (int64_t)b * a.win_max;
   int cnt = a.u_count ? a.u_count[b] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.win_max ? a.win_max : cnt);
-  for (int w = tid; w < a.win_max; w += blockDim.x) plist[w] = -1;
+  if (tid == 0) pr_sh = -1;
   __syncthreads();
-  for (int r = tid; r < cnt; r += blockDim.x) {
-    const int w = a.u_idx[wbase + r];
-    if (w >= 0 && w < nwin) plist[w] = r;
-  }
-  if (tid == 0) {
-    int m = 0;
-    for (int w = 0; w < nwin; ++w)
-      if (a.win_m[wbase + w] == c) mem[m++] = w;
-    nmem_sh = m;
-  }
+  // packet row of this window row (the last one when an index repeats)
+  for (int r = tid; r < cnt; r += blockDim.x)
+    if (a.u_idx[wbase + r] == w) atomicMax(&pr_sh, r);
   __syncthreads();
-  const int nmem = nmem_sh;
-  if (nmem == 0) return;
-  T* rows = (T*)a.ws_rows;
+  const int pr = pr_sh;
+  int c = a.win_m[wbase + w];
+  c = (c < 0 || c >= a.K) ? 0 : c;
   const T* zc = (const T*)a.win_z + ((int64_t)b * a.K + c) * d;
-  // 1. current rows: packet row, else raw window row or centroid + dequantised residual
-  for (int m = 0; m < nmem; ++m) {
-    const int w = mem[m];
-    const int pr = plist[w];
-    const int64_t dst = (wbase + w) * d;
-    double ss = 0.0;
-    for (int n = tid; n < d; n += blockDim.x) {
-      float x;
-      if (pr >= 0) {
-        x = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n);
-      } else if (a.nvfp4) {
-        const uint8_t byte = a.codes[(wbase + w) * (d / 2) + n / 2];
-        const uint32_t code = (n & 1) ? (byte >> 4) : (byte & 15u);
-        const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n / 16]);
-        x = St<T>::round(St<T>::load(zc, n) + sv * e2m1_value(code));
-      } else {
-        x = St<T>::load((const T*)a.win_h, dst + n);
-      }
-      St<T>::store(rows, dst + n, x);
-      if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n, x);
-      ss += (double)x * (double)x;
-    }
-    ss = block_sum_d(ss, red);
-    if (tid == 0) {
-      nrm[m] = sqrt(ss);
-      a.flags[wbase + w] = pr >= 0;
-    }
-  }
-  __syncthreads();
-  // 2. normalised member sum (float64)
-  double* s = a.z64 + ((int64_t)b * a.K + c) * d;
+  T* rows = (T*)a.ws_rows;
+  const int64_t dst = (wbase + w) * d;
   double ss = 0.0;
   for (int n = tid; n < d; n += blockDim.x) {
-    double acc = 0.0;
-    for (int m = 0; m < nmem; ++m) {
-      const double nr = nrm[m];
-      if (nr > 0.0) acc += (double)St<T>::load(rows, (wbase + mem[m]) * d + n) / nr;
+    float x;
+    if (pr >= 0) {
+      x = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n);
+    } else if (a.nvfp4) {
+      const uint8_t byte = a.codes[(wbase + w) * (d / 2) + n / 2];
+      const uint32_t code = (n & 1) ? (byte >> 4) : (byte & 15u);
+      const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n / 16]);
+      x = St<T>::round(St<T>::load(zc, n) + sv * e2m1_value(code));
+    } else {
+      x = St<T>::load((const T*)a.win_h, dst + n);
     }
-    s[n] = acc;
-    ss += acc * acc;
+    St<T>::store(rows, dst + n, x);
+    if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n, x);
+    ss += (double)x * (double)x;
   }
   ss = block_sum_d(ss, red);
+  if (tid == 0) {
+    a.wnorm[wbase + w] = sqrt(ss);
+    a.flags[wbase + w] = pr >= 0;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void centroid_sum_kernel(ClusterArgs a) {
+  __shared__ double red[4];
+  __shared__ int mem[256];
+  __shared__ double nr[256];
+  __shared__ int wcnt[4];
+  const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int d = a.d, n = ch * kChunk + tid;
+  const int nmem = members_of(a, b, c, mem, nr, wcnt);
+  if (nmem == 0) return;
+  const int64_t wbase = (int64_t)b * a.win_max;
+  const T* rows = (const T*)a.ws_rows;
+  double acc = 0.0;
+  if (n < d)
+    for (int m = 0; m < nmem; ++m)
+      if (nr[m] > 0.0) acc += (double)St<T>::load(rows, (wbase + mem[m]) * d + n) / nr[m];
+  if (n < d) a.z64[((int64_t)b * a.K + c) * d + n] = acc;
+  const double ss = block_sum_d(acc * acc, red);
+  if (tid == 0) a.cpart[((int64_t)b * a.K + c) * a.nchunk + ch] = ss;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
+  __shared__ int mem[256];
+  __shared__ int wcnt[4];
+  __shared__ float zsh[kChunk];
+  const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int d = a.d, n0 = ch * kChunk, n = n0 + tid;
+  const int nmem = members_of(a, b, c, mem, nullptr, wcnt);
+  if (nmem == 0) return;   // no members: the centroid is kept and no row refers to it
+  const int64_t zrow = (int64_t)b * a.K + c;
+  double ss = 0.0;
+  for (int i = 0; i < a.nchunk; ++i) ss += a.cpart[zrow * a.nchunk + i];
   const double ns = sqrt(ss);
-  // 3. centroid (kept when the sum vanishes)
-  if (ns > 0.0)
-    for (int n = tid; n < d; n += blockDim.x) St<T>::store_d((T*)zc, n, s[n] / ns);
+  T* zc = (T*)a.win_z + zrow * d;
+  if (n < d) {
+    if (ns > 0.0) St<T>::store_d(zc, n, a.z64[zrow * d + n] / ns);   // kept when the sum vanishes
+    zsh[tid] = St<T>::load(zc, n);
+  }
+  if (!a.nvfp4) return;
   __syncthreads();
-  // 4. NVFP4: residual to the new centroid
-  if (a.nvfp4) {
-    const int ng = d / 16;
-    for (int i = tid; i < nmem * ng; i += blockDim.x) {
-      const int w = mem[i / ng], gi = i % ng;
-      float r[16];
-      uint32_t codes[16];
-      for (int e = 0; e < 16; ++e)
-        r[e] = St<T>::load(rows, (wbase + w) * d + gi * 16 + e) - St<T>::load(zc, gi * 16 + e);
-      const uint32_t sc = nvfp4_group(r, codes);
-      a.scales[(wbase + w) * ng + gi] = (uint8_t)sc;
-      for (int e = 0; e < 8; ++e)
-        a.codes[(wbase + w) * (d / 2) + gi * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
-    }
+  // residuals of the members' 16-element groups in this chunk against the new centroid
+  const int64_t wbase = (int64_t)b * a.win_max;
+  const int gpc = min(kChunk, d - n0) / 16;
+  const T* rows = (const T*)a.ws_rows;
+  for (int i = tid; i < nmem * gpc; i += blockDim.x) {
+    const int w = mem[i / gpc], gi = i % gpc;
+    const int64_t row = wbase + w;
+    float r[16];
+    uint32_t codes[16];
+    for (int e = 0; e < 16; ++e) r[e] = St<T>::load(rows, row * d + n0 + gi * 16 + e) - zsh[gi * 16 + e];
+    const uint32_t sc = nvfp4_group(r, codes);
+    const int g = n0 / 16 + gi;
+    a.scales[row * (d / 16) + g] = (uint8_t)sc;
+    for (int e = 0; e < 8; ++e) a.codes[row * (d / 2) + g * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
   }
 }
 
@@ -267,7 +307,10 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
     double* s64 = a.z64 + (int64_t)a.batch * a.K * a.d;   // scratch row per sequence after the centroids
     hipLaunchKernelGGL(kmeans_entry_kernel<T>, dim3(a.batch), dim3(1024), 0, s, a, s64);
   } else {
-    hipLaunchKernelGGL(window_update_kernel<T>, dim3(a.K, a.batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(window_rows_kernel<T>, dim3(a.geom.n_win, a.batch), dim3(256), 0, s, a);
+    const dim3 g(a.nchunk, a.K, a.batch);
+    hipLaunchKernelGGL(centroid_sum_kernel<T>, g, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(centroid_finish_kernel<T>, g, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -4,7 +4,7 @@
 
 // Handle contents (host only).
 struct WsLayout {
-  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64,
+  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat,
       lm_a, lm_inv, lm_stats, lm_meta, total;
 };
 
@@ -126,6 +126,9 @@ struct ClusterArgs {
   void* ws_rows;            // patched window rows [batch][win_max][d] (storage dtype)
   int32_t* flags;           // [batch][win_max]
   double* xhat; double* z64;
+  double* wnorm;            // [batch][win_max] float64 norms of the current window rows
+  double* cpart;            // [batch][K][nchunk] chunk sums of squares of the member sums
+  int32_t nchunk;           // ceil(d / 256)
   int nvfp4;
 };
 template <typename T>
