@@ -1,6 +1,7 @@
 // C ABI of the Polestar refresh library: host-side validation, workspace layout
 // and the launch sequence of each call.  Every argument is checked before the
 // first launch, so a call that returns an error has enqueued nothing.
+#include <algorithm>
 #include <new>
 #include <string.h>
 #include <vector>
@@ -70,8 +71,17 @@ void layout(polestar_handle* h) {
   w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
   w.akl = take(Bt * d.block * d.n_heads * 4);
   w.lg = take(Bt * (size_t)(d.n_clusters + d.block) * d.n_heads * d.n_pos * 4);
-  w.part = take((size_t)h->ksplit * Bt * h->mt * d.d * 4);
+  size_t part = (size_t)h->ksplit * Bt * h->mt * d.d;
+  if (d.dtype == POLESTAR_BF16) {
+    const size_t nqkv = (size_t)h->nq + 2 * (size_t)h->nkv;
+    part = std::max(part, (size_t)h->ks_qkv * Bt * h->mq * nqkv);
+    part = std::max(part, (size_t)h->ks_o * Bt * h->mt * d.d);
+    part = std::max(part, (size_t)h->ks_down * Bt * h->mt * d.d);
+    part = std::max(part, (size_t)h->ks_kv * Bt * h->win_max * 2 * (size_t)h->nkv);
+  }
+  w.part = take(part * 4);
   w.hp = take(Bt * h->mt * d.d * 4);
+  w.hp_pl = take(d.dtype == POLESTAR_BF16 ? Bt * 2 * h->mt * d.d * 2 : 0);
   w.inv_hp = take(Bt * h->mt * 4);
   w.act = take(Bt * h->mt * (size_t)d.ffn * 4);
   w.inv_out = take(Bt * h->mt * 4);
@@ -217,7 +227,25 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   ep.chk = h->chk.qkv;
   ep.chk_rows = h->mq;
   ep.chk_ld = ga.N;
-  {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    DlArgs dl;
+    memset(&dl, 0, sizeof(dl));
+    dl.A = ga.A;
+    dl.planes = 1;
+    dl.W = ga.W;
+    dl.N = ga.N;
+    dl.K = ga.K;
+    dl.batch = d.batch;
+    dl.ksplit = h->ks_qkv;
+    dl.part = at<float>(ws, h->ws.part);
+    dl.part_rows = h->mq;
+    dl.e = ep;
+    {
+      PROF(POLESTAR_K_QKV);
+      e = launch_dl<T>(dl, DL_NARROW, rows, s);
+      if (e == hipSuccess) e = launch_dl_finish<T>(dl, rows, s);
+    }
+  } else {
     PROF(POLESTAR_K_QKV);
     e = launch_gemm<T>(ga, ep, rows, s);
   }
@@ -239,6 +267,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.kc = L->k_cache;
   at_.vc = L->v_cache;
   at_.o = at<char>(ws, h->ws.o);
+  at_.o_planes = std::is_same<T, bf16_t>::value;
   at_.proxy_logits = L->proxy_logits;
   at_.kl = at<float>(ws, h->ws.kl);
   at_.act_logits = act_logits;
@@ -280,10 +309,195 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   return hip_status(launch_topk(tk, s));
 }
 
+// bf16 storage: projections by the weight-streaming kernel; float32 activations travel as
+// bf16 hi/lo planes between the projections.
+int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                  const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
+                  void* u_rows, void* ws, hipStream_t s) {
+  typedef bf16_t T;
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const int max_rows = d.block + g.n_win;
+  float* part = at<float>(ws, h->ws.part);
+  hipError_t e;
+  // 1. h' = h + o W_O^T over rows [active; S]
+  DlArgs dl;
+  memset(&dl, 0, sizeof(dl));
+  dl.A.base = at<char>(ws, h->ws.o);
+  dl.A.plane_stride = (int64_t)h->mt * h->nq;
+  dl.A.bstride = 2 * dl.A.plane_stride;
+  dl.A.lda = h->nq;
+  dl.A.rowmap = sel->idx;
+  dl.A.map_bstride = h->win_max;
+  dl.A.map_from = d.block;
+  dl.A.map_off = d.block;
+  dl.A.rows_dev = sel->count;
+  dl.A.rows_add = d.block;
+  dl.A.rows_max = max_rows;
+  dl.planes = 2;
+  dl.W = L->w_o;
+  dl.N = d.d;
+  dl.K = h->nq;
+  dl.batch = d.batch;
+  dl.ksplit = h->ks_o;
+  dl.part = part;
+  dl.part_rows = h->mt;
+  dl.e.kind = EPI_PARTIAL;
+  {
+    PROF(POLESTAR_K_OPROJ);
+    e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  RowReduceArgs rr;
+  memset(&rr, 0, sizeof(rr));
+  rr.part = part;
+  rr.ksplit = h->ks_o;
+  rr.part_rows = h->mt;
+  rr.batch = d.batch;
+  rr.d = d.d;
+  rr.count = sel->count;
+  rr.block = d.block;
+  rr.win_max = h->win_max;
+  rr.res_a = h_active;
+  rr.res_a_bstride = (int64_t)d.block * d.d;
+  rr.res_split = d.block;
+  rr.res_b = at<char>(ws, h->ws.win_rows);
+  rr.res_b_bstride = (int64_t)h->win_max * d.d;
+  rr.sel_idx = sel->idx;
+  rr.out_a = at<char>(ws, h->ws.hp);
+  rr.out_a_bstride = (int64_t)h->mt * d.d;
+  rr.out_split = h->mt;
+  rr.out_f32 = 1;
+  rr.out_pl = at<uint16_t>(ws, h->ws.hp_pl);
+  rr.pl_stride = (int64_t)h->mt * d.d;
+  rr.pl_bstride = 2 * rr.pl_stride;
+  rr.inv_rms = at<float>(ws, h->ws.inv_hp);
+  rr.inv_bstride = h->mt;
+  rr.eps = h->pr.rms_eps;
+  rr.chk = h->chk.hp;
+  rr.chk_rows = h->mt;
+  {
+    PROF(POLESTAR_K_OREDUCE);
+    e = launch_row_reduce<T>(rr, max_rows, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 2. act = silu(g) * u with g, u the projections of RMSNorm(h'), stored as hi/lo planes
+  memset(&dl, 0, sizeof(dl));
+  dl.A.base = rr.out_pl;
+  dl.A.plane_stride = rr.pl_stride;
+  dl.A.bstride = rr.pl_bstride;
+  dl.A.lda = d.d;
+  dl.A.rows_dev = sel->count;
+  dl.A.rows_add = d.block;
+  dl.A.rows_max = max_rows;
+  dl.planes = 2;
+  dl.W = L->w_gu;
+  dl.N = 2 * d.ffn;
+  dl.K = d.d;
+  dl.batch = d.batch;
+  dl.ksplit = 1;
+  dl.e.kind = EPI_SWIGLU;
+  dl.e.inv_rms = rr.inv_rms;
+  dl.e.inv_bstride = h->mt;
+  dl.e.act = at<char>(ws, h->ws.act);
+  dl.e.act_rows = h->mt;
+  dl.e.ffn = d.ffn;
+  {
+    PROF(POLESTAR_K_GU);
+    e = launch_dl<T>(dl, DL_MID, max_rows, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 3. out = h' + act W_down^T -> next active rows and the update packet
+  const int64_t act_plane = (int64_t)h->mt * d.ffn;
+  memset(&dl, 0, sizeof(dl));
+  dl.A.base = at<char>(ws, h->ws.act);
+  dl.A.plane_stride = act_plane;
+  dl.A.bstride = 2 * act_plane;
+  dl.A.lda = d.ffn;
+  dl.A.rows_dev = sel->count;
+  dl.A.rows_add = d.block;
+  dl.A.rows_max = max_rows;
+  dl.planes = 2;
+  dl.W = L->w_down;
+  dl.N = d.d;
+  dl.K = d.ffn;
+  dl.batch = d.batch;
+  dl.ksplit = h->ks_down;
+  dl.part = part;
+  dl.part_rows = h->mt;
+  dl.e.kind = EPI_PARTIAL;
+  {
+    PROF(POLESTAR_K_DOWN);
+    e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // the residual stream continues from the unrounded h'
+  RowReduceArgs r2 = rr;
+  r2.ksplit = h->ks_down;
+  r2.res_a = rr.out_a;
+  r2.res_a_f32 = 1;
+  r2.res_a_bstride = (int64_t)h->mt * d.d;
+  r2.res_split = h->mt;
+  r2.out_f32 = 0;
+  r2.out_pl = nullptr;
+  r2.res_b = nullptr;
+  r2.out_a = h_active_out;
+  r2.out_a_bstride = (int64_t)d.block * d.d;
+  r2.out_split = d.block;
+  r2.out_b = u_rows;
+  r2.out_b_bstride = (int64_t)h->win_max * d.d;
+  r2.inv_rms = at<float>(ws, h->ws.inv_out);
+  r2.chk = h->chk.out;
+  {
+    PROF(POLESTAR_K_DREDUCE);
+    e = launch_row_reduce<T>(r2, max_rows, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  // 4. K/V of layer l+1 for the packet rows
+  if (w_kv_next && g.n_win > 0) {
+    memset(&dl, 0, sizeof(dl));
+    dl.A.base = u_rows;
+    dl.A.bstride = (int64_t)h->win_max * d.d;
+    dl.A.lda = d.d;
+    dl.A.rows_dev = sel->count;
+    dl.A.rows_max = g.n_win;
+    dl.planes = 1;
+    dl.W = w_kv_next;
+    dl.N = 2 * h->nkv;
+    dl.K = d.d;
+    dl.batch = d.batch;
+    dl.ksplit = h->ks_kv;
+    dl.part = part;
+    dl.part_rows = h->win_max;
+    dl.e.kind = EPI_KV;
+    dl.e.inv_rms = r2.inv_rms;
+    dl.e.inv_bstride = h->mt;
+    dl.e.inv_off = d.block;
+    dl.e.kc = k_next;
+    dl.e.vc = v_next;
+    dl.e.nkv = h->nkv;
+    dl.e.dh = d.head_dim;
+    dl.e.win_max = h->win_max;
+    dl.e.n_pos = d.n_pos;
+    dl.e.geom = g;
+    dl.e.sel_idx = sel->idx;
+    dl.e.chk = h->chk.kv_next;
+    dl.e.chk_rows = h->win_max;
+    dl.e.chk_ld = 2 * h->nkv;
+    PROF(POLESTAR_K_KVNEXT);
+    e = launch_dl<T>(dl, DL_NARROW, g.n_win, s);
+    if (e == hipSuccess) e = launch_dl_finish<T>(dl, g.n_win, s);
+    if (e != hipSuccess) return POLESTAR_E_HIP;
+  }
+  return POLESTAR_OK;
+}
+
 template <typename T>
 int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
                const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
                void* u_rows, void* ws, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value)
+    return do_refresh_dl(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s);
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
   const int max_rows = d.block + g.n_win;
@@ -612,6 +826,17 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
   int ks = PS_CEIL_DIV(256, ntiles);
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
+  // bf16 projections: split K until about 256 workgroups are busy
+  auto ks_for = [&](int n_cols, int tile_cols, int k, int cap) {
+    const int tiles = PS_CEIL_DIV(n_cols, tile_cols) * d.batch;
+    int v = 256 / tiles;
+    v = v < 1 ? 1 : (v > cap ? cap : v);
+    return v > k / 32 ? k / 32 : v;
+  };
+  h->ks_qkv = ks_for(h->nq + 2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 8);
+  h->ks_o = ks_for(d.d, dl_tile_cols(DL_WIDE), h->nq, 16);
+  h->ks_down = ks_for(d.d, dl_tile_cols(DL_WIDE), d.ffn, 16);
+  h->ks_kv = ks_for(2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 16);
   h->lm_tiles = PS_CEIL_DIV(d.vocab, 64);
   layout(h);
   *out = h;

@@ -221,7 +221,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       }
       const float val = num / den;
       const int row = r0 + lrow;
-      ((float*)a.o)[((int64_t)b * a.mt + row) * (a.hq * DH) + h * DH + dd] = val;
+      if (a.o_planes) {
+        const int64_t plane = (int64_t)a.mt * a.hq * DH;
+        uint16_t hi, lo;
+        split_bf16(val, hi, lo);
+        uint16_t* o = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH + dd;
+        o[0] = hi;
+        o[plane] = lo;
+      } else {
+        ((float*)a.o)[((int64_t)b * a.mt + row) * (a.hq * DH) + h * DH + dd] = val;
+      }
       if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + dd] = val;
     }
   }

@@ -56,13 +56,6 @@ __global__ void pack_f32_kernel(const float* __restrict__ src, float* __restrict
 }
 
 // ---- epilogues ------------------------------------------------------------------------
-// Cache element of position pos, K/V column col (= kv head * dh + d):
-// K token-major [b][n][Hkv][dh]; V transposed [b][Hkv][dh][n].
-PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
-  if (!is_v) return ((int64_t)b * e.n_pos + pos) * e.nkv + col;
-  return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
-}
-
 template <typename T, int KIND>
 PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, int n0, int nt,
                      const float* tile) {
@@ -76,24 +69,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
   } else if constexpr (KIND == EPI_QKV) {
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
       const int r = idx / kNT, c = idx % kNT, n = n0 + c;
-      if (n >= g.N) continue;
-      const float v = tile[r * kLDT + c] * e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
-      if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
-      if (n < e.nq) {
-        e.q[((int64_t)b * e.q_rows + r) * e.nq + n] = v;
-      } else {
-        const int kv = n - e.nq;
-        const int which = kv >= e.nkv;
-        const int col = kv - which * e.nkv;
-        int pos = -1;
-        if (r < e.block) {
-          pos = e.geom.blk_start + r;
-        } else {
-          const int w = r - e.block;
-          if (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) pos = e.geom.pos(w);
-        }
-        if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
-      }
+      if (n < g.N) epi_qkv_elem<T>(e, b, r, n, tile[r * kLDT + c]);
     }
   } else if constexpr (KIND == EPI_SWIGLU) {
     // tile columns: [gate 16 | up 16] x 2 pairs -> 32 output columns starting at n0/2
@@ -111,15 +87,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
   } else if constexpr (KIND == EPI_KV) {
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
       const int r = idx / kNT, c = idx % kNT, n = n0 + c;
-      if (n >= g.N) continue;
-      const float v = tile[r * kLDT + c] * e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
-      if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
-      const int which = n >= e.nkv;
-      const int col = n - which * e.nkv;
-      const int w = e.sel_idx[(int64_t)b * e.win_max + r];
-      if (w < 0 || w >= e.geom.n_win) continue;
-      const int pos = e.geom.pos(w);
-      St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
+      if (n < g.N) epi_kv_elem<T>(e, b, r, n, tile[r * kLDT + c]);
     }
   } else if constexpr (KIND == EPI_LMSTAT) {
     // Per row, over this tile's vocabulary ids: max logit, sum exp(logit - max), and the
@@ -170,9 +138,18 @@ PS_DEV void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// Each wave walks its K range in 32-wide steps.  Weight fragments are kept in a
+// ring of kDW steps and the activation fragments of the next step are loaded
+// while the current one is multiplied, so a wave always has several KiB of
+// HBM reads in flight.  Loads past the wave's range re-read its last step
+// (valid addresses, results unused) so the loop body has no load branches.
+constexpr int kDW = 4;   // weight prefetch depth in 32-wide K steps
+
 template <typename T, int RT, int KIND, int AF32>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e) {
   constexpr int NSUB = kNT / 16;
+  constexpr int AW = AF32 ? 2 : 1;        // 16-byte A pieces per lane, row tile and step
+  constexpr int ASTEP = AF32 ? 8 : 4;     // 16-byte units per 32 elements of a row
   __shared__ float tile[RT * 16 * kLDT];
   const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
@@ -180,20 +157,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
   if (rows_b <= 0) return;
   const int nrt = (rows_b + 15) >> 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ksteps = g.K >> 7;
-  const int s0 = (int)((int64_t)ksteps * sp / g.ksplit), s1 = (int)((int64_t)ksteps * (sp + 1) / g.ksplit);
+  const int k32n = g.K >> 5;
+  const int s0 = (int)((int64_t)k32n * sp / g.ksplit), s1 = (int)((int64_t)k32n * (sp + 1) / g.ksplit);
   const int w0 = s0 + (s1 - s0) * wave / 4, w1 = s0 + (s1 - s0) * (wave + 1) / 4;
+  const int wlast = w1 > 0 ? w1 - 1 : 0;
 
   typedef typename std::conditional<AF32 != 0, float, uint16_t>::type AE;
   const AE* Ab = (const AE*)g.A.base + (int64_t)b * g.A.bstride;
-  const AE* arow[RT];
+  const uint4* arow[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     int r = rt * 16 + (lane & 15);
     if (r >= rows_b) r = 0;
-    arow[rt] = Ab + g.A.src_row(b, r) * g.A.lda + 8 * (lane >> 4);
+    arow[rt] = (const uint4*)(Ab + g.A.src_row(b, r) * g.A.lda + 8 * (lane >> 4));
   }
-  const int64_t k32n = g.K >> 5;
   const int n16_total = g.N >> 4;
   // per-subtile fragment stream; subtiles past N re-read the first one (their columns are never stored)
   const uint4* Wsub[NSUB];
@@ -210,37 +187,49 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = w0; ks < w1; ++ks) {
-    uint4 wf[NSUB][4];
+  uint4 wr[kDW][NSUB];
+  uint4 ar[2][RT][AW];
+  auto load_w = [&](uint4 (&w)[NSUB], int st) {
+    st = st < wlast ? st : wlast;
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb)
+    for (int sb = 0; sb < NSUB; ++sb) w[sb] = Wsub[sb][(int64_t)st * 64];
+  };
+  auto load_a = [&](uint4 (&a)[RT][AW], int st) {
+    st = st < wlast ? st : wlast;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[sb][j] = Wsub[sb][((int64_t)ks * 4 + j) * 64];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < AW; ++q) a[rt][q] = arow[rt][st * ASTEP + q];
+  };
+  auto compute = [&](const uint4 (&w)[NSUB], const uint4 (&a)[RT][AW]) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (rt < nrt) {
         if constexpr (AF32 != 0) {
+          uint4 hi, lo;
+          split8(__builtin_bit_cast(float4, a[rt][0]), __builtin_bit_cast(float4, a[rt][1]), hi, lo);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float4* ap = (const float4*)(arow[rt] + ks * 128 + 32 * j);
-            uint4 hi, lo;
-            split8(ap[0], ap[1], hi, lo);
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) {
-              acc[rt][sb] = mfma(hi, wf[sb][j], acc[rt][sb]);
-              acc[rt][sb] = mfma(lo, wf[sb][j], acc[rt][sb]);
-            }
+          for (int sb = 0; sb < NSUB; ++sb) {
+            acc[rt][sb] = mfma(hi, w[sb], acc[rt][sb]);
+            acc[rt][sb] = mfma(lo, w[sb], acc[rt][sb]);
           }
         } else {
-          uint4 af[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = *(const uint4*)(arow[rt] + ks * 128 + 32 * j);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(af[j], wf[sb][j], acc[rt][sb]);
+          for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(a[rt][0], w[sb], acc[rt][sb]);
         }
       }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kDW; ++u) load_w(wr[u], w0 + u);
+  load_a(ar[0], w0);
+  load_a(ar[1], w0 + 1);
+  for (int t = w0; t < w1; t += kDW) {
+#pragma unroll
+    for (int u = 0; u < kDW; ++u) {
+      if (t + u < w1) compute(wr[u], ar[u & 1]);
+      load_w(wr[u], t + u + kDW);
+      load_a(ar[u & 1], t + u + 2);
     }
   }
   // Combine the four waves' partial sums in LDS, wave 0 first.
@@ -322,8 +311,11 @@ hipError_t dispatch_kind(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
 }
 
 // ---- split-K row reduction ------------------------------------------------------------------
+// One workgroup per output row: partial sums (added in split order) + residual, stored as
+// float32 or rounded to the storage dtype, optionally also as bf16 hi/lo planes, and the
+// 1/rms of the stored row for the next projection.  Four columns per thread and step.
 template <typename T>
-__global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
+__global__ __launch_bounds__(512) void row_reduce_kernel(RowReduceArgs a) {
   __shared__ float red[8];
   const int r = blockIdx.x, b = blockIdx.y;
   int rows_b = a.block + (a.count ? a.count[b] : 0);
@@ -342,23 +334,37 @@ __global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
   const int64_t ooff = (r < a.out_split) ? (int64_t)b * a.out_a_bstride + (int64_t)r * a.d
                                          : (int64_t)b * a.out_b_bstride + (int64_t)(r - a.out_split) * a.d;
   void* obase = (r < a.out_split) ? a.out_a : a.out_b;
+  uint16_t* pl = (a.out_pl && r < a.out_split) ? a.out_pl + (int64_t)b * a.pl_bstride + (int64_t)r * a.d : nullptr;
   const int64_t pstride = (int64_t)a.batch * a.part_rows * a.d;
   const float* p = a.part + ((int64_t)b * a.part_rows + r) * a.d;
   float ss = 0.f;
-  for (int n = threadIdx.x; n < a.d; n += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < a.ksplit; ++s) v += p[s * pstride + n];
-    v += res32 ? res32[n] : St<T>::load(res, n);
-    if (a.chk) a.chk[((int64_t)b * a.chk_rows + r) * a.d + n] = v;
-    float q;
-    if (a.out_f32) {
-      q = v;
-      ((float*)obase)[ooff + n] = v;
-    } else {
-      q = St<T>::round(v);
-      St<T>::store((T*)obase, ooff + n, v);
+  for (int n = threadIdx.x * 4; n < a.d; n += blockDim.x * 4) {
+    float4 v = *(const float4*)(p + n);
+    for (int s = 1; s < a.ksplit; ++s) {
+      const float4 t = *(const float4*)(p + s * pstride + n);
+      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
     }
-    ss += q * q;
+    float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = vv[i] + (res32 ? res32[n + i] : St<T>::load(res, n + i));
+      if (a.chk) a.chk[((int64_t)b * a.chk_rows + r) * a.d + n + i] = x;
+      float q;
+      if (a.out_f32) {
+        q = x;
+        ((float*)obase)[ooff + n + i] = x;
+      } else {
+        q = St<T>::round(x);
+        St<T>::store((T*)obase, ooff + n + i, x);
+      }
+      if (pl) {
+        uint16_t hi, lo;
+        split_bf16(x, hi, lo);
+        pl[n + i] = hi;
+        pl[a.pl_stride + n + i] = lo;
+      }
+      ss += q * q;
+    }
   }
   ss = block_sum(ss, red);
   if (threadIdx.x == 0 && a.inv_rms) a.inv_rms[(int64_t)b * a.inv_bstride + r] = 1.f / sqrtf(ss / (float)a.d + a.eps);
@@ -394,7 +400,7 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 template <typename T>
 hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, a.batch), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,302 @@
+// Weight-streaming projections of the gathered rows for bf16 storage (gfx950).
+//
+// Per sequence a projection multiplies at most 144 rows by a large weight, so
+// the kernel is organised around moving bytes: every 32-wide K step is one
+// pipeline stage that holds the A fragments of all row tiles and the weight
+// fragments of the workgroup.  Stages are filled by direct global -> LDS loads
+// (global_load_lds_dwordx4, no VGPR staging) in a ring of P buffers; stage s is
+// consumed after a wait that leaves the P-2 younger stages in flight and one
+// workgroup barrier.  Each ring buffer is its own LDS object, which lets the
+// compiler see that reads of one stage do not alias the loads still landing in
+// the others.
+//
+// Waves form RG row groups x CG column groups: the CG waves of a row group read
+// the same A fragments, the RG waves of a column group the same weight
+// fragments.  Fragments are 16x16x32 MFMA operands in lane order; weights are
+// pre-packed in that order, A rows are gathered per lane (any row map).
+//
+// float32 activations arrive as two bf16 planes (hi = rn(x), lo = rn(x - hi))
+// written by their producers; both planes are multiplied into the same float32
+// accumulators.
+//
+// With split-K (grid.z > 1) the raw sums go to row-major partial buffers that a
+// row kernel (O, down projections) or launch_dl_finish (QKV, next-layer K/V)
+// adds in split order.  Without split-K the QKV and SwiGLU epilogues run on the
+// accumulators directly.
+#include <utility>
+
+#include "kernels.h"
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define DL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+PS_DEV floatx4_t mfma_bf16(uint4 a, uint4 w, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, w), c,
+                                                 0, 0, 0);
+}
+
+template <int RTW, int RG, int CG, int NSUB, int PL>
+struct DlCfg {
+  static constexpr int NWV = RG * CG;              // waves per workgroup
+  static constexpr int RT = RTW * RG;              // 16-row tiles per workgroup
+  static constexpr int FA = PL * RT;               // A fragments per stage
+  static constexpr int F = FA + CG * NSUB;         // fragments per stage
+  static constexpr int LPW = (F + NWV - 1) / NWV;  // direct loads per wave per stage
+  static constexpr int FP = LPW * NWV;             // fragment slots per stage (with padding)
+  static constexpr int STAGE = FP * 1024;          // bytes
+  static constexpr int P0 = (150 * 1024) / STAGE;
+  static constexpr int P = P0 > 6 ? 6 : P0;        // ring depth
+  static constexpr int NCOL = CG * NSUB * 16;      // columns per workgroup
+  static_assert(P >= 3, "pipeline needs three stages");
+  static_assert(LPW * (P - 2) < 64, "vmcnt range");
+};
+
+template <typename T, int RTW, int RG, int CG, int NSUB, int PL, int KIND>
+__global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
+  using C = DlCfg<RTW, RG, CG, NSUB, PL>;
+  constexpr int NWV = C::NWV, RT = C::RT, FA = C::FA, F = C::F, LPW = C::LPW, FP = C::FP, P = C::P;
+  __shared__ uint4 b0[FP * 64], b1[FP * 64], b2[FP * 64], b3[FP * 64], b4[FP * 64], b5[FP * 64];
+  auto bp = [&](auto I) -> uint4* {
+    if constexpr (I == 0) return b0;
+    else if constexpr (I == 1) return b1;
+    else if constexpr (I == 2) return b2;
+    else if constexpr (I == 3) return b3;
+    else if constexpr (I == 4) return b4;
+    else return b5;
+  };
+  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  int rows_b = g.A.rows(b);
+  if (rows_b > RT * 16) rows_b = RT * 16;
+  if (rows_b <= 0) return;
+  const int nrt = (rows_b + 15) >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = wave / CG, cg = wave % CG;
+  const int k32n = g.K >> 5;
+  const int g0 = (int)((int64_t)k32n * sp / g.ksplit), g1 = (int)((int64_t)k32n * (sp + 1) / g.ksplit);
+  const int n = g1 - g0;
+  const int n16_total = g.N >> 4;
+
+  // Per load slot: source address of this lane at step 0 of the range, and the step stride.
+  const char* src[LPW];
+  int stride[LPW];
+  const uint16_t* Ab = (const uint16_t*)g.A.base + (int64_t)b * g.A.bstride;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    int f = i * NWV + wave;
+    if (f >= F) f = 0;   // padding slot: repeats slot 0's source into its own LDS slot
+    if (f < FA) {
+      const int p = f / RT, rt = f % RT;
+      int r = rt * 16 + (lane & 15);
+      if (r >= rows_b) r = 0;
+      src[i] = (const char*)(Ab + p * g.A.plane_stride + g.A.src_row(b, r) * g.A.lda + (int64_t)g0 * 32 +
+                             8 * (lane >> 4));
+      stride[i] = 64;
+    } else {
+      const int wf = f - FA, c2 = wf / NSUB, sb = wf % NSUB;
+      int n16 = (nt * CG + c2) * NSUB + sb;
+      if (n16 >= n16_total) n16 = nt * CG * NSUB;   // columns past N: re-read a valid subtile, never stored
+      src[i] = (const char*)((const uint4*)g.W + ((int64_t)n16 * k32n + g0) * 64 + lane);
+      stride[i] = 1024;
+    }
+  }
+  auto issue = [&](uint4* buf, int step) {
+    step = step < n ? step : n - 1;   // past the range: reload the last step (unused)
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + (int64_t)step * stride[i]),
+                                       (lds_void*)&buf[(i * NWV + wave) * 64], 16, 0, 0);
+  };
+
+  floatx4_t acc[RTW][NSUB];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint4* buf) {
+    uint4 w[NSUB];
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) w[sb] = buf[(FA + cg * NSUB + sb) * 64 + lane];
+#pragma unroll
+    for (int p = 0; p < PL; ++p)
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        if (rg * RTW + rt < nrt) {
+          const uint4 a = buf[(p * RT + rg * RTW + rt) * 64 + lane];
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma_bf16(a, w[sb], acc[rt][sb]);
+        }
+      }
+  };
+
+  [&]<int... U>(std::integer_sequence<int, U...>) {
+    (issue(bp(std::integral_constant<int, U>{}), U), ...);
+  }(std::make_integer_sequence<int, P - 1>{});
+  for (int s = 0; s < n; s += P) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      ([&] {
+        DL_VMCNT(LPW * (P - 2));          // this wave's loads of stage s+U have landed
+        __builtin_amdgcn_s_barrier();     // ... and everyone's; stage s+U-1 is fully consumed
+        issue(bp(std::integral_constant<int, (U + P - 1) % P>{}), s + U + P - 1);
+        if (s + U < n) compute(bp(std::integral_constant<int, U>{}));
+      }(), ...);
+    }(std::make_integer_sequence<int, P>{});
+  }
+  DL_VMCNT(0);   // no load may land in LDS after the workgroup ends
+
+  // accumulator element (rt, sb, i) of this lane: row r, column n
+  const int col0 = (nt * CG + cg) * NSUB * 16 + (lane & 15);
+  const int row0 = rg * RTW * 16 + 4 * (lane >> 4);
+  if (g.ksplit > 1 || KIND == EPI_PARTIAL) {
+    float* out = g.part + ((int64_t)sp * g.batch + b) * g.part_rows * g.N;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + rt * 16 + i, c = col0 + sb * 16;
+          if (r < rows_b && c < g.N) out[(int64_t)r * g.N + c] = acc[rt][sb][i];
+        }
+    return;
+  }
+  if constexpr (KIND == EPI_QKV || KIND == EPI_KV) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + rt * 16 + i, c = col0 + sb * 16;
+          if (r < rows_b && c < g.N) {
+            if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
+            else epi_kv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
+          }
+        }
+  } else if constexpr (KIND == EPI_SWIGLU) {
+    // subtile pairs (2j, 2j+1) are the gate and up weights of 16 consecutive FFN columns
+    static_assert(NSUB % 2 == 0, "gate/up pairs inside one wave");
+    const EpiParams& e = g.e;
+    const int64_t plane = (int64_t)e.act_rows * e.ffn;
+    uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int j = 0; j < NSUB / 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + rt * 16 + i;
+          const int oc = ((nt * CG + cg) * NSUB / 2 + j) * 16 + (lane & 15);
+          if (r < rows_b && oc < e.ffn) {
+            const float sc = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+            const float gv = acc[rt][2 * j][i] * sc, uv = acc[rt][2 * j + 1][i] * sc;
+            const float a = gv / (1.f + expf(-gv)) * uv;
+            uint16_t hi, lo;
+            split_bf16(a, hi, lo);
+            act[(int64_t)r * e.ffn + oc] = hi;
+            act[plane + (int64_t)r * e.ffn + oc] = lo;
+          }
+        }
+  }
+}
+
+// Split-K finish of the element-wise epilogues: sum the partials in split order.
+template <typename T, int KIND>
+__global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
+  const int r = blockIdx.y, b = blockIdx.z;
+  int rows_b = g.A.rows(b);
+  if (r >= rows_b) return;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (c >= g.N) return;
+  const int64_t sstride = (int64_t)g.batch * g.part_rows * g.N;
+  const float* p = g.part + ((int64_t)b * g.part_rows + r) * g.N + c;
+  float4 v = *(const float4*)p;
+  for (int s = 1; s < g.ksplit; ++s) {
+    const float4 t = *(const float4*)(p + s * sstride);
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, r, c + i, vv[i]);
+    else epi_kv_elem<T>(g.e, b, r, c + i, vv[i]);
+  }
+}
+
+template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
+hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
+  using C = DlCfg<RTW, RG, CG, NSUB, PL>;
+  const dim3 grid(PS_CEIL_DIV(g.N, C::NCOL), g.batch, g.ksplit), block(64 * RG * CG);
+  switch (g.e.kind) {
+    case EPI_PARTIAL: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_PARTIAL>), grid, block, 0, s, g); break;
+    case EPI_QKV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_QKV>), grid, block, 0, s, g); break;
+    case EPI_KV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_KV>), grid, block, 0, s, g); break;
+    case EPI_SWIGLU:
+      if constexpr (PL == 2 && CG == 2) {
+        hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_SWIGLU>), grid, block, 0, s, g);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int dl_tile_cols(int shape) { return shape == DL_WIDE ? 256 : 128; }
+
+template <typename T>
+hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
+  if constexpr (!std::is_same<T, bf16_t>::value) {
+    return hipErrorInvalidValue;
+  } else {
+    if (max_rows <= 0) return hipSuccess;
+    if (g.K % 32 || g.N % 16 || g.ksplit < 1 || g.ksplit > (g.K >> 5)) return hipErrorInvalidValue;
+    if (shape == DL_NARROW) {   // 3 x 2 waves, bf16 rows
+      if (g.planes != 1) return hipErrorInvalidValue;
+      if (max_rows <= 48) return launch_cfg<T, 1, 3, 2, 4, 1>(g, s);
+      if (max_rows <= 96) return launch_cfg<T, 2, 3, 2, 4, 1>(g, s);
+      if (max_rows <= 144) return launch_cfg<T, 3, 3, 2, 4, 1>(g, s);
+      return hipErrorInvalidValue;
+    }
+    if (g.planes != 2) return hipErrorInvalidValue;
+    if (shape == DL_WIDE) {   // 2 x 4 waves, hi/lo planes
+      if (max_rows <= 32) return launch_cfg<T, 1, 2, 4, 4, 2>(g, s);
+      if (max_rows <= 64) return launch_cfg<T, 2, 2, 4, 4, 2>(g, s);
+      if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 4, 2>(g, s);
+      if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 4, 2>(g, s);
+      if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 4, 2>(g, s);
+      return hipErrorInvalidValue;
+    }
+    if (shape == DL_MID) {    // 2 x 2 waves, hi/lo planes
+      if (max_rows <= 32) return launch_cfg<T, 1, 2, 2, 4, 2>(g, s);
+      if (max_rows <= 64) return launch_cfg<T, 2, 2, 2, 4, 2>(g, s);
+      if (max_rows <= 96) return launch_cfg<T, 3, 2, 2, 4, 2>(g, s);
+      if (max_rows <= 128) return launch_cfg<T, 4, 2, 2, 4, 2>(g, s);
+      if (max_rows <= 160) return launch_cfg<T, 5, 2, 2, 4, 2>(g, s);
+      return hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_dl_finish(const DlArgs& g, int max_rows, hipStream_t s) {
+  if (max_rows <= 0 || g.ksplit <= 1) return hipSuccess;
+  if (g.N % 4) return hipErrorInvalidValue;
+  const dim3 grid(PS_CEIL_DIV(g.N, 1024), max_rows, g.batch);
+  if (g.e.kind == EPI_QKV) hipLaunchKernelGGL((dl_finish_kernel<T, EPI_QKV>), grid, dim3(256), 0, s, g);
+  else if (g.e.kind == EPI_KV) hipLaunchKernelGGL((dl_finish_kernel<T, EPI_KV>), grid, dim3(256), 0, s, g);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template hipError_t launch_dl<float>(const DlArgs&, int, int, hipStream_t);
+template hipError_t launch_dl<bf16_t>(const DlArgs&, int, int, hipStream_t);
+template hipError_t launch_dl_finish<float>(const DlArgs&, int, hipStream_t);
+template hipError_t launch_dl_finish<bf16_t>(const DlArgs&, int, hipStream_t);

@@ -4,7 +4,7 @@
 
 // Handle contents (host only).
 struct WsLayout {
-  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat,
+  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat, hp_pl,
       lm_a, lm_inv, lm_stats, lm_meta, total;
 };
 
@@ -18,7 +18,8 @@ struct polestar_handle {
   int32_t mq;        // QKV rows per sequence: B + win_max + K
   int32_t mt;        // token rows per sequence: B + win_max
   int32_t nq, nkv;   // Hq*dh, Hkv*dh
-  int32_t ksplit;    // split-K factor of the N = d projections
+  int32_t ksplit;    // split-K factor of the N = d projections (float32 path)
+  int32_t ks_qkv, ks_o, ks_down, ks_kv;   // split-K factors of the bf16 projections
   int32_t lm_tiles;  // vocab / 64 rounded up
   WsLayout ws;
   polestar_check chk;
@@ -31,6 +32,7 @@ struct polestar_handle {
 struct GemmA {
   const void* base;
   int32_t f32;           // rows are float32 (bf16 path: fed to MFMA as a hi + lo bf16 pair)
+  int64_t plane_stride;  // bf16 plane layout: elements from the hi plane to the lo plane
   int64_t bstride;       // elements between sequences
   int32_t lda;           // elements between rows
   const int32_t* rowmap;
@@ -85,8 +87,78 @@ struct EpiParams {
   float* lm_stats; int32_t lm_rows, lm_tiles, vocab, mask_id;
 };
 
+// Cache element of position pos, K/V column col (= kv head * dh + d):
+// K token-major [b][n][Hkv][dh]; V transposed [b][Hkv][dh][n].
+PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
+  if (!is_v) return ((int64_t)b * e.n_pos + pos) * e.nkv + col;
+  return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
+}
+
+// QKV projection row r (active block, window rows, centroids), column n, raw sum v:
+// queries stay float32; K/V of the active block and of patched window rows go to the cache.
+template <typename T>
+PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
+  v *= e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+  if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
+  if (n < e.nq) {
+    e.q[((int64_t)b * e.q_rows + r) * e.nq + n] = v;
+    return;
+  }
+  const int kv = n - e.nq;
+  const int which = kv >= e.nkv;
+  const int col = kv - which * e.nkv;
+  int pos = -1;
+  if (r < e.block) {
+    pos = e.geom.blk_start + r;
+  } else {
+    const int w = r - e.block;
+    if (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) pos = e.geom.pos(w);
+  }
+  if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
+}
+
+// K/V of the next layer for packet row r (window row sel_idx[r]).
+template <typename T>
+PS_DEV void epi_kv_elem(const EpiParams& e, int b, int r, int n, float v) {
+  v *= e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+  if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
+  const int which = n >= e.nkv;
+  const int col = n - which * e.nkv;
+  const int w = e.sel_idx[(int64_t)b * e.win_max + r];
+  if (w < 0 || w >= e.geom.n_win) return;
+  St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, e.geom.pos(w), col, which), v);
+}
+
+// float32 -> bf16 hi/lo pair: hi = rn(x), lo = rn(x - hi); hi + lo keeps ~16 significant bits.
+PS_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
 template <typename T>
 hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s);
+
+// ---- bf16 weight-streaming projection (gemm_dl.hip) ------------------------------------
+// A: bf16 planes (1 = bf16 rows, 2 = hi/lo of float32 rows), rows gathered per lane.
+// ksplit > 1: raw sums to part[((s*batch + b)*part_rows + r)*N + n], finished by
+// launch_dl_finish (QKV, KV) or the row reduction (O, down).
+struct DlArgs {
+  GemmA A;
+  int32_t planes;
+  const void* W;
+  int32_t N, K, batch, ksplit;
+  float* part;
+  int32_t part_rows;
+  EpiParams e;
+};
+enum DlShape { DL_NARROW = 0,   // 3 row groups x 2 column groups x 64 columns: 128-column tiles
+               DL_WIDE = 1,     // 2 row groups x 4 column groups: 256-column tiles
+               DL_MID = 2 };    // 2 row groups x 2 column groups: 128-column tiles
+int dl_tile_cols(int shape);
+template <typename T>
+hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s);
+template <typename T>
+hipError_t launch_dl_finish(const DlArgs& g, int max_rows, hipStream_t s);
 template <typename T>
 hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s);
 size_t packed_elems(int N, int K);
@@ -106,6 +178,8 @@ struct RowReduceArgs {
   void* out_a; int64_t out_a_bstride; int32_t out_split;
   void* out_b; int64_t out_b_bstride;
   int32_t out_f32;              // outputs are float32 rows (else storage dtype)
+  uint16_t* out_pl;             // also the bf16 hi/lo planes of out_a rows (or null)
+  int64_t pl_bstride, pl_stride;
   float* inv_rms; int32_t inv_bstride;
   float eps;
   float* chk; int32_t chk_rows;
@@ -151,7 +225,8 @@ struct AttnArgs {
   int32_t block;
   const float* q;         // [batch][mq][hq*dh]
   const void* kc; const void* vc;
-  void* o;                // [batch][mt][hq*dh] float32
+  void* o;                // [batch][mt][hq*dh] float32, or bf16 hi/lo planes [batch][2][mt][hq*dh]
+  int32_t o_planes;
   float* proxy_logits;    // [batch][K][hq][n]
   float* kl;              // [batch][K][hq]
   float* act_logits;      // [batch][block][hq][n] or null
