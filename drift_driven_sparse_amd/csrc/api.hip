@@ -77,6 +77,7 @@ void layout(polestar_handle* h) {
     part = std::max(part, (size_t)h->ks_qkv * Bt * h->mq * nqkv);
     part = std::max(part, (size_t)h->ks_o * Bt * h->mt * d.d);
     part = std::max(part, (size_t)h->ks_down * Bt * h->mt * d.d);
+    part = std::max(part, (size_t)h->ks_gu * Bt * h->mt * 2 * (size_t)d.ffn);
     part = std::max(part, (size_t)h->ks_kv * Bt * h->win_max * 2 * (size_t)h->nkv);
   }
   w.part = take(part * 4);
@@ -395,7 +396,9 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.N = 2 * d.ffn;
   dl.K = d.d;
   dl.batch = d.batch;
-  dl.ksplit = 1;
+  dl.ksplit = h->ks_gu;
+  dl.part = part;
+  dl.part_rows = h->mt;
   dl.e.kind = EPI_SWIGLU;
   dl.e.inv_rms = rr.inv_rms;
   dl.e.inv_bstride = h->mt;
@@ -404,7 +407,12 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.e.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
-    e = launch_dl<T>(dl, DL_MID, max_rows, s);
+    if (dl.ksplit > 1) {
+      e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
+      if (e == hipSuccess) e = launch_dl_finish<T>(dl, max_rows, s);
+    } else {
+      e = launch_dl<T>(dl, DL_MID, max_rows, s);
+    }
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 3. out = h' + act W_down^T -> next active rows and the update packet
@@ -835,6 +843,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   };
   h->ks_qkv = ks_for(h->nq + 2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 8);
   h->ks_o = ks_for(d.d, dl_tile_cols(DL_WIDE), h->nq, 16);
+  h->ks_gu = ks_for(2 * d.ffn, dl_tile_cols(DL_WIDE), d.d, 4);
   h->ks_down = ks_for(d.d, dl_tile_cols(DL_WIDE), d.ffn, 16);
   h->ks_kv = ks_for(2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 16);
   h->lm_tiles = PS_CEIL_DIV(d.vocab, 64);

@@ -20,8 +20,8 @@
 // accumulators.
 //
 // With split-K (grid.z > 1) the raw sums go to row-major partial buffers that a
-// row kernel (O, down projections) or launch_dl_finish (QKV, next-layer K/V)
-// adds in split order.  Without split-K the QKV and SwiGLU epilogues run on the
+// row kernel (O, down projections) or launch_dl_finish (QKV, gate/up, next-layer
+// K/V) adds in split order.  Without split-K the QKV and SwiGLU epilogues run on the
 // accumulators directly.
 #include <utility>
 
@@ -227,6 +227,38 @@ __global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
   }
 }
 
+// Split-K finish of the gate/up projection: output column oc takes gate column
+// 32*(oc/16) + oc%16 and the up column 16 after it (16-column groups interleaved).
+__global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
+  const int r = blockIdx.y, b = blockIdx.z;
+  int rows_b = g.A.rows(b);
+  if (r >= rows_b) return;
+  const EpiParams& e = g.e;
+  const int oc = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (oc >= e.ffn) return;
+  const int cg = (oc >> 4) * 32 + (oc & 15);
+  const int64_t sstride = (int64_t)g.batch * g.part_rows * g.N;
+  const float* p = g.part + ((int64_t)b * g.part_rows + r) * g.N + cg;
+  float4 gv = *(const float4*)p, uv = *(const float4*)(p + 16);
+  for (int s = 1; s < g.ksplit; ++s) {
+    const float4 tg = *(const float4*)(p + s * sstride), tu = *(const float4*)(p + s * sstride + 16);
+    gv.x += tg.x; gv.y += tg.y; gv.z += tg.z; gv.w += tg.w;
+    uv.x += tu.x; uv.y += tu.y; uv.z += tu.z; uv.w += tu.w;
+  }
+  const float sc = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+  const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
+  const int64_t plane = (int64_t)e.act_rows * e.ffn;
+  uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane + (int64_t)r * e.ffn + oc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = ga[i] * sc, u = ua[i] * sc;
+    uint16_t hi, lo;
+    split_bf16(x / (1.f + expf(-x)) * u, hi, lo);
+    act[i] = hi;
+    act[plane + i] = lo;
+  }
+}
+
 template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
 hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
   using C = DlCfg<RTW, RG, CG, NSUB, PL>;
@@ -236,7 +268,7 @@ hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
     case EPI_QKV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_QKV>), grid, block, 0, s, g); break;
     case EPI_KV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_KV>), grid, block, 0, s, g); break;
     case EPI_SWIGLU:
-      if constexpr (PL == 2 && CG == 2) {
+      if constexpr (PL == 2) {
         hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_SWIGLU>), grid, block, 0, s, g);
         break;
       }
@@ -289,6 +321,11 @@ template <typename T>
 hipError_t launch_dl_finish(const DlArgs& g, int max_rows, hipStream_t s) {
   if (max_rows <= 0 || g.ksplit <= 1) return hipSuccess;
   if (g.N % 4) return hipErrorInvalidValue;
+  if (g.e.kind == EPI_SWIGLU) {
+    if (g.e.ffn % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dl_finish_swiglu_kernel, dim3(PS_CEIL_DIV(g.e.ffn, 1024), max_rows, g.batch), dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
   const dim3 grid(PS_CEIL_DIV(g.N, 1024), max_rows, g.batch);
   if (g.e.kind == EPI_QKV) hipLaunchKernelGGL((dl_finish_kernel<T, EPI_QKV>), grid, dim3(256), 0, s, g);
   else if (g.e.kind == EPI_KV) hipLaunchKernelGGL((dl_finish_kernel<T, EPI_KV>), grid, dim3(256), 0, s, g);

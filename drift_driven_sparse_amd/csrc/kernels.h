@@ -19,7 +19,7 @@ struct polestar_handle {
   int32_t mt;        // token rows per sequence: B + win_max
   int32_t nq, nkv;   // Hq*dh, Hkv*dh
   int32_t ksplit;    // split-K factor of the N = d projections (float32 path)
-  int32_t ks_qkv, ks_o, ks_down, ks_kv;   // split-K factors of the bf16 projections
+  int32_t ks_qkv, ks_o, ks_gu, ks_down, ks_kv;   // split-K factors of the bf16 projections
   int32_t lm_tiles;  // vocab / 64 rounded up
   WsLayout ws;
   polestar_check chk;
