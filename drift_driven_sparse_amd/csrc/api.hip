@@ -83,6 +83,9 @@ void layout(polestar_handle* h) {
   w.part = take(part * 4);
   w.hp = take(Bt * h->mt * d.d * 4);
   w.hp_pl = take(d.dtype == POLESTAR_BF16 ? Bt * 2 * h->mt * d.d * 2 : 0);
+  w.attn_part = take(d.dtype == POLESTAR_BF16 && h->attn_nchunks > 1
+                         ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->mt * (d.head_dim + 2) * 4
+                         : 0);
   w.inv_hp = take(Bt * h->mt * 4);
   w.act = take(Bt * h->mt * (size_t)d.ffn * 4);
   w.inv_out = take(Bt * h->mt * 4);
@@ -275,11 +278,16 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.act_kl = delta != nullptr;
   at_.akl = at<float>(ws, h->ws.akl);
   at_.lg_stage = at<float>(ws, h->ws.lg);
+  at_.chunk_keys = h->attn_chunk;
+  at_.n_chunks = h->attn_nchunks;
+  at_.part_o = at<float>(ws, h->ws.attn_part);
+  at_.part_ml = at_.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * h->mt * d.head_dim;
   at_.chk = h->chk.attn_out;
   at_.chk_rows = h->mt;
   {
     PROF(POLESTAR_K_ATTN);
     e = launch_attention<T>(at_, s);
+    if (e == hipSuccess && std::is_same<T, bf16_t>::value) e = launch_attn_merge(at_, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   {
@@ -806,7 +814,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   if (d.n_pos > 1024) return POLESTAR_E_UNSUPPORTED;
   if (d.d % 16 != 0) return POLESTAR_E_UNSUPPORTED;
   if (d.dtype == POLESTAR_BF16) {
-    if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16 || d.n_pos % 4)
+    if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16 || d.n_pos % 4 || d.n_pos < 8)
       return POLESTAR_E_UNSUPPORTED;
   } else {
     if (d.ffn % 4 || d.d % 4) return POLESTAR_E_UNSUPPORTED;
@@ -846,6 +854,16 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->ks_gu = ks_for(2 * d.ffn, dl_tile_cols(DL_WIDE), d.d, 4);
   h->ks_down = ks_for(d.d, dl_tile_cols(DL_WIDE), d.ffn, 16);
   h->ks_kv = ks_for(2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 16);
+  // bf16 attention: split the keys so that about 256 workgroups run, at least 128 keys each
+  {
+    const int blocks32 = PS_CEIL_DIV(d.n_pos, 32);
+    int want = 256 / (d.n_heads * d.batch);
+    want = want < 1 ? 1 : want;
+    const int max_chunks = PS_CEIL_DIV(d.n_pos, 128);
+    want = want > max_chunks ? max_chunks : want;
+    h->attn_chunk = 32 * PS_CEIL_DIV(blocks32, want);
+    h->attn_nchunks = PS_CEIL_DIV(d.n_pos, h->attn_chunk);
+  }
   h->lm_tiles = PS_CEIL_DIV(d.vocab, 64);
   layout(h);
   *out = h;

@@ -5,17 +5,15 @@
 // Cache layouts: K token-major [batch][n][Hkv][dh]; V transposed
 // [batch][Hkv][dh][n] so that V^T fragments are contiguous along keys.
 //
-// bf16 path (attn_mfma_kernel): one workgroup = 32 query rows (two 16-row MFMA
-// tiles) of one head; its four waves split the keys into interleaved 32-key
-// blocks.  Per block a wave computes S^T = K Q^T with MFMA 16x16x32 (the
-// float32 queries as a bf16 hi + lo pair), keeps an online softmax per row, and
-// accumulates O^T += V^T P^T (probabilities as a bf16 hi + lo pair), so the
-// result carries float32-level accuracy.  The four partial
-// (max, sum, O) states are merged in LDS.  Logits of proxy rows and (when
-// requested) active rows go to a staging buffer; kl_kernel then forms the KL
-// drift against the previous logits and replaces them.
+// bf16 path (attn_chunk_kernel): workgroups over (key chunk, head); MFMA 16x16x32 with the
+// float32 queries and the probabilities as bf16 hi + lo pairs, online softmax per chunk, and
+// attn_merge_kernel combining the chunks.  Logits of proxy rows and (when requested) active rows
+// go to a staging buffer; kl_kernel then forms the KL drift against the previous logits and
+// replaces them.
 //
 // float32 path (attn_f32_kernel, small models): LDS-staged vector FMA.
+#include <utility>
+
 #include "kernels.h"
 
 namespace {
@@ -38,120 +36,156 @@ PS_DEV int stage_row(const AttnArgs& a, int row) {   // staging buffer row: [pro
   return row >= a.n_tok ? row - a.n_tok : a.n_proxy + row;
 }
 
-// ---- bf16 MFMA attention --------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int DT = DH / 16;      // dh tiles of the output
-  constexpr int KS = DH / 32;      // k-steps of S^T = K Q^T
-  __shared__ float sm_o[4][16][DH + 1];
-  __shared__ float sm_m[4][16], sm_l[4][16];
+// ---- bf16 MFMA attention over key chunks ------------------------------------------------------
+// Workgroup = (key chunk, query head, sequence); its four waves split the 16-row query tiles
+// (RTW tiles each) and share the chunk's K and V^T, which stream through a four-stage LDS ring
+// in 32-key steps (direct global -> LDS loads, one fragment per load instruction).
+//
+// S^T = K Q^T per 16-key tile with the keys of the A operand permuted so that lane l ends up
+// holding the 8 consecutive keys 8(l/16)..+8 of the step for query row l%16: A row m of tile kt
+// is key 8(m/4) + 4kt + m%4.  The probabilities then form the B operand of O^T += V^T P^T
+// directly, and a V^T fragment is one 16-byte load per lane.  n_pos is a multiple of 4 only, so
+// the last 8-key group can hold 4 keys: its lanes load V^T from n-8 and shift their
+// probabilities by 4 positions to match.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+#define AT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-  const int n = a.n_pos;
-  const int rg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int nrows = a.n_tok + a.n_proxy;
-  const int r0 = rg * 32;
+PS_DEV uint4 frag_hi(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack2(x[2 * e], x[2 * e + 1]);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+PS_DEV uint4 frag_lo(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = pack2(x[2 * e] - bf16_to_f32(f32_to_bf16(x[2 * e])), x[2 * e + 1] - bf16_to_f32(f32_to_bf16(x[2 * e + 1])));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int DH, int RTW>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
+  constexpr int KS = DH / 32, DT = DH / 16;
+  constexpr int FK = 2 * KS, F = FK + DT;   // K and V^T fragments per 32-key step
+  constexpr int LPW = F / 4;                // loads per wave per step
+  static_assert(F % 4 == 0, "fragments per wave");
+  __shared__ uint4 b0[F * 64], b1[F * 64], b2[F * 64], b3[F * 64];
+  auto bp = [&](auto I) -> uint4* {
+    if constexpr (I == 0) return b0;
+    else if constexpr (I == 1) return b1;
+    else if constexpr (I == 2) return b2;
+    else return b3;
+  };
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = a.n_pos, nrows = a.n_tok + a.n_proxy;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int kvh = (h * a.hkv) / a.hq;
+  const int k0 = chunk * a.chunk_keys;
+  const int k1 = min(n, k0 + a.chunk_keys);
+  const int nst = (k1 - k0 + 31) >> 5;
   const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)b * n * a.hkv * DH + kvh * DH;
   const uint16_t* vt = (const uint16_t*)a.vc + ((int64_t)b * a.hkv + kvh) * DH * n;
   const float scale = 1.f / sqrtf((float)DH);
-  const int nblk = (n + 31) >> 5;
 
-  // query fragments (B operand of S^T): lane holds row c16, dh [32 ks + 8 g4, +8)
-  uint4 qhi[2][KS], qlo[2][KS];
-  bool keep[2];
+  // this lane's source for load slot i of a step starting at key0
+  auto issue = [&](uint4* buf, int step) __attribute__((always_inline)) {
+    step = step < nst ? step : nst - 1;
+    const int key0 = k0 + 32 * step;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = r0 + rt * 16 + c16;
+    for (int i = 0; i < LPW; ++i) {
+      const int f = i * 4 + wave;
+      const uint16_t* src;
+      if (f < FK) {
+        const int kt = f / KS, ks = f % KS;
+        int key = key0 + 8 * (c16 >> 2) + 4 * kt + (c16 & 3);
+        key = key < n ? key : n - 1;
+        src = kc + (int64_t)key * a.hkv * DH + 32 * ks + 8 * g4;
+      } else {
+        int kg = key0 + 8 * g4;
+        kg = kg + 8 <= n ? kg : n - 8;
+        src = vt + (int64_t)(16 * (f - FK) + c16) * n + kg;
+      }
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)&buf[f * 64], 16, 0, 0);
+    }
+  };
+
+  // query fragments (B operand of S^T): lane holds row c16 of each tile, dh [32 ks + 8 g4, +8)
+  uint4 qhi[RTW][KS], qlo[RTW][KS];
+  bool tile_on[RTW];
+  auto load_q = [&](auto Tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(Tc)::value;
+    const int tile = wave * RTW + t;
+    tile_on[t] = tile * 16 < nrows;
+    const int row = tile * 16 + c16;
     const bool valid = row < nrows;
-    bool kp = false;
-    for (int i = 0; i < 16; ++i) kp |= (r0 + rt * 16 + i < nrows) && row_keeps_logits(a, r0 + rt * 16 + i);
-    keep[rt] = kp;
     const float* qr = a.q + ((int64_t)b * a.mq + (valid ? row : 0)) * (a.hq * DH) + h * DH + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = valid ? qr[32 * ks + e] : 0.f;
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(x[2 * e]), h1 = f32_to_bf16(x[2 * e + 1]);
-        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[e] = pack2(x[2 * e] - bf16_to_f32(h0), x[2 * e + 1] - bf16_to_f32(h1));
-      }
-      qhi[rt][ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      qlo[rt][ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      qhi[t][ks] = frag_hi(x);
+      qlo[t][ks] = frag_lo(x);
     }
+  };
+  [&]<int... T>(std::integer_sequence<int, T...>) {
+    (load_q(std::integral_constant<int, T>{}), ...);
+  }(std::make_integer_sequence<int, RTW>{});
+  floatx4_t o[RTW][DT];
+  float m_run[RTW], l_run[RTW];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const bool any_rows1 = r0 + 16 < nrows;
 
-  floatx4_t o[2][DT];
+  auto compute = [&](const uint4* buf, int step) __attribute__((always_inline)) {
+    const int key0 = k0 + 32 * step;
+    const int kg = key0 + 8 * g4;            // first key of this lane's 8-key group
+    const bool shift = kg < n && kg + 8 > n; // ragged tail: V^T was loaded from n - 8
+    auto tile_step = [&](auto Tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(Tc)::value;
+      if (!tile_on[t]) return;
+      floatx4_t sacc[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  for (int blk = wave; blk < nblk; blk += 4) {
-    const int key0 = blk * 32;
-    // S^T tiles [kt][rt]: lane holds keys key0 + 16 kt + 4 g4 + i (i < 4), row c16
-    floatx4_t s[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      int key = key0 + 16 * kt + c16;
-      key = key < n ? key : n - 1;
-      const uint16_t* kr = kc + (int64_t)key * a.hkv * DH + 8 * g4;
-      uint4 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const uint4*)(kr + 32 * ks);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int kt = 0; kt < 2; ++kt) {
         floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        if (rt == 0 || any_rows1) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            acc = mfma(kf[ks], qhi[rt][ks], acc);
-            acc = mfma(kf[ks], qlo[rt][ks], acc);
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 kf = buf[(kt * KS + ks) * 64 + lane];
+          acc = mfma(kf, qhi[t][ks], acc);
+          acc = mfma(kf, qlo[t][ks], acc);
         }
-        s[kt][rt] = acc;
+        sacc[kt] = acc;
       }
-    }
-    // scale, mask, stage kept logits, online softmax, P^T fragments
-    uint4 pf[2], pl[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
       float v[8];
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * kt + 4 * g4 + i;
-          const float x = key < n ? s[kt][rt][i] * scale : -INFINITY;
-          v[kt * 4 + i] = x;
-          mx = fmaxf(mx, x);
-        }
-      const int row = r0 + rt * 16 + c16;
-      if (keep[rt] && row < nrows && row_keeps_logits(a, row)) {
-        float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int key = key0 + 16 * kt + 4 * g4;
-          if (key + 3 < n) {
-            *(float4*)(lg + key) = make_float4(v[kt * 4], v[kt * 4 + 1], v[kt * 4 + 2], v[kt * 4 + 3]);
-          } else {
-            for (int i = 0; i < 4; ++i)
-              if (key + i < n) lg[key + i] = v[kt * 4 + i];
-          }
+      for (int e = 0; e < 8; ++e) {
+        const float x = kg + e < k1 ? sacc[e >> 2][e & 3] * scale : -INFINITY;
+        v[e] = x;
+        mx = fmaxf(mx, x);
+      }
+      const int row = (wave * RTW + t) * 16 + c16;
+      if (row < nrows && row_keeps_logits(a, row)) {
+        float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n + kg;
+        if (kg + 8 <= k1) {
+          *(float4*)lg = make_float4(v[0], v[1], v[2], v[3]);
+          *(float4*)(lg + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (kg + e < k1) lg[e] = v[e];
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[rt], mx);
-      const float corr = m_run[rt] == -INFINITY ? 0.f : expf(m_run[rt] - m_new);
+      const float m_new = fmaxf(m_run[t], mx);
+      const float corr = m_run[t] == -INFINITY ? 0.f : expf(m_run[t] - m_new);
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -160,80 +194,101 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l_run[rt] = l_run[rt] * corr + ps;
-      m_run[rt] = m_new;
+      l_run[t] = l_run[t] * corr + ps;
+      m_run[t] = m_new;
+      if (shift) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= corr;
-      uint32_t hi[4], lo[4];
+        for (int e = 7; e >= 4; --e) v[e] = v[e - 4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(v[2 * e]), h1 = f32_to_bf16(v[2 * e + 1]);
-        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[e] = pack2(v[2 * e] - bf16_to_f32(h0), v[2 * e + 1] - bf16_to_f32(h1));
+        for (int e = 0; e < 4; ++e) v[e] = 0.f;
       }
-      pf[rt] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      pl[rt] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-    // V^T fragments: lane holds dh row 16 dt + c16, keys {key0 + 4 g4 + i} U {key0 + 16 + 4 g4 + i};
-    // key chunks at or past n (their probabilities are 0) re-read chunk 0
-    int ka = key0 + 4 * g4, kb = key0 + 16 + 4 * g4;
-    ka = ka < n ? ka : 0;
-    kb = kb < n ? kb : 0;
+      const uint4 phi = frag_hi(v), plo = frag_lo(v);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vr = vt + (int64_t)(16 * dt + c16) * n;
-      const uint2 va = *(const uint2*)(vr + ka), vb = *(const uint2*)(vr + kb);
-      const uint4 vf = make_uint4(va.x, va.y, vb.x, vb.y);
-      o[0][dt] = mfma(vf, pf[0], o[0][dt]);
-      o[0][dt] = mfma(vf, pl[0], o[0][dt]);
-      if (any_rows1) {
-        o[1][dt] = mfma(vf, pf[1], o[1][dt]);
-        o[1][dt] = mfma(vf, pl[1], o[1][dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        o[t][dt] *= corr;
+        const uint4 vf = buf[(FK + dt) * 64 + lane];
+        o[t][dt] = mfma(vf, phi, o[t][dt]);
+        o[t][dt] = mfma(vf, plo, o[t][dt]);
       }
-    }
+    };
+    [&]<int... T>(std::integer_sequence<int, T...>) {
+      (tile_step(std::integral_constant<int, T>{}), ...);
+    }(std::make_integer_sequence<int, RTW>{});
+  };
+
+  issue(b0, 0);
+  issue(b1, 1);
+  issue(b2, 2);
+  for (int s = 0; s < nst; s += 4) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      ([&] {
+        AT_VMCNT(LPW * 2);
+        __builtin_amdgcn_s_barrier();
+        issue(bp(std::integral_constant<int, (U + 3) % 4>{}), s + U + 3);
+        if (s + U < nst) compute(bp(std::integral_constant<int, U>{}), s + U);
+      }(), ...);
+    }(std::make_integer_sequence<int, 4>{});
   }
-  // merge the four waves' partial states, one 16-row tile at a time
-  const int n_out = min(32, a.n_tok - r0);   // token rows of this workgroup that produce outputs
+  AT_VMCNT(0);
+
+  // outputs of token rows: lane holds O^T[16 dt + 4 g4 + i][row c16]
+  auto store_tile = [&](auto Tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(Tc)::value;
+    const int row = (wave * RTW + t) * 16 + c16;
+    if (!tile_on[t] || row >= a.n_tok) return;
+    if (a.n_chunks == 1) {
+      const float inv = 1.f / l_run[t];
+      const int64_t plane = (int64_t)a.mt * a.hq * DH;
+      uint16_t* op = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    if (rt == 1 && !any_rows1) break;
-    __syncthreads();
-    if (g4 == 0) {
-      sm_m[wave][c16] = m_run[rt];
-      sm_l[wave][c16] = l_run[rt];
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dd = 16 * dt + 4 * g4 + i;
+          const float val = o[t][dt][i] * inv;
+          uint16_t hi, lo;
+          split_bf16(val, hi, lo);
+          op[dd] = hi;
+          op[plane + dd] = lo;
+          if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + dd] = val;
+        }
+    } else {
+      const int64_t slot = (((int64_t)b * a.n_chunks + chunk) * a.hq + h) * a.mt + row;
+      float* po = a.part_o + slot * DH;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *(float4*)(po + 16 * dt + 4 * g4) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
+      if (g4 == 0) *(float2*)(a.part_ml + slot * 2) = make_float2(m_run[t], l_run[t]);
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[wave][c16][16 * dt + 4 * g4 + i] = o[rt][dt][i];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * DH; idx += blockDim.x) {
-      const int rr = idx / DH, dd = idx % DH;
-      const int lrow = rt * 16 + rr;
-      if (lrow >= n_out) continue;
-      float M = -INFINITY;
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][rr]);
-      float num = 0.f, den = 0.f;
-      for (int w = 0; w < 4; ++w) {
-        const float f = sm_m[w][rr] == -INFINITY ? 0.f : expf(sm_m[w][rr] - M);
-        num += f * sm_o[w][rr][dd];
-        den += f * sm_l[w][rr];
-      }
-      const float val = num / den;
-      const int row = r0 + lrow;
-      if (a.o_planes) {
-        const int64_t plane = (int64_t)a.mt * a.hq * DH;
-        uint16_t hi, lo;
-        split_bf16(val, hi, lo);
-        uint16_t* o = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH + dd;
-        o[0] = hi;
-        o[plane] = lo;
-      } else {
-        ((float*)a.o)[((int64_t)b * a.mt + row) * (a.hq * DH) + h * DH + dd] = val;
-      }
-      if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + dd] = val;
-    }
+  };
+  [&]<int... T>(std::integer_sequence<int, T...>) {
+    (store_tile(std::integral_constant<int, T>{}), ...);
+  }(std::make_integer_sequence<int, RTW>{});
+}
+
+// Merge of the per-chunk states of one (token row, head): o = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+template <int DH>
+__global__ __launch_bounds__(DH) void attn_merge_kernel(AttnArgs a) {
+  const int row = blockIdx.x, h = blockIdx.y, b = blockIdx.z, dd = threadIdx.x;
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunks; ++c)
+    M = fmaxf(M, a.part_ml[((((int64_t)b * a.n_chunks + c) * a.hq + h) * a.mt + row) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const int64_t slot = (((int64_t)b * a.n_chunks + c) * a.hq + h) * a.mt + row;
+    const float m = a.part_ml[slot * 2], l = a.part_ml[slot * 2 + 1];
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    num += f * a.part_o[slot * DH + dd];
+    den += f * l;
   }
+  const float val = num / den;
+  const int64_t plane = (int64_t)a.mt * a.hq * DH;
+  uint16_t* op = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH + dd;
+  uint16_t hi, lo;
+  split_bf16(val, hi, lo);
+  op[0] = hi;
+  op[plane] = lo;
+  if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + dd] = val;
 }
 
 // ---- float32 attention (small models) ----------------------------------------------------------
@@ -444,11 +499,39 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     else if (a.dh == 128) hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(256), sm, s, a);
     else return hipErrorInvalidValue;
   } else {
-    dim3 grid(PS_CEIL_DIV(nrows, 32), a.hq, a.batch);
-    if (a.dh == 64) hipLaunchKernelGGL((attn_mfma_kernel<64>), grid, dim3(256), 0, s, a);
-    else if (a.dh == 128) hipLaunchKernelGGL((attn_mfma_kernel<128>), grid, dim3(256), 0, s, a);
-    else return hipErrorInvalidValue;
+    const int tiles = PS_CEIL_DIV(nrows, 16);
+    const int rtw = PS_CEIL_DIV(tiles, 4);
+    if (rtw > 3 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos) return hipErrorInvalidValue;
+    dim3 grid(a.n_chunks, a.hq, a.batch);
+    auto go = [&](auto DHc, auto RTWc) {
+      hipLaunchKernelGGL((attn_chunk_kernel<decltype(DHc)::value, decltype(RTWc)::value>), grid, dim3(256), 0, s, a);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
+    using R3 = std::integral_constant<int, 3>;
+    if (a.dh == 64) {
+      if (rtw == 1) go(I64{}, R1{});
+      else if (rtw == 2) go(I64{}, R2{});
+      else go(I64{}, R3{});
+    } else if (a.dh == 128) {
+      if (rtw == 1) go(I128{}, R1{});
+      else if (rtw == 2) go(I128{}, R2{});
+      else go(I128{}, R3{});
+    } else {
+      return hipErrorInvalidValue;
+    }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
+  if (a.n_chunks <= 1 || a.n_tok <= 0) return hipSuccess;
+  const dim3 grid(a.n_tok, a.hq, a.batch);
+  if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(64), 0, s, a);
+  else if (a.dh == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(128), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@
 
 // Handle contents (host only).
 struct WsLayout {
-  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat, hp_pl,
+  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat, hp_pl, attn_part,
       lm_a, lm_inv, lm_stats, lm_meta, total;
 };
 
@@ -20,6 +20,7 @@ struct polestar_handle {
   int32_t nq, nkv;   // Hq*dh, Hkv*dh
   int32_t ksplit;    // split-K factor of the N = d projections (float32 path)
   int32_t ks_qkv, ks_o, ks_gu, ks_down, ks_kv;   // split-K factors of the bf16 projections
+  int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
   int32_t lm_tiles;  // vocab / 64 rounded up
   WsLayout ws;
   polestar_check chk;
@@ -231,12 +232,17 @@ struct AttnArgs {
   float* kl;              // [batch][K][hq]
   float* act_logits;      // [batch][block][hq][n] or null
   float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
+  int32_t chunk_keys;     // bf16 path: keys per workgroup (multiple of 32)
+  int32_t n_chunks;       // workgroups along the keys; > 1 -> partial states merged by launch_attn_merge
+  float* part_o;          // [batch][n_chunks][hq][mt][dh] unnormalised outputs of token rows
+  float* part_ml;         // [batch][n_chunks][hq][mt][2] running max and sum
   int32_t act_kl;         // compute active-row KL against act_logits before overwrite
   float* akl;             // [batch][block][hq]
   float* chk; int32_t chk_rows;
 };
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_kl(const AttnArgs& a, hipStream_t s);
 
 struct TopkArgs {
