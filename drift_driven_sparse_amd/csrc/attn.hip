@@ -37,9 +37,9 @@ PS_DEV int stage_row(const AttnArgs& a, int row) {   // staging buffer row: [pro
 }
 
 // ---- bf16 MFMA attention over key chunks ------------------------------------------------------
-// Workgroup = (key chunk, query head, sequence); its four waves split the 16-row query tiles
-// (RTW tiles each) and share the chunk's K and V^T, which stream through a four-stage LDS ring
-// in 32-key steps (direct global -> LDS loads, one fragment per load instruction).
+// Workgroup = (key chunk, query head, sequence); each of its NWV waves owns one 16-row query
+// tile, and all share the chunk's K and V^T, which stream through a four-stage LDS ring in
+// 32-key steps (direct global -> LDS loads, one fragment per load instruction).
 //
 // S^T = K Q^T per 16-key tile with the keys of the A operand permuted so that lane l ends up
 // holding the 8 consecutive keys 8(l/16)..+8 of the step for query row l%16: A row m of tile kt
@@ -65,13 +65,14 @@ PS_DEV uint4 frag_lo(const float* x) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int DH, int RTW>
-__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
+template <int DH, int NWV>
+__global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
+  constexpr int RTW = 1;                    // query tiles per wave
   constexpr int KS = DH / 32, DT = DH / 16;
   constexpr int FK = 2 * KS, F = FK + DT;   // K and V^T fragments per 32-key step
-  constexpr int LPW = F / 4;                // loads per wave per step
-  static_assert(F % 4 == 0, "fragments per wave");
-  __shared__ uint4 b0[F * 64], b1[F * 64], b2[F * 64], b3[F * 64];
+  constexpr int LPW = (F + NWV - 1) / NWV;  // loads per wave per step
+  constexpr int FP = LPW * NWV;             // fragment slots per step (with padding)
+  __shared__ uint4 b0[FP * 64], b1[FP * 64], b2[FP * 64], b3[FP * 64];
   auto bp = [&](auto I) -> uint4* {
     if constexpr (I == 0) return b0;
     else if constexpr (I == 1) return b1;
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
     const int key0 = k0 + 32 * step;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int f = i * 4 + wave;
+      const int slot = i * NWV + wave;
+      const int f = slot < F ? slot : 0;   // padding slots repeat fragment 0 into their own slot
       const uint16_t* src;
       if (f < FK) {
         const int kt = f / KS, ks = f % KS;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
         kg = kg + 8 <= n ? kg : n - 8;
         src = vt + (int64_t)(16 * (f - FK) + c16) * n + kg;
       }
-      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)&buf[f * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)&buf[slot * 64], 16, 0, 0);
     }
   };
 
@@ -500,28 +502,26 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     else return hipErrorInvalidValue;
   } else {
     const int tiles = PS_CEIL_DIV(nrows, 16);
-    const int rtw = PS_CEIL_DIV(tiles, 4);
-    if (rtw > 3 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos) return hipErrorInvalidValue;
-    dim3 grid(a.n_chunks, a.hq, a.batch);
-    auto go = [&](auto DHc, auto RTWc) {
-      hipLaunchKernelGGL((attn_chunk_kernel<decltype(DHc)::value, decltype(RTWc)::value>), grid, dim3(256), 0, s, a);
-    };
-    using I64 = std::integral_constant<int, 64>;
-    using I128 = std::integral_constant<int, 128>;
-    using R1 = std::integral_constant<int, 1>;
-    using R2 = std::integral_constant<int, 2>;
-    using R3 = std::integral_constant<int, 3>;
-    if (a.dh == 64) {
-      if (rtw == 1) go(I64{}, R1{});
-      else if (rtw == 2) go(I64{}, R2{});
-      else go(I64{}, R3{});
-    } else if (a.dh == 128) {
-      if (rtw == 1) go(I128{}, R1{});
-      else if (rtw == 2) go(I128{}, R2{});
-      else go(I128{}, R3{});
-    } else {
+    const int nwv = 2 * PS_CEIL_DIV(tiles, 2);   // one wave per 16-row tile, even count
+    if (nwv > 10 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos)
       return hipErrorInvalidValue;
-    }
+    dim3 grid(a.n_chunks, a.hq, a.batch);
+    auto go = [&](auto DHc, auto NWc) {
+      constexpr int NW = decltype(NWc)::value;
+      hipLaunchKernelGGL((attn_chunk_kernel<decltype(DHc)::value, NW>), grid, dim3(64 * NW), 0, s, a);
+    };
+    auto by_waves = [&](auto DHc) {
+      switch (nwv) {
+        case 2: go(DHc, std::integral_constant<int, 2>{}); break;
+        case 4: go(DHc, std::integral_constant<int, 4>{}); break;
+        case 6: go(DHc, std::integral_constant<int, 6>{}); break;
+        case 8: go(DHc, std::integral_constant<int, 8>{}); break;
+        default: go(DHc, std::integral_constant<int, 10>{}); break;
+      }
+    };
+    if (a.dh == 64) by_waves(std::integral_constant<int, 64>{});
+    else if (a.dh == 128) by_waves(std::integral_constant<int, 128>{});
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
