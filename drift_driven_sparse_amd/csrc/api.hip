@@ -86,9 +86,9 @@ void layout(polestar_handle* h) {
   w.attn_part = take(d.dtype == POLESTAR_BF16 && h->attn_nchunks > 1
                          ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->mt * (d.head_dim + 2) * 4
                          : 0);
-  w.inv_hp = take(Bt * h->mt * 4);
+  w.inv_hp = take(Bt * h->mt * (size_t)row_reduce_chunks(d.d) * 4);   // sum-of-squares chunks of h'
   w.act = take(Bt * h->mt * (size_t)d.ffn * 4);
-  w.inv_out = take(Bt * h->mt * 4);
+  w.inv_out = take(Bt * h->mt * (size_t)row_reduce_chunks(d.d) * 4);  // sum-of-squares chunks of out
   w.xhat = take(Bt * h->win_max * d.d * 8);
   w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
   w.wstat = take(Bt * (h->win_max + (size_t)d.n_clusters * PS_CEIL_DIV(d.d, 256)) * 8);
@@ -380,9 +380,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.out_pl = at<uint16_t>(ws, h->ws.hp_pl);
   rr.pl_stride = (int64_t)h->mt * d.d;
   rr.pl_bstride = 2 * rr.pl_stride;
-  rr.inv_rms = at<float>(ws, h->ws.inv_hp);
-  rr.inv_bstride = h->mt;
-  rr.eps = h->pr.rms_eps;
+  rr.ss_out = at<float>(ws, h->ws.inv_hp);
+  rr.ss_bstride = h->mt;
   rr.chk = h->chk.hp;
   rr.chk_rows = h->mt;
   {
@@ -408,7 +407,10 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.part = part;
   dl.part_rows = h->mt;
   dl.e.kind = EPI_SWIGLU;
-  dl.e.inv_rms = rr.inv_rms;
+  dl.e.ss_in = rr.ss_out;
+  dl.e.ss_chunks = row_reduce_chunks(d.d);
+  dl.e.ss_d = (float)d.d;
+  dl.e.eps = h->pr.rms_eps;
   dl.e.inv_bstride = h->mt;
   dl.e.act = at<char>(ws, h->ws.act);
   dl.e.act_rows = h->mt;
@@ -462,7 +464,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   r2.out_split = d.block;
   r2.out_b = u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
-  r2.inv_rms = at<float>(ws, h->ws.inv_out);
+  r2.ss_out = at<float>(ws, h->ws.inv_out);
   r2.chk = h->chk.out;
   {
     PROF(POLESTAR_K_DREDUCE);
@@ -486,7 +488,10 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
     dl.part = part;
     dl.part_rows = h->win_max;
     dl.e.kind = EPI_KV;
-    dl.e.inv_rms = r2.inv_rms;
+    dl.e.ss_in = r2.ss_out;
+    dl.e.ss_chunks = row_reduce_chunks(d.d);
+    dl.e.ss_d = (float)d.d;
+    dl.e.eps = h->pr.rms_eps;
     dl.e.inv_bstride = h->mt;
     dl.e.inv_off = d.block;
     dl.e.kc = k_next;
@@ -568,9 +573,8 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.out_a_bstride = (int64_t)h->mt * d.d;
   rr.out_split = h->mt;
   rr.out_f32 = 1;
-  rr.inv_rms = at<float>(ws, h->ws.inv_hp);
-  rr.inv_bstride = h->mt;
-  rr.eps = h->pr.rms_eps;
+  rr.ss_out = at<float>(ws, h->ws.inv_hp);
+  rr.ss_bstride = h->mt;
   rr.chk = h->chk.hp;
   rr.chk_rows = h->mt;
   {
@@ -594,7 +598,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.ksplit = 1;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_SWIGLU;
-  ep.inv_rms = rr.inv_rms;
+  ep.ss_in = rr.ss_out;
+  ep.ss_chunks = row_reduce_chunks(d.d);
+  ep.ss_d = (float)d.d;
+  ep.eps = h->pr.rms_eps;
   ep.inv_bstride = h->mt;
   ep.act = at<char>(ws, h->ws.act);
   ep.act_rows = h->mt;
@@ -640,7 +647,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   r2.out_split = d.block;
   r2.out_b = u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
-  r2.inv_rms = at<float>(ws, h->ws.inv_out);
+  r2.ss_out = at<float>(ws, h->ws.inv_out);
   r2.chk = h->chk.out;
   {
     PROF(POLESTAR_K_DREDUCE);
@@ -662,7 +669,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     ga.ksplit = 1;
     memset(&ep, 0, sizeof(ep));
     ep.kind = EPI_KV;
-    ep.inv_rms = r2.inv_rms;
+    ep.ss_in = r2.ss_out;
+    ep.ss_chunks = row_reduce_chunks(d.d);
+    ep.ss_d = (float)d.d;
+    ep.eps = h->pr.rms_eps;
     ep.inv_bstride = h->mt;
     ep.inv_off = d.block;
     ep.kc = k_next;

@@ -378,25 +378,36 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 //   u_j = exp(sp_j - max sp), e_j = (s_j - sp_j) - mean_u(s - sp),
 //   S0 = sum u, S1 = sum u expm1(e), S2 = sum u exp(e) e,
 //   KL = (S2/S0) / (1 + S1/S0) - log1p(S1/S0)   (invariant to the shift of e).
-PS_DEV float wave_kl(const float* s, const float* sp, int n, int lane) {
+// The n <= 1024 logits of one (row, head) sit in registers (16 per lane, lane + 64 i), so
+// the three passes read memory once; per-lane sums run in i order, then a wavefront sum.
+constexpr int kKlPer = 16;
+
+PS_DEV float wave_kl(const float* sv, const float* pv, int n, int lane) {
   float mp = -INFINITY;
-  for (int j = lane; j < n; j += 64) mp = fmaxf(mp, sp[j]);
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i)
+    if (lane + 64 * i < n) mp = fmaxf(mp, pv[i]);
   mp = wave_max(mp);
+  float u[kKlPer];
   float s0 = 0.f, sd = 0.f;
-  for (int j = lane; j < n; j += 64) {
-    const float u = expf(sp[j] - mp);
-    s0 += u;
-    sd += u * (s[j] - sp[j]);
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    const bool ok = lane + 64 * i < n;
+    u[i] = ok ? expf(pv[i] - mp) : 0.f;
+    s0 += u[i];
+    sd += ok ? u[i] * (sv[i] - pv[i]) : 0.f;
   }
   s0 = wave_sum(s0);
   sd = wave_sum(sd);
   const float dbar = sd / s0;
   float s1 = 0.f, s2 = 0.f;
-  for (int j = lane; j < n; j += 64) {
-    const float u = expf(sp[j] - mp);
-    const float e = (s[j] - sp[j]) - dbar;
-    s1 += u * expm1f(e);
-    s2 += u * expf(e) * e;
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    if (lane + 64 * i < n) {
+      const float e = (sv[i] - pv[i]) - dbar;
+      s1 += u[i] * expm1f(e);
+      s2 += u[i] * expf(e) * e;
+    }
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
@@ -428,63 +439,78 @@ __global__ __launch_bounds__(256) void kl_kernel(AttnArgs a) {
     out = a.akl + ((int64_t)b * a.block + r) * a.hq + h;
     do_kl = a.act_kl != 0;
   }
+  float sv[kKlPer], pv[kKlPer];
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    const int j = lane + 64 * i;
+    sv[i] = j < n ? s[j] : 0.f;
+    pv[i] = (do_kl && j < n) ? prev[j] : 0.f;
+  }
   if (do_kl) {
-    const float kl = wave_kl(s, prev, n, lane);
+    const float kl = wave_kl(sv, pv, n, lane);
     if (lane == 0) *out = kl;
   }
-  for (int j = lane; j < n; j += 64) prev[j] = s[j];
+#pragma unroll
+  for (int i = 0; i < kKlPer; ++i) {
+    const int j = lane + 64 * i;
+    if (j < n) prev[j] = sv[i];
+  }
 }
 
-// Per sequence: D_c = sum_h max(0, KL_{c,h}) (heads in order); top-k clusters by
-// (D desc, index asc); S = window rows whose label is selected, ascending; and the
-// per-row active drift delta_j = sum_h max(0, KL_{j,h}).
-__global__ __launch_bounds__(64) void topk_kernel(TopkArgs a) {
+// Per sequence: D_c = sum_h max(0, KL_{c,h}); top-k clusters by (D desc, index asc), found by
+// ranking every cluster against the others; S = window rows whose label is selected, ascending;
+// and the per-row active drift delta_j = sum_h max(0, KL_{j,h}).  Head sums are wavefront
+// reductions (fixed order).  One 256-thread workgroup per sequence.
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ float D[16];
   __shared__ int chosen[16];
-  const int b = blockIdx.x, lane = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.refresh) {
     const int keff = min(a.K, a.n_win);
-    if (lane < a.K) {
+    for (int c = wave; c < a.K; c += 4) {
       float s = 0.f;
-      if (lane < keff)
-        for (int h = 0; h < a.hq; ++h) s += fmaxf(0.f, a.kl[((int64_t)b * a.K + lane) * a.hq + h]);
-      D[lane] = s;
-      chosen[lane] = 0;
-      if (a.D) a.D[(int64_t)b * a.K + lane] = s;
-    }
-    __syncthreads();
-    if (lane == 0) {
-      const int kk = min(a.k, keff);
-      for (int t = 0; t < a.k; ++t) {
-        int best = -1;
-        if (t < kk) {
-          for (int c = 0; c < keff; ++c)
-            if (!chosen[c] && (best < 0 || D[c] > D[best])) best = c;
-          chosen[best] = 1;
-        }
-        if (a.topk) a.topk[(int64_t)b * a.k + t] = best;
+      if (c < keff)
+        for (int h = lane; h < a.hq; h += 64) s += fmaxf(0.f, a.kl[((int64_t)b * a.K + c) * a.hq + h]);
+      s = wave_sum(s);
+      if (lane == 0) {
+        D[c] = s;
+        if (a.D) a.D[(int64_t)b * a.K + c] = s;
       }
     }
     __syncthreads();
-    int base = 0;
-    for (int w0 = 0; w0 < a.n_win; w0 += 64) {
-      const int w = w0 + lane;
-      int c = w < a.n_win ? a.win_m[(int64_t)b * a.win_max + w] : -1;
-      const bool sel = c >= 0 && c < a.K && chosen[c];
-      const unsigned long long m = __ballot(sel);
-      const int before = __popcll(m & ((1ull << lane) - 1ull));
-      if (sel) a.sel_idx[(int64_t)b * a.win_max + base + before] = w;
-      base += __popcll(m);
+    const int kk = min(a.k, keff);
+    if (tid < a.K) {
+      int rank = 0;
+      if (tid < keff)
+        for (int c = 0; c < keff; ++c) rank += (D[c] > D[tid]) || (D[c] == D[tid] && c < tid);
+      const int sel = tid < keff && rank < kk;
+      chosen[tid] = sel;
+      if (sel && a.topk) a.topk[(int64_t)b * a.k + rank] = tid;
     }
-    if (lane == 0) a.sel_count[b] = base;
+    if (tid >= kk && tid < a.k && a.topk) a.topk[(int64_t)b * a.k + tid] = -1;
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int w0 = 0; w0 < a.n_win; w0 += 64) {
+        const int w = w0 + lane;
+        const int c = w < a.n_win ? a.win_m[(int64_t)b * a.win_max + w] : -1;
+        const bool sel = c >= 0 && c < a.K && chosen[c];
+        const unsigned long long m = __ballot(sel);
+        const int before = __popcll(m & ((1ull << lane) - 1ull));
+        if (sel) a.sel_idx[(int64_t)b * a.win_max + base + before] = w;
+        base += __popcll(m);
+      }
+      if (lane == 0) a.sel_count[b] = base;
+    }
   } else {
-    if (lane == 0) a.sel_count[b] = 0;
+    if (tid == 0) a.sel_count[b] = 0;
   }
   if (a.delta) {
-    for (int j = lane; j < a.block; j += 64) {
+    for (int j = wave; j < a.block; j += 4) {
       float s = 0.f;
-      for (int h = 0; h < a.hq; ++h) s += fmaxf(0.f, a.akl[((int64_t)b * a.block + j) * a.hq + h]);
-      a.delta[(int64_t)b * a.block + j] = s;
+      for (int h = lane; h < a.hq; h += 64) s += fmaxf(0.f, a.akl[((int64_t)b * a.block + j) * a.hq + h]);
+      s = wave_sum(s);
+      if (lane == 0) a.delta[(int64_t)b * a.block + j] = s;
     }
   }
 }
@@ -543,7 +569,7 @@ hipError_t launch_kl(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.batch), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

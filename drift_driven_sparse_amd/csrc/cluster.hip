@@ -174,21 +174,28 @@ __global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
   T* rows = (T*)a.ws_rows;
   const int64_t dst = (wbase + w) * d;
   double ss = 0.0;
-  for (int n = tid; n < d; n += blockDim.x) {
-    float x;
+  // eight consecutive elements per thread and step (d is a multiple of 16)
+  for (int n0 = tid * 8; n0 < d; n0 += blockDim.x * 8) {
+    float x[8];
     if (pr >= 0) {
-      x = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n0 + e);
     } else if (a.nvfp4) {
-      const uint8_t byte = a.codes[(wbase + w) * (d / 2) + n / 2];
-      const uint32_t code = (n & 1) ? (byte >> 4) : (byte & 15u);
-      const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n / 16]);
-      x = St<T>::round(St<T>::load(zc, n) + sv * e2m1_value(code));
+      const uint32_t bytes = *(const uint32_t*)(a.codes + (wbase + w) * (d / 2) + n0 / 2);
+      const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n0 / 16]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = St<T>::round(St<T>::load(zc, n0 + e) + sv * e2m1_value((bytes >> (4 * e)) & 15u));
     } else {
-      x = St<T>::load((const T*)a.win_h, dst + n);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = St<T>::load((const T*)a.win_h, dst + n0 + e);
     }
-    St<T>::store(rows, dst + n, x);
-    if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n, x);
-    ss += (double)x * (double)x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      St<T>::store(rows, dst + n0 + e, x[e]);
+      if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n0 + e, x[e]);
+      ss += (double)x[e] * (double)x[e];
+    }
   }
   ss = block_sum_d(ss, red);
   if (tid == 0) {
@@ -210,9 +217,13 @@ __global__ __launch_bounds__(256) void centroid_sum_kernel(ClusterArgs a) {
   const int64_t wbase = (int64_t)b * a.win_max;
   const T* rows = (const T*)a.ws_rows;
   double acc = 0.0;
-  if (n < d)
-    for (int m = 0; m < nmem; ++m)
-      if (nr[m] > 0.0) acc += (double)St<T>::load(rows, (wbase + mem[m]) * d + n) / nr[m];
+  if (n < d) {
+#pragma unroll 4
+    for (int m = 0; m < nmem; ++m) {
+      const float x = St<T>::load(rows, (wbase + mem[m]) * d + n);
+      if (nr[m] > 0.0) acc += (double)x / nr[m];
+    }
+  }
   if (n < d) a.z64[((int64_t)b * a.K + c) * d + n] = acc;
   const double ss = block_sum_d(acc * acc, red);
   if (tid == 0) a.cpart[((int64_t)b * a.K + c) * a.nchunk + ch] = ss;

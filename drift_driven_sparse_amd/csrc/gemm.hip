@@ -78,7 +78,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
       const int p = j >> 4, jj = j & 15;
       const int oc = (n0 >> 1) + j;
       if (oc >= e.ffn) continue;
-      const float s = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      const float s = row_scale(e, b, r);
       const float gv = tile[r * kLDT + (2 * p) * 16 + jj] * s;
       const float uv = tile[r * kLDT + (2 * p + 1) * 16 + jj] * s;
       const float a = gv / (1.f + expf(-gv)) * uv;
@@ -96,7 +96,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
     for (int r = wave; r < rows_b; r += nwave) {
       const int n = n0 + lane;
       const bool valid = n < e.vocab;
-      const float s = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+      const float s = row_scale(e, b, r);
       const float l = valid ? tile[r * kLDT + lane] * s : -INFINITY;
       const float m = wave_max(l);
       const float se = wave_sum(valid ? expf(l - m) : 0.f);
@@ -311,13 +311,15 @@ hipError_t dispatch_kind(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
 }
 
 // ---- split-K row reduction ------------------------------------------------------------------
-// One workgroup per output row: partial sums (added in split order) + residual, stored as
-// float32 or rounded to the storage dtype, optionally also as bf16 hi/lo planes, and the
-// 1/rms of the stored row for the next projection.  Four columns per thread and step.
+// Workgroup = (row, 1024-column chunk): partial sums (added in split order) + residual, stored
+// as float32 or rounded to the storage dtype, optionally also as bf16 hi/lo planes, and the sum
+// of squares of the stored chunk (the next projection's RMSNorm adds the chunks in order).
+constexpr int kRrCols = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(512) void row_reduce_kernel(RowReduceArgs a) {
-  __shared__ float red[8];
-  const int r = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
   int rows_b = a.block + (a.count ? a.count[b] : 0);
   if (rows_b > (int)gridDim.x) rows_b = gridDim.x;
   if (r >= rows_b) return;
@@ -338,7 +340,8 @@ __global__ __launch_bounds__(512) void row_reduce_kernel(RowReduceArgs a) {
   const int64_t pstride = (int64_t)a.batch * a.part_rows * a.d;
   const float* p = a.part + ((int64_t)b * a.part_rows + r) * a.d;
   float ss = 0.f;
-  for (int n = threadIdx.x * 4; n < a.d; n += blockDim.x * 4) {
+  const int n = chunk * kRrCols + threadIdx.x * 4;
+  if (n < a.d) {
     float4 v = *(const float4*)(p + n);
     for (int s = 1; s < a.ksplit; ++s) {
       const float4 t = *(const float4*)(p + s * pstride + n);
@@ -367,12 +370,13 @@ __global__ __launch_bounds__(512) void row_reduce_kernel(RowReduceArgs a) {
     }
   }
   ss = block_sum(ss, red);
-  if (threadIdx.x == 0 && a.inv_rms) a.inv_rms[(int64_t)b * a.inv_bstride + r] = 1.f / sqrtf(ss / (float)a.d + a.eps);
+  if (threadIdx.x == 0 && a.ss_out) a.ss_out[((int64_t)b * a.ss_bstride + r) * gridDim.y + chunk] = ss;
 }
 
 }  // namespace
 
 size_t packed_elems(int N, int K) { return (size_t)N * (size_t)K; }
+int row_reduce_chunks(int d) { return PS_CEIL_DIV(d, kRrCols); }
 
 template <typename T>
 hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s) {
@@ -400,7 +404,7 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 template <typename T>
 hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, a.batch), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, PS_CEIL_DIV(a.d, kRrCols), a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

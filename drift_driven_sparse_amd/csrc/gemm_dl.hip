@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
           const int r = row0 + rt * 16 + i;
           const int oc = ((nt * CG + cg) * NSUB / 2 + j) * 16 + (lane & 15);
           if (r < rows_b && oc < e.ffn) {
-            const float sc = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+            const float sc = row_scale(e, b, r);
             const float gv = acc[rt][2 * j][i] * sc, uv = acc[rt][2 * j + 1][i] * sc;
             const float a = gv / (1.f + expf(-gv)) * uv;
             uint16_t hi, lo;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
     gv.x += tg.x; gv.y += tg.y; gv.z += tg.z; gv.w += tg.w;
     uv.x += tu.x; uv.y += tu.y; uv.z += tu.z; uv.w += tu.w;
   }
-  const float sc = e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+  const float sc = row_scale(e, b, r);
   const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
   const int64_t plane = (int64_t)e.act_rows * e.ffn;
   uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane + (int64_t)r * e.ffn + oc;

@@ -70,9 +70,13 @@ enum EpiKind { EPI_PARTIAL = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_KV = 3, EPI_LMS
 
 struct EpiParams {
   int kind;
-  // row scale (RMSNorm as an output scale): inv_rms[b*inv_bstride + inv_off + r]
+  // row scale (RMSNorm as an output scale) of row r, with i = b*inv_bstride + inv_off + r:
+  // inv_rms[i], or from chunk sums of squares 1/sqrt(sum_c ss_in[i*ss_chunks + c] / ss_d + eps)
   const float* inv_rms;
   int32_t inv_bstride, inv_off;
+  const float* ss_in;
+  int32_t ss_chunks;
+  float ss_d, eps;
   // QKV
   float* q; int32_t q_rows;     // q[(b*q_rows + r)*nq + n]
   void* kc; void* vc;           // caches (storage dtype)
@@ -93,6 +97,14 @@ struct EpiParams {
 PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
   if (!is_v) return ((int64_t)b * e.n_pos + pos) * e.nkv + col;
   return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
+}
+
+PS_DEV float row_scale(const EpiParams& e, int b, int r) {
+  const int64_t i = (int64_t)b * e.inv_bstride + e.inv_off + r;
+  if (!e.ss_in) return e.inv_rms[i];
+  float ss = 0.f;
+  for (int c = 0; c < e.ss_chunks; ++c) ss += e.ss_in[i * e.ss_chunks + c];
+  return 1.f / sqrtf(ss / e.ss_d + e.eps);
 }
 
 // QKV projection row r (active block, window rows, centroids), column n, raw sum v:
@@ -121,7 +133,7 @@ PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
 // K/V of the next layer for packet row r (window row sel_idx[r]).
 template <typename T>
 PS_DEV void epi_kv_elem(const EpiParams& e, int b, int r, int n, float v) {
-  v *= e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
+  v *= row_scale(e, b, r);
   if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
   const int which = n >= e.nkv;
   const int col = n - which * e.nkv;
@@ -181,12 +193,13 @@ struct RowReduceArgs {
   int32_t out_f32;              // outputs are float32 rows (else storage dtype)
   uint16_t* out_pl;             // also the bf16 hi/lo planes of out_a rows (or null)
   int64_t pl_bstride, pl_stride;
-  float* inv_rms; int32_t inv_bstride;
-  float eps;
+  // sums of squares of the stored row per 1024-column chunk: ss_out[(b*ss_bstride + r)*chunks + c]
+  float* ss_out; int32_t ss_bstride;
   float* chk; int32_t chk_rows;
 };
 template <typename T>
 hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s);
+int row_reduce_chunks(int d);   // column chunks of the row reduction (sum-of-squares partials per row)
 
 // ---- window / clustering ----------------------------------------------------------
 struct ClusterArgs {
