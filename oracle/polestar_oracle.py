@@ -505,12 +505,19 @@ def confidence(x: np.ndarray, w_lm: np.ndarray, mask_id: int, eps: float):
     c = max over ids != mask_id, yhat = its argmax (lowest id on ties).
     """
     logits = project(x, w_lm, eps)
+    c, yhat = confidence_from_logits(logits, mask_id)
+    return c, yhat, logits
+
+
+def confidence_from_logits(logits: np.ndarray, mask_id: int):
+    """The softmax part of :func:`confidence` for given LM-head logits [rows, vocab]."""
+    logits = np.asarray(logits, dtype=np.float64)
     lse = logsumexp(logits)
     lg = logits.copy()
     lg[:, mask_id] = -np.inf
     yhat = np.argmax(lg, axis=1)
-    c = np.exp(lg[np.arange(len(x)), yhat] - lse)
-    return c, yhat.astype(np.int32), logits
+    c = np.exp(lg[np.arange(len(lg)), yhat] - lse)
+    return c, yhat.astype(np.int32)
 
 
 def commit_decide(delta, conf, masked, hist_vals, hist_cnt, hist_len, alpha, tau_s):

@@ -86,12 +86,16 @@ def _normal_table(device) -> torch.Tensor:
 _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f64": torch.float64}
 
 
-def normal(shape, std: float, seed: int, device="cpu", dtype="f32") -> torch.Tensor:
-    """Seeded N(0, std^2) tensor (quantile-table generator, see module doc)."""
+def normal(shape, std: float, seed: int, device="cpu", dtype="f32", offset: int = 0) -> torch.Tensor:
+    """Seeded N(0, std^2) tensor (quantile-table generator, see module doc).
+
+    ``offset`` shifts the element counter: the result equals elements
+    [offset, offset + numel) of the flat tensor drawn with the same seed.
+    """
     shape = tuple(int(s) for s in shape)
     numel = int(np.prod(shape)) if shape else 1
-    assert numel < 2**32
-    idx = torch.arange(numel, dtype=torch.int64, device=device)
+    assert offset + numel < 2**32
+    idx = torch.arange(offset, offset + numel, dtype=torch.int64, device=device)
     h = hash32((hash32(idx) + (seed & _M32)) & _M32)
     u = h >> 16
     vals = _normal_table(device)[u] * torch.tensor(std, dtype=torch.float32, device=device)
@@ -177,6 +181,15 @@ def weight(w: Workload, layer: int, mat: str, run: int = 0, device="cpu", dtype=
               "wg": (f, d), "wu": (f, d), "wd": (d, f), "wlm": (w.vocab, d)}
     seed = stream_seed(w.seed(run), 1, layer, MAT_IDS[mat])
     return normal(shapes[mat], w.weight_std, seed, device, dtype or w.dtype)
+
+
+def weight_rows(w: Workload, layer: int, mat: str, r0: int, r1: int, run: int = 0, device="cpu",
+                dtype=None) -> torch.Tensor:
+    """Rows [r0, r1) of :func:`weight` without drawing the whole matrix."""
+    cols = {"wq": w.d, "wk": w.d, "wv": w.d, "wo": w.n_heads * w.head_dim, "wg": w.d, "wu": w.d, "wd": w.ffn,
+            "wlm": w.d}[mat]
+    seed = stream_seed(w.seed(run), 1, layer, MAT_IDS[mat])
+    return normal((r1 - r0, cols), w.weight_std, seed, device, dtype or w.dtype, offset=r0 * cols)
 
 
 def layer_weights(w: Workload, layer: int, run: int = 0, device="cpu", dtype=None) -> Dict[str, torch.Tensor]:

@@ -1,0 +1,153 @@
+"""GPU parity of Polestar-Commit: LM-head confidence of the active rows and of the
+suffix rows of the final update packet, the current-block commit rule with its
+drift history, and the suffix commit rule.
+
+Inputs are seeded synthetic tensors.  Some rows are planted close to one
+LM-head row so that the confidences spread over (0, 1) and straddle tau_s; one
+row is planted on the mask token's row so that the argmax has to skip it.
+Confidences are compared with the oracle's float64 values; the decisions are
+checked bit-exactly by evaluating the oracle's rule on the GPU's confidences
+(the rule is a float32 comparison, taken in the same precision on both sides).
+The full-vocabulary case streams W_lm through the oracle in row chunks.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from drift_driven_sparse_amd import binding as B
+from oracle import polestar_oracle as O
+from tests.harness import Dev, log, np64, packet
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, batch, blk_start)
+    "llada_full_vocab_batch2": (synth.shrink(synth.WORKLOADS[5], resid="raw"), 2, 512),
+    "small_ragged_vocab_batch3": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128),
+                                  3, 96),
+}
+
+CHUNK = 8192   # LM-head rows per oracle chunk
+
+
+def _lm_logits(w, rows64: np.ndarray, eps: float) -> np.ndarray:
+    """Oracle logits RMSNorm(x) W_lm^T for all vocabulary ids, W_lm drawn chunk by chunk."""
+    out = np.empty((rows64.shape[0], w.vocab), dtype=np.float64)
+    for r0 in range(0, w.vocab, CHUNK):
+        r1 = min(w.vocab, r0 + CHUNK)
+        wc = np64(synth.weight_rows(w, 0, "wlm", r0, r1, device="cuda"))
+        out[:, r0:r1] = O.project(rows64, wc, eps)
+    return out
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_commit_parity(case):
+    w, batch, blk_start = CASES[case]
+    torch.manual_seed(0)
+    dev = Dev(w, batch=batch)
+    d, Bk, V = w.d, w.block, w.vocab
+    mask_id = V - 1
+    log(f"[commit] case={case} d={d} vocab={V} batch={batch} blk_start={blk_start}")
+    try:
+        g = O.window_positions(blk_start, w.n_pos, Bk, w.win_prefix, w.win_suffix)
+        n_pre = int(np.sum(g < blk_start))
+        n_win = len(g)
+        n_suf = n_win - n_pre
+        seed = w.seed(0)
+        # LM head on the GPU
+        wlm = synth.weight(w, 0, "wlm", device="cuda")
+        w_lm = dev.pack(B.W_LM, wlm)
+        # active rows: random, with planted rows near W_lm rows (confidences spread over (0, 1))
+        # x = sqrt(d) W_lm[v] + l g (g ~ N(0, 1) per element) gives the planted logit about
+        # sqrt(d) / sqrt(1 + l^2) against N(0, 1) logits elsewhere; l0 puts c near 0.9.
+        h_fin = synth.tensor(w, (90, 1), (batch, Bk, d), 1.0, device="cuda", dtype="f32")
+        target = np.log(V) + 0.5 + np.log(9.0)
+        l0 = np.sqrt(max((np.sqrt(d) / target) ** 2 - 1.0, 0.01))
+        for b in range(batch):
+            for i, f in enumerate([0.6, 0.85, 0.94, 0.99, 1.04, 1.11, 1.33, 1.7]):
+                j = (3 * i + b) % (Bk - 1)
+                v = int(synth.hash32_int(seed + 31 * b + i) % (V - 1))
+                h_fin[b, j] = wlm[v].float() * np.sqrt(d) + (l0 * f) * h_fin[b, j]
+            h_fin[b, Bk - 1] = wlm[mask_id].float() * np.sqrt(d)   # argmax must skip the mask id
+        h_fin = h_fin.to(torch.bfloat16)
+        # final update packet: ascending window rows, a mix of prefix and suffix rows
+        win_max = dev.win_max
+        u_rows = synth.tensor(w, (90, 2), (batch, win_max, d), 1.0, device="cuda", dtype="f32")
+        u_idx = torch.full((batch, win_max), -1, dtype=torch.int32)
+        u_cnt = torch.zeros(batch, dtype=torch.int32)
+        rng = np.random.default_rng(seed)
+        for b in range(batch):
+            pick = np.sort(rng.choice(n_win, size=min(n_win, 12 + 7 * b), replace=False))
+            u_idx[b, :len(pick)] = torch.tensor(pick, dtype=torch.int32)
+            u_cnt[b] = len(pick)
+            for t, wr in enumerate(pick[::3]):      # some confident suffix/prefix packet rows
+                v = int(synth.hash32_int(seed + 7 * b + t + 1000) % (V - 1))
+                r = int(np.nonzero(pick == wr)[0][0])
+                u_rows[b, r] = wlm[v].float() * np.sqrt(d) + 0.05 * u_rows[b, r]
+        u_rows = u_rows.to(torch.bfloat16)
+        u_idx_d, u_cnt_d = u_idx.cuda(), u_cnt.cuda()
+        # drift, masks, history
+        delta = (synth.tensor(w, (90, 3), (batch, Bk), 1.0, device="cuda").abs() * 2.0).contiguous()
+        act_mask = torch.tensor(rng.integers(0, 2, size=(batch, Bk)), dtype=torch.uint8)
+        act_mask[:, :8] = 1
+        suf_mask = torch.tensor(rng.integers(0, 2, size=(batch, max(w.win_suffix, 1))), dtype=torch.uint8)
+        H = max(w.hist, 1)
+        hist_vals = synth.tensor(w, (90, 4), (batch, Bk, H), 1.0, device="cuda").abs().contiguous()
+        hist_cnt = torch.tensor(rng.integers(0, w.hist + 1, size=(batch, Bk)), dtype=torch.int32)
+        hv0, hc0 = hist_vals.cpu().numpy().copy(), hist_cnt.numpy().copy()
+        outs = dict(commit_active=torch.zeros(batch, Bk, dtype=torch.uint8),
+                    commit_suffix=torch.zeros(batch, w.win_suffix, dtype=torch.uint8),
+                    conf_active=torch.zeros(batch, Bk), yhat=torch.zeros(batch, Bk, dtype=torch.int32),
+                    spike=torch.zeros(batch, Bk), conf_suffix=torch.zeros(batch, w.win_suffix))
+        outs = {k: v.cuda() for k, v in outs.items()}
+        hist_cnt_d = hist_cnt.cuda()
+        act_mask_d, suf_mask_d = act_mask.cuda(), suf_mask.cuda()
+        B.polestar_commit(dev.h, blk_start, w_lm, h_fin, packet(u_rows, u_idx_d, u_cnt_d), delta, act_mask_d,
+                          suf_mask_d, hist_vals, hist_cnt_d, outs["commit_active"], outs["commit_suffix"],
+                          outs["conf_active"], outs["yhat"], outs["spike"], outs["conf_suffix"], dev.ws,
+                          dev.ws_bytes)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in outs.items()}
+        for b in range(batch):
+            # oracle confidences of the active rows and the suffix packet rows
+            cnt = int(u_cnt[b])
+            idx = u_idx[b, :cnt].numpy()
+            suf_r = [r for r in range(cnt) if idx[r] >= n_pre]
+            rows = np.concatenate([np64(h_fin[b]), np64(u_rows[b])[suf_r]], axis=0)
+            lg = _lm_logits(w, rows, w.rms_eps)
+            c, yhat = O.confidence_from_logits(lg, mask_id)
+            ca, ya = c[:Bk], yhat[:Bk]
+            err = np.abs(got["conf_active"][b] - ca) / np.maximum(ca, 1e-30)
+            log(f"    seq {b}: active confidences {np.round(ca[:8], 3)} max rel err {err.max():.2e}")
+            assert err.max() <= 2e-3, f"seq {b}: confidence rel err {err.max():.3e}"
+            assert np.array_equal(got["yhat"][b], ya), f"seq {b}: argmax ids differ"
+            assert got["yhat"][b][Bk - 1] != mask_id
+            assert (ca >= w.tau_s).any() and (ca < w.tau_s).any(), "planted rows should straddle tau_s"
+            # the rule on the GPU's confidences: bit-exact decisions, spikes and history
+            com, sp, _, hv, hc = O.commit_decide(np64(delta[b]), got["conf_active"][b], act_mask[b].numpy(),
+                                                 hv0[b], hc0[b], w.hist, w.alpha, w.tau_s)
+            assert np.array_equal(got["commit_active"][b], com), f"seq {b}: commit mask differs"
+            assert np.array_equal(got["spike"][b].astype(np.float32), sp), f"seq {b}: spike differs"
+            assert np.array_equal(hist_cnt_d[b].cpu().numpy(), hc)
+            assert np.array_equal(hist_vals[b].cpu().numpy().reshape(Bk, -1)[:, :w.hist],
+                                  hv.reshape(Bk, -1)[:, :w.hist].astype(np.float32))
+            # suffix rows
+            cs = c[Bk:]
+            conf_suf = np.zeros(w.win_suffix, dtype=np.float32)
+            elig = np.zeros(w.win_suffix, dtype=bool)
+            for t, r in enumerate(suf_r):
+                slot = int(idx[r]) - n_pre
+                err = abs(got["conf_suffix"][b][slot] - cs[t]) / max(cs[t], 1e-30)
+                assert err <= 2e-3, f"seq {b}: suffix confidence rel err {err:.3e}"
+                conf_suf[slot] = got["conf_suffix"][b][slot]
+                elig[slot] = suf_mask[b, slot] != 0
+            want = O.suffix_commit(conf_suf, elig, w.tau_suf)
+            assert np.array_equal(got["commit_suffix"][b], want), f"seq {b}: suffix commit differs"
+            log(f"    seq {b}: {int(com.sum())} active commits, {int(want.sum())} suffix commits, "
+                f"{len(suf_r)} suffix packet rows of {n_suf}")
+    finally:
+        dev.close()
+    log(f"[commit] case={case} passed")
