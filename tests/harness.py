@@ -102,6 +102,27 @@ def topk_margin(D, topk, k_eff):
     return (lo - max(rest)) / max(abs(lo), 1e-30)
 
 
+def check_topk(tg, Dg, D_or, topk_or, k, k_eff, tag):
+    """Top-k comparison.  The GPU's clusters must follow the rule on its own drift
+    values; the selected set must equal the oracle's unless the oracle's margin
+    between the k-th selected and the best unselected drift is below 1e-3
+    (returns False: both sets are admissible); within the set, the order may
+    differ only between drifts equal to 1e-3 relative."""
+    kk = min(k, k_eff)
+    tg = np.asarray(tg)[:kk]
+    assert np.array_equal(tg, O.topk_clusters(Dg, k, k_eff)[:kk]), f"{tag}: top-k does not follow the rule"
+    if set(tg.tolist()) != set(np.asarray(topk_or)[:kk].tolist()):
+        mg = topk_margin(D_or, topk_or, k_eff)
+        if mg < 1e-3:
+            log(f"    {tag}: top-k near-tie (oracle margin {mg:.2e})")
+            return False
+        raise AssertionError(f"{tag}: top-k {tg.tolist()} != oracle {list(topk_or)} (margin {mg:.2e})")
+    D_or = np.asarray(D_or, dtype=np.float64)
+    for a, b in zip(tg[:-1], tg[1:]):
+        assert D_or[a] >= D_or[b] * (1 - 1e-3) - 1e-12, f"{tag}: top-k order {tg.tolist()} vs oracle drift"
+    return True
+
+
 # ---------------------------------------------------------------- device handle
 class Dev:
     def __init__(self, w: synth.Workload, batch: Optional[int] = None, vocab: Optional[int] = None,
