@@ -1,0 +1,114 @@
+"""The layer stack in the launch configuration the benchmark times: one refresh
+step of a LLaDA-8B-shaped stack (hidden 4096, 32 heads, FFN 12288, n 1024)
+captured in a HIP graph.  Every replay must reproduce the eager step bit for
+bit: the last layer's active rows, its drift outputs, every update packet and
+all state the step leaves behind (K/V caches, window rows, centroids, proxy
+and active logits).  The graph is replayed several times from the same saved
+state, with eager work and synchronisations in between.  (Oracle parity of the
+same kernels at these shapes is covered by the layer and trajectory tests.)
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import synth
+from drift_driven_sparse_amd import binding as B
+from drift_driven_sparse_amd.stack import RefreshStack
+from tests.harness import log
+
+pytestmark = pytest.mark.gpu
+
+STATE = ("k_cache", "v_cache", "win_h", "win_z", "win_m", "proxy_logits")
+
+
+def _snapshot(st: RefreshStack):
+    snap = [{k: L[k].clone() for k in STATE} for L in st.layers]
+    snap.append({"act_logits": st.act_logits.clone()})
+    return snap
+
+
+def _restore(st: RefreshStack, snap):
+    for L, s in zip(st.layers, snap):
+        for k in STATE:
+            L[k].copy_(s[k])
+    st.act_logits.copy_(snap[-1]["act_logits"])
+
+
+def _outputs(st: RefreshStack, out_h: torch.Tensor):
+    o = {"h_out": out_h.clone(), "D": st.D.clone(), "topk": st.topk.clone(), "delta": st.delta.clone()}
+    for i in range(2):   # packet rows past the count are whatever an earlier step left there
+        c = int(st.pk_cnt[i][0])
+        o[f"pk_rows{i}"] = st.pk_rows[i][:, :c].clone()
+        o[f"pk_idx{i}"] = st.pk_idx[i][:, :c].clone()
+        o[f"pk_cnt{i}"] = st.pk_cnt[i].clone()
+    for l, L in enumerate(st.layers):
+        for k in STATE:
+            o[f"{k}{l}"] = L[k].clone()
+    o["act_logits"] = st.act_logits.clone()
+    return o
+
+
+def test_stack_graph_replay_matches_eager():
+    w = synth.WORKLOADS[3]
+    n_layers = 3
+    dims = B.Dims(d=w.d, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn,
+                  n_pos=w.n_pos, batch=1, block=w.block, win_prefix=w.win_prefix, win_suffix=w.win_suffix,
+                  n_clusters=w.n_clusters, top_k=w.top_k, vocab=0, dtype=B.BF16, resid_fmt=B.RESID_RAW)
+    params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist, mask_id=0,
+                      kmeans_iters=w.kmeans_iters)
+    log(f"[stack] {n_layers} layers of {w.name}, n={w.n_pos}")
+    st = RefreshStack(dims, params, n_layers)
+    try:
+        blk = w.prompt
+        entry_rows, inits = [], []
+        for l in range(n_layers):
+            st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
+            L = st.layers[l]
+            L["k_cache"].copy_(synth.tensor(w, (l, 10), L["k_cache"].shape, 1.0, 0, "cuda", "bf16"))
+            L["v_cache"].copy_(synth.tensor(w, (l, 11), L["v_cache"].shape, 1.0, 0, "cuda", "bf16"))
+            L["win_h"].copy_(synth.tensor(w, (l, 12), L["win_h"].shape, 1.0, 0, "cuda", "bf16"))
+            entry_rows.append(L["win_h"])
+            inits.append(torch.tensor(synth.kmeans_init(w, st.win_max, l, 0), dtype=torch.int32, device="cuda")[None])
+        st.block_entry(blk, entry_rows, inits)
+        inputs = synth.tensor(w, (99,), (3, 1, w.block, w.d), 1.0, 0, "cuda", "bf16")
+        h_in = torch.zeros(1, w.block, w.d, dtype=torch.bfloat16, device="cuda")
+        h_in.copy_(inputs[0])
+        st.step(blk, h_in)                      # first step: drift references
+        torch.cuda.synchronize()
+        snap = _snapshot(st)
+        h_in.copy_(inputs[1])
+        out = st.step(blk, h_in)
+        torch.cuda.synchronize()
+        want = _outputs(st, out)
+        log(f"[stack] eager step: selected rows per packet {[int(want[f'pk_cnt{i}'][0]) for i in range(2)]}, "
+            f"topk {want['topk'].tolist()}")
+        # capture on a side stream after a warm eager run there
+        _restore(st, snap)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            st.step(blk, h_in)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gout = st.step(blk, h_in)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            _restore(st, snap)
+            h_in.copy_(inputs[1])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = _outputs(st, gout)
+            bad = [k for k in want if not torch.equal(got[k], want[k])]
+            log(f"[stack] replay {rep}: {len(want) - len(bad)}/{len(want)} tensors bit-identical")
+            assert not bad, f"replay {rep} differs from the eager step in {bad}"
+            # eager work between replays
+            h_in.copy_(inputs[2])
+            st.step(blk, h_in)
+            torch.cuda.synchronize()
+    finally:
+        st.close()
+    log("[stack] graph replays match the eager step")
