@@ -49,6 +49,21 @@ def layer_bytes(w, n_sel: float) -> dict:
     return b
 
 
+def counter_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when the projection sources changed since the counters were taken."""
+    import re
+    from drift_driven_sparse_amd import prof_summary
+    path = os.path.join(ROOT, "profiles", "gate_up_projection_llada8b_pmc.md")
+    try:
+        text = open(path).read()
+        m = re.search(r"```json\n(.*?)\n```", text, re.S)
+        rec = json.loads(m.group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    return rec["traffic_bytes"] if rec.get("source_hash") == prof_summary.source_hash() else None
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The CPU oracle on a bounded sample of the same workload: whole refresh steps of
     single layers (fp64 NumPy/BLAS), weights already in host memory, timed per layer."""
@@ -101,6 +116,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel from the host loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="(diagnostics) fewer layers than the workload")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="also run one element-wise copy of MB MiB (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this refresh path runs on a single MI355X and uses no "
@@ -220,8 +237,9 @@ def main():
     per = {k: (v[0] / max(v[1], 1), v[1]) for k, v in prof.items() if v[1]}
     gu_ms, gu_n = per.get("gu", (float("nan"), 0))
     achieved = lb["gu_launch"] / (gu_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": "gemm_bf16 gate/up projection (SwiGLU epilogue)", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+    roof = {"bound": "hbm", "kernel": "gate/up projection (split-K bf16 GEMM + SwiGLU finish)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
             "bytes_per_launch": lb["gu_launch"], "avg_launch_ms": round(gu_ms, 5), "launches": gu_n,
             "timing": "HIP events around each launch of the kernel during a profiled pass of the same steps"}
     kern = {k: {"avg_ms": round(v[0], 5), "launches": v[1]} for k, v in per.items()}
@@ -241,6 +259,15 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    if args.copy_probe > 0:
+        src = torch.ones(args.copy_probe * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: one element-wise kernel reading {src.numel() * 4} B and writing "
+            f"{dst.numel() * 4} B")
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -1,55 +1,124 @@
-"""Summarise a rocprofv3 results database (kernel trace) as a markdown table.
+"""Summaries of rocprofv3 output as short markdown.
 
-Usage: python -m drift_driven_sparse_amd.prof_summary <results.db> [--title T] [--command C]
-Kernels of this library are listed first; other kernels (e.g. input generation)
-are aggregated in one line.  The top_kernels view stores durations in
-microseconds.
+  python -m drift_driven_sparse_amd.prof_summary trace <results.db> [--title T] [--command C]
+      kernel-trace statistics (the top_kernels view stores durations in microseconds);
+      this library's kernels one per line, everything else (input generation, copies)
+      aggregated.
+  python -m drift_driven_sparse_amd.prof_summary pmc --fetch <fetch.csv> --write <write.csv>
+      --kernels NAME [NAME ...] --probe-bytes B [--title T] [--command C]
+      per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the named kernels from two counter
+      runs, each scaled by the counter's reading for an element-wise copy kernel that
+      reads and writes B bytes (the run's last float add kernel); ends with a JSON line
+      of the figures and a hash of the projection sources they were taken from.
 """
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
 import re
 import sqlite3
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/gemm_dl.hip", "csrc/kernels.h", "csrc/common.h"]
 
 
 def short(name: str) -> str:
     name = name.replace("(anonymous namespace)::", "")
-    m = re.match(r"(?:void )?([A-Za-z0-9_]+(?:<[^()]*>)?)", name)
+    m = re.match(r"(?:void )?([A-Za-z0-9_:]+(?:<[^()]*>)?)", name)
     return m.group(1) if m else name[:80]
 
 
-def summarise(db_path: str):
-    db = sqlite3.connect(db_path)
+def foreign(name: str) -> bool:
+    return name.startswith("at::") or "at::native" in name or "rocclr" in name or name.startswith("__amd")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def trace(a):
+    db = sqlite3.connect(a.db)
     rows = list(db.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
-    ours, other = [], [0, 0.0]
-    for name, calls, total, avg, pct in rows:
-        n = short(name)
-        if n.split("<")[0] in ("gemm_bf16_kernel", "gemm_f32_kernel", "attn_kernel", "topk_kernel",
-                               "window_update_kernel", "kmeans_entry_kernel", "prep_qkv_kernel", "row_reduce_kernel",
-                               "lm_prep_kernel", "decide_kernel", "pack_bf16_kernel", "pack_f32_kernel",
-                               "nvfp4_pack_kernel", "nvfp4_unpack_kernel"):
-            ours.append((n, calls, total, avg))
-        else:
-            other[0] += calls
-            other[1] += total
-    return ours, other
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("db")
-    ap.add_argument("--title", default="rocprofv3 kernel trace")
-    ap.add_argument("--command", default="")
-    a = ap.parse_args()
-    ours, other = summarise(a.db)
     print(f"# {a.title}\n")
     if a.command:
         print(f"Command (from the repository root on the GPU box):\n\n```\n{a.command}\n```\n")
     print("| kernel | calls | total ms | avg us |")
     print("|---|---:|---:|---:|")
-    for n, calls, total, avg in ours:
-        print(f"| `{n}` | {calls} | {total / 1e3:.3f} | {avg:.2f} |")
+    other = [0, 0.0]
+    for name, calls, total, avg, _ in rows:
+        n = short(name)
+        if foreign(n):
+            other[0] += calls
+            other[1] += total
+        else:
+            print(f"| `{n}` | {calls} | {total / 1e3:.3f} | {avg:.2f} |")
     print(f"| (other kernels: input generation, copies) | {other[0]} | {other[1] / 1e3:.3f} | |")
+
+
+def _per_kernel(path):
+    agg = collections.defaultdict(list)
+    probe = None
+    for r in csv.DictReader(open(path)):
+        n = short(r["Kernel_Name"])
+        v = float(r["Counter_Value"])
+        agg[n].append(v)
+        if "CUDAFunctorOnSelf_add<float>" in n:
+            probe = v
+    return agg, probe
+
+
+def pmc(a):
+    fetch, pf = _per_kernel(a.fetch)
+    write, pw = _per_kernel(a.write)
+    kib = 1024.0
+    f_scale = a.probe_bytes / (pf * kib)
+    w_scale = a.probe_bytes / (pw * kib)
+    print(f"# {a.title}\n")
+    if a.command:
+        print(f"Commands (from the repository root on the GPU box, one counter per run):\n\n```\n{a.command}\n```\n")
+    print(f"Calibration: the element-wise copy reads and writes {a.probe_bytes} B; FETCH_SIZE reads "
+          f"{pf:.0f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads {pw:.0f} KiB (scale {w_scale:.3f}).\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |")
+    print("|---|---:|---:|---:|---:|---:|")
+    total = 0.0
+    for k in a.kernels:
+        fv, wv = fetch.get(k), write.get(k)
+        if not fv or not wv:
+            raise SystemExit(f"kernel {k} not in both runs")
+        fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
+        rd, wr = fa * kib * f_scale / 1e6, wa * kib * w_scale / 1e6
+        total += rd + wr
+        print(f"| `{k}` | {len(fv)} | {fa:.1f} | {wa:.1f} | {rd:.2f} | {wr:.2f} |")
+    print(f"\nHBM bytes per launch of the whole unit: {total:.2f} MB.\n")
+    print("```json")
+    print(json.dumps({"traffic_bytes": round(total * 1e6), "kernels": a.kernels, "source_hash": source_hash()}))
+    print("```")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--title", default="rocprofv3 kernel trace")
+    t.add_argument("--command", default="")
+    p = sub.add_parser("pmc")
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--kernels", nargs="+", required=True)
+    p.add_argument("--probe-bytes", type=int, required=True)
+    p.add_argument("--title", default="rocprofv3 memory counters")
+    p.add_argument("--command", default="")
+    a = ap.parse_args()
+    trace(a) if a.cmd == "trace" else pmc(a)
 
 
 if __name__ == "__main__":
