@@ -82,13 +82,21 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   const int n16_total = g.N >> 4;
 
   // Per load slot: source address of this lane at step 0 of the range, and the step stride.
+  // Slots past the fragment count and A slots of row tiles without rows re-read one fixed
+  // 16-byte location every step (stride 0): it stays in the vector L1 and costs no L2 or HBM
+  // traffic, while every wave keeps the same number of loads per stage for the waits.
   const char* src[LPW];
   int stride[LPW];
   const uint16_t* Ab = (const uint16_t*)g.A.base + (int64_t)b * g.A.bstride;
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     int f = i * NWV + wave;
-    if (f >= F) f = 0;   // padding slot: repeats slot 0's source into its own LDS slot
+    const bool idle = f >= F || (f < FA && (f % RT) >= nrt);
+    if (idle) {
+      src[i] = (const char*)(Ab + 8 * (lane >> 4));
+      stride[i] = 0;
+      continue;
+    }
     if (f < FA) {
       const int p = f / RT, rt = f % RT;
       int r = rt * 16 + (lane & 15);
