@@ -9,20 +9,23 @@ Efficient Inference of Diffusion LLMs" (arXiv 2607.14107).  Citations below
 name that page's sections, equations, tables and Algorithm 1.
 
 Everything is plain NumPy in float64.  The method is a heuristic iteration, so
-the oracle follows its steps in the page's order.  It emulates the storage
-precision of the GPU path at exactly these points (``st`` = round to the
-storage dtype, identity for "f64"):
-  * projections: RMSNorm (unit gain, eps) is applied as a per-row scale of the
-    projection output, ``y = (x @ W.T) / rms(x)``; K and V are stored
-    (``st``); queries (token and centroid rows) are never stored and stay
-    unrounded;
-  * values that live only inside one call (attention output ``o``,
-    ``h' = h + o Wo^T``, the SwiGLU product ``act``) stay unrounded; the layer
-    output ``out = st(h' + act Wd^T)`` is stored;
+the oracle follows its steps in the page's order.  The page runs a bf16 model
+(App. B setup) without naming where values are rounded; the oracle takes the
+plain reading of a bf16 transformer and rounds (``st`` = round to the storage
+dtype, identity for "f64") at exactly these points:
+  * every projection input: the RMSNorm output (unit gain, eps) of the row,
+    ``st(x / rms(x))``, the attention output ``st(o)`` and the SwiGLU product
+    ``st(silu(g) * u)``;
+  * projection outputs of token rows: Q, K and V (K and V also as the cache);
+    the proxy queries of the centroids stay unrounded, as do the gate and up
+    projections, which live only inside the SwiGLU product;
+  * the residual stream: ``h' = st(h + st(o) Wo^T)`` and the layer output
+    ``out = st(h' + act Wd^T)`` (the active rows and the update packet U);
   * centroids are stored after normalisation; attention logits that are kept
     as the next step's reference are stored as float32;
   * the NVFP4 codec and the commit rule are evaluated in float32, the
     precision in which the GPU takes those integer decisions.
+Softmax, log-sum-exp, KL and every accumulation stay in float64.
 Functions that only the mathematics pins are marked in their docstrings.
 """
 from __future__ import annotations
@@ -101,10 +104,15 @@ def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
     return np.asarray(x, dtype=np.float64) / rms(x, eps)[..., None]
 
 
-def project(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
-    """RMSNorm(x) @ W^T with unit gain, evaluated as (x @ W^T) / rms(x)."""
-    x = np.asarray(x, dtype=np.float64)
-    return (x @ np.asarray(w, dtype=np.float64).T) / rms(x, eps)[:, None]
+def norm_in(x: np.ndarray, eps: float, st=None) -> np.ndarray:
+    """RMSNorm output (unit gain) as a projection input, rounded by ``st`` when given."""
+    a = rmsnorm(x, eps)
+    return a if st is None else st(a)
+
+
+def project(x: np.ndarray, w: np.ndarray, eps: float, st=None) -> np.ndarray:
+    """RMSNorm(x) @ W^T with unit gain; ``st`` rounds the normalised rows first."""
+    return norm_in(x, eps, st) @ np.asarray(w, dtype=np.float64).T
 
 
 def silu(x: np.ndarray) -> np.ndarray:
@@ -428,7 +436,8 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     recomputed active-block KV; §4.1 proxy attention of the projected
     centroids over the same keys; Eq. 4 drift; top-k clusters and S.]
     Mutates the layer's K/V cache (active rows and patched window rows) and its
-    stored proxy logits.  Returns a dict of outputs.
+    stored proxy logits.  Returns a dict of outputs; "o" is the attention output
+    of the token rows before its rounding.
     """
     st, eps = cfg.st, cfg.eps
     jpos = active_positions(blk_start, cfg.B)
@@ -436,9 +445,9 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     nw = len(wpos)
     hq, hkv, dh = cfg.hq, cfg.hkv, cfg.dh
     toks = np.concatenate([h_act, h_win], axis=0) if refresh else np.asarray(h_act)
-    q = project(toks, W["wq"], eps).reshape(-1, hq, dh)
-    kr = st(project(toks, W["wk"], eps)).reshape(-1, hkv, dh)
-    vr = st(project(toks, W["wv"], eps)).reshape(-1, hkv, dh)
+    q = st(project(toks, W["wq"], eps, st)).reshape(-1, hq, dh)
+    kr = st(project(toks, W["wk"], eps, st)).reshape(-1, hkv, dh)
+    vr = st(project(toks, W["wv"], eps, st)).reshape(-1, hkv, dh)
     K, V = ls["K"], ls["V"]
     K[jpos], V[jpos] = kr[: cfg.B], vr[: cfg.B]
     if refresh and patched is not None and patched.any():
@@ -452,7 +461,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
         res["delta"] = head_summed_drift(logits[: cfg.B], commit_prev)
     if refresh:
         k_eff = min(cfg.K, nw)
-        zq = project(ls["Z"], W["wq"], eps).reshape(cfg.K, hq, dh)
+        zq = project(ls["Z"], W["wq"], eps, st).reshape(cfg.K, hq, dh)
         _, plog = attention(zq, K, V, hq, hkv)
         kl = kl_logits(plog, ls["P"])                 # [K, Hq]
         D = np.sum(np.maximum(kl, 0.0), axis=1)
@@ -470,25 +479,27 @@ def refresh_layer(W: Dict, cfg: Cfg, h_act: np.ndarray, h_win: np.ndarray, o_tok
 
     [§4.1: layer forward only over the hidden states of the top-k clusters;
     its outputs form the update packet for layer l+1.]  Rows are
-    [active block; S].  Returns (h_act_out, U, pre-rounding copies).
+    [active block; S].  Returns the stored outputs (h_act_out, U) and the
+    values before their rounding (hp: h', out_pre: the layer output).
     """
     st, eps, B = cfg.st, cfg.eps, cfg.B
     S = np.asarray(S, dtype=np.int64)
     x = np.concatenate([h_act, h_win[S]], axis=0)
-    o = np.concatenate([o_tok[:B], o_tok[B + S]], axis=0)
-    hp = x + o @ np.asarray(W["wo"], dtype=np.float64).T
-    g = project(hp, W["wg"], eps)
-    u = project(hp, W["wu"], eps)
-    act = silu(g) * u
+    o = st(np.concatenate([o_tok[:B], o_tok[B + S]], axis=0))
+    hp_pre = x + o @ np.asarray(W["wo"], dtype=np.float64).T
+    hp = st(hp_pre)
+    g = project(hp, W["wg"], eps, st)
+    u = project(hp, W["wu"], eps, st)
+    act = st(silu(g) * u)
     out_pre = hp + act @ np.asarray(W["wd"], dtype=np.float64).T
     out = st(out_pre)
-    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp, "act": act}
+    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp_pre, "act": act}
 
 
 def kv_rows(u: np.ndarray, wk: np.ndarray, wv: np.ndarray, cfg: Cfg):
     """K/V of layer l+1 for the packet rows, from the fresh U [§4.1; Algorithm 1 Patch]."""
-    k = cfg.st(project(u, wk, cfg.eps)).reshape(-1, cfg.hkv, cfg.dh)
-    v = cfg.st(project(u, wv, cfg.eps)).reshape(-1, cfg.hkv, cfg.dh)
+    k = cfg.st(project(u, wk, cfg.eps, cfg.st)).reshape(-1, cfg.hkv, cfg.dh)
+    v = cfg.st(project(u, wv, cfg.eps, cfg.st)).reshape(-1, cfg.hkv, cfg.dh)
     return k, v
 
 
@@ -498,13 +509,14 @@ def kv_rows(u: np.ndarray, wk: np.ndarray, wv: np.ndarray, cfg: Cfg):
 # ---------------------------------------------------------------------------
 
 
-def confidence(x: np.ndarray, w_lm: np.ndarray, mask_id: int, eps: float):
+def confidence(x: np.ndarray, w_lm: np.ndarray, mask_id: int, eps: float, st=None):
     """Softmax max-probability over the vocabulary excluding the mask token [§2 Eq. 1].
 
-    Logits = RMSNorm(x) @ W_lm^T (unit gain); the softmax runs over every id;
+    Logits = st(RMSNorm(x)) @ W_lm^T (unit gain, the normalised rows rounded
+    like every projection input); the softmax runs over every id;
     c = max over ids != mask_id, yhat = its argmax (lowest id on ties).
     """
-    logits = project(x, w_lm, eps)
+    logits = project(x, w_lm, eps, st)
     c, yhat = confidence_from_logits(logits, mask_id)
     return c, yhat, logits
 
@@ -582,13 +594,13 @@ def full_forward(h0: np.ndarray, layers: List[Dict], cfg: Cfg):
     Hs, Ks, Vs = [h], [], []
     logits = None
     for W in layers:
-        q = project(h, W["wq"], eps).reshape(-1, cfg.hq, cfg.dh)
-        k = st(project(h, W["wk"], eps)).reshape(-1, cfg.hkv, cfg.dh)
-        v = st(project(h, W["wv"], eps)).reshape(-1, cfg.hkv, cfg.dh)
+        q = st(project(h, W["wq"], eps, st)).reshape(-1, cfg.hq, cfg.dh)
+        k = st(project(h, W["wk"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
+        v = st(project(h, W["wv"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
         out, logits = attention(q, k, v, cfg.hq, cfg.hkv)
-        o = out.reshape(out.shape[0], -1)
-        hp = h + o @ np.asarray(W["wo"], dtype=np.float64).T
-        act = silu(project(hp, W["wg"], eps)) * project(hp, W["wu"], eps)
+        o = st(out.reshape(out.shape[0], -1))
+        hp = st(h + o @ np.asarray(W["wo"], dtype=np.float64).T)
+        act = st(silu(project(hp, W["wg"], eps, st)) * project(hp, W["wu"], eps, st))
         h = st(hp + act @ np.asarray(W["wd"], dtype=np.float64).T)
         Hs.append(h)
         Ks.append(k)
@@ -613,7 +625,7 @@ def block_entry_layer_state(H_in: np.ndarray, K: np.ndarray, V: np.ndarray, Wq: 
         ls["codes"], ls["scales"] = residual_quantize(hw, z, m)
     else:
         ls["H"] = hw.copy()
-    zq = project(z, Wq, cfg.eps).reshape(cfg.K, cfg.hq, cfg.dh)
+    zq = project(z, Wq, cfg.eps, cfg.st).reshape(cfg.K, cfg.hq, cfg.dh)
     _, plog = attention(zq, ls["K"], ls["V"], cfg.hq, cfg.hkv)
     ls["P"] = round_f32(plog)
     return ls

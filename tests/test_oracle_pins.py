@@ -130,6 +130,47 @@ def test_full_forward_one_layer_matches_torch_modules():
     assert np.allclose(Hs[1], out.numpy(), rtol=1e-11, atol=1e-11)
 
 
+# The bf16 storage points of a layer: every projection input (RMSNorm outputs, the attention
+# output, the SwiGLU product), Q/K/V of the token rows and the residual stream h' and out.
+BF16_POINTS = ("a", "q", "k", "v", "o", "hp", "b", "act", "out")
+
+
+def _torch_layer_bf16(x, T, hq, hkv, dh, skip=None):
+    """One layer in float64 torch modules with a bfloat16 cast at each named point."""
+    def c(t, name):
+        return t if name == skip else t.to(torch.bfloat16).to(torch.float64)
+    n, d = x.shape
+    a = c(F.rms_norm(x, (d,), eps=1e-6), "a")
+    q = c(F.linear(a, T["wq"]), "q").view(n, hq, dh).permute(1, 0, 2)
+    k = c(F.linear(a, T["wk"]), "k").view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    v = c(F.linear(a, T["wv"]), "v").view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    o = c(F.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).reshape(n, hq * dh), "o")
+    hp = c(x + F.linear(o, T["wo"]), "hp")
+    b = c(F.rms_norm(hp, (d,), eps=1e-6), "b")
+    act = c(F.silu(F.linear(b, T["wg"])) * F.linear(b, T["wu"]), "act")
+    return c(hp + F.linear(act, T["wd"]), "out")
+
+
+def test_full_forward_bf16_rounds_at_the_storage_points():
+    d, hq, hkv, dh, f, n = 32, 4, 2, 8, 48, 11
+    cfg = O.Cfg(d=d, n_heads=hq, n_kv_heads=hkv, head_dim=dh, ffn=f, n_pos=n, block=4,
+                win_prefix=4, win_suffix=2, n_clusters=2, top_k=1, dtype="bf16")
+    rng = np.random.default_rng(41)
+    W = {"wq": rng.normal(size=(hq * dh, d)) / 6, "wk": rng.normal(size=(hkv * dh, d)) / 6,
+         "wv": rng.normal(size=(hkv * dh, d)) / 6, "wo": rng.normal(size=(d, hq * dh)) / 6,
+         "wg": rng.normal(size=(f, d)) / 6, "wu": rng.normal(size=(f, d)) / 6, "wd": rng.normal(size=(d, f)) / 6}
+    h0 = O.round_bf16(rng.normal(size=(n, d)))
+    Hs, Ks, Vs, _ = O.full_forward(h0, [W], cfg)
+    T = {k: torch.tensor(v) for k, v in W.items()}
+    want = _torch_layer_bf16(torch.tensor(h0), T, hq, hkv, dh).numpy()
+    assert np.array_equal(O.round_bf16(Hs[1]), Hs[1])
+    assert np.allclose(Hs[1], want, rtol=1e-12, atol=1e-12)
+    # every point matters: dropping any one cast moves the output off the oracle's
+    for p in BF16_POINTS:
+        other = _torch_layer_bf16(torch.tensor(h0), T, hq, hkv, dh, skip=p).numpy()
+        assert not np.allclose(Hs[1], other, rtol=0, atol=1e-9), f"rounding of {p} has no effect"
+
+
 # ---------------------------------------------------------------- rounding
 def test_round_bf16_matches_torch_on_fp32_values():
     x = (RNG.normal(size=20000) * np.exp(RNG.uniform(-20, 20, size=20000))).astype(np.float32)
@@ -478,7 +519,8 @@ def test_kv_rows_follow_fresh_packet():
     u = O.round_bf16(RNG.normal(size=(5, 32)))
     wk, wv = RNG.normal(size=(16, 32)), RNG.normal(size=(16, 32))
     k, v = O.kv_rows(u, wk, wv, cfg)
-    want = F.linear(F.rms_norm(torch.tensor(u), (32,), eps=1e-6), torch.tensor(wk)).to(torch.float32)
-    # every stored value is a bf16 number within half a bf16 ulp of the exact projection
+    a = F.rms_norm(torch.tensor(u), (32,), eps=1e-6).to(torch.bfloat16).to(torch.float64)
+    want = F.linear(a, torch.tensor(wk)).numpy()
+    # the projection of the bf16-rounded normalised rows, itself rounded once to bf16
     assert np.array_equal(O.round_bf16(k.reshape(5, 16)), k.reshape(5, 16))
-    assert np.allclose(k.reshape(5, 16), want.numpy(), rtol=2 ** -8, atol=1e-6)
+    assert np.array_equal(k.reshape(5, 16), O.round_bf16(want))
