@@ -65,9 +65,8 @@ void layout(polestar_handle* h) {
   w.win_rows = take(Bt * h->win_max * d.d * T);
   w.flags = take(Bt * h->win_max * 4);
   w.a_qkv = take(Bt * h->mq * d.d * T);
-  w.inv_qkv = take(Bt * h->mq * 4);
   w.q = take(Bt * h->mq * (size_t)h->nq * 4);
-  w.o = take(Bt * h->mt * (size_t)h->nq * 4);
+  w.o = take(Bt * h->mt * (size_t)h->nq * 4);    // float32 rows, or two bf16 planes
   w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
   w.akl = take(Bt * d.block * d.n_heads * 4);
   w.lg = take(Bt * (size_t)(d.n_clusters + d.block) * d.n_heads * d.n_pos * 4);
@@ -81,25 +80,23 @@ void layout(polestar_handle* h) {
     part = std::max(part, (size_t)h->ks_kv * Bt * h->win_max * 2 * (size_t)h->nkv);
   }
   w.part = take(part * 4);
-  w.hp = take(Bt * h->mt * d.d * 4);
-  w.hp_pl = take(d.dtype == POLESTAR_BF16 ? Bt * 2 * h->mt * d.d * 2 : 0);
+  w.hp = take(Bt * h->mt * d.d * 4);          // h' (float32)
+  w.a_gu = take(Bt * h->mt * d.d * 4);        // RMSNorm(h'): float32 rows, or two bf16 planes
   w.attn_part = take(d.dtype == POLESTAR_BF16 && h->attn_nchunks > 1
                          ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->mt * (d.head_dim + 2) * 4
                          : 0);
-  w.inv_hp = take(Bt * h->mt * (size_t)row_reduce_chunks(d.d) * 4);   // sum-of-squares chunks of h'
-  w.act = take(Bt * h->mt * (size_t)d.ffn * 4);
-  w.inv_out = take(Bt * h->mt * (size_t)row_reduce_chunks(d.d) * 4);  // sum-of-squares chunks of out
+  w.act = take(Bt * h->mt * (size_t)d.ffn * 4);   // float32 rows, or two bf16 planes
+  w.a_kv = take(Bt * h->win_max * d.d * T);   // round(RMSNorm(U)): next-layer K/V input
   w.xhat = take(Bt * h->win_max * d.d * 8);
   w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
   w.wstat = take(Bt * (h->win_max + (size_t)d.n_clusters * PS_CEIL_DIV(d.d, 256)) * 8);
   const size_t lm_rows = d.block + d.win_suffix;
   if (d.vocab > 0) {
     w.lm_a = take(Bt * lm_rows * d.d * T);
-    w.lm_inv = take(Bt * lm_rows * 4);
     w.lm_stats = take(Bt * lm_rows * (size_t)h->lm_tiles * 4 * 4);
     w.lm_meta = take(Bt * 2 * 4);
   } else {
-    w.lm_a = w.lm_inv = w.lm_stats = w.lm_meta = 0;
+    w.lm_a = w.lm_stats = w.lm_meta = 0;
   }
   w.total = off;
 }
@@ -190,7 +187,6 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.ws_rows = at<char>(ws, h->ws.win_rows);
   p.win_z = L->win_z;
   p.a_qkv = at<char>(ws, h->ws.a_qkv);
-  p.inv = at<float>(ws, h->ws.inv_qkv);
   p.eps = h->pr.rms_eps;
   hipError_t e;
   {
@@ -214,8 +210,6 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   EpiParams ep;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_QKV;
-  ep.inv_rms = p.inv;
-  ep.inv_bstride = h->mq;
   ep.q = at<float>(ws, h->ws.q);
   ep.q_rows = h->mq;
   ep.kc = L->k_cache;
@@ -318,8 +312,8 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   return hip_status(launch_topk(tk, s));
 }
 
-// bf16 storage: projections by the weight-streaming kernel; float32 activations travel as
-// bf16 hi/lo planes between the projections.
+// bf16 storage: projections by the weight-streaming kernel; the float32 values inside the call
+// (attention output, RMSNorm(h'), SwiGLU product) travel as bf16 hi/lo planes.
 int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
                   const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
                   void* u_rows, void* ws, hipStream_t s) {
@@ -327,6 +321,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
   const int max_rows = d.block + g.n_win;
+  const bool kv_next = w_kv_next && g.n_win > 0;
   float* part = at<float>(ws, h->ws.part);
   hipError_t e;
   // 1. h' = h + o W_O^T over rows [active; S]
@@ -377,11 +372,12 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.out_a_bstride = (int64_t)h->mt * d.d;
   rr.out_split = h->mt;
   rr.out_f32 = 1;
-  rr.out_pl = at<uint16_t>(ws, h->ws.hp_pl);
-  rr.pl_stride = (int64_t)h->mt * d.d;
-  rr.pl_bstride = 2 * rr.pl_stride;
-  rr.ss_out = at<float>(ws, h->ws.inv_hp);
-  rr.ss_bstride = h->mt;
+  rr.norm = at<char>(ws, h->ws.a_gu);
+  rr.norm_planes = 1;
+  rr.norm_plane_stride = (int64_t)h->mt * d.d;
+  rr.norm_bstride = 2 * rr.norm_plane_stride;
+  rr.norm_from = 0;
+  rr.eps = h->pr.rms_eps;
   rr.chk = h->chk.hp;
   rr.chk_rows = h->mt;
   {
@@ -389,11 +385,11 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
     e = launch_row_reduce<T>(rr, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 2. act = silu(g) * u with g, u the projections of RMSNorm(h'), stored as hi/lo planes
+  // 2. act = silu(g) * u with g, u the projections of RMSNorm(h')
   memset(&dl, 0, sizeof(dl));
-  dl.A.base = rr.out_pl;
-  dl.A.plane_stride = rr.pl_stride;
-  dl.A.bstride = rr.pl_bstride;
+  dl.A.base = rr.norm;
+  dl.A.plane_stride = rr.norm_plane_stride;
+  dl.A.bstride = rr.norm_bstride;
   dl.A.lda = d.d;
   dl.A.rows_dev = sel->count;
   dl.A.rows_add = d.block;
@@ -407,11 +403,6 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.part = part;
   dl.part_rows = h->mt;
   dl.e.kind = EPI_SWIGLU;
-  dl.e.ss_in = rr.ss_out;
-  dl.e.ss_chunks = row_reduce_chunks(d.d);
-  dl.e.ss_d = (float)d.d;
-  dl.e.eps = h->pr.rms_eps;
-  dl.e.inv_bstride = h->mt;
   dl.e.act = at<char>(ws, h->ws.act);
   dl.e.act_rows = h->mt;
   dl.e.ffn = d.ffn;
@@ -426,11 +417,10 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 3. out = h' + act W_down^T -> next active rows and the update packet
-  const int64_t act_plane = (int64_t)h->mt * d.ffn;
   memset(&dl, 0, sizeof(dl));
   dl.A.base = at<char>(ws, h->ws.act);
-  dl.A.plane_stride = act_plane;
-  dl.A.bstride = 2 * act_plane;
+  dl.A.plane_stride = (int64_t)h->mt * d.ffn;
+  dl.A.bstride = 2 * dl.A.plane_stride;
   dl.A.lda = d.ffn;
   dl.A.rows_dev = sel->count;
   dl.A.rows_add = d.block;
@@ -449,33 +439,35 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
     e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // the residual stream continues from the unrounded h'
+  // the residual stream continues from the float32 h'
   RowReduceArgs r2 = rr;
   r2.ksplit = h->ks_down;
   r2.res_a = rr.out_a;
   r2.res_a_f32 = 1;
   r2.res_a_bstride = (int64_t)h->mt * d.d;
   r2.res_split = h->mt;
-  r2.out_f32 = 0;
-  r2.out_pl = nullptr;
   r2.res_b = nullptr;
   r2.out_a = h_active_out;
   r2.out_a_bstride = (int64_t)d.block * d.d;
   r2.out_split = d.block;
   r2.out_b = u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
-  r2.ss_out = at<float>(ws, h->ws.inv_out);
+  r2.out_f32 = 0;
+  r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only, rounded
+  r2.norm_planes = 0;
+  r2.norm_bstride = (int64_t)h->win_max * d.d;
+  r2.norm_from = d.block;
   r2.chk = h->chk.out;
   {
     PROF(POLESTAR_K_DREDUCE);
     e = launch_row_reduce<T>(r2, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 4. K/V of layer l+1 for the packet rows
-  if (w_kv_next && g.n_win > 0) {
+  // 4. K/V of layer l+1 for the packet rows, from round(RMSNorm(U))
+  if (kv_next) {
     memset(&dl, 0, sizeof(dl));
-    dl.A.base = u_rows;
-    dl.A.bstride = (int64_t)h->win_max * d.d;
+    dl.A.base = r2.norm;
+    dl.A.bstride = r2.norm_bstride;
     dl.A.lda = d.d;
     dl.A.rows_dev = sel->count;
     dl.A.rows_max = g.n_win;
@@ -488,12 +480,6 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
     dl.part = part;
     dl.part_rows = h->win_max;
     dl.e.kind = EPI_KV;
-    dl.e.ss_in = r2.ss_out;
-    dl.e.ss_chunks = row_reduce_chunks(d.d);
-    dl.e.ss_d = (float)d.d;
-    dl.e.eps = h->pr.rms_eps;
-    dl.e.inv_bstride = h->mt;
-    dl.e.inv_off = d.block;
     dl.e.kc = k_next;
     dl.e.vc = v_next;
     dl.e.nkv = h->nkv;
@@ -522,12 +508,12 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
   const int max_rows = d.block + g.n_win;
+  const bool kv_next = w_kv_next && g.n_win > 0;
   float* part = at<float>(ws, h->ws.part);
   // 1. h' = h + o W_O^T over rows [active; S]
   GemmArgs ga;
   memset(&ga, 0, sizeof(ga));
   ga.A.base = at<char>(ws, h->ws.o);
-  ga.A.f32 = 1;
   ga.A.bstride = (int64_t)h->mt * h->nq;
   ga.A.lda = h->nq;
   ga.A.rowmap = sel->idx;
@@ -573,8 +559,10 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.out_a_bstride = (int64_t)h->mt * d.d;
   rr.out_split = h->mt;
   rr.out_f32 = 1;
-  rr.ss_out = at<float>(ws, h->ws.inv_hp);
-  rr.ss_bstride = h->mt;
+  rr.norm = at<char>(ws, h->ws.a_gu);
+  rr.norm_bstride = (int64_t)h->mt * d.d;
+  rr.norm_from = 0;
+  rr.eps = h->pr.rms_eps;
   rr.chk = h->chk.hp;
   rr.chk_rows = h->mt;
   {
@@ -584,9 +572,8 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 2. act = silu(g) * u with g, u the projections of RMSNorm(h')
   memset(&ga, 0, sizeof(ga));
-  ga.A.base = rr.out_a;
-  ga.A.f32 = 1;
-  ga.A.bstride = (int64_t)h->mt * d.d;
+  ga.A.base = rr.norm;
+  ga.A.bstride = rr.norm_bstride;
   ga.A.lda = d.d;
   ga.A.rows_dev = sel->count;
   ga.A.rows_add = d.block;
@@ -598,11 +585,6 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.ksplit = 1;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_SWIGLU;
-  ep.ss_in = rr.ss_out;
-  ep.ss_chunks = row_reduce_chunks(d.d);
-  ep.ss_d = (float)d.d;
-  ep.eps = h->pr.rms_eps;
-  ep.inv_bstride = h->mt;
   ep.act = at<char>(ws, h->ws.act);
   ep.act_rows = h->mt;
   ep.ffn = d.ffn;
@@ -614,7 +596,6 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&ga, 0, sizeof(ga));
   ga.A.base = ep.act;
-  ga.A.f32 = 1;
   ga.A.bstride = (int64_t)h->mt * d.ffn;
   ga.A.lda = d.ffn;
   ga.A.rows_dev = sel->count;
@@ -634,31 +615,32 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     e = launch_gemm<T>(ga, ep, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // the residual stream continues from the unrounded h'
   RowReduceArgs r2 = rr;
   r2.res_a = rr.out_a;
   r2.res_a_f32 = 1;
   r2.res_a_bstride = (int64_t)h->mt * d.d;
   r2.res_split = h->mt;
-  r2.out_f32 = 0;
   r2.res_b = nullptr;
   r2.out_a = h_active_out;
   r2.out_a_bstride = (int64_t)d.block * d.d;
   r2.out_split = d.block;
   r2.out_b = u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
-  r2.ss_out = at<float>(ws, h->ws.inv_out);
+  r2.out_f32 = 0;
+  r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only
+  r2.norm_bstride = (int64_t)h->win_max * d.d;
+  r2.norm_from = d.block;
   r2.chk = h->chk.out;
   {
     PROF(POLESTAR_K_DREDUCE);
     e = launch_row_reduce<T>(r2, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 4. K/V of layer l+1 for the packet rows
-  if (w_kv_next && g.n_win > 0) {
+  // 4. K/V of layer l+1 for the packet rows, from RMSNorm(U)
+  if (kv_next) {
     memset(&ga, 0, sizeof(ga));
-    ga.A.base = u_rows;
-    ga.A.bstride = (int64_t)h->win_max * d.d;
+    ga.A.base = r2.norm;
+    ga.A.bstride = r2.norm_bstride;
     ga.A.lda = d.d;
     ga.A.rows_dev = sel->count;
     ga.A.rows_max = g.n_win;
@@ -669,12 +651,6 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     ga.ksplit = 1;
     memset(&ep, 0, sizeof(ep));
     ep.kind = EPI_KV;
-    ep.ss_in = r2.ss_out;
-    ep.ss_chunks = row_reduce_chunks(d.d);
-    ep.ss_d = (float)d.d;
-    ep.eps = h->pr.rms_eps;
-    ep.inv_bstride = h->mt;
-    ep.inv_off = d.block;
     ep.kc = k_next;
     ep.vc = v_next;
     ep.nkv = h->nkv;
@@ -718,7 +694,6 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
     lp.u_count = u_final->count;
   }
   lp.a_lm = at<char>(ws, h->ws.lm_a);
-  lp.inv = at<float>(ws, h->ws.lm_inv);
   lp.meta = at<int32_t>(ws, h->ws.lm_meta);
   lp.eps = h->pr.rms_eps;
   hipError_t e;
@@ -742,8 +717,6 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   EpiParams ep;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_LMSTAT;
-  ep.inv_rms = lp.inv;
-  ep.inv_bstride = lm_rows;
   ep.lm_stats = at<float>(ws, h->ws.lm_stats);
   ep.lm_rows = lm_rows;
   ep.lm_tiles = h->lm_tiles;
@@ -974,6 +947,9 @@ int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int3
   if (nv ? (!L->win_codes || !L->win_scales) : !L->win_h) return POLESTAR_E_NULL;
   if (mode == POLESTAR_CLUSTER_ENTRY && (!init_idx || !entry_h)) return POLESTAR_E_NULL;
   if (u_in && (!u_in->rows || !u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
+  if (!aligned16(L->win_z) || (!nv && !aligned16(L->win_h)) || (entry_h && !aligned16(entry_h)) ||
+      (u_in && !aligned16(u_in->rows)))
+    return POLESTAR_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
              ? do_cluster<bf16_t>(h, mode, L, blk_start, u_in, init_idx, entry_h, objective, ws, s)
@@ -991,6 +967,7 @@ int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_
   if (!L->w_qkv || !L->k_cache || !L->v_cache) return POLESTAR_E_NULL;
   if (mode == POLESTAR_DRIFT_REFRESH && (!L->win_z || !L->win_m || !L->proxy_logits)) return POLESTAR_E_NULL;
   if (!aligned16(L->w_qkv) || !aligned16(h_active)) return POLESTAR_E_ALIGN;
+  if (mode == POLESTAR_DRIFT_REFRESH && !aligned16(L->win_z)) return POLESTAR_E_ALIGN;
   if (delta && !act_logits) return POLESTAR_E_NULL;
   if (u_in && (!u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
   hipStream_t s = (hipStream_t)stream;
@@ -1009,7 +986,7 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
   if (!L->w_o || !L->w_gu || !L->w_down) return POLESTAR_E_NULL;
   if (w_kv_next && (!k_next || !v_next)) return POLESTAR_E_NULL;
   if (!aligned16(L->w_o) || !aligned16(L->w_gu) || !aligned16(L->w_down) || !aligned16(h_active) ||
-      !aligned16(u_rows) || (w_kv_next && !aligned16(w_kv_next)))
+      !aligned16(h_active_out) || !aligned16(u_rows) || (w_kv_next && !aligned16(w_kv_next)))
     return POLESTAR_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
@@ -1030,7 +1007,7 @@ int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, con
   if (rc) return rc;
   if ((rc = check_blk(h, blk_start))) return rc;
   if (u_final && (!u_final->rows || !u_final->idx || !u_final->count)) return POLESTAR_E_NULL;
-  if (!aligned16(w_lm) || !aligned16(h_final)) return POLESTAR_E_ALIGN;
+  if (!aligned16(w_lm) || !aligned16(h_final) || (u_final && !aligned16(u_final->rows))) return POLESTAR_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
              ? do_commit<bf16_t>(h, blk_start, w_lm, h_final, u_final, delta, active_masked, suffix_masked,

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
   }
 }
 
-// ---- QKV rows: [active; window; centroids] + 1/rms ---------------------------------------------
+// ---- QKV input rows: round(RMSNorm(x)) of [active; window; centroids] ---------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   __shared__ float red[4];
@@ -276,16 +276,7 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   if (r < a.block) src = (const T*)a.h_act + ((int64_t)b * a.block + r) * d;
   else if (r < a.block + a.n_win) src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + (r - a.block)) * d;
   else src = (const T*)a.win_z + ((int64_t)b * a.K + (r - a.block - a.n_win)) * d;
-  T* dst = (T*)a.a_qkv + ((int64_t)b * a.mq + r) * d;
-  float ss = 0.f;
-  for (int n = threadIdx.x; n < d; n += blockDim.x) {
-    const T v = src[n];
-    dst[n] = v;
-    const float x = St<T>::load(&v, 0);
-    ss += x * x;
-  }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) a.inv[(int64_t)b * a.mq + r] = 1.f / sqrtf(ss / (float)d + a.eps);
+  rmsnorm_row<T>(src, (T*)a.a_qkv + ((int64_t)b * a.mq + r) * d, d, a.eps, red);
 }
 
 // ---- NVFP4 test hooks ---------------------------------------------------------------------------

@@ -31,16 +31,7 @@ __global__ __launch_bounds__(256) void lm_prep_kernel(LmPrepArgs a, int32_t* met
     if (j >= cnt_sh) return;
     src = (const T*)a.u_rows + ((int64_t)b * a.win_max + j) * d;
   }
-  T* dst = (T*)a.a_lm + ((int64_t)b * a.lm_rows + r) * d;
-  float ss = 0.f;
-  for (int n = threadIdx.x; n < d; n += blockDim.x) {
-    const T v = src[n];
-    dst[n] = v;
-    const float x = St<T>::load(&v, 0);
-    ss += x * x;
-  }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) a.inv[(int64_t)b * a.lm_rows + r] = 1.f / sqrtf(ss / (float)d + a.eps);
+  rmsnorm_row<T>(src, (T*)a.a_lm + ((int64_t)b * a.lm_rows + r) * d, d, a.eps, red);
 }
 
 // Combine per-tile (max, sum exp, best non-mask logit, its id) in tile order.

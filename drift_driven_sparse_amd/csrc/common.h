@@ -89,6 +89,49 @@ PS_DEV V block_sum(V v, V* red) {
   return s;
 }
 
+// ---- rows in the storage dtype ----------------------------------------------
+// Four consecutive elements as float32 (8- or 16-byte accesses).
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+  static PS_DEV void load(const float* p, float* x) {
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  static PS_DEV void store(float* p, const float* x) { *(float4*)p = make_float4(x[0], x[1], x[2], x[3]); }
+};
+template <> struct Quad<bf16_t> {
+  static PS_DEV void load(const bf16_t* p, float* x) {
+    const uint2 v = *(const uint2*)p;
+    x[0] = bf16_to_f32(v.x & 0xFFFFu); x[1] = bf16_to_f32(v.x >> 16);
+    x[2] = bf16_to_f32(v.y & 0xFFFFu); x[3] = bf16_to_f32(v.y >> 16);
+  }
+  static PS_DEV void store(bf16_t* p, const float* x) {
+    *(uint2*)p = make_uint2((uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16),
+                            (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16));
+  }
+};
+
+// RMSNorm with unit gain of one row of d elements (d a multiple of 4), rounded to the storage
+// dtype: dst = round(src * 1/sqrt(mean(src^2) + eps)).  Every thread of the block takes part;
+// `red` holds one float per wave.
+template <typename T>
+PS_DEV void rmsnorm_row(const T* src, T* dst, int d, float eps, float* red) {
+  float ss = 0.f;
+  for (int n = 4 * threadIdx.x; n < d; n += 4 * blockDim.x) {
+    float x[4];
+    Quad<T>::load(src + n, x);
+    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  for (int n = 4 * threadIdx.x; n < d; n += 4 * blockDim.x) {
+    float x[4];
+    Quad<T>::load(src + n, x);
+    x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;
+    Quad<T>::store(dst + n, x);
+  }
+}
+
 // ---- window geometry -------------------------------------------------------
 // Window row w -> sequence position: first the prefix rows, then the suffix rows.
 struct WinGeom {

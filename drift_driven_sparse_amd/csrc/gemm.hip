@@ -78,11 +78,9 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
       const int p = j >> 4, jj = j & 15;
       const int oc = (n0 >> 1) + j;
       if (oc >= e.ffn) continue;
-      const float s = row_scale(e, b, r);
-      const float gv = tile[r * kLDT + (2 * p) * 16 + jj] * s;
-      const float uv = tile[r * kLDT + (2 * p + 1) * 16 + jj] * s;
-      const float a = gv / (1.f + expf(-gv)) * uv;
-      ((float*)e.act)[((int64_t)b * e.act_rows + r) * e.ffn + oc] = a;
+      const float gv = tile[r * kLDT + (2 * p) * 16 + jj];
+      const float uv = tile[r * kLDT + (2 * p + 1) * 16 + jj];
+      St<T>::store((T*)e.act, ((int64_t)b * e.act_rows + r) * e.ffn + oc, gv / (1.f + expf(-gv)) * uv);
     }
   } else if constexpr (KIND == EPI_KV) {
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
@@ -96,8 +94,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
     for (int r = wave; r < rows_b; r += nwave) {
       const int n = n0 + lane;
       const bool valid = n < e.vocab;
-      const float s = row_scale(e, b, r);
-      const float l = valid ? tile[r * kLDT + lane] * s : -INFINITY;
+      const float l = valid ? tile[r * kLDT + lane] : -INFINITY;
       const float m = wave_max(l);
       const float se = wave_sum(valid ? expf(l - m) : 0.f);
       const float lb = (valid && n != e.mask_id) ? l : -INFINITY;
@@ -122,22 +119,6 @@ PS_DEV floatx4_t mfma(uint4 a, uint4 w, floatx4_t c) {
                                                  0, 0, 0);
 }
 
-// Split 8 float32 values into bf16 hi (round to nearest) and lo = bf16(x - hi):
-// hi + lo reproduces x to 2^-18 relative.
-PS_DEV void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
-  const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t h0 = f32_to_bf16(xs[2 * i]), h1 = f32_to_bf16(xs[2 * i + 1]);
-    const uint16_t l0 = f32_to_bf16(xs[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(xs[2 * i + 1] - bf16_to_f32(h1));
-    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
 // Each wave walks its K range in 32-wide steps.  Weight fragments are kept in a
 // ring of kDW steps and the activation fragments of the next step are loaded
 // while the current one is multiplied, so a wave always has several KiB of
@@ -145,11 +126,9 @@ PS_DEV void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
 // (valid addresses, results unused) so the loop body has no load branches.
 constexpr int kDW = 4;   // weight prefetch depth in 32-wide K steps
 
-template <typename T, int RT, int KIND, int AF32>
+template <typename T, int RT, int KIND>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e) {
   constexpr int NSUB = kNT / 16;
-  constexpr int AW = AF32 ? 2 : 1;        // 16-byte A pieces per lane, row tile and step
-  constexpr int ASTEP = AF32 ? 8 : 4;     // 16-byte units per 32 elements of a row
   __shared__ float tile[RT * 16 * kLDT];
   const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
@@ -162,8 +141,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
   const int w0 = s0 + (s1 - s0) * wave / 4, w1 = s0 + (s1 - s0) * (wave + 1) / 4;
   const int wlast = w1 > 0 ? w1 - 1 : 0;
 
-  typedef typename std::conditional<AF32 != 0, float, uint16_t>::type AE;
-  const AE* Ab = (const AE*)g.A.base + (int64_t)b * g.A.bstride;
+  const uint16_t* Ab = (const uint16_t*)g.A.base + (int64_t)b * g.A.bstride;
   const uint4* arow[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -188,35 +166,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
     for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   uint4 wr[kDW][NSUB];
-  uint4 ar[2][RT][AW];
+  uint4 ar[2][RT];
   auto load_w = [&](uint4 (&w)[NSUB], int st) {
     st = st < wlast ? st : wlast;
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) w[sb] = Wsub[sb][(int64_t)st * 64];
   };
-  auto load_a = [&](uint4 (&a)[RT][AW], int st) {
+  auto load_a = [&](uint4 (&a)[RT], int st) {
     st = st < wlast ? st : wlast;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int q = 0; q < AW; ++q) a[rt][q] = arow[rt][st * ASTEP + q];
+    for (int rt = 0; rt < RT; ++rt) a[rt] = arow[rt][st * 4];
   };
-  auto compute = [&](const uint4 (&w)[NSUB], const uint4 (&a)[RT][AW]) {
+  auto compute = [&](const uint4 (&w)[NSUB], const uint4 (&a)[RT]) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (rt < nrt) {
-        if constexpr (AF32 != 0) {
-          uint4 hi, lo;
-          split8(__builtin_bit_cast(float4, a[rt][0]), __builtin_bit_cast(float4, a[rt][1]), hi, lo);
 #pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb) {
-            acc[rt][sb] = mfma(hi, w[sb], acc[rt][sb]);
-            acc[rt][sb] = mfma(lo, w[sb], acc[rt][sb]);
-          }
-        } else {
-#pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(a[rt][0], w[sb], acc[rt][sb]);
-        }
+        for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(a[rt], w[sb], acc[rt][sb]);
       }
     }
   };
@@ -292,8 +258,7 @@ hipError_t launch_one(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
   if constexpr (std::is_same<T, float>::value) {
     hipLaunchKernelGGL((gemm_f32_kernel<RT, KIND>), grid, dim3(256), 0, s, g, e);
   } else {
-    if (g.A.f32) hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND, 1>), grid, dim3(256), 0, s, g, e);
-    else hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND, 0>), grid, dim3(256), 0, s, g, e);
+    hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND>), grid, dim3(256), 0, s, g, e);
   }
   return hipGetLastError();
 }
@@ -311,23 +276,22 @@ hipError_t dispatch_kind(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
 }
 
 // ---- split-K row reduction ------------------------------------------------------------------
-// Workgroup = (row, 1024-column chunk): partial sums (added in split order) + residual, stored
-// as float32 or rounded to the storage dtype, optionally also as bf16 hi/lo planes, and the sum
-// of squares of the stored chunk (the next projection's RMSNorm adds the chunks in order).
-constexpr int kRrCols = 1024;
-
+// Workgroup = one row: partial sums (added in split order) + residual, kept as float32 or
+// rounded to the storage dtype; rows from norm_from on also get RMSNorm of the stored row, the
+// input of the next projection (bf16 hi/lo planes of the float32 value, or rounded to the
+// storage dtype).  Each thread re-reads only the elements it stored itself.
 template <typename T>
-__global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
-  __shared__ float red[4];
-  const int r = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
+  __shared__ float red[16];
+  const int r = blockIdx.x, b = blockIdx.y;
   int rows_b = a.block + (a.count ? a.count[b] : 0);
   if (rows_b > (int)gridDim.x) rows_b = gridDim.x;
   if (r >= rows_b) return;
-  const T* res = nullptr;
-  const float* res32 = nullptr;
+  const void* res;
+  bool res32 = false;
   if (r < a.res_split) {
-    if (a.res_a_f32) res32 = (const float*)a.res_a + (int64_t)b * a.res_a_bstride + (int64_t)r * a.d;
-    else res = (const T*)a.res_a + (int64_t)b * a.res_a_bstride + (int64_t)r * a.d;
+    res32 = a.res_a_f32 != 0;
+    res = (const char*)a.res_a + ((int64_t)b * a.res_a_bstride + (int64_t)r * a.d) * (res32 ? 4 : sizeof(T));
   } else {
     int src = a.sel_idx[(int64_t)b * a.win_max + r - a.res_split];
     src = (src < 0 || src >= a.win_max) ? 0 : src;
@@ -336,47 +300,58 @@ __global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
   const int64_t ooff = (r < a.out_split) ? (int64_t)b * a.out_a_bstride + (int64_t)r * a.d
                                          : (int64_t)b * a.out_b_bstride + (int64_t)(r - a.out_split) * a.d;
   void* obase = (r < a.out_split) ? a.out_a : a.out_b;
-  uint16_t* pl = (a.out_pl && r < a.out_split) ? a.out_pl + (int64_t)b * a.pl_bstride + (int64_t)r * a.d : nullptr;
   const int64_t pstride = (int64_t)a.batch * a.part_rows * a.d;
   const float* p = a.part + ((int64_t)b * a.part_rows + r) * a.d;
+  float* chk = a.chk ? a.chk + ((int64_t)b * a.chk_rows + r) * a.d : nullptr;
+  auto load_out = [&](int n, float* x) {
+    if (a.out_f32) Quad<float>::load((const float*)obase + ooff + n, x);
+    else Quad<T>::load((const T*)obase + ooff + n, x);
+  };
   float ss = 0.f;
-  const int n = chunk * kRrCols + threadIdx.x * 4;
-  if (n < a.d) {
+  for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
     float4 v = *(const float4*)(p + n);
     for (int s = 1; s < a.ksplit; ++s) {
       const float4 t = *(const float4*)(p + s * pstride + n);
       v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
     }
-    float vv[4] = {v.x, v.y, v.z, v.w};
+    float x[4];
+    if (res32) Quad<float>::load((const float*)res + n, x);
+    else Quad<T>::load((const T*)res + n, x);
+    x[0] += v.x; x[1] += v.y; x[2] += v.z; x[3] += v.w;
+    if (chk) *(float4*)(chk + n) = make_float4(x[0], x[1], x[2], x[3]);
+    if (a.out_f32) {
+      Quad<float>::store((float*)obase + ooff + n, x);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = vv[i] + (res32 ? res32[n + i] : St<T>::load(res, n + i));
-      if (a.chk) a.chk[((int64_t)b * a.chk_rows + r) * a.d + n + i] = x;
-      float q;
-      if (a.out_f32) {
-        q = x;
-        ((float*)obase)[ooff + n + i] = x;
-      } else {
-        q = St<T>::round(x);
-        St<T>::store((T*)obase, ooff + n + i, x);
-      }
-      if (pl) {
-        uint16_t hi, lo;
-        split_bf16(x, hi, lo);
-        pl[n + i] = hi;
-        pl[a.pl_stride + n + i] = lo;
-      }
-      ss += q * q;
+      for (int i = 0; i < 4; ++i) x[i] = St<T>::round(x[i]);
+      Quad<T>::store((T*)obase + ooff + n, x);
+    }
+    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  }
+  if (!a.norm || r < a.norm_from) return;   // uniform over the workgroup
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)a.d + a.eps);
+  const int64_t noff = (int64_t)b * a.norm_bstride + (int64_t)(r - a.norm_from) * a.d;
+  for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
+    float x[4];
+    load_out(n, x);
+    x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;
+    if (a.norm_planes) {
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_bf16(x[i], hi[i], lo[i]);
+      uint16_t* pl = (uint16_t*)a.norm + noff + n;
+      *(uint2*)pl = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *(uint2*)(pl + a.norm_plane_stride) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    } else {
+      Quad<T>::store((T*)a.norm + noff + n, x);
     }
   }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0 && a.ss_out) a.ss_out[((int64_t)b * a.ss_bstride + r) * gridDim.y + chunk] = ss;
 }
 
 }  // namespace
 
 size_t packed_elems(int N, int K) { return (size_t)N * (size_t)K; }
-int row_reduce_chunks(int d) { return PS_CEIL_DIV(d, kRrCols); }
 
 template <typename T>
 hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s) {
@@ -404,7 +379,10 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 template <typename T>
 hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, PS_CEIL_DIV(a.d, kRrCols), a.batch), dim3(256), 0, s, a);
+  if (a.d % 4) return hipErrorInvalidValue;
+  int threads = 64 * PS_CEIL_DIV(a.d / 4, 64);
+  threads = threads > 1024 ? 1024 : threads;
+  hipLaunchKernelGGL(row_reduce_kernel<T>, dim3(max_rows, a.batch), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

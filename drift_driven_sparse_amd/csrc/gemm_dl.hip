@@ -15,9 +15,9 @@
 // fragments.  Fragments are 16x16x32 MFMA operands in lane order; weights are
 // pre-packed in that order, A rows are gathered per lane (any row map).
 //
-// float32 activations arrive as two bf16 planes (hi = rn(x), lo = rn(x - hi))
-// written by their producers; both planes are multiplied into the same float32
-// accumulators.
+// float32 activations (the attention output, RMSNorm(h') and the SwiGLU product)
+// arrive as two bf16 planes (hi = rn(x), lo = rn(x - hi)) written by their
+// producers; both planes are multiplied into the same float32 accumulators.
 //
 // With split-K (grid.z > 1) the raw sums go to row-major partial buffers that a
 // row kernel (O, down projections) or launch_dl_finish (QKV, gate/up, next-layer
@@ -200,8 +200,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
           const int r = row0 + rt * 16 + i;
           const int oc = ((nt * CG + cg) * NSUB / 2 + j) * 16 + (lane & 15);
           if (r < rows_b && oc < e.ffn) {
-            const float sc = row_scale(e, b, r);
-            const float gv = acc[rt][2 * j][i] * sc, uv = acc[rt][2 * j + 1][i] * sc;
+            const float gv = acc[rt][2 * j][i], uv = acc[rt][2 * j + 1][i];
             const float a = gv / (1.f + expf(-gv)) * uv;
             uint16_t hi, lo;
             split_bf16(a, hi, lo);
@@ -253,13 +252,12 @@ __global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
     gv.x += tg.x; gv.y += tg.y; gv.z += tg.z; gv.w += tg.w;
     uv.x += tu.x; uv.y += tu.y; uv.z += tu.z; uv.w += tu.w;
   }
-  const float sc = row_scale(e, b, r);
   const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
   const int64_t plane = (int64_t)e.act_rows * e.ffn;
   uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane + (int64_t)r * e.ffn + oc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x = ga[i] * sc, u = ua[i] * sc;
+    const float x = ga[i], u = ua[i];
     uint16_t hi, lo;
     split_bf16(x / (1.f + expf(-x)) * u, hi, lo);
     act[i] = hi;

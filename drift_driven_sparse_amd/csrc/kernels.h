@@ -4,8 +4,8 @@
 
 // Handle contents (host only).
 struct WsLayout {
-  size_t win_rows, flags, a_qkv, inv_qkv, q, o, kl, akl, lg, part, hp, inv_hp, act, inv_out, xhat, z64, wstat, hp_pl, attn_part,
-      lm_a, lm_inv, lm_stats, lm_meta, total;
+  size_t win_rows, flags, a_qkv, q, o, kl, akl, lg, part, hp, a_gu, act, a_kv, xhat, z64, wstat, attn_part, lm_a,
+      lm_stats, lm_meta, total;
 };
 
 struct ProfState;   // per-kernel event records (api.hip)
@@ -31,8 +31,7 @@ struct polestar_handle {
 //   r                                  when rowmap == nullptr or r < map_from
 //   map_off + rowmap[b*map_bstride + r - map_from]   otherwise.
 struct GemmA {
-  const void* base;
-  int32_t f32;           // rows are float32 (bf16 path: fed to MFMA as a hi + lo bf16 pair)
+  const void* base;      // rows in the storage dtype (bf16 projections: bf16 planes)
   int64_t plane_stride;  // bf16 plane layout: elements from the hi plane to the lo plane
   int64_t bstride;       // elements between sequences
   int32_t lda;           // elements between rows
@@ -70,13 +69,6 @@ enum EpiKind { EPI_PARTIAL = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_KV = 3, EPI_LMS
 
 struct EpiParams {
   int kind;
-  // row scale (RMSNorm as an output scale) of row r, with i = b*inv_bstride + inv_off + r:
-  // inv_rms[i], or from chunk sums of squares 1/sqrt(sum_c ss_in[i*ss_chunks + c] / ss_d + eps)
-  const float* inv_rms;
-  int32_t inv_bstride, inv_off;
-  const float* ss_in;
-  int32_t ss_chunks;
-  float ss_d, eps;
   // QKV
   float* q; int32_t q_rows;     // q[(b*q_rows + r)*nq + n]
   void* kc; void* vc;           // caches (storage dtype)
@@ -84,7 +76,8 @@ struct EpiParams {
   int32_t nq, nkv, block, win_max, n_pos, dh;
   WinGeom geom;
   float* chk; int32_t chk_rows, chk_ld;   // chk[(b*chk_rows + r)*chk_ld + n]
-  // SwiGLU
+  // SwiGLU product: float32 rows [batch][act_rows][ffn], or for bf16 storage the hi/lo planes
+  // [batch][2][act_rows][ffn]
   void* act; int32_t act_rows, ffn;
   // KV scatter of packet rows: dest pos = geom.pos(sel_idx[b*win_max + r])
   const int32_t* sel_idx;
@@ -99,19 +92,11 @@ PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
   return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
 }
 
-PS_DEV float row_scale(const EpiParams& e, int b, int r) {
-  const int64_t i = (int64_t)b * e.inv_bstride + e.inv_off + r;
-  if (!e.ss_in) return e.inv_rms[i];
-  float ss = 0.f;
-  for (int c = 0; c < e.ss_chunks; ++c) ss += e.ss_in[i * e.ss_chunks + c];
-  return 1.f / sqrtf(ss / e.ss_d + e.eps);
-}
-
-// QKV projection row r (active block, window rows, centroids), column n, raw sum v:
-// queries stay float32; K/V of the active block and of patched window rows go to the cache.
+// QKV projection row r (active block, window rows, centroids) of the rounded normalised row,
+// column n, sum v: queries stay float32; K/V of the active block and of patched window rows go
+// to the cache.
 template <typename T>
 PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
-  v *= e.inv_rms[(int64_t)b * e.inv_bstride + e.inv_off + r];
   if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
   if (n < e.nq) {
     e.q[((int64_t)b * e.q_rows + r) * e.nq + n] = v;
@@ -133,7 +118,6 @@ PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
 // K/V of the next layer for packet row r (window row sel_idx[r]).
 template <typename T>
 PS_DEV void epi_kv_elem(const EpiParams& e, int b, int r, int n, float v) {
-  v *= row_scale(e, b, r);
   if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
   const int which = n >= e.nkv;
   const int col = n - which * e.nkv;
@@ -154,7 +138,7 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 // ---- bf16 weight-streaming projection (gemm_dl.hip) ------------------------------------
 // A: bf16 planes (1 = bf16 rows, 2 = hi/lo of float32 rows), rows gathered per lane.
 // ksplit > 1: raw sums to part[((s*batch + b)*part_rows + r)*N + n], finished by
-// launch_dl_finish (QKV, KV) or the row reduction (O, down).
+// launch_dl_finish (QKV, gate/up, KV) or the row reduction (O, down).
 struct DlArgs {
   GemmA A;
   int32_t planes;
@@ -176,8 +160,9 @@ template <typename T>
 hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s);
 size_t packed_elems(int N, int K);
 
-// Row reductions after split-K projections: out = round(sum of partials + residual),
-// one row per workgroup, plus 1/rms of the stored row (RMSNorm of the next projection).
+// Row reductions after split-K projections, one row per workgroup: out = sum of partials in
+// split order + residual, kept as float32 or rounded to the storage dtype, and for rows
+// r >= norm_from also RMSNorm(out), the input of the next projection.
 struct RowReduceArgs {
   const float* part; int32_t ksplit, part_rows, batch, d;
   const int32_t* count;   // rows of seq b = block + count[b]
@@ -191,15 +176,16 @@ struct RowReduceArgs {
   void* out_a; int64_t out_a_bstride; int32_t out_split;
   void* out_b; int64_t out_b_bstride;
   int32_t out_f32;              // outputs are float32 rows (else storage dtype)
-  uint16_t* out_pl;             // also the bf16 hi/lo planes of out_a rows (or null)
-  int64_t pl_bstride, pl_stride;
-  // sums of squares of the stored row per 1024-column chunk: ss_out[(b*ss_bstride + r)*chunks + c]
-  float* ss_out; int32_t ss_bstride;
+  // RMSNorm of row r >= norm_from -> norm[b][r - norm_from] (null: none): float32 rows given as
+  // bf16 hi/lo planes norm_plane_stride elements apart when norm_planes, else rounded to the
+  // storage dtype
+  void* norm; int64_t norm_bstride; int32_t norm_from;
+  int32_t norm_planes; int64_t norm_plane_stride;
+  float eps;
   float* chk; int32_t chk_rows;
 };
 template <typename T>
 hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s);
-int row_reduce_chunks(int d);   // column chunks of the row reduction (sum-of-squares partials per row)
 
 // ---- window / clustering ----------------------------------------------------------
 struct ClusterArgs {
@@ -222,11 +208,11 @@ struct ClusterArgs {
 template <typename T>
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 
-// Active rows, window rows and centroids -> contiguous QKV A rows + 1/rms.
+// Active rows, window rows and centroids -> contiguous QKV input rows round(RMSNorm(x)).
 struct PrepArgs {
   int32_t batch, d, block, win_max, n_win, K, mq, refresh;
   const void* h_act; const void* ws_rows; const void* win_z;
-  void* a_qkv; float* inv; float eps;
+  void* a_qkv; float eps;
 };
 template <typename T>
 hipError_t launch_prep_qkv(const PrepArgs& a, hipStream_t s);
@@ -271,7 +257,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 struct LmPrepArgs {
   int32_t batch, d, block, win_max, win_suffix, n_pre, lm_rows;
   const void* h_final; const void* u_rows; const int32_t* u_idx; const int32_t* u_count;
-  void* a_lm; float* inv; int32_t* meta; float eps;   // meta[b*? ]: [n_rows, suffix start in packet]
+  void* a_lm; int32_t* meta; float eps;   // a_lm: round(RMSNorm(row)); meta: rows per sequence, suffix start
 };
 template <typename T>
 hipError_t launch_lm_prep(const LmPrepArgs& a, hipStream_t s);

@@ -35,6 +35,17 @@
  *   proxy logits         [batch, n_clusters, n_heads, n_pos] f32
  *   active-block logits  [batch, block, n_heads, n_pos] f32
  *   packed weights       produced by polestar_pack_weight (opaque layout)
+ * Precision: storage dtype f32 or bf16.  Rounded to it: tensors that
+ *   outlive a call (K/V caches, window rows, centroids, active outputs,
+ *   update packets) and the input of each projection of such a row, its
+ *   RMSNorm output with unit gain (QKV and proxy queries, next-layer K/V,
+ *   LM head).  Values produced and consumed inside one call (queries,
+ *   attention output, h', RMSNorm(h'), the SwiGLU product), logits, softmax,
+ *   KL and every accumulation are float32.  The pages fix no rounding points
+ *   (their full-precision baseline is a 16-bit model, Table 11).
+ * Alignment: row tensors (hidden rows, window rows, centroids, packets) and
+ *   packed weights start on 16-byte boundaries; a call that reads or writes
+ *   one row-wise checks it and returns POLESTAR_E_ALIGN otherwise.
  * Streams: every call enqueues asynchronously on the given hipStream_t
  *   (passed as void*; NULL = the null stream) and never synchronises.
  *   Outputs are valid once the caller synchronises that stream.  A handle is

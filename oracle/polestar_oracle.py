@@ -9,22 +9,25 @@ Efficient Inference of Diffusion LLMs" (arXiv 2607.14107).  Citations below
 name that page's sections, equations, tables and Algorithm 1.
 
 Everything is plain NumPy in float64.  The method is a heuristic iteration, so
-the oracle follows its steps in the page's order.  The page runs a bf16 model
-(App. B setup) without naming where values are rounded; the oracle takes the
-plain reading of a bf16 transformer and rounds (``st`` = round to the storage
-dtype, identity for "f64") at exactly these points:
-  * every projection input: the RMSNorm output (unit gain, eps) of the row,
-    ``st(x / rms(x))``, the attention output ``st(o)`` and the SwiGLU product
-    ``st(silu(g) * u)``;
-  * projection outputs of token rows: Q, K and V (K and V also as the cache);
-    the proxy queries of the centroids stay unrounded, as do the gate and up
-    projections, which live only inside the SwiGLU product;
-  * the residual stream: ``h' = st(h + st(o) Wo^T)`` and the layer output
-    ``out = st(h' + act Wd^T)`` (the active rows and the update packet U);
-  * centroids are stored after normalisation; attention logits that are kept
-    as the next step's reference are stored as float32;
+the oracle follows its steps in the page's order.  The page's full-precision
+baseline is a 16-bit model (Table 11) and it does not say where values are
+rounded.  The oracle rounds (``st`` = round to the storage dtype, identity for
+"f64") at exactly these points:
+  * tensors that outlive a call: the K/V cache, window rows, centroids (after
+    normalisation), the layer outputs ``out = st(h' + act Wd^T)`` (active rows
+    and update packet U); attention logits kept as the next step's reference
+    are stored as float32;
+  * the input of every projection of such a stored row, its RMSNorm output
+    (unit gain, eps): ``st(x / rms(x))`` for the QKV and proxy-query
+    projections of hidden rows and centroids, the next layer's K/V of U and the
+    LM head;
   * the NVFP4 codec and the commit rule are evaluated in float32, the
     precision in which the GPU takes those integer decisions.
+Values produced and consumed inside one call stay unrounded: the queries, the
+attention output ``o``, ``h' = h + o Wo^T``, RMSNorm(h') and the SwiGLU
+product ``act``.  (Rounding them too would chain five roundings inside one
+refresh call; each turns a deviation of relative size e between two correct
+implementations into one of about sqrt(e * 2^-8), which ends near 2e-3.)
 Softmax, log-sum-exp, KL and every accumulation stay in float64.
 Functions that only the mathematics pins are marked in their docstrings.
 """
@@ -436,8 +439,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     recomputed active-block KV; §4.1 proxy attention of the projected
     centroids over the same keys; Eq. 4 drift; top-k clusters and S.]
     Mutates the layer's K/V cache (active rows and patched window rows) and its
-    stored proxy logits.  Returns a dict of outputs; "o" is the attention output
-    of the token rows before its rounding.
+    stored proxy logits.  Returns a dict of outputs.
     """
     st, eps = cfg.st, cfg.eps
     jpos = active_positions(blk_start, cfg.B)
@@ -445,7 +447,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     nw = len(wpos)
     hq, hkv, dh = cfg.hq, cfg.hkv, cfg.dh
     toks = np.concatenate([h_act, h_win], axis=0) if refresh else np.asarray(h_act)
-    q = st(project(toks, W["wq"], eps, st)).reshape(-1, hq, dh)
+    q = project(toks, W["wq"], eps, st).reshape(-1, hq, dh)
     kr = st(project(toks, W["wk"], eps, st)).reshape(-1, hkv, dh)
     vr = st(project(toks, W["wv"], eps, st)).reshape(-1, hkv, dh)
     K, V = ls["K"], ls["V"]
@@ -479,21 +481,21 @@ def refresh_layer(W: Dict, cfg: Cfg, h_act: np.ndarray, h_win: np.ndarray, o_tok
 
     [§4.1: layer forward only over the hidden states of the top-k clusters;
     its outputs form the update packet for layer l+1.]  Rows are
-    [active block; S].  Returns the stored outputs (h_act_out, U) and the
-    values before their rounding (hp: h', out_pre: the layer output).
+    [active block; S].  Returns the stored outputs (h_act_out, U), the
+    layer output before its rounding (out_pre) and the unrounded h' and SwiGLU
+    product.
     """
     st, eps, B = cfg.st, cfg.eps, cfg.B
     S = np.asarray(S, dtype=np.int64)
     x = np.concatenate([h_act, h_win[S]], axis=0)
-    o = st(np.concatenate([o_tok[:B], o_tok[B + S]], axis=0))
-    hp_pre = x + o @ np.asarray(W["wo"], dtype=np.float64).T
-    hp = st(hp_pre)
-    g = project(hp, W["wg"], eps, st)
-    u = project(hp, W["wu"], eps, st)
-    act = st(silu(g) * u)
+    o = np.concatenate([o_tok[:B], o_tok[B + S]], axis=0)
+    hp = x + o @ np.asarray(W["wo"], dtype=np.float64).T
+    g = project(hp, W["wg"], eps)
+    u = project(hp, W["wu"], eps)
+    act = silu(g) * u
     out_pre = hp + act @ np.asarray(W["wd"], dtype=np.float64).T
     out = st(out_pre)
-    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp_pre, "act": act}
+    return {"h_act_out": out[:B], "U": out[B:], "out_pre": out_pre, "hp": hp, "act": act}
 
 
 def kv_rows(u: np.ndarray, wk: np.ndarray, wv: np.ndarray, cfg: Cfg):
@@ -594,13 +596,13 @@ def full_forward(h0: np.ndarray, layers: List[Dict], cfg: Cfg):
     Hs, Ks, Vs = [h], [], []
     logits = None
     for W in layers:
-        q = st(project(h, W["wq"], eps, st)).reshape(-1, cfg.hq, cfg.dh)
+        q = project(h, W["wq"], eps, st).reshape(-1, cfg.hq, cfg.dh)
         k = st(project(h, W["wk"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
         v = st(project(h, W["wv"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
         out, logits = attention(q, k, v, cfg.hq, cfg.hkv)
-        o = st(out.reshape(out.shape[0], -1))
-        hp = st(h + o @ np.asarray(W["wo"], dtype=np.float64).T)
-        act = st(silu(project(hp, W["wg"], eps, st)) * project(hp, W["wu"], eps, st))
+        o = out.reshape(out.shape[0], -1)
+        hp = h + o @ np.asarray(W["wo"], dtype=np.float64).T
+        act = silu(project(hp, W["wg"], eps)) * project(hp, W["wu"], eps)
         h = st(hp + act @ np.asarray(W["wd"], dtype=np.float64).T)
         Hs.append(h)
         Ks.append(k)

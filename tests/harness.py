@@ -91,6 +91,40 @@ def assert_stored(a, b, dtype, name, rtol=2e-3):
     return frac
 
 
+def assert_rounded(stored, pre, dtype, name):
+    """A stored tensor is its own pre-rounding value rounded once to the storage dtype.
+
+    Floating-point parity is judged on the values before their storage rounding (a
+    bf16 store alone moves a value by up to 2^-9 relative); this checks the store.
+    """
+    stored = np.asarray(stored, dtype=np.float64)
+    want = O.storer(dtype)(np.asarray(pre, dtype=np.float64))
+    bad = int(np.sum(stored != want))
+    log(f"    {name}: stored = round(pre-rounding value) for {stored.size - bad}/{stored.size}")
+    assert bad == 0, f"{name}: {bad} stored values are not the rounding of their pre-rounding value"
+
+
+def assert_traj(a, b, dtype, name, rtol=2e-3):
+    """Free-running values (each side continues from its own stored values; ``dtype`` is
+    the storage dtype of the run): the tensor within rtol normwise; with bf16 storage
+    every row within one bf16 ulp (2^-8) normwise and every element within a few ulps,
+    with float32 storage both within rtol."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if b.size == 0:
+        return 0.0
+    t = float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+    r, e = row_err(a, b), rel_err(a, b)
+    row_bound = rtol if dtype == "f32" else 2.0 ** -8
+    el_bound = rtol if dtype == "f32" else BF16_ELEM_BOUND
+    log(f"    {name}: {float(np.mean(a != b)):.3%} values differ; tensor err {t:.2e}, max row err {r.max():.2e}, "
+        f"max elem err {e.max():.2e}")
+    assert t <= rtol, f"{name}: tensor error {t:.3e} > {rtol}"
+    assert r.max() <= row_bound, f"{name}: row error {r.max():.3e} > {row_bound:.3e}"
+    assert e.max() <= el_bound, f"{name}: element error {e.max():.3e} > {el_bound:.3e}"
+    return t
+
+
 def topk_margin(D, topk, k_eff):
     """Gap between the k-th selected and the best unselected drift (relative)."""
     D = np.asarray(D, dtype=np.float64)[:k_eff]

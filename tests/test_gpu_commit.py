@@ -34,12 +34,12 @@ CHUNK = 8192   # LM-head rows per oracle chunk
 
 
 def _lm_logits(w, rows64: np.ndarray, eps: float) -> np.ndarray:
-    """Oracle logits RMSNorm(x) W_lm^T for all vocabulary ids, W_lm drawn chunk by chunk."""
+    """Oracle logits round(RMSNorm(x)) W_lm^T for all vocabulary ids, W_lm drawn chunk by chunk."""
     out = np.empty((rows64.shape[0], w.vocab), dtype=np.float64)
     for r0 in range(0, w.vocab, CHUNK):
         r1 = min(w.vocab, r0 + CHUNK)
         wc = np64(synth.weight_rows(w, 0, "wlm", r0, r1, device="cuda"))
-        out[:, r0:r1] = O.project(rows64, wc, eps)
+        out[:, r0:r1] = O.project(rows64, wc, eps, O.storer(w.dtype))
     return out
 
 

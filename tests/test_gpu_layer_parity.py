@@ -7,9 +7,13 @@ packet, the previous logits), runs on the GPU
   -> cluster(UPDATE) of layer l+1 with the new packet,
 and after every call compares against the oracle run on the identical inputs.
 Discrete outputs (labels, top-k, S, NVFP4 codes) must match exactly; floating
-point values before their storage rounding must match within 2e-3 relative;
-stored bf16 values may differ from the oracle's rounding by at most one ulp at
-isolated near-midpoints.
+point values before their storage rounding must match within 2e-3 relative.
+Where the GPU's pre-rounding value is available (check copies), its stored
+value must be exactly that value rounded once; stored values whose inputs are
+identical on both sides must also stay within the bounds of the oracle's stored
+values.  The next layer's K/V rows are projections of each side's own stored
+update packet, so there only the pre-rounding values are compared with the
+oracle.
 """
 import math
 
@@ -20,8 +24,8 @@ import torch
 import synth
 from drift_driven_sparse_amd import binding as B
 from oracle import polestar_oracle as O
-from tests.harness import (check_topk, Dev, assert_close, assert_stored, layer_struct, log, np64, oracle_weights,
-                           packed_layer, packet, to_dev, topk_margin, weights)
+from tests.harness import (row_err, check_topk, Dev, assert_close, assert_rounded, assert_stored, layer_struct, log, np64,
+                           oracle_weights, packed_layer, packet, to_dev, topk_margin, weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,7 +147,7 @@ def test_layer_step_parity(case):
             ls["H"] = Hb
             ls1["H"] = np64(s["H1"])
         # first drift reference: proxy logits of the entry centroids (oracle -> device)
-        zq = O.project(ls["Z"], Wo["wq"], cfg.eps).reshape(K, hq, dh)
+        zq = O.project(ls["Z"], Wo["wq"], cfg.eps, st).reshape(K, hq, dh)
         _, pl = O.attention(zq, ls["K"], ls["V"], hq, hkv)
         ls["P"] = O.round_f32(pl)
         plog[b] = torch.tensor(ls["P"], dtype=torch.float32)
@@ -207,8 +211,8 @@ def test_layer_step_parity(case):
                            commit_prev=np64(s["act_prev"]))
         DR.append(dr)
         toks = np.concatenate([ha, CU[b]["h"]], 0)
-        proj = np.concatenate([O.project(toks, np.concatenate([Wo["wq"], Wo["wk"], Wo["wv"]], 0), cfg.eps),
-                               O.project(OL[b]["Z"], np.concatenate([Wo["wq"], Wo["wk"], Wo["wv"]], 0), cfg.eps)], 0)
+        wqkv = np.concatenate([Wo["wq"], Wo["wk"], Wo["wv"]], 0)
+        proj = np.concatenate([O.project(toks, wqkv, cfg.eps, st), O.project(OL[b]["Z"], wqkv, cfg.eps, st)], 0)
         assert_close(chk_qkv[b, : Bk + nw + K].cpu().numpy(), proj, "QKV projections", dtype=w.dtype)
         # caches: active rows and patched rows rewritten, every other row bit-identical
         assert_stored(np64(kc[b]).reshape(n, -1), OL[b]["K"].reshape(n, -1), w.dtype, "K cache")
@@ -240,17 +244,26 @@ def test_layer_step_parity(case):
         rf = O.refresh_layer(Wo, cfg, np64(s["h_act"]), CU[b]["h"], DR[b]["o"], Sb)
         RF.append(rf)
         rows = Bk + len(Sb)
+        out_pre = chk_out[b, :rows].cpu().numpy()
         assert_close(chk_hp[b, :rows].cpu().numpy(), rf["hp"], "h' = h + o W_O", dtype=w.dtype)
-        assert_close(chk_out[b, :rows].cpu().numpy(), rf["out_pre"], "layer outputs", dtype=w.dtype)
+        assert_close(out_pre, rf["out_pre"], "layer outputs", dtype=w.dtype)
+        assert_rounded(np64(h_out[b]), out_pre[:Bk], w.dtype, "active outputs")
+        assert_rounded(np64(u_new[b, : len(Sb)]), out_pre[Bk:], w.dtype, "update packet U")
         assert_stored(np64(h_out[b]), rf["h_act_out"], w.dtype, "active outputs")
         assert_stored(np64(u_new[b, : len(Sb)]), rf["U"], w.dtype, "update packet U")
+        # next layer's K/V: projections of round(RMSNorm(U)), each side from its own stored U
         k1, v1 = O.kv_rows(rf["U"], wk1, wv1, cfg)
-        pre = np.concatenate([O.project(rf["U"], wk1, cfg.eps), O.project(rf["U"], wv1, cfg.eps)], 1)
-        assert_close(chk_kv[b, : len(Sb)].cpu().numpy(), pre, "next-layer K/V projections", dtype=w.dtype)
+        pre = np.concatenate([O.project(rf["U"], wk1, cfg.eps, st), O.project(rf["U"], wv1, cfg.eps, st)], 1)
+        kv_pre = chk_kv[b, : len(Sb)].cpu().numpy()
+        assert_close(kv_pre, pre, "next-layer K/V projections", dtype=w.dtype)
         pos = wpos[Sb]
-        assert_stored(np64(kc1[b, pos]).reshape(len(pos), -1), k1.reshape(len(pos), -1), w.dtype, "next-layer K rows")
-        assert_stored(np64(vc1[b].permute(2, 0, 1)[pos]).reshape(len(pos), -1), v1.reshape(len(pos), -1), w.dtype,
-                      "next-layer V rows")
+        nkv = hkv * dh
+        assert_rounded(np64(kc1[b, pos]).reshape(len(pos), -1), kv_pre[:, :nkv], w.dtype, "next-layer K rows")
+        assert_rounded(np64(vc1[b].permute(2, 0, 1)[pos]).reshape(len(pos), -1), kv_pre[:, nkv:], w.dtype,
+                       "next-layer V rows")
+        log(f"    next-layer K/V rows vs the oracle's stored rows: max row err "
+            f"{row_err(np64(kc1[b, pos]).reshape(len(pos), -1), k1.reshape(len(pos), -1)).max():.2e} (K), "
+            f"{row_err(np64(vc1[b].permute(2, 0, 1)[pos]).reshape(len(pos), -1), v1.reshape(len(pos), -1)).max():.2e} (V)")
         others = np.setdiff1d(np.arange(n), pos)
         assert torch.equal(kc1[b, others], S[b]["K1"][others])
     log("[layer-parity] refresh ok")

@@ -6,9 +6,11 @@ update packet to the next layer) interleaved with steps without a refresh
 Both sides start from the oracle's block-entry state (dense forward of all
 positions, k-means of the window rows, proxy logits).  Each step feeds the
 same seeded layer-0 active rows to both; every later value is each side's own.
-Per step and layer the drift, the top-k clusters and the selected rows must
-match; the active outputs, the update packets and the active drift must stay
-within the comparison bounds.  At the end of each step the state each side
+Per step and layer the top-k clusters and the selected rows must match; every
+floating-point tensor (drift values, active outputs, update packets, logits and
+the state below) must stay within 2e-3 normwise per tensor, and for bf16
+storage within one bf16 ulp normwise per row and a few ulps per element, since
+each side continues from its own stored values.  At the end of each step the state each side
 carries into the next one (K/V caches, window rows or NVFP4 codes, centroids,
 proxy logits, active logits) is compared, then the oracle's copy is written
 back to the device so that storage-rounding differences of one step do not
@@ -24,7 +26,7 @@ import torch
 import synth
 from drift_driven_sparse_amd import binding as B
 from oracle import polestar_oracle as O
-from tests.harness import (Dev, assert_close, assert_stored, check_topk, layer_struct, log, np64, packed_layer,
+from tests.harness import (Dev, assert_traj, check_topk, layer_struct, log, np64, packed_layer,
                            packet, to_dev, weights)
 
 pytestmark = pytest.mark.gpu
@@ -63,7 +65,7 @@ def test_trajectory_parity(case):
         P = [packed_layer(dev, W) for W in Wd]
         del Wd
         h0 = st(np64(synth.embeddings(w)))
-        Hs, Ks, Vs, _ = O.full_forward(h0, Wo, cfg)
+        Hs, Ks, Vs, last_logits = O.full_forward(h0, Wo, cfg)
         OL, L, Ls = [], [], []
         for l in range(n_layers):
             init = synth.kmeans_init(w, nw, l, 0)
@@ -90,9 +92,6 @@ def test_trajectory_parity(case):
             L.append(Ld)
             Ls.append(layer_struct(Ld))
         # active drift reference: the entry forward's last-layer logits of the active rows
-        _, last_logits = O.attention(
-            O.project(Hs[n_layers - 1], Wo[n_layers - 1]["wq"], cfg.eps).reshape(n, hq, dh),
-            Ks[n_layers - 1], Vs[n_layers - 1], hq, hkv)
         act_prev = O.round_f32(last_logits[blk_start: blk_start + Bk])
         act_logits = torch.tensor(act_prev, dtype=torch.float32, device="cuda")[None].contiguous()
         log("[trajectory] entry state ready")
@@ -142,18 +141,18 @@ def test_trajectory_parity(case):
                 tag = f"step {t} layer {l} ({'refresh' if refresh else 'active only'})"
                 if refresh:
                     Dg = D[0].cpu().numpy()
-                    assert_close(Dg, dr["D"], f"{tag}: cluster drift D")
+                    assert_traj(Dg, dr["D"], w.dtype, f"{tag}: cluster drift D")
                     if not check_topk(topk[0].cpu().numpy(), Dg, dr["D"], dr["topk"], w.top_k, keff, tag):
                         log(f"[trajectory] {tag}: trajectories part here")
                         return
                     cnt = int(pk_cnt[pk][0])
                     assert np.array_equal(pk_idx[pk][0, :cnt].cpu().numpy(), dr["S"]), f"{tag}: rows S differ"
-                    assert_stored(np64(pk_rows[pk][0, :cnt]), rf["U"], w.dtype, f"{tag}: update packet U")
+                    assert_traj(np64(pk_rows[pk][0, :cnt]), rf["U"], w.dtype, f"{tag}: update packet U")
                 else:
                     assert int(pk_cnt[pk][0]) == 0
-                assert_stored(np64(h_act[1 - cur][0]), rf["h_act_out"], w.dtype, f"{tag}: active outputs")
+                assert_traj(np64(h_act[1 - cur][0]), rf["h_act_out"], w.dtype, f"{tag}: active outputs")
                 if last:
-                    assert_close(delta[0].cpu().numpy(), dr["delta"], f"{tag}: active drift delta")
+                    assert_traj(delta[0].cpu().numpy(), dr["delta"], w.dtype, f"{tag}: active drift delta")
                     act_prev = dr["act_logits"]
                 # both sides continue from their own values
                 x = rf["h_act_out"]
@@ -163,12 +162,12 @@ def test_trajectory_parity(case):
             # carried state: compare, then continue from the oracle's copy on both sides
             for l in range(n_layers):
                 ls, Ld, tag = OL[l], L[l], f"step {t} layer {l} state"
-                assert_stored(np64(Ld["k_cache"][0]).reshape(n, -1), ls["K"].reshape(n, -1), w.dtype, f"{tag}: K")
-                assert_stored(np64(Ld["v_cache"][0].permute(2, 0, 1)).reshape(n, -1), ls["V"].reshape(n, -1),
+                assert_traj(np64(Ld["k_cache"][0]).reshape(n, -1), ls["K"].reshape(n, -1), w.dtype, f"{tag}: K")
+                assert_traj(np64(Ld["v_cache"][0].permute(2, 0, 1)).reshape(n, -1), ls["V"].reshape(n, -1),
                               w.dtype, f"{tag}: V")
-                assert_stored(np64(Ld["win_z"][0]), ls["Z"], w.dtype, f"{tag}: centroids")
+                assert_traj(np64(Ld["win_z"][0]), ls["Z"], w.dtype, f"{tag}: centroids")
                 assert np.array_equal(Ld["win_m"][0, :nw].cpu().numpy(), ls["M"]), f"{tag}: labels changed"
-                assert_close(Ld["proxy_logits"][0].cpu().numpy(), ls["P"], f"{tag}: proxy logits", dtype=w.dtype)
+                assert_traj(Ld["proxy_logits"][0].cpu().numpy(), ls["P"], w.dtype, f"{tag}: proxy logits")
                 if nv:
                     frac = float(np.mean(Ld["win_codes"][0, :nw].cpu().numpy() != ls["codes"]))
                     log(f"    {tag}: {frac:.3%} NVFP4 code bytes differ")
@@ -176,13 +175,13 @@ def test_trajectory_parity(case):
                     Ld["win_codes"][0, :nw] = torch.tensor(ls["codes"])
                     Ld["win_scales"][0, :nw] = torch.tensor(ls["scales"])
                 else:
-                    assert_stored(np64(Ld["win_h"][0, :nw]), ls["H"], w.dtype, f"{tag}: window rows")
+                    assert_traj(np64(Ld["win_h"][0, :nw]), ls["H"], w.dtype, f"{tag}: window rows")
                     Ld["win_h"][0, :nw] = to_dev(ls["H"], w.dtype)
                 Ld["k_cache"][0] = to_dev(ls["K"], w.dtype)
                 Ld["v_cache"][0] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)
                 Ld["win_z"][0] = to_dev(ls["Z"], w.dtype)
                 Ld["proxy_logits"][0] = torch.tensor(ls["P"], dtype=torch.float32)
-            assert_close(act_logits[0].cpu().numpy(), act_prev, f"step {t}: active logits", dtype=w.dtype)
+            assert_traj(act_logits[0].cpu().numpy(), act_prev, w.dtype, f"step {t}: active logits")
             act_logits[0] = torch.tensor(act_prev, dtype=torch.float32)
             log(f"[trajectory] step {t} ok ({'refresh' if refresh else 'active only'})")
     finally:

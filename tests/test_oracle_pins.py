@@ -130,9 +130,10 @@ def test_full_forward_one_layer_matches_torch_modules():
     assert np.allclose(Hs[1], out.numpy(), rtol=1e-11, atol=1e-11)
 
 
-# The bf16 storage points of a layer: every projection input (RMSNorm outputs, the attention
-# output, the SwiGLU product), Q/K/V of the token rows and the residual stream h' and out.
-BF16_POINTS = ("a", "q", "k", "v", "o", "hp", "b", "act", "out")
+# The bf16 storage points of a layer: the rounded RMSNorm output of the stored input row as
+# the input of the Q/K/V projections, K and V (the cache) and the layer output.  Queries, the
+# attention output, h', RMSNorm(h') and the SwiGLU product stay unrounded.
+BF16_POINTS = ("a", "k", "v", "out")
 
 
 def _torch_layer_bf16(x, T, hq, hkv, dh, skip=None):
@@ -141,13 +142,13 @@ def _torch_layer_bf16(x, T, hq, hkv, dh, skip=None):
         return t if name == skip else t.to(torch.bfloat16).to(torch.float64)
     n, d = x.shape
     a = c(F.rms_norm(x, (d,), eps=1e-6), "a")
-    q = c(F.linear(a, T["wq"]), "q").view(n, hq, dh).permute(1, 0, 2)
+    q = F.linear(a, T["wq"]).view(n, hq, dh).permute(1, 0, 2)
     k = c(F.linear(a, T["wk"]), "k").view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
     v = c(F.linear(a, T["wv"]), "v").view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
-    o = c(F.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).reshape(n, hq * dh), "o")
-    hp = c(x + F.linear(o, T["wo"]), "hp")
-    b = c(F.rms_norm(hp, (d,), eps=1e-6), "b")
-    act = c(F.silu(F.linear(b, T["wg"])) * F.linear(b, T["wu"]), "act")
+    o = F.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).reshape(n, hq * dh)
+    hp = x + F.linear(o, T["wo"])
+    b = F.rms_norm(hp, (d,), eps=1e-6)
+    act = F.silu(F.linear(b, T["wg"])) * F.linear(b, T["wu"])
     return c(hp + F.linear(act, T["wd"]), "out")
 
 
