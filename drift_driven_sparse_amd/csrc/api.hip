@@ -64,7 +64,7 @@ void layout(polestar_handle* h) {
   auto take = [&](size_t bytes) { size_t o = off; off += ps_align256(bytes); return o; };
   w.win_rows = take(Bt * h->win_max * d.d * T);
   w.flags = take(Bt * h->win_max * 4);
-  w.a_qkv = take(Bt * h->mq * d.d * T);
+  w.a_qkv = take(Bt * h->rq * d.d * T);
   w.q = take(Bt * h->mq * (size_t)h->nq * 4);
   w.o = take(Bt * h->mt * (size_t)h->nq * 4);    // float32 rows, or two bf16 planes
   w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
@@ -81,12 +81,12 @@ void layout(polestar_handle* h) {
   }
   w.part = take(part * 4);
   w.hp = take(Bt * h->mt * d.d * 4);          // h' (float32)
-  w.a_gu = take(Bt * h->mt * d.d * 4);        // RMSNorm(h'): float32 rows, or two bf16 planes
+  w.a_gu = take(Bt * h->rt * d.d * 4);        // RMSNorm(h'): float32 rows, or two bf16 planes
   w.attn_part = take(d.dtype == POLESTAR_BF16 && h->attn_nchunks > 1
                          ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->mt * (d.head_dim + 2) * 4
                          : 0);
-  w.act = take(Bt * h->mt * (size_t)d.ffn * 4);   // float32 rows, or two bf16 planes
-  w.a_kv = take(Bt * h->win_max * d.d * T);   // round(RMSNorm(U)): next-layer K/V input
+  w.act = take(Bt * h->rt * (size_t)d.ffn * 4);   // float32 rows, or two bf16 planes
+  w.a_kv = take(Bt * h->rw * d.d * T);        // round(RMSNorm(U)): next-layer K/V input
   w.xhat = take(Bt * h->win_max * d.d * 8);
   w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
   w.wstat = take(Bt * (h->win_max + (size_t)d.n_clusters * PS_CEIL_DIV(d.d, 256)) * 8);
@@ -117,6 +117,18 @@ int check_blk(const polestar_handle* h, int32_t blk_start) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POLESTAR_OK : POLESTAR_E_HIP; }
+
+// Subtiles per packed weight group: the column width of the projection shape that streams the
+// weight (bf16); the LM head and float32 weights keep one subtile per group.
+int weight_group(const polestar_handle* h, int which) {
+  if (h->dm.dtype != POLESTAR_BF16) return 1;
+  switch (which) {
+    case POLESTAR_W_QKV: case POLESTAR_W_KV: return dl_tile_cols(DL_NARROW) / 16;
+    case POLESTAR_W_O: case POLESTAR_W_DOWN: return dl_tile_cols(DL_WIDE) / 16;
+    case POLESTAR_W_GU: return dl_tile_cols(DL_WIDE) / 16;   // DL_MID reads half groups
+    default: return 1;
+  }
+}
 
 WinGeom geom_of(const polestar_handle* h, int32_t blk_start) {
   return make_geom(blk_start, h->dm.n_pos, h->dm.block, h->dm.win_prefix, h->dm.win_suffix);
@@ -187,6 +199,8 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.ws_rows = at<char>(ws, h->ws.win_rows);
   p.win_z = L->win_z;
   p.a_qkv = at<char>(ws, h->ws.a_qkv);
+  p.a_bstride = (int64_t)h->rq * d.d;
+  p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
   p.eps = h->pr.rms_eps;
   hipError_t e;
   {
@@ -199,7 +213,8 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   GemmArgs ga;
   memset(&ga, 0, sizeof(ga));
   ga.A.base = p.a_qkv;
-  ga.A.bstride = (int64_t)h->mq * d.d;
+  ga.A.bstride = p.a_bstride;
+  ga.A.tiles = p.a_tiles;
   ga.A.lda = d.d;
   ga.A.rows_static = rows;
   ga.W = L->w_qkv;
@@ -230,6 +245,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
     memset(&dl, 0, sizeof(dl));
     dl.A = ga.A;
     dl.planes = 1;
+    dl.wg = weight_group(h, POLESTAR_W_QKV);
     dl.W = ga.W;
     dl.N = ga.N;
     dl.K = ga.K;
@@ -339,6 +355,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.A.rows_add = d.block;
   dl.A.rows_max = max_rows;
   dl.planes = 2;
+  dl.wg = weight_group(h, POLESTAR_W_O);
   dl.W = L->w_o;
   dl.N = d.d;
   dl.K = h->nq;
@@ -374,8 +391,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.out_f32 = 1;
   rr.norm = at<char>(ws, h->ws.a_gu);
   rr.norm_planes = 1;
-  rr.norm_plane_stride = (int64_t)h->mt * d.d;
-  rr.norm_bstride = 2 * rr.norm_plane_stride;
+  rr.norm_tiles = h->rt / 16;
+  rr.norm_bstride = 2 * (int64_t)h->rt * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
   rr.chk = h->chk.hp;
@@ -388,13 +405,14 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   // 2. act = silu(g) * u with g, u the projections of RMSNorm(h')
   memset(&dl, 0, sizeof(dl));
   dl.A.base = rr.norm;
-  dl.A.plane_stride = rr.norm_plane_stride;
+  dl.A.tiles = rr.norm_tiles;
   dl.A.bstride = rr.norm_bstride;
   dl.A.lda = d.d;
   dl.A.rows_dev = sel->count;
   dl.A.rows_add = d.block;
   dl.A.rows_max = max_rows;
   dl.planes = 2;
+  dl.wg = weight_group(h, POLESTAR_W_GU);
   dl.W = L->w_gu;
   dl.N = 2 * d.ffn;
   dl.K = d.d;
@@ -404,7 +422,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.part_rows = h->mt;
   dl.e.kind = EPI_SWIGLU;
   dl.e.act = at<char>(ws, h->ws.act);
-  dl.e.act_rows = h->mt;
+  dl.e.act_rows = h->rt;
+  dl.e.act_tiles = h->rt / 16;
   dl.e.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
@@ -419,13 +438,14 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&dl, 0, sizeof(dl));
   dl.A.base = at<char>(ws, h->ws.act);
-  dl.A.plane_stride = (int64_t)h->mt * d.ffn;
-  dl.A.bstride = 2 * dl.A.plane_stride;
+  dl.A.tiles = h->rt / 16;
+  dl.A.bstride = 2 * (int64_t)h->rt * d.ffn;
   dl.A.lda = d.ffn;
   dl.A.rows_dev = sel->count;
   dl.A.rows_add = d.block;
   dl.A.rows_max = max_rows;
   dl.planes = 2;
+  dl.wg = weight_group(h, POLESTAR_W_DOWN);
   dl.W = L->w_down;
   dl.N = d.d;
   dl.K = d.ffn;
@@ -455,7 +475,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   r2.out_f32 = 0;
   r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only, rounded
   r2.norm_planes = 0;
-  r2.norm_bstride = (int64_t)h->win_max * d.d;
+  r2.norm_tiles = h->rw / 16;
+  r2.norm_bstride = (int64_t)h->rw * d.d;
   r2.norm_from = d.block;
   r2.chk = h->chk.out;
   {
@@ -467,11 +488,13 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   if (kv_next) {
     memset(&dl, 0, sizeof(dl));
     dl.A.base = r2.norm;
+    dl.A.tiles = r2.norm_tiles;
     dl.A.bstride = r2.norm_bstride;
     dl.A.lda = d.d;
     dl.A.rows_dev = sel->count;
     dl.A.rows_max = g.n_win;
     dl.planes = 1;
+    dl.wg = weight_group(h, POLESTAR_W_KV);
     dl.W = w_kv_next;
     dl.N = 2 * h->nkv;
     dl.K = d.d;
@@ -560,7 +583,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.out_split = h->mt;
   rr.out_f32 = 1;
   rr.norm = at<char>(ws, h->ws.a_gu);
-  rr.norm_bstride = (int64_t)h->mt * d.d;
+  rr.norm_bstride = (int64_t)h->rt * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
   rr.chk = h->chk.hp;
@@ -586,7 +609,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_SWIGLU;
   ep.act = at<char>(ws, h->ws.act);
-  ep.act_rows = h->mt;
+  ep.act_rows = h->rt;
   ep.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
@@ -596,7 +619,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&ga, 0, sizeof(ga));
   ga.A.base = ep.act;
-  ga.A.bstride = (int64_t)h->mt * d.ffn;
+  ga.A.bstride = (int64_t)h->rt * d.ffn;
   ga.A.lda = d.ffn;
   ga.A.rows_dev = sel->count;
   ga.A.rows_add = d.block;
@@ -628,7 +651,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
   r2.out_f32 = 0;
   r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only
-  r2.norm_bstride = (int64_t)h->win_max * d.d;
+  r2.norm_bstride = (int64_t)h->rw * d.d;
   r2.norm_from = d.block;
   r2.chk = h->chk.out;
   {
@@ -822,6 +845,9 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->mt = d.block + h->win_max;
   h->nq = d.n_heads * d.head_dim;
   h->nkv = d.n_kv_heads * d.head_dim;
+  h->rq = 16 * PS_CEIL_DIV(h->mq, 16);
+  h->rt = 16 * PS_CEIL_DIV(h->mt, 16);
+  h->rw = 16 * PS_CEIL_DIV(h->win_max, 16);
   const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
   int ks = PS_CEIL_DIV(256, ntiles);
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
@@ -918,7 +944,7 @@ int polestar_weight_packed_size(const polestar_handle* h, int which, size_t* byt
   int N, K;
   int rc = weight_shape(h, which, &N, &K);
   if (rc) return rc;
-  *bytes = packed_elems(N, K) * elt(h);
+  *bytes = packed_elems(N, K, weight_group(h, which)) * elt(h);
   return POLESTAR_OK;
 }
 
@@ -929,8 +955,9 @@ int polestar_pack_weight(const polestar_handle* h, int which, const void* src, v
   if (rc) return rc;
   if (!aligned16(src) || !aligned16(dst)) return POLESTAR_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = h->dm.dtype == POLESTAR_BF16 ? launch_pack<bf16_t>(which, src, dst, N, K, h->dm.ffn, s)
-                                              : launch_pack<float>(which, src, dst, N, K, h->dm.ffn, s);
+  const int G = weight_group(h, which);
+  hipError_t e = h->dm.dtype == POLESTAR_BF16 ? launch_pack<bf16_t>(which, src, dst, N, K, G, h->dm.ffn, s)
+                                              : launch_pack<float>(which, src, dst, N, K, G, h->dm.ffn, s);
   return hip_status(e);
 }
 

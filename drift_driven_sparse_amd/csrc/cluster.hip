@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
   }
 }
 
-// ---- QKV input rows: round(RMSNorm(x)) of [active; window; centroids] ---------------------------
+// ---- QKV input rows: round(RMSNorm(x)) of [active; window; centroids], fragment-packed (bf16) ----
 template <typename T>
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   __shared__ float red[4];
@@ -276,7 +276,11 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   if (r < a.block) src = (const T*)a.h_act + ((int64_t)b * a.block + r) * d;
   else if (r < a.block + a.n_win) src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + (r - a.block)) * d;
   else src = (const T*)a.win_z + ((int64_t)b * a.K + (r - a.block - a.n_win)) * d;
-  rmsnorm_row<T>(src, (T*)a.a_qkv + ((int64_t)b * a.mq + r) * d, d, a.eps, red);
+  T* dst = (T*)a.a_qkv + (int64_t)b * a.a_bstride;
+  if (a.a_tiles > 0)
+    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + apack(r, n, 0, 1, a.a_tiles), x); });
+  else
+    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + (int64_t)r * d + n, x); });
 }
 
 // ---- NVFP4 test hooks ---------------------------------------------------------------------------

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void lm_prep_kernel(LmPrepArgs a, int32_t* met
     if (j >= cnt_sh) return;
     src = (const T*)a.u_rows + ((int64_t)b * a.win_max + j) * d;
   }
-  rmsnorm_row<T>(src, (T*)a.a_lm + ((int64_t)b * a.lm_rows + r) * d, d, a.eps, red);
+  T* dst = (T*)a.a_lm + ((int64_t)b * a.lm_rows + r) * d;
+  rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + n, x); });
 }
 
 // Combine per-tile (max, sum exp, best non-mask logit, its id) in tile order.

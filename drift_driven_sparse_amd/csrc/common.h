@@ -111,11 +111,11 @@ template <> struct Quad<bf16_t> {
   }
 };
 
-// RMSNorm with unit gain of one row of d elements (d a multiple of 4), rounded to the storage
-// dtype: dst = round(src * 1/sqrt(mean(src^2) + eps)).  Every thread of the block takes part;
-// `red` holds one float per wave.
-template <typename T>
-PS_DEV void rmsnorm_row(const T* src, T* dst, int d, float eps, float* red) {
+// RMSNorm with unit gain of one row of d elements (d a multiple of 4): calls
+// store(n, x) with x[0..3] = src[n..n+3] * 1/sqrt(mean(src^2) + eps).  Every thread of the block
+// takes part; `red` holds one float per wave.
+template <typename T, typename Store>
+PS_DEV void rmsnorm_row(const T* src, int d, float eps, float* red, Store&& store) {
   float ss = 0.f;
   for (int n = 4 * threadIdx.x; n < d; n += 4 * blockDim.x) {
     float x[4];
@@ -128,7 +128,7 @@ PS_DEV void rmsnorm_row(const T* src, T* dst, int d, float eps, float* red) {
     float x[4];
     Quad<T>::load(src + n, x);
     x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;
-    Quad<T>::store(dst + n, x);
+    store(n, x);
   }
 }
 

@@ -28,18 +28,24 @@ PS_HD int64_t gu_src_row(int64_t p, int ffn) {
 }
 
 // ---- weight packing -----------------------------------------------------------------
-// bf16: dst[((n16*(K/32) + k32)*64 + lane)*8 + e] = W'[n16*16 + lane%16][k32*32 + (lane/16)*8 + e]
-// f32:  dst[n][k] = W'[n][k]
+// bf16: fragment f = (n16/G * (K/32) + k32) * G + n16%G holds
+//   dst[(f*64 + lane)*8 + e] = W'[n16*16 + lane%16][k32*32 + (lane/16)*8 + e]
+// (subtiles past N are zero); f32: dst[n][k] = W'[n][k].
 // W' = W with rows permuted for the gate/up weight (gate and up 16-row groups interleaved).
-__global__ void pack_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K,
+__global__ void pack_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K, int G,
                                  int is_gu, int ffn) {
   const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // one 8-element chunk
   const int64_t k32n = K >> 5;
-  const int64_t total = (int64_t)N * K / 8;
-  if (c >= total) return;
+  const int64_t groups = ((N >> 4) + G - 1) / G;
+  if (c >= groups * G * k32n * 64) return;
   const int lane = (int)(c & 63);
-  const int64_t blk = c >> 6;
-  const int64_t n16 = blk / k32n, k32 = blk % k32n;
+  const int64_t f = c >> 6;
+  const int64_t j = f % G, rest = f / G;
+  const int64_t k32 = rest % k32n, n16 = (rest / k32n) * G + j;
+  if (n16 >= (N >> 4)) {
+    *(uint4*)(dst + c * 8) = make_uint4(0, 0, 0, 0);
+    return;
+  }
   const int64_t n = n16 * 16 + (lane & 15);
   const int64_t k = k32 * 32 + (lane >> 4) * 8;
   const int64_t row = is_gu ? gu_src_row(n, ffn) : n;
@@ -331,39 +337,48 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
   if (!a.norm || r < a.norm_from) return;   // uniform over the workgroup
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)a.d + a.eps);
-  const int64_t noff = (int64_t)b * a.norm_bstride + (int64_t)(r - a.norm_from) * a.d;
+  const int rn = r - a.norm_from;
+  const int planes = a.norm_planes ? 2 : 1;
   for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
     float x[4];
     load_out(n, x);
     x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;
-    if (a.norm_planes) {
-      uint16_t hi[4], lo[4];
+    const int64_t o0 = (int64_t)b * a.norm_bstride +
+                       (a.norm_tiles > 0 ? apack(rn, n, 0, planes, a.norm_tiles) : (int64_t)rn * a.d + n);
+    if (a.norm_planes) {   // bf16 hi/lo planes (fragment-packed)
+      const int64_t o1 = (int64_t)b * a.norm_bstride + apack(rn, n, 1, planes, a.norm_tiles);
+      float hi[4], lo[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf16(x[i], hi[i], lo[i]);
-      uint16_t* pl = (uint16_t*)a.norm + noff + n;
-      *(uint2*)pl = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *(uint2*)(pl + a.norm_plane_stride) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = St<bf16_t>::round(x[i]);
+        lo[i] = x[i] - hi[i];
+      }
+      Quad<bf16_t>::store((bf16_t*)a.norm + o0, hi);
+      Quad<bf16_t>::store((bf16_t*)a.norm + o1, lo);
     } else {
-      Quad<T>::store((T*)a.norm + noff + n, x);
+      Quad<T>::store((T*)a.norm + o0, x);
     }
   }
 }
 
 }  // namespace
 
-size_t packed_elems(int N, int K) { return (size_t)N * (size_t)K; }
+size_t packed_elems(int N, int K, int G) {
+  const size_t n16 = (size_t)(N >> 4);
+  return G > 1 ? (n16 + G - 1) / G * G * 16 * (size_t)K : (size_t)N * (size_t)K;
+}
 
 template <typename T>
-hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s) {
+hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int G, int ffn, hipStream_t s) {
   const int is_gu = kind == POLESTAR_W_GU;
   if constexpr (std::is_same<T, float>::value) {
     const int64_t total = (int64_t)N * K;
     hipLaunchKernelGGL(pack_f32_kernel, dim3((unsigned)PS_CEIL_DIV(total, 256)), dim3(256), 0, s,
                        (const float*)src, (float*)dst, N, K, is_gu, ffn);
   } else {
-    const int64_t total = (int64_t)N * K / 8;
+    const int64_t total = (int64_t)packed_elems(N, K, G) / 8;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)PS_CEIL_DIV(total, 256)), dim3(256), 0, s,
-                       (const uint16_t*)src, (uint16_t*)dst, N, K, is_gu, ffn);
+                       (const uint16_t*)src, (uint16_t*)dst, N, K, G, is_gu, ffn);
   }
   return hipGetLastError();
 }
@@ -386,8 +401,8 @@ hipError_t launch_row_reduce(const RowReduceArgs& a, int max_rows, hipStream_t s
   return hipGetLastError();
 }
 
-template hipError_t launch_pack<float>(int, const void*, void*, int, int, int, hipStream_t);
-template hipError_t launch_pack<bf16_t>(int, const void*, void*, int, int, int, hipStream_t);
+template hipError_t launch_pack<float>(int, const void*, void*, int, int, int, int, hipStream_t);
+template hipError_t launch_pack<bf16_t>(int, const void*, void*, int, int, int, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, const EpiParams&, int, hipStream_t);
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, const EpiParams&, int, hipStream_t);
 template hipError_t launch_row_reduce<float>(const RowReduceArgs&, int, hipStream_t);

@@ -12,8 +12,14 @@
 //
 // Waves form RG row groups x CG column groups: the CG waves of a row group read
 // the same A fragments, the RG waves of a column group the same weight
-// fragments.  Fragments are 16x16x32 MFMA operands in lane order; weights are
-// pre-packed in that order, A rows are gathered per lane (any row map).
+// fragments.  Fragments are 16x16x32 MFMA operands in lane order.  Weights are
+// pre-packed in groups of subtiles so that a workgroup's weights for one step are
+// one contiguous block and its whole range one contiguous stream.  A operands are
+// fragment-packed by their producers (one contiguous block per step), except the
+// output projection's, whose rows are gathered per lane through the row map.
+// Both layouts keep the number of memory requests per step low: A fragments
+// gathered row by row cost twice the requests of packed ones, and the requests a
+// compute unit can keep in flight bound its share of the weight stream.
 //
 // float32 activations (the attention output, RMSNorm(h') and the SwiGLU product)
 // arrive as two bf16 planes (hi = rn(x), lo = rn(x - hi)) written by their
@@ -47,10 +53,9 @@ struct DlCfg {
   static constexpr int FA = PL * RT;               // A fragments per stage
   static constexpr int F = FA + CG * NSUB;         // fragments per stage
   static constexpr int LPW = (F + NWV - 1) / NWV;  // direct loads per wave per stage
-  static constexpr int FP = LPW * NWV;             // fragment slots per stage (with padding)
-  static constexpr int STAGE = FP * 1024;          // bytes
-  static constexpr int P0 = (150 * 1024) / STAGE;
-  static constexpr int P = P0 > 6 ? 6 : P0;        // ring depth
+  static constexpr int STAGE = F * 1024;           // bytes
+  static constexpr int P0 = (150 * 1024 - 1024) / STAGE;
+  static constexpr int P = P0 > 8 ? 8 : P0;        // ring depth
   static constexpr int NCOL = CG * NSUB * 16;      // columns per workgroup
   static_assert(P >= 3, "pipeline needs three stages");
   static_assert(LPW * (P - 2) < 64, "vmcnt range");
@@ -59,15 +64,20 @@ struct DlCfg {
 template <typename T, int RTW, int RG, int CG, int NSUB, int PL, int KIND>
 __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   using C = DlCfg<RTW, RG, CG, NSUB, PL>;
-  constexpr int NWV = C::NWV, RT = C::RT, FA = C::FA, F = C::F, LPW = C::LPW, FP = C::FP, P = C::P;
-  __shared__ uint4 b0[FP * 64], b1[FP * 64], b2[FP * 64], b3[FP * 64], b4[FP * 64], b5[FP * 64];
+  constexpr int NWV = C::NWV, RT = C::RT, FA = C::FA, F = C::F, LPW = C::LPW, P = C::P;
+  // ring stages (only the first P are referenced) and one slot that the padding loads of the
+  // waves with fewer than LPW fragments write to and nothing reads
+  __shared__ uint4 b0[F * 64], b1[F * 64], b2[F * 64], b3[F * 64], b4[F * 64], b5[F * 64], b6[F * 64],
+      b7[F * 64], bd[64];
   auto bp = [&](auto I) -> uint4* {
     if constexpr (I == 0) return b0;
     else if constexpr (I == 1) return b1;
     else if constexpr (I == 2) return b2;
     else if constexpr (I == 3) return b3;
     else if constexpr (I == 4) return b4;
-    else return b5;
+    else if constexpr (I == 5) return b5;
+    else if constexpr (I == 6) return b6;
+    else return b7;
   };
   const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
@@ -79,7 +89,6 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   const int k32n = g.K >> 5;
   const int g0 = (int)((int64_t)k32n * sp / g.ksplit), g1 = (int)((int64_t)k32n * (sp + 1) / g.ksplit);
   const int n = g1 - g0;
-  const int n16_total = g.N >> 4;
 
   // Per load slot: source address of this lane at step 0 of the range, and the step stride.
   // Slots past the fragment count and A slots of row tiles without rows re-read one fixed
@@ -99,25 +108,31 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     }
     if (f < FA) {
       const int p = f / RT, rt = f % RT;
-      int r = rt * 16 + (lane & 15);
-      if (r >= rows_b) r = 0;
-      src[i] = (const char*)(Ab + p * g.A.plane_stride + g.A.src_row(b, r) * g.A.lda + (int64_t)g0 * 32 +
-                             8 * (lane >> 4));
-      stride[i] = 64;
+      if (g.A.tiles > 0) {   // fragment-packed: step s, plane p, tile rt
+        src[i] = (const char*)(Ab + ((((int64_t)g0 * PL + p) * g.A.tiles + rt) * 64 + lane) * 8);
+        stride[i] = PL * g.A.tiles * 1024;
+      } else {
+        int r = rt * 16 + (lane & 15);
+        if (r >= rows_b) r = 0;
+        src[i] = (const char*)(Ab + p * g.A.plane_stride + g.A.src_row(b, r) * g.A.lda + (int64_t)g0 * 32 +
+                               8 * (lane >> 4));
+        stride[i] = 64;
+      }
     } else {
-      const int wf = f - FA, c2 = wf / NSUB, sb = wf % NSUB;
-      int n16 = (nt * CG + c2) * NSUB + sb;
-      if (n16 >= n16_total) n16 = nt * CG * NSUB;   // columns past N: re-read a valid subtile, never stored
-      src[i] = (const char*)((const uint4*)g.W + ((int64_t)n16 * k32n + g0) * 64 + lane);
-      stride[i] = 1024;
+      // subtile n16 of group n16 / wg (packed groups are padded, so every subtile exists)
+      const int n16 = nt * CG * NSUB + (f - FA);
+      src[i] = (const char*)((const uint4*)g.W + (((int64_t)(n16 / g.wg) * k32n + g0) * g.wg + n16 % g.wg) * 64 + lane);
+      stride[i] = 1024 * g.wg;
     }
   }
   auto issue = [&](uint4* buf, int step) {
     step = step < n ? step : n - 1;   // past the range: reload the last step (unused)
 #pragma unroll
-    for (int i = 0; i < LPW; ++i)
+    for (int i = 0; i < LPW; ++i) {
+      const int slot = i * NWV + wave;
       __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + (int64_t)step * stride[i]),
-                                       (lds_void*)&buf[(i * NWV + wave) * 64], 16, 0, 0);
+                                       (lds_void*)(slot < F ? &buf[slot * 64] : bd), 16, 0, 0);
+    }
   };
 
   floatx4_t acc[RTW][NSUB];
@@ -189,8 +204,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     // subtile pairs (2j, 2j+1) are the gate and up weights of 16 consecutive FFN columns
     static_assert(NSUB % 2 == 0, "gate/up pairs inside one wave");
     const EpiParams& e = g.e;
-    const int64_t plane = (int64_t)e.act_rows * e.ffn;
-    uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane;
+    bf16_t* act = (bf16_t*)e.act + (int64_t)b * 2 * e.act_rows * e.ffn;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -204,8 +218,8 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
             const float a = gv / (1.f + expf(-gv)) * uv;
             uint16_t hi, lo;
             split_bf16(a, hi, lo);
-            act[(int64_t)r * e.ffn + oc] = hi;
-            act[plane + (int64_t)r * e.ffn + oc] = lo;
+            act[apack(r, oc, 0, 2, e.act_tiles)].bits = hi;
+            act[apack(r, oc, 1, 2, e.act_tiles)].bits = lo;
           }
         }
   }
@@ -253,16 +267,16 @@ __global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
     uv.x += tu.x; uv.y += tu.y; uv.z += tu.z; uv.w += tu.w;
   }
   const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
-  const int64_t plane = (int64_t)e.act_rows * e.ffn;
-  uint16_t* act = (uint16_t*)e.act + (int64_t)b * 2 * plane + (int64_t)r * e.ffn + oc;
+  bf16_t* act = (bf16_t*)e.act + (int64_t)b * 2 * e.act_rows * e.ffn;
+  float hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x = ga[i], u = ua[i];
-    uint16_t hi, lo;
-    split_bf16(x / (1.f + expf(-x)) * u, hi, lo);
-    act[i] = hi;
-    act[plane + i] = lo;
+    const float a = ga[i] / (1.f + expf(-ga[i])) * ua[i];
+    hi[i] = St<bf16_t>::round(a);
+    lo[i] = a - hi[i];
   }
+  Quad<bf16_t>::store(act + apack(r, oc, 0, 2, e.act_tiles), hi);
+  Quad<bf16_t>::store(act + apack(r, oc, 1, 2, e.act_tiles), lo);
 }
 
 template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
@@ -295,6 +309,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
   } else {
     if (max_rows <= 0) return hipSuccess;
     if (g.K % 32 || g.N % 16 || g.ksplit < 1 || g.ksplit > (g.K >> 5)) return hipErrorInvalidValue;
+    if (g.wg < 1 || g.wg % (dl_tile_cols(shape) / 16) != 0) return hipErrorInvalidValue;
     if (shape == DL_NARROW) {   // 3 x 2 waves, bf16 rows
       if (g.planes != 1) return hipErrorInvalidValue;
       if (max_rows <= 48) return launch_cfg<T, 1, 3, 2, 4, 1>(g, s);

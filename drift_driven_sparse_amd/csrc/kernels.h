@@ -20,6 +20,7 @@ struct polestar_handle {
   int32_t nq, nkv;   // Hq*dh, Hkv*dh
   int32_t ksplit;    // split-K factor of the N = d projections (float32 path)
   int32_t ks_qkv, ks_o, ks_gu, ks_down, ks_kv;   // split-K factors of the bf16 projections
+  int32_t rq, rt, rw;   // mq, mt, win_max rounded up to whole 16-row tiles (packed operands)
   int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
   int32_t lm_tiles;  // vocab / 64 rounded up
   WsLayout ws;
@@ -27,12 +28,23 @@ struct polestar_handle {
 };
 
 // ---- GEMM ---------------------------------------------------------------------
-// A operand: rows of M-block b (one sequence).  Row r reads source row
+// Fragment-packed operand of the bf16 projections: per 32-column step s, plane p and 16-row
+// tile t one 1 KiB MFMA 16x16x32 A fragment, so that a workgroup's operand for one step is
+// contiguous; element (r, k) is element k%8 of lane (r%16) + 16*((k%32)/8).  `tiles` is the
+// number of row tiles per step and plane.
+PS_HD int64_t apack(int r, int k, int p, int planes, int tiles) {
+  return (((((int64_t)(k >> 5) * planes + p) * tiles + (r >> 4)) * 64) + (r & 15) + 16 * ((k & 31) >> 3)) * 8 +
+         (k & 7);
+}
+
+// A operand: rows of M-block b (one sequence).  Row-major: row r reads source row
 //   r                                  when rowmap == nullptr or r < map_from
 //   map_off + rowmap[b*map_bstride + r - map_from]   otherwise.
+// Fragment-packed (tiles > 0, bf16 projections only): rows in order, no row map.
 struct GemmA {
   const void* base;      // rows in the storage dtype (bf16 projections: bf16 planes)
-  int64_t plane_stride;  // bf16 plane layout: elements from the hi plane to the lo plane
+  int32_t tiles;         // > 0: fragment-packed with this many row tiles per step and plane
+  int64_t plane_stride;  // row-major bf16 planes: elements from the hi plane to the lo plane
   int64_t bstride;       // elements between sequences
   int32_t lda;           // elements between rows
   const int32_t* rowmap;
@@ -77,8 +89,8 @@ struct EpiParams {
   WinGeom geom;
   float* chk; int32_t chk_rows, chk_ld;   // chk[(b*chk_rows + r)*chk_ld + n]
   // SwiGLU product: float32 rows [batch][act_rows][ffn], or for bf16 storage the hi/lo planes
-  // [batch][2][act_rows][ffn]
-  void* act; int32_t act_rows, ffn;
+  // fragment-packed with act_tiles row tiles ([batch] stride act_rows*ffn*2 elements)
+  void* act; int32_t act_rows, ffn, act_tiles;
   // KV scatter of packet rows: dest pos = geom.pos(sel_idx[b*win_max + r])
   const int32_t* sel_idx;
   // LM statistics
@@ -142,8 +154,9 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 struct DlArgs {
   GemmA A;
   int32_t planes;
-  const void* W;
+  const void* W;         // packed in groups of wg 16-column subtiles (weight_group)
   int32_t N, K, batch, ksplit;
+  int32_t wg;
   float* part;
   int32_t part_rows;
   EpiParams e;
@@ -156,9 +169,12 @@ template <typename T>
 hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s);
 template <typename T>
 hipError_t launch_dl_finish(const DlArgs& g, int max_rows, hipStream_t s);
+// Packed weights: fragment (16-column subtile n16, 32-row step k32) of the bf16 layout sits at
+// ((n16/G * (K/32) + k32) * G + n16%G) KiB, so the G subtiles of one group are contiguous per
+// step; the last group is padded with zeros.  float32 weights stay row-major.
 template <typename T>
-hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int ffn, hipStream_t s);
-size_t packed_elems(int N, int K);
+hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int G, int ffn, hipStream_t s);
+size_t packed_elems(int N, int K, int G);
 
 // Row reductions after split-K projections, one row per workgroup: out = sum of partials in
 // split order + residual, kept as float32 or rounded to the storage dtype, and for rows
@@ -176,11 +192,11 @@ struct RowReduceArgs {
   void* out_a; int64_t out_a_bstride; int32_t out_split;
   void* out_b; int64_t out_b_bstride;
   int32_t out_f32;              // outputs are float32 rows (else storage dtype)
-  // RMSNorm of row r >= norm_from -> norm[b][r - norm_from] (null: none): float32 rows given as
-  // bf16 hi/lo planes norm_plane_stride elements apart when norm_planes, else rounded to the
-  // storage dtype
+  // RMSNorm of row r >= norm_from as row r - norm_from of norm (null: none): bf16 hi/lo planes
+  // of the float32 value when norm_planes, else rounded to the storage dtype; fragment-packed
+  // with norm_tiles row tiles when norm_tiles > 0, else row-major
   void* norm; int64_t norm_bstride; int32_t norm_from;
-  int32_t norm_planes; int64_t norm_plane_stride;
+  int32_t norm_planes, norm_tiles;
   float eps;
   float* chk; int32_t chk_rows;
 };
@@ -211,8 +227,9 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 // Active rows, window rows and centroids -> contiguous QKV input rows round(RMSNorm(x)).
 struct PrepArgs {
   int32_t batch, d, block, win_max, n_win, K, mq, refresh;
+  int32_t a_tiles;        // > 0: a_qkv fragment-packed with this many row tiles (bf16)
   const void* h_act; const void* ws_rows; const void* win_z;
-  void* a_qkv; float eps;
+  void* a_qkv; int64_t a_bstride; float eps;
 };
 template <typename T>
 hipError_t launch_prep_qkv(const PrepArgs& a, hipStream_t s);
