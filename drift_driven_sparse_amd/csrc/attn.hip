@@ -26,7 +26,13 @@ PS_DEV floatx4_t mfma(uint4 a, uint4 b, floatx4_t c) {
                                                  0, 0, 0);
 }
 
-PS_DEV uint32_t pack2(float a, float b) { return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two float32 values -> packed bf16 pair, round to nearest even (one conversion instruction).
+PS_DEV uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{a, b}), bf16x2_t));
+}
 
 // Row kinds of the query row list [active (block); window (n_win); centroids (n_proxy)].
 PS_DEV bool row_keeps_logits(const AttnArgs& a, int row) {
@@ -57,11 +63,13 @@ PS_DEV uint4 frag_hi(const float* x) {
   for (int e = 0; e < 4; ++e) w[e] = pack2(x[2 * e], x[2 * e + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
-PS_DEV uint4 frag_lo(const float* x) {
+// lo part of the bf16 hi/lo pair of x (hi = the pair frag_hi packs)
+PS_DEV uint4 frag_lo(const float* x, const uint4& hi) {
+  const uint32_t h[4] = {hi.x, hi.y, hi.z, hi.w};
   uint32_t w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    w[e] = pack2(x[2 * e] - bf16_to_f32(f32_to_bf16(x[2 * e])), x[2 * e + 1] - bf16_to_f32(f32_to_bf16(x[2 * e + 1])));
+    w[e] = pack2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -89,7 +97,10 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   const int nst = (k1 - k0 + 31) >> 5;
   const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)b * n * a.hkv * DH + kvh * DH;
   const uint16_t* vt = (const uint16_t*)a.vc + ((int64_t)b * a.hkv + kvh) * DH * n;
-  const float scale = 1.f / sqrtf((float)DH);
+  // logits are carried in log2 units: the queries are pre-scaled by log2(e)/sqrt(dh), so that
+  // softmax terms are single exp2 instructions; staged logits are converted back to natural units
+  const float qscale = 1.4426950408889634f / sqrtf((float)DH);
+  constexpr float kLn2 = 0.6931471805599453f;
 
   // this lane's source for load slot i of a step starting at key0
   auto issue = [&](uint4* buf, int step) __attribute__((always_inline)) {
@@ -115,22 +126,34 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   };
 
   // query fragments (B operand of S^T): lane holds row c16 of each tile, dh [32 ks + 8 g4, +8)
+  // (loaded before the first K/V stages are issued and converted after, so that the query
+  // loads overlap the K/V loads)
   uint4 qhi[RTW][KS], qlo[RTW][KS];
-  bool tile_on[RTW];
+  float4 qraw[RTW][KS][2];
+  bool tile_on[RTW], q_valid[RTW];
   auto load_q = [&](auto Tc) __attribute__((always_inline)) {
     constexpr int t = decltype(Tc)::value;
     const int tile = wave * RTW + t;
     tile_on[t] = tile * 16 < nrows;
     const int row = tile * 16 + c16;
-    const bool valid = row < nrows;
-    const float* qr = a.q + ((int64_t)b * a.mq + (valid ? row : 0)) * (a.hq * DH) + h * DH + 8 * g4;
+    q_valid[t] = row < nrows;
+    const float* qr = a.q + ((int64_t)b * a.mq + (q_valid[t] ? row : 0)) * (a.hq * DH) + h * DH + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      float x[8];
+      qraw[t][ks][0] = *(const float4*)(qr + 32 * ks);
+      qraw[t][ks][1] = *(const float4*)(qr + 32 * ks + 4);
+    }
+  };
+  auto convert_q = [&](auto Tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(Tc)::value;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = valid ? qr[32 * ks + e] : 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 u = qraw[t][ks][0], v = qraw[t][ks][1];
+      float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = q_valid[t] ? x[e] * qscale : 0.f;
       qhi[t][ks] = frag_hi(x);
-      qlo[t][ks] = frag_lo(x);
+      qlo[t][ks] = frag_lo(x, qhi[t][ks]);
     }
   };
   [&]<int... T>(std::integer_sequence<int, T...>) {
@@ -150,6 +173,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
     const int key0 = k0 + 32 * step;
     const int kg = key0 + 8 * g4;            // first key of this lane's 8-key group
     const bool shift = kg < n && kg + 8 > n; // ragged tail: V^T was loaded from n - 8
+    const bool full = key0 + 32 <= k1;       // no key of the step is past the chunk
     auto tile_step = [&](auto Tc) __attribute__((always_inline)) {
       constexpr int t = decltype(Tc)::value;
       if (!tile_on[t]) return;
@@ -166,48 +190,54 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
         sacc[kt] = acc;
       }
       float v[8];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kg + e < k1 ? sacc[e >> 2][e & 3] * scale : -INFINITY;
-        v[e] = x;
-        mx = fmaxf(mx, x);
+      for (int e = 0; e < 8; ++e) v[e] = sacc[e >> 2][e & 3];
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = kg + e < k1 ? v[e] : -INFINITY;
       }
+      float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
       const int row = (wave * RTW + t) * 16 + c16;
       if (row < nrows && row_keeps_logits(a, row)) {
         float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n + kg;
         if (kg + 8 <= k1) {
-          *(float4*)lg = make_float4(v[0], v[1], v[2], v[3]);
-          *(float4*)(lg + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          *(float4*)lg = make_float4(v[0] * kLn2, v[1] * kLn2, v[2] * kLn2, v[3] * kLn2);
+          *(float4*)(lg + 4) = make_float4(v[4] * kLn2, v[5] * kLn2, v[6] * kLn2, v[7] * kLn2);
         } else {
           for (int e = 0; e < 8; ++e)
-            if (kg + e < k1) lg[e] = v[e];
+            if (kg + e < k1) lg[e] = v[e] * kLn2;
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // every step has a key in range, so m_new is finite; exp2(-inf) = 0 covers the first step
+      // and masked keys
       const float m_new = fmaxf(m_run[t], mx);
-      const float corr = m_run[t] == -INFINITY ? 0.f : expf(m_run[t] - m_new);
+      const float corr = __builtin_amdgcn_exp2f(m_run[t] - m_new);
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = v[e] == -INFINITY ? 0.f : expf(v[e] - m_new);
+        v[e] = __builtin_amdgcn_exp2f(v[e] - m_new);
         ps += v[e];
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
       l_run[t] = l_run[t] * corr + ps;
       m_run[t] = m_new;
+      const bool rescale = __builtin_amdgcn_ballot_w64(corr != 1.f) != 0;   // wave-uniform
       if (shift) {
 #pragma unroll
         for (int e = 7; e >= 4; --e) v[e] = v[e - 4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = 0.f;
       }
-      const uint4 phi = frag_hi(v), plo = frag_lo(v);
+      const uint4 phi = frag_hi(v), plo = frag_lo(v, phi);
+      if (rescale) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[t][dt] *= corr;
         const uint4 vf = buf[(FK + dt) * 64 + lane];
         o[t][dt] = mfma(vf, phi, o[t][dt]);
         o[t][dt] = mfma(vf, plo, o[t][dt]);
@@ -221,6 +251,10 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   issue(b0, 0);
   issue(b1, 1);
   issue(b2, 2);
+  AT_VMCNT(LPW * 3);   // the query loads (issued before the three stages) have landed
+  [&]<int... T>(std::integer_sequence<int, T...>) {
+    (convert_q(std::integral_constant<int, T>{}), ...);
+  }(std::make_integer_sequence<int, RTW>{});
   for (int s = 0; s < nst; s += 4) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
       ([&] {
@@ -279,7 +313,7 @@ __global__ __launch_bounds__(DH) void attn_merge_kernel(AttnArgs a) {
   for (int c = 0; c < a.n_chunks; ++c) {
     const int64_t slot = (((int64_t)b * a.n_chunks + c) * a.hq + h) * a.mt + row;
     const float m = a.part_ml[slot * 2], l = a.part_ml[slot * 2 + 1];
-    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    const float f = __builtin_amdgcn_exp2f(m - M);   // running maxima in log2 units
     num += f * a.part_o[slot * DH + dd];
     den += f * l;
   }
