@@ -302,29 +302,54 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   }(std::make_integer_sequence<int, RTW>{});
 }
 
-// Merge of the per-chunk states of one (token row, head): o = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} l_c.
+// Merge of the per-chunk states of one (token row, head): o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
+// (running maxima in log2 units).  One wave per (row, head): lane c reads chunk c's (m, l), and
+// each lane then adds the chunks' outputs for its DH/64 columns in chunk order.
 template <int DH>
-__global__ __launch_bounds__(DH) void attn_merge_kernel(AttnArgs a) {
-  const int row = blockIdx.x, h = blockIdx.y, b = blockIdx.z, dd = threadIdx.x;
-  float M = -INFINITY;
-  for (int c = 0; c < a.n_chunks; ++c)
-    M = fmaxf(M, a.part_ml[((((int64_t)b * a.n_chunks + c) * a.hq + h) * a.mt + row) * 2]);
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const int64_t slot = (((int64_t)b * a.n_chunks + c) * a.hq + h) * a.mt + row;
-    const float m = a.part_ml[slot * 2], l = a.part_ml[slot * 2 + 1];
-    const float f = __builtin_amdgcn_exp2f(m - M);   // running maxima in log2 units
-    num += f * a.part_o[slot * DH + dd];
-    den += f * l;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int E = DH / 64;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.n_tok * a.hq) return;
+  const int row = pair / a.hq, h = pair % a.hq, b = blockIdx.y;
+  const int64_t cstride = (int64_t)a.hq * a.mt;                       // slots between chunks
+  const int64_t slot0 = ((int64_t)b * a.n_chunks * a.hq + h) * a.mt + row;
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (lane < a.n_chunks) ml = *(const float2*)(a.part_ml + (slot0 + lane * cstride) * 2);
+  const float M = wave_max(ml.x);
+  const float f = __builtin_amdgcn_exp2f(ml.x - M);                 // 0 for lanes past the chunks
+  const float den = wave_sum(f * ml.y);
+  float num[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) num[e] = 0.f;
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+    float t[8][E];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.n_chunks) {
+        const float* po = a.part_o + (slot0 + (c0 + j) * cstride) * DH + E * lane;
+#pragma unroll
+        for (int e = 0; e < E; ++e) t[j][e] = po[e];
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.n_chunks) {
+        const float fc = __shfl(f, c0 + j, 64);
+#pragma unroll
+        for (int e = 0; e < E; ++e) num[e] += fc * t[j][e];
+      }
   }
-  const float val = num / den;
   const int64_t plane = (int64_t)a.mt * a.hq * DH;
-  uint16_t* op = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH + dd;
-  uint16_t hi, lo;
-  split_bf16(val, hi, lo);
-  op[0] = hi;
-  op[plane] = lo;
-  if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + dd] = val;
+  uint16_t* op = (uint16_t*)a.o + (int64_t)b * 2 * plane + (int64_t)row * (a.hq * DH) + h * DH + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float val = num[e] / den;
+    uint16_t hi, lo;
+    split_bf16(val, hi, lo);
+    op[e] = hi;
+    op[plane + e] = lo;
+    if (a.chk) a.chk[((int64_t)b * a.chk_rows + row) * (a.hq * DH) + h * DH + E * lane + e] = val;
+  }
 }
 
 // ---- float32 attention (small models) ----------------------------------------------------------
@@ -588,9 +613,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
   if (a.n_chunks <= 1 || a.n_tok <= 0) return hipSuccess;
-  const dim3 grid(a.n_tok, a.hq, a.batch);
-  if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(64), 0, s, a);
-  else if (a.dh == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(128), 0, s, a);
+  if (a.n_chunks > 64) return hipErrorInvalidValue;
+  const dim3 grid(PS_CEIL_DIV(a.n_tok * a.hq, 4), a.batch);
+  if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, s, a);
+  else if (a.dh == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

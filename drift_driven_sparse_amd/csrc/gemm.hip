@@ -315,11 +315,7 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
   };
   float ss = 0.f;
   for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
-    float4 v = *(const float4*)(p + n);
-    for (int s = 1; s < a.ksplit; ++s) {
-      const float4 t = *(const float4*)(p + s * pstride + n);
-      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
-    }
+    const float4 v = sum_splits(p + n, pstride, a.ksplit);
     float x[4];
     if (res32) Quad<float>::load((const float*)res + n, x);
     else Quad<T>::load((const T*)res + n, x);

@@ -235,11 +235,7 @@ __global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
   if (c >= g.N) return;
   const int64_t sstride = (int64_t)g.batch * g.part_rows * g.N;
   const float* p = g.part + ((int64_t)b * g.part_rows + r) * g.N + c;
-  float4 v = *(const float4*)p;
-  for (int s = 1; s < g.ksplit; ++s) {
-    const float4 t = *(const float4*)(p + s * sstride);
-    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
-  }
+  const float4 v = sum_splits(p, sstride, g.ksplit);
   const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -260,12 +256,7 @@ __global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
   const int cg = (oc >> 4) * 32 + (oc & 15);
   const int64_t sstride = (int64_t)g.batch * g.part_rows * g.N;
   const float* p = g.part + ((int64_t)b * g.part_rows + r) * g.N + cg;
-  float4 gv = *(const float4*)p, uv = *(const float4*)(p + 16);
-  for (int s = 1; s < g.ksplit; ++s) {
-    const float4 tg = *(const float4*)(p + s * sstride), tu = *(const float4*)(p + s * sstride + 16);
-    gv.x += tg.x; gv.y += tg.y; gv.z += tg.z; gv.w += tg.w;
-    uv.x += tu.x; uv.y += tu.y; uv.z += tu.z; uv.w += tu.w;
-  }
+  const float4 gv = sum_splits(p, sstride, g.ksplit), uv = sum_splits(p + 16, sstride, g.ksplit);
   const float ga[4] = {gv.x, gv.y, gv.z, gv.w}, ua[4] = {uv.x, uv.y, uv.z, uv.w};
   bf16_t* act = (bf16_t*)e.act + (int64_t)b * 2 * e.act_rows * e.ffn;
   float hi[4], lo[4];

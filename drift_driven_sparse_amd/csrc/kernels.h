@@ -144,6 +144,24 @@ PS_DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// Sum of the split-K partials p[0], p[stride], ..., p[(ks-1)*stride] (four floats each), added
+// in split order; the loads of up to eight splits are issued before their additions.
+PS_DEV float4 sum_splits(const float* p, int64_t stride, int ks) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ks; s0 += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < ks) t[j] = *(const float4*)(p + (int64_t)(s0 + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < ks) {
+        v.x += t[j].x; v.y += t[j].y; v.z += t[j].z; v.w += t[j].w;
+      }
+  }
+  return v;
+}
+
 template <typename T>
 hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s);
 
