@@ -123,10 +123,40 @@ int hip_status(hipError_t e) { return e == hipSuccess ? POLESTAR_OK : POLESTAR_E
 int weight_group(const polestar_handle* h, int which) {
   if (h->dm.dtype != POLESTAR_BF16) return 1;
   switch (which) {
-    case POLESTAR_W_QKV: case POLESTAR_W_KV: return dl_tile_cols(DL_NARROW) / 16;
-    case POLESTAR_W_O: case POLESTAR_W_DOWN: return dl_tile_cols(DL_WIDE) / 16;
-    case POLESTAR_W_GU: return dl_tile_cols(DL_WIDE) / 16;   // DL_MID reads half groups
+    case POLESTAR_W_QKV: return dl_tile_cols(h->sh_qkv) / 16;
+    case POLESTAR_W_KV: return dl_tile_cols(h->sh_kv) / 16;
+    case POLESTAR_W_O: return dl_tile_cols(h->sh_o) / 16;
+    case POLESTAR_W_DOWN: return dl_tile_cols(h->sh_down) / 16;
+    case POLESTAR_W_GU: return dl_tile_cols(h->sh_gu) / 16;
     default: return 1;
+  }
+}
+
+// Shape and split-K factor of one bf16 projection (n_cols x k weight, batch sequences): the
+// candidate that keeps the largest share of the 256 compute units streaming weights, counting
+// the columns a partial last tile wastes and the rounds of workgroups past the first; ties go
+// to the smaller split (less partial-sum traffic), then to the earlier shape.  With pairs set
+// (gate/up), a shape whose waves hold an odd number of subtiles is only taken with split-K,
+// whose finish kernel forms the SwiGLU product.
+void plan_projection(int n_cols, int k, int batch, const int* shapes, int n_shapes, int cap, bool pairs,
+                     int32_t* shape, int32_t* ks) {
+  double best = -1.0;
+  *shape = shapes[0];
+  *ks = 1;
+  for (int i = 0; i < n_shapes; ++i) {
+    const int tc = dl_tile_cols(shapes[i]);
+    const int tiles = PS_CEIL_DIV(n_cols, tc) * batch;
+    const int v0 = pairs && dl_subtiles_per_wave(shapes[i]) % 2 ? 2 : 1;
+    for (int v = v0; v <= cap && v <= k / 32; ++v) {
+      const int wgs = tiles * v;
+      const int rounds = PS_CEIL_DIV(wgs, 256);
+      const double use = (double)n_cols * batch / ((double)tiles * tc) * wgs / (256.0 * rounds);
+      if (use > best + 1e-9 || (use > best - 1e-9 && v < *ks)) {
+        best = use;
+        *shape = shapes[i];
+        *ks = v;
+      }
+    }
   }
 }
 
@@ -256,7 +286,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
     dl.e = ep;
     {
       PROF(POLESTAR_K_QKV);
-      e = launch_dl<T>(dl, DL_NARROW, rows, s);
+      e = launch_dl<T>(dl, h->sh_qkv, rows, s);
       if (e == hipSuccess) e = launch_dl_finish<T>(dl, rows, s);
     }
   } else {
@@ -366,7 +396,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.e.kind = EPI_PARTIAL;
   {
     PROF(POLESTAR_K_OPROJ);
-    e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
+    e = launch_dl<T>(dl, h->sh_o, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   RowReduceArgs rr;
@@ -427,12 +457,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.e.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
-    if (dl.ksplit > 1) {
-      e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
-      if (e == hipSuccess) e = launch_dl_finish<T>(dl, max_rows, s);
-    } else {
-      e = launch_dl<T>(dl, DL_MID, max_rows, s);
-    }
+    e = launch_dl<T>(dl, h->sh_gu, max_rows, s);
+    if (e == hipSuccess) e = launch_dl_finish<T>(dl, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 3. out = h' + act W_down^T -> next active rows and the update packet
@@ -456,7 +482,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.e.kind = EPI_PARTIAL;
   {
     PROF(POLESTAR_K_DOWN);
-    e = launch_dl<T>(dl, DL_WIDE, max_rows, s);
+    e = launch_dl<T>(dl, h->sh_down, max_rows, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // the residual stream continues from the float32 h'
@@ -515,7 +541,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
     dl.e.chk_rows = h->win_max;
     dl.e.chk_ld = 2 * h->nkv;
     PROF(POLESTAR_K_KVNEXT);
-    e = launch_dl<T>(dl, DL_NARROW, g.n_win, s);
+    e = launch_dl<T>(dl, h->sh_kv, g.n_win, s);
     if (e == hipSuccess) e = launch_dl_finish<T>(dl, g.n_win, s);
     if (e != hipSuccess) return POLESTAR_E_HIP;
   }
@@ -851,18 +877,15 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
   int ks = PS_CEIL_DIV(256, ntiles);
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
-  // bf16 projections: split K until about 256 workgroups are busy
-  auto ks_for = [&](int n_cols, int tile_cols, int k, int cap) {
-    const int tiles = PS_CEIL_DIV(n_cols, tile_cols) * d.batch;
-    int v = 256 / tiles;
-    v = v < 1 ? 1 : (v > cap ? cap : v);
-    return v > k / 32 ? k / 32 : v;
-  };
-  h->ks_qkv = ks_for(h->nq + 2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 8);
-  h->ks_o = ks_for(d.d, dl_tile_cols(DL_WIDE), h->nq, 16);
-  h->ks_gu = ks_for(2 * d.ffn, dl_tile_cols(DL_WIDE), d.d, 4);
-  h->ks_down = ks_for(d.d, dl_tile_cols(DL_WIDE), d.ffn, 16);
-  h->ks_kv = ks_for(2 * h->nkv, dl_tile_cols(DL_NARROW), d.d, 16);
+  // bf16 projections: tile width and split-K so that about 256 workgroups are busy
+  {
+    const int one[] = {DL_NARROW, DL_N192, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8};
+    plan_projection(h->nq + 2 * h->nkv, d.d, d.batch, one, 3, 8, false, &h->sh_qkv, &h->ks_qkv);
+    plan_projection(d.d, h->nq, d.batch, two, 3, 16, false, &h->sh_o, &h->ks_o);
+    plan_projection(2 * d.ffn, d.d, d.batch, two, 3, 4, true, &h->sh_gu, &h->ks_gu);
+    plan_projection(d.d, d.ffn, d.batch, two, 3, 16, false, &h->sh_down, &h->ks_down);
+    plan_projection(2 * h->nkv, d.d, d.batch, one, 3, 16, false, &h->sh_kv, &h->ks_kv);
+  }
   // bf16 attention: split the keys so that about 256 workgroups run, at least 128 keys each
   {
     const int blocks32 = PS_CEIL_DIV(d.n_pos, 32);

@@ -12,7 +12,11 @@
 //
 // Waves form RG row groups x CG column groups: the CG waves of a row group read
 // the same A fragments, the RG waves of a column group the same weight
-// fragments.  Fragments are 16x16x32 MFMA operands in lane order.  Weights are
+// fragments.  Row tiles are dealt to the row groups in turn and the shapes used
+// have RG = 2 and CG = 4 where it matters, so each SIMD holds one wave of each row
+// group and carries the same number of matrix products: with hi/lo planes and
+// real data the products are what the projection's time depends on once the
+// stream is fed.  Fragments are 16x16x32 MFMA operands in lane order.  Weights are
 // pre-packed in groups of subtiles so that a workgroup's weights for one step are
 // one contiguous block and its whole range one contiguous stream.  A operands are
 // fragment-packed by their producers (one contiguous block per step), except the
@@ -140,40 +144,50 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const uint4* buf) {
-    uint4 w[NSUB];
+  // Row tiles are dealt to the row groups in turn (tile j*RG + rg is this wave's j-th), so the
+  // waves of a workgroup differ by at most one tile; a wave's tile count is uniform, and the
+  // loop below is instantiated once per count so that every stage reads all of its fragments
+  // before its first product, with no per-tile branch.
+  const int my_tiles = __builtin_amdgcn_readfirstlane(nrt > rg ? min(RTW, (nrt - rg + RG - 1) / RG) : 0);
+  auto run = [&](auto NTc) {
+    constexpr int NT = decltype(NTc)::value;
+    auto compute = [&](const uint4* buf) {
+      uint4 w[NSUB], a[PL][NT > 0 ? NT : 1];
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) w[sb] = buf[(FA + cg * NSUB + sb) * 64 + lane];
+      for (int sb = 0; sb < NSUB; ++sb) w[sb] = buf[(FA + cg * NSUB + sb) * 64 + lane];
 #pragma unroll
-    for (int p = 0; p < PL; ++p)
+      for (int p = 0; p < PL; ++p)
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-        if (rg * RTW + rt < nrt) {
-          const uint4 a = buf[(p * RT + rg * RTW + rt) * 64 + lane];
+        for (int j = 0; j < NT; ++j) a[p][j] = buf[(p * RT + j * RG + rg) * 64 + lane];
 #pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma_bf16(a, w[sb], acc[rt][sb]);
-        }
-      }
-  };
-
-  [&]<int... U>(std::integer_sequence<int, U...>) {
-    (issue(bp(std::integral_constant<int, U>{}), U), ...);
-  }(std::make_integer_sequence<int, P - 1>{});
-  for (int s = 0; s < n; s += P) {
+      for (int p = 0; p < PL; ++p)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int sb = 0; sb < NSUB; ++sb) acc[j][sb] = mfma_bf16(a[p][j], w[sb], acc[j][sb]);
+    };
     [&]<int... U>(std::integer_sequence<int, U...>) {
-      ([&] {
-        DL_VMCNT(LPW * (P - 2));          // this wave's loads of stage s+U have landed
-        __builtin_amdgcn_s_barrier();     // ... and everyone's; stage s+U-1 is fully consumed
-        issue(bp(std::integral_constant<int, (U + P - 1) % P>{}), s + U + P - 1);
-        if (s + U < n) compute(bp(std::integral_constant<int, U>{}));
-      }(), ...);
-    }(std::make_integer_sequence<int, P>{});
-  }
+      (issue(bp(std::integral_constant<int, U>{}), U), ...);
+    }(std::make_integer_sequence<int, P - 1>{});
+    for (int s = 0; s < n; s += P) {
+      [&]<int... U>(std::integer_sequence<int, U...>) {
+        ([&] {
+          DL_VMCNT(LPW * (P - 2));          // this wave's loads of stage s+U have landed
+          __builtin_amdgcn_s_barrier();     // ... and everyone's; stage s+U-1 is fully consumed
+          issue(bp(std::integral_constant<int, (U + P - 1) % P>{}), s + U + P - 1);
+          if (NT > 0 && s + U < n) compute(bp(std::integral_constant<int, U>{}));
+        }(), ...);
+      }(std::make_integer_sequence<int, P>{});
+    }
+  };
+  [&]<int... V>(std::integer_sequence<int, V...>) {
+    ((my_tiles == V ? (run(std::integral_constant<int, V>{}), 0) : 0), ...);
+  }(std::make_integer_sequence<int, RTW + 1>{});
   DL_VMCNT(0);   // no load may land in LDS after the workgroup ends
 
   // accumulator element (rt, sb, i) of this lane: row r, column n
   const int col0 = (nt * CG + cg) * NSUB * 16 + (lane & 15);
-  const int row0 = rg * RTW * 16 + 4 * (lane >> 4);
+  const int row0 = rg * 16 + 4 * (lane >> 4);   // accumulator tile j holds rows of tile j*RG + rg
   if (g.ksplit > 1 || KIND == EPI_PARTIAL) {
     float* out = g.part + ((int64_t)sp * g.batch + b) * g.part_rows * g.N;
 #pragma unroll
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * 16 + i, c = col0 + sb * 16;
+          const int r = row0 + rt * RG * 16 + i, c = col0 + sb * 16;
           if (r < rows_b && c < g.N) out[(int64_t)r * g.N + c] = acc[rt][sb][i];
         }
     return;
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * 16 + i, c = col0 + sb * 16;
+          const int r = row0 + rt * RG * 16 + i, c = col0 + sb * 16;
           if (r < rows_b && c < g.N) {
             if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
             else epi_kv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int j = 0; j < NSUB / 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * 16 + i;
+          const int r = row0 + rt * RG * 16 + i;
           const int oc = ((nt * CG + cg) * NSUB / 2 + j) * 16 + (lane & 15);
           if (r < rows_b && oc < e.ffn) {
             const float gv = acc[rt][2 * j][i], uv = acc[rt][2 * j + 1][i];
@@ -274,12 +288,13 @@ template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
 hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
   using C = DlCfg<RTW, RG, CG, NSUB, PL>;
   const dim3 grid(PS_CEIL_DIV(g.N, C::NCOL), g.batch, g.ksplit), block(64 * RG * CG);
-  switch (g.e.kind) {
+  // with split-K every kind writes raw partial sums; its epilogue runs in launch_dl_finish
+  switch (g.ksplit > 1 ? (int)EPI_PARTIAL : g.e.kind) {
     case EPI_PARTIAL: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_PARTIAL>), grid, block, 0, s, g); break;
     case EPI_QKV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_QKV>), grid, block, 0, s, g); break;
     case EPI_KV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_KV>), grid, block, 0, s, g); break;
     case EPI_SWIGLU:
-      if constexpr (PL == 2) {
+      if constexpr (PL == 2 && NSUB % 2 == 0) {
         hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_SWIGLU>), grid, block, 0, s, g);
         break;
       }
@@ -291,7 +306,22 @@ hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
 
 }  // namespace
 
-int dl_tile_cols(int shape) { return shape == DL_WIDE ? 256 : 128; }
+int dl_subtiles_per_wave(int shape) {
+  switch (shape) {
+    case DL_N192: case DL_W192: case DL_N96: return 3;
+    case DL_MID8: return 2;
+    default: return 4;
+  }
+}
+
+int dl_tile_cols(int shape) {
+  switch (shape) {
+    case DL_WIDE: return 256;
+    case DL_N192: case DL_W192: return 192;
+    case DL_N96: return 96;
+    default: return 128;
+  }
+}
 
 template <typename T>
 hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
@@ -301,14 +331,44 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     if (g.K % 32 || g.N % 16 || g.ksplit < 1 || g.ksplit > (g.K >> 5)) return hipErrorInvalidValue;
     if (g.wg < 1 || g.wg % (dl_tile_cols(shape) / 16) != 0) return hipErrorInvalidValue;
-    if (shape == DL_NARROW) {   // 3 x 2 waves, bf16 rows
+    if (shape == DL_NARROW || shape == DL_N192 || shape == DL_N96) {   // bf16 rows
       if (g.planes != 1) return hipErrorInvalidValue;
+      if (shape == DL_N96) {   // 4 x 2 waves of 48 columns
+        if (max_rows <= 64) return launch_cfg<T, 1, 4, 2, 3, 1>(g, s);
+        if (max_rows <= 128) return launch_cfg<T, 2, 4, 2, 3, 1>(g, s);
+        if (max_rows <= 192) return launch_cfg<T, 3, 4, 2, 3, 1>(g, s);
+        return hipErrorInvalidValue;
+      }
+      if (shape == DL_N192) {   // 2 x 4 waves of 48 columns
+        if (max_rows <= 32) return launch_cfg<T, 1, 2, 4, 3, 1>(g, s);
+        if (max_rows <= 64) return launch_cfg<T, 2, 2, 4, 3, 1>(g, s);
+        if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 3, 1>(g, s);
+        if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 3, 1>(g, s);
+        if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 3, 1>(g, s);
+        return hipErrorInvalidValue;
+      }
       if (max_rows <= 48) return launch_cfg<T, 1, 3, 2, 4, 1>(g, s);
       if (max_rows <= 96) return launch_cfg<T, 2, 3, 2, 4, 1>(g, s);
       if (max_rows <= 144) return launch_cfg<T, 3, 3, 2, 4, 1>(g, s);
       return hipErrorInvalidValue;
     }
     if (g.planes != 2) return hipErrorInvalidValue;
+    if (shape == DL_MID8) {   // 2 x 4 waves of 32 columns, hi/lo planes
+      if (max_rows <= 32) return launch_cfg<T, 1, 2, 4, 2, 2>(g, s);
+      if (max_rows <= 64) return launch_cfg<T, 2, 2, 4, 2, 2>(g, s);
+      if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 2, 2>(g, s);
+      if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 2, 2>(g, s);
+      if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 2, 2>(g, s);
+      return hipErrorInvalidValue;
+    }
+    if (shape == DL_W192) {   // 2 x 4 waves of 48 columns, hi/lo planes
+      if (max_rows <= 32) return launch_cfg<T, 1, 2, 4, 3, 2>(g, s);
+      if (max_rows <= 64) return launch_cfg<T, 2, 2, 4, 3, 2>(g, s);
+      if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 3, 2>(g, s);
+      if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 3, 2>(g, s);
+      if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 3, 2>(g, s);
+      return hipErrorInvalidValue;
+    }
     if (shape == DL_WIDE) {   // 2 x 4 waves, hi/lo planes
       if (max_rows <= 32) return launch_cfg<T, 1, 2, 4, 4, 2>(g, s);
       if (max_rows <= 64) return launch_cfg<T, 2, 2, 4, 4, 2>(g, s);

@@ -20,6 +20,7 @@ struct polestar_handle {
   int32_t nq, nkv;   // Hq*dh, Hkv*dh
   int32_t ksplit;    // split-K factor of the N = d projections (float32 path)
   int32_t ks_qkv, ks_o, ks_gu, ks_down, ks_kv;   // split-K factors of the bf16 projections
+  int32_t sh_qkv, sh_o, sh_gu, sh_down, sh_kv;   // their workgroup shapes (DlShape)
   int32_t rq, rt, rw;   // mq, mt, win_max rounded up to whole 16-row tiles (packed operands)
   int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
   int32_t lm_tiles;  // vocab / 64 rounded up
@@ -179,10 +180,18 @@ struct DlArgs {
   int32_t part_rows;
   EpiParams e;
 };
-enum DlShape { DL_NARROW = 0,   // 3 row groups x 2 column groups x 64 columns: 128-column tiles
-               DL_WIDE = 1,     // 2 row groups x 4 column groups: 256-column tiles
-               DL_MID = 2 };    // 2 row groups x 2 column groups: 128-column tiles
+// Workgroup shapes: row groups x column groups (waves), columns per wave.  One bf16 plane:
+// NARROW, N192, N96; hi/lo planes: WIDE, MID, W192, MID8.
+enum DlShape { DL_NARROW = 0,   // 3 x 2 waves of 64 columns: 128-column tiles
+               DL_WIDE = 1,     // 2 x 4 waves of 64 columns: 256-column tiles
+               DL_MID = 2,      // 2 x 2 waves of 64 columns: 128-column tiles
+               DL_N192 = 3,     // 2 x 4 waves of 48 columns: 192-column tiles
+               DL_W192 = 4,     // 2 x 4 waves of 48 columns: 192-column tiles
+               DL_N96 = 5,      // 4 x 2 waves of 48 columns: 96-column tiles
+               DL_MID8 = 6 };   // 2 x 4 waves of 32 columns: 128-column tiles
 int dl_tile_cols(int shape);
+// 16-column subtiles per wave; the in-kernel SwiGLU epilogue needs an even count (gate/up pairs)
+int dl_subtiles_per_wave(int shape);
 template <typename T>
 hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s);
 template <typename T>
