@@ -327,12 +327,11 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   {
     PROF(POLESTAR_K_ATTN);
     e = launch_attention<T>(at_, s);
-    if (e == hipSuccess && std::is_same<T, bf16_t>::value) e = launch_attn_merge(at_, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   {
-    PROF(POLESTAR_K_KL);
-    e = launch_kl(at_, s);
+    PROF(POLESTAR_K_KL);   // chunk merge and KL drift
+    e = launch_merge_kl(at_, std::is_same<T, bf16_t>::value, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
   // 4. top-k clusters and the selected rows

@@ -6,10 +6,10 @@
 // [batch][Hkv][dh][n] so that V^T fragments are contiguous along keys.
 //
 // bf16 path (attn_chunk_kernel): workgroups over (key chunk, head); MFMA 16x16x32 with the
-// float32 queries and the probabilities as bf16 hi + lo pairs, online softmax per chunk, and
-// attn_merge_kernel combining the chunks.  Logits of proxy rows and (when requested) active rows
-// go to a staging buffer; kl_kernel then forms the KL drift against the previous logits and
-// replaces them.
+// float32 queries and the probabilities as bf16 hi + lo pairs, online softmax per chunk.  Logits
+// of proxy rows and (when requested) active rows go to a staging buffer.  One following launch
+// (attn_merge_kl_kernel) combines the chunks of the token rows and forms the KL drift of the
+// staged rows against the previous logits, which the staged logits then replace.
 //
 // float32 path (attn_f32_kernel, small models): LDS-staged vector FMA.
 #include <utility>
@@ -306,12 +306,11 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 // (running maxima in log2 units).  One wave per (row, head): lane c reads chunk c's (m, l), and
 // each lane then adds the chunks' outputs for its DH/64 columns in chunk order.
 template <int DH>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+PS_DEV void attn_merge_pair(const AttnArgs& a, int pair, int b) {
   constexpr int E = DH / 64;
   const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= a.n_tok * a.hq) return;
-  const int row = pair / a.hq, h = pair % a.hq, b = blockIdx.y;
+  const int row = pair / a.hq, h = pair % a.hq;
   const int64_t cstride = (int64_t)a.hq * a.mt;                       // slots between chunks
   const int64_t slot0 = ((int64_t)b * a.n_chunks * a.hq + h) * a.mt + row;
   float2 ml = make_float2(-INFINITY, 0.f);
@@ -476,11 +475,9 @@ PS_DEV float wave_kl(const float* sv, const float* pv, int n, int lane) {
 
 // One wave per (staged row, head): KL against the previous logits (when wanted),
 // then the staged logits replace them.  Staged rows: [proxies; active].
-__global__ __launch_bounds__(256) void kl_kernel(AttnArgs a) {
+PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
-  const int b = blockIdx.y;
   if (item >= nst * a.hq) return;
   const int sr = item / a.hq, h = item % a.hq;
   const int n = a.n_pos;
@@ -514,6 +511,16 @@ __global__ __launch_bounds__(256) void kl_kernel(AttnArgs a) {
     const int j = lane + 64 * i;
     if (j < n) prev[j] = sv[i];
   }
+}
+
+// One launch for the two consumers of the chunk kernel's outputs: workgroups below
+// merge_wgs merge token rows (four (row, head) pairs each), the rest form the KL items
+// (four each).  Both only read what the attention kernel wrote and write disjoint outputs.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_merge_kl_kernel(AttnArgs a, int merge_wgs) {
+  const int wave = threadIdx.x >> 6, b = blockIdx.y;
+  if ((int)blockIdx.x < merge_wgs) attn_merge_pair<DH>(a, blockIdx.x * 4 + wave, b);
+  else kl_item(a, (blockIdx.x - merge_wgs) * 4 + wave, b);
 }
 
 // Per sequence: D_c = sum_h max(0, KL_{c,h}); top-k clusters by (D desc, index asc), found by
@@ -611,20 +618,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
-  if (a.n_chunks <= 1 || a.n_tok <= 0) return hipSuccess;
-  if (a.n_chunks > 64) return hipErrorInvalidValue;
-  const dim3 grid(PS_CEIL_DIV(a.n_tok * a.hq, 4), a.batch);
-  if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, s, a);
-  else if (a.dh == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_kl(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_merge_kl(const AttnArgs& a, bool merge, hipStream_t s) {
+  merge = merge && a.n_chunks > 1 && a.n_tok > 0;
+  if (merge && a.n_chunks > 64) return hipErrorInvalidValue;
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
-  if (nst == 0) return hipSuccess;
-  hipLaunchKernelGGL(kl_kernel, dim3(PS_CEIL_DIV(nst * a.hq, 4), a.batch), dim3(256), 0, s, a);
+  const int mw = merge ? PS_CEIL_DIV(a.n_tok * a.hq, 4) : 0, kw = PS_CEIL_DIV(nst * a.hq, 4);
+  if (mw + kw == 0) return hipSuccess;
+  const dim3 grid(mw + kw, a.batch);
+  if (!merge || a.dh == 128) hipLaunchKernelGGL(attn_merge_kl_kernel<128>, grid, dim3(256), 0, s, a, mw);
+  else if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kl_kernel<64>, grid, dim3(256), 0, s, a, mw);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

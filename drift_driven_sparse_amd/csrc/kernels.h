@@ -276,7 +276,7 @@ struct AttnArgs {
   float* act_logits;      // [batch][block][hq][n] or null
   float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
   int32_t chunk_keys;     // bf16 path: keys per workgroup (multiple of 32)
-  int32_t n_chunks;       // workgroups along the keys; > 1 -> partial states merged by launch_attn_merge
+  int32_t n_chunks;       // workgroups along the keys; > 1 -> partial states merged by launch_merge_kl
   float* part_o;          // [batch][n_chunks][hq][mt][dh] unnormalised outputs of token rows
   float* part_ml;         // [batch][n_chunks][hq][mt][2] running max and sum
   int32_t act_kl;         // compute active-row KL against act_logits before overwrite
@@ -285,8 +285,8 @@ struct AttnArgs {
 };
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
-hipError_t launch_kl(const AttnArgs& a, hipStream_t s);
+// merge of the key chunks (bf16 path: merge = true) and the KL drift, one launch
+hipError_t launch_merge_kl(const AttnArgs& a, bool merge, hipStream_t s);
 
 struct TopkArgs {
   int32_t batch, K, k, hq, block, win_max, n_win;
