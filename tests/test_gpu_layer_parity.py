@@ -41,6 +41,15 @@ CASES = {
                               {"blk_start": 96}),
     "tiny_bf16_small_window": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=4, gen=64), 1,
                                {"blk_start": 4}),
+    # sweep ranges of the page's ablations: clusters K, selected clusters k, block B, window (p, s)*B
+    "sweep_K4_k2_B8_w10": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, n_clusters=4,
+                                        top_k=2, block=8, win_prefix=8, win_suffix=0), 1, {}),
+    "sweep_K16_k6_B16_w21": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, n_clusters=16,
+                                          top_k=6, block=16, win_prefix=32, win_suffix=16), 1, {}),
+    "sweep_K16_k8_B64_w10": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, n_clusters=16,
+                                          top_k=8, block=64, win_prefix=64, win_suffix=0), 1, {}),
+    "sweep_K8_k4_B16_w31": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, block=16,
+                                         win_prefix=48, win_suffix=16), 1, {}),
 }
 
 
