@@ -50,7 +50,7 @@ struct ProfScope {
 };
 #define PROF(id) ProfScope _prof_##__LINE__(h, s, id)
 
-constexpr int kMaxRows = 144;   // rows of one projection tile column
+constexpr int kMaxRows = 192;   // rows of one projection tile column (block + window + centroids)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

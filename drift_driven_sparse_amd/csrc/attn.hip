@@ -595,7 +595,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   } else {
     const int tiles = PS_CEIL_DIV(nrows, 16);
     const int nwv = 2 * PS_CEIL_DIV(tiles, 2);   // one wave per 16-row tile, even count
-    if (nwv > 10 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos)
+    if (nwv > 12 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos)
       return hipErrorInvalidValue;
     dim3 grid(a.n_chunks, a.hq, a.batch);
     auto go = [&](auto DHc, auto NWc) {
@@ -608,7 +608,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         case 4: go(DHc, std::integral_constant<int, 4>{}); break;
         case 6: go(DHc, std::integral_constant<int, 6>{}); break;
         case 8: go(DHc, std::integral_constant<int, 8>{}); break;
-        default: go(DHc, std::integral_constant<int, 10>{}); break;
+        case 10: go(DHc, std::integral_constant<int, 10>{}); break;
+        default: go(DHc, std::integral_constant<int, 12>{}); break;
       }
     };
     if (a.dh == 64) by_waves(std::integral_constant<int, 64>{});

@@ -384,6 +384,7 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
   if (max_rows <= 32) return dispatch_kind<T, 2>(g, e, s);
   if (max_rows <= 64) return dispatch_kind<T, 4>(g, e, s);
   if (max_rows <= 144) return dispatch_kind<T, 9>(g, e, s);
+  if (max_rows <= 192) return dispatch_kind<T, 12>(g, e, s);
   return hipErrorInvalidValue;
 }
 

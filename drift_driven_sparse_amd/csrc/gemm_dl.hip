@@ -345,11 +345,13 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
         if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 3, 1>(g, s);
         if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 3, 1>(g, s);
         if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 3, 1>(g, s);
+        if (max_rows <= 192) return launch_cfg<T, 6, 2, 4, 3, 1>(g, s);
         return hipErrorInvalidValue;
       }
       if (max_rows <= 48) return launch_cfg<T, 1, 3, 2, 4, 1>(g, s);
       if (max_rows <= 96) return launch_cfg<T, 2, 3, 2, 4, 1>(g, s);
       if (max_rows <= 144) return launch_cfg<T, 3, 3, 2, 4, 1>(g, s);
+      if (max_rows <= 192) return launch_cfg<T, 4, 3, 2, 4, 1>(g, s);
       return hipErrorInvalidValue;
     }
     if (g.planes != 2) return hipErrorInvalidValue;
@@ -359,6 +361,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
       if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 2, 2>(g, s);
       if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 2, 2>(g, s);
       if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 2, 2>(g, s);
+      if (max_rows <= 192) return launch_cfg<T, 6, 2, 4, 2, 2>(g, s);
       return hipErrorInvalidValue;
     }
     if (shape == DL_W192) {   // 2 x 4 waves of 48 columns, hi/lo planes
@@ -367,6 +370,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
       if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 3, 2>(g, s);
       if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 3, 2>(g, s);
       if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 3, 2>(g, s);
+      if (max_rows <= 192) return launch_cfg<T, 6, 2, 4, 3, 2>(g, s);
       return hipErrorInvalidValue;
     }
     if (shape == DL_WIDE) {   // 2 x 4 waves, hi/lo planes
@@ -375,6 +379,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
       if (max_rows <= 96) return launch_cfg<T, 3, 2, 4, 4, 2>(g, s);
       if (max_rows <= 128) return launch_cfg<T, 4, 2, 4, 4, 2>(g, s);
       if (max_rows <= 160) return launch_cfg<T, 5, 2, 4, 4, 2>(g, s);
+      if (max_rows <= 192) return launch_cfg<T, 6, 2, 4, 4, 2>(g, s);
       return hipErrorInvalidValue;
     }
     if (shape == DL_MID) {    // 2 x 2 waves, hi/lo planes
@@ -383,6 +388,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
       if (max_rows <= 96) return launch_cfg<T, 3, 2, 2, 4, 2>(g, s);
       if (max_rows <= 128) return launch_cfg<T, 4, 2, 2, 4, 2>(g, s);
       if (max_rows <= 160) return launch_cfg<T, 5, 2, 2, 4, 2>(g, s);
+      if (max_rows <= 192) return launch_cfg<T, 6, 2, 2, 4, 2>(g, s);
       return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;

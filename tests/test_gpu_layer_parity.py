@@ -50,6 +50,11 @@ CASES = {
                                           top_k=8, block=64, win_prefix=64, win_suffix=0), 1, {}),
     "sweep_K8_k4_B16_w31": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, block=16,
                                          win_prefix=48, win_suffix=16), 1, {}),
+    "sweep_K8_k4_B32_w31": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256,
+                                         win_prefix=96, win_suffix=32), 1, {}),
+    # 188 rows per sequence: the widest row tiling of every kernel
+    "rows188_K4_k2_B64": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, n_clusters=4,
+                                       top_k=2, block=64, win_prefix=96, win_suffix=24), 1, {}),
 }
 
 
