@@ -129,9 +129,10 @@ __global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, doubl
 //            the new centroid columns and, for NVFP4 storage, the members' re-quantised groups.
 constexpr int kChunk = 256;
 
-// Window rows of sequence b labelled c, ascending, into mem[] (with their norms when nr != null).
-// Returns the member count; every thread of the 256-thread workgroup gets it.
-PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* nr, int* wcnt) {
+// Window rows of sequence b labelled c, ascending, into mem[] (with the reciprocals of their norms,
+// 0 for a zero row, when rinv != null).  Returns the member count; every thread of the
+// 256-thread workgroup gets it.
+PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* rinv, int* wcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t wbase = (int64_t)b * a.win_max;
   const bool in = tid < a.geom.n_win && a.win_m[wbase + tid] == c;
@@ -146,7 +147,10 @@ PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* nr, 
   if (in) {
     const int pos = off + __popcll(m & ((1ull << lane) - 1ull));
     mem[pos] = tid;
-    if (nr) nr[pos] = a.wnorm[wbase + tid];
+    if (rinv) {
+      const double nr = a.wnorm[wbase + tid];
+      rinv[pos] = nr > 0.0 ? 1.0 / nr : 0.0;
+    }
   }
   __syncthreads();
   return tot;
@@ -208,20 +212,24 @@ template <typename T>
 __global__ __launch_bounds__(256) void centroid_sum_kernel(ClusterArgs a) {
   __shared__ double red[4];
   __shared__ int mem[256];
-  __shared__ double nr[256];
+  __shared__ double rinv[256];
   __shared__ int wcnt[4];
   const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = a.d, n = ch * kChunk + tid;
-  const int nmem = members_of(a, b, c, mem, nr, wcnt);
+  const int nmem = members_of(a, b, c, mem, rinv, wcnt);
   if (nmem == 0) return;
   const int64_t wbase = (int64_t)b * a.win_max;
   const T* rows = (const T*)a.ws_rows;
-  double acc = 0.0;
+  double acc = 0.0;   // unit rows added in ascending row order; a zero row adds nothing
   if (n < d) {
-#pragma unroll 4
-    for (int m = 0; m < nmem; ++m) {
-      const float x = St<T>::load(rows, (wbase + mem[m]) * d + n);
-      if (nr[m] > 0.0) acc += (double)x / nr[m];
+    constexpr int U = 16;   // members loaded per batch before they are added
+    for (int m0 = 0; m0 < nmem; m0 += U) {
+      float x[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) x[j] = St<T>::load(rows, (wbase + mem[min(m0 + j, nmem - 1)]) * d + n);
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if (m0 + j < nmem) acc += (double)x[j] * rinv[m0 + j];
     }
   }
   if (n < d) a.z64[((int64_t)b * a.K + c) * d + n] = acc;
