@@ -116,15 +116,35 @@ template <> struct Quad<bf16_t> {
 // takes part; `red` holds one float per wave.
 template <typename T, typename Store>
 PS_DEV void rmsnorm_row(const T* src, int d, float eps, float* red, Store&& store) {
+  // the first QH quads of each thread stay in registers between the two passes
+  constexpr int QH = 4;
+  const int step = 4 * blockDim.x, n1 = 4 * threadIdx.x + QH * step;
+  float xs[QH][4];
   float ss = 0.f;
-  for (int n = 4 * threadIdx.x; n < d; n += 4 * blockDim.x) {
+#pragma unroll
+  for (int i = 0; i < QH; ++i) {
+    const int n = 4 * threadIdx.x + i * step;
+    if (n < d) {
+      Quad<T>::load(src + n, xs[i]);
+      ss += xs[i][0] * xs[i][0] + xs[i][1] * xs[i][1] + xs[i][2] * xs[i][2] + xs[i][3] * xs[i][3];
+    }
+  }
+  for (int n = n1; n < d; n += step) {
     float x[4];
     Quad<T>::load(src + n, x);
     ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  for (int n = 4 * threadIdx.x; n < d; n += 4 * blockDim.x) {
+#pragma unroll
+  for (int i = 0; i < QH; ++i) {
+    const int n = 4 * threadIdx.x + i * step;
+    if (n < d) {
+      float x[4] = {xs[i][0] * inv, xs[i][1] * inv, xs[i][2] * inv, xs[i][3] * inv};
+      store(n, x);
+    }
+  }
+  for (int n = n1; n < d; n += step) {
     float x[4];
     Quad<T>::load(src + n, x);
     x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;

@@ -313,10 +313,12 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
     if (a.out_f32) Quad<float>::load((const float*)obase + ooff + n, x);
     else Quad<T>::load((const T*)obase + ooff + n, x);
   };
-  float ss = 0.f;
-  for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
+  // the first RH quads of each thread stay in registers for the normalisation pass
+  constexpr int RH = 2;
+  const int step = 4 * blockDim.x;
+  float xs[RH][4];
+  auto reduce_quad = [&](int n, float* x) __attribute__((always_inline)) {
     const float4 v = sum_splits(p + n, pstride, a.ksplit);
-    float x[4];
     if (res32) Quad<float>::load((const float*)res + n, x);
     else Quad<T>::load((const T*)res + n, x);
     x[0] += v.x; x[1] += v.y; x[2] += v.z; x[3] += v.w;
@@ -328,6 +330,19 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
       for (int i = 0; i < 4; ++i) x[i] = St<T>::round(x[i]);
       Quad<T>::store((T*)obase + ooff + n, x);
     }
+  };
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RH; ++i) {
+    const int n = 4 * threadIdx.x + i * step;
+    if (n < a.d) {
+      reduce_quad(n, xs[i]);
+      ss += xs[i][0] * xs[i][0] + xs[i][1] * xs[i][1] + xs[i][2] * xs[i][2] + xs[i][3] * xs[i][3];
+    }
+  }
+  for (int n = 4 * threadIdx.x + RH * step; n < a.d; n += step) {
+    float x[4];
+    reduce_quad(n, x);
     ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   if (!a.norm || r < a.norm_from) return;   // uniform over the workgroup
@@ -335,9 +350,7 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
   const float inv = 1.f / sqrtf(ss / (float)a.d + a.eps);
   const int rn = r - a.norm_from;
   const int planes = a.norm_planes ? 2 : 1;
-  for (int n = 4 * threadIdx.x; n < a.d; n += 4 * blockDim.x) {
-    float x[4];
-    load_out(n, x);
+  auto norm_quad = [&](int n, float* x) __attribute__((always_inline)) {
     x[0] *= inv; x[1] *= inv; x[2] *= inv; x[3] *= inv;
     const int64_t o0 = (int64_t)b * a.norm_bstride +
                        (a.norm_tiles > 0 ? apack(rn, n, 0, planes, a.norm_tiles) : (int64_t)rn * a.d + n);
@@ -354,6 +367,16 @@ __global__ __launch_bounds__(1024) void row_reduce_kernel(RowReduceArgs a) {
     } else {
       Quad<T>::store((T*)a.norm + o0, x);
     }
+  };
+#pragma unroll
+  for (int i = 0; i < RH; ++i) {
+    const int n = 4 * threadIdx.x + i * step;
+    if (n < a.d) norm_quad(n, xs[i]);
+  }
+  for (int n = 4 * threadIdx.x + RH * step; n < a.d; n += step) {
+    float x[4];
+    load_out(n, x);
+    norm_quad(n, x);
   }
 }
 
