@@ -327,16 +327,106 @@ def nvfp4_dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (vals * sv[..., None]).reshape(rows, half * 2).astype(np.float32)
 
 
-def residual_quantize(h: np.ndarray, z: np.ndarray, m: np.ndarray):
-    """NVFP4 codes of r = float32(h) - float32(z_M(i)) (one float32 subtraction)."""
+# ---------------------------------------------------------------------------
+# Other residual formats  [Polestar Table 11 ablation: FP8, INT8, MXFP4 residuals.
+# The pages name the formats only; readings: FP8 = OCP E4M3FN per value, no scale;
+# INT8 and MXFP4 = OCP microscaling blocks of 32 values sharing one E8M0
+# (power-of-two) scale, X = 2^(floor(log2 amax) - emax), emax = 0 for INT8
+# (values q * 2^-6, q in [-128, 127]) and 2 for E2M1 (MXFP4).]
+# ---------------------------------------------------------------------------
+
+
+def fp8_quantize(r: np.ndarray):
+    """Residual rows [rows, d] -> E4M3FN bytes [rows, d] (sign bit | magnitude code, nearest
+    even, saturating at 448; zero is +0).  No scales."""
+    r = np.asarray(r, dtype=np.float32)
+    mag = e4m3_encode(np.abs(r).astype(np.float64)).astype(np.uint8)
+    neg = (r < 0) & (mag != 0)
+    return (mag | np.where(neg, 0x80, 0)).astype(np.uint8), np.zeros((r.shape[0], 0), dtype=np.uint8)
+
+
+def fp8_dequantize(codes: np.ndarray, scales=None) -> np.ndarray:
+    return e4m3_value(np.asarray(codes, dtype=np.int64)).astype(np.float32)
+
+
+def mx_exponent(amax: np.ndarray, emax: int) -> np.ndarray:
+    """Shared E8M0 exponent of a block: floor(log2(amax)) - emax, clamped to [-127, 127];
+    -127 for an all-zero block."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = f * 2^e, f in [0.5, 1)
+    x = np.where(amax > 0, e - 1 - emax, -127)
+    return np.clip(x, -127, 127).astype(np.int64)
+
+
+def mxint8_quantize(r: np.ndarray):
+    """Rows [rows, d] -> (int8 codes as u8 [rows, d], E8M0 scale bytes [rows, d/32]).
+
+    Per block of 32: X = 2^(floor(log2 amax)); q = clamp(rne(r / X * 64), -128, 127).
+    """
+    r = np.asarray(r, dtype=np.float32)
+    rows, d = r.shape
+    assert d % 32 == 0
+    g = r.reshape(rows, d // 32, 32).astype(np.float64)
+    ex = mx_exponent(np.max(np.abs(g), axis=-1), 0)
+    y = np.ldexp(g, (6 - ex)[..., None])                 # exact: r / X * 2^6
+    q = np.clip(np.rint(y), -128, 127).astype(np.int64)  # np.rint: nearest, ties to even
+    return (q & 0xFF).astype(np.uint8).reshape(rows, d), (ex + 127).astype(np.uint8)
+
+
+def mxint8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    q = np.where(c >= 128, c - 256, c)
+    rows, d = q.shape
+    ex = np.asarray(scales, dtype=np.int64) - 127
+    v = np.ldexp(q.reshape(rows, d // 32, 32).astype(np.float64), (ex - 6)[..., None])
+    return v.reshape(rows, d).astype(np.float32)
+
+
+def mxfp4_quantize(r: np.ndarray):
+    """Rows [rows, d] -> (E2M1 nibbles packed [rows, d/2], E8M0 scale bytes [rows, d/32]).
+
+    Per block of 32: X = 2^(floor(log2 amax) - 2); code = E2M1(r / X) (nearest even,
+    saturating at 6).  Element 2j goes in the low nibble.
+    """
+    r = np.asarray(r, dtype=np.float32)
+    rows, d = r.shape
+    assert d % 32 == 0
+    g = r.reshape(rows, d // 32, 32).astype(np.float64)
+    ex = mx_exponent(np.max(np.abs(g), axis=-1), 2)
+    codes = e2m1_encode(np.ldexp(g, (-ex)[..., None])).astype(np.uint8).reshape(rows, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (ex + 127).astype(np.uint8)
+
+
+def mxfp4_dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows, half = packed.shape
+    codes = np.empty((rows, half * 2), dtype=np.int64)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    ex = np.asarray(scales, dtype=np.int64) - 127
+    v = np.ldexp(e2m1_value(codes).reshape(rows, half * 2 // 32, 32), ex[..., None])
+    return v.reshape(rows, half * 2).astype(np.float32)
+
+
+RESID_CODECS = {
+    "nvfp4": (nvfp4_quantize, nvfp4_dequantize),
+    "fp8": (fp8_quantize, fp8_dequantize),
+    "mxint8": (mxint8_quantize, mxint8_dequantize),
+    "mxfp4": (mxfp4_quantize, mxfp4_dequantize),
+}
+
+
+def residual_quantize(h: np.ndarray, z: np.ndarray, m: np.ndarray, fmt: str = "nvfp4"):
+    """Codes of r = float32(h) - float32(z_M(i)) (one float32 subtraction) in format fmt."""
     r = (np.asarray(h, dtype=np.float32) - np.asarray(z, dtype=np.float32)[np.asarray(m)]).astype(np.float32)
-    return nvfp4_quantize(r)
+    return RESID_CODECS[fmt][0](r)
 
 
-def residual_dequantize(packed, scales, z, m, st) -> np.ndarray:
+def residual_dequantize(packed, scales, z, m, st, fmt: str = "nvfp4") -> np.ndarray:
     """Window rows rebuilt as st(float32(z_M(i)) + dequant(r)) (float32 add, then store)."""
     base = np.asarray(z, dtype=np.float32)[np.asarray(m)]
-    s = (base + nvfp4_dequantize(packed, scales)).astype(np.float32)
+    s = (base + RESID_CODECS[fmt][1](packed, scales)).astype(np.float32)
     return st(s.astype(np.float64))
 
 
@@ -404,8 +494,8 @@ class Cfg:
 
 def window_rows_now(ls: Dict, cfg: Cfg) -> np.ndarray:
     """Current window hidden rows: raw storage, or NVFP4 residual + centroid."""
-    if cfg.resid == "nvfp4":
-        return residual_dequantize(ls["codes"], ls["scales"], ls["Z"], ls["M"], cfg.st)
+    if cfg.resid != "raw":
+        return residual_dequantize(ls["codes"], ls["scales"], ls["Z"], ls["M"], cfg.st, cfg.resid)
     return np.array(ls["H"], dtype=np.float64, copy=True)
 
 
@@ -424,8 +514,8 @@ def cluster_update(ls: Dict, cfg: Cfg, u_rows=None, u_idx=None) -> Dict:
         patched[np.asarray(u_idx)] = True
     z_new = cfg.st(centroid_update(h, ls["M"], ls["Z"]))
     ls["Z"] = z_new
-    if cfg.resid == "nvfp4":
-        ls["codes"], ls["scales"] = residual_quantize(h, z_new, ls["M"])
+    if cfg.resid != "raw":
+        ls["codes"], ls["scales"] = residual_quantize(h, z_new, ls["M"], cfg.resid)
     else:
         ls["H"] = h.copy()
     return {"h": h, "patched": patched}
@@ -623,8 +713,8 @@ def block_entry_layer_state(H_in: np.ndarray, K: np.ndarray, V: np.ndarray, Wq: 
     z = cfg.st(z)
     ls = {"K": np.array(K, dtype=np.float64, copy=True), "V": np.array(V, dtype=np.float64, copy=True),
           "Z": z, "M": m, "trace": trace}
-    if cfg.resid == "nvfp4":
-        ls["codes"], ls["scales"] = residual_quantize(hw, z, m)
+    if cfg.resid != "raw":
+        ls["codes"], ls["scales"] = residual_quantize(hw, z, m, cfg.resid)
     else:
         ls["H"] = hw.copy()
     zq = project(z, Wq, cfg.eps, cfg.st).reshape(cfg.K, cfg.hq, cfg.dh)

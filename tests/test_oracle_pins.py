@@ -338,6 +338,67 @@ def test_nvfp4_nibble_order():
     assert packed[0, 0] == (0x7 | (0x1 << 4))
 
 
+def test_fp8_codes_match_the_e4m3fn_encoding():
+    # OCP E4M3FN: 1.0 = 0x38, 448 = 0x7E (largest finite), 2^-6 = 0x08 (smallest normal),
+    # 2^-9 = 0x01 (smallest subnormal); negative values set bit 7; zero is +0
+    x = np.array([[1.0, 448.0, 2.0 ** -6, 2.0 ** -9, -1.0, -448.0, 0.0, -0.0]], dtype=np.float32)
+    codes, scales = O.fp8_quantize(x)
+    assert codes.tolist() == [[0x38, 0x7E, 0x08, 0x01, 0xB8, 0xFE, 0x00, 0x00]] and scales.shape == (1, 0)
+    # every finite code round-trips; beyond 448 saturates; ties go to the even mantissa
+    mags = O.e4m3_value(np.arange(0x7F)).astype(np.float32)[None]
+    assert np.array_equal(O.fp8_quantize(mags)[0][0], np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(O.fp8_dequantize(O.fp8_quantize(-mags[:, 1:])[0]), -mags[:, 1:])
+    assert O.fp8_quantize(np.array([[1000.0, 1.0625, 1.1875]], dtype=np.float32))[0].tolist() == [[0x7E, 0x38, 0x3A]]
+
+
+def test_mxint8_hand_blocks():
+    r = np.zeros((3, 32), dtype=np.float32)
+    r[0, :4] = [1.5, -0.75, 0.5, 2.0 ** -7]           # amax 1.5 -> X = 1; 2^-7 * 64 = 0.5 -> 0 (even)
+    r[1, :3] = [-2.0, 1.0, 3 * 2.0 ** -6]             # amax 2 -> X = 2; 3*2^-6 / 2 * 64 = 1.5 -> 2
+    r[2, :2] = [127.5 / 64, -1.0]                     # 127.5 rounds to 128 -> clamped to 127
+    codes, scales = O.mxint8_quantize(r)
+    q = codes.astype(np.int64)
+    q = np.where(q >= 128, q - 256, q)
+    assert q[0, :4].tolist() == [96, -48, 32, 0] and scales[0, 0] == 127
+    assert q[1, :3].tolist() == [-64, 32, 2] and scales[1, 0] == 128
+    assert q[2, :2].tolist() == [127, -64] and scales[2, 0] == 127
+    z, zs = O.mxint8_quantize(np.zeros((1, 32), dtype=np.float32))
+    assert not z.any() and zs[0, 0] == 0                # all-zero block: exponent -127
+    assert np.array_equal(O.mxint8_dequantize(codes[:1], scales[:1])[0, :3], np.float32([1.5, -0.75, 0.5]))
+
+
+def test_mxint8_error_bound():
+    r = (RNG.normal(size=(8, 256)) * np.exp(RNG.uniform(-8, 6, size=(8, 1)))).astype(np.float32)
+    codes, scales = O.mxint8_quantize(r)
+    deq = O.mxint8_dequantize(codes, scales).astype(np.float64)
+    X = np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)
+    # half a step of X * 2^-6, or one step where the largest value is clamped at 127
+    assert np.all(np.abs(deq - r) <= X * 2.0 ** -6 + 1e-300)
+    assert np.all((np.abs(deq - r) <= X * 2.0 ** -7) | (np.abs(r) >= X * 127 / 64))
+
+
+def test_mxfp4_hand_blocks_and_round_trip():
+    r = np.zeros((3, 32), dtype=np.float32)
+    r[0, :3] = [6.0, 0.5, -1.5]                       # amax 6 -> X = 1, exact
+    r[1, :2] = [7.0, -0.25]                           # amax 7 -> X = 1: 7 saturates to 6
+    r[2, :2] = [0.75, 0.125]                          # amax 0.75 -> X = 1/8: 6 and 1
+    packed, scales = O.mxfp4_quantize(r)
+    assert (scales[:, 0].astype(int) - 127).tolist() == [0, 0, -3]
+    deq = O.mxfp4_dequantize(packed, scales)
+    assert deq[0, :3].tolist() == [6.0, 0.5, -1.5] and deq[1, :2].tolist() == [6.0, -0.0]
+    assert deq[2, :2].tolist() == [0.75, 0.125]
+    assert packed[0, 0] == (0x7 | (0x1 << 4))           # element 2j in the low nibble
+    # representable blocks (values on the E2M1 grid times 2^k, each block holding +-4 or +-6)
+    rows, d = 6, 128
+    grid = np.concatenate([O.E2M1_MAG, -O.E2M1_MAG[1:]])
+    vals = RNG.choice(grid, size=(rows, d))
+    vals[:, ::32] = RNG.choice([4.0, -6.0], size=(rows, d // 32))
+    k = RNG.integers(-20, 20, size=(rows, d // 32))
+    x = np.ldexp(vals.reshape(rows, d // 32, 32), k[..., None]).reshape(rows, d).astype(np.float32)
+    p2, s2 = O.mxfp4_quantize(x)
+    assert np.array_equal(O.mxfp4_dequantize(p2, s2), x)
+
+
 # ---------------------------------------------------------------- selection
 def test_topk_bruteforce_and_ties():
     for _ in range(200):
