@@ -368,7 +368,8 @@ def test_mxint8_hand_blocks():
 
 
 def test_mxint8_error_bound():
-    r = (RNG.normal(size=(8, 256)) * np.exp(RNG.uniform(-8, 6, size=(8, 1)))).astype(np.float32)
+    rng = np.random.default_rng(57)
+    r = (rng.normal(size=(8, 256)) * np.exp(rng.uniform(-8, 6, size=(8, 1)))).astype(np.float32)
     codes, scales = O.mxint8_quantize(r)
     deq = O.mxint8_dequantize(codes, scales).astype(np.float64)
     X = np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)
@@ -389,11 +390,12 @@ def test_mxfp4_hand_blocks_and_round_trip():
     assert deq[2, :2].tolist() == [0.75, 0.125]
     assert packed[0, 0] == (0x7 | (0x1 << 4))           # element 2j in the low nibble
     # representable blocks (values on the E2M1 grid times 2^k, each block holding +-4 or +-6)
+    rng = np.random.default_rng(58)
     rows, d = 6, 128
     grid = np.concatenate([O.E2M1_MAG, -O.E2M1_MAG[1:]])
-    vals = RNG.choice(grid, size=(rows, d))
-    vals[:, ::32] = RNG.choice([4.0, -6.0], size=(rows, d // 32))
-    k = RNG.integers(-20, 20, size=(rows, d // 32))
+    vals = rng.choice(grid, size=(rows, d))
+    vals[:, ::32] = rng.choice([4.0, -6.0], size=(rows, d // 32))
+    k = rng.integers(-20, 20, size=(rows, d // 32))
     x = np.ldexp(vals.reshape(rows, d // 32, 32), k[..., None]).reshape(rows, d).astype(np.float32)
     p2, s2 = O.mxfp4_quantize(x)
     assert np.array_equal(O.mxfp4_dequantize(p2, s2), x)
