@@ -8,14 +8,16 @@ from __future__ import annotations
 
 import ctypes as C
 import os
-from typing import Optional
+from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpolestar.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_ALIGN, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F32, BF16 = 0, 1
-RESID_RAW, RESID_NVFP4 = 0, 1
+RESID_RAW, RESID_NVFP4, RESID_FP8, RESID_MXINT8, RESID_MXFP4 = 0, 1, 2, 3, 4
+RESID_BY_NAME = {"raw": RESID_RAW, "nvfp4": RESID_NVFP4, "fp8": RESID_FP8, "mxint8": RESID_MXINT8,
+                 "mxfp4": RESID_MXFP4}
 CLUSTER_ENTRY, CLUSTER_UPDATE = 0, 1
 DRIFT_REFRESH, DRIFT_ACTIVE_ONLY = 0, 1
 W_QKV, W_O, W_GU, W_DOWN, W_KV, W_LM = 0, 1, 2, 3, 4, 5
@@ -25,7 +27,7 @@ EXPORTED = [
     "polestar_set_check", "polestar_weight_packed_size", "polestar_pack_weight", "polestar_cluster",
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
-    "polestar_profile_read",
+    "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -93,6 +95,9 @@ def lib() -> C.CDLL:
         L.polestar_nvfp4_pack.argtypes = [vp, i64, i32, vp, vp, vp]
         L.polestar_nvfp4_unpack.argtypes = [vp, vp, i64, i32, vp, vp]
         L.polestar_nvfp4_pack_host.argtypes = [vp, i64, i32, vp, vp]
+        L.polestar_resid_bytes.argtypes = [i32, i32, C.POINTER(i64), C.POINTER(i64)]
+        L.polestar_resid_pack.argtypes = [i32, vp, i64, i32, vp, vp, vp]
+        L.polestar_resid_unpack.argtypes = [i32, vp, vp, i64, i32, vp, vp]
         L.polestar_profile.argtypes = [vp, C.c_int]
         L.polestar_profile_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32)]
         for name in EXPORTED:
@@ -205,6 +210,22 @@ def polestar_nvfp4_pack(x, rows, d, codes, scales, stream=None) -> None:
 def polestar_nvfp4_unpack(codes, scales, rows, d, x, stream=None) -> None:
     _ck(lib().polestar_nvfp4_unpack(ptr(codes), ptr(scales), rows, d, ptr(x), stream_ptr(stream)),
         "polestar_nvfp4_unpack")
+
+
+def polestar_resid_bytes(fmt: int, d: int) -> Tuple[int, int]:
+    cb, sb = C.c_int64(), C.c_int64()
+    _ck(lib().polestar_resid_bytes(fmt, d, C.byref(cb), C.byref(sb)), "polestar_resid_bytes")
+    return cb.value, sb.value
+
+
+def polestar_resid_pack(fmt, x, rows, d, codes, scales, stream=None) -> None:
+    _ck(lib().polestar_resid_pack(fmt, ptr(x), rows, d, ptr(codes), ptr(scales), stream_ptr(stream)),
+        "polestar_resid_pack")
+
+
+def polestar_resid_unpack(fmt, codes, scales, rows, d, x, stream=None) -> None:
+    _ck(lib().polestar_resid_unpack(fmt, ptr(codes), ptr(scales), rows, d, ptr(x), stream_ptr(stream)),
+        "polestar_resid_unpack")
 
 
 def polestar_nvfp4_pack_host(x, rows, d, codes, scales) -> None:

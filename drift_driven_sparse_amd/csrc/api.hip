@@ -200,7 +200,7 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.wnorm = at<double>(ws, h->ws.wstat);
   a.nchunk = PS_CEIL_DIV(d.d, 256);
   a.cpart = a.wnorm + (size_t)d.batch * h->win_max;
-  a.nvfp4 = d.resid_fmt == POLESTAR_RESID_NVFP4;
+  a.resid = d.resid_fmt;
   if (a.geom.n_win == 0) return POLESTAR_OK;
   PROF(POLESTAR_K_CLUSTER);
   return hip_status(launch_cluster<T>(a, s));
@@ -831,7 +831,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   *out = nullptr;
   const polestar_dims& d = *dims;
   if (d.dtype != POLESTAR_F32 && d.dtype != POLESTAR_BF16) return POLESTAR_E_DTYPE;
-  if (d.resid_fmt != POLESTAR_RESID_RAW && d.resid_fmt != POLESTAR_RESID_NVFP4) return POLESTAR_E_DTYPE;
+  if (d.resid_fmt < POLESTAR_RESID_RAW || d.resid_fmt > POLESTAR_RESID_MXFP4) return POLESTAR_E_DTYPE;
   if (d.d <= 0 || d.n_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 || d.ffn <= 0 || d.n_pos <= 0 ||
       d.batch <= 0 || d.block <= 0 || d.win_prefix < 0 || d.win_suffix < 0 || d.n_clusters <= 0 ||
       d.top_k <= 0 || d.vocab < 0)
@@ -850,7 +850,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   } else {
     if (d.ffn % 4 || d.d % 4) return POLESTAR_E_UNSUPPORTED;
   }
-  if (d.resid_fmt == POLESTAR_RESID_NVFP4 && d.dtype != POLESTAR_BF16) return POLESTAR_E_UNSUPPORTED;
+  if (d.resid_fmt != POLESTAR_RESID_RAW && d.dtype != POLESTAR_BF16) return POLESTAR_E_UNSUPPORTED;
   const polestar_params& p = *params;
   if (!(p.rms_eps >= 0.f) || p.hist < 0 || p.hist > 16 || p.kmeans_iters < 0 || p.kmeans_iters > 1000)
     return POLESTAR_E_ARG;
@@ -991,9 +991,10 @@ int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int3
   int rc = check_ws(h, ws, ws_bytes);
   if (rc) return rc;
   if ((rc = check_blk(h, blk_start))) return rc;
-  const bool nv = h->dm.resid_fmt == POLESTAR_RESID_NVFP4;
+  const bool nv = h->dm.resid_fmt != POLESTAR_RESID_RAW;   // residual codes instead of raw rows
   if (!L->win_z || !L->win_m) return POLESTAR_E_NULL;
-  if (nv ? (!L->win_codes || !L->win_scales) : !L->win_h) return POLESTAR_E_NULL;
+  if (nv ? (!L->win_codes || (resid_scale_bytes(h->dm.resid_fmt, h->dm.d) > 0 && !L->win_scales)) : !L->win_h)
+    return POLESTAR_E_NULL;
   if (mode == POLESTAR_CLUSTER_ENTRY && (!init_idx || !entry_h)) return POLESTAR_E_NULL;
   if (u_in && (!u_in->rows || !u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
   if (!aligned16(L->win_z) || (!nv && !aligned16(L->win_h)) || (entry_h && !aligned16(entry_h)) ||
@@ -1084,6 +1085,31 @@ int polestar_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t r
   if (!x || !codes || !scales) return POLESTAR_E_NULL;
   if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;
   return hip_status(launch_nvfp4_unpack(codes, scales, rows, d, x, (hipStream_t)stream));
+}
+
+int polestar_resid_bytes(int32_t fmt, int32_t d, int64_t* code_bytes, int64_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return POLESTAR_E_NULL;
+  if (fmt < POLESTAR_RESID_RAW || fmt > POLESTAR_RESID_MXFP4) return POLESTAR_E_DTYPE;
+  if (d <= 0 || d % 32) return POLESTAR_E_SHAPE;
+  *code_bytes = resid_code_bytes(fmt, d);
+  *scale_bytes = resid_scale_bytes(fmt, d);
+  return POLESTAR_OK;
+}
+
+int polestar_resid_pack(int32_t fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                        void* stream) {
+  if (fmt <= POLESTAR_RESID_RAW || fmt > POLESTAR_RESID_MXFP4) return POLESTAR_E_DTYPE;
+  if (rows < 0 || d <= 0 || d % 32) return POLESTAR_E_SHAPE;
+  if (rows > 0 && (!x || !codes || (resid_scale_bytes(fmt, d) > 0 && !scales))) return POLESTAR_E_NULL;
+  return hip_status(launch_resid_pack(fmt, x, rows, d, codes, scales, (hipStream_t)stream));
+}
+
+int polestar_resid_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                          void* stream) {
+  if (fmt <= POLESTAR_RESID_RAW || fmt > POLESTAR_RESID_MXFP4) return POLESTAR_E_DTYPE;
+  if (rows < 0 || d <= 0 || d % 32) return POLESTAR_E_SHAPE;
+  if (rows > 0 && (!x || !codes || (resid_scale_bytes(fmt, d) > 0 && !scales))) return POLESTAR_E_NULL;
+  return hip_status(launch_resid_unpack(fmt, codes, scales, rows, d, x, (hipStream_t)stream));
 }
 
 int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales) {

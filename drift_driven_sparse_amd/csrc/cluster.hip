@@ -38,7 +38,7 @@ __global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, doubl
     for (int n = tid; n < d; n += blockDim.x) {
       const float x = St<T>::load(src, (int64_t)w * d + n);
       xh[(int64_t)w * d + n] = nr > 0.0 ? (double)x / nr : 0.0;
-      if (!a.nvfp4 && a.win_h != a.entry_h)
+      if (!a.resid && a.win_h != a.entry_h)
         ((T*)a.win_h)[((int64_t)b * a.win_max + w) * d + n] = ((const T*)src)[(int64_t)w * d + n];
     }
   }
@@ -99,22 +99,20 @@ __global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, doubl
   for (int i = tid; i < K * d; i += blockDim.x)
     St<T>::store_d((T*)a.win_z + (int64_t)b * K * d, i, z[i]);
   __syncthreads();
-  if (a.nvfp4) {
-    const int ng = d / 16;
+  if (a.resid) {
+    const int G = resid_group(a.resid), ng = d / G;
+    const int64_t cb = resid_code_bytes(a.resid, d), sb = resid_scale_bytes(a.resid, d);
     for (int i = tid; i < nwin * ng; i += blockDim.x) {
-      const int w = i / ng, gi = i % ng;
+      const int w = i / ng, g0 = (i % ng) * G;
       const int c = a.iters > 0 ? lab[w] : 0;
-      float r[16];
-      uint32_t codes[16];
-      for (int e = 0; e < 16; ++e) {
-        const float h = St<T>::load(src, (int64_t)w * d + gi * 16 + e);
-        const float zz = St<T>::load((const T*)a.win_z + ((int64_t)b * K + c) * d, gi * 16 + e);
+      float r[32];
+      for (int e = 0; e < G; ++e) {
+        const float h = St<T>::load(src, (int64_t)w * d + g0 + e);
+        const float zz = St<T>::load((const T*)a.win_z + ((int64_t)b * K + c) * d, g0 + e);
         r[e] = h - zz;
       }
-      const uint32_t sc = nvfp4_group(r, codes);
       const int64_t row = (int64_t)b * a.win_max + w;
-      a.scales[row * ng + gi] = (uint8_t)sc;
-      for (int e = 0; e < 8; ++e) a.codes[row * (d / 2) + gi * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
+      resid_encode_group(a.resid, r, a.codes + row * cb, a.scales + row * sb, g0);
     }
   }
 }
@@ -184,12 +182,11 @@ __global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
     if (pr >= 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = St<T>::load((const T*)a.u_rows, (wbase + pr) * d + n0 + e);
-    } else if (a.nvfp4) {
-      const uint32_t bytes = *(const uint32_t*)(a.codes + (wbase + w) * (d / 2) + n0 / 2);
-      const float sv = e4m3_value(a.scales[(wbase + w) * (d / 16) + n0 / 16]);
+    } else if (a.resid) {
+      const uint8_t* cr = a.codes + (wbase + w) * resid_code_bytes(a.resid, d);
+      const uint8_t* sr = a.scales + (wbase + w) * resid_scale_bytes(a.resid, d);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = St<T>::round(St<T>::load(zc, n0 + e) + sv * e2m1_value((bytes >> (4 * e)) & 15u));
+      for (int e = 0; e < 8; ++e) x[e] = St<T>::round(St<T>::load(zc, n0 + e) + resid_value(a.resid, cr, sr, n0 + e));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = St<T>::load((const T*)a.win_h, dst + n0 + e);
@@ -197,7 +194,7 @@ __global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       St<T>::store(rows, dst + n0 + e, x[e]);
-      if (pr >= 0 && !a.nvfp4) St<T>::store((T*)a.win_h, dst + n0 + e, x[e]);
+      if (pr >= 0 && !a.resid) St<T>::store((T*)a.win_h, dst + n0 + e, x[e]);
       ss += (double)x[e] * (double)x[e];
     }
   }
@@ -255,22 +252,19 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
     if (ns > 0.0) St<T>::store_d(zc, n, a.z64[zrow * d + n] / ns);   // kept when the sum vanishes
     zsh[tid] = St<T>::load(zc, n);
   }
-  if (!a.nvfp4) return;
+  if (!a.resid) return;
   __syncthreads();
-  // residuals of the members' 16-element groups in this chunk against the new centroid
+  // residuals of the members' groups in this chunk against the new centroid
   const int64_t wbase = (int64_t)b * a.win_max;
-  const int gpc = min(kChunk, d - n0) / 16;
+  const int G = resid_group(a.resid), gpc = min(kChunk, d - n0) / G;
+  const int64_t cb = resid_code_bytes(a.resid, d), sb = resid_scale_bytes(a.resid, d);
   const T* rows = (const T*)a.ws_rows;
   for (int i = tid; i < nmem * gpc; i += blockDim.x) {
     const int w = mem[i / gpc], gi = i % gpc;
     const int64_t row = wbase + w;
-    float r[16];
-    uint32_t codes[16];
-    for (int e = 0; e < 16; ++e) r[e] = St<T>::load(rows, row * d + n0 + gi * 16 + e) - zsh[gi * 16 + e];
-    const uint32_t sc = nvfp4_group(r, codes);
-    const int g = n0 / 16 + gi;
-    a.scales[row * (d / 16) + g] = (uint8_t)sc;
-    for (int e = 0; e < 8; ++e) a.codes[row * (d / 2) + g * 8 + e] = (uint8_t)(codes[2 * e] | (codes[2 * e + 1] << 4));
+    float r[32];
+    for (int e = 0; e < G; ++e) r[e] = St<T>::load(rows, row * d + n0 + gi * G + e) - zsh[gi * G + e];
+    resid_encode_group(a.resid, r, a.codes + row * cb, a.scales + row * sb, n0 + gi * G);
   }
 }
 
@@ -313,6 +307,27 @@ __global__ void nvfp4_unpack_kernel(const uint8_t* codes, const uint8_t* scales,
   }
 }
 
+// One thread per group of resid_group(fmt) values of a row.
+__global__ void resid_pack_kernel(int fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales) {
+  const int G = resid_group(fmt), ng = d / G;
+  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (g >= rows * ng) return;
+  const int64_t row = g / ng;
+  const int g0 = (int)(g % ng) * G;
+  float r[32];
+  for (int e = 0; e < G; ++e) r[e] = x[row * d + g0 + e];
+  resid_encode_group(fmt, r, codes + row * resid_code_bytes(fmt, d), scales + row * resid_scale_bytes(fmt, d), g0);
+}
+
+__global__ void resid_unpack_kernel(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d,
+                                    float* x) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= rows * d) return;
+  const int64_t row = i / d;
+  const int n = (int)(i % d);
+  x[i] = resid_value(fmt, codes + row * resid_code_bytes(fmt, d), scales + row * resid_scale_bytes(fmt, d), n);
+}
+
 }  // namespace
 
 template <typename T>
@@ -351,6 +366,24 @@ hipError_t launch_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int6
   if (groups == 0) return hipSuccess;
   hipLaunchKernelGGL(nvfp4_unpack_kernel, dim3((unsigned)PS_CEIL_DIV(groups, 256)), dim3(256), 0, s, codes, scales,
                      groups, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_pack(int fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s) {
+  const int64_t groups = rows * (d / resid_group(fmt));
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(resid_pack_kernel, dim3((unsigned)PS_CEIL_DIV(groups, 256)), dim3(256), 0, s, fmt, x, rows, d,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_unpack(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                               hipStream_t s) {
+  const int64_t n = rows * d;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(resid_unpack_kernel, dim3((unsigned)PS_CEIL_DIV(n, 256)), dim3(256), 0, s, fmt, codes, scales,
+                     rows, d, x);
   return hipGetLastError();
 }
 

@@ -243,6 +243,86 @@ PS_HD uint32_t nvfp4_group(const float* r, uint32_t* codes) {
   return sc;
 }
 
+// ---- residual formats (window storage) --------------------------------------
+// Per row of d values: code bytes and scale bytes, and the values sharing one scale.
+//   NVFP4:  E2M1 nibbles, E4M3FN scale per 16           (d/2 + d/16 bytes)
+//   FP8:    E4M3FN byte per value, no scale             (d bytes)
+//   MXINT8: int8 per value, E8M0 scale per 32 (OCP MX)  (d + d/32 bytes)
+//   MXFP4:  E2M1 nibbles, E8M0 scale per 32 (OCP MX)    (d/2 + d/32 bytes)
+// Element 2j of a nibble format is the low nibble of byte j.
+PS_HD int64_t resid_code_bytes(int fmt, int64_t d) {
+  return (fmt == POLESTAR_RESID_NVFP4 || fmt == POLESTAR_RESID_MXFP4) ? d / 2 : (fmt == POLESTAR_RESID_RAW ? 0 : d);
+}
+PS_HD int64_t resid_scale_bytes(int fmt, int64_t d) {
+  return fmt == POLESTAR_RESID_NVFP4 ? d / 16 : ((fmt == POLESTAR_RESID_MXINT8 || fmt == POLESTAR_RESID_MXFP4) ? d / 32 : 0);
+}
+PS_HD int resid_group(int fmt) { return (fmt == POLESTAR_RESID_MXINT8 || fmt == POLESTAR_RESID_MXFP4) ? 32 : 16; }
+
+// E8M0 exponent of an OCP MX block: floor(log2 amax) - emax, clamped to [-127, 127]; -127 for
+// an all-zero block.
+PS_HD int mx_exponent(float amax, int emax) {
+  if (!(amax > 0.f)) return -127;
+  int e = ilogbf(amax) - emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Value n of a row's residual (codes/scales point at the row).
+PS_HD float resid_value(int fmt, const uint8_t* codes, const uint8_t* scales, int n) {
+  switch (fmt) {
+    case POLESTAR_RESID_NVFP4:
+      return e4m3_value(scales[n >> 4]) * e2m1_value((codes[n >> 1] >> (4 * (n & 1))) & 15u);
+    case POLESTAR_RESID_FP8:
+      return e4m3_value(codes[n]);
+    case POLESTAR_RESID_MXINT8:
+      return ldexpf((float)(int8_t)codes[n], (int)scales[n >> 5] - 127 - 6);
+    case POLESTAR_RESID_MXFP4:
+      return ldexpf(e2m1_value((codes[n >> 1] >> (4 * (n & 1))) & 15u), (int)scales[n >> 5] - 127);
+    default:
+      return 0.f;
+  }
+}
+
+// Quantise the resid_group(fmt) values r of the group starting at column g0 of a row.
+PS_HD void resid_encode_group(int fmt, const float* r, uint8_t* codes, uint8_t* scales, int g0) {
+  switch (fmt) {
+    case POLESTAR_RESID_NVFP4: {
+      uint32_t c[16];
+      scales[g0 >> 4] = (uint8_t)nvfp4_group(r, c);
+      for (int e = 0; e < 8; ++e) codes[(g0 >> 1) + e] = (uint8_t)(c[2 * e] | (c[2 * e + 1] << 4));
+      break;
+    }
+    case POLESTAR_RESID_FP8:
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t m = e4m3_encode(fabsf(r[e]));
+        codes[g0 + e] = (uint8_t)((r[e] < 0.f && m != 0u) ? (m | 0x80u) : m);
+      }
+      break;
+    case POLESTAR_RESID_MXINT8: {
+      float amax = 0.f;
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(r[e]));
+      const int ex = mx_exponent(amax, 0);
+      scales[g0 >> 5] = (uint8_t)(ex + 127);
+      for (int e = 0; e < 32; ++e) {
+        float q = rintf(ldexpf(r[e], 6 - ex));   // exact scaling, nearest even
+        q = q < -128.f ? -128.f : (q > 127.f ? 127.f : q);
+        codes[g0 + e] = (uint8_t)(int8_t)(int)q;
+      }
+      break;
+    }
+    case POLESTAR_RESID_MXFP4: {
+      float amax = 0.f;
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(r[e]));
+      const int ex = mx_exponent(amax, 2);
+      scales[g0 >> 5] = (uint8_t)(ex + 127);
+      for (int e = 0; e < 16; ++e)
+        codes[(g0 >> 1) + e] = (uint8_t)(e2m1_encode(ldexpf(r[2 * e], -ex)) | (e2m1_encode(ldexpf(r[2 * e + 1], -ex)) << 4));
+      break;
+    }
+    default:
+      break;
+  }
+}
+
 // ---- misc -------------------------------------------------------------------
 #define PS_CEIL_DIV(a, b) (((a) + (b) - 1) / (b))
 

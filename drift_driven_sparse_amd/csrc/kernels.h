@@ -246,7 +246,7 @@ struct ClusterArgs {
   double* wnorm;            // [batch][win_max] float64 norms of the current window rows
   double* cpart;            // [batch][K][nchunk] chunk sums of squares of the member sums
   int32_t nchunk;           // ceil(d / 256)
-  int nvfp4;
+  int resid;                // residual format of the window storage (POLESTAR_RESID_*; 0: raw rows)
 };
 template <typename T>
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
@@ -318,6 +318,10 @@ struct DecideArgs {
 hipError_t launch_decide(const DecideArgs& a, hipStream_t s);
 
 // ---- NVFP4 test hooks -------------------------------------------------------------
+hipError_t launch_resid_pack(int fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s);
+hipError_t launch_resid_unpack(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,
+                               hipStream_t s);
 hipError_t launch_nvfp4_pack(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
 hipError_t launch_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,

@@ -32,7 +32,8 @@ class RefreshStack:
         d, bt, n = dims.d, dims.batch, dims.n_pos
         self.win_max = dims.win_prefix + dims.win_suffix
         self.tdt = _TDT[dims.dtype]
-        self.nvfp4 = dims.resid_fmt == B.RESID_NVFP4
+        self.resid = dims.resid_fmt != B.RESID_RAW   # window rows stored as residual codes
+        cb, sb = B.polestar_resid_bytes(dims.resid_fmt, dims.d) if self.resid else (0, 0)
         kvd = dims.n_kv_heads * dims.head_dim
         self.layers: List[Dict[str, torch.Tensor]] = []
         for _ in range(n_layers):
@@ -43,9 +44,9 @@ class RefreshStack:
                 "win_m": torch.zeros(bt, self.win_max, dtype=torch.int32, device=device),
                 "proxy_logits": torch.zeros(bt, dims.n_clusters, dims.n_heads, n, dtype=torch.float32, device=device),
             }
-            if self.nvfp4:
-                L["win_codes"] = torch.zeros(bt, self.win_max, d // 2, dtype=torch.uint8, device=device)
-                L["win_scales"] = torch.zeros(bt, self.win_max, d // 16, dtype=torch.uint8, device=device)
+            if self.resid:
+                L["win_codes"] = torch.zeros(bt, self.win_max, cb, dtype=torch.uint8, device=device)
+                L["win_scales"] = torch.zeros(bt, self.win_max, max(sb, 1), dtype=torch.uint8, device=device)
             else:
                 L["win_h"] = torch.zeros(bt, self.win_max, d, dtype=self.tdt, device=device)
             self.layers.append(L)

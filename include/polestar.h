@@ -28,9 +28,12 @@
  *                        [blk_start - win_prefix, blk_start) U
  *                        [blk_start + block, blk_start + block + win_suffix),
  *                        clipped to [0, n_pos); n_win <= win_max rows are used.
- *   NVFP4 window codes   [batch, win_max, d/2] u8 (element 2j low nibble,
- *                        2j+1 high nibble), scales [batch, win_max, d/16] u8
- *                        (OCP E4M3FN bytes)
+ *   window codes         [batch, win_max, code bytes per row] u8 and scales
+ *                        [batch, win_max, scale bytes per row] u8 of the
+ *                        residual format (polestar_resid_bytes): NVFP4 d/2
+ *                        nibbles (element 2j low nibble, 2j+1 high) + d/16
+ *                        E4M3FN scales; FP8 d E4M3FN bytes; MXINT8 d int8
+ *                        + d/32 E8M0 scales; MXFP4 d/2 nibbles + d/32 E8M0
  *   centroids            [batch, n_clusters, d]; labels [batch, win_max] i32
  *   proxy logits         [batch, n_clusters, n_heads, n_pos] f32
  *   active-block logits  [batch, block, n_heads, n_pos] f32
@@ -84,7 +87,13 @@ enum {
 };
 
 enum { POLESTAR_F32 = 0, POLESTAR_BF16 = 1 };
-enum { POLESTAR_RESID_RAW = 0, POLESTAR_RESID_NVFP4 = 1 };
+enum {
+  POLESTAR_RESID_RAW = 0,     /* window rows stored as they are */
+  POLESTAR_RESID_NVFP4 = 1,   /* residual to the centroid: E2M1 + E4M3FN scale per 16 [App. C.3] */
+  POLESTAR_RESID_FP8 = 2,     /* residual as E4M3FN per value, no scale [Table 11] */
+  POLESTAR_RESID_MXINT8 = 3,  /* residual as int8 with an E8M0 scale per 32 (OCP MX) [Table 11 "INT8"] */
+  POLESTAR_RESID_MXFP4 = 4    /* residual as E2M1 with an E8M0 scale per 32 (OCP MX) [Table 11] */
+};
 enum { POLESTAR_CLUSTER_ENTRY = 0, POLESTAR_CLUSTER_UPDATE = 1 };
 enum { POLESTAR_DRIFT_REFRESH = 0, POLESTAR_DRIFT_ACTIVE_ONLY = 1 };
 enum {
@@ -112,7 +121,7 @@ typedef struct polestar_dims {
   int32_t top_k;      /* k (1..K) */
   int32_t vocab;      /* LM-head rows, 0 when polestar_commit is not used */
   int32_t dtype;      /* POLESTAR_F32 | POLESTAR_BF16 */
-  int32_t resid_fmt;  /* POLESTAR_RESID_RAW | POLESTAR_RESID_NVFP4 (bf16 only) */
+  int32_t resid_fmt;  /* POLESTAR_RESID_* (formats other than RAW: bf16 only) */
 } polestar_dims;
 
 /* Scalar hyper-parameters [Polestar §5.1 and Table 5]. */
@@ -137,8 +146,8 @@ typedef struct polestar_layer {
   void* k_cache;        /* [batch, n_pos, n_kv_heads, head_dim], in/out */
   void* v_cache;        /* [batch, n_kv_heads, head_dim, n_pos], in/out */
   void* win_h;          /* RAW: window rows [batch, win_max, d], in/out */
-  uint8_t* win_codes;   /* NVFP4: [batch, win_max, d/2], in/out */
-  uint8_t* win_scales;  /* NVFP4: [batch, win_max, d/16], in/out */
+  uint8_t* win_codes;   /* residual formats: [batch, win_max, code bytes], in/out */
+  uint8_t* win_scales;  /* residual formats: [batch, win_max, scale bytes] (FP8: unused), in/out */
   void* win_z;          /* centroids [batch, n_clusters, d], in/out */
   int32_t* win_m;       /* cluster labels [batch, win_max], in/out */
   float* proxy_logits;  /* previous proxy-attention logits [batch, K, n_heads, n_pos], in/out */
@@ -191,14 +200,15 @@ int polestar_pack_weight(const polestar_handle* h, int which, const void* src, v
  *          centroids at rows init_idx [batch, K] (i32, device), then
  *          kmeans_iters Lloyd iterations (assign by largest cosine, lowest
  *          index on ties; empty clusters keep their centroid).  Writes win_z,
- *          win_m, and win_h (RAW) or the NVFP4 residual codes (h - z_M(i)).
+ *          win_m, and win_h (RAW) or the residual codes (h - z_M(i)) in the
+ *          handle's residual format.
  *          objective (nullable, device f64 [batch, 2*kmeans_iters]) receives
  *          the objective after every assignment and every update.
- *  UPDATE: per refresh step.  Rebuilds the window rows (RAW: win_h; NVFP4:
- *          z_M(i) + dequantised residual, stored as bf16), overwrites rows
+ *  UPDATE: per refresh step.  Rebuilds the window rows (RAW: win_h; other
+ *          formats: z_M(i) + dequantised residual, stored as bf16), overwrites rows
  *          named by the packet u_in (nullable = no packet), recomputes every
  *          non-empty centroid from its members with the labels fixed (§4.1
- *          incremental centroid update), and re-quantises (NVFP4).  The
+ *          incremental centroid update), and re-quantises (residual formats).  The
  *          patched rows stay in the workspace for polestar_drift/refresh.
  */
 int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
@@ -308,6 +318,25 @@ int polestar_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t r
                           void* stream);
 /* Host evaluation of the same encoders (host pointers), for checks without a GPU. */
 int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales);
+
+/* ---- residual formats [App. C.3; Table 11 ablation] ------------------------ */
+/* Bytes per row of d values of format fmt: codes and scales (0 for RAW; FP8 has
+ * no scales).  E_DTYPE for an unknown format, E_SHAPE when d is not a positive
+ * multiple of 32. */
+int polestar_resid_bytes(int32_t fmt, int32_t d, int64_t* code_bytes, int64_t* scale_bytes);
+/* Quantise float32 rows x [rows, d] (device) in format fmt (not RAW) to codes
+ * and scales laid out as polestar_resid_bytes gives:
+ *   NVFP4  as polestar_nvfp4_pack;
+ *   FP8    code = sign | E4M3FN(|x|) (nearest even, saturating at 448; zero +0);
+ *   MXINT8 per 32 values X = 2^e, e = floor(log2 amax) (clamped to [-127, 127],
+ *          -127 for zeros), byte e + 127; q = clamp(rne(x / X * 64), -128, 127);
+ *   MXFP4  per 32 values X = 2^e, e = floor(log2 amax) - 2 (clamped likewise);
+ *          code = E2M1(x / X) (nearest even, saturating at 6). */
+int polestar_resid_pack(int32_t fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+/* Exact dequantisation of the same formats into float32 x [rows, d]. */
+int polestar_resid_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d,
+                          float* x, void* stream);
 
 #ifdef __cplusplus
 }

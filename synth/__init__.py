@@ -134,7 +134,7 @@ class Workload:
     tau_s: float = 0.9
     tau_suf: float = 0.9
     kmeans_iters: int = 10
-    resid: str = "raw"        # "raw" or "nvfp4"
+    resid: str = "raw"        # "raw", "nvfp4", "fp8", "mxint8" or "mxfp4"
     vocab: int = 0
     unmask_pmf: Tuple[float, ...] = (1.0, 1.0, 1.0, 1.0)   # over counts 1..len
     noise_var: float = 0.1

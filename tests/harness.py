@@ -169,7 +169,7 @@ class Dev:
                            n_pos=w.n_pos, batch=self.batch, block=w.block, win_prefix=w.win_prefix,
                            win_suffix=w.win_suffix, n_clusters=w.n_clusters, top_k=top_k or w.top_k,
                            vocab=self.vocab, dtype=B.BF16 if w.dtype == "bf16" else B.F32,
-                           resid_fmt=B.RESID_NVFP4 if w.resid == "nvfp4" else B.RESID_RAW)
+                           resid_fmt=B.RESID_BY_NAME[w.resid])
         self.params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist,
                                mask_id=max(self.vocab - 1, 0), kmeans_iters=w.kmeans_iters)
         self.h = B.polestar_create(self.dims, self.params)

@@ -63,7 +63,7 @@ def test_create_accepts_the_five_workload_shapes():
     (dict(head_dim=96), B.E_UNSUPPORTED),
     (dict(n_heads=6, n_kv_heads=4), B.E_SHAPE),
     (dict(dtype=7), B.E_DTYPE),
-    (dict(resid_fmt=3), B.E_DTYPE),
+    (dict(resid_fmt=9), B.E_DTYPE),
     (dict(resid_fmt=B.RESID_NVFP4), B.E_UNSUPPORTED),       # NVFP4 needs bf16 storage
     (dict(d=0), B.E_SHAPE),
     (dict(n_pos=16), B.E_SHAPE),
@@ -143,3 +143,25 @@ def test_host_nvfp4_encoder_matches_oracle():
     oc, os_ = O.nvfp4_quantize(x)
     assert np.array_equal(scales, os_)
     assert np.array_equal(codes, oc)
+
+
+def test_residual_format_sizes_and_rejections():
+    # bytes per row [App. C.3; Table 11]: nibbles + E4M3 per 16, E4M3 bytes, int8 + E8M0 per 32,
+    # nibbles + E8M0 per 32
+    assert B.polestar_resid_bytes(B.RESID_NVFP4, 4096) == (2048, 256)
+    assert B.polestar_resid_bytes(B.RESID_FP8, 4096) == (4096, 0)
+    assert B.polestar_resid_bytes(B.RESID_MXINT8, 4096) == (4096, 128)
+    assert B.polestar_resid_bytes(B.RESID_MXFP4, 3584) == (1792, 112)
+    assert B.polestar_resid_bytes(B.RESID_RAW, 256) == (0, 0)
+    lib = B.lib()
+    cb, sb = C.c_int64(), C.c_int64()
+    assert lib.polestar_resid_bytes(7, 256, C.byref(cb), C.byref(sb)) == B.E_DTYPE
+    assert lib.polestar_resid_bytes(B.RESID_FP8, 48, C.byref(cb), C.byref(sb)) == B.E_SHAPE
+    assert lib.polestar_resid_pack(B.RESID_RAW, None, 1, 32, None, None, None) == B.E_DTYPE
+    assert lib.polestar_resid_pack(B.RESID_MXFP4, None, 1, 32, None, None, None) == B.E_NULL
+    assert lib.polestar_resid_unpack(B.RESID_MXINT8, None, None, 1, 40, None, None) == B.E_SHAPE
+    # residual formats need bf16 storage; unknown formats are a dtype error
+    h = C.c_void_p()
+    for fmt in (B.RESID_FP8, B.RESID_MXINT8, B.RESID_MXFP4):
+        assert lib.polestar_create(C.byref(_dims(resid_fmt=fmt)), C.byref(_params()), C.byref(h)) == B.E_UNSUPPORTED
+    assert lib.polestar_create(C.byref(_dims(resid_fmt=9)), C.byref(_params()), C.byref(h)) == B.E_DTYPE

@@ -6,7 +6,7 @@ packet, the previous logits), runs on the GPU
   cluster(ENTRY) -> cluster(UPDATE, packet) -> drift(REFRESH) -> refresh(+ next-layer K/V)
   -> cluster(UPDATE) of layer l+1 with the new packet,
 and after every call compares against the oracle run on the identical inputs.
-Discrete outputs (labels, top-k, S, NVFP4 codes) must match exactly; floating
+Discrete outputs (labels, top-k, S, residual codes) must match exactly; floating
 point values before their storage rounding must match within 2e-3 relative.
 Where the GPU's pre-rounding value is available (check copies), its stored
 value must be exactly that value rounded once; stored values whose inputs are
@@ -55,6 +55,11 @@ CASES = {
     # 188 rows per sequence: the widest row tiling of every kernel
     "rows188_K4_k2_B64": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, n_clusters=4,
                                        top_k=2, block=64, win_prefix=96, win_suffix=24), 1, {}),
+    # residual formats of the quantisation ablation
+    "resid_fp8": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, resid="fp8"), 1, {}),
+    "resid_mxint8": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, resid="mxint8"), 1, {}),
+    "resid_mxfp4_batch2": (synth.shrink(synth.WORKLOADS[2], d=512, n_heads=4, n_kv_heads=4, ffn=1536, prompt=128,
+                                        gen=128, resid="mxfp4"), 2, {}),
 }
 
 
@@ -94,7 +99,7 @@ def test_layer_step_parity(case):
     wpos = O.window_positions(blk_start, n, Bk, w.win_prefix, w.win_suffix)
     nw, WM, K = len(wpos), dev.win_max, w.n_clusters
     keff = min(K, nw)
-    nv = w.resid == "nvfp4"
+    nv = w.resid != "raw"   # window rows stored as residual codes
     W0, W1 = weights(w, 0), weights(w, 1)
     P0 = packed_layer(dev, W0)
     wkv1 = dev.pack(B.W_KV, torch.cat([W1["wk"], W1["wv"]], 0))
@@ -113,8 +118,9 @@ def test_layer_step_parity(case):
     for b, s in enumerate(S):
         win[b, :nw] = s["H"]
         win1[b, :nw] = s["H1"]
-    codes = torch.zeros(batch, WM, d // 2, dtype=torch.uint8, device="cuda")
-    scales = torch.zeros(batch, WM, d // 16, dtype=torch.uint8, device="cuda")
+    cb, sb = B.polestar_resid_bytes(B.RESID_BY_NAME[w.resid], d) if nv else (d // 2, d // 16)
+    codes = torch.zeros(batch, WM, cb, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(batch, WM, max(sb, 1), dtype=torch.uint8, device="cuda")
     codes1, scales1 = codes.clone(), scales.clone()
     z = dev.zeros(batch, K, d)
     z1 = dev.zeros(batch, K, d)
@@ -153,10 +159,10 @@ def test_layer_step_parity(case):
         ls = {"K": np64(s["K"]), "V": np64(s["V"]), "Z": st(zo), "M": mo}
         ls1 = {"K": np64(s["K1"]), "V": np64(s["V1"]), "Z": st(zo1), "M": mo1}
         if nv:
-            ls["codes"], ls["scales"] = O.residual_quantize(Hb, ls["Z"], mo)
-            ls1["codes"], ls1["scales"] = O.residual_quantize(np64(s["H1"]), ls1["Z"], mo1)
-            assert np.array_equal(codes[b, :nw].cpu().numpy(), ls["codes"]), "entry NVFP4 codes differ"
-            assert np.array_equal(scales[b, :nw].cpu().numpy(), ls["scales"])
+            ls["codes"], ls["scales"] = O.residual_quantize(Hb, ls["Z"], mo, w.resid)
+            ls1["codes"], ls1["scales"] = O.residual_quantize(np64(s["H1"]), ls1["Z"], mo1, w.resid)
+            assert np.array_equal(codes[b, :nw].cpu().numpy(), ls["codes"]), f"entry {w.resid} codes differ"
+            assert np.array_equal(scales[b, :nw, :sb].cpu().numpy(), ls["scales"])
         else:
             ls["H"] = Hb
             ls1["H"] = np64(s["H1"])
@@ -191,7 +197,7 @@ def test_layer_step_parity(case):
         assert_stored(np64(z[b]), OL[b]["Z"], w.dtype, "updated centroids")
         if nv:
             assert np.array_equal(codes[b, :nw].cpu().numpy(), OL[b]["codes"]), "re-quantised codes differ"
-            assert np.array_equal(scales[b, :nw].cpu().numpy(), OL[b]["scales"])
+            assert np.array_equal(scales[b, :nw, :sb].cpu().numpy(), OL[b]["scales"])
         else:
             assert np.array_equal(np64(win[b, :nw]), OL[b]["H"]), "patched window rows differ"
         z[b] = to_dev(OL[b]["Z"], w.dtype)
