@@ -431,6 +431,45 @@ def residual_dequantize(packed, scales, z, m, st, fmt: str = "nvfp4") -> np.ndar
 
 
 # ---------------------------------------------------------------------------
+# KV-cache staleness and selection accuracy  [Polestar App. C.2: E_i = 1 - mean of
+# the K and V cosine similarities between cached and recomputed rows, each averaged
+# over heads; §3 / Fig. 6(a): accuracy of a policy's top-25% positions against the
+# true top-25% most stale positions]
+# ---------------------------------------------------------------------------
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Cosine similarity along the last axis; 0 where either vector is zero (reading)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    na, nb = np.linalg.norm(a, axis=-1), np.linalg.norm(b, axis=-1)
+    dot = np.sum(a * b, axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where((na > 0) & (nb > 0), dot / (na * nb), 0.0)
+
+
+def kv_staleness(k: np.ndarray, v: np.ndarray, k_ref: np.ndarray, v_ref: np.ndarray) -> np.ndarray:
+    """E_i for every position of caches [n, H, dh] against recomputed [n, H, dh]."""
+    ck = np.mean(cosine(k, k_ref), axis=-1)
+    cv = np.mean(cosine(v, v_ref), axis=-1)
+    return 1.0 - 0.5 * (ck + cv)
+
+
+def top_fraction(scores: np.ndarray, frac: float) -> np.ndarray:
+    """Indices of the ceil(frac * n) largest scores; equal scores -> lower index first."""
+    scores = np.asarray(scores, dtype=np.float64)
+    m = int(math.ceil(frac * len(scores)))
+    order = sorted(range(len(scores)), key=lambda i: (-scores[i], i))
+    return np.asarray(sorted(order[:m]), dtype=np.int64)
+
+
+def selection_accuracy(chosen, stale: np.ndarray, frac: float = 0.25) -> float:
+    """Share of the true top-frac most stale positions that a policy's choice contains."""
+    truth = set(int(i) for i in top_fraction(stale, frac))
+    return len(truth & set(int(i) for i in chosen)) / max(len(truth), 1)
+
+
+# ---------------------------------------------------------------------------
 # selection  [§4.1 top-k clusters by drift; Algorithm 1 TopK and S = M[K]]
 # ---------------------------------------------------------------------------
 

@@ -401,6 +401,35 @@ def test_mxfp4_hand_blocks_and_round_trip():
     assert np.array_equal(O.mxfp4_dequantize(p2, s2), x)
 
 
+def test_kv_staleness_special_cases_and_brute_force():
+    rng = np.random.default_rng(61)
+    n, H, dh = 7, 3, 8
+    k = rng.normal(size=(n, H, dh))
+    v = rng.normal(size=(n, H, dh))
+    assert np.allclose(O.kv_staleness(k, v, k, v), 0.0, atol=1e-15)                 # fresh cache
+    assert np.allclose(O.kv_staleness(k, v, -k, -v), 2.0)                           # opposite rows
+    assert np.allclose(O.kv_staleness(2.5 * k, v, k, 0.1 * v), 0.0, atol=1e-15)      # scale invariant
+    kr, vr = rng.normal(size=(n, H, dh)), rng.normal(size=(n, H, dh))
+    e = O.kv_staleness(k, v, kr, vr)
+    for i in range(n):   # per-head cosines written out, then the App. C.2 combination
+        ck = [float(k[i, h] @ kr[i, h]) / math.sqrt(float(k[i, h] @ k[i, h]) * float(kr[i, h] @ kr[i, h]))
+              for h in range(H)]
+        cv = [float(v[i, h] @ vr[i, h]) / math.sqrt(float(v[i, h] @ v[i, h]) * float(vr[i, h] @ vr[i, h]))
+              for h in range(H)]
+        assert abs(e[i] - (1 - 0.5 * (sum(ck) / H + sum(cv) / H))) < 1e-12
+    z = np.zeros((1, H, dh))
+    assert np.allclose(O.kv_staleness(z, z, k[:1], v[:1]), 1.0)                      # zero rows: cos 0
+
+
+def test_selection_accuracy_counts_the_true_top_quarter():
+    stale = np.array([0.1, 0.9, 0.3, 0.9, 0.0, 0.5, 0.2, 0.8])
+    assert O.top_fraction(stale, 0.25).tolist() == [1, 3]                            # ties -> lower index
+    assert O.selection_accuracy([1, 3], stale) == 1.0
+    assert O.selection_accuracy([1, 5], stale) == 0.5
+    assert O.selection_accuracy([0, 2, 4], stale) == 0.0
+    assert O.top_fraction(np.zeros(5), 0.25).tolist() == [0, 1]                      # ceil(1.25) = 2
+
+
 # ---------------------------------------------------------------- selection
 def test_topk_bruteforce_and_ties():
     for _ in range(200):
