@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpolestar.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "gemm.hip", "gemm_dl.hip", "attn.hip", "cluster.hip", "commit.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm_dl.hip", "attn.hip", "cluster.hip", "commit.hip", "staleness.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

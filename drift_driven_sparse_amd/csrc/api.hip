@@ -1112,6 +1112,23 @@ int polestar_resid_unpack(int32_t fmt, const uint8_t* codes, const uint8_t* scal
   return hip_status(launch_resid_unpack(fmt, codes, scales, rows, d, x, (hipStream_t)stream));
 }
 
+int polestar_kv_staleness(const polestar_handle* h, const void* k_cache, const void* v_cache, const void* k_ref,
+                          const void* v_ref, float* stale, void* stream) {
+  if (!h || !k_cache || !v_cache || !k_ref || !v_ref || !stale) return POLESTAR_E_NULL;
+  StaleArgs a;
+  a.batch = h->dm.batch;
+  a.n_pos = h->dm.n_pos;
+  a.hkv = h->dm.n_kv_heads;
+  a.dh = h->dm.head_dim;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_ref = k_ref;
+  a.v_ref = v_ref;
+  a.stale = stale;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_status(h->dm.dtype == POLESTAR_BF16 ? launch_kv_staleness<bf16_t>(a, s) : launch_kv_staleness<float>(a, s));
+}
+
 int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales) {
   if (!x || !codes || !scales) return POLESTAR_E_NULL;
   if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;

@@ -318,6 +318,16 @@ struct DecideArgs {
 hipError_t launch_decide(const DecideArgs& a, hipStream_t s);
 
 // ---- NVFP4 test hooks -------------------------------------------------------------
+// ---- KV-cache staleness (measurement) ----------------------------------------------
+struct StaleArgs {
+  int32_t batch, n_pos, hkv, dh;
+  const void* k; const void* v;          // caches being measured (cache layouts, storage dtype)
+  const void* k_ref; const void* v_ref;  // recomputed rows, same layouts
+  float* stale;                          // [batch][n_pos]
+};
+template <typename T>
+hipError_t launch_kv_staleness(const StaleArgs& a, hipStream_t s);
+
 hipError_t launch_resid_pack(int fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
 hipError_t launch_resid_unpack(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,

@@ -319,6 +319,16 @@ int polestar_nvfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t r
 /* Host evaluation of the same encoders (host pointers), for checks without a GPU. */
 int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales);
 
+/* ---- KV-cache staleness [App. C.2; §3 Fig. 3(a), Fig. 6(a)] ---------------- */
+/* Measurement of what the refresh is for: for every position i of every
+ * sequence, E_i = 1 - (mean_h cos(K_i,h, Kref_i,h) + mean_h cos(V_i,h, Vref_i,h))/2
+ * over the KV heads h, written to stale [batch, n_pos] (f32, device).  k_cache,
+ * v_cache are a layer's caches and k_ref, v_ref recomputed rows in the same
+ * layouts and storage dtype (device).  A zero row has cosine 0 with any row.
+ * float32 accumulation. */
+int polestar_kv_staleness(const polestar_handle* h, const void* k_cache, const void* v_cache, const void* k_ref,
+                          const void* v_ref, float* stale, void* stream);
+
 /* ---- residual formats [App. C.3; Table 11 ablation] ------------------------ */
 /* Bytes per row of d values of format fmt: codes and scales (0 for RAW; FP8 has
  * no scales).  E_DTYPE for an unknown format, E_SHAPE when d is not a positive
