@@ -320,6 +320,11 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.lg_stage = at<float>(ws, h->ws.lg);
   at_.chunk_keys = h->attn_chunk;
   at_.n_chunks = h->attn_nchunks;
+  {
+    const int tiles = PS_CEIL_DIV(at_.n_tok + at_.n_proxy, 16);
+    at_.row_groups = tiles >= 2 * h->attn_rgroups ? h->attn_rgroups : 1;
+    at_.group_tiles = PS_CEIL_DIV(tiles, at_.row_groups);
+  }
   at_.part_o = at<float>(ws, h->ws.attn_part);
   at_.part_ml = at_.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * h->mt * d.head_dim;
   at_.chk = h->chk.attn_out;
@@ -885,10 +890,12 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
     plan_projection(d.d, d.ffn, d.batch, two, 3, 16, false, &h->sh_down, &h->ks_down);
     plan_projection(2 * h->nkv, d.d, d.batch, one, 3, 16, false, &h->sh_kv, &h->ks_kv);
   }
-  // bf16 attention: split the keys so that about 256 workgroups run, at least 128 keys each
+  // bf16 attention: query rows in two groups when there are enough of them, and the keys split
+  // so that about 256 workgroups run, at least 128 keys each
   {
+    h->attn_rgroups = PS_CEIL_DIV(h->mq, 16) >= 6 ? 2 : 1;
     const int blocks32 = PS_CEIL_DIV(d.n_pos, 32);
-    int want = 256 / (d.n_heads * d.batch);
+    int want = 256 / (d.n_heads * d.batch * h->attn_rgroups);
     want = want < 1 ? 1 : want;
     const int max_chunks = PS_CEIL_DIV(d.n_pos, 128);
     want = want > max_chunks ? max_chunks : want;

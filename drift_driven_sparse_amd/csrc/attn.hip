@@ -43,9 +43,11 @@ PS_DEV int stage_row(const AttnArgs& a, int row) {   // staging buffer row: [pro
 }
 
 // ---- bf16 MFMA attention over key chunks ------------------------------------------------------
-// Workgroup = (key chunk, query head, sequence); each of its NWV waves owns one 16-row query
-// tile, and all share the chunk's K and V^T, which stream through a four-stage LDS ring in
-// 32-key steps (direct global -> LDS loads, one fragment per load instruction).
+// Workgroup = (key chunk, query head, sequence, row group); each of its NWV waves owns one
+// 16-row query tile of the group, and all share the chunk's K and V^T, which stream through a
+// four-stage LDS ring in 32-key steps (direct global -> LDS loads, one fragment per load
+// instruction).  Splitting the rows into groups lets the key chunks be longer at the same
+// workgroup count: fewer chunk states to merge, more steps to spread the prologue over.
 //
 // S^T = K Q^T per 16-key tile with the keys of the A operand permuted so that lane l ends up
 // holding the 8 consecutive keys 8(l/16)..+8 of the step for query row l%16: A row m of tile kt
@@ -87,8 +89,9 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
     else if constexpr (I == 2) return b2;
     else return b3;
   };
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z / a.row_groups, rgi = blockIdx.z % a.row_groups;
   const int n = a.n_pos, nrows = a.n_tok + a.n_proxy;
+  const int tile0 = rgi * a.group_tiles;   // this workgroup's row tiles: [tile0, tile0 + group_tiles)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int kvh = (h * a.hkv) / a.hq;
@@ -133,8 +136,8 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   bool tile_on[RTW], q_valid[RTW];
   auto load_q = [&](auto Tc) __attribute__((always_inline)) {
     constexpr int t = decltype(Tc)::value;
-    const int tile = wave * RTW + t;
-    tile_on[t] = tile * 16 < nrows;
+    const int tile = tile0 + wave * RTW + t;
+    tile_on[t] = tile * 16 < nrows && wave * RTW + t < a.group_tiles;
     const int row = tile * 16 + c16;
     q_valid[t] = row < nrows;
     const float* qr = a.q + ((int64_t)b * a.mq + (q_valid[t] ? row : 0)) * (a.hq * DH) + h * DH + 8 * g4;
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) v[e] = kg + e < k1 ? v[e] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-      const int row = (wave * RTW + t) * 16 + c16;
+      const int row = (tile0 + wave * RTW + t) * 16 + c16;
       if (row < nrows && row_keeps_logits(a, row)) {
         float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n + kg;
         if (kg + 8 <= k1) {
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   // outputs of token rows: lane holds O^T[16 dt + 4 g4 + i][row c16]
   auto store_tile = [&](auto Tc) __attribute__((always_inline)) {
     constexpr int t = decltype(Tc)::value;
-    const int row = (wave * RTW + t) * 16 + c16;
+    const int row = (tile0 + wave * RTW + t) * 16 + c16;
     if (!tile_on[t] || row >= a.n_tok) return;
     if (a.n_chunks == 1) {
       const float inv = 1.f / l_run[t];
@@ -594,10 +597,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     else return hipErrorInvalidValue;
   } else {
     const int tiles = PS_CEIL_DIV(nrows, 16);
-    const int nwv = 2 * PS_CEIL_DIV(tiles, 2);   // one wave per 16-row tile, even count
+    if (a.row_groups < 1 || a.group_tiles * a.row_groups < tiles) return hipErrorInvalidValue;
+    const int nwv = 2 * PS_CEIL_DIV(a.group_tiles, 2);   // one wave per 16-row tile, even count
     if (nwv > 12 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos)
       return hipErrorInvalidValue;
-    dim3 grid(a.n_chunks, a.hq, a.batch);
+    dim3 grid(a.n_chunks, a.hq, a.batch * a.row_groups);
     auto go = [&](auto DHc, auto NWc) {
       constexpr int NW = decltype(NWc)::value;
       hipLaunchKernelGGL((attn_chunk_kernel<decltype(DHc)::value, NW>), grid, dim3(64 * NW), 0, s, a);

@@ -23,6 +23,7 @@ struct polestar_handle {
   int32_t sh_qkv, sh_o, sh_gu, sh_down, sh_kv;   // their workgroup shapes (DlShape)
   int32_t rq, rt, rw;   // mq, mt, win_max rounded up to whole 16-row tiles (packed operands)
   int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
+  int32_t attn_rgroups;                         // bf16 attention: workgroups along the query rows
   int32_t lm_tiles;  // vocab / 64 rounded up
   WsLayout ws;
   polestar_check chk;
@@ -277,6 +278,8 @@ struct AttnArgs {
   float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
   int32_t chunk_keys;     // bf16 path: keys per workgroup (multiple of 32)
   int32_t n_chunks;       // workgroups along the keys; > 1 -> partial states merged by launch_merge_kl
+  int32_t row_groups;     // bf16 path: workgroups along the query rows, group_tiles 16-row tiles each
+  int32_t group_tiles;
   float* part_o;          // [batch][n_chunks][hq][mt][dh] unnormalised outputs of token rows
   float* part_ml;         // [batch][n_chunks][hq][mt][2] running max and sum
   int32_t act_kl;         // compute active-row KL against act_logits before overwrite
