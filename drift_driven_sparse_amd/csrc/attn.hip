@@ -441,47 +441,76 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 //   KL = (S2/S0) / (1 + S1/S0) - log1p(S1/S0)   (invariant to the shift of e).
 // The n <= 1024 logits of one (row, head) sit in registers (16 per lane, lane + 64 i), so
 // the three passes read memory once; per-lane sums run in i order, then a wavefront sum.
-constexpr int kKlPer = 16;
+constexpr int kKlPer = 4;   // logits per thread of a 256-thread workgroup (n_pos <= 1024)
 
-PS_DEV float wave_kl(const float* sv, const float* pv, int n, int lane) {
+// Block-wide max (fixed combination order); every thread gets the result.
+PS_DEV float block_max_f(float v, float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float m = -INFINITY;
+  for (int i = 0; i < nw; ++i) m = fmaxf(m, red[i]);
+  __syncthreads();
+  return m;
+}
+
+// Two block-wide sums in one exchange (fixed combination order); `red` holds two slots per wave.
+PS_DEV void block_sum2(float& x, float& y, float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  x = wave_sum(x);
+  y = wave_sum(y);
+  __syncthreads();
+  if (lane == 0) { red[2 * wid] = x; red[2 * wid + 1] = y; }
+  __syncthreads();
+  x = 0.f;
+  y = 0.f;
+  for (int i = 0; i < nw; ++i) { x += red[2 * i]; y += red[2 * i + 1]; }
+  __syncthreads();
+}
+
+// KL(softmax(s) || softmax(p)) of one row held kKlPer values per thread across the workgroup,
+// from the logit differences: with u = exp(p - max p), dbar the u-weighted mean of s - p and
+// e = s - p - dbar, KL = E_u[e^e e] / E_u[e^e] - log E_u[e^e], formed with expm1/log1p so that
+// small drifts keep their relative precision.
+PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
   float mp = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i)
-    if (lane + 64 * i < n) mp = fmaxf(mp, pv[i]);
-  mp = wave_max(mp);
+    if (threadIdx.x + 256 * i < n) mp = fmaxf(mp, pv[i]);
+  mp = block_max_f(mp, red);
   float u[kKlPer];
   float s0 = 0.f, sd = 0.f;
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i) {
-    const bool ok = lane + 64 * i < n;
+    const bool ok = threadIdx.x + 256 * i < n;
     u[i] = ok ? expf(pv[i] - mp) : 0.f;
     s0 += u[i];
     sd += ok ? u[i] * (sv[i] - pv[i]) : 0.f;
   }
-  s0 = wave_sum(s0);
-  sd = wave_sum(sd);
+  block_sum2(s0, sd, red);
   const float dbar = sd / s0;
   float s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i) {
-    if (lane + 64 * i < n) {
+    if (threadIdx.x + 256 * i < n) {
       const float e = (sv[i] - pv[i]) - dbar;
       s1 += u[i] * expm1f(e);
       s2 += u[i] * expf(e) * e;
     }
   }
-  s1 = wave_sum(s1);
-  s2 = wave_sum(s2);
+  block_sum2(s1, s2, red);
   const float r1 = s1 / s0;
   return (s2 / s0) / (1.f + r1) - log1pf(r1);
 }
 
-// One wave per (staged row, head): KL against the previous logits (when wanted),
-// then the staged logits replace them.  Staged rows: [proxies; active].
+// One 256-thread workgroup per (staged row, head): KL against the previous logits (when
+// wanted), then the staged logits replace them.  Staged rows: [proxies; active].
 PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
-  const int lane = threadIdx.x & 63;
+  __shared__ float red[8];
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
-  if (item >= nst * a.hq) return;
+  if (item >= nst * a.hq) return;   // uniform over the workgroup
   const int sr = item / a.hq, h = item % a.hq;
   const int n = a.n_pos;
   const float* s = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + sr) * a.hq + h) * n;
@@ -501,29 +530,29 @@ PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   float sv[kKlPer], pv[kKlPer];
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i) {
-    const int j = lane + 64 * i;
+    const int j = threadIdx.x + 256 * i;
     sv[i] = j < n ? s[j] : 0.f;
     pv[i] = (do_kl && j < n) ? prev[j] : 0.f;
   }
   if (do_kl) {
-    const float kl = wave_kl(sv, pv, n, lane);
-    if (lane == 0) *out = kl;
+    const float kl = block_kl(sv, pv, n, red);
+    if (threadIdx.x == 0) *out = kl;
   }
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i) {
-    const int j = lane + 64 * i;
+    const int j = threadIdx.x + 256 * i;
     if (j < n) prev[j] = sv[i];
   }
 }
 
 // One launch for the two consumers of the chunk kernel's outputs: workgroups below
-// merge_wgs merge token rows (four (row, head) pairs each), the rest form the KL items
-// (four each).  Both only read what the attention kernel wrote and write disjoint outputs.
+// merge_wgs merge token rows (four (row, head) pairs each, one per wave), the rest form one KL
+// item each.  Both only read what the attention kernel wrote and write disjoint outputs.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_merge_kl_kernel(AttnArgs a, int merge_wgs) {
   const int wave = threadIdx.x >> 6, b = blockIdx.y;
   if ((int)blockIdx.x < merge_wgs) attn_merge_pair<DH>(a, blockIdx.x * 4 + wave, b);
-  else kl_item(a, (blockIdx.x - merge_wgs) * 4 + wave, b);
+  else kl_item(a, blockIdx.x - merge_wgs, b);
 }
 
 // Per sequence: D_c = sum_h max(0, KL_{c,h}); top-k clusters by (D desc, index asc), found by
@@ -627,7 +656,8 @@ hipError_t launch_merge_kl(const AttnArgs& a, bool merge, hipStream_t s) {
   merge = merge && a.n_chunks > 1 && a.n_tok > 0;
   if (merge && a.n_chunks > 64) return hipErrorInvalidValue;
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
-  const int mw = merge ? PS_CEIL_DIV(a.n_tok * a.hq, 4) : 0, kw = PS_CEIL_DIV(nst * a.hq, 4);
+  if (a.n_pos > 256 * kKlPer) return hipErrorInvalidValue;
+  const int mw = merge ? PS_CEIL_DIV(a.n_tok * a.hq, 4) : 0, kw = nst * a.hq;
   if (mw + kw == 0) return hipSuccess;
   const dim3 grid(mw + kw, a.batch);
   if (!merge || a.dh == 128) hipLaunchKernelGGL(attn_merge_kl_kernel<128>, grid, dim3(256), 0, s, a, mw);
