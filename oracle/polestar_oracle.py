@@ -739,6 +739,38 @@ def full_forward(h0: np.ndarray, layers: List[Dict], cfg: Cfg):
     return Hs, Ks, Vs, logits
 
 
+def entry_positions(blk_start: int, n: int, B: int, pre: int, suf: int, full: bool) -> np.ndarray:
+    """Positions whose hidden rows the block-entry forward recomputes.
+
+    [§4.1 "Update Schedule": a forward of the whole sequence at every other
+    block entry; Algorithm 1 block entry.]  Reading: a full entry covers every
+    position; the other entries cover the window and the active block, the
+    positions [blk_start - pre, blk_start + B + suf) cut at the sequence ends.
+    """
+    if full:
+        return np.arange(n, dtype=np.int64)
+    return np.arange(max(0, blk_start - pre), min(n, blk_start + B + suf), dtype=np.int64)
+
+
+def layer_forward_rows(h_rows: np.ndarray, pos: np.ndarray, W: Dict, cfg: Cfg, K: np.ndarray, V: np.ndarray):
+    """One layer's forward of the hidden rows at positions ``pos``.
+
+    Their K/V replace the cache rows at ``pos`` first; every row then attends
+    to all n cache positions (bidirectional), and the residual, RMSNorm and
+    SwiGLU steps follow as in :func:`full_forward`.  Mutates K and V; returns
+    the stored output rows.
+    """
+    st, eps = cfg.st, cfg.eps
+    h = np.asarray(h_rows, dtype=np.float64)
+    q = project(h, W["wq"], eps, st).reshape(-1, cfg.hq, cfg.dh)
+    K[pos] = st(project(h, W["wk"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
+    V[pos] = st(project(h, W["wv"], eps, st)).reshape(-1, cfg.hkv, cfg.dh)
+    out, _ = attention(q, K, V, cfg.hq, cfg.hkv)
+    hp = h + out.reshape(out.shape[0], -1) @ np.asarray(W["wo"], dtype=np.float64).T
+    act = silu(project(hp, W["wg"], eps)) * project(hp, W["wu"], eps)
+    return st(hp + act @ np.asarray(W["wd"], dtype=np.float64).T)
+
+
 def block_entry_layer_state(H_in: np.ndarray, K: np.ndarray, V: np.ndarray, Wq: np.ndarray, cfg: Cfg,
                             blk_start: int, init_idx) -> Dict:
     """Cached state of one layer at block entry [§4.1 "Block entry"; Algorithm 1].

@@ -172,6 +172,71 @@ def test_full_forward_bf16_rounds_at_the_storage_points():
         assert not np.allclose(Hs[1], other, rtol=0, atol=1e-9), f"rounding of {p} has no effect"
 
 
+# ---------------------------------------------------------------- block-entry forward
+def test_entry_positions_cover_window_and_block():
+    n, B, pre, suf = 40, 4, 8, 4
+    assert np.array_equal(O.entry_positions(12, n, B, pre, suf, True), np.arange(n))
+    assert np.array_equal(O.entry_positions(12, n, B, pre, suf, False), np.arange(4, 20))
+    assert np.array_equal(O.entry_positions(0, n, B, pre, suf, False), np.arange(0, 8))      # prefix cut at 0
+    assert np.array_equal(O.entry_positions(36, n, B, pre, suf, False), np.arange(28, 40))   # suffix cut at n
+    for blk in range(0, n - B + 1, B):
+        both = np.sort(np.concatenate([O.window_positions(blk, n, B, pre, suf), O.active_positions(blk, B)]))
+        assert np.array_equal(O.entry_positions(blk, n, B, pre, suf, False), both)
+
+
+def _torch_rows_bf16(x_rows, pos, k_all, v_all, T, hq, hkv, dh):
+    """Layer rows at positions pos in float64 torch modules, bf16 casts at the storage points;
+    k_all/v_all [n, Hkv*dh] hold the other positions' keys and values."""
+    c = lambda t: t.to(torch.bfloat16).to(torch.float64)
+    r, d = x_rows.shape
+    a = c(F.rms_norm(x_rows, (d,), eps=1e-6))
+    k_all, v_all = k_all.clone(), v_all.clone()
+    k_all[pos] = c(F.linear(a, T["wk"]))
+    v_all[pos] = c(F.linear(a, T["wv"]))
+    n = k_all.shape[0]
+    q = F.linear(a, T["wq"]).view(r, hq, dh).permute(1, 0, 2)
+    k = k_all.view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    v = v_all.view(n, hkv, dh).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    o = F.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).reshape(r, hq * dh)
+    hp = x_rows + F.linear(o, T["wo"])
+    b = F.rms_norm(hp, (d,), eps=1e-6)
+    act = F.silu(F.linear(b, T["wg"])) * F.linear(b, T["wu"])
+    return c(hp + F.linear(act, T["wd"])), k_all, v_all
+
+
+@pytest.mark.parametrize("full", [True, False])
+def test_layer_forward_rows_matches_torch_modules(full):
+    # Rows of the entry set against torch modules; the other cache positions hold stale keys and
+    # values that the rows must attend to and leave untouched.
+    d, hq, hkv, dh, f, n, B, pre, suf = 32, 4, 2, 8, 48, 23, 4, 8, 4
+    cfg = O.Cfg(d=d, n_heads=hq, n_kv_heads=hkv, head_dim=dh, ffn=f, n_pos=n, block=B,
+                win_prefix=pre, win_suffix=suf, n_clusters=2, top_k=1, dtype="bf16")
+    rng = np.random.default_rng(57)
+    W = {"wq": rng.normal(size=(hq * dh, d)) / 6, "wk": rng.normal(size=(hkv * dh, d)) / 6,
+         "wv": rng.normal(size=(hkv * dh, d)) / 6, "wo": rng.normal(size=(d, hq * dh)) / 6,
+         "wg": rng.normal(size=(f, d)) / 6, "wu": rng.normal(size=(f, d)) / 6, "wd": rng.normal(size=(d, f)) / 6}
+    h = O.round_bf16(rng.normal(size=(n, d)))
+    k_old = O.round_bf16(rng.normal(size=(n, hkv, dh)))
+    v_old = O.round_bf16(rng.normal(size=(n, hkv, dh)))
+    pos = O.entry_positions(8, n, B, pre, suf, full)
+    K, V = k_old.copy(), v_old.copy()
+    got = O.layer_forward_rows(h[pos], pos, W, cfg, K, V)
+    T = {k: torch.tensor(v) for k, v in W.items()}
+    want, kw, vw = _torch_rows_bf16(torch.tensor(h[pos]), torch.tensor(pos), torch.tensor(k_old.reshape(n, -1)),
+                                    torch.tensor(v_old.reshape(n, -1)), T, hq, hkv, dh)
+    assert np.allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(K.reshape(n, -1), kw.numpy()) and np.array_equal(V.reshape(n, -1), vw.numpy())
+    rest = np.setdiff1d(np.arange(n), pos)
+    assert np.array_equal(K[rest], k_old[rest]) and np.array_equal(V[rest], v_old[rest])
+    if not full:
+        # with the stale rows replaced by the dense forward's, the window rows equal the dense rows
+        Hs, Ks, Vs, _ = O.full_forward(h, [W], cfg)
+        K2, V2 = Ks[0].copy(), Vs[0].copy()
+        K2[pos], V2[pos] = k_old[pos], v_old[pos]
+        assert np.allclose(O.layer_forward_rows(h[pos], pos, W, cfg, K2, V2), Hs[1][pos], rtol=0, atol=1e-12)
+        assert not np.allclose(got, Hs[1][pos], rtol=0, atol=1e-6)
+
+
 # ---------------------------------------------------------------- rounding
 def test_round_bf16_matches_torch_on_fp32_values():
     x = (RNG.normal(size=20000) * np.exp(RNG.uniform(-20, 20, size=20000))).astype(np.float32)
