@@ -24,6 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD specification
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD specification
 METRIC = "drift-refresh steps/s (32-layer LLaDA-8B shape) + % peak HBM GB/s, 1 GPU"
 
 
@@ -108,6 +109,36 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"forward), {t_total:.1f} s of CPU time, scaled to a {w.n_layers}-layer step"}
 
 
+def entry_flops(w, rows: int, n_layers: int) -> float:
+    """Algorithmic flops of the block-entry forward of `rows` rows: the four projections and the
+    two attention products over all n_pos keys."""
+    nq, nkv = w.n_heads * w.head_dim, w.n_kv_heads * w.head_dim
+    proj = 2.0 * rows * (w.d * (nq + 2 * nkv) + nq * w.d + 2 * w.d * w.ffn + w.ffn * w.d)
+    attn = 4.0 * rows * w.n_pos * nq
+    return n_layers * (proj + attn)
+
+
+def entry_timing(st, w, blk, h0, inits, n_layers, reps=2):
+    import torch
+    res = {}
+    for name, full in (("full", True), ("window", False)):
+        st.entry_forward(blk, h0, inits, full=full)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            st.entry_forward(blk, h0, inits, full=full)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        rows = w.n_pos if full else min(w.n_pos, blk + w.block + w.win_suffix) - max(0, blk - w.win_prefix)
+        tf = entry_flops(w, rows, n_layers) / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 3), "rows": rows, "TFLOPs": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] block entry ({name}, {rows} rows x {n_layers} layers): {ms:.2f} ms, {tf:.1f} TFLOP/s")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,18 +176,17 @@ def main():
     st = RefreshStack(dims, params, n_layers)
     blk = w.prompt
     nw = st.win_max
-    entry_rows, inits = [], []
+    inits = []
     for l in range(n_layers):
         st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
-        L = st.layers[l]
-        L["k_cache"].copy_(synth.tensor(w, (l, 10), L["k_cache"].shape, 1.0, 0, "cuda", "bf16"))
-        L["v_cache"].copy_(synth.tensor(w, (l, 11), L["v_cache"].shape, 1.0, 0, "cuda", "bf16"))
-        L["win_h"].copy_(synth.tensor(w, (l, 12), L["win_h"].shape, 1.0, 0, "cuda", "bf16"))
-        entry_rows.append(L["win_h"])
         inits.append(torch.tensor(synth.kmeans_init(w, nw, l, 0), dtype=torch.int32, device="cuda")[None])
     torch.cuda.synchronize()
     log(f"[bench] weights and state of {n_layers} layers ready in {time.time() - t0:.1f}s")
-    st.block_entry(blk, entry_rows, inits)
+    # block entry on the GPU: whole-sequence forward of every layer, window clustering, proxy logits
+    h0 = synth.embeddings(w, 0, "cuda").to(torch.bfloat16)[None].contiguous()
+    st.entry_forward(blk, h0, inits, full=True)
+    torch.cuda.synchronize()
+    log("[bench] block entry done")
     n_in = args.warmup + args.steps + 1
     inputs = synth.tensor(w, (99,), (n_in, 1, w.block, w.d), 1.0, 0, "cuda", "bf16")
     h_in = torch.zeros(1, w.block, w.d, dtype=torch.bfloat16, device="cuda")
@@ -276,6 +306,8 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    # block entry of the whole stack, both kinds, timed after the steps (it rewrites the layer state)
+    out["block_entry"] = entry_timing(st, w, blk, h0, inits, n_layers)
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe * (1 << 20) // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -20,6 +20,7 @@ RESID_BY_NAME = {"raw": RESID_RAW, "nvfp4": RESID_NVFP4, "fp8": RESID_FP8, "mxin
                  "mxfp4": RESID_MXFP4}
 CLUSTER_ENTRY, CLUSTER_UPDATE = 0, 1
 DRIFT_REFRESH, DRIFT_ACTIVE_ONLY = 0, 1
+ENTRY_FULL, ENTRY_WINDOW = 0, 1
 W_QKV, W_O, W_GU, W_DOWN, W_KV, W_LM = 0, 1, 2, 3, 4, 5
 
 EXPORTED = [
@@ -28,7 +29,7 @@ EXPORTED = [
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
     "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
-    "polestar_kv_staleness",
+    "polestar_kv_staleness", "polestar_entry",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -87,6 +88,7 @@ def lib() -> C.CDLL:
         L.polestar_weight_packed_size.argtypes = [vp, C.c_int, C.POINTER(sz)]
         L.polestar_pack_weight.argtypes = [vp, C.c_int, vp, vp, vp]
         L.polestar_cluster.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, C.POINTER(Packet), vp, vp, vp, vp, sz, vp]
+        L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
                                      C.POINTER(Packet), vp, vp, vp, sz, vp]
         L.polestar_refresh.argtypes = [vp, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp, vp, vp, vp, vp, sz, vp]
@@ -190,6 +192,12 @@ def polestar_refresh(h, layer: Layer, blk_start, h_active, sel: Packet, w_kv_nex
     _ck(lib().polestar_refresh(h, C.byref(layer), blk_start, ptr(h_active), C.byref(sel), ptr(w_kv_next),
                                ptr(k_next), ptr(v_next), ptr(h_active_out), ptr(u_rows), ptr(ws), ws_bytes,
                                stream_ptr(stream)), "polestar_refresh")
+
+
+def polestar_entry(h, mode, layer: Layer, blk_start, h_in, init_idx, h_out, objective, ws, ws_bytes,
+                   stream=None) -> None:
+    _ck(lib().polestar_entry(h, mode, C.byref(layer), blk_start, ptr(h_in), ptr(init_idx), ptr(h_out),
+                             ptr(objective), ptr(ws), ws_bytes, stream_ptr(stream)), "polestar_entry")
 
 
 def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,

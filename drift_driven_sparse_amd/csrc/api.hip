@@ -98,6 +98,10 @@ void layout(polestar_handle* h) {
   } else {
     w.lm_a = w.lm_stats = w.lm_meta = 0;
   }
+  w.q_all = take(Bt * d.n_pos * (size_t)h->nq * 4);   // block entry: queries of every position
+  w.km_lab = take(Bt * h->win_max * 4);                // block entry: k-means labels, counts, sums
+  w.km_cnt = take(Bt * d.n_clusters * 4);
+  w.km_sum = take(Bt * d.n_clusters * (size_t)d.d * 8);
   w.total = off;
 }
 
@@ -167,7 +171,7 @@ WinGeom geom_of(const polestar_handle* h, int32_t blk_start) {
 template <typename T>
 int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
                const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, double* objective,
-               void* ws, hipStream_t s) {
+               void* ws, hipStream_t s, bool entry_full = false) {
   const polestar_dims& d = h->dm;
   ClusterArgs a;
   memset(&a, 0, sizeof(a));
@@ -186,6 +190,7 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.win_z = L->win_z;
   a.win_m = L->win_m;
   a.entry_h = entry_h;
+  a.entry_full = entry_full;
   a.init_idx = init_idx;
   a.objective = objective;
   if (u_in) {
@@ -200,46 +205,28 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.wnorm = at<double>(ws, h->ws.wstat);
   a.nchunk = PS_CEIL_DIV(d.d, 256);
   a.cpart = a.wnorm + (size_t)d.batch * h->win_max;
+  a.km_lab = at<int32_t>(ws, h->ws.km_lab);
+  a.km_cnt = at<int32_t>(ws, h->ws.km_cnt);
+  a.km_sum = at<double>(ws, h->ws.km_sum);
   a.resid = d.resid_fmt;
   if (a.geom.n_win == 0) return POLESTAR_OK;
   PROF(POLESTAR_K_CLUSTER);
   return hip_status(launch_cluster<T>(a, s));
 }
 
+// round(RMSNorm(rows)) of the rows p stages, then their Q/K/V: queries to q (float32, q_rows rows
+// per sequence), K/V of rows below `block` to the cache at g.blk_start + r and of window rows
+// with a patch flag at their window positions.
 template <typename T>
-int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
-             const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
-             float* delta, void* ws, hipStream_t s) {
+int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int rows, int block, const WinGeom& g,
+            float* q, int q_rows, bool checks, void* ws, hipStream_t s) {
   const polestar_dims& d = h->dm;
-  const WinGeom g = geom_of(h, blk_start);
-  const int refresh = mode == POLESTAR_DRIFT_REFRESH && g.n_win > 0;
-  (void)u_in;
-  // 1. QKV rows
-  PrepArgs p;
-  memset(&p, 0, sizeof(p));
-  p.batch = d.batch;
-  p.d = d.d;
-  p.block = d.block;
-  p.win_max = h->win_max;
-  p.n_win = g.n_win;
-  p.K = d.n_clusters;
-  p.mq = h->mq;
-  p.refresh = refresh;
-  p.h_act = h_active;
-  p.ws_rows = at<char>(ws, h->ws.win_rows);
-  p.win_z = L->win_z;
-  p.a_qkv = at<char>(ws, h->ws.a_qkv);
-  p.a_bstride = (int64_t)h->rq * d.d;
-  p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
-  p.eps = h->pr.rms_eps;
   hipError_t e;
   {
     PROF(POLESTAR_K_PREP);
     e = launch_prep_qkv<T>(p, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 2. projections; K/V of the active block and of the packet rows go to the cache
-  const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
   GemmArgs ga;
   memset(&ga, 0, sizeof(ga));
   ga.A.base = p.a_qkv;
@@ -255,19 +242,19 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   EpiParams ep;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_QKV;
-  ep.q = at<float>(ws, h->ws.q);
-  ep.q_rows = h->mq;
+  ep.q = q;
+  ep.q_rows = q_rows;
   ep.kc = L->k_cache;
   ep.vc = L->v_cache;
   ep.flags = at<int32_t>(ws, h->ws.flags);
   ep.nq = h->nq;
   ep.nkv = h->nkv;
   ep.dh = d.head_dim;
-  ep.block = d.block;
+  ep.block = block;
   ep.win_max = h->win_max;
   ep.n_pos = d.n_pos;
   ep.geom = g;
-  ep.chk = h->chk.qkv;
+  ep.chk = checks ? h->chk.qkv : nullptr;
   ep.chk_rows = h->mq;
   ep.chk_ld = ga.N;
   if constexpr (std::is_same<T, bf16_t>::value) {
@@ -284,62 +271,107 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
     dl.part = at<float>(ws, h->ws.part);
     dl.part_rows = h->mq;
     dl.e = ep;
-    {
-      PROF(POLESTAR_K_QKV);
-      e = launch_dl<T>(dl, h->sh_qkv, rows, s);
-      if (e == hipSuccess) e = launch_dl_finish<T>(dl, rows, s);
-    }
+    PROF(POLESTAR_K_QKV);
+    e = launch_dl<T>(dl, h->sh_qkv, rows, s);
+    if (e == hipSuccess) e = launch_dl_finish<T>(dl, rows, s);
   } else {
     PROF(POLESTAR_K_QKV);
     e = launch_gemm<T>(ga, ep, rows, s);
   }
-  if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 3. attention, proxy attention and drift
-  AttnArgs at_;
-  memset(&at_, 0, sizeof(at_));
-  at_.batch = d.batch;
-  at_.n_pos = d.n_pos;
-  at_.hq = d.n_heads;
-  at_.hkv = d.n_kv_heads;
-  at_.dh = d.head_dim;
-  at_.mq = h->mq;
-  at_.mt = h->mt;
-  at_.n_tok = refresh ? d.block + g.n_win : d.block;
-  at_.n_proxy = refresh ? d.n_clusters : 0;
-  at_.block = d.block;
-  at_.q = ep.q;
-  at_.kc = L->k_cache;
-  at_.vc = L->v_cache;
-  at_.o = at<char>(ws, h->ws.o);
-  at_.o_planes = std::is_same<T, bf16_t>::value;
-  at_.proxy_logits = L->proxy_logits;
-  at_.kl = at<float>(ws, h->ws.kl);
-  at_.act_logits = act_logits;
-  at_.act_kl = delta != nullptr;
-  at_.akl = at<float>(ws, h->ws.akl);
-  at_.lg_stage = at<float>(ws, h->ws.lg);
-  at_.chunk_keys = h->attn_chunk;
-  at_.n_chunks = h->attn_nchunks;
-  {
-    const int tiles = PS_CEIL_DIV(at_.n_tok + at_.n_proxy, 16);
-    at_.row_groups = tiles >= 2 * h->attn_rgroups ? h->attn_rgroups : 1;
-    at_.group_tiles = PS_CEIL_DIV(tiles, at_.row_groups);
-  }
-  at_.part_o = at<float>(ws, h->ws.attn_part);
-  at_.part_ml = at_.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * h->mt * d.head_dim;
-  at_.chk = h->chk.attn_out;
-  at_.chk_rows = h->mt;
+  return hip_status(e);
+}
+
+// Attention arguments shared by every call: the layer's cache and the workspace buffers.  The
+// caller sets the query rows (q, mq, n_tok, n_proxy, block) and the logit outputs.
+template <typename T>
+AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws) {
+  const polestar_dims& d = h->dm;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = d.batch;
+  a.n_pos = d.n_pos;
+  a.hq = d.n_heads;
+  a.hkv = d.n_kv_heads;
+  a.dh = d.head_dim;
+  a.mq = h->mq;
+  a.mt = h->mt;
+  a.block = d.block;
+  a.kc = L->k_cache;
+  a.vc = L->v_cache;
+  a.o = at<char>(ws, h->ws.o);
+  a.o_planes = std::is_same<T, bf16_t>::value;
+  a.kl = at<float>(ws, h->ws.kl);
+  a.akl = at<float>(ws, h->ws.akl);
+  a.lg_stage = at<float>(ws, h->ws.lg);
+  a.chunk_keys = h->attn_chunk;
+  a.n_chunks = h->attn_nchunks;
+  a.part_o = at<float>(ws, h->ws.attn_part);
+  a.part_ml = a.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * h->mt * d.head_dim;
+  a.chk_rows = h->mt;
+  return a;
+}
+
+// Attention of the query rows over all n_pos keys, then the merge of the key chunks and the KL
+// drift of the kept logit rows.
+template <typename T>
+int run_attention(polestar_handle* h, AttnArgs& a, hipStream_t s) {
+  const int tiles = PS_CEIL_DIV(a.n_tok + a.n_proxy, 16);
+  a.row_groups = tiles >= 2 * h->attn_rgroups ? h->attn_rgroups : 1;
+  a.group_tiles = PS_CEIL_DIV(tiles, a.row_groups);
+  hipError_t e;
   {
     PROF(POLESTAR_K_ATTN);
-    e = launch_attention<T>(at_, s);
+    e = launch_attention<T>(a, s);
   }
   if (e != hipSuccess) return POLESTAR_E_HIP;
-  {
-    PROF(POLESTAR_K_KL);   // chunk merge and KL drift
-    e = launch_merge_kl(at_, std::is_same<T, bf16_t>::value, s);
-  }
-  if (e != hipSuccess) return POLESTAR_E_HIP;
-  // 4. top-k clusters and the selected rows
+  PROF(POLESTAR_K_KL);   // chunk merge and KL drift
+  return hip_status(launch_merge_kl(a, std::is_same<T, bf16_t>::value, s));
+}
+
+template <typename T>
+int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
+             const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
+             float* delta, void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const int refresh = mode == POLESTAR_DRIFT_REFRESH && g.n_win > 0;
+  (void)u_in;
+  // 1. QKV rows [active; window; centroids]; K/V of the active block and of the packet rows go
+  //    to the cache
+  PrepArgs p;
+  memset(&p, 0, sizeof(p));
+  p.batch = d.batch;
+  p.d = d.d;
+  p.block = d.block;
+  p.win_max = h->win_max;
+  p.n_win = g.n_win;
+  p.K = d.n_clusters;
+  p.mq = h->mq;
+  p.refresh = refresh;
+  p.h_act = h_active;
+  p.act_bstride = (int64_t)d.block * d.d;
+  p.ws_rows = at<char>(ws, h->ws.win_rows);
+  p.win_z = L->win_z;
+  p.a_qkv = at<char>(ws, h->ws.a_qkv);
+  p.a_bstride = (int64_t)h->rq * d.d;
+  p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
+  p.eps = h->pr.rms_eps;
+  const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
+  float* q = at<float>(ws, h->ws.q);
+  int rc = run_qkv<T>(h, L, p, rows, d.block, g, q, h->mq, true, ws, s);
+  if (rc) return rc;
+  // 2. attention, proxy attention and drift
+  AttnArgs at_ = attn_base<T>(h, L, ws);
+  at_.n_tok = refresh ? d.block + g.n_win : d.block;
+  at_.n_proxy = refresh ? d.n_clusters : 0;
+  at_.q = q;
+  at_.proxy_logits = L->proxy_logits;
+  at_.proxy_kl = 1;
+  at_.act_logits = act_logits;
+  at_.act_kl = delta != nullptr;
+  at_.chk = h->chk.attn_out;
+  if ((rc = run_attention<T>(h, at_, s))) return rc;
+  // 3. top-k clusters and the selected rows
   TopkArgs tk;
   memset(&tk, 0, sizeof(tk));
   tk.batch = d.batch;
@@ -362,16 +394,38 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   return hip_status(launch_topk(tk, s));
 }
 
+// Token rows of the second half of a layer (O projection, residual, RMSNorm, SwiGLU FFN): n_act
+// contiguous rows, read from h_act and written to h_out (the active block, or a slab of
+// block-entry rows, whose attention output sits in rows [0, n_act) of the workspace), and with
+// sel the selected window rows (attention output rows block + w, residual rows from the
+// workspace window rows, outputs to u_rows).
+struct TokRows {
+  int32_t n_act;
+  const void* h_act; int64_t act_bstride;   // elements between sequences
+  void* h_out; int64_t out_bstride;
+  const polestar_packet* sel;               // null: no window rows
+  void* u_rows;
+  bool checks;                              // fill the check buffers (per-step calls)
+};
+
+// Row count of a projection over [n_act rows; selected window rows].
+void set_rows(GemmA& A, const TokRows& t, int max_rows) {
+  A.rows_dev = t.sel ? t.sel->count : nullptr;
+  A.rows_add = t.n_act;
+  A.rows_static = t.n_act;
+  A.rows_max = max_rows;
+}
+
 // bf16 storage: projections by the weight-streaming kernel; the float32 values inside the call
 // (attention output, RMSNorm(h'), SwiGLU product) travel as bf16 hi/lo planes.
-int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
-                  const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
-                  void* u_rows, void* ws, hipStream_t s) {
+int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const TokRows& t,
+                  const void* w_kv_next, void* k_next, void* v_next, void* ws, hipStream_t s) {
   typedef bf16_t T;
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
-  const int max_rows = d.block + g.n_win;
-  const bool kv_next = w_kv_next && g.n_win > 0;
+  const polestar_packet* sel = t.sel;
+  const int max_rows = t.n_act + (sel ? g.n_win : 0);
+  const bool kv_next = w_kv_next && sel && g.n_win > 0;
   float* part = at<float>(ws, h->ws.part);
   hipError_t e;
   // 1. h' = h + o W_O^T over rows [active; S]
@@ -381,13 +435,11 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.A.plane_stride = (int64_t)h->mt * h->nq;
   dl.A.bstride = 2 * dl.A.plane_stride;
   dl.A.lda = h->nq;
-  dl.A.rowmap = sel->idx;
+  dl.A.rowmap = sel ? sel->idx : nullptr;
   dl.A.map_bstride = h->win_max;
-  dl.A.map_from = d.block;
+  dl.A.map_from = t.n_act;
   dl.A.map_off = d.block;
-  dl.A.rows_dev = sel->count;
-  dl.A.rows_add = d.block;
-  dl.A.rows_max = max_rows;
+  set_rows(dl.A, t, max_rows);
   dl.planes = 2;
   dl.wg = weight_group(h, POLESTAR_W_O);
   dl.W = L->w_o;
@@ -410,15 +462,15 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.part_rows = h->mt;
   rr.batch = d.batch;
   rr.d = d.d;
-  rr.count = sel->count;
-  rr.block = d.block;
+  rr.count = sel ? sel->count : nullptr;
+  rr.block = t.n_act;
   rr.win_max = h->win_max;
-  rr.res_a = h_active;
-  rr.res_a_bstride = (int64_t)d.block * d.d;
-  rr.res_split = d.block;
+  rr.res_a = t.h_act;
+  rr.res_a_bstride = t.act_bstride;
+  rr.res_split = t.n_act;
   rr.res_b = at<char>(ws, h->ws.win_rows);
   rr.res_b_bstride = (int64_t)h->win_max * d.d;
-  rr.sel_idx = sel->idx;
+  rr.sel_idx = sel ? sel->idx : nullptr;
   rr.out_a = at<char>(ws, h->ws.hp);
   rr.out_a_bstride = (int64_t)h->mt * d.d;
   rr.out_split = h->mt;
@@ -429,7 +481,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.norm_bstride = 2 * (int64_t)h->rt * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
-  rr.chk = h->chk.hp;
+  rr.chk = t.checks ? h->chk.hp : nullptr;
   rr.chk_rows = h->mt;
   {
     PROF(POLESTAR_K_OREDUCE);
@@ -442,9 +494,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.A.tiles = rr.norm_tiles;
   dl.A.bstride = rr.norm_bstride;
   dl.A.lda = d.d;
-  dl.A.rows_dev = sel->count;
-  dl.A.rows_add = d.block;
-  dl.A.rows_max = max_rows;
+  set_rows(dl.A, t, max_rows);
   dl.planes = 2;
   dl.wg = weight_group(h, POLESTAR_W_GU);
   dl.W = L->w_gu;
@@ -471,9 +521,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.A.tiles = h->rt / 16;
   dl.A.bstride = 2 * (int64_t)h->rt * d.ffn;
   dl.A.lda = d.ffn;
-  dl.A.rows_dev = sel->count;
-  dl.A.rows_add = d.block;
-  dl.A.rows_max = max_rows;
+  set_rows(dl.A, t, max_rows);
   dl.planes = 2;
   dl.wg = weight_group(h, POLESTAR_W_DOWN);
   dl.W = L->w_down;
@@ -497,18 +545,18 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   r2.res_a_bstride = (int64_t)h->mt * d.d;
   r2.res_split = h->mt;
   r2.res_b = nullptr;
-  r2.out_a = h_active_out;
-  r2.out_a_bstride = (int64_t)d.block * d.d;
-  r2.out_split = d.block;
-  r2.out_b = u_rows;
+  r2.out_a = t.h_out;
+  r2.out_a_bstride = t.out_bstride;
+  r2.out_split = t.n_act;
+  r2.out_b = t.u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
   r2.out_f32 = 0;
   r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only, rounded
   r2.norm_planes = 0;
   r2.norm_tiles = h->rw / 16;
   r2.norm_bstride = (int64_t)h->rw * d.d;
-  r2.norm_from = d.block;
-  r2.chk = h->chk.out;
+  r2.norm_from = t.n_act;
+  r2.chk = t.checks ? h->chk.out : nullptr;
   {
     PROF(POLESTAR_K_DREDUCE);
     e = launch_row_reduce<T>(r2, max_rows, s);
@@ -553,15 +601,15 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
 }
 
 template <typename T>
-int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
-               const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next, void* h_active_out,
-               void* u_rows, void* ws, hipStream_t s) {
+int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const TokRows& t,
+               const void* w_kv_next, void* k_next, void* v_next, void* ws, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value)
-    return do_refresh_dl(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s);
+    return do_refresh_dl(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s);
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
-  const int max_rows = d.block + g.n_win;
-  const bool kv_next = w_kv_next && g.n_win > 0;
+  const polestar_packet* sel = t.sel;
+  const int max_rows = t.n_act + (sel ? g.n_win : 0);
+  const bool kv_next = w_kv_next && sel && g.n_win > 0;
   float* part = at<float>(ws, h->ws.part);
   // 1. h' = h + o W_O^T over rows [active; S]
   GemmArgs ga;
@@ -569,13 +617,11 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.A.base = at<char>(ws, h->ws.o);
   ga.A.bstride = (int64_t)h->mt * h->nq;
   ga.A.lda = h->nq;
-  ga.A.rowmap = sel->idx;
+  ga.A.rowmap = sel ? sel->idx : nullptr;
   ga.A.map_bstride = h->win_max;
-  ga.A.map_from = d.block;
+  ga.A.map_from = t.n_act;
   ga.A.map_off = d.block;
-  ga.A.rows_dev = sel->count;
-  ga.A.rows_add = d.block;
-  ga.A.rows_max = max_rows;
+  set_rows(ga.A, t, max_rows);
   ga.W = L->w_o;
   ga.N = d.d;
   ga.K = h->nq;
@@ -599,15 +645,15 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.part_rows = h->mt;
   rr.batch = d.batch;
   rr.d = d.d;
-  rr.count = sel->count;
-  rr.block = d.block;
+  rr.count = sel ? sel->count : nullptr;
+  rr.block = t.n_act;
   rr.win_max = h->win_max;
-  rr.res_a = h_active;
-  rr.res_a_bstride = (int64_t)d.block * d.d;
-  rr.res_split = d.block;
+  rr.res_a = t.h_act;
+  rr.res_a_bstride = t.act_bstride;
+  rr.res_split = t.n_act;
   rr.res_b = at<char>(ws, h->ws.win_rows);
   rr.res_b_bstride = (int64_t)h->win_max * d.d;
-  rr.sel_idx = sel->idx;
+  rr.sel_idx = sel ? sel->idx : nullptr;
   rr.out_a = at<char>(ws, h->ws.hp);
   rr.out_a_bstride = (int64_t)h->mt * d.d;
   rr.out_split = h->mt;
@@ -616,7 +662,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.norm_bstride = (int64_t)h->rt * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
-  rr.chk = h->chk.hp;
+  rr.chk = t.checks ? h->chk.hp : nullptr;
   rr.chk_rows = h->mt;
   {
     PROF(POLESTAR_K_OREDUCE);
@@ -628,9 +674,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.A.base = rr.norm;
   ga.A.bstride = rr.norm_bstride;
   ga.A.lda = d.d;
-  ga.A.rows_dev = sel->count;
-  ga.A.rows_add = d.block;
-  ga.A.rows_max = max_rows;
+  set_rows(ga.A, t, max_rows);
   ga.W = L->w_gu;
   ga.N = 2 * d.ffn;
   ga.K = d.d;
@@ -651,9 +695,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.A.base = ep.act;
   ga.A.bstride = (int64_t)h->rt * d.ffn;
   ga.A.lda = d.ffn;
-  ga.A.rows_dev = sel->count;
-  ga.A.rows_add = d.block;
-  ga.A.rows_max = max_rows;
+  set_rows(ga.A, t, max_rows);
   ga.W = L->w_down;
   ga.N = d.d;
   ga.K = d.ffn;
@@ -674,16 +716,16 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   r2.res_a_bstride = (int64_t)h->mt * d.d;
   r2.res_split = h->mt;
   r2.res_b = nullptr;
-  r2.out_a = h_active_out;
-  r2.out_a_bstride = (int64_t)d.block * d.d;
-  r2.out_split = d.block;
-  r2.out_b = u_rows;
+  r2.out_a = t.h_out;
+  r2.out_a_bstride = t.out_bstride;
+  r2.out_split = t.n_act;
+  r2.out_b = t.u_rows;
   r2.out_b_bstride = (int64_t)h->win_max * d.d;
   r2.out_f32 = 0;
   r2.norm = kv_next ? at<char>(ws, h->ws.a_kv) : nullptr;   // packet rows only
   r2.norm_bstride = (int64_t)h->rw * d.d;
-  r2.norm_from = d.block;
-  r2.chk = h->chk.out;
+  r2.norm_from = t.n_act;
+  r2.chk = t.checks ? h->chk.out : nullptr;
   {
     PROF(POLESTAR_K_DREDUCE);
     e = launch_row_reduce<T>(r2, max_rows, s);
@@ -720,6 +762,78 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
     if (e != hipSuccess) return POLESTAR_E_HIP;
   }
   return POLESTAR_OK;
+}
+
+// Block entry of one layer: the forward of the rows at positions [r0, r1) (every position, or the
+// window and the active block) with attention over the whole cache, the k-means of the window
+// rows of h_in, and the centroids' proxy logits over the fresh cache.  The rows are taken in
+// slabs of the workspace's token-row capacity: first the Q/K/V of every slab (the cache must be
+// complete before any row attends), then attention and the rest of the layer slab by slab.
+template <typename T>
+int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
+             const int32_t* init_idx, void* h_out, double* objective, void* ws, hipStream_t s) {
+  const polestar_dims& d = h->dm;
+  const WinGeom g = geom_of(h, blk_start);
+  const bool full = mode == POLESTAR_ENTRY_FULL;
+  const int r0 = full ? 0 : blk_start - g.n_pre;
+  const int r1 = full ? d.n_pos : blk_start + d.block + (g.n_win - g.n_pre);
+  const int slab = h->mt;
+  const int64_t hb = (int64_t)d.n_pos * d.d;   // elements between sequences of h_in, h_out
+  const T* hin = (const T*)h_in;
+  T* hout = (T*)h_out;
+  float* q_all = at<float>(ws, h->ws.q_all);
+  // 1. window clustering of the entry rows
+  int rc = do_cluster<T>(h, POLESTAR_CLUSTER_ENTRY, L, blk_start, nullptr, init_idx, h_in, objective, ws, s, true);
+  if (rc) return rc;
+  // 2. Q/K/V of every recomputed row
+  PrepArgs p;
+  memset(&p, 0, sizeof(p));
+  p.batch = d.batch;
+  p.d = d.d;
+  p.win_max = h->win_max;
+  p.K = d.n_clusters;
+  p.mq = h->mq;
+  p.act_bstride = hb;
+  p.win_z = L->win_z;
+  p.a_qkv = at<char>(ws, h->ws.a_qkv);
+  p.a_bstride = (int64_t)h->rq * d.d;
+  p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
+  p.eps = h->pr.rms_eps;
+  for (int p0 = r0; p0 < r1; p0 += slab) {
+    const int rows = std::min(slab, r1 - p0);
+    p.block = rows;
+    p.h_act = hin + (int64_t)p0 * d.d;
+    const WinGeom gs = make_geom(p0, d.n_pos, rows, 0, 0);
+    if ((rc = run_qkv<T>(h, L, p, rows, rows, gs, q_all + (int64_t)p0 * h->nq, d.n_pos, false, ws, s))) return rc;
+  }
+  // 3. attention over all positions, O projection, SwiGLU FFN
+  for (int p0 = r0; p0 < r1; p0 += slab) {
+    const int rows = std::min(slab, r1 - p0);
+    AttnArgs a = attn_base<T>(h, L, ws);
+    a.q = q_all + (int64_t)p0 * h->nq;
+    a.mq = d.n_pos;
+    a.n_tok = rows;
+    a.block = rows;
+    if ((rc = run_attention<T>(h, a, s))) return rc;
+    const TokRows t = {rows, hin + (int64_t)p0 * d.d, hb, hout + (int64_t)p0 * d.d, hb, nullptr, nullptr, false};
+    if ((rc = do_refresh<T>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s))) return rc;
+  }
+  // 4. proxy logits of the centroids: the first drift reference
+  p.block = 0;
+  p.n_win = 0;
+  p.refresh = 1;
+  p.h_act = nullptr;
+  const WinGeom g0 = make_geom(0, d.n_pos, 0, 0, 0);
+  float* q = at<float>(ws, h->ws.q);
+  if ((rc = run_qkv<T>(h, L, p, d.n_clusters, 0, g0, q, h->mq, false, ws, s))) return rc;
+  AttnArgs a = attn_base<T>(h, L, ws);
+  a.q = q;
+  a.n_tok = 0;
+  a.n_proxy = d.n_clusters;
+  a.block = 0;
+  a.proxy_logits = L->proxy_logits;
+  a.proxy_kl = 0;
+  return run_attention<T>(h, a, s);
 }
 
 template <typename T>
@@ -1046,9 +1160,35 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
       !aligned16(h_active_out) || !aligned16(u_rows) || (w_kv_next && !aligned16(w_kv_next)))
     return POLESTAR_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
+  const int64_t bs = (int64_t)h->dm.block * h->dm.d;
+  const TokRows t = {h->dm.block, h_active, bs, h_active_out, bs, sel, u_rows, true};
+  return h->dm.dtype == POLESTAR_BF16 ? do_refresh<bf16_t>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s)
+                                      : do_refresh<float>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s);
+}
+
+int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
+                   const int32_t* init_idx, void* h_out, double* objective, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !L || !h_in || !init_idx || !h_out) return POLESTAR_E_NULL;
+  if (mode != POLESTAR_ENTRY_FULL && mode != POLESTAR_ENTRY_WINDOW) return POLESTAR_E_ARG;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  const bool nv = h->dm.resid_fmt != POLESTAR_RESID_RAW;
+  if (!L->w_qkv || !L->w_o || !L->w_gu || !L->w_down || !L->k_cache || !L->v_cache || !L->win_z || !L->win_m ||
+      !L->proxy_logits)
+    return POLESTAR_E_NULL;
+  if (nv ? (!L->win_codes || (resid_scale_bytes(h->dm.resid_fmt, h->dm.d) > 0 && !L->win_scales)) : !L->win_h)
+    return POLESTAR_E_NULL;
+  if (!aligned16(L->w_qkv) || !aligned16(L->w_o) || !aligned16(L->w_gu) || !aligned16(L->w_down) ||
+      !aligned16(L->win_z) || (!nv && !aligned16(L->win_h)) || !aligned16(h_in) || !aligned16(h_out))
+    return POLESTAR_E_ALIGN;
+  const size_t bytes = (size_t)h->dm.batch * h->dm.n_pos * h->dm.d * elt(h);
+  const char *a0 = (const char*)h_in, *b0 = (const char*)h_out;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return POLESTAR_E_ARG;   // h_out must not overlap h_in
+  hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
-             ? do_refresh<bf16_t>(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s)
-             : do_refresh<float>(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws, s);
+             ? do_entry<bf16_t>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, ws, s)
+             : do_entry<float>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, ws, s);
 }
 
 int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,

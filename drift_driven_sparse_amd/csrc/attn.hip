@@ -520,7 +520,7 @@ PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   if (sr < a.n_proxy) {
     prev = a.proxy_logits + (((int64_t)b * a.n_proxy + sr) * a.hq + h) * n;
     out = a.kl + ((int64_t)b * a.n_proxy + sr) * a.hq + h;
-    do_kl = true;
+    do_kl = a.proxy_kl != 0;
   } else {
     const int r = sr - a.n_proxy;
     prev = a.act_logits + (((int64_t)b * a.block + r) * a.hq + h) * n;

@@ -10,110 +10,176 @@ namespace {
 // Row reduction in float64 over a whole workgroup (fixed order).
 PS_DEV double block_sum_d(double v, double* red) { return block_sum<double>(v, red); }
 
-// ---- block entry: spherical k-means ---------------------------------------------------
-// One workgroup per sequence.  xhat/z64/s64 are float64 workspace rows.
-template <typename T>
-__global__ __launch_bounds__(1024) void kmeans_entry_kernel(ClusterArgs a, double* s64) {
-  __shared__ double red[16];
-  __shared__ int lab[256];
-  __shared__ double best[256];
-  __shared__ double snorm_sh;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int d = a.d, nwin = a.geom.n_win, K = a.K;
-  const int keff = min(K, nwin);
-  const T* src = (const T*)a.entry_h + (int64_t)b * a.win_max * d;
-  double* xh = a.xhat + (int64_t)b * a.win_max * d;
-  double* z = a.z64 + (int64_t)b * K * d;
-  double* sb = s64 + (int64_t)b * d;
+// ---- block entry: spherical k-means, spread over the chip ------------------------------------
+// Lloyd iterations in float64 as a chain of small launches: unit rows (one workgroup per window
+// row), then per iteration assign (one workgroup per row), update (one workgroup per 256-column
+// chunk and cluster: member sums and the chunk's sum of squares) and finish (same grid: the norm
+// of the whole sum from the chunk partials in chunk order, then the new centroid columns); last,
+// labels and rounded centroids, and the residual codes of each row.  Every sum runs in a fixed
+// order, so the labels do not depend on scheduling.
 
-  // unit rows (a zero row stays zero); raw storage copies the rows into the window
-  for (int w = 0; w < nwin; ++w) {
-    double ss = 0.0;
-    for (int n = tid; n < d; n += blockDim.x) {
-      const double x = St<T>::load(src, (int64_t)w * d + n);
-      ss += x * x;
-    }
-    ss = block_sum_d(ss, red);
-    const double nr = sqrt(ss);
-    for (int n = tid; n < d; n += blockDim.x) {
-      const float x = St<T>::load(src, (int64_t)w * d + n);
-      xh[(int64_t)w * d + n] = nr > 0.0 ? (double)x / nr : 0.0;
-      if (!a.resid && a.win_h != a.entry_h)
-        ((T*)a.win_h)[((int64_t)b * a.win_max + w) * d + n] = ((const T*)src)[(int64_t)w * d + n];
-    }
+// Window row w of sequence b in the entry rows: row w of a window block, or the row at its
+// position among all positions.
+template <typename T>
+PS_DEV const T* entry_row(const ClusterArgs& a, int b, int w) {
+  const int64_t rows = a.entry_full ? a.n_pos : a.win_max;
+  const int64_t r = a.entry_full ? a.geom.pos(w) : w;
+  return (const T*)a.entry_h + ((int64_t)b * rows + r) * a.d;
+}
+
+// Unit row (a zero row stays zero); raw storage copies the row into the window; the workgroup of
+// the row named by init_idx[c] seeds centroid c (row 0's workgroup zeroes the clusters with no
+// valid seed).
+template <typename T>
+__global__ __launch_bounds__(256) void km_unit_kernel(ClusterArgs a) {
+  __shared__ double red[4];
+  const int w = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K, nwin = a.geom.n_win;
+  const int keff = min(K, nwin);
+  const T* src = entry_row<T>(a, b, w);
+  double ss = 0.0;
+  for (int n = threadIdx.x; n < d; n += blockDim.x) {
+    const double x = St<T>::load(src, n);
+    ss += x * x;
   }
-  __syncthreads();
+  ss = block_sum_d(ss, red);
+  const double nr = sqrt(ss);
+  double* xh = a.xhat + ((int64_t)b * a.win_max + w) * d;
+  const bool copy = !a.resid && (a.entry_full || a.win_h != a.entry_h);
+  T* wrow = (T*)a.win_h + ((int64_t)b * a.win_max + w) * d;
+  for (int n = threadIdx.x; n < d; n += blockDim.x) {
+    const float x = St<T>::load(src, n);
+    xh[n] = nr > 0.0 ? (double)x / nr : 0.0;
+    if (copy) wrow[n] = src[n];
+  }
+  double* z = a.z64 + (int64_t)b * K * d;
   for (int c = 0; c < K; ++c) {
     int r = c < keff ? a.init_idx[(int64_t)b * K + c] : -1;
     if (r < 0 || r >= nwin) r = -1;
-    for (int n = tid; n < d; n += blockDim.x) z[(int64_t)c * d + n] = (c < keff && r >= 0) ? xh[(int64_t)r * d + n] : 0.0;
+    if (r == w || (r < 0 && w == 0))
+      for (int n = threadIdx.x; n < d; n += blockDim.x) z[(int64_t)c * d + n] = r >= 0 ? xh[n] : 0.0;
   }
-  __syncthreads();
-  for (int it = 0; it < a.iters; ++it) {
-    // assignment: largest cosine, lowest index on ties
-    for (int w = wave; w < nwin; w += nw) {
-      int bc = 0;
-      double bv = -INFINITY;
-      for (int c = 0; c < keff; ++c) {
-        double t = 0.0;
-        for (int n = lane; n < d; n += 64) t += xh[(int64_t)w * d + n] * z[(int64_t)c * d + n];
-        t = wave_sum(t);
-        if (t > bv) { bv = t; bc = c; }
-      }
-      if (lane == 0) { lab[w] = bc; best[w] = bv; }
+}
+
+// Largest cosine over the first keff centroids, lowest index on ties.
+constexpr int kKmMax = 16;   // clusters per sequence (the handle's limit)
+__global__ __launch_bounds__(256) void km_assign_kernel(ClusterArgs a) {
+  __shared__ double red[4][kKmMax];
+  const int w = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K;
+  const int keff = min(K, a.geom.n_win);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double* xh = a.xhat + ((int64_t)b * a.win_max + w) * d;
+  const double* z = a.z64 + (int64_t)b * K * d;
+  double t[kKmMax];
+#pragma unroll
+  for (int c = 0; c < kKmMax; ++c) t[c] = 0.0;
+  for (int n = threadIdx.x; n < d; n += blockDim.x) {
+    const double x = xh[n];
+#pragma unroll
+    for (int c = 0; c < kKmMax; ++c)
+      if (c < keff) t[c] += x * z[(int64_t)c * d + n];
+  }
+#pragma unroll
+  for (int c = 0; c < kKmMax; ++c)
+    if (c < keff) {
+      const double v = wave_sum(t[c]);
+      if (lane == 0) red[wave][c] = v;
     }
-    __syncthreads();
-    if (tid == 0 && a.objective) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int bc = 0;
+    double bv = -INFINITY;
+    for (int c = 0; c < keff; ++c) {
+      const double v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+      if (v > bv) {
+        bv = v;
+        bc = c;
+      }
+    }
+    a.km_lab[(int64_t)b * a.win_max + w] = bc;
+    a.wnorm[(int64_t)b * a.win_max + w] = bv;   // best cosine of the row
+  }
+}
+
+// Member sum of cluster c over one 256-column chunk, and the chunk's sum of squares.  The first
+// workgroup of a sequence also records the objective after the assignment.
+__global__ __launch_bounds__(256) void km_update_kernel(ClusterArgs a, int it) {
+  __shared__ int lab[256];
+  __shared__ double red[4];
+  const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, d = a.d, K = a.K, nwin = a.geom.n_win;
+  for (int w = threadIdx.x; w < nwin; w += blockDim.x) lab[w] = a.km_lab[(int64_t)b * a.win_max + w];
+  __syncthreads();
+  int cnt = 0;
+  for (int w = 0; w < nwin; ++w) cnt += lab[w] == c;
+  if (threadIdx.x == 0 && ch == 0) {
+    a.km_cnt[(int64_t)b * K + c] = cnt;
+    if (c == 0 && a.objective) {
       double J = 0.0;
-      for (int w = 0; w < nwin; ++w) J += best[w];
+      for (int w = 0; w < nwin; ++w) J += a.wnorm[(int64_t)b * a.win_max + w];
       a.objective[(int64_t)b * 2 * a.iters + 2 * it] = J;
     }
-    // update: normalised member sum; empty clusters (or a zero sum) keep their centroid
-    double Jup = 0.0;
-    for (int c = 0; c < keff; ++c) {
-      int cnt = 0;
-      for (int w = 0; w < nwin; ++w) cnt += lab[w] == c;
-      if (cnt == 0) continue;
-      double ss = 0.0;
-      for (int n = tid; n < d; n += blockDim.x) {
-        double s = 0.0;
-        for (int w = 0; w < nwin; ++w)
-          if (lab[w] == c) s += xh[(int64_t)w * d + n];
-        sb[n] = s;
-        ss += s * s;
-      }
-      ss = block_sum_d(ss, red);
-      const double ns = sqrt(ss);
-      if (tid == 0) snorm_sh = ns;
-      Jup += ns;
-      if (ns > 0.0)
-        for (int n = tid; n < d; n += blockDim.x) z[(int64_t)c * d + n] = sb[n] / ns;
-      __syncthreads();
-    }
-    if (tid == 0 && a.objective) a.objective[(int64_t)b * 2 * a.iters + 2 * it + 1] = Jup;
-    __syncthreads();
   }
-  // outputs: labels, centroids (rounded once), NVFP4 residual codes
-  for (int w = tid; w < a.win_max; w += blockDim.x)
-    a.win_m[(int64_t)b * a.win_max + w] = w < nwin ? (a.iters > 0 ? lab[w] : 0) : 0;
-  for (int i = tid; i < K * d; i += blockDim.x)
-    St<T>::store_d((T*)a.win_z + (int64_t)b * K * d, i, z[i]);
-  __syncthreads();
-  if (a.resid) {
-    const int G = resid_group(a.resid), ng = d / G;
-    const int64_t cb = resid_code_bytes(a.resid, d), sb = resid_scale_bytes(a.resid, d);
-    for (int i = tid; i < nwin * ng; i += blockDim.x) {
-      const int w = i / ng, g0 = (i % ng) * G;
-      const int c = a.iters > 0 ? lab[w] : 0;
-      float r[32];
-      for (int e = 0; e < G; ++e) {
-        const float h = St<T>::load(src, (int64_t)w * d + g0 + e);
-        const float zz = St<T>::load((const T*)a.win_z + ((int64_t)b * K + c) * d, g0 + e);
-        r[e] = h - zz;
-      }
-      const int64_t row = (int64_t)b * a.win_max + w;
-      resid_encode_group(a.resid, r, a.codes + row * cb, a.scales + row * sb, g0);
-    }
+  if (cnt == 0) return;   // an empty cluster keeps its centroid
+  const int n = ch * 256 + threadIdx.x;
+  double s = 0.0;
+  if (n < d) {
+    const double* xh = a.xhat + (int64_t)b * a.win_max * d + n;
+    for (int w = 0; w < nwin; ++w)
+      if (lab[w] == c) s += xh[(int64_t)w * d];
+    a.km_sum[((int64_t)b * K + c) * d + n] = s;
+  }
+  const double ss = block_sum_d(s * s, red);
+  if (threadIdx.x == 0) a.cpart[((int64_t)b * K + c) * a.nchunk + ch] = ss;
+}
+
+// New centroid columns: the member sum over the norm of the whole sum (kept when the sum
+// vanishes).  The first workgroup of a sequence records the objective after the update, the sum
+// of those norms over the non-empty clusters.
+__global__ __launch_bounds__(256) void km_finish_kernel(ClusterArgs a, int it) {
+  const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, d = a.d, K = a.K;
+  auto norm_of = [&](int cc) {
+    double ss = 0.0;
+    for (int k = 0; k < a.nchunk; ++k) ss += a.cpart[((int64_t)b * K + cc) * a.nchunk + k];
+    return sqrt(ss);
+  };
+  if (threadIdx.x == 0 && ch == 0 && c == 0 && a.objective) {
+    const int keff = min(K, a.geom.n_win);
+    double J = 0.0;
+    for (int cc = 0; cc < keff; ++cc)
+      if (a.km_cnt[(int64_t)b * K + cc] > 0) J += norm_of(cc);
+    a.objective[(int64_t)b * 2 * a.iters + 2 * it + 1] = J;
+  }
+  if (a.km_cnt[(int64_t)b * K + c] == 0) return;
+  const double ns = norm_of(c);
+  const int n = ch * 256 + threadIdx.x;
+  if (ns > 0.0 && n < d)
+    a.z64[((int64_t)b * K + c) * d + n] = a.km_sum[((int64_t)b * K + c) * d + n] / ns;
+}
+
+// Labels (0 past the window) and the centroids rounded once to the storage dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void km_store_kernel(ClusterArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K, nwin = a.geom.n_win;
+  if (c == 0)
+    for (int w = threadIdx.x; w < a.win_max; w += blockDim.x)
+      a.win_m[(int64_t)b * a.win_max + w] = (w < nwin && a.iters > 0) ? a.km_lab[(int64_t)b * a.win_max + w] : 0;
+  for (int n = threadIdx.x; n < d; n += blockDim.x)
+    St<T>::store_d((T*)a.win_z + ((int64_t)b * K + c) * d, n, a.z64[((int64_t)b * K + c) * d + n]);
+}
+
+// Residual codes of window row w against its stored centroid, one group per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void km_resid_kernel(ClusterArgs a) {
+  const int w = blockIdx.x, b = blockIdx.y, d = a.d;
+  const int G = resid_group(a.resid), ng = d / G;
+  const int c = a.iters > 0 ? a.km_lab[(int64_t)b * a.win_max + w] : 0;
+  const T* src = entry_row<T>(a, b, w);
+  const T* zc = (const T*)a.win_z + ((int64_t)b * a.K + c) * d;
+  const int64_t row = (int64_t)b * a.win_max + w;
+  const int64_t cb = resid_code_bytes(a.resid, d), sb = resid_scale_bytes(a.resid, d);
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) {
+    float r[32];
+    for (int e = 0; e < G; ++e) r[e] = St<T>::load(src, g * G + e) - St<T>::load(zc, g * G + e);
+    resid_encode_group(a.resid, r, a.codes + row * cb, a.scales + row * sb, g * G);
   }
 }
 
@@ -275,7 +341,7 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int d = a.d;
   const T* src;
-  if (r < a.block) src = (const T*)a.h_act + ((int64_t)b * a.block + r) * d;
+  if (r < a.block) src = (const T*)a.h_act + (int64_t)b * a.act_bstride + (int64_t)r * d;
   else if (r < a.block + a.n_win) src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + (r - a.block)) * d;
   else src = (const T*)a.win_z + ((int64_t)b * a.K + (r - a.block - a.n_win)) * d;
   T* dst = (T*)a.a_qkv + (int64_t)b * a.a_bstride;
@@ -333,8 +399,17 @@ __global__ void resid_unpack_kernel(int fmt, const uint8_t* codes, const uint8_t
 template <typename T>
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
   if (a.mode == POLESTAR_CLUSTER_ENTRY) {
-    double* s64 = a.z64 + (int64_t)a.batch * a.K * a.d;   // scratch row per sequence after the centroids
-    hipLaunchKernelGGL(kmeans_entry_kernel<T>, dim3(a.batch), dim3(1024), 0, s, a, s64);
+    const int nwin = a.geom.n_win, keff = a.K < nwin ? a.K : nwin;
+    if (a.K > kKmMax || nwin > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(km_unit_kernel<T>, dim3(nwin, a.batch), dim3(256), 0, s, a);
+    const dim3 g(a.nchunk, keff, a.batch);
+    for (int it = 0; it < a.iters; ++it) {
+      hipLaunchKernelGGL(km_assign_kernel, dim3(nwin, a.batch), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(km_update_kernel, g, dim3(256), 0, s, a, it);
+      hipLaunchKernelGGL(km_finish_kernel, g, dim3(256), 0, s, a, it);
+    }
+    hipLaunchKernelGGL(km_store_kernel<T>, dim3(a.K, a.batch), dim3(256), 0, s, a);
+    if (a.resid) hipLaunchKernelGGL(km_resid_kernel<T>, dim3(nwin, a.batch), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(window_rows_kernel<T>, dim3(a.geom.n_win, a.batch), dim3(256), 0, s, a);
     const dim3 g(a.nchunk, a.K, a.batch);

@@ -5,7 +5,7 @@
 // Handle contents (host only).
 struct WsLayout {
   size_t win_rows, flags, a_qkv, q, o, kl, akl, lg, part, hp, a_gu, act, a_kv, xhat, z64, wstat, attn_part, lm_a,
-      lm_stats, lm_meta, total;
+      lm_stats, lm_meta, q_all, km_lab, km_cnt, km_sum, total;
 };
 
 struct ProfState;   // per-kernel event records (api.hip)
@@ -237,7 +237,8 @@ struct ClusterArgs {
   int32_t batch, d, K, win_max, block, n_pos, iters;
   WinGeom geom;
   void* win_h; uint8_t* codes; uint8_t* scales; void* win_z; int32_t* win_m;
-  const void* entry_h;
+  const void* entry_h;       // entry rows: [batch][win_max][d], or with entry_full the rows of
+  int32_t entry_full;        // all positions [batch][n_pos][d], read at the window positions
   const int32_t* init_idx;
   double* objective;
   const void* u_rows; const int32_t* u_idx; const int32_t* u_count;
@@ -247,6 +248,9 @@ struct ClusterArgs {
   double* wnorm;            // [batch][win_max] float64 norms of the current window rows
   double* cpart;            // [batch][K][nchunk] chunk sums of squares of the member sums
   int32_t nchunk;           // ceil(d / 256)
+  int32_t* km_lab;          // block entry: labels [batch][win_max], member counts [batch][K],
+  int32_t* km_cnt;          //   member sums [batch][K][d] (float64); wnorm holds the best cosines
+  double* km_sum;
   int resid;                // residual format of the window storage (POLESTAR_RESID_*; 0: raw rows)
 };
 template <typename T>
@@ -256,7 +260,8 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
 struct PrepArgs {
   int32_t batch, d, block, win_max, n_win, K, mq, refresh;
   int32_t a_tiles;        // > 0: a_qkv fragment-packed with this many row tiles (bf16)
-  const void* h_act; const void* ws_rows; const void* win_z;
+  const void* h_act; int64_t act_bstride;   // block rows per sequence, act_bstride elements apart
+  const void* ws_rows; const void* win_z;
   void* a_qkv; int64_t a_bstride; float eps;
 };
 template <typename T>
@@ -274,6 +279,7 @@ struct AttnArgs {
   int32_t o_planes;
   float* proxy_logits;    // [batch][K][hq][n]
   float* kl;              // [batch][K][hq]
+  int32_t proxy_kl;       // 1: KL of the proxy rows against proxy_logits; 0: only store their logits
   float* act_logits;      // [batch][block][hq][n] or null
   float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
   int32_t chunk_keys;     // bf16 path: keys per workgroup (multiple of 32)

@@ -62,6 +62,7 @@ class RefreshStack:
         self.act_logits = torch.zeros(bt, dims.block, dims.n_heads, n, dtype=torch.float32, device=device)
         self.delta = torch.zeros(bt, dims.block, dtype=torch.float32, device=device)
         self.last_packet = 0
+        self.h_seq: Optional[List[torch.Tensor]] = None   # block entry: layer inputs of every position
 
     def _packet(self, i: int) -> B.Packet:
         return B.Packet(rows=self.pk_rows[i].data_ptr(), idx=self.pk_idx[i].data_ptr(),
@@ -105,6 +106,23 @@ class RefreshStack:
         for l in range(self.n_layers):
             B.polestar_cluster(self.h, B.CLUSTER_ENTRY, self.struct(l), blk_start, None, init_idx[l], entry_rows[l],
                                None, self.ws, self.ws_bytes)
+
+    def entry_forward(self, blk_start: int, h0: torch.Tensor, init_idx: List[torch.Tensor], full: bool = True,
+                      stream=None) -> torch.Tensor:
+        """Block entry of every layer: h0 [batch, n_pos, d] is layer 0's input; each layer recomputes
+        every position (full) or the window and the active block, clusters its window rows and sets
+        its first drift reference.  Returns the last layer's output rows."""
+        if self.h_seq is None:
+            shape = (self.dims.batch, self.dims.n_pos, self.dims.d)
+            self.h_seq = [torch.empty(shape, dtype=self.tdt, device=self.device) for _ in range(2)]
+        mode = B.ENTRY_FULL if full else B.ENTRY_WINDOW
+        self.h_seq[0].copy_(h0)
+        cur = 0
+        for l in range(self.n_layers):
+            B.polestar_entry(self.h, mode, self.struct(l), blk_start, self.h_seq[cur], init_idx[l],
+                             self.h_seq[1 - cur], None, self.ws, self.ws_bytes, stream)
+            cur = 1 - cur
+        return self.h_seq[cur]
 
     # ---- one denoising step -----------------------------------------------------------------
     def step(self, blk_start: int, h_in: torch.Tensor, refresh: bool = True, commit_delta: bool = True) -> torch.Tensor:

@@ -96,6 +96,7 @@ enum {
 };
 enum { POLESTAR_CLUSTER_ENTRY = 0, POLESTAR_CLUSTER_UPDATE = 1 };
 enum { POLESTAR_DRIFT_REFRESH = 0, POLESTAR_DRIFT_ACTIVE_ONLY = 1 };
+enum { POLESTAR_ENTRY_FULL = 0, POLESTAR_ENTRY_WINDOW = 1 };
 enum {
   POLESTAR_W_QKV = 0,  /* src [(n_heads + 2 n_kv_heads) head_dim, d] = rows of W_Q, W_K, W_V */
   POLESTAR_W_O = 1,    /* src [d, n_heads head_dim] */
@@ -258,6 +259,30 @@ int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_
 int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
                      const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
                      void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * polestar_entry — block-entry state of one layer [§4.1 "Update Schedule"
+ * (a whole-sequence forward at every other block entry) and "Cluster and
+ * Quantize Hidden States"; Algorithm 1 block entry].
+ *  mode POLESTAR_ENTRY_FULL recomputes every position; POLESTAR_ENTRY_WINDOW
+ *  the window and the active block, positions [blk_start - win_prefix,
+ *  blk_start + B + win_suffix) cut at 0 and n_pos.  For those rows of
+ *  h_in [batch, n_pos, d] (storage dtype, device): their K/V (RMSNorm with unit
+ *  gain, W_K/W_V) replace the layer's cache rows; then each row attends to all
+ *  n_pos cache positions and the layer's residual, RMSNorm and SwiGLU steps
+ *  give its row of h_out [batch, n_pos, d] (the next layer's input).  Rows of
+ *  h_out outside the set, and cache rows outside it, are left as they are.
+ *  h_out must not overlap h_in (POLESTAR_E_ARG).
+ *  Then, as polestar_cluster(ENTRY) but on the window rows of h_in (read at
+ *  their positions): k-means from init_idx [batch, K], storing win_z, win_m and
+ *  the window rows or their residual codes; objective as there (nullable).
+ *  Last, the proxy logits of the new centroids over the fresh cache are
+ *  written to L->proxy_logits: the reference of the first drift score.
+ *  Needs every weight, cache and window pointer of L.
+ */
+int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
+                   const int32_t* init_idx, void* h_out, double* objective, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /*
  * polestar_commit — Polestar-Commit [§4.2 "Current Block Commit" and

@@ -1,0 +1,151 @@
+"""Parity of the block-entry call (polestar_entry) with the CPU oracle.
+
+For each case the GPU runs polestar_entry on one or two layers from seeded
+hidden rows and a seeded stale cache; the oracle runs the same rows through
+layer_forward_rows on the same stale cache, then block_entry_layer_state
+(spherical k-means of the window rows of the layer input, residual codes,
+proxy logits of the centroids over the fresh cache).  Compared:
+  * the recomputed rows of h_out and of the K/V caches (stored values within
+    the storage-dtype bounds), every other row bit-identical to what it held;
+  * k-means labels and residual codes bit-exact, centroids within the bounds;
+  * the proxy logits within 2e-3 (each side from its own stored cache and
+    centroids).
+A second layer takes each side's own first-layer output, so its values are
+compared as free-running values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from drift_driven_sparse_amd import binding as B
+from oracle import polestar_oracle as O
+from tests.harness import (Dev, assert_close, assert_stored, assert_traj, layer_struct, log, np64, oracle_weights,
+                           packed_layer, weights)
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WORKLOADS[1]
+CASES = {
+    # name: (workload, batch, layers, full, blk_start)
+    "tiny_fp32_full_2layers": (TINY, 1, 2, True, 64),
+    "tiny_fp32_window": (TINY, 1, 1, False, 160),
+    "tiny_bf16_full_2layers_batch2": (synth.shrink(TINY, dtype="bf16"), 2, 2, True, 96),
+    "tiny_bf16_window_at_start": (synth.shrink(TINY, dtype="bf16"), 1, 1, False, 0),
+    "tiny_bf16_window_at_end": (synth.shrink(TINY, dtype="bf16"), 1, 1, False, 288),
+    "tiny_bf16_nvfp4_full": (synth.shrink(TINY, dtype="bf16", resid="nvfp4"), 1, 1, True, 128),
+    "tiny_bf16_mxfp4_window_batch2": (synth.shrink(TINY, dtype="bf16", resid="mxfp4"), 2, 1, False, 128),
+    "small_window_B8": (synth.shrink(TINY, dtype="bf16", prompt=32, gen=96, n_clusters=4, top_k=2, block=8,
+                                     win_prefix=8, win_suffix=0), 1, 1, False, 48),
+    "llada_layer_full": (synth.WORKLOADS[2], 1, 1, True, 512),
+    "llada_n1024_full": (synth.shrink(synth.WORKLOADS[3], n_layers=1), 1, 1, True, 512),
+    "dream_gqa_window": (synth.shrink(synth.WORKLOADS[4], n_layers=1), 1, 1, False, 384),
+}
+
+
+def _cache_pair(w, batch, run):
+    """Seeded stale K/V caches (device layouts) and their oracle copies [n, Hkv, dh]."""
+    n, hkv, dh = w.n_pos, w.n_kv_heads, w.head_dim
+    ks = [synth.tensor(w, (b, 30), (n, hkv, dh), 1.0, run, "cuda", w.dtype) for b in range(batch)]
+    vs = [synth.tensor(w, (b, 31), (n, hkv, dh), 1.0, run, "cuda", w.dtype) for b in range(batch)]
+    kc = torch.stack(ks).contiguous()
+    vc = torch.stack([v.permute(1, 2, 0) for v in vs]).contiguous()
+    return kc, vc, [np64(k) for k in ks], [np64(v) for v in vs]
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_block_entry_parity(case):
+    w, batch, n_layers, full, blk_start = CASES[case]
+    log(f"[entry] case={case} d={w.d} n={w.n_pos} heads={w.n_heads}/{w.n_kv_heads} batch={batch} dtype={w.dtype} "
+        f"resid={w.resid} layers={n_layers} mode={'full' if full else 'window'} blk_start={blk_start}")
+    dev = Dev(w, batch=batch, vocab=0)
+    cfg = O.Cfg.from_workload(w)
+    st = cfg.st
+    n, d, hq, hkv, dh, K, WM = w.n_pos, w.d, w.n_heads, w.n_kv_heads, w.head_dim, w.n_clusters, dev.win_max
+    nv = w.resid != "raw"
+    wpos = O.window_positions(blk_start, n, w.block, w.win_prefix, w.win_suffix)
+    nw = len(wpos)
+    keff = min(K, nw)
+    rows = O.entry_positions(blk_start, n, w.block, w.win_prefix, w.win_suffix, full)
+    others = np.setdiff1d(np.arange(n), rows)
+    cb, sb = B.polestar_resid_bytes(B.RESID_BY_NAME[w.resid], d) if nv else (0, 0)
+    mode = B.ENTRY_FULL if full else B.ENTRY_WINDOW
+
+    # layer inputs: seeded rows for every position, rounded to the storage dtype
+    h_in = torch.stack([synth.embeddings(w, 0, "cuda", b).to(dev.tdt) for b in range(batch)]).contiguous()
+    h_or = [np64(h_in[b]) for b in range(batch)]
+    for l in range(n_layers):
+        W = weights(w, l)
+        P = packed_layer(dev, W)
+        Wo = oracle_weights(W)
+        del W
+        kc, vc, k_or, v_or = _cache_pair(w, batch, l)
+        kc0, vc0 = kc.clone(), vc.clone()
+        z = dev.zeros(batch, K, d)
+        m = torch.zeros(batch, WM, dtype=torch.int32, device="cuda")
+        plog = torch.full((batch, K, hq, n), 7.0, dtype=torch.float32, device="cuda")
+        init = torch.zeros(batch, K, dtype=torch.int32, device="cuda")
+        inits = [synth.kmeans_init(w, nw, l, 0, 0, b) for b in range(batch)]
+        for b in range(batch):
+            init[b, :keff] = torch.tensor(inits[b])
+        Ld = dict(P, k_cache=kc, v_cache=vc, win_z=z, win_m=m, proxy_logits=plog)
+        if nv:
+            codes = torch.zeros(batch, WM, cb, dtype=torch.uint8, device="cuda")
+            scales = torch.zeros(batch, WM, max(sb, 1), dtype=torch.uint8, device="cuda")
+            Ld.update(win_codes=codes, win_scales=scales)
+        else:
+            win = dev.zeros(batch, WM, d)
+            Ld.update(win_h=win)
+        h_out = torch.full_like(h_in, 3.0)
+        obj = torch.zeros(batch, 2 * w.kmeans_iters, dtype=torch.float64, device="cuda")
+        B.polestar_entry(dev.h, mode, layer_struct(Ld), blk_start, h_in, init, h_out, obj, dev.ws, dev.ws_bytes)
+        torch.cuda.synchronize()
+        log(f"[entry] layer {l}: GPU done")
+        cmp_rows = assert_stored if l == 0 else (lambda a, b_, dt, name: assert_traj(a, b_, dt, name))
+        nxt = []
+        for b in range(batch):
+            Kb, Vb = k_or[b].copy(), v_or[b].copy()
+            out_or = O.layer_forward_rows(h_or[b][rows], rows, Wo, cfg, Kb, Vb)
+            ls = O.block_entry_layer_state(h_or[b], Kb, Vb, Wo["wq"], cfg, blk_start, inits[b])
+            # recomputed rows and cache rows; the rest untouched
+            cmp_rows(np64(h_out[b, rows]), out_or, w.dtype, f"layer {l} seq {b} outputs")
+            assert torch.all(h_out[b, others] == 3.0), "rows outside the entry set were written"
+            kg = np64(kc[b]).reshape(n, -1)
+            vg = np64(vc[b].permute(2, 0, 1)).reshape(n, -1)
+            cmp_rows(kg[rows], Kb.reshape(n, -1)[rows], w.dtype, f"layer {l} seq {b} K rows")
+            cmp_rows(vg[rows], Vb.reshape(n, -1)[rows], w.dtype, f"layer {l} seq {b} V rows")
+            assert torch.equal(kc[b, others], kc0[b, others]), "K rows outside the entry set changed"
+            assert torch.equal(vc[b][..., others], vc0[b][..., others]), "V rows outside the entry set changed"
+            # clustering of the window rows of this layer's input (each side's own input rows)
+            if l == 0:
+                assert np.array_equal(m[b, :nw].cpu().numpy(), ls["M"]), "k-means labels differ"
+                assert np.allclose(obj[b].cpu().numpy(), ls["trace"], rtol=1e-12, atol=0), "k-means objective"
+                assert_stored(np64(z[b]), ls["Z"], w.dtype, "entry centroids")
+                if nv:
+                    c_or, s_or = O.residual_quantize(h_or[b][wpos], np64(z[b]), m[b, :nw].cpu().numpy(), w.resid)
+                    assert np.array_equal(codes[b, :nw].cpu().numpy(), c_or), f"entry {w.resid} codes differ"
+                    assert np.array_equal(scales[b, :nw, :sb].cpu().numpy(), s_or)
+                else:
+                    assert torch.equal(win[b, :nw], h_in[b, wpos]), "window rows not stored as they are"
+            else:
+                # inputs differ by storage roundings: compare the GPU's labels with k-means of its own rows
+                zg, mg, _ = O.spherical_kmeans(np64(h_in[b, wpos]), K, inits[b], w.kmeans_iters)
+                assert np.array_equal(m[b, :nw].cpu().numpy(), mg), "k-means labels differ (GPU input rows)"
+                assert_stored(np64(z[b]), st(zg), w.dtype, "entry centroids (GPU input rows)")
+            # proxy logits: from the GPU's stored centroids and cache by the oracle's definition, and
+            # (first layer) against the oracle's own state
+            zq = O.project(np64(z[b]), Wo["wq"], cfg.eps, st).reshape(K, hq, dh)
+            _, pl = O.attention(zq, kg.reshape(n, hkv, dh), vg.reshape(n, hkv, dh), hq, hkv)
+            assert_close(plog[b].cpu().numpy(), pl, f"layer {l} seq {b} proxy logits", dtype=w.dtype)
+            if l == 0:
+                assert_close(plog[b].cpu().numpy(), ls["P"], f"seq {b} proxy logits (oracle state)", dtype=w.dtype)
+            hn = h_or[b].copy()
+            hn[rows] = out_or
+            nxt.append(hn)
+        log(f"[entry] layer {l} ok")
+        # the next layer continues from each side's own outputs
+        h_in = h_out.clone()
+        h_or = nxt
+        del P, Ld
+    dev.close()
+    log(f"[entry] case={case} passed")
