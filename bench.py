@@ -118,24 +118,43 @@ def entry_flops(w, rows: int, n_layers: int) -> float:
     return n_layers * (proj + attn)
 
 
-def entry_timing(st, w, blk, h0, inits, n_layers, reps=2):
+def entry_timing(st, w, blk, h0, inits, n_layers, reps=3):
     import torch
+    from drift_driven_sparse_amd import binding as B
     res = {}
     for name, full in (("full", True), ("window", False)):
-        st.entry_forward(blk, h0, inits, full=full)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # the entry is launch-bound in its k-means (short launches), so it is captured in a HIP graph
+        # like the step; replays are timed
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            st.entry_forward(blk, h0, inits, full=full)
+        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.entry_forward(blk, h0, inits, full=full)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         for _ in range(reps):
-            st.entry_forward(blk, h0, inits, full=full)
+            g.replay()
         ev1.record()
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / reps
+        del g
         rows = w.n_pos if full else min(w.n_pos, blk + w.block + w.win_suffix) - max(0, blk - w.win_prefix)
         tf = entry_flops(w, rows, n_layers) / (ms * 1e-3) / 1e12
+        # one more run with HIP events around every launch (summed per kernel kind)
+        B.polestar_profile(st.h, True)
+        st.entry_forward(blk, h0, inits, full=full)
+        prof = B.polestar_profile_read(st.h)
+        B.polestar_profile(st.h, False)
+        kern = {k: round(v[0], 3) for k, v in prof.items() if v[1]}
         res[name] = {"ms": round(ms, 3), "rows": rows, "TFLOPs": round(tf, 1),
-                     "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-        log(f"[bench] block entry ({name}, {rows} rows x {n_layers} layers): {ms:.2f} ms, {tf:.1f} TFLOP/s")
+                     "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "kernel_ms": kern}
+        log(f"[bench] block entry ({name}, {rows} rows x {n_layers} layers): {ms:.2f} ms, {tf:.1f} TFLOP/s; "
+            f"per kind (ms, eager, events around each launch): {kern}")
     return res
 
 

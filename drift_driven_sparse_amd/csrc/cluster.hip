@@ -27,12 +27,24 @@ PS_DEV const T* entry_row(const ClusterArgs& a, int b, int w) {
   return (const T*)a.entry_h + ((int64_t)b * rows + r) * a.d;
 }
 
+// Sum of vals[0..n) in index order, the values first gathered into LDS by up to blockDim.x
+// threads at once (so their loads overlap); every thread gets the sum.  n <= kGather.
+constexpr int kGather = 512;
+PS_DEV double gather_sum(const double* vals, int n, double* sh) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sh[i] = vals[i];
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += sh[i];
+  __syncthreads();
+  return s;
+}
+
 // Unit row (a zero row stays zero); raw storage copies the row into the window; the workgroup of
 // the row named by init_idx[c] seeds centroid c (row 0's workgroup zeroes the clusters with no
-// valid seed).
+// valid seed).  1024 threads: a 4096-wide row is one load per thread.
 template <typename T>
-__global__ __launch_bounds__(256) void km_unit_kernel(ClusterArgs a) {
-  __shared__ double red[4];
+__global__ __launch_bounds__(1024) void km_unit_kernel(ClusterArgs a) {
+  __shared__ double red[16];
   const int w = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K, nwin = a.geom.n_win;
   const int keff = min(K, nwin);
   const T* src = entry_row<T>(a, b, w);
@@ -60,23 +72,31 @@ __global__ __launch_bounds__(256) void km_unit_kernel(ClusterArgs a) {
   }
 }
 
-// Largest cosine over the first keff centroids, lowest index on ties.
+// Largest cosine over the first keff centroids, lowest index on ties.  1024 threads, the column
+// loop unrolled so that a thread's loads are in flight together.
 constexpr int kKmMax = 16;   // clusters per sequence (the handle's limit)
-__global__ __launch_bounds__(256) void km_assign_kernel(ClusterArgs a) {
-  __shared__ double red[4][kKmMax];
+__global__ __launch_bounds__(1024) void km_assign_kernel(ClusterArgs a) {
+  __shared__ double red[16][kKmMax];
   const int w = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K;
   const int keff = min(K, a.geom.n_win);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const double* xh = a.xhat + ((int64_t)b * a.win_max + w) * d;
   const double* z = a.z64 + (int64_t)b * K * d;
   double t[kKmMax];
 #pragma unroll
   for (int c = 0; c < kKmMax; ++c) t[c] = 0.0;
-  for (int n = threadIdx.x; n < d; n += blockDim.x) {
-    const double x = xh[n];
+  int n = threadIdx.x;
+  for (; n + blockDim.x < d; n += 2 * blockDim.x) {
+    const double x0 = xh[n], x1 = xh[n + blockDim.x];
 #pragma unroll
     for (int c = 0; c < kKmMax; ++c)
-      if (c < keff) t[c] += x * z[(int64_t)c * d + n];
+      if (c < keff) t[c] += x0 * z[(int64_t)c * d + n] + x1 * z[(int64_t)c * d + n + blockDim.x];
+  }
+  if (n < d) {
+    const double x0 = xh[n];
+#pragma unroll
+    for (int c = 0; c < kKmMax; ++c)
+      if (c < keff) t[c] += x0 * z[(int64_t)c * d + n];
   }
 #pragma unroll
   for (int c = 0; c < kKmMax; ++c)
@@ -89,7 +109,8 @@ __global__ __launch_bounds__(256) void km_assign_kernel(ClusterArgs a) {
     int bc = 0;
     double bv = -INFINITY;
     for (int c = 0; c < keff; ++c) {
-      const double v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+      double v = 0.0;
+      for (int i = 0; i < nwv; ++i) v += red[i][c];
       if (v > bv) {
         bv = v;
         bc = c;
@@ -100,31 +121,44 @@ __global__ __launch_bounds__(256) void km_assign_kernel(ClusterArgs a) {
   }
 }
 
-// Member sum of cluster c over one 256-column chunk, and the chunk's sum of squares.  The first
-// workgroup of a sequence also records the objective after the assignment.
+// Member sum of cluster c over one 256-column chunk, and the chunk's sum of squares.  The members
+// are listed in LDS first, so each thread's loads of member values overlap.  The first workgroup
+// of a sequence also records the objective after the assignment.
 __global__ __launch_bounds__(256) void km_update_kernel(ClusterArgs a, int it) {
   __shared__ int lab[256];
-  __shared__ double red[4];
+  __shared__ int mem[256];
+  __shared__ int nmem_sh;
+  __shared__ double red[kGather];
   const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, d = a.d, K = a.K, nwin = a.geom.n_win;
   for (int w = threadIdx.x; w < nwin; w += blockDim.x) lab[w] = a.km_lab[(int64_t)b * a.win_max + w];
   __syncthreads();
-  int cnt = 0;
-  for (int w = 0; w < nwin; ++w) cnt += lab[w] == c;
-  if (threadIdx.x == 0 && ch == 0) {
-    a.km_cnt[(int64_t)b * K + c] = cnt;
-    if (c == 0 && a.objective) {
-      double J = 0.0;
-      for (int w = 0; w < nwin; ++w) J += a.wnorm[(int64_t)b * a.win_max + w];
-      a.objective[(int64_t)b * 2 * a.iters + 2 * it] = J;
-    }
+  if (threadIdx.x == 0) {
+    int k = 0;
+    for (int w = 0; w < nwin; ++w)
+      if (lab[w] == c) mem[k++] = w;
+    nmem_sh = k;
+    if (ch == 0) a.km_cnt[(int64_t)b * K + c] = k;
   }
-  if (cnt == 0) return;   // an empty cluster keeps its centroid
+  __syncthreads();
+  const int nmem = nmem_sh;
+  if (ch == 0 && c == 0 && a.objective) {
+    const double J = gather_sum(a.wnorm + (int64_t)b * a.win_max, nwin, red);
+    if (threadIdx.x == 0) a.objective[(int64_t)b * 2 * a.iters + 2 * it] = J;
+  }
+  if (nmem == 0) return;   // an empty cluster keeps its centroid
   const int n = ch * 256 + threadIdx.x;
   double s = 0.0;
   if (n < d) {
     const double* xh = a.xhat + (int64_t)b * a.win_max * d + n;
-    for (int w = 0; w < nwin; ++w)
-      if (lab[w] == c) s += xh[(int64_t)w * d];
+    int j = 0;
+    for (; j + 4 <= nmem; j += 4) {
+      double v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = xh[(int64_t)mem[j + u] * d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; j < nmem; ++j) s += xh[(int64_t)mem[j] * d];
     a.km_sum[((int64_t)b * K + c) * d + n] = s;
   }
   const double ss = block_sum_d(s * s, red);
@@ -135,21 +169,29 @@ __global__ __launch_bounds__(256) void km_update_kernel(ClusterArgs a, int it) {
 // vanishes).  The first workgroup of a sequence records the objective after the update, the sum
 // of those norms over the non-empty clusters.
 __global__ __launch_bounds__(256) void km_finish_kernel(ClusterArgs a, int it) {
+  __shared__ double sh[kGather];
+  __shared__ double norms[kKmMax];
   const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, d = a.d, K = a.K;
-  auto norm_of = [&](int cc) {
-    double ss = 0.0;
-    for (int k = 0; k < a.nchunk; ++k) ss += a.cpart[((int64_t)b * K + cc) * a.nchunk + k];
-    return sqrt(ss);
-  };
-  if (threadIdx.x == 0 && ch == 0 && c == 0 && a.objective) {
-    const int keff = min(K, a.geom.n_win);
-    double J = 0.0;
-    for (int cc = 0; cc < keff; ++cc)
-      if (a.km_cnt[(int64_t)b * K + cc] > 0) J += norm_of(cc);
-    a.objective[(int64_t)b * 2 * a.iters + 2 * it + 1] = J;
+  const int keff = min(K, a.geom.n_win);
+  const double* cp = a.cpart + (int64_t)b * K * a.nchunk;
+  if (ch == 0 && c == 0 && a.objective) {
+    // norms of every cluster: chunk partials gathered at once, each cluster's added in chunk order
+    for (int i = threadIdx.x; i < keff * a.nchunk; i += blockDim.x) sh[i] = cp[i];
+    __syncthreads();
+    if (threadIdx.x < keff) {
+      double ss = 0.0;
+      for (int k = 0; k < a.nchunk; ++k) ss += sh[threadIdx.x * a.nchunk + k];
+      norms[threadIdx.x] = a.km_cnt[(int64_t)b * K + threadIdx.x] > 0 ? sqrt(ss) : 0.0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double J = 0.0;
+      for (int cc = 0; cc < keff; ++cc) J += norms[cc];
+      a.objective[(int64_t)b * 2 * a.iters + 2 * it + 1] = J;
+    }
   }
   if (a.km_cnt[(int64_t)b * K + c] == 0) return;
-  const double ns = norm_of(c);
+  const double ns = sqrt(gather_sum(cp + (int64_t)c * a.nchunk, a.nchunk, sh));
   const int n = ch * 256 + threadIdx.x;
   if (ns > 0.0 && n < d)
     a.z64[((int64_t)b * K + c) * d + n] = a.km_sum[((int64_t)b * K + c) * d + n] / ns;
@@ -401,10 +443,11 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
   if (a.mode == POLESTAR_CLUSTER_ENTRY) {
     const int nwin = a.geom.n_win, keff = a.K < nwin ? a.K : nwin;
     if (a.K > kKmMax || nwin > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(km_unit_kernel<T>, dim3(nwin, a.batch), dim3(256), 0, s, a);
+    if (a.nchunk > kGather || keff * a.nchunk > kGather) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(km_unit_kernel<T>, dim3(nwin, a.batch), dim3(1024), 0, s, a);
     const dim3 g(a.nchunk, keff, a.batch);
     for (int it = 0; it < a.iters; ++it) {
-      hipLaunchKernelGGL(km_assign_kernel, dim3(nwin, a.batch), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(km_assign_kernel, dim3(nwin, a.batch), dim3(1024), 0, s, a);
       hipLaunchKernelGGL(km_update_kernel, g, dim3(256), 0, s, a, it);
       hipLaunchKernelGGL(km_finish_kernel, g, dim3(256), 0, s, a, it);
     }

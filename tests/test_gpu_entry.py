@@ -149,3 +149,54 @@ def test_block_entry_parity(case):
         del P, Ld
     dev.close()
     log(f"[entry] case={case} passed")
+
+
+def test_entry_graph_replay_matches_eager():
+    """The block entry of a 2-layer stack captured in a HIP graph: every replay (with eager work
+    between replays) gives the eager entry's state bit for bit."""
+    from drift_driven_sparse_amd.stack import RefreshStack
+    w = synth.shrink(TINY, dtype="bf16", resid="nvfp4")
+    dims = B.Dims(d=w.d, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn, n_pos=w.n_pos,
+                  batch=2, block=w.block, win_prefix=w.win_prefix, win_suffix=w.win_suffix, n_clusters=w.n_clusters,
+                  top_k=w.top_k, vocab=0, dtype=B.BF16, resid_fmt=B.RESID_NVFP4)
+    params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist, mask_id=0,
+                      kmeans_iters=w.kmeans_iters)
+    st = RefreshStack(dims, params, 2)
+    try:
+        blk = 96
+        nw = len(O.window_positions(blk, w.n_pos, w.block, w.win_prefix, w.win_suffix))
+        inits = []
+        for l in range(2):
+            st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
+            inits.append(torch.stack([torch.tensor(synth.kmeans_init(w, nw, l, 0, 0, b), dtype=torch.int32)
+                                      for b in range(2)]).cuda())
+        h0 = torch.stack([synth.embeddings(w, 0, "cuda", b).to(torch.bfloat16) for b in range(2)]).contiguous()
+        names = ("k_cache", "v_cache", "win_codes", "win_scales", "win_z", "win_m", "proxy_logits")
+
+        def state(out):
+            return [out.clone()] + [L[k].clone() for L in st.layers for k in names]
+
+        want = state(st.entry_forward(blk, h0, inits, full=True))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            st.entry_forward(blk, h0, inits, full=True)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gout = st.entry_forward(blk, h0, inits, full=True)
+        for rep in range(3):
+            for L in st.layers:
+                for k in names:
+                    L[k].zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            got = state(gout)
+            bad = [i for i, (a, b_) in enumerate(zip(got, want)) if not torch.equal(a, b_)]
+            log(f"[entry-graph] replay {rep}: {len(want) - len(bad)}/{len(want)} tensors bit-identical")
+            assert not bad, f"replay {rep} differs from the eager entry in tensors {bad}"
+            st.entry_forward(blk, h0, inits, full=False)   # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        st.close()
