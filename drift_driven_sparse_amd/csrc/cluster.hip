@@ -347,14 +347,13 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
   __shared__ int mem[256];
   __shared__ int wcnt[4];
   __shared__ float zsh[kChunk];
+  __shared__ double gsh[kGather];
   const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = a.d, n0 = ch * kChunk, n = n0 + tid;
   const int nmem = members_of(a, b, c, mem, nullptr, wcnt);
   if (nmem == 0) return;   // no members: the centroid is kept and no row refers to it
   const int64_t zrow = (int64_t)b * a.K + c;
-  double ss = 0.0;
-  for (int i = 0; i < a.nchunk; ++i) ss += a.cpart[zrow * a.nchunk + i];
-  const double ns = sqrt(ss);
+  const double ns = sqrt(gather_sum(a.cpart + zrow * a.nchunk, a.nchunk, gsh));
   T* zc = (T*)a.win_z + zrow * d;
   if (n < d) {
     if (ns > 0.0) St<T>::store_d(zc, n, a.z64[zrow * d + n] / ns);   // kept when the sum vanishes
@@ -454,6 +453,7 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(km_store_kernel<T>, dim3(a.K, a.batch), dim3(256), 0, s, a);
     if (a.resid) hipLaunchKernelGGL(km_resid_kernel<T>, dim3(nwin, a.batch), dim3(256), 0, s, a);
   } else {
+    if (a.nchunk > kGather) return hipErrorInvalidValue;
     hipLaunchKernelGGL(window_rows_kernel<T>, dim3(a.geom.n_win, a.batch), dim3(256), 0, s, a);
     const dim3 g(a.nchunk, a.K, a.batch);
     hipLaunchKernelGGL(centroid_sum_kernel<T>, g, dim3(256), 0, s, a);
