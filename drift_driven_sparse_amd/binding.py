@@ -88,7 +88,7 @@ def lib() -> C.CDLL:
         L.polestar_weight_packed_size.argtypes = [vp, C.c_int, C.POINTER(sz)]
         L.polestar_pack_weight.argtypes = [vp, C.c_int, vp, vp, vp]
         L.polestar_cluster.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, C.POINTER(Packet), vp, vp, vp, vp, sz, vp]
-        L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, sz, vp]
+        L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
                                      C.POINTER(Packet), vp, vp, vp, sz, vp]
         L.polestar_refresh.argtypes = [vp, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp, vp, vp, vp, vp, sz, vp]
@@ -194,10 +194,11 @@ def polestar_refresh(h, layer: Layer, blk_start, h_active, sel: Packet, w_kv_nex
                                stream_ptr(stream)), "polestar_refresh")
 
 
-def polestar_entry(h, mode, layer: Layer, blk_start, h_in, init_idx, h_out, objective, ws, ws_bytes,
+def polestar_entry(h, mode, layer: Layer, blk_start, h_in, init_idx, h_out, objective, act_logits, ws, ws_bytes,
                    stream=None) -> None:
     _ck(lib().polestar_entry(h, mode, C.byref(layer), blk_start, ptr(h_in), ptr(init_idx), ptr(h_out),
-                             ptr(objective), ptr(ws), ws_bytes, stream_ptr(stream)), "polestar_entry")
+                             ptr(objective), ptr(act_logits), ptr(ws), ws_bytes, stream_ptr(stream)),
+        "polestar_entry")
 
 
 def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,

@@ -771,7 +771,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
 // complete before any row attends), then attention and the rest of the layer slab by slab.
 template <typename T>
 int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
-             const int32_t* init_idx, void* h_out, double* objective, void* ws, hipStream_t s) {
+             const int32_t* init_idx, void* h_out, double* objective, float* act_logits, void* ws, hipStream_t s) {
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
   const bool full = mode == POLESTAR_ENTRY_FULL;
@@ -818,7 +818,18 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
     const TokRows t = {rows, hin + (int64_t)p0 * d.d, hb, hout + (int64_t)p0 * d.d, hb, nullptr, nullptr, false};
     if ((rc = do_refresh<T>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s))) return rc;
   }
-  // 4. proxy logits of the centroids: the first drift reference
+  // 4. (when asked) the active block's main-attention logits: the first reference of the commit
+  //    drift; the block's queries are rows blk_start.. of q_all
+  if (act_logits) {
+    AttnArgs a = attn_base<T>(h, L, ws);
+    a.q = q_all + (int64_t)blk_start * h->nq;
+    a.mq = d.n_pos;
+    a.n_tok = d.block;
+    a.act_logits = act_logits;
+    a.act_kl = 0;
+    if ((rc = run_attention<T>(h, a, s))) return rc;
+  }
+  // 5. proxy logits of the centroids: the first drift reference
   p.block = 0;
   p.n_win = 0;
   p.refresh = 1;
@@ -1167,7 +1178,8 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
 }
 
 int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
-                   const int32_t* init_idx, void* h_out, double* objective, void* ws, size_t ws_bytes, void* stream) {
+                   const int32_t* init_idx, void* h_out, double* objective, float* act_logits, void* ws,
+                   size_t ws_bytes, void* stream) {
   if (!h || !L || !h_in || !init_idx || !h_out) return POLESTAR_E_NULL;
   if (mode != POLESTAR_ENTRY_FULL && mode != POLESTAR_ENTRY_WINDOW) return POLESTAR_E_ARG;
   int rc = check_ws(h, ws, ws_bytes);
@@ -1187,8 +1199,8 @@ int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_
   if (a0 < b0 + bytes && b0 < a0 + bytes) return POLESTAR_E_ARG;   // h_out must not overlap h_in
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
-             ? do_entry<bf16_t>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, ws, s)
-             : do_entry<float>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, ws, s);
+             ? do_entry<bf16_t>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, act_logits, ws, s)
+             : do_entry<float>(h, mode, L, blk_start, h_in, init_idx, h_out, objective, act_logits, ws, s);
 }
 
 int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,

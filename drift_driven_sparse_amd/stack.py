@@ -111,7 +111,8 @@ class RefreshStack:
                       stream=None) -> torch.Tensor:
         """Block entry of every layer: h0 [batch, n_pos, d] is layer 0's input; each layer recomputes
         every position (full) or the window and the active block, clusters its window rows and sets
-        its first drift reference.  Returns the last layer's output rows."""
+        its first drift reference; the last layer also sets the active block's logits, the first
+        reference of the commit drift.  Returns the last layer's output rows."""
         if self.h_seq is None:
             shape = (self.dims.batch, self.dims.n_pos, self.dims.d)
             self.h_seq = [torch.empty(shape, dtype=self.tdt, device=self.device) for _ in range(2)]
@@ -119,8 +120,10 @@ class RefreshStack:
         self.h_seq[0].copy_(h0)
         cur = 0
         for l in range(self.n_layers):
+            last = l == self.n_layers - 1
             B.polestar_entry(self.h, mode, self.struct(l), blk_start, self.h_seq[cur], init_idx[l],
-                             self.h_seq[1 - cur], None, self.ws, self.ws_bytes, stream)
+                             self.h_seq[1 - cur], None, self.act_logits if last else None, self.ws, self.ws_bytes,
+                             stream)
             cur = 1 - cur
         return self.h_seq[cur]
 

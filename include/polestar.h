@@ -276,13 +276,16 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
  *  Then, as polestar_cluster(ENTRY) but on the window rows of h_in (read at
  *  their positions): k-means from init_idx [batch, K], storing win_z, win_m and
  *  the window rows or their residual codes; objective as there (nullable).
- *  Last, the proxy logits of the new centroids over the fresh cache are
- *  written to L->proxy_logits: the reference of the first drift score.
- *  Needs every weight, cache and window pointer of L.
+ *  act_logits (nullable, f32 [batch, B, Hq, n_pos], device): receives the
+ *  active block's main-attention logits over the fresh cache, the reference
+ *  of the first commit drift delta (pass it for the last layer; §4.2
+ *  "Current Block Commit").  Last, the proxy logits of the new centroids over
+ *  the fresh cache are written to L->proxy_logits: the reference of the
+ *  first drift score.  Needs every weight, cache and window pointer of L.
  */
 int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
-                   const int32_t* init_idx, void* h_out, double* objective, void* ws, size_t ws_bytes,
-                   void* stream);
+                   const int32_t* init_idx, void* h_out, double* objective, float* act_logits, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /*
  * polestar_commit — Polestar-Commit [§4.2 "Current Block Commit" and

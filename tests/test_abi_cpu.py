@@ -110,24 +110,24 @@ def test_calls_validate_before_launching():
                                     ws_bytes, None) == B.E_ALIGN
         # block entry: missing inputs, an unknown mode, a missing layer buffer, overlapping rows
         entry = lib.polestar_entry
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, None, 4096, 8192, None, 4096, ws_bytes, None) == B.E_NULL
-        assert entry(h, 7, C.byref(L), 64, 4096, 4096, 1 << 30, None, 4096, ws_bytes, None) == B.E_ARG
-        assert entry(h, B.ENTRY_WINDOW, C.byref(L), 300, 4096, 4096, 1 << 30, None, 4096, ws_bytes,
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, None, 4096, 8192, None, None, 4096, ws_bytes, None) == B.E_NULL
+        assert entry(h, 7, C.byref(L), 64, 4096, 4096, 1 << 30, None, None, 4096, ws_bytes, None) == B.E_ARG
+        assert entry(h, B.ENTRY_WINDOW, C.byref(L), 300, 4096, 4096, 1 << 30, None, None, 4096, ws_bytes,
                      None) == B.E_ARG
         L.w_o = 4096
         L.w_qkv = L.k_cache = L.v_cache = L.proxy_logits = 4096
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, 4096, ws_bytes - 1,
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, None, 4096, ws_bytes - 1,
                      None) == B.E_WORKSPACE
         L.w_qkv = 4096 + 8
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, 4096, ws_bytes, None) == B.E_ALIGN
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, None, 4096, ws_bytes, None) == B.E_ALIGN
         L.w_qkv = 4096
         L.proxy_logits = None
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, 4096, ws_bytes, None) == B.E_NULL
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 4096, 4096, 1 << 30, None, None, 4096, ws_bytes, None) == B.E_NULL
         L.proxy_logits = 4096
         rows_bytes = 320 * 256 * 4
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 1 << 20, 4096, (1 << 20) + rows_bytes - 16, None, 4096,
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, 1 << 20, 4096, (1 << 20) + rows_bytes - 16, None, None, 4096,
                      ws_bytes, None) == B.E_ARG
-        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, (1 << 20) + rows_bytes - 16, 4096, 1 << 20, None, 4096,
+        assert entry(h, B.ENTRY_FULL, C.byref(L), 64, (1 << 20) + rows_bytes - 16, 4096, 1 << 20, None, None, 4096,
                      ws_bytes, None) == B.E_ARG
         # commit needs a vocabulary
         assert lib.polestar_commit(h, 64, 4096, 4096, None, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096,

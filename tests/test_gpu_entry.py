@@ -8,8 +8,8 @@ proxy logits of the centroids over the fresh cache).  Compared:
   * the recomputed rows of h_out and of the K/V caches (stored values within
     the storage-dtype bounds), every other row bit-identical to what it held;
   * k-means labels and residual codes bit-exact, centroids within the bounds;
-  * the proxy logits within 2e-3 (each side from its own stored cache and
-    centroids).
+  * the proxy logits and (last layer) the active block's attention logits
+    within 2e-3 (each side from its own stored cache and centroids).
 A second layer takes each side's own first-layer output, so its values are
 compared as free-running values.
 """
@@ -98,7 +98,10 @@ def test_block_entry_parity(case):
             Ld.update(win_h=win)
         h_out = torch.full_like(h_in, 3.0)
         obj = torch.zeros(batch, 2 * w.kmeans_iters, dtype=torch.float64, device="cuda")
-        B.polestar_entry(dev.h, mode, layer_struct(Ld), blk_start, h_in, init, h_out, obj, dev.ws, dev.ws_bytes)
+        last = l == n_layers - 1
+        act = torch.full((batch, w.block, hq, n), 5.0, dtype=torch.float32, device="cuda") if last else None
+        B.polestar_entry(dev.h, mode, layer_struct(Ld), blk_start, h_in, init, h_out, obj, act, dev.ws,
+                         dev.ws_bytes)
         torch.cuda.synchronize()
         log(f"[entry] layer {l}: GPU done")
         cmp_rows = assert_stored if l == 0 else (lambda a, b_, dt, name: assert_traj(a, b_, dt, name))
@@ -139,6 +142,16 @@ def test_block_entry_parity(case):
             assert_close(plog[b].cpu().numpy(), pl, f"layer {l} seq {b} proxy logits", dtype=w.dtype)
             if l == 0:
                 assert_close(plog[b].cpu().numpy(), ls["P"], f"seq {b} proxy logits (oracle state)", dtype=w.dtype)
+            if last:
+                # the active block's main-attention logits over the fresh cache: from the GPU's
+                # stored cache by the oracle's definition, and against the oracle's own state
+                jpos = O.active_positions(blk_start, w.block)
+                qg = O.project(np64(h_in[b, jpos]), Wo["wq"], cfg.eps, st).reshape(-1, hq, dh)
+                _, lg = O.attention(qg, kg.reshape(n, hkv, dh), vg.reshape(n, hkv, dh), hq, hkv)
+                assert_close(act[b].cpu().numpy(), lg, f"seq {b} active logits", dtype=w.dtype)
+                qa = O.project(h_or[b][jpos], Wo["wq"], cfg.eps, st).reshape(-1, hq, dh)
+                _, lo = O.attention(qa, Kb, Vb, hq, hkv)
+                assert_close(act[b].cpu().numpy(), lo, f"seq {b} active logits (oracle state)", dtype=w.dtype)
             hn = h_or[b].copy()
             hn[rows] = out_or
             nxt.append(hn)
@@ -174,7 +187,7 @@ def test_entry_graph_replay_matches_eager():
         names = ("k_cache", "v_cache", "win_codes", "win_scales", "win_z", "win_m", "proxy_logits")
 
         def state(out):
-            return [out.clone()] + [L[k].clone() for L in st.layers for k in names]
+            return [out.clone(), st.act_logits.clone()] + [L[k].clone() for L in st.layers for k in names]
 
         want = state(st.entry_forward(blk, h0, inits, full=True))
         s = torch.cuda.Stream()
@@ -187,6 +200,7 @@ def test_entry_graph_replay_matches_eager():
         with torch.cuda.graph(g):
             gout = st.entry_forward(blk, h0, inits, full=True)
         for rep in range(3):
+            st.act_logits.zero_()
             for L in st.layers:
                 for k in names:
                     L[k].zero_()
