@@ -29,7 +29,7 @@ EXPORTED = [
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
     "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
-    "polestar_kv_staleness", "polestar_entry",
+    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -89,6 +89,7 @@ def lib() -> C.CDLL:
         L.polestar_pack_weight.argtypes = [vp, C.c_int, vp, vp, vp]
         L.polestar_cluster.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, C.POINTER(Packet), vp, vp, vp, vp, sz, vp]
         L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.polestar_entry_commit.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
                                      C.POINTER(Packet), vp, vp, vp, sz, vp]
         L.polestar_refresh.argtypes = [vp, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp, vp, vp, vp, vp, sz, vp]
@@ -199,6 +200,14 @@ def polestar_entry(h, mode, layer: Layer, blk_start, h_in, init_idx, h_out, obje
     _ck(lib().polestar_entry(h, mode, C.byref(layer), blk_start, ptr(h_in), ptr(init_idx), ptr(h_out),
                              ptr(objective), ptr(act_logits), ptr(ws), ws_bytes, stream_ptr(stream)),
         "polestar_entry")
+
+
+def polestar_entry_commit(h, blk_start, w_lm, h_full, active_masked, suffix_masked, commit_active, commit_suffix,
+                          conf_active, yhat_active, conf_suffix, ws, ws_bytes, stream=None) -> None:
+    _ck(lib().polestar_entry_commit(h, blk_start, ptr(w_lm), ptr(h_full), ptr(active_masked), ptr(suffix_masked),
+                                    ptr(commit_active), ptr(commit_suffix), ptr(conf_active), ptr(yhat_active),
+                                    ptr(conf_suffix), ptr(ws), ws_bytes, stream_ptr(stream)),
+        "polestar_entry_commit")
 
 
 def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,

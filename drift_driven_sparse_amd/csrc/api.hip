@@ -847,12 +847,14 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   return run_attention<T>(h, a, s);
 }
 
+// With h_full set (block entry): the rows are the active block and the suffix window read from the
+// rows of every position, and the confidence alone decides (no drift, history untouched).
 template <typename T>
 int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_final,
               const polestar_packet* u_final, const float* delta, const uint8_t* active_masked,
               const uint8_t* suffix_masked, float* hist_vals, int32_t* hist_cnt, uint8_t* commit_active,
               uint8_t* commit_suffix, float* conf_active, int32_t* yhat_active, float* spike, float* conf_suffix,
-              void* ws, hipStream_t s) {
+              void* ws, hipStream_t s, const void* h_full = nullptr) {
   const polestar_dims& d = h->dm;
   const WinGeom g = geom_of(h, blk_start);
   const int lm_rows = d.block + d.win_suffix;
@@ -866,6 +868,10 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   lp.n_pre = g.n_pre;
   lp.lm_rows = lm_rows;
   lp.h_final = h_final;
+  lp.h_full = h_full;
+  lp.n_pos = d.n_pos;
+  lp.blk_start = blk_start;
+  lp.n_suf = g.n_win - g.n_pre;
   if (u_final) {
     lp.u_rows = u_final->rows;
     lp.u_idx = u_final->idx;
@@ -933,6 +939,7 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   da.yhat_active = yhat_active;
   da.spike = spike;
   da.conf_suffix = conf_suffix;
+  da.entry = h_full != nullptr;
   PROF(POLESTAR_K_DECIDE);
   return hip_status(launch_decide(da, s));
 }
@@ -1225,6 +1232,28 @@ int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, con
              : do_commit<float>(h, blk_start, w_lm, h_final, u_final, delta, active_masked, suffix_masked,
                                 hist_vals, hist_cnt, commit_active, commit_suffix, conf_active, yhat_active, spike,
                                 conf_suffix, ws, s);
+}
+
+int polestar_entry_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_full,
+                          const uint8_t* active_masked, const uint8_t* suffix_masked, uint8_t* commit_active,
+                          uint8_t* commit_suffix, float* conf_active, int32_t* yhat_active, float* conf_suffix,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !w_lm || !h_full || !active_masked || !suffix_masked || !commit_active || !commit_suffix ||
+      !conf_active || !yhat_active || !conf_suffix)
+    return POLESTAR_E_NULL;
+  if (h->dm.vocab <= 0) return POLESTAR_E_SHAPE;
+  int rc = check_ws(h, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_blk(h, blk_start))) return rc;
+  if (!aligned16(w_lm) || !aligned16(h_full)) return POLESTAR_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  return h->dm.dtype == POLESTAR_BF16
+             ? do_commit<bf16_t>(h, blk_start, w_lm, nullptr, nullptr, nullptr, active_masked, suffix_masked, nullptr,
+                                 nullptr, commit_active, commit_suffix, conf_active, yhat_active, nullptr,
+                                 conf_suffix, ws, s, h_full)
+             : do_commit<float>(h, blk_start, w_lm, nullptr, nullptr, nullptr, active_masked, suffix_masked, nullptr,
+                                nullptr, commit_active, commit_suffix, conf_active, yhat_active, nullptr,
+                                conf_suffix, ws, s, h_full);
 }
 
 int polestar_should_refresh(int32_t decoded_since_refresh, int32_t tau_upd) {

@@ -11,10 +11,11 @@ __global__ __launch_bounds__(256) void lm_prep_kernel(LmPrepArgs a, int32_t* met
   __shared__ int p0_sh, cnt_sh;
   const int r = blockIdx.x, b = blockIdx.y, d = a.d;
   if (threadIdx.x == 0) {
-    int cnt = a.u_count ? a.u_count[b] : 0;
+    int cnt = a.h_full ? a.n_suf : (a.u_count ? a.u_count[b] : 0);
     cnt = cnt < 0 ? 0 : (cnt > a.win_max ? a.win_max : cnt);
     int p0 = 0;
-    while (p0 < cnt && a.u_idx[(int64_t)b * a.win_max + p0] < a.n_pre) ++p0;
+    if (!a.h_full)
+      while (p0 < cnt && a.u_idx[(int64_t)b * a.win_max + p0] < a.n_pre) ++p0;
     p0_sh = p0;
     cnt_sh = cnt;
     if (r == 0) {
@@ -24,7 +25,11 @@ __global__ __launch_bounds__(256) void lm_prep_kernel(LmPrepArgs a, int32_t* met
   }
   __syncthreads();
   const T* src;
-  if (r < a.block) {
+  if (a.h_full) {
+    // block entry: the active rows, then the suffix rows, read at their positions
+    if (r >= a.block + cnt_sh) return;
+    src = (const T*)a.h_full + ((int64_t)b * a.n_pos + a.blk_start + r) * d;
+  } else if (r < a.block) {
     src = (const T*)a.h_final + ((int64_t)b * a.block + r) * d;
   } else {
     const int j = p0_sh + (r - a.block);
@@ -60,6 +65,12 @@ __global__ __launch_bounds__(64) void decide_kernel(DecideArgs a, const int32_t*
     int y;
     combine_stats(a.lm_stats + ((int64_t)b * a.lm_rows + j) * a.lm_tiles * 4, a.lm_tiles, &c, &y);
     const int64_t row = (int64_t)b * a.block + j;
+    if (a.entry) {   // no drift at block entry: the confidence alone decides
+      a.commit_active[row] = (a.active_masked[row] != 0 && c >= a.tau_s) ? 1 : 0;
+      a.conf_active[row] = c;
+      a.yhat_active[row] = y;
+      continue;
+    }
     float* hv = a.hist_vals + row * H;
     const int cnt = a.hist_cnt[row];
     float mean = 0.f;
@@ -97,8 +108,7 @@ __global__ __launch_bounds__(64) void decide_kernel(DecideArgs a, const int32_t*
     float c;
     int y;
     combine_stats(a.lm_stats + ((int64_t)b * a.lm_rows + a.block + i) * a.lm_tiles * 4, a.lm_tiles, &c, &y);
-    const int w = a.u_idx[(int64_t)b * a.win_max + p0 + i];
-    const int slot = w - a.n_pre;
+    const int slot = a.entry ? i : a.u_idx[(int64_t)b * a.win_max + p0 + i] - a.n_pre;
     if (slot < 0 || slot >= a.win_suffix) continue;
     const int64_t o = (int64_t)b * a.win_suffix + slot;
     a.conf_suffix[o] = c;

@@ -310,6 +310,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 struct LmPrepArgs {
   int32_t batch, d, block, win_max, win_suffix, n_pre, lm_rows;
   const void* h_final; const void* u_rows; const int32_t* u_idx; const int32_t* u_count;
+  // block entry (h_full set): rows of every position [batch][n_pos][d]; the active rows sit at
+  // blk_start.., the n_suf suffix rows right after them
+  const void* h_full; int32_t n_pos, blk_start, n_suf;
   void* a_lm; int32_t* meta; float eps;   // a_lm: round(RMSNorm(row)); meta: rows per sequence, suffix start
 };
 template <typename T>
@@ -323,6 +326,8 @@ struct DecideArgs {
   float* hist_vals; int32_t* hist_cnt;
   uint8_t* commit_active; uint8_t* commit_suffix; float* conf_active; int32_t* yhat_active;
   float* spike; float* conf_suffix;
+  int32_t entry;   // block entry: confidence alone decides (no drift, history untouched); suffix
+                   // row i is suffix slot i
 };
 hipError_t launch_decide(const DecideArgs& a, hipStream_t s);
 

@@ -312,6 +312,25 @@ int polestar_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, con
                     int32_t* yhat_active, float* spike, float* conf_suffix,
                     void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * polestar_entry_commit — the commit at block entry [§4.2 "Current Block
+ * Commit" and "Suffix Block Commit"; Algorithm 1 block entry].  After the
+ * entry forward there is no drift yet, so the confidence alone decides:
+ * active row j commits when masked and c >= tau_s; suffix window row i
+ * (positions blk_start + B + i, all of them fresh from the forward) commits
+ * when masked and c >= tau_suf.  Confidences as in polestar_commit, read from
+ * the last layer's output h_full [batch, n_pos, d] (storage dtype, device) at
+ * those positions.  Drift history and spikes are not touched.  Outputs:
+ * commit_active [batch, B] u8, conf_active [batch, B] f32, yhat_active
+ * [batch, B] i32, commit_suffix / conf_suffix [batch, win_suffix] (0 past the
+ * sequence end).  Masks as in polestar_commit.  Needs a vocabulary
+ * (POLESTAR_E_SHAPE otherwise).
+ */
+int polestar_entry_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const void* h_full,
+                          const uint8_t* active_masked, const uint8_t* suffix_masked, uint8_t* commit_active,
+                          uint8_t* commit_suffix, float* conf_active, int32_t* yhat_active, float* conf_suffix,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* ---- per-kernel timing (diagnostics) ------------------------------------ */
 enum {
   POLESTAR_K_CLUSTER = 0, POLESTAR_K_PREP, POLESTAR_K_QKV, POLESTAR_K_ATTN, POLESTAR_K_TOPK,

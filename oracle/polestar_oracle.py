@@ -704,6 +704,14 @@ def commit_decide(delta, conf, masked, hist_vals, hist_cnt, hist_len, alpha, tau
     return commit, spike, taud, hv, hc
 
 
+def entry_commit(conf, masked, tau):
+    """Commit at block entry [§4.2; Algorithm 1 block entry]: there is no drift yet,
+    so a masked row commits when its confidence reaches the threshold (tau_s for the
+    active block, tau_suf for the suffix window), compared in float32."""
+    conf = np.asarray(conf, dtype=np.float32)
+    return (np.asarray(masked, dtype=bool) & (conf >= np.float32(tau))).astype(np.uint8)
+
+
 def suffix_commit(conf, eligible, tau_suf):
     conf = np.asarray(conf, dtype=np.float32)
     return (np.asarray(eligible, dtype=bool) & (conf >= np.float32(tau_suf))).astype(np.uint8)

@@ -129,6 +129,11 @@ def test_calls_validate_before_launching():
                      ws_bytes, None) == B.E_ARG
         assert entry(h, B.ENTRY_FULL, C.byref(L), 64, (1 << 20) + rows_bytes - 16, 4096, 1 << 20, None, None, 4096,
                      ws_bytes, None) == B.E_ARG
+        # the entry commit needs its outputs and a vocabulary
+        assert lib.polestar_entry_commit(h, 64, 4096, 4096, 4096, 4096, None, 4096, 4096, 4096, 4096, 4096,
+                                         ws_bytes, None) == B.E_NULL
+        assert lib.polestar_entry_commit(h, 64, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096,
+                                         ws_bytes, None) == B.E_SHAPE
         # commit needs a vocabulary
         assert lib.polestar_commit(h, 64, 4096, 4096, None, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096,
                                    4096, 4096, 4096, ws_bytes, None) == B.E_SHAPE

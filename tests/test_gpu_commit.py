@@ -156,3 +156,79 @@ def test_commit_parity(case):
     finally:
         dev.close()
     log(f"[commit] case={case} passed")
+
+
+ENTRY_CASES = {
+    # name: (workload, batch, blk_start)
+    "llada_full_vocab_entry_batch2": (synth.shrink(synth.WORKLOADS[5], resid="raw"), 2, 512),
+    "small_ragged_vocab_entry_suffix_cut": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64,
+                                                         gen=128), 2, 144),
+    "small_ragged_vocab_entry_at_end": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64,
+                                                     gen=128), 1, 160),
+}
+
+
+@pytest.mark.parametrize("case", list(ENTRY_CASES))
+def test_entry_commit_parity(case):
+    """Block-entry commit: confidences of the active rows and of every suffix window row, read at
+    their positions in the rows of all positions; decisions by confidence alone."""
+    w, batch, blk_start = ENTRY_CASES[case]
+    dev = Dev(w, batch=batch)
+    d, Bk, V, n = w.d, w.block, w.vocab, w.n_pos
+    mask_id = V - 1
+    log(f"[entry-commit] case={case} d={d} vocab={V} batch={batch} blk_start={blk_start}")
+    try:
+        g = O.window_positions(blk_start, n, Bk, w.win_prefix, w.win_suffix)
+        n_suf = int(np.sum(g >= blk_start + Bk))
+        seed = w.seed(0)
+        wlm = synth.weight(w, 0, "wlm", device="cuda")
+        w_lm = dev.pack(B.W_LM, wlm)
+        # rows of every position, with planted rows near W_lm rows in the active block and suffix
+        h_full = synth.tensor(w, (91, 1), (batch, n, d), 1.0, device="cuda", dtype="f32")
+        target = np.log(V) + 0.5 + np.log(9.0)
+        l0 = np.sqrt(max((np.sqrt(d) / target) ** 2 - 1.0, 0.01))
+        rows_of = np.arange(blk_start, blk_start + Bk + n_suf)
+        for b in range(batch):
+            for i, f in enumerate([0.6, 0.85, 0.94, 0.99, 1.04, 1.11, 1.33, 1.7, 0.9, 1.0]):
+                p = int(rows_of[(5 * i + 2 * b) % len(rows_of)])
+                v = int(synth.hash32_int(seed + 41 * b + i) % (V - 1))
+                h_full[b, p] = wlm[v].float() * np.sqrt(d) + (l0 * f) * h_full[b, p]
+            h_full[b, blk_start] = wlm[mask_id].float() * np.sqrt(d)   # argmax must skip the mask id
+        h_full = h_full.to(torch.bfloat16).contiguous()
+        rng = np.random.default_rng(seed + 5)
+        act_mask = torch.tensor(rng.integers(0, 2, size=(batch, Bk)), dtype=torch.uint8)
+        act_mask[:, :4] = 1
+        suf_mask = torch.tensor(rng.integers(0, 2, size=(batch, max(w.win_suffix, 1))), dtype=torch.uint8)
+        outs = dict(commit_active=torch.zeros(batch, Bk, dtype=torch.uint8),
+                    commit_suffix=torch.full((batch, w.win_suffix), 7, dtype=torch.uint8),
+                    conf_active=torch.zeros(batch, Bk), yhat=torch.zeros(batch, Bk, dtype=torch.int32),
+                    conf_suffix=torch.full((batch, w.win_suffix), -1.0))
+        outs = {k: v.cuda() for k, v in outs.items()}
+        B.polestar_entry_commit(dev.h, blk_start, w_lm, h_full, act_mask.cuda(), suf_mask.cuda(),
+                                outs["commit_active"], outs["commit_suffix"], outs["conf_active"], outs["yhat"],
+                                outs["conf_suffix"], dev.ws, dev.ws_bytes)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in outs.items()}
+        for b in range(batch):
+            lg = _lm_logits(w, np64(h_full[b, rows_of]), w.rms_eps)
+            c, yhat = O.confidence_from_logits(lg, mask_id)
+            ca, cs = c[:Bk], c[Bk:]
+            err = np.abs(got["conf_active"][b] - ca) / np.maximum(ca, 1e-30)
+            assert err.max() <= 2e-3, f"seq {b}: active confidence rel err {err.max():.3e}"
+            assert np.array_equal(got["yhat"][b], yhat[:Bk]), f"seq {b}: argmax ids differ"
+            assert got["yhat"][b][0] != mask_id
+            assert (ca >= w.tau_s).any() or (cs >= w.tau_suf).any(), "planted rows should reach the thresholds"
+            es = np.abs(got["conf_suffix"][b][:n_suf] - cs) / np.maximum(cs, 1e-30)
+            assert es.size == 0 or es.max() <= 2e-3, f"seq {b}: suffix confidence rel err {es.max():.3e}"
+            assert np.all(got["conf_suffix"][b][n_suf:] == 0) and np.all(got["commit_suffix"][b][n_suf:] == 0)
+            # the rule on the GPU's confidences, bit-exact
+            assert np.array_equal(got["commit_active"][b],
+                                  O.entry_commit(got["conf_active"][b], act_mask[b].numpy(), w.tau_s))
+            assert np.array_equal(got["commit_suffix"][b][:n_suf],
+                                  O.entry_commit(got["conf_suffix"][b][:n_suf], suf_mask[b, :n_suf].numpy(),
+                                                 w.tau_suf))
+            log(f"    seq {b}: {int(got['commit_active'][b].sum())} active and "
+                f"{int(got['commit_suffix'][b].sum())} suffix commits of {Bk} + {n_suf} rows")
+    finally:
+        dev.close()
+    log(f"[entry-commit] case={case} passed")

@@ -579,6 +579,22 @@ def test_suffix_commit_rule():
     assert out.tolist() == [1, 1, 0, 0]
 
 
+def test_entry_commit_rule():
+    # hand cases: the threshold itself commits, one float32 step below does not, unmasked never
+    f = np.float32
+    c = [f(0.9), np.nextafter(f(0.9), f(0)), f(0.99), f(0.99)]
+    assert O.entry_commit(c, [1, 1, 1, 0], 0.9).tolist() == [1, 0, 1, 0]
+    # the in-block rule with no drift and an empty history reduces to it: spike 0 never exceeds
+    # tau_d = alpha (tau_s - c)^2 >= 0, so only the confidence can commit
+    rng = np.random.default_rng(88)
+    for alpha in (2.0, 10.0, 40.0):
+        conf = rng.uniform(0.5, 1.0, size=64).astype(np.float32)
+        masked = rng.integers(0, 2, size=64)
+        com, _, _, _, _ = O.commit_decide(np.zeros(64), conf, masked, np.zeros((64, 5)), np.zeros(64, dtype=int), 5,
+                                          alpha, 0.9)
+        assert np.array_equal(O.entry_commit(conf, masked, 0.9), com)
+
+
 # ---------------------------------------------------------------- the k = K identity
 def _tiny_stack(n_layers, d=32, hq=4, hkv=2, dh=8, f=48, seed=7):
     rng = np.random.default_rng(seed)
