@@ -222,7 +222,10 @@ int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int3
  * Algorithm 1 forward of the active block, ProxyAttn, KL, TopK, S = M[K]].
  *  REFRESH: projects [active rows h_active [batch, B, d]; window rows; the
  *    centroids] with W_Q/W_K/W_V (RMSNorm with unit gain), writes the active
- *    block's K/V and the K/V of the packet rows u_in into the layer's cache,
+ *    block's K/V and the K/V of the packet rows into the layer's cache (the
+ *    window rows that the preceding polestar_cluster(UPDATE) on the same
+ *    workspace patched from its packet; u_in itself is not read and may be
+ *    NULL),
  *    runs softmax attention of the active and window rows over all n_pos
  *    keys, runs proxy attention of the centroid queries over the same keys,
  *    scores each cluster by D_c = sum over heads of max(0, KL(P_t || P_prev))
