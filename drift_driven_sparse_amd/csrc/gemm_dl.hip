@@ -251,6 +251,21 @@ __global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
   const float* p = g.part + ((int64_t)b * g.part_rows + r) * g.N + c;
   const float4 v = sum_splits(p, sstride, g.ksplit);
   const float vv[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (KIND == EPI_QKV) {
+    // four columns of one kind (nq and nkv are multiples of 4): queries and keys are contiguous
+    // in their outputs and take one store; values (transposed cache) go element by element
+    const EpiParams& e = g.e;
+    if (c < e.nq + e.nkv) {
+      if (e.chk) *(float4*)(e.chk + ((int64_t)b * e.chk_rows + r) * e.chk_ld + c) = v;
+      if (c < e.nq) {
+        *(float4*)(e.q + ((int64_t)b * e.q_rows + r) * e.nq + c) = v;
+      } else {
+        const int pos = qkv_pos(e, b, r);
+        if (pos >= 0) Quad<T>::store((T*)e.kc + kv_index(e, b, pos, c - e.nq, 0), vv);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, r, c + i, vv[i]);

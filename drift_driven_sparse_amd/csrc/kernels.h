@@ -109,6 +109,14 @@ PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
 // QKV projection row r (active block, window rows, centroids) of the rounded normalised row,
 // column n, sum v: queries stay float32; K/V of the active block and of patched window rows go
 // to the cache.
+// Cache position whose K/V QKV row r writes: the active block's, or a patched window row's; -1:
+// none (unpatched window rows, centroids).
+PS_DEV int qkv_pos(const EpiParams& e, int b, int r) {
+  if (r < e.block) return e.geom.blk_start + r;
+  const int w = r - e.block;
+  return (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) ? e.geom.pos(w) : -1;
+}
+
 template <typename T>
 PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
   if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
@@ -119,13 +127,7 @@ PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
   const int kv = n - e.nq;
   const int which = kv >= e.nkv;
   const int col = kv - which * e.nkv;
-  int pos = -1;
-  if (r < e.block) {
-    pos = e.geom.blk_start + r;
-  } else {
-    const int w = r - e.block;
-    if (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) pos = e.geom.pos(w);
-  }
+  const int pos = qkv_pos(e, b, r);
   if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
 }
 
