@@ -564,6 +564,16 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ int chosen[16];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.refresh) {
+    // wave 0 loads the window labels first, so that their round trip overlaps the drift sums
+    constexpr int kLab = 4;   // labels per lane: n_win <= 256
+    int lab[kLab];
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < kLab; ++i) {
+        const int w = 64 * i + lane;
+        lab[i] = w < a.n_win ? a.win_m[(int64_t)b * a.win_max + w] : -1;
+      }
+    }
     const int keff = min(a.K, a.n_win);
     for (int c = wave; c < a.K; c += 4) {
       float s = 0.f;
@@ -589,9 +599,10 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __syncthreads();
     if (wave == 0) {
       int base = 0;
-      for (int w0 = 0; w0 < a.n_win; w0 += 64) {
-        const int w = w0 + lane;
-        const int c = w < a.n_win ? a.win_m[(int64_t)b * a.win_max + w] : -1;
+#pragma unroll
+      for (int i = 0; i < kLab; ++i) {
+        const int w = 64 * i + lane;
+        const int c = lab[i];
         const bool sel = c >= 0 && c < a.K && chosen[c];
         const unsigned long long m = __ballot(sel);
         const int before = __popcll(m & ((1ull << lane) - 1ull));

@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
   const int w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int d = a.d;
   const int64_t wbase = (int64_t)b * a.win_max;
+  int c = a.win_m[wbase + w];   // issued first: its round trip overlaps the packet search
   int cnt = a.u_count ? a.u_count[b] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.win_max ? a.win_max : cnt);
   if (tid == 0) pr_sh = -1;
@@ -278,7 +279,6 @@ __global__ __launch_bounds__(256) void window_rows_kernel(ClusterArgs a) {
     if (a.u_idx[wbase + r] == w) atomicMax(&pr_sh, r);
   __syncthreads();
   const int pr = pr_sh;
-  int c = a.win_m[wbase + w];
   c = (c < 0 || c >= a.K) ? 0 : c;
   const T* zc = (const T*)a.win_z + ((int64_t)b * a.K + c) * d;
   T* rows = (T*)a.ws_rows;
