@@ -241,6 +241,8 @@ constexpr int kChunk = 256;
 PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* rinv, int* wcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t wbase = (int64_t)b * a.win_max;
+  // the norm is loaded with the label (one round trip for both)
+  const double nr = (rinv && tid < a.geom.n_win) ? a.wnorm[wbase + tid] : 0.0;
   const bool in = tid < a.geom.n_win && a.win_m[wbase + tid] == c;
   const unsigned long long m = __ballot(in);
   if (lane == 0) wcnt[wave] = __popcll(m);
@@ -253,10 +255,7 @@ PS_DEV int members_of(const ClusterArgs& a, int b, int c, int* mem, double* rinv
   if (in) {
     const int pos = off + __popcll(m & ((1ull << lane) - 1ull));
     mem[pos] = tid;
-    if (rinv) {
-      const double nr = a.wnorm[wbase + tid];
-      rinv[pos] = nr > 0.0 ? 1.0 / nr : 0.0;
-    }
+    if (rinv) rinv[pos] = nr > 0.0 ? 1.0 / nr : 0.0;
   }
   __syncthreads();
   return tot;
@@ -350,10 +349,16 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
   __shared__ double gsh[kGather];
   const int ch = blockIdx.x, c = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = a.d, n0 = ch * kChunk, n = n0 + tid;
+  const int64_t zrow = (int64_t)b * a.K + c;
+  // chunk partials loaded before the labels, so the two round trips overlap (nchunk <= 256)
+  const double cpv = tid < a.nchunk ? a.cpart[zrow * a.nchunk + tid] : 0.0;
   const int nmem = members_of(a, b, c, mem, nullptr, wcnt);
   if (nmem == 0) return;   // no members: the centroid is kept and no row refers to it
-  const int64_t zrow = (int64_t)b * a.K + c;
-  const double ns = sqrt(gather_sum(a.cpart + zrow * a.nchunk, a.nchunk, gsh));
+  if (tid < a.nchunk) gsh[tid] = cpv;
+  __syncthreads();
+  double ss = 0.0;
+  for (int i = 0; i < a.nchunk; ++i) ss += gsh[i];   // chunk order
+  const double ns = sqrt(ss);
   T* zc = (T*)a.win_z + zrow * d;
   if (n < d) {
     if (ns > 0.0) St<T>::store_d(zc, n, a.z64[zrow * d + n] / ns);   // kept when the sum vanishes
@@ -453,7 +458,7 @@ hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(km_store_kernel<T>, dim3(a.K, a.batch), dim3(256), 0, s, a);
     if (a.resid) hipLaunchKernelGGL(km_resid_kernel<T>, dim3(nwin, a.batch), dim3(256), 0, s, a);
   } else {
-    if (a.nchunk > kGather) return hipErrorInvalidValue;
+    if (a.nchunk > 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL(window_rows_kernel<T>, dim3(a.geom.n_win, a.batch), dim3(256), 0, s, a);
     const dim3 g(a.nchunk, a.K, a.batch);
     hipLaunchKernelGGL(centroid_sum_kernel<T>, g, dim3(256), 0, s, a);
