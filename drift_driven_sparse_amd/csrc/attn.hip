@@ -433,14 +433,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-// KL(softmax(s) || softmax(sp)) over n logits held by one wavefront (s staged, sp in
-// place), evaluated through the logit differences so that the result keeps its
-// relative accuracy when the two distributions are close:
-//   u_j = exp(sp_j - max sp), e_j = (s_j - sp_j) - mean_u(s - sp),
-//   S0 = sum u, S1 = sum u expm1(e), S2 = sum u exp(e) e,
-//   KL = (S2/S0) / (1 + S1/S0) - log1p(S1/S0)   (invariant to the shift of e).
-// The n <= 1024 logits of one (row, head) sit in registers (16 per lane, lane + 64 i), so
-// the three passes read memory once; per-lane sums run in i order, then a wavefront sum.
 constexpr int kKlPer = 4;   // logits per thread of a 256-thread workgroup (n_pos <= 1024)
 
 // Block-wide max (fixed combination order); every thread gets the result.
