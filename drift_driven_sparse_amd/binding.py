@@ -29,7 +29,7 @@ EXPORTED = [
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
     "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
-    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit",
+    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit", "polestar_step",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -89,6 +89,8 @@ def lib() -> C.CDLL:
         L.polestar_pack_weight.argtypes = [vp, C.c_int, vp, vp, vp]
         L.polestar_cluster.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, C.POINTER(Packet), vp, vp, vp, vp, sz, vp]
         L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.polestar_step.argtypes = [vp, C.c_int, i32, C.POINTER(Layer), i32, vp, vp, C.POINTER(Packet),
+                                    C.POINTER(Packet), vp, vp, vp, vp, vp, sz, vp]
         L.polestar_entry_commit.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
                                      C.POINTER(Packet), vp, vp, vp, sz, vp]
@@ -208,6 +210,14 @@ def polestar_entry_commit(h, blk_start, w_lm, h_full, active_masked, suffix_mask
                                     ptr(commit_active), ptr(commit_suffix), ptr(conf_active), ptr(yhat_active),
                                     ptr(conf_suffix), ptr(ws), ws_bytes, stream_ptr(stream)),
         "polestar_entry_commit")
+
+
+def polestar_step(h, mode, layers, blk_start, h_act0, h_act1, pk0: Packet, pk1: Packet, D, topk, act_logits, delta,
+                  ws, ws_bytes, stream=None) -> None:
+    arr = (Layer * len(layers))(*layers)
+    _ck(lib().polestar_step(h, mode, len(layers), arr, blk_start, ptr(h_act0), ptr(h_act1), C.byref(pk0),
+                            C.byref(pk1), ptr(D), ptr(topk), ptr(act_logits), ptr(delta), ptr(ws), ws_bytes,
+                            stream_ptr(stream)), "polestar_step")
 
 
 def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,

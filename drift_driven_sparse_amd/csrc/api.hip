@@ -1122,9 +1122,9 @@ int polestar_pack_weight(const polestar_handle* h, int which, const void* src, v
   return hip_status(e);
 }
 
-int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
-                     const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, double* objective,
-                     void* ws, size_t ws_bytes, void* stream) {
+static int check_cluster(const polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                         const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, const void* ws,
+                         size_t ws_bytes) {
   if (!h || !L) return POLESTAR_E_NULL;
   if (mode != POLESTAR_CLUSTER_ENTRY && mode != POLESTAR_CLUSTER_UPDATE) return POLESTAR_E_ARG;
   int rc = check_ws(h, ws, ws_bytes);
@@ -1139,15 +1139,23 @@ int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int3
   if (!aligned16(L->win_z) || (!nv && !aligned16(L->win_h)) || (entry_h && !aligned16(entry_h)) ||
       (u_in && !aligned16(u_in->rows)))
     return POLESTAR_E_ALIGN;
+  return POLESTAR_OK;
+}
+
+int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                     const polestar_packet* u_in, const int32_t* init_idx, const void* entry_h, double* objective,
+                     void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_cluster(h, mode, L, blk_start, u_in, init_idx, entry_h, ws, ws_bytes);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
              ? do_cluster<bf16_t>(h, mode, L, blk_start, u_in, init_idx, entry_h, objective, ws, s)
              : do_cluster<float>(h, mode, L, blk_start, u_in, init_idx, entry_h, objective, ws, s);
 }
 
-int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
-                   const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
-                   float* delta, void* ws, size_t ws_bytes, void* stream) {
+static int check_drift(const polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start,
+                       const void* h_active, const polestar_packet* u_in, const polestar_packet* sel,
+                       const float* act_logits, const float* delta, const void* ws, size_t ws_bytes) {
   if (!h || !L || !h_active || !sel || !sel->idx || !sel->count) return POLESTAR_E_NULL;
   if (mode != POLESTAR_DRIFT_REFRESH && mode != POLESTAR_DRIFT_ACTIVE_ONLY) return POLESTAR_E_ARG;
   int rc = check_ws(h, ws, ws_bytes);
@@ -1159,15 +1167,24 @@ int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_
   if (mode == POLESTAR_DRIFT_REFRESH && !aligned16(L->win_z)) return POLESTAR_E_ALIGN;
   if (delta && !act_logits) return POLESTAR_E_NULL;
   if (u_in && (!u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
+  return POLESTAR_OK;
+}
+
+int polestar_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                   const polestar_packet* u_in, float* D, int32_t* topk, polestar_packet* sel, float* act_logits,
+                   float* delta, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_drift(h, mode, L, blk_start, h_active, u_in, sel, act_logits, delta, ws, ws_bytes);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   return h->dm.dtype == POLESTAR_BF16
              ? do_drift<bf16_t>(h, mode, L, blk_start, h_active, u_in, D, topk, sel, act_logits, delta, ws, s)
              : do_drift<float>(h, mode, L, blk_start, h_active, u_in, D, topk, sel, act_logits, delta, ws, s);
 }
 
-int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
-                     const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
-                     void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream) {
+static int check_refresh(const polestar_handle* h, const polestar_layer* L, int32_t blk_start,
+                         const void* h_active, const polestar_packet* sel, const void* w_kv_next,
+                         const void* k_next, const void* v_next, const void* h_active_out, const void* u_rows,
+                         const void* ws, size_t ws_bytes) {
   if (!h || !L || !h_active || !sel || !sel->idx || !sel->count || !h_active_out || !u_rows) return POLESTAR_E_NULL;
   int rc = check_ws(h, ws, ws_bytes);
   if (rc) return rc;
@@ -1177,11 +1194,69 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
   if (!aligned16(L->w_o) || !aligned16(L->w_gu) || !aligned16(L->w_down) || !aligned16(h_active) ||
       !aligned16(h_active_out) || !aligned16(u_rows) || (w_kv_next && !aligned16(w_kv_next)))
     return POLESTAR_E_ALIGN;
+  return POLESTAR_OK;
+}
+
+int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, const void* h_active,
+                     const polestar_packet* sel, const void* w_kv_next, void* k_next, void* v_next,
+                     void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_refresh(h, L, blk_start, h_active, sel, w_kv_next, k_next, v_next, h_active_out, u_rows, ws,
+                               ws_bytes);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int64_t bs = (int64_t)h->dm.block * h->dm.d;
   const TokRows t = {h->dm.block, h_active, bs, h_active_out, bs, sel, u_rows, true};
   return h->dm.dtype == POLESTAR_BF16 ? do_refresh<bf16_t>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s)
                                       : do_refresh<float>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s);
+}
+
+int polestar_step(polestar_handle* h, int mode, int32_t n_layers, const polestar_layer* layers, int32_t blk_start,
+                  void* h_act0, void* h_act1, polestar_packet* pk0, polestar_packet* pk1, float* D, int32_t* topk,
+                  float* act_logits, float* delta, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !layers || !h_act0 || !h_act1 || !pk0 || !pk1 || !pk0->rows || !pk1->rows) return POLESTAR_E_NULL;
+  if (n_layers < 1) return POLESTAR_E_ARG;
+  if (mode != POLESTAR_DRIFT_REFRESH && mode != POLESTAR_DRIFT_ACTIVE_ONLY) return POLESTAR_E_ARG;
+  void* act[2] = {h_act0, h_act1};
+  polestar_packet* pk[2] = {pk0, pk1};
+  const bool refresh = mode == POLESTAR_DRIFT_REFRESH;
+  // every call of the step is validated before the first launch
+  for (int l = 0; l < n_layers; ++l) {
+    const polestar_layer* L = &layers[l];
+    const bool last = l == n_layers - 1;
+    const polestar_packet* u_in = refresh && l > 0 ? pk[(l - 1) % 2] : nullptr;
+    int rc;
+    if (refresh && (rc = check_cluster(h, POLESTAR_CLUSTER_UPDATE, L, blk_start, u_in, nullptr, nullptr, ws, ws_bytes)))
+      return rc;
+    if ((rc = check_drift(h, mode, L, blk_start, act[l % 2], u_in, pk[l % 2], last ? act_logits : nullptr,
+                          last ? delta : nullptr, ws, ws_bytes)))
+      return rc;
+    if ((rc = check_refresh(h, L, blk_start, act[l % 2], pk[l % 2], nullptr, nullptr, nullptr, act[(l + 1) % 2],
+                            pk[l % 2]->rows, ws, ws_bytes)))
+      return rc;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = h->dm.dtype == POLESTAR_BF16;
+  const int64_t bs = (int64_t)h->dm.block * h->dm.d;
+  for (int l = 0; l < n_layers; ++l) {
+    const polestar_layer* L = &layers[l];
+    const bool last = l == n_layers - 1;
+    const polestar_packet* u_in = refresh && l > 0 ? pk[(l - 1) % 2] : nullptr;
+    float* al = last ? act_logits : nullptr;
+    float* dl = last ? delta : nullptr;
+    int rc = POLESTAR_OK;
+    if (refresh)
+      rc = bf ? do_cluster<bf16_t>(h, POLESTAR_CLUSTER_UPDATE, L, blk_start, u_in, nullptr, nullptr, nullptr, ws, s)
+              : do_cluster<float>(h, POLESTAR_CLUSTER_UPDATE, L, blk_start, u_in, nullptr, nullptr, nullptr, ws, s);
+    if (rc) return rc;
+    rc = bf ? do_drift<bf16_t>(h, mode, L, blk_start, act[l % 2], u_in, D, topk, pk[l % 2], al, dl, ws, s)
+            : do_drift<float>(h, mode, L, blk_start, act[l % 2], u_in, D, topk, pk[l % 2], al, dl, ws, s);
+    if (rc) return rc;
+    const TokRows t = {h->dm.block, act[l % 2], bs, act[(l + 1) % 2], bs, pk[l % 2], pk[l % 2]->rows, true};
+    rc = bf ? do_refresh<bf16_t>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s)
+            : do_refresh<float>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s);
+    if (rc) return rc;
+  }
+  return POLESTAR_OK;
 }
 
 int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,

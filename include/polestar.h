@@ -264,6 +264,27 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
                      void* h_active_out, void* u_rows, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * polestar_step — one denoising step over a stack of n_layers layers, the
+ * composition of the per-layer calls above in one call [Algorithm 1 layer
+ * loop; §4.1].  layers: host array [n_layers].  Layer l reads its active rows
+ * from buffer l % 2 of (h_act0, h_act1) ([batch, B, d] storage dtype, device;
+ * h_act0 holds layer 0's input) and writes them to the other; the output is in
+ * buffer n_layers % 2.  mode POLESTAR_DRIFT_REFRESH: per layer,
+ * polestar_cluster(UPDATE) with the previous layer's packet (none for layer
+ * 0), polestar_drift(REFRESH) selecting into packet l % 2 of (pk0, pk1), and
+ * polestar_refresh writing that packet's rows (its rows buffer
+ * [batch, win_max, d]); POLESTAR_DRIFT_ACTIVE_ONLY: drift and refresh of the
+ * active rows only.  D and topk (nullable) end with the last layer's values;
+ * act_logits and delta (nullable) are used by the last layer as in
+ * polestar_drift.  Every call is validated before the first launch (same
+ * codes as the single calls); then the launches equal those of the single
+ * calls issued in this order.
+ */
+int polestar_step(polestar_handle* h, int mode, int32_t n_layers, const polestar_layer* layers, int32_t blk_start,
+                  void* h_act0, void* h_act1, polestar_packet* pk0, polestar_packet* pk1, float* D, int32_t* topk,
+                  float* act_logits, float* delta, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * polestar_entry — block-entry state of one layer [§4.1 "Update Schedule"
  * (a whole-sequence forward at every other block entry) and "Cluster and
  * Quantize Hidden States"; Algorithm 1 block entry].

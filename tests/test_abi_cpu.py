@@ -129,6 +129,18 @@ def test_calls_validate_before_launching():
                      ws_bytes, None) == B.E_ARG
         assert entry(h, B.ENTRY_FULL, C.byref(L), 64, (1 << 20) + rows_bytes - 16, 4096, 1 << 20, None, None, 4096,
                      ws_bytes, None) == B.E_ARG
+        # the whole-stack step: layer count, mode, and every layer validated before any launch
+        pk = B.Packet(rows=4096, idx=4096, count=4096)
+        arr = (B.Layer * 2)(B.Layer(), B.Layer())
+        step = lib.polestar_step
+        assert step(h, B.DRIFT_REFRESH, 0, arr, 64, 4096, 4096, C.byref(pk), C.byref(pk), None, None, None, None,
+                    4096, ws_bytes, None) == B.E_ARG
+        assert step(h, 9, 2, arr, 64, 4096, 4096, C.byref(pk), C.byref(pk), None, None, None, None, 4096, ws_bytes,
+                    None) == B.E_ARG
+        assert step(h, B.DRIFT_REFRESH, 2, None, 64, 4096, 4096, C.byref(pk), C.byref(pk), None, None, None, None,
+                    4096, ws_bytes, None) == B.E_NULL
+        assert step(h, B.DRIFT_ACTIVE_ONLY, 2, arr, 64, 4096, 4096, C.byref(pk), C.byref(pk), None, None, None,
+                    None, 4096, ws_bytes, None) == B.E_NULL      # layers without weights
         # the entry commit needs its outputs and a vocabulary
         assert lib.polestar_entry_commit(h, 64, 4096, 4096, 4096, 4096, None, 4096, 4096, 4096, 4096, 4096,
                                          ws_bytes, None) == B.E_NULL

@@ -112,3 +112,50 @@ def test_stack_graph_replay_matches_eager():
     finally:
         st.close()
     log("[stack] graph replays match the eager step")
+
+
+@pytest.mark.parametrize("refresh", [True, False])
+def test_step_call_matches_layer_calls(refresh):
+    """polestar_step (one call for the whole stack) against the stack's per-layer calls from the
+    same saved state: every output and all state left behind bit for bit."""
+    w = synth.shrink(synth.WORKLOADS[1], dtype="bf16")
+    n_layers = 3
+    dims = B.Dims(d=w.d, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn,
+                  n_pos=w.n_pos, batch=2, block=w.block, win_prefix=w.win_prefix, win_suffix=w.win_suffix,
+                  n_clusters=w.n_clusters, top_k=w.top_k, vocab=0, dtype=B.BF16, resid_fmt=B.RESID_RAW)
+    params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist, mask_id=0,
+                      kmeans_iters=w.kmeans_iters)
+    log(f"[step-call] {n_layers} layers of {w.name} (bf16, batch 2), refresh={refresh}")
+    st = RefreshStack(dims, params, n_layers)
+    try:
+        blk = w.prompt
+        entry_rows, inits = [], []
+        for l in range(n_layers):
+            st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
+            L = st.layers[l]
+            L["k_cache"].copy_(synth.tensor(w, (l, 10), L["k_cache"].shape, 1.0, 0, "cuda", "bf16"))
+            L["v_cache"].copy_(synth.tensor(w, (l, 11), L["v_cache"].shape, 1.0, 0, "cuda", "bf16"))
+            L["win_h"].copy_(synth.tensor(w, (l, 12), L["win_h"].shape, 1.0, 0, "cuda", "bf16"))
+            entry_rows.append(L["win_h"])
+            inits.append(torch.stack([torch.tensor(synth.kmeans_init(w, st.win_max, l, 0, 0, b), dtype=torch.int32)
+                                      for b in range(2)]).cuda())
+        st.block_entry(blk, entry_rows, inits)
+        inputs = synth.tensor(w, (99,), (2, 2, w.block, w.d), 1.0, 0, "cuda", "bf16")
+        st.step(blk, inputs[0])                 # drift references
+        torch.cuda.synchronize()
+        snap = _snapshot(st)
+        out = st.step(blk, inputs[1], refresh=refresh)
+        torch.cuda.synchronize()
+        want = _outputs(st, out)
+        _restore(st, snap)
+        st.h_act[0].copy_(inputs[1])
+        mode = B.DRIFT_REFRESH if refresh else B.DRIFT_ACTIVE_ONLY
+        B.polestar_step(st.h, mode, [st.struct(l) for l in range(n_layers)], blk, st.h_act[0], st.h_act[1],
+                        st.packets[0], st.packets[1], st.D, st.topk, st.act_logits, st.delta, st.ws, st.ws_bytes)
+        torch.cuda.synchronize()
+        got = _outputs(st, st.h_act[n_layers % 2])
+        bad = [k for k in want if not torch.equal(got[k], want[k])]
+        log(f"[step-call] {len(want) - len(bad)}/{len(want)} tensors bit-identical")
+        assert not bad, f"polestar_step differs from the per-layer calls in {bad}"
+    finally:
+        st.close()
