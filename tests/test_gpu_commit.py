@@ -29,8 +29,8 @@ CASES = {
     "small_ragged_vocab_batch3": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128),
                                   3, 96),
     # drift-history length h and spike weight alpha at the ends of the page's ranges
-    "small_hist0_alpha2": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128, hist=0,
-                                        alpha=2.0), 2, 64),
+    "small_hist0_alpha2p5": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128, hist=0,
+                                          alpha=2.5), 2, 64),
     "small_hist7_alpha40": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128, hist=7,
                                          alpha=40.0), 2, 64),
 }
