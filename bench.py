@@ -109,6 +109,46 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"forward), {t_total:.1f} s of CPU time, scaled to a {w.n_layers}-layer step"}
 
 
+def entry_cpu_baseline(w, blk: int, full: bool, budget_s: float = 20.0):
+    """The CPU oracle's block entry on a bounded sample: single layers of the whole-stack entry
+    (forward of the entry rows over the cache, k-means, codes, proxy logits; fp64), scaled to
+    the stack."""
+    import numpy as np
+    import torch
+
+    import synth
+    from oracle import polestar_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    cfg = O.Cfg.from_workload(w)
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    rows = O.entry_positions(blk, w.n_pos, w.block, w.win_prefix, w.win_suffix, full)
+    nw = len(O.window_positions(blk, w.n_pos, w.block, w.win_prefix, w.win_suffix))
+    h = synth.embeddings(w, 0, dev).to(torch.bfloat16).double().cpu().numpy()
+    t_total, layers = 0.0, 0
+    for l in range(w.n_layers):
+        W = {k: v.double().cpu().numpy() for k, v in synth.layer_weights(w, l, device=dev).items()}
+        K = synth.tensor(w, (l, 10), (w.n_pos, w.n_kv_heads, w.head_dim), 1.0, 0, dev, "bf16").double().cpu().numpy()
+        V = synth.tensor(w, (l, 11), (w.n_pos, w.n_kv_heads, w.head_dim), 1.0, 0, dev, "bf16").double().cpu().numpy()
+        t0 = time.perf_counter()
+        out = O.layer_forward_rows(h[rows], rows, W, cfg, K, V)
+        O.block_entry_layer_state(h, K, V, W["wq"], cfg, blk, synth.kmeans_init(w, nw, l, 0))
+        t_total += time.perf_counter() - t0
+        layers += 1
+        h = h.copy()
+        h[rows] = out
+        del W
+        if t_total >= budget_s:
+            break
+    ms = t_total / layers * w.n_layers * 1e3
+    return {"value": round(ms, 1), "unit": "ms per block entry", "cores": int(threads), "kind": "oracle",
+            "sample": f"{layers} of {w.n_layers} layers of the {'full' if full else 'window'} entry, "
+                      f"{t_total:.1f} s of CPU time, scaled to {w.n_layers} layers"}
+
+
 def entry_flops(w, rows: int, n_layers: int) -> float:
     """Algorithmic flops of the block-entry forward of `rows` rows: the four projections and the
     two attention products over all n_pos keys."""
@@ -213,6 +253,10 @@ def main():
         h0 = synth.embeddings(w, 0, "cuda").to(torch.bfloat16)[None].contiguous()
         res = entry_timing(st, w, blk, h0, inits, n_layers)
         st.close()
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle's block entry on a bounded sample")
+            for name, full in (("full", True), ("window", False)):
+                res[name]["cpu_baseline"] = entry_cpu_baseline(w, blk, full, budget_s=10.0)
         print(json.dumps({"metric": "block entry ms (32-layer LLaDA-8B shape), 1 GPU", "unit": "ms",
                           "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": f"{w.name}: {n_layers} layers, n {w.n_pos}, block start {blk}",
