@@ -64,28 +64,28 @@ void layout(polestar_handle* h) {
   auto take = [&](size_t bytes) { size_t o = off; off += ps_align256(bytes); return o; };
   w.win_rows = take(Bt * h->win_max * d.d * T);
   w.flags = take(Bt * h->win_max * 4);
-  w.a_qkv = take(Bt * h->rq * d.d * T);
+  w.a_qkv = take(Bt * h->ec * d.d * T);
   w.q = take(Bt * h->mq * (size_t)h->nq * 4);
-  w.o = take(Bt * h->mt * (size_t)h->nq * 4);    // float32 rows, or two bf16 planes
+  w.o = take(Bt * h->ec * (size_t)h->nq * 4);    // float32 rows, or two bf16 planes
   w.kl = take(Bt * d.n_clusters * d.n_heads * 4);
   w.akl = take(Bt * d.block * d.n_heads * 4);
   w.lg = take(Bt * (size_t)(d.n_clusters + d.block) * d.n_heads * d.n_pos * 4);
-  size_t part = (size_t)h->ksplit * Bt * h->mt * d.d;
+  size_t part = (size_t)h->ksplit * Bt * h->ec * d.d;
   if (d.dtype == POLESTAR_BF16) {
     const size_t nqkv = (size_t)h->nq + 2 * (size_t)h->nkv;
-    part = std::max(part, (size_t)h->ks_qkv * Bt * h->mq * nqkv);
-    part = std::max(part, (size_t)h->ks_o * Bt * h->mt * d.d);
-    part = std::max(part, (size_t)h->ks_down * Bt * h->mt * d.d);
-    part = std::max(part, (size_t)h->ks_gu * Bt * h->mt * 2 * (size_t)d.ffn);
+    part = std::max(part, (size_t)h->ks_qkv * Bt * h->ec * nqkv);
+    part = std::max(part, (size_t)h->ks_o * Bt * h->ec * d.d);
+    part = std::max(part, (size_t)h->ks_down * Bt * h->ec * d.d);
+    part = std::max(part, (size_t)h->ks_gu * Bt * h->ec * 2 * (size_t)d.ffn);
     part = std::max(part, (size_t)h->ks_kv * Bt * h->win_max * 2 * (size_t)h->nkv);
   }
   w.part = take(part * 4);
-  w.hp = take(Bt * h->mt * d.d * 4);          // h' (float32)
-  w.a_gu = take(Bt * h->rt * d.d * 4);        // RMSNorm(h'): float32 rows, or two bf16 planes
+  w.hp = take(Bt * h->ec * d.d * 4);          // h' (float32)
+  w.a_gu = take(Bt * h->ec * d.d * 4);        // RMSNorm(h'): float32 rows, or two bf16 planes
   w.attn_part = take(d.dtype == POLESTAR_BF16 && h->attn_nchunks > 1
-                         ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->mt * (d.head_dim + 2) * 4
+                         ? Bt * h->attn_nchunks * d.n_heads * (size_t)h->ec * (d.head_dim + 2) * 4
                          : 0);
-  w.act = take(Bt * h->rt * (size_t)d.ffn * 4);   // float32 rows, or two bf16 planes
+  w.act = take(Bt * h->ec * (size_t)d.ffn * 4);   // float32 rows, or two bf16 planes
   w.a_kv = take(Bt * h->rw * d.d * T);        // round(RMSNorm(U)): next-layer K/V input
   w.xhat = take(Bt * h->win_max * d.d * 8);
   w.z64 = take(Bt * (d.n_clusters + 1) * (size_t)d.d * 8);
@@ -219,7 +219,7 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
 // with a patch flag at their window positions.
 template <typename T>
 int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int rows, int block, const WinGeom& g,
-            float* q, int q_rows, bool checks, void* ws, hipStream_t s) {
+            float* q, int q_rows, int part_rows, bool checks, void* ws, hipStream_t s) {
   const polestar_dims& d = h->dm;
   hipError_t e;
   {
@@ -269,7 +269,7 @@ int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int 
     dl.batch = d.batch;
     dl.ksplit = h->ks_qkv;
     dl.part = at<float>(ws, h->ws.part);
-    dl.part_rows = h->mq;
+    dl.part_rows = part_rows;
     dl.e = ep;
     PROF(POLESTAR_K_QKV);
     e = launch_dl<T>(dl, h->sh_qkv, rows, s);
@@ -284,7 +284,7 @@ int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int 
 // Attention arguments shared by every call: the layer's cache and the workspace buffers.  The
 // caller sets the query rows (q, mq, n_tok, n_proxy, block) and the logit outputs.
 template <typename T>
-AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws) {
+AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws, int cap) {
   const polestar_dims& d = h->dm;
   AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -294,7 +294,7 @@ AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws) {
   a.hkv = d.n_kv_heads;
   a.dh = d.head_dim;
   a.mq = h->mq;
-  a.mt = h->mt;
+  a.mt = cap;   // token-row capacity of the output and chunk-state buffers
   a.block = d.block;
   a.kc = L->k_cache;
   a.vc = L->v_cache;
@@ -306,8 +306,8 @@ AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws) {
   a.chunk_keys = h->attn_chunk;
   a.n_chunks = h->attn_nchunks;
   a.part_o = at<float>(ws, h->ws.attn_part);
-  a.part_ml = a.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * h->mt * d.head_dim;
-  a.chk_rows = h->mt;
+  a.part_ml = a.part_o + (size_t)d.batch * h->attn_nchunks * d.n_heads * cap * d.head_dim;
+  a.chk_rows = cap;
   return a;
 }
 
@@ -358,10 +358,10 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.eps = h->pr.rms_eps;
   const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
   float* q = at<float>(ws, h->ws.q);
-  int rc = run_qkv<T>(h, L, p, rows, d.block, g, q, h->mq, true, ws, s);
+  int rc = run_qkv<T>(h, L, p, rows, d.block, g, q, h->mq, h->mq, true, ws, s);
   if (rc) return rc;
   // 2. attention, proxy attention and drift
-  AttnArgs at_ = attn_base<T>(h, L, ws);
+  AttnArgs at_ = attn_base<T>(h, L, ws, h->mt);
   at_.n_tok = refresh ? d.block + g.n_win : d.block;
   at_.n_proxy = refresh ? d.n_clusters : 0;
   at_.q = q;
@@ -406,6 +406,8 @@ struct TokRows {
   const polestar_packet* sel;               // null: no window rows
   void* u_rows;
   bool checks;                              // fill the check buffers (per-step calls)
+  int32_t cap, rcap;                        // rows per sequence of the workspace's token-row
+                                            // buffers as laid out by the call (rcap: in 16-row tiles)
 };
 
 // Row count of a projection over [n_act rows; selected window rows].
@@ -432,7 +434,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   DlArgs dl;
   memset(&dl, 0, sizeof(dl));
   dl.A.base = at<char>(ws, h->ws.o);
-  dl.A.plane_stride = (int64_t)h->mt * h->nq;
+  dl.A.plane_stride = (int64_t)t.cap * h->nq;
   dl.A.bstride = 2 * dl.A.plane_stride;
   dl.A.lda = h->nq;
   dl.A.rowmap = sel ? sel->idx : nullptr;
@@ -448,7 +450,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.batch = d.batch;
   dl.ksplit = h->ks_o;
   dl.part = part;
-  dl.part_rows = h->mt;
+  dl.part_rows = t.cap;
   dl.e.kind = EPI_PARTIAL;
   {
     PROF(POLESTAR_K_OPROJ);
@@ -459,7 +461,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   memset(&rr, 0, sizeof(rr));
   rr.part = part;
   rr.ksplit = h->ks_o;
-  rr.part_rows = h->mt;
+  rr.part_rows = t.cap;
   rr.batch = d.batch;
   rr.d = d.d;
   rr.count = sel ? sel->count : nullptr;
@@ -472,17 +474,17 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   rr.res_b_bstride = (int64_t)h->win_max * d.d;
   rr.sel_idx = sel ? sel->idx : nullptr;
   rr.out_a = at<char>(ws, h->ws.hp);
-  rr.out_a_bstride = (int64_t)h->mt * d.d;
-  rr.out_split = h->mt;
+  rr.out_a_bstride = (int64_t)t.cap * d.d;
+  rr.out_split = t.cap;
   rr.out_f32 = 1;
   rr.norm = at<char>(ws, h->ws.a_gu);
   rr.norm_planes = 1;
-  rr.norm_tiles = h->rt / 16;
-  rr.norm_bstride = 2 * (int64_t)h->rt * d.d;
+  rr.norm_tiles = t.rcap / 16;
+  rr.norm_bstride = 2 * (int64_t)t.rcap * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
   rr.chk = t.checks ? h->chk.hp : nullptr;
-  rr.chk_rows = h->mt;
+  rr.chk_rows = t.cap;
   {
     PROF(POLESTAR_K_OREDUCE);
     e = launch_row_reduce<T>(rr, max_rows, s);
@@ -503,11 +505,11 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.batch = d.batch;
   dl.ksplit = h->ks_gu;
   dl.part = part;
-  dl.part_rows = h->mt;
+  dl.part_rows = t.cap;
   dl.e.kind = EPI_SWIGLU;
   dl.e.act = at<char>(ws, h->ws.act);
-  dl.e.act_rows = h->rt;
-  dl.e.act_tiles = h->rt / 16;
+  dl.e.act_rows = t.rcap;
+  dl.e.act_tiles = t.rcap / 16;
   dl.e.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
@@ -518,8 +520,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&dl, 0, sizeof(dl));
   dl.A.base = at<char>(ws, h->ws.act);
-  dl.A.tiles = h->rt / 16;
-  dl.A.bstride = 2 * (int64_t)h->rt * d.ffn;
+  dl.A.tiles = t.rcap / 16;
+  dl.A.bstride = 2 * (int64_t)t.rcap * d.ffn;
   dl.A.lda = d.ffn;
   set_rows(dl.A, t, max_rows);
   dl.planes = 2;
@@ -530,7 +532,7 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   dl.batch = d.batch;
   dl.ksplit = h->ks_down;
   dl.part = part;
-  dl.part_rows = h->mt;
+  dl.part_rows = t.cap;
   dl.e.kind = EPI_PARTIAL;
   {
     PROF(POLESTAR_K_DOWN);
@@ -542,8 +544,8 @@ int do_refresh_dl(polestar_handle* h, const polestar_layer* L, int32_t blk_start
   r2.ksplit = h->ks_down;
   r2.res_a = rr.out_a;
   r2.res_a_f32 = 1;
-  r2.res_a_bstride = (int64_t)h->mt * d.d;
-  r2.res_split = h->mt;
+  r2.res_a_bstride = (int64_t)t.cap * d.d;
+  r2.res_split = t.cap;
   r2.res_b = nullptr;
   r2.out_a = t.h_out;
   r2.out_a_bstride = t.out_bstride;
@@ -615,7 +617,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   GemmArgs ga;
   memset(&ga, 0, sizeof(ga));
   ga.A.base = at<char>(ws, h->ws.o);
-  ga.A.bstride = (int64_t)h->mt * h->nq;
+  ga.A.bstride = (int64_t)t.cap * h->nq;
   ga.A.lda = h->nq;
   ga.A.rowmap = sel ? sel->idx : nullptr;
   ga.A.map_bstride = h->win_max;
@@ -628,7 +630,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.batch = d.batch;
   ga.ksplit = h->ksplit;
   ga.part = part;
-  ga.part_rows = h->mt;
+  ga.part_rows = t.cap;
   EpiParams ep;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_PARTIAL;
@@ -642,7 +644,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   memset(&rr, 0, sizeof(rr));
   rr.part = part;
   rr.ksplit = h->ksplit;
-  rr.part_rows = h->mt;
+  rr.part_rows = t.cap;
   rr.batch = d.batch;
   rr.d = d.d;
   rr.count = sel ? sel->count : nullptr;
@@ -655,15 +657,15 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   rr.res_b_bstride = (int64_t)h->win_max * d.d;
   rr.sel_idx = sel ? sel->idx : nullptr;
   rr.out_a = at<char>(ws, h->ws.hp);
-  rr.out_a_bstride = (int64_t)h->mt * d.d;
-  rr.out_split = h->mt;
+  rr.out_a_bstride = (int64_t)t.cap * d.d;
+  rr.out_split = t.cap;
   rr.out_f32 = 1;
   rr.norm = at<char>(ws, h->ws.a_gu);
-  rr.norm_bstride = (int64_t)h->rt * d.d;
+  rr.norm_bstride = (int64_t)t.rcap * d.d;
   rr.norm_from = 0;
   rr.eps = h->pr.rms_eps;
   rr.chk = t.checks ? h->chk.hp : nullptr;
-  rr.chk_rows = h->mt;
+  rr.chk_rows = t.cap;
   {
     PROF(POLESTAR_K_OREDUCE);
     e = launch_row_reduce<T>(rr, max_rows, s);
@@ -683,7 +685,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_SWIGLU;
   ep.act = at<char>(ws, h->ws.act);
-  ep.act_rows = h->rt;
+  ep.act_rows = t.rcap;
   ep.ffn = d.ffn;
   {
     PROF(POLESTAR_K_GU);
@@ -693,7 +695,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   // 3. out = h' + act W_down^T -> next active rows and the update packet
   memset(&ga, 0, sizeof(ga));
   ga.A.base = ep.act;
-  ga.A.bstride = (int64_t)h->rt * d.ffn;
+  ga.A.bstride = (int64_t)t.rcap * d.ffn;
   ga.A.lda = d.ffn;
   set_rows(ga.A, t, max_rows);
   ga.W = L->w_down;
@@ -702,7 +704,7 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   ga.batch = d.batch;
   ga.ksplit = h->ksplit;
   ga.part = part;
-  ga.part_rows = h->mt;
+  ga.part_rows = t.cap;
   memset(&ep, 0, sizeof(ep));
   ep.kind = EPI_PARTIAL;
   {
@@ -713,8 +715,8 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
   RowReduceArgs r2 = rr;
   r2.res_a = rr.out_a;
   r2.res_a_f32 = 1;
-  r2.res_a_bstride = (int64_t)h->mt * d.d;
-  r2.res_split = h->mt;
+  r2.res_a_bstride = (int64_t)t.cap * d.d;
+  r2.res_split = t.cap;
   r2.res_b = nullptr;
   r2.out_a = t.h_out;
   r2.out_a_bstride = t.out_bstride;
@@ -767,8 +769,8 @@ int do_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_start, c
 // Block entry of one layer: the forward of the rows at positions [r0, r1) (every position, or the
 // window and the active block) with attention over the whole cache, the k-means of the window
 // rows of h_in, and the centroids' proxy logits over the fresh cache.  The rows are taken in
-// slabs of the workspace's token-row capacity: first the Q/K/V of every slab (the cache must be
-// complete before any row attends), then attention and the rest of the layer slab by slab.
+// slabs of up to ec rows: first the Q/K/V of every slab (the cache must be complete before any
+// row attends), then attention and the rest of the layer slab by slab.
 template <typename T>
 int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
              const int32_t* init_idx, void* h_out, double* objective, float* act_logits, void* ws, hipStream_t s) {
@@ -777,7 +779,9 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   const bool full = mode == POLESTAR_ENTRY_FULL;
   const int r0 = full ? 0 : blk_start - g.n_pre;
   const int r1 = full ? d.n_pos : blk_start + d.block + (g.n_win - g.n_pre);
-  const int slab = h->mt;
+  // slabs of at most ec rows, as even as 16-row tiles allow (one weight pass per slab)
+  const int n_rows = r1 - r0, n_slabs = PS_CEIL_DIV(n_rows, h->ec);
+  const int slab = std::min(h->ec, 16 * PS_CEIL_DIV(PS_CEIL_DIV(n_rows, n_slabs), 16));
   const int64_t hb = (int64_t)d.n_pos * d.d;   // elements between sequences of h_in, h_out
   const T* hin = (const T*)h_in;
   T* hout = (T*)h_out;
@@ -796,32 +800,34 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.act_bstride = hb;
   p.win_z = L->win_z;
   p.a_qkv = at<char>(ws, h->ws.a_qkv);
-  p.a_bstride = (int64_t)h->rq * d.d;
-  p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
+  p.a_bstride = (int64_t)h->ec * d.d;
+  p.a_tiles = std::is_same<T, bf16_t>::value ? h->ec / 16 : 0;
   p.eps = h->pr.rms_eps;
   for (int p0 = r0; p0 < r1; p0 += slab) {
     const int rows = std::min(slab, r1 - p0);
     p.block = rows;
     p.h_act = hin + (int64_t)p0 * d.d;
     const WinGeom gs = make_geom(p0, d.n_pos, rows, 0, 0);
-    if ((rc = run_qkv<T>(h, L, p, rows, rows, gs, q_all + (int64_t)p0 * h->nq, d.n_pos, false, ws, s))) return rc;
+    if ((rc = run_qkv<T>(h, L, p, rows, rows, gs, q_all + (int64_t)p0 * h->nq, d.n_pos, h->ec, false, ws, s)))
+      return rc;
   }
   // 3. attention over all positions, O projection, SwiGLU FFN
   for (int p0 = r0; p0 < r1; p0 += slab) {
     const int rows = std::min(slab, r1 - p0);
-    AttnArgs a = attn_base<T>(h, L, ws);
+    AttnArgs a = attn_base<T>(h, L, ws, h->ec);
     a.q = q_all + (int64_t)p0 * h->nq;
     a.mq = d.n_pos;
     a.n_tok = rows;
     a.block = rows;
     if ((rc = run_attention<T>(h, a, s))) return rc;
-    const TokRows t = {rows, hin + (int64_t)p0 * d.d, hb, hout + (int64_t)p0 * d.d, hb, nullptr, nullptr, false};
+    const TokRows t = {rows, hin + (int64_t)p0 * d.d, hb, hout + (int64_t)p0 * d.d, hb, nullptr, nullptr, false,
+                       h->ec, h->ec};
     if ((rc = do_refresh<T>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s))) return rc;
   }
   // 4. (when asked) the active block's main-attention logits: the first reference of the commit
   //    drift; the block's queries are rows blk_start.. of q_all
   if (act_logits) {
-    AttnArgs a = attn_base<T>(h, L, ws);
+    AttnArgs a = attn_base<T>(h, L, ws, h->mt);
     a.q = q_all + (int64_t)blk_start * h->nq;
     a.mq = d.n_pos;
     a.n_tok = d.block;
@@ -836,8 +842,8 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.h_act = nullptr;
   const WinGeom g0 = make_geom(0, d.n_pos, 0, 0, 0);
   float* q = at<float>(ws, h->ws.q);
-  if ((rc = run_qkv<T>(h, L, p, d.n_clusters, 0, g0, q, h->mq, false, ws, s))) return rc;
-  AttnArgs a = attn_base<T>(h, L, ws);
+  if ((rc = run_qkv<T>(h, L, p, d.n_clusters, 0, g0, q, h->mq, h->ec, false, ws, s))) return rc;
+  AttnArgs a = attn_base<T>(h, L, ws, h->mt);
   a.q = q;
   a.n_tok = 0;
   a.n_proxy = d.n_clusters;
@@ -1009,6 +1015,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->nkv = d.n_kv_heads * d.head_dim;
   h->rq = 16 * PS_CEIL_DIV(h->mq, 16);
   h->rt = 16 * PS_CEIL_DIV(h->mt, 16);
+  h->ec = kMaxRows;   // >= rq: the rows of a sequence never exceed kMaxRows
   h->rw = 16 * PS_CEIL_DIV(h->win_max, 16);
   const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
   int ks = PS_CEIL_DIV(256, ntiles);
@@ -1205,7 +1212,7 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int64_t bs = (int64_t)h->dm.block * h->dm.d;
-  const TokRows t = {h->dm.block, h_active, bs, h_active_out, bs, sel, u_rows, true};
+  const TokRows t = {h->dm.block, h_active, bs, h_active_out, bs, sel, u_rows, true, h->mt, h->rt};
   return h->dm.dtype == POLESTAR_BF16 ? do_refresh<bf16_t>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s)
                                       : do_refresh<float>(h, L, blk_start, t, w_kv_next, k_next, v_next, ws, s);
 }
@@ -1251,7 +1258,8 @@ int polestar_step(polestar_handle* h, int mode, int32_t n_layers, const polestar
     rc = bf ? do_drift<bf16_t>(h, mode, L, blk_start, act[l % 2], u_in, D, topk, pk[l % 2], al, dl, ws, s)
             : do_drift<float>(h, mode, L, blk_start, act[l % 2], u_in, D, topk, pk[l % 2], al, dl, ws, s);
     if (rc) return rc;
-    const TokRows t = {h->dm.block, act[l % 2], bs, act[(l + 1) % 2], bs, pk[l % 2], pk[l % 2]->rows, true};
+    const TokRows t = {h->dm.block, act[l % 2], bs, act[(l + 1) % 2], bs, pk[l % 2], pk[l % 2]->rows, true,
+                       h->mt, h->rt};
     rc = bf ? do_refresh<bf16_t>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s)
             : do_refresh<float>(h, L, blk_start, t, nullptr, nullptr, nullptr, ws, s);
     if (rc) return rc;

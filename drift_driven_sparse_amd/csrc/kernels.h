@@ -22,6 +22,8 @@ struct polestar_handle {
   int32_t ks_qkv, ks_o, ks_gu, ks_down, ks_kv;   // split-K factors of the bf16 projections
   int32_t sh_qkv, sh_o, sh_gu, sh_down, sh_kv;   // their workgroup shapes (DlShape)
   int32_t rq, rt, rw;   // mq, mt, win_max rounded up to whole 16-row tiles (packed operands)
+  int32_t ec;           // block entry: rows per slab at most (a multiple of 16, >= rq); the
+                        // token-row buffers of the workspace hold this many rows per sequence
   int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
   int32_t attn_rgroups;                         // bf16 attention: workgroups along the query rows
   int32_t lm_tiles;  // vocab / 64 rounded up
