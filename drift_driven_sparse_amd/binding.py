@@ -50,7 +50,7 @@ class Layer(C.Structure):
     _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gu", C.c_void_p), ("w_down", C.c_void_p),
                 ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("win_h", C.c_void_p),
                 ("win_codes", C.c_void_p), ("win_scales", C.c_void_p), ("win_z", C.c_void_p),
-                ("win_m", C.c_void_p), ("proxy_logits", C.c_void_p)]
+                ("win_m", C.c_void_p), ("proxy_logits", C.c_void_p), ("q_win", C.c_void_p), ("q_ok", C.c_void_p)]
 
 
 class Packet(C.Structure):

@@ -99,6 +99,7 @@ void layout(polestar_handle* h) {
     w.lm_a = w.lm_stats = w.lm_meta = 0;
   }
   w.q_all = take(Bt * d.n_pos * (size_t)h->nq * 4);   // block entry: queries of every position
+  w.qmap = take(Bt * (h->win_max + 1) * 4);           // query cache: staged window rows, count
   w.km_lab = take(Bt * h->win_max * 4);                // block entry: k-means labels, counts, sums
   w.km_cnt = take(Bt * d.n_clusters * 4);
   w.km_sum = take(Bt * d.n_clusters * (size_t)d.d * 8);
@@ -209,6 +210,7 @@ int do_cluster(polestar_handle* h, int mode, const polestar_layer* L, int32_t bl
   a.km_cnt = at<int32_t>(ws, h->ws.km_cnt);
   a.km_sum = at<double>(ws, h->ws.km_sum);
   a.resid = d.resid_fmt;
+  a.q_ok = L->q_win ? L->q_ok : nullptr;
   if (a.geom.n_win == 0) return POLESTAR_OK;
   PROF(POLESTAR_K_CLUSTER);
   return hip_status(launch_cluster<T>(a, s));
@@ -234,6 +236,11 @@ int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int 
   ga.A.tiles = p.a_tiles;
   ga.A.lda = d.d;
   ga.A.rows_static = rows;
+  if (p.map) {   // block + staged window rows + K of the rows at most
+    ga.A.rows_dev = p.count;
+    ga.A.rows_add = block + p.K;
+    ga.A.rows_max = rows;
+  }
   ga.W = L->w_qkv;
   ga.N = h->nq + 2 * h->nkv;
   ga.K = d.d;
@@ -254,6 +261,11 @@ int run_qkv(polestar_handle* h, const polestar_layer* L, const PrepArgs& p, int 
   ep.win_max = h->win_max;
   ep.n_pos = d.n_pos;
   ep.geom = g;
+  if (p.map) {   // query cache: rows [active; staged window rows; centroids]
+    ep.q_win = p.q_win;
+    ep.qmap = p.map;
+    ep.qcount = p.count;
+  }
   ep.chk = checks ? h->chk.qkv : nullptr;
   ep.chk_rows = h->mq;
   ep.chk_ld = ga.N;
@@ -356,6 +368,17 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   p.a_bstride = (int64_t)h->rq * d.d;
   p.a_tiles = std::is_same<T, bf16_t>::value ? h->rq / 16 : 0;
   p.eps = h->pr.rms_eps;
+  // raw window rows change only where a packet patches them (residual formats are rebuilt
+  // against a new centroid every step), so only then are the other rows' queries kept
+  const bool qcache = refresh && L->q_win != nullptr && std::is_same<T, bf16_t>::value &&
+                      d.resid_fmt == POLESTAR_RESID_RAW;
+  if (qcache) {
+    p.flags = at<int32_t>(ws, h->ws.flags);
+    p.q_ok = L->q_ok;
+    p.map = at<int32_t>(ws, h->ws.qmap);
+    p.count = p.map + (size_t)d.batch * h->win_max;
+    p.q_win = L->q_win;
+  }
   const int rows = refresh ? d.block + g.n_win + d.n_clusters : d.block;
   float* q = at<float>(ws, h->ws.q);
   int rc = run_qkv<T>(h, L, p, rows, d.block, g, q, h->mq, h->mq, true, ws, s);
@@ -365,6 +388,10 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.n_tok = refresh ? d.block + g.n_win : d.block;
   at_.n_proxy = refresh ? d.n_clusters : 0;
   at_.q = q;
+  if (qcache) {
+    at_.q_win = L->q_win;
+    at_.win_max = h->win_max;
+  }
   at_.proxy_logits = L->proxy_logits;
   at_.proxy_kl = 1;
   at_.act_logits = act_logits;
@@ -390,6 +417,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   tk.akl = at_.akl;
   tk.delta = (act_logits && delta) ? delta : nullptr;
   tk.refresh = refresh;
+  tk.q_ok = qcache ? L->q_ok : nullptr;
   PROF(POLESTAR_K_TOPK);
   return hip_status(launch_topk(tk, s));
 }
@@ -1174,6 +1202,8 @@ static int check_drift(const polestar_handle* h, int mode, const polestar_layer*
   if (mode == POLESTAR_DRIFT_REFRESH && !aligned16(L->win_z)) return POLESTAR_E_ALIGN;
   if (delta && !act_logits) return POLESTAR_E_NULL;
   if (u_in && (!u_in->idx || !u_in->count)) return POLESTAR_E_NULL;
+  if (L->q_win && (!L->q_ok)) return POLESTAR_E_NULL;
+  if (L->q_win && !aligned16(L->q_win)) return POLESTAR_E_ALIGN;
   return POLESTAR_OK;
 }
 

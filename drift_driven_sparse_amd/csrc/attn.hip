@@ -140,7 +140,10 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
     tile_on[t] = tile * 16 < nrows && wave * RTW + t < a.group_tiles;
     const int row = tile * 16 + c16;
     q_valid[t] = row < nrows;
-    const float* qr = a.q + ((int64_t)b * a.mq + (q_valid[t] ? row : 0)) * (a.hq * DH) + h * DH + 8 * g4;
+    const int qrow = q_valid[t] ? row : 0;
+    const bool from_cache = a.q_win && qrow >= a.block && qrow < a.n_tok;   // window rows' cached queries
+    const float* qr = (from_cache ? a.q_win + ((int64_t)b * a.win_max + (qrow - a.block)) * (a.hq * DH)
+                                  : a.q + ((int64_t)b * a.mq + qrow) * (a.hq * DH)) + h * DH + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qraw[t][ks][0] = *(const float4*)(qr + 32 * ks);
@@ -603,6 +606,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
       }
       if (lane == 0) a.sel_count[b] = base;
     }
+    if (tid == 0 && a.q_ok) a.q_ok[b] = 1;   // every window row's query is now current
   } else {
     if (tid == 0) a.sel_count[b] = 0;
   }

@@ -201,6 +201,7 @@ __global__ __launch_bounds__(256) void km_finish_kernel(ClusterArgs a, int it) {
 template <typename T>
 __global__ __launch_bounds__(256) void km_store_kernel(ClusterArgs a) {
   const int c = blockIdx.x, b = blockIdx.y, d = a.d, K = a.K, nwin = a.geom.n_win;
+  if (c == 0 && threadIdx.x == 0 && a.q_ok) a.q_ok[b] = 0;   // every window row changed
   if (c == 0)
     for (int w = threadIdx.x; w < a.win_max; w += blockDim.x)
       a.win_m[(int64_t)b * a.win_max + w] = (w < nwin && a.iters > 0) ? a.km_lab[(int64_t)b * a.win_max + w] : 0;
@@ -384,17 +385,51 @@ __global__ __launch_bounds__(256) void centroid_finish_kernel(ClusterArgs a) {
 template <typename T>
 __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
   __shared__ float red[4];
+  __shared__ unsigned long long bal[4];
   const int r = blockIdx.x, b = blockIdx.y;
   const int d = a.d;
   const T* src;
-  if (r < a.block) src = (const T*)a.h_act + (int64_t)b * a.act_bstride + (int64_t)r * d;
-  else if (r < a.block + a.n_win) src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + (r - a.block)) * d;
-  else src = (const T*)a.win_z + ((int64_t)b * a.K + (r - a.block - a.n_win)) * d;
+  int out = r;   // staged row
+  if (r < a.block) {
+    src = (const T*)a.h_act + (int64_t)b * a.act_bstride + (int64_t)r * d;
+  } else {
+    const int w = r - a.block;
+    if (a.map) {
+      // query cache: window rows that need a query (all of them after block entry, else the
+      // patched ones) are staged in row order after the active rows, then the centroids
+      const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+      const bool all = a.q_ok[b] == 0;
+      const bool need = tid < a.n_win && (all || a.flags[(int64_t)b * a.win_max + tid] != 0);
+      const unsigned long long m = __ballot(need);
+      if (lane == 0) bal[wave] = m;
+      __syncthreads();
+      int total = 0, before = 0;   // staged window rows, and those before row w
+      for (int k = 0; k < 4; ++k) total += __popcll(bal[k]);
+      if (w < a.n_win) {
+        const int ww = w >> 6;
+        if (!((bal[ww] >> (w & 63)) & 1ull)) return;   // uniform: its query is kept from an earlier step
+        for (int k = 0; k < ww; ++k) before += __popcll(bal[k]);
+        before += __popcll(bal[ww] & ((1ull << (w & 63)) - 1ull));
+        out = a.block + before;
+        if (tid == 0) a.map[(int64_t)b * a.win_max + before] = w;
+        src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + w) * d;
+      } else {
+        const int c = w - a.n_win;
+        out = a.block + total + c;
+        if (c == 0 && tid == 0) a.count[b] = total;
+        src = (const T*)a.win_z + ((int64_t)b * a.K + c) * d;
+      }
+    } else if (w < a.n_win) {
+      src = (const T*)a.ws_rows + ((int64_t)b * a.win_max + w) * d;
+    } else {
+      src = (const T*)a.win_z + ((int64_t)b * a.K + (w - a.n_win)) * d;
+    }
+  }
   T* dst = (T*)a.a_qkv + (int64_t)b * a.a_bstride;
   if (a.a_tiles > 0)
-    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + apack(r, n, 0, 1, a.a_tiles), x); });
+    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + apack(out, n, 0, 1, a.a_tiles), x); });
   else
-    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + (int64_t)r * d + n, x); });
+    rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + (int64_t)out * d + n, x); });
 }
 
 // ---- NVFP4 test hooks ---------------------------------------------------------------------------

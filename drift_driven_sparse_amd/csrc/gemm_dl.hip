@@ -257,12 +257,9 @@ __global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
     const EpiParams& e = g.e;
     if (c < e.nq + e.nkv) {
       if (e.chk) *(float4*)(e.chk + ((int64_t)b * e.chk_rows + r) * e.chk_ld + c) = v;
-      if (c < e.nq) {
-        *(float4*)(e.q + ((int64_t)b * e.q_rows + r) * e.nq + c) = v;
-      } else {
-        const int pos = qkv_pos(e, b, r);
-        if (pos >= 0) Quad<T>::store((T*)e.kc + kv_index(e, b, pos, c - e.nq, 0), vv);
-      }
+      const QkvDest dst = qkv_dest(e, b, r);
+      if (c < e.nq) *(float4*)(dst.q + c) = v;
+      else if (dst.pos >= 0) Quad<T>::store((T*)e.kc + kv_index(e, b, dst.pos, c - e.nq, 0), vv);
       return;
     }
   }

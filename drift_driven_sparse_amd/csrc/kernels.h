@@ -5,7 +5,7 @@
 // Handle contents (host only).
 struct WsLayout {
   size_t win_rows, flags, a_qkv, q, o, kl, akl, lg, part, hp, a_gu, act, a_kv, xhat, z64, wstat, attn_part, lm_a,
-      lm_stats, lm_meta, q_all, km_lab, km_cnt, km_sum, total;
+      lm_stats, lm_meta, q_all, qmap, km_lab, km_cnt, km_sum, total;
 };
 
 struct ProfState;   // per-kernel event records (api.hip)
@@ -91,6 +91,9 @@ struct EpiParams {
   const int32_t* flags;         // patched flags [batch][win_max]
   int32_t nq, nkv, block, win_max, n_pos, dh;
   WinGeom geom;
+  // query cache: rows [active; qcount staged window rows (window row qmap[b*win_max + j]); centroids];
+  // window-row queries go to q_win[b][w], centroid c's to q row block + n_win + c
+  float* q_win; const int32_t* qmap; const int32_t* qcount;
   float* chk; int32_t chk_rows, chk_ld;   // chk[(b*chk_rows + r)*chk_ld + n]
   // SwiGLU product: float32 rows [batch][act_rows][ffn], or for bf16 storage the hi/lo planes
   // fragment-packed with act_tiles row tiles ([batch] stride act_rows*ffn*2 elements)
@@ -113,24 +116,36 @@ PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
 // to the cache.
 // Cache position whose K/V QKV row r writes: the active block's, or a patched window row's; -1:
 // none (unpatched window rows, centroids).
-PS_DEV int qkv_pos(const EpiParams& e, int b, int r) {
-  if (r < e.block) return e.geom.blk_start + r;
-  const int w = r - e.block;
-  return (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) ? e.geom.pos(w) : -1;
+// Destination of QKV row r: its query row (as a pointer to column 0) and the cache position of its
+// K/V (-1: none).
+struct QkvDest { float* q; int pos; };
+PS_DEV QkvDest qkv_dest(const EpiParams& e, int b, int r) {
+  if (r < e.block) return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, e.geom.blk_start + r};
+  int w = r - e.block;
+  if (e.qmap) {
+    const int np = e.qcount[b];
+    if (w >= np)   // centroid rows follow the staged window rows
+      return {e.q + ((int64_t)b * e.q_rows + e.block + e.geom.n_win + (w - np)) * e.nq, -1};
+    w = e.qmap[(int64_t)b * e.win_max + w];
+    const int pos = e.flags[(int64_t)b * e.win_max + w] ? e.geom.pos(w) : -1;
+    return {e.q_win + ((int64_t)b * e.win_max + w) * e.nq, pos};
+  }
+  const int pos = (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) ? e.geom.pos(w) : -1;
+  return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, pos};
 }
 
 template <typename T>
 PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
   if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
+  const QkvDest dst = qkv_dest(e, b, r);
   if (n < e.nq) {
-    e.q[((int64_t)b * e.q_rows + r) * e.nq + n] = v;
+    dst.q[n] = v;
     return;
   }
   const int kv = n - e.nq;
   const int which = kv >= e.nkv;
   const int col = kv - which * e.nkv;
-  const int pos = qkv_pos(e, b, r);
-  if (pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, pos, col, which), v);
+  if (dst.pos >= 0) St<T>::store((T*)(which ? e.vc : e.kc), kv_index(e, b, dst.pos, col, which), v);
 }
 
 // K/V of the next layer for packet row r (window row sel_idx[r]).
@@ -256,6 +271,7 @@ struct ClusterArgs {
   int32_t* km_cnt;          //   member sums [batch][K][d] (float64); wnorm holds the best cosines
   double* km_sum;
   int resid;                // residual format of the window storage (POLESTAR_RESID_*; 0: raw rows)
+  int32_t* q_ok;            // query cache validity [batch] (nullable): block entry clears it
 };
 template <typename T>
 hipError_t launch_cluster(const ClusterArgs& a, hipStream_t s);
@@ -266,6 +282,11 @@ struct PrepArgs {
   int32_t a_tiles;        // > 0: a_qkv fragment-packed with this many row tiles (bf16)
   const void* h_act; int64_t act_bstride;   // block rows per sequence, act_bstride elements apart
   const void* ws_rows; const void* win_z;
+  // query cache (map set): only the window rows that need a query (all when q_ok[b] == 0, else
+  // the patched ones) are staged, after the active rows and before the centroids; map[b][j] is the
+  // window row of staged row block + j, count[b] their number
+  const int32_t* flags; const int32_t* q_ok; int32_t* map; int32_t* count;
+  float* q_win;   // the layer's cached window-row queries (passed on to the QKV epilogue)
   void* a_qkv; int64_t a_bstride; float eps;
 };
 template <typename T>
@@ -278,6 +299,8 @@ struct AttnArgs {
   int32_t n_proxy;        // centroid query rows (K or 0)
   int32_t block;
   const float* q;         // [batch][mq][hq*dh]
+  const float* q_win;     // nullable: queries of token rows block.. (window rows), [batch][win_max][hq*dh]
+  int32_t win_max;
   const void* kc; const void* vc;
   void* o;                // [batch][mt][hq*dh] float32, or bf16 hi/lo planes [batch][2][mt][hq*dh]
   int32_t o_planes;
@@ -307,6 +330,7 @@ struct TopkArgs {
   float* D; int32_t* topk; int32_t* sel_idx; int32_t* sel_count;
   const float* akl; float* delta;
   int32_t refresh;
+  int32_t* q_ok;   // query cache validity [batch] (nullable): set after a refresh
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

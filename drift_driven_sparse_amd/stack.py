@@ -24,7 +24,7 @@ _TDT = {B.F32: torch.float32, B.BF16: torch.bfloat16}
 
 
 class RefreshStack:
-    def __init__(self, dims: B.Dims, params: B.Params, n_layers: int, device="cuda"):
+    def __init__(self, dims: B.Dims, params: B.Params, n_layers: int, device="cuda", q_cache: bool = True):
         self.dims, self.params, self.n_layers, self.device = dims, params, n_layers, device
         self.h = B.polestar_create(dims, params)
         self.ws_bytes = B.polestar_workspace_size(self.h)
@@ -44,6 +44,10 @@ class RefreshStack:
                 "win_m": torch.zeros(bt, self.win_max, dtype=torch.int32, device=device),
                 "proxy_logits": torch.zeros(bt, dims.n_clusters, dims.n_heads, n, dtype=torch.float32, device=device),
             }
+            if q_cache and dims.dtype == B.BF16 and not self.resid:   # window-row queries kept across steps
+                L["q_win"] = torch.zeros(bt, self.win_max, dims.n_heads * dims.head_dim, dtype=torch.float32,
+                                         device=device)
+                L["q_ok"] = torch.zeros(bt, dtype=torch.int32, device=device)
             if self.resid:
                 L["win_codes"] = torch.zeros(bt, self.win_max, cb, dtype=torch.uint8, device=device)
                 L["win_scales"] = torch.zeros(bt, self.win_max, max(sb, 1), dtype=torch.uint8, device=device)
@@ -94,7 +98,7 @@ class RefreshStack:
             L = self.layers[l]
             s = B.Layer()
             for name in ("w_qkv", "w_o", "w_gu", "w_down", "k_cache", "v_cache", "win_h", "win_codes",
-                         "win_scales", "win_z", "win_m", "proxy_logits"):
+                         "win_scales", "win_z", "win_m", "proxy_logits", "q_win", "q_ok"):
                 t = L.get(name)
                 setattr(s, name, t.data_ptr() if t is not None else None)
             self.structs[l] = s

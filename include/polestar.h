@@ -152,6 +152,13 @@ typedef struct polestar_layer {
   void* win_z;          /* centroids [batch, n_clusters, d], in/out */
   int32_t* win_m;       /* cluster labels [batch, win_max], in/out */
   float* proxy_logits;  /* previous proxy-attention logits [batch, K, n_heads, n_pos], in/out */
+  float* q_win;         /* nullable (bf16 storage, raw window rows; ignored otherwise): the
+                           window rows' queries [batch, win_max, n_heads * head_dim] f32 kept
+                           across steps, in/out; a refresh-mode drift then projects only the
+                           rows a packet patched (a raw row changes only there, and its query
+                           depends on its stored value alone) */
+  int32_t* q_ok;        /* with q_win: [batch]; block entry sets 0 (every window row is
+                           projected at the next refresh), a refresh-mode drift sets 1 */
 } polestar_layer;
 
 /* Update packet U(t,l): rows of selected window positions.  Row r of

@@ -19,7 +19,7 @@ from tests.harness import log
 
 pytestmark = pytest.mark.gpu
 
-STATE = ("k_cache", "v_cache", "win_h", "win_z", "win_m", "proxy_logits")
+STATE = ("k_cache", "v_cache", "win_h", "win_z", "win_m", "proxy_logits", "q_win", "q_ok")
 
 
 def _snapshot(st: RefreshStack):
@@ -159,3 +159,45 @@ def test_step_call_matches_layer_calls(refresh):
         assert not bad, f"polestar_step differs from the per-layer calls in {bad}"
     finally:
         st.close()
+
+
+def test_query_cache_matches_full_projection():
+    """The window-row query cache (raw window rows: only patched rows projected after the first
+    refresh of a block) against a stack that projects every window row: bit-identical outputs and
+    state over a block entry and five steps, refresh and active-only."""
+    w = synth.shrink(synth.WORKLOADS[1], dtype="bf16")
+    n_layers = 3
+    dims = B.Dims(d=w.d, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn,
+                  n_pos=w.n_pos, batch=2, block=w.block, win_prefix=w.win_prefix, win_suffix=w.win_suffix,
+                  n_clusters=w.n_clusters, top_k=w.top_k, vocab=0, dtype=B.BF16, resid_fmt=B.RESID_RAW)
+    params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist, mask_id=0,
+                      kmeans_iters=w.kmeans_iters)
+    blk = w.prompt
+    nw = w.win_prefix + w.win_suffix
+    stacks = [RefreshStack(dims, params, n_layers, q_cache=qc) for qc in (True, False)]
+    try:
+        h0 = torch.stack([synth.embeddings(w, 0, "cuda", b).to(torch.bfloat16) for b in range(2)]).contiguous()
+        inits = [torch.stack([torch.tensor(synth.kmeans_init(w, nw, l, 0, 0, b), dtype=torch.int32)
+                              for b in range(2)]).cuda() for l in range(n_layers)]
+        inputs = synth.tensor(w, (98,), (6, 2, w.block, w.d), 1.0, 0, "cuda", "bf16")
+        outs = []
+        for st in stacks:
+            for l in range(n_layers):
+                st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
+            st.entry_forward(blk, h0, inits, full=True)
+            seq = []
+            for i, refresh in enumerate([True, True, False, True, True]):
+                out = st.step(blk, inputs[i], refresh=refresh)
+                torch.cuda.synchronize()
+                seq.append([out.clone(), st.D.clone(), st.topk.clone(), st.delta.clone()] +
+                           [L[k].clone() for L in st.layers for k in ("k_cache", "v_cache", "win_h", "win_z",
+                                                                         "proxy_logits")])
+            outs.append(seq)
+        assert int(stacks[0].layers[0]["q_ok"][0]) == 1
+        for i, (a, b_) in enumerate(zip(*outs)):
+            bad = [j for j, (x, y) in enumerate(zip(a, b_)) if not torch.equal(x, y)]
+            log(f"[q-cache] step {i}: {len(a) - len(bad)}/{len(a)} tensors bit-identical")
+            assert not bad, f"step {i}: the query cache changes tensors {bad}"
+    finally:
+        for st in stacks:
+            st.close()
