@@ -104,6 +104,13 @@ def test_calls_validate_before_launching():
         sel.idx = sel.count = 4096
         assert lib.polestar_drift(h, B.DRIFT_REFRESH, C.byref(L), 64, 4096, None, None, None, C.byref(sel), None,
                                   4096, 4096, ws_bytes, None) == B.E_NULL
+        # a query cache needs its validity flags and 16-byte alignment
+        Lq = B.Layer(w_qkv=4096, k_cache=4096, v_cache=4096, win_z=4096, win_m=4096, proxy_logits=4096, q_win=4096)
+        assert lib.polestar_drift(h, B.DRIFT_REFRESH, C.byref(Lq), 64, 4096, None, None, None, C.byref(sel), None,
+                                  None, 4096, ws_bytes, None) == B.E_NULL
+        Lq.q_ok, Lq.q_win = 4096, 4096 + 8
+        assert lib.polestar_drift(h, B.DRIFT_REFRESH, C.byref(Lq), 64, 4096, None, None, None, C.byref(sel), None,
+                                  None, 4096, ws_bytes, None) == B.E_ALIGN
         # refresh with a misaligned weight
         L.w_o, L.w_gu, L.w_down = 4096 + 2, 4096, 4096
         assert lib.polestar_refresh(h, C.byref(L), 64, 4096, C.byref(sel), None, None, None, 4096, 4096, 4096,
