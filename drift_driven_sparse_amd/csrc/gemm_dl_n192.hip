@@ -1,0 +1,6 @@
+// Instantiations of the weight-streaming projection for workgroup shape DL_N192: 2 x 4 waves of 48 columns, one bf16 plane.
+#include "gemm_dl_impl.h"
+
+hipError_t dl_launch_n192(const DlArgs& g, int max_rows, hipStream_t s) {
+  return dl_impl::launch_shape<2, 4, 3, 1>(g, max_rows, s);
+}

@@ -1,0 +1,6 @@
+// Instantiations of the weight-streaming projection for workgroup shape DL_WIDE: 2 x 4 waves of 64 columns, hi/lo planes.
+#include "gemm_dl_impl.h"
+
+hipError_t dl_launch_wide(const DlArgs& g, int max_rows, hipStream_t s) {
+  return dl_impl::launch_shape<2, 4, 4, 2>(g, max_rows, s);
+}
