@@ -698,3 +698,123 @@ def test_kv_rows_follow_fresh_packet():
     # the projection of the bf16-rounded normalised rows, itself rounded once to bf16
     assert np.array_equal(O.round_bf16(k.reshape(5, 16)), k.reshape(5, 16))
     assert np.array_equal(k.reshape(5, 16), O.round_bf16(want))
+
+
+# ---------------------------------------------------------------- pins of the compositions
+def test_head_summed_drift_clamps_rounding_negatives():
+    """Each head's KL is clamped at 0 before the head sum [Eq. 4 reading: D = sum_h max(0, KL)].
+
+    fp64 rounding makes KL of two nearly equal logit vectors slightly negative about half the
+    time; a seeded search finds such a pair, so an unclamped sum would come out negative."""
+    rng = np.random.default_rng(7)
+    neg = None
+    for _ in range(200):
+        s = rng.normal(size=40) * 3
+        sp = s + rng.normal(size=40) * 1e-9
+        if float(O.kl_logits(s, sp)) < 0:
+            neg = (s, sp)
+            break
+    assert neg is not None
+    s_same = rng.normal(size=40)
+    s_far, sp_far = rng.normal(size=40), rng.normal(size=40)
+    kl_far = float(O.kl_logits(s_far, sp_far))
+    assert kl_far > 0.1
+    heads = np.stack([s_same, neg[0], s_far])[None]          # [1 row, 3 heads, 40 keys]
+    heads_prev = np.stack([s_same, neg[1], sp_far])[None]
+    kl = O.kl_logits(heads, heads_prev)[0]
+    assert kl[0] == 0.0 and kl[1] < 0.0
+    # clamped: the negative head adds nothing; without the clamp the first sum would be < 0
+    assert O.head_summed_drift(heads[:, :2], heads_prev[:, :2])[0] == 0.0
+    assert O.head_summed_drift(heads, heads_prev)[0] == kl_far
+
+
+def _tiny_layer(dtype="f64", K=2, k=1):
+    cfg = O.Cfg(d=32, n_heads=2, n_kv_heads=2, head_dim=16, ffn=48, n_pos=20, block=4, win_prefix=8,
+                win_suffix=4, n_clusters=K, top_k=k, dtype=dtype)
+    rng = np.random.default_rng(11)
+    W = {"wq": rng.normal(size=(32, 32)) / 6, "wk": rng.normal(size=(32, 32)) / 6,
+         "wv": rng.normal(size=(32, 32)) / 6, "wo": rng.normal(size=(32, 32)) / 6,
+         "wg": rng.normal(size=(48, 32)) / 6, "wu": rng.normal(size=(48, 32)) / 6,
+         "wd": rng.normal(size=(32, 48)) / 7}
+    blk = 8
+    nw = len(O.window_positions(blk, cfg.n, cfg.B, cfg.pre, cfg.suf))
+    H = rng.normal(size=(nw, 32))
+    z, m, _ = O.spherical_kmeans(H, K, np.arange(K), 10)
+    ls = {"K": rng.normal(size=(20, 2, 16)), "V": rng.normal(size=(20, 2, 16)),
+          "P": O.round_f32(rng.normal(size=(K, 2, 20)) * 3), "Z": cfg.st(z), "M": m, "H": H}
+    return cfg, W, ls, blk, rng.normal(size=(4, 32)), H
+
+
+def test_drift_reference_is_replaced_after_the_kl():
+    """The drift compares this step's proxy logits with the reference and only then stores them as
+    the next reference [Algorithm 1: P_t is measured against P_{t-1}, then kept].
+
+    First call against a random reference: a clearly positive drift.  A second call on the
+    unchanged state compares the recomputed logits with their own float32 copy, so its drift is
+    zero up to that rounding.  Storing before the KL would make the first drift zero too; not
+    storing would repeat the first drift."""
+    cfg, W, ls, blk, h_act, H = _tiny_layer()
+    no_patch = np.zeros(len(H), dtype=bool)
+    r1 = O.drift_layer(ls, W, cfg, blk, h_act, H, no_patch, True)
+    assert np.array_equal(ls["P"], O.round_f32(r1["proxy_logits"]))
+    assert r1["D"].min() > 0.1
+    r2 = O.drift_layer(ls, W, cfg, blk, h_act, H, no_patch, True)
+    assert np.array_equal(r2["proxy_logits"], r1["proxy_logits"])
+    assert r2["D"].max() <= 1e-9
+
+
+def _grid_residuals(fmt, rows, d, rng):
+    """Residual rows that the format represents exactly, with every block's scale attained."""
+    if fmt == "fp8":
+        # E4M3 values m/8 * 2^e, e in [-4, -2]: multiples of 2^-7 below 0.5
+        mant = rng.integers(8, 16, size=(rows, d)) / 8.0
+        r = mant * np.ldexp(1.0, rng.integers(-4, -1, size=(rows, d))) * rng.choice([-1, 1], size=(rows, d))
+        r[rng.random(size=(rows, d)) < 0.1] = 0.0
+        return r
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    G = 16 if fmt == "nvfp4" else 32
+    r = np.zeros((rows, d))
+    for i in range(rows):
+        for g0 in range(0, d, G):
+            if fmt == "mxint8":
+                X = 2.0 ** -2                        # amax in [2^-2, 2^-1): q_max in [64, 127]
+                q = rng.integers(-63, 64, size=G)
+                q[rng.integers(G)] = int(rng.choice([-1, 1]) * rng.integers(64, 128))
+                r[i, g0:g0 + G] = q * X / 64
+                continue
+            if fmt == "nvfp4":
+                sc = float(rng.choice([2.0 ** -4, 2.0 ** -3, 1.5 * 2.0 ** -4]))   # E4M3 values
+                top = 6.0                            # amax / 6 is the scale itself
+            else:                                    # mxfp4: X = 2^(floor(log2 amax) - 2)
+                sc = 2.0 ** -4
+                top = float(rng.choice([4.0, 6.0]))
+            g = rng.choice(grid[grid <= top], size=G) * rng.choice([-1, 1], size=G)
+            g[rng.integers(G)] = top * rng.choice([-1, 1])
+            r[i, g0:g0 + G] = g * sc
+    return r
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8", "mxint8", "mxfp4"])
+def test_residual_composition_exact_round_trip(fmt):
+    """Window rows stored as residuals to their own cluster's centroid and rebuilt by adding that
+    centroid back [§4.1 "Cluster and Quantize Hidden States"; App. C.3]: on residuals the format
+    represents exactly, rebuild(quantise(h - z_M(i))) == h bit for bit, and the codes decode to
+    h - z_M(i).  Subtracting another cluster's centroid, or rebuilding without the centroid,
+    breaks both (checked on the same rows)."""
+    rng = np.random.default_rng(5)
+    rows, d, K = 9, 64, 3
+    z = rng.integers(-8, 9, size=(K, d)) / 16.0          # bf16-exact, distinct per cluster
+    m = np.arange(rows) % K
+    r = _grid_residuals(fmt, rows, d, rng)
+    h = z[m] + r
+    assert np.array_equal(O.round_bf16(h), h)              # the rows are bf16 values
+    codes, scales = O.residual_quantize(h, z, m, fmt)
+    deq = O.RESID_CODECS[fmt][1](codes, scales).astype(np.float64)
+    assert np.array_equal(deq, r)
+    back = O.residual_dequantize(codes, scales, z, m, O.round_bf16, fmt)
+    assert np.array_equal(back, h)
+    # the mistakes this pins: the wrong centroid, or none, at either end
+    wrong = (m + 1) % K
+    c2, s2 = O.residual_quantize(h, z, wrong, fmt)
+    assert not np.array_equal(O.residual_dequantize(c2, s2, z, wrong, O.round_bf16, fmt), h)
+    assert not np.array_equal(O.residual_dequantize(codes, scales, np.zeros_like(z), m, O.round_bf16, fmt), h)
