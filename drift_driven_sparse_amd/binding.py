@@ -21,6 +21,7 @@ RESID_BY_NAME = {"raw": RESID_RAW, "nvfp4": RESID_NVFP4, "fp8": RESID_FP8, "mxin
 CLUSTER_ENTRY, CLUSTER_UPDATE = 0, 1
 DRIFT_REFRESH, DRIFT_ACTIVE_ONLY = 0, 1
 ENTRY_FULL, ENTRY_WINDOW = 0, 1
+PROXY_ALL, PROXY_ACTIVE = 0, 1
 W_QKV, W_O, W_GU, W_DOWN, W_KV, W_LM = 0, 1, 2, 3, 4, 5
 
 EXPORTED = [
@@ -43,7 +44,8 @@ class Dims(C.Structure):
 
 class Params(C.Structure):
     _fields_ = [("rms_eps", C.c_float), ("tau_s", C.c_float), ("tau_suf", C.c_float), ("alpha", C.c_float),
-                ("hist", C.c_int32), ("mask_id", C.c_int32), ("kmeans_iters", C.c_int32)]
+                ("hist", C.c_int32), ("mask_id", C.c_int32), ("kmeans_iters", C.c_int32),
+                ("proxy_support", C.c_int32)]
 
 
 class Layer(C.Structure):

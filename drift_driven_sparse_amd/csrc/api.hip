@@ -310,6 +310,10 @@ AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws, int ca
   a.block = d.block;
   a.kc = L->k_cache;
   a.vc = L->v_cache;
+  a.key_lo = 0;
+  a.key_hi = d.n_pos;
+  a.pkey_lo = 0;
+  a.pkey_hi = d.n_pos;
   a.o = at<char>(ws, h->ws.o);
   a.o_planes = std::is_same<T, bf16_t>::value;
   a.kl = at<float>(ws, h->ws.kl);
@@ -325,11 +329,16 @@ AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws, int ca
 
 // Attention of the query rows over all n_pos keys, then the merge of the key chunks and the KL
 // drift of the kept logit rows.
-template <typename T>
-int run_attention(polestar_handle* h, AttnArgs& a, hipStream_t s) {
+void set_row_groups(const polestar_handle* h, AttnArgs& a) {
   const int tiles = PS_CEIL_DIV(a.n_tok + a.n_proxy, 16);
   a.row_groups = tiles >= 2 * h->attn_rgroups ? h->attn_rgroups : 1;
   a.group_tiles = PS_CEIL_DIV(tiles, a.row_groups);
+}
+
+template <typename T>
+int run_attention(polestar_handle* h, AttnArgs& a, hipStream_t s) {
+  a.n_stage_proxy = a.n_proxy;
+  set_row_groups(h, a);
   hipError_t e;
   {
     PROF(POLESTAR_K_ATTN);
@@ -338,6 +347,46 @@ int run_attention(polestar_handle* h, AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return POLESTAR_E_HIP;
   PROF(POLESTAR_K_KL);   // chunk merge and KL drift
   return hip_status(launch_merge_kl(a, std::is_same<T, bf16_t>::value, s));
+}
+
+// Proxy attention over the active block's keys only (POLESTAR_PROXY_ACTIVE): `a` describes the
+// rows as for run_attention (n_tok token rows, then n_proxy centroid rows whose queries start at
+// q_proxy); the token rows attend over every key, the centroid rows over [blk_start,
+// blk_start + block) in a launch of their own; one merge/KL launch follows.
+template <typename T>
+int run_attention_active_keys(polestar_handle* h, AttnArgs& a, const float* q_proxy, int32_t blk_start,
+                              hipStream_t s) {
+  const int K = a.n_proxy;
+  hipError_t e = hipSuccess;
+  AttnArgs tok = a;
+  tok.n_proxy = 0;
+  tok.n_stage_proxy = K;
+  if (tok.n_tok > 0) {
+    set_row_groups(h, tok);
+    PROF(POLESTAR_K_ATTN);
+    e = launch_attention<T>(tok, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  AttnArgs px = a;
+  px.n_tok = 0;
+  px.n_stage_proxy = K;
+  px.q = q_proxy;
+  px.q_win = nullptr;
+  px.key_lo = blk_start;
+  px.key_hi = blk_start + h->dm.block;
+  px.chunk_keys = 32 * PS_CEIL_DIV(px.key_hi - (px.key_lo & ~7), 32);
+  px.n_chunks = 1;
+  set_row_groups(h, px);
+  {
+    PROF(POLESTAR_K_ATTN);
+    e = launch_attention<T>(px, s);
+  }
+  if (e != hipSuccess) return POLESTAR_E_HIP;
+  tok.n_proxy = K;
+  tok.pkey_lo = px.key_lo;
+  tok.pkey_hi = px.key_hi;
+  PROF(POLESTAR_K_KL);
+  return hip_status(launch_merge_kl(tok, std::is_same<T, bf16_t>::value, s));
 }
 
 template <typename T>
@@ -375,6 +424,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   if (qcache) {
     p.flags = at<int32_t>(ws, h->ws.flags);
     p.q_ok = L->q_ok;
+    p.q_tag = blk_start + 1;
     p.map = at<int32_t>(ws, h->ws.qmap);
     p.count = p.map + (size_t)d.batch * h->win_max;
     p.q_win = L->q_win;
@@ -397,7 +447,11 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   at_.act_logits = act_logits;
   at_.act_kl = delta != nullptr;
   at_.chk = h->chk.attn_out;
-  if ((rc = run_attention<T>(h, at_, s))) return rc;
+  if (at_.n_proxy > 0 && h->pr.proxy_support == POLESTAR_PROXY_ACTIVE)
+    rc = run_attention_active_keys<T>(h, at_, q + (size_t)(d.block + g.n_win) * h->nq, blk_start, s);
+  else
+    rc = run_attention<T>(h, at_, s);
+  if (rc) return rc;
   // 3. top-k clusters and the selected rows
   TopkArgs tk;
   memset(&tk, 0, sizeof(tk));
@@ -418,6 +472,7 @@ int do_drift(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   tk.delta = (act_logits && delta) ? delta : nullptr;
   tk.refresh = refresh;
   tk.q_ok = qcache ? L->q_ok : nullptr;
+  tk.q_tag = blk_start + 1;
   PROF(POLESTAR_K_TOPK);
   return hip_status(launch_topk(tk, s));
 }
@@ -878,6 +933,7 @@ int do_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_
   a.block = 0;
   a.proxy_logits = L->proxy_logits;
   a.proxy_kl = 0;
+  if (h->pr.proxy_support == POLESTAR_PROXY_ACTIVE) return run_attention_active_keys<T>(h, a, q, blk_start, s);
   return run_attention<T>(h, a, s);
 }
 
@@ -1026,6 +1082,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   if (!(p.rms_eps >= 0.f) || p.hist < 0 || p.hist > 16 || p.kmeans_iters < 0 || p.kmeans_iters > 1000)
     return POLESTAR_E_ARG;
   if (d.vocab > 0 && (p.mask_id < -1 || p.mask_id >= d.vocab)) return POLESTAR_E_ARG;
+  if (p.proxy_support != POLESTAR_PROXY_ALL && p.proxy_support != POLESTAR_PROXY_ACTIVE) return POLESTAR_E_ARG;
   polestar_handle* h = new (std::nothrow) polestar_handle;
   if (!h) return POLESTAR_E_SHAPE;
   memset(h, 0, sizeof(*h));

@@ -6,7 +6,8 @@
 // [batch][Hkv][dh][n] so that V^T fragments are contiguous along keys.
 //
 // bf16 path (attn_chunk_kernel): workgroups over (key chunk, head); MFMA 16x16x32 with the
-// float32 queries and the probabilities as bf16 hi + lo pairs, online softmax per chunk.  Logits
+// float32 queries and the probabilities as three-term bf16 splits (float32 precision), online
+// softmax per chunk.  Logits
 // of proxy rows and (when requested) active rows go to a staging buffer.  One following launch
 // (attn_merge_kl_kernel) combines the chunks of the token rows and forms the KL drift of the
 // staged rows against the previous logits, which the staged logits then replace.
@@ -39,7 +40,7 @@ PS_DEV bool row_keeps_logits(const AttnArgs& a, int row) {
   return row >= a.n_tok || (row < a.block && a.act_logits != nullptr);
 }
 PS_DEV int stage_row(const AttnArgs& a, int row) {   // staging buffer row: [proxies; active]
-  return row >= a.n_tok ? row - a.n_tok : a.n_proxy + row;
+  return row >= a.n_tok ? row - a.n_tok : a.n_stage_proxy + row;
 }
 
 // ---- bf16 MFMA attention over key chunks ------------------------------------------------------
@@ -65,14 +66,28 @@ PS_DEV uint4 frag_hi(const float* x) {
   for (int e = 0; e < 4; ++e) w[e] = pack2(x[2 * e], x[2 * e + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
-// lo part of the bf16 hi/lo pair of x (hi = the pair frag_hi packs)
-PS_DEV uint4 frag_lo(const float* x, const uint4& hi) {
-  const uint32_t h[4] = {hi.x, hi.y, hi.z, hi.w};
-  uint32_t w[4];
+// Three-term bf16 split of eight float32 values: x = t0 + t1 + t2 + e with t0 = rn(x),
+// t1 = rn(x - t0), t2 = rn(x - t0 - t1) (each difference exact in float32), |e| <= 2^-24 |x|
+// roughly: the float32 operands of the attention products keep float32 precision through
+// bf16 matrix products.
+struct Split3 { uint4 t[3]; };
+PS_DEV Split3 frag_split3(const float* x) {
+  Split3 s;
+  float r[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = pack2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const uint4 h = frag_hi(r);
+    s.t[k] = h;
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[2 * e] -= __uint_as_float(hw[e] << 16);
+      r[2 * e + 1] -= __uint_as_float(hw[e] & 0xFFFF0000u);
+    }
+  }
+  return s;
 }
 
 template <int DH, int NWV>
@@ -95,8 +110,9 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int kvh = (h * a.hkv) / a.hq;
-  const int k0 = chunk * a.chunk_keys;
-  const int k1 = min(n, k0 + a.chunk_keys);
+  // keys [key_lo, key_hi), in chunks from key_lo rounded down to 8 keys (aligned V^T loads)
+  const int k0 = (a.key_lo & ~7) + chunk * a.chunk_keys;
+  const int k1 = min(a.key_hi, k0 + a.chunk_keys);
   const int nst = (k1 - k0 + 31) >> 5;
   const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)b * n * a.hkv * DH + kvh * DH;
   const uint16_t* vt = (const uint16_t*)a.vc + ((int64_t)b * a.hkv + kvh) * DH * n;
@@ -131,7 +147,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   // query fragments (B operand of S^T): lane holds row c16 of each tile, dh [32 ks + 8 g4, +8)
   // (loaded before the first K/V stages are issued and converted after, so that the query
   // loads overlap the K/V loads)
-  uint4 qhi[RTW][KS], qlo[RTW][KS];
+  Split3 qs[RTW][KS];
   float4 qraw[RTW][KS][2];
   bool tile_on[RTW], q_valid[RTW];
   auto load_q = [&](auto Tc) __attribute__((always_inline)) {
@@ -158,8 +174,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
       float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = q_valid[t] ? x[e] * qscale : 0.f;
-      qhi[t][ks] = frag_hi(x);
-      qlo[t][ks] = frag_lo(x, qhi[t][ks]);
+      qs[t][ks] = frag_split3(x);
     }
   };
   [&]<int... T>(std::integer_sequence<int, T...>) {
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
     const int key0 = k0 + 32 * step;
     const int kg = key0 + 8 * g4;            // first key of this lane's 8-key group
     const bool shift = kg < n && kg + 8 > n; // ragged tail: V^T was loaded from n - 8
-    const bool full = key0 + 32 <= k1;       // no key of the step is past the chunk
+    const bool full = key0 >= a.key_lo && key0 + 32 <= k1;   // every key of the step is in range
     auto tile_step = [&](auto Tc) __attribute__((always_inline)) {
       constexpr int t = decltype(Tc)::value;
       if (!tile_on[t]) return;
@@ -190,8 +205,9 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const uint4 kf = buf[(kt * KS + ks) * 64 + lane];
-          acc = mfma(kf, qhi[t][ks], acc);
-          acc = mfma(kf, qlo[t][ks], acc);
+          acc = mfma(kf, qs[t][ks].t[2], acc);   // smallest terms first
+          acc = mfma(kf, qs[t][ks].t[1], acc);
+          acc = mfma(kf, qs[t][ks].t[0], acc);
         }
         sacc[kt] = acc;
       }
@@ -200,18 +216,18 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) v[e] = sacc[e >> 2][e & 3];
       if (!full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = kg + e < k1 ? v[e] : -INFINITY;
+        for (int e = 0; e < 8; ++e) v[e] = (kg + e >= a.key_lo && kg + e < k1) ? v[e] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
       const int row = (tile0 + wave * RTW + t) * 16 + c16;
       if (row < nrows && row_keeps_logits(a, row)) {
-        float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n + kg;
-        if (kg + 8 <= k1) {
+        float* lg = a.lg_stage + (((int64_t)b * (a.n_stage_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n + kg;
+        if (kg >= a.key_lo && kg + 8 <= k1) {
           *(float4*)lg = make_float4(v[0] * kLn2, v[1] * kLn2, v[2] * kLn2, v[3] * kLn2);
           *(float4*)(lg + 4) = make_float4(v[4] * kLn2, v[5] * kLn2, v[6] * kLn2, v[7] * kLn2);
         } else {
           for (int e = 0; e < 8; ++e)
-            if (kg + e < k1) lg[e] = v[e] * kLn2;
+            if (kg + e >= a.key_lo && kg + e < k1) lg[e] = v[e] * kLn2;
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -237,7 +253,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = 0.f;
       }
-      const uint4 phi = frag_hi(v), plo = frag_lo(v, phi);
+      const Split3 pv = frag_split3(v);
       if (rescale) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
@@ -245,8 +261,9 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint4 vf = buf[(FK + dt) * 64 + lane];
-        o[t][dt] = mfma(vf, phi, o[t][dt]);
-        o[t][dt] = mfma(vf, plo, o[t][dt]);
+        o[t][dt] = mfma(vf, pv.t[2], o[t][dt]);
+        o[t][dt] = mfma(vf, pv.t[1], o[t][dt]);
+        o[t][dt] = mfma(vf, pv.t[0], o[t][dt]);
       }
     };
     [&]<int... T>(std::integer_sequence<int, T...>) {
@@ -381,8 +398,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int rr = i / DH, dd = i % DH;
     qs[i] = rr < nr ? a.q[((int64_t)b * a.mq + r0 + rr) * (a.hq * DH) + h * DH + dd] : 0.f;
   }
-  for (int c0 = 0; c0 < n; c0 += kKC) {
-    const int nk = min(kKC, n - c0);
+  const int klo = a.key_lo, khi = a.key_hi;
+  for (int c0 = klo; c0 < khi; c0 += kKC) {
+    const int nk = min(kKC, khi - c0);
     __syncthreads();
     for (int i = tid; i < kKC * DH; i += blockDim.x) {
       const int j = i / DH, dd = i % DH;
@@ -405,14 +423,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int row = r0 + rr;
     float* s = sc + rr * n;
     if (row_keeps_logits(a, row)) {
-      float* lg = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n;
-      for (int j = lane; j < n; j += 64) lg[j] = s[j];
+      float* lg = a.lg_stage + (((int64_t)b * (a.n_stage_proxy + a.block) + stage_row(a, row)) * a.hq + h) * n;
+      for (int j = klo + lane; j < khi; j += 64) lg[j] = s[j];
     }
     float m = -INFINITY;
-    for (int j = lane; j < n; j += 64) m = fmaxf(m, s[j]);
+    for (int j = klo + lane; j < khi; j += 64) m = fmaxf(m, s[j]);
     m = wave_max(m);
     float z = 0.f;
-    for (int j = lane; j < n; j += 64) {
+    for (int j = klo + lane; j < khi; j += 64) {
       const float p = expf(s[j] - m);
       s[j] = p;
       z += p;
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const float* p = sc + rr * n;
     const float* vr = vt + (int64_t)dd * n;
     float t = 0.f;
-    for (int j = 0; j < n; ++j) t = fmaf(p[j], vr[j], t);
+    for (int j = klo; j < khi; ++j) t = fmaf(p[j], vr[j], t);
     const float v = t * rinv[rr];
     const int row = r0 + rr;
     ((float*)a.o)[((int64_t)b * a.mt + row) * (a.hq * DH) + h * DH + dd] = v;
@@ -507,21 +525,26 @@ PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
   if (item >= nst * a.hq) return;   // uniform over the workgroup
   const int sr = item / a.hq, h = item % a.hq;
-  const int n = a.n_pos;
-  const float* s = a.lg_stage + (((int64_t)b * (a.n_proxy + a.block) + sr) * a.hq + h) * n;
+  const int np = a.n_pos;
+  const float* s = a.lg_stage + (((int64_t)b * (a.n_stage_proxy + a.block) + sr) * a.hq + h) * np;
   float* prev;
   float* out;
   bool do_kl;
+  int lo = 0, n = np;   // key range of the row's logits
   if (sr < a.n_proxy) {
-    prev = a.proxy_logits + (((int64_t)b * a.n_proxy + sr) * a.hq + h) * n;
+    prev = a.proxy_logits + (((int64_t)b * a.n_proxy + sr) * a.hq + h) * np;
     out = a.kl + ((int64_t)b * a.n_proxy + sr) * a.hq + h;
     do_kl = a.proxy_kl != 0;
+    lo = a.pkey_lo;
+    n = a.pkey_hi - a.pkey_lo;
   } else {
     const int r = sr - a.n_proxy;
-    prev = a.act_logits + (((int64_t)b * a.block + r) * a.hq + h) * n;
+    prev = a.act_logits + (((int64_t)b * a.block + r) * a.hq + h) * np;
     out = a.akl + ((int64_t)b * a.block + r) * a.hq + h;
     do_kl = a.act_kl != 0;
   }
+  s += lo;
+  prev += lo;
   float sv[kKlPer], pv[kKlPer];
 #pragma unroll
   for (int i = 0; i < kKlPer; ++i) {
@@ -606,7 +629,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
       }
       if (lane == 0) a.sel_count[b] = base;
     }
-    if (tid == 0 && a.q_ok) a.q_ok[b] = 1;   // every window row's query is now current
+    if (tid == 0 && a.q_ok) a.q_ok[b] = a.q_tag;   // every window row's query is now current for this block
   } else {
     if (tid == 0) a.sel_count[b] = 0;
   }
@@ -635,7 +658,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int tiles = PS_CEIL_DIV(nrows, 16);
     if (a.row_groups < 1 || a.group_tiles * a.row_groups < tiles) return hipErrorInvalidValue;
     const int nwv = 2 * PS_CEIL_DIV(a.group_tiles, 2);   // one wave per 16-row tile, even count
-    if (nwv > 12 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.n_pos)
+    if (nwv > 12 || a.n_pos < 8 || a.chunk_keys % 32 || a.n_chunks * a.chunk_keys < a.key_hi - (a.key_lo & ~7) ||
+        a.key_lo < 0 || a.key_hi > a.n_pos || a.key_lo >= a.key_hi)
       return hipErrorInvalidValue;
     dim3 grid(a.n_chunks, a.hq, a.batch * a.row_groups);
     auto go = [&](auto DHc, auto NWc) {

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void prep_qkv_kernel(PrepArgs a) {
       // query cache: window rows that need a query (all of them after block entry, else the
       // patched ones) are staged in row order after the active rows, then the centroids
       const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-      const bool all = a.q_ok[b] == 0;
+      const bool all = a.q_ok[b] != a.q_tag;   // cached queries of another block position, or none
       const bool need = tid < a.n_win && (all || a.flags[(int64_t)b * a.win_max + tid] != 0);
       const unsigned long long m = __ballot(need);
       if (lane == 0) bal[wave] = m;

@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256) void dl_finish_kernel(DlArgs g) {
     // in their outputs and take one store; values (transposed cache) go element by element
     const EpiParams& e = g.e;
     if (c < e.nq + e.nkv) {
-      if (e.chk) *(float4*)(e.chk + ((int64_t)b * e.chk_rows + r) * e.chk_ld + c) = v;
       const QkvDest dst = qkv_dest(e, b, r);
+      if (e.chk) *(float4*)(e.chk + ((int64_t)b * e.chk_rows + dst.row) * e.chk_ld + c) = v;
       if (c < e.nq) *(float4*)(dst.q + c) = v;
       else if (dst.pos >= 0) Quad<T>::store((T*)e.kc + kv_index(e, b, dst.pos, c - e.nq, 0), vv);
       return;

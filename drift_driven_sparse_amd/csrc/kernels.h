@@ -111,33 +111,32 @@ PS_DEV int64_t kv_index(const EpiParams& e, int b, int pos, int col, int is_v) {
   return ((int64_t)b * e.nkv + col) * e.n_pos + pos;
 }
 
-// QKV projection row r (active block, window rows, centroids) of the rounded normalised row,
-// column n, sum v: queries stay float32; K/V of the active block and of patched window rows go
-// to the cache.
-// Cache position whose K/V QKV row r writes: the active block's, or a patched window row's; -1:
-// none (unpatched window rows, centroids).
-// Destination of QKV row r: its query row (as a pointer to column 0) and the cache position of its
-// K/V (-1: none).
-struct QkvDest { float* q; int pos; };
+// Destination of QKV row r (active block, window rows, centroids): its query row (as a pointer to
+// column 0), the cache position of its K/V (-1: none, i.e. unpatched window rows and centroids)
+// and its logical row [active; window row w at block + w; centroid c at block + n_win + c], the
+// row of the check copy.  With the query cache only the staged window rows are projected.
+struct QkvDest { float* q; int pos; int row; };
 PS_DEV QkvDest qkv_dest(const EpiParams& e, int b, int r) {
-  if (r < e.block) return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, e.geom.blk_start + r};
+  if (r < e.block) return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, e.geom.blk_start + r, r};
   int w = r - e.block;
   if (e.qmap) {
     const int np = e.qcount[b];
-    if (w >= np)   // centroid rows follow the staged window rows
-      return {e.q + ((int64_t)b * e.q_rows + e.block + e.geom.n_win + (w - np)) * e.nq, -1};
+    if (w >= np) {   // centroid rows follow the staged window rows
+      const int lr = e.block + e.geom.n_win + (w - np);
+      return {e.q + ((int64_t)b * e.q_rows + lr) * e.nq, -1, lr};
+    }
     w = e.qmap[(int64_t)b * e.win_max + w];
     const int pos = e.flags[(int64_t)b * e.win_max + w] ? e.geom.pos(w) : -1;
-    return {e.q_win + ((int64_t)b * e.win_max + w) * e.nq, pos};
+    return {e.q_win + ((int64_t)b * e.win_max + w) * e.nq, pos, e.block + w};
   }
   const int pos = (w < e.geom.n_win && e.flags[(int64_t)b * e.win_max + w]) ? e.geom.pos(w) : -1;
-  return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, pos};
+  return {e.q + ((int64_t)b * e.q_rows + r) * e.nq, pos, r};
 }
 
 template <typename T>
 PS_DEV void epi_qkv_elem(const EpiParams& e, int b, int r, int n, float v) {
-  if (e.chk) e.chk[((int64_t)b * e.chk_rows + r) * e.chk_ld + n] = v;
   const QkvDest dst = qkv_dest(e, b, r);
+  if (e.chk) e.chk[((int64_t)b * e.chk_rows + dst.row) * e.chk_ld + n] = v;
   if (n < e.nq) {
     dst.q[n] = v;
     return;
@@ -282,10 +281,10 @@ struct PrepArgs {
   int32_t a_tiles;        // > 0: a_qkv fragment-packed with this many row tiles (bf16)
   const void* h_act; int64_t act_bstride;   // block rows per sequence, act_bstride elements apart
   const void* ws_rows; const void* win_z;
-  // query cache (map set): only the window rows that need a query (all when q_ok[b] == 0, else
-  // the patched ones) are staged, after the active rows and before the centroids; map[b][j] is the
+  // query cache (map set): only the window rows that need a query (all unless q_ok[b] == q_tag,
+  // the tag of this block position, else the patched ones) are staged, after the active rows and before the centroids; map[b][j] is the
   // window row of staged row block + j, count[b] their number
-  const int32_t* flags; const int32_t* q_ok; int32_t* map; int32_t* count;
+  const int32_t* flags; const int32_t* q_ok; int32_t q_tag; int32_t* map; int32_t* count;
   float* q_win;   // the layer's cached window-row queries (passed on to the QKV epilogue)
   void* a_qkv; int64_t a_bstride; float eps;
 };
@@ -297,7 +296,10 @@ struct AttnArgs {
   int32_t batch, n_pos, hq, hkv, dh, mq, mt;
   int32_t n_tok;          // token query rows per sequence (block + n_win, or block)
   int32_t n_proxy;        // centroid query rows (K or 0)
+  int32_t n_stage_proxy;  // proxy rows in the logit staging layout [proxies; active]
   int32_t block;
+  int32_t key_lo, key_hi; // keys the query rows of this launch attend to: [key_lo, key_hi)
+  int32_t pkey_lo, pkey_hi;   // KL: key range of the proxy rows' logits (active rows: all keys)
   const float* q;         // [batch][mq][hq*dh]
   const float* q_win;     // nullable: queries of token rows block.. (window rows), [batch][win_max][hq*dh]
   int32_t win_max;
@@ -308,7 +310,7 @@ struct AttnArgs {
   float* kl;              // [batch][K][hq]
   int32_t proxy_kl;       // 1: KL of the proxy rows against proxy_logits; 0: only store their logits
   float* act_logits;      // [batch][block][hq][n] or null
-  float* lg_stage;        // staged logits of kept rows [batch][n_proxy + block][hq][n]
+  float* lg_stage;        // staged logits of kept rows [batch][n_stage_proxy + block][hq][n]
   int32_t chunk_keys;     // bf16 path: keys per workgroup (multiple of 32)
   int32_t n_chunks;       // workgroups along the keys; > 1 -> partial states merged by launch_merge_kl
   int32_t row_groups;     // bf16 path: workgroups along the query rows, group_tiles 16-row tiles each
@@ -330,7 +332,8 @@ struct TopkArgs {
   float* D; int32_t* topk; int32_t* sel_idx; int32_t* sel_count;
   const float* akl; float* delta;
   int32_t refresh;
-  int32_t* q_ok;   // query cache validity [batch] (nullable): set after a refresh
+  int32_t* q_ok;   // query cache validity [batch] (nullable): set to q_tag after a refresh
+  int32_t q_tag;   // blk_start + 1: the block position the cached queries belong to
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 

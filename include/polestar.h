@@ -97,6 +97,12 @@ enum {
 enum { POLESTAR_CLUSTER_ENTRY = 0, POLESTAR_CLUSTER_UPDATE = 1 };
 enum { POLESTAR_DRIFT_REFRESH = 0, POLESTAR_DRIFT_ACTIVE_ONLY = 1 };
 enum { POLESTAR_ENTRY_FULL = 0, POLESTAR_ENTRY_WINDOW = 1 };
+/* Keys of the proxy attention [§4.1 "Measuring Drift and Layer-wise KV Updates"; Eq. 3]:
+ * ALL    every position, the cached keys together with the recomputed active-block keys (the
+ *        attention support the page's drift is defined over);
+ * ACTIVE the active block's keys only, positions [blk_start, blk_start + block).  The proxy
+ *        logits buffer then holds meaningful values at those key positions only. */
+enum { POLESTAR_PROXY_ALL = 0, POLESTAR_PROXY_ACTIVE = 1 };
 enum {
   POLESTAR_W_QKV = 0,  /* src [(n_heads + 2 n_kv_heads) head_dim, d] = rows of W_Q, W_K, W_V */
   POLESTAR_W_O = 1,    /* src [d, n_heads head_dim] */
@@ -134,6 +140,7 @@ typedef struct polestar_params {
   int32_t hist;         /* drift history length h (5), 0..16 */
   int32_t mask_id;      /* vocabulary id excluded from the confidence max */
   int32_t kmeans_iters; /* Lloyd iterations at block entry (10) */
+  int32_t proxy_support; /* POLESTAR_PROXY_ALL (0) | POLESTAR_PROXY_ACTIVE */
 } polestar_params;
 
 typedef struct polestar_handle polestar_handle;
@@ -156,9 +163,14 @@ typedef struct polestar_layer {
                            window rows' queries [batch, win_max, n_heads * head_dim] f32 kept
                            across steps, in/out; a refresh-mode drift then projects only the
                            rows a packet patched (a raw row changes only there, and its query
-                           depends on its stored value alone) */
-  int32_t* q_ok;        /* with q_win: [batch]; block entry sets 0 (every window row is
-                           projected at the next refresh), a refresh-mode drift sets 1 */
+                           depends on its stored value and W_Q alone) */
+  int32_t* q_ok;        /* with q_win: [batch] i32, the block position the cached queries
+                           belong to: a refresh-mode drift at blk_start sets blk_start + 1;
+                           a refresh at any other blk_start, or q_ok[b] == 0, projects every
+                           window row again; block entry (polestar_entry,
+                           polestar_cluster(ENTRY)) sets 0.  A caller that writes win_h or the
+                           packed w_qkv outside those calls (e.g. layer-0 window rows of newly
+                           decoded tokens, new weights) must set q_ok to 0 first. */
 } polestar_layer;
 
 /* Update packet U(t,l): rows of selected window positions.  Row r of
@@ -183,7 +195,9 @@ typedef struct polestar_check {
 
 /* ---- handle ------------------------------------------------------------ */
 /* Validates dims/params (host only, no HIP call) and creates a handle.
- * Returns E_NULL, E_SHAPE, E_DTYPE or E_UNSUPPORTED on bad input. */
+ * Returns E_NULL, E_SHAPE, E_DTYPE or E_UNSUPPORTED on bad input, E_ARG on a bad scalar
+ * parameter (eps < 0, hist outside 0..16, kmeans_iters outside 0..1000, mask_id, an unknown
+ * proxy_support). */
 int polestar_create(const polestar_dims* dims, const polestar_params* params, polestar_handle** out);
 void polestar_destroy(polestar_handle* h);
 const char* polestar_strerror(int code);
@@ -234,7 +248,8 @@ int polestar_cluster(polestar_handle* h, int mode, const polestar_layer* L, int3
  *    workspace patched from its packet; u_in itself is not read and may be
  *    NULL),
  *    runs softmax attention of the active and window rows over all n_pos
- *    keys, runs proxy attention of the centroid queries over the same keys,
+ *    keys, runs proxy attention of the centroid queries over the keys that
+ *    params.proxy_support names (all positions, or the active block's),
  *    scores each cluster by D_c = sum over heads of max(0, KL(P_t || P_prev))
  *    against L->proxy_logits (then overwritten with P_t's logits), picks the
  *    top-k clusters (largest D, lowest index on ties) and writes the selected
@@ -312,7 +327,8 @@ int polestar_step(polestar_handle* h, int mode, int32_t n_layers, const polestar
  *  of the first commit drift delta (pass it for the last layer; §4.2
  *  "Current Block Commit").  Last, the proxy logits of the new centroids over
  *  the fresh cache are written to L->proxy_logits: the reference of the
- *  first drift score.  Needs every weight, cache and window pointer of L.
+ *  first drift score (over the keys params.proxy_support names).  Needs every
+ *  weight, cache and window pointer of L.
  */
 int polestar_entry(polestar_handle* h, int mode, const polestar_layer* L, int32_t blk_start, const void* h_in,
                    const int32_t* init_idx, void* h_out, double* objective, float* act_logits, void* ws,

@@ -511,13 +511,15 @@ class Cfg:
 
     def __init__(self, d, n_heads, n_kv_heads, head_dim, ffn, n_pos, block, win_prefix, win_suffix,
                  n_clusters, top_k, dtype, resid="raw", rms_eps=1e-6, hist=5, alpha=10.0,
-                 tau_s=0.9, tau_suf=0.9, kmeans_iters=10, **_):
+                 tau_s=0.9, tau_suf=0.9, kmeans_iters=10, proxy_support="all", **_):
         self.d, self.hq, self.hkv, self.dh, self.ffn = d, n_heads, n_kv_heads, head_dim, ffn
         self.n, self.B, self.pre, self.suf = n_pos, block, win_prefix, win_suffix
         self.K, self.k = n_clusters, top_k
         self.dtype, self.resid, self.eps = dtype, resid, rms_eps
         self.hist, self.alpha, self.tau_s, self.tau_suf = hist, alpha, tau_s, tau_suf
         self.iters = kmeans_iters
+        assert proxy_support in ("all", "active")
+        self.proxy_support = proxy_support
         self.st = storer(dtype)
 
     @staticmethod
@@ -526,9 +528,27 @@ class Cfg:
                   n_pos=w.n_pos, block=w.block, win_prefix=w.win_prefix, win_suffix=w.win_suffix,
                   n_clusters=w.n_clusters, top_k=w.top_k, dtype=dtype or w.dtype, resid=w.resid,
                   rms_eps=w.rms_eps, hist=w.hist, alpha=w.alpha, tau_s=w.tau_s, tau_suf=w.tau_suf,
-                  kmeans_iters=w.kmeans_iters)
+                  kmeans_iters=w.kmeans_iters, proxy_support=getattr(w, "proxy_support", "all"))
         kw.update(over)
         return Cfg(**kw)
+
+
+def proxy_keys(cfg: Cfg, blk_start: int) -> np.ndarray:
+    """Key positions of the proxy attention [§4.1 "Measuring Drift and Layer-wise KV Updates";
+    Eq. 3].  "all": every position, the cached keys joined with the recomputed active-block keys
+    (the support the drift of Eq. 4 is defined over); "active": the active block's keys only."""
+    if cfg.proxy_support == "active":
+        return active_positions(blk_start, cfg.B)
+    return np.arange(cfg.n, dtype=np.int64)
+
+
+def proxy_drift(zq: np.ndarray, K: np.ndarray, V: np.ndarray, P_prev: np.ndarray, cfg: Cfg, blk_start: int):
+    """Proxy attention logits of the centroid queries over the proxy keys and their KL drift
+    against the previous logits of the same keys (P_prev [K, Hq, n], logits at key positions).
+    Returns (logits [K, Hq, len(keys)], kl [K, Hq], key positions)."""
+    keys = proxy_keys(cfg, blk_start)
+    _, plog = attention(zq, K[keys], V[keys], cfg.hq, cfg.hkv)
+    return plog, kl_logits(plog, np.asarray(P_prev)[..., keys]), keys
 
 
 def window_rows_now(ls: Dict, cfg: Cfg) -> np.ndarray:
@@ -593,14 +613,15 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
     if refresh:
         k_eff = min(cfg.K, nw)
         zq = project(ls["Z"], W["wq"], eps, st).reshape(cfg.K, hq, dh)
-        _, plog = attention(zq, K, V, hq, hkv)
-        kl = kl_logits(plog, ls["P"])                 # [K, Hq]
+        plog, kl, keys = proxy_drift(zq, K, V, ls["P"], cfg, blk_start)   # kl: [K, Hq]
         D = np.sum(np.maximum(kl, 0.0), axis=1)
         D[k_eff:] = 0.0
         topk = topk_clusters(D, cfg.k, k_eff)
         S = select_rows(ls["M"], topk)
-        ls["P"] = round_f32(plog)
-        res.update(D=D, kl=kl, topk=topk, S=S, proxy_q=zq, proxy_logits=plog)
+        P = np.array(ls["P"], dtype=np.float64, copy=True)
+        P[..., keys] = round_f32(plog)
+        ls["P"] = P
+        res.update(D=D, kl=kl, topk=topk, S=S, proxy_q=zq, proxy_logits=plog, proxy_keys=keys)
     return res
 
 
@@ -797,6 +818,8 @@ def block_entry_layer_state(H_in: np.ndarray, K: np.ndarray, V: np.ndarray, Wq: 
     else:
         ls["H"] = hw.copy()
     zq = project(z, Wq, cfg.eps, cfg.st).reshape(cfg.K, cfg.hq, cfg.dh)
-    _, plog = attention(zq, ls["K"], ls["V"], cfg.hq, cfg.hkv)
-    ls["P"] = round_f32(plog)
+    keys = proxy_keys(cfg, blk_start)
+    _, plog = attention(zq, ls["K"][keys], ls["V"][keys], cfg.hq, cfg.hkv)
+    ls["P"] = np.zeros((cfg.K, cfg.hq, cfg.n))
+    ls["P"][..., keys] = round_f32(plog)
     return ls

@@ -140,6 +140,7 @@ class Workload:
     noise_var: float = 0.1
     single_layer_next: bool = False   # also instantiate layer l+1 (norm, W_K, W_V, KV, window)
     rms_eps: float = 1e-6
+    proxy_support: str = "all"        # keys of the proxy attention: "all" positions or the "active" block
 
     @property
     def n_pos(self) -> int:

@@ -60,13 +60,58 @@ def row_err(a, b):
 
 # One bfloat16 ulp relative to a value's scale is at most 2^-7.  Storage-rounding
 # decisions that the float32 GPU and the float64 oracle take differently at
-# isolated near-midpoints move downstream elements by a few such ulps; rows as a
-# whole stay within the 2e-3 bound.
+# isolated near-midpoints move a stored element by one such ulp, and the elements
+# computed from it by a few; rows as a whole stay within the 2e-3 bound.
 BF16_ELEM_BOUND = 4 * 2.0 ** -8
+FLOOR = 1e-3     # absolute floor of the per-call rule, as a fraction of the tensor's max |b|
+# Attention logits are defined up to a shift of each row (the softmax does not see it), so their
+# absolute error, set by the float32 accumulation of the 4096-long projections that produce the
+# queries (about 1e-6 of |q||k|), is what matters; near zero it is judged against this floor.  The
+# drift values the logits determine are held to FLOOR.
+LOGIT_FLOOR = 1e-2
 
 
-def assert_close(a, b, name, rtol=2e-3, dtype="f32"):
-    """Rows within rtol normwise; elements within rtol (float32) or a few bf16 ulps (bf16)."""
+def rel_err_floor(a, b, floor=FLOOR):
+    """Elementwise |a - b| / max(|b|, floor * max|b|), max|b| over the whole tensor."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if b.size == 0:
+        return np.zeros(b.shape)
+    den = np.maximum(np.abs(b), floor * np.abs(b).max())
+    return np.abs(a - b) / np.maximum(den, 1e-300)
+
+
+def assert_close(a, b, name, rtol=2e-3, dtype="f32", allow=None, floor=FLOOR):
+    """Per-call floating point (values before their storage rounding: projections, attention
+    outputs, logits, drift, h', layer outputs): every element within rtol of the oracle's value,
+    relative to max(|b|, floor max|b|) (floor 1e-3; logits LOGIT_FLOOR).  The floor keeps an element near zero from being judged
+    against its own tiny magnitude.  ``allow`` (same shape, from tests.flips, computed from the
+    oracle alone) adds the first-order effect of admissible alternative roundings of values
+    stored earlier in the same call; the elements that need it are counted and reported.
+    ``dtype`` only labels the log line."""
+    from tests import flips as FL
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    e = rel_err_floor(a, b, floor)
+    if e.size == 0:
+        return 0.0
+    r = row_err(a, b)
+    al = np.zeros_like(b) if allow is None else np.broadcast_to(np.asarray(allow, np.float64), b.shape)
+    ok, n_tie = FL.explained(a, b, al, rtol, floor)
+    log(f"    {name}: max elem err {e.max():.2e} (floor {floor:g} max|b|), max row err {r.max():.2e}; "
+        f"{n_tie} elements within the bound only through admissible tie roundings [{dtype}]")
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[int(np.argmax(e[tuple(bad.T)]))])
+        raise AssertionError(f"{name}: {len(bad)} elements outside 2e-3 + tie allowance; worst at {i} of "
+                             f"{b.shape}: got {a[i]!r}, want {b[i]!r}, allowance {al[i]:.3e}, rel err {e[i]:.3e}")
+    return float(e.max())
+
+
+def assert_derived(a, b, dtype, name, rtol=2e-3):
+    """Values stored in the storage dtype, or computed from tensors that each side stored itself
+    (so that inputs differ wherever a storage rounding went the other way): rows within rtol
+    normwise; elements within rtol (float32) or a few bf16 ulps of their row's scale (bf16)."""
     e = rel_err(a, b)
     r = row_err(a, b)
     if e.size == 0:
@@ -82,13 +127,15 @@ def assert_close(a, b, name, rtol=2e-3, dtype="f32"):
 
 
 def assert_stored(a, b, dtype, name, rtol=2e-3):
-    """Stored tensors: the same bounds; also report how many values differ at all."""
+    """Stored tensors (K/V cache, window rows, centroids, layer outputs): the bounds of
+    assert_derived; also reports how many stored values differ at all, i.e. how many rounding
+    decisions went the other way (for bf16: values one ulp apart)."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
-    frac = float(np.mean(a != b)) if a.size else 0.0
-    log(f"    {name}: {frac:.3%} stored values differ from the oracle's")
-    assert_close(a, b, name, rtol, dtype)
-    return frac
+    diff = int(np.sum(a != b)) if a.size else 0
+    log(f"    {name}: {diff} of {a.size} stored values differ from the oracle's ({diff / max(a.size, 1):.3%})")
+    assert_derived(a, b, dtype, name, rtol)
+    return diff / max(a.size, 1)
 
 
 def assert_rounded(stored, pre, dtype, name):
@@ -136,24 +183,35 @@ def topk_margin(D, topk, k_eff):
     return (lo - max(rest)) / max(abs(lo), 1e-30)
 
 
-def check_topk(tg, Dg, D_or, topk_or, k, k_eff, tag):
-    """Top-k comparison.  The GPU's clusters must follow the rule on its own drift
-    values; the selected set must equal the oracle's unless the oracle's margin
-    between the k-th selected and the best unselected drift is below 1e-3
-    (returns False: both sets are admissible); within the set, the order may
-    differ only between drifts equal to 1e-3 relative."""
+TIE_REL = 1e-6   # drift values this close (relative) are a tie whichever implementation computes them
+
+
+def check_topk(tg, Dg, D_or, topk_or, k, k_eff, tag, D_allow=None):
+    """Top-k comparison.  The GPU's clusters must follow the rule on its own drift values; the
+    selected set must equal the oracle's unless the oracle's gap between the k-th selected and
+    the best unselected drift is within their admissible deviation (TIE_REL relative, plus
+    SAFETY times D_allow, the oracle-derived effect of admissible tie roundings): then both sets
+    are admissible, the near-tie is reported and False returned.  Within the set, the order may
+    differ only between drifts tied in the same sense."""
+    from tests import flips as FL
     kk = min(k, k_eff)
     tg = np.asarray(tg)[:kk]
-    assert np.array_equal(tg, O.topk_clusters(Dg, k, k_eff)[:kk]), f"{tag}: top-k does not follow the rule"
-    if set(tg.tolist()) != set(np.asarray(topk_or)[:kk].tolist()):
-        mg = topk_margin(D_or, topk_or, k_eff)
-        if mg < 1e-3:
-            log(f"    {tag}: top-k near-tie (oracle margin {mg:.2e})")
-            return False
-        raise AssertionError(f"{tag}: top-k {tg.tolist()} != oracle {list(topk_or)} (margin {mg:.2e})")
     D_or = np.asarray(D_or, dtype=np.float64)
+    al = np.zeros_like(D_or) if D_allow is None else np.asarray(D_allow, np.float64)
+    tie = lambda x, y: abs(D_or[x] - D_or[y]) <= TIE_REL * max(abs(D_or[x]), abs(D_or[y])) + FL.SAFETY * (al[x] + al[y])
+    assert np.array_equal(tg, O.topk_clusters(Dg, k, k_eff)[:kk]), f"{tag}: top-k does not follow the rule"
+    sel_or = [int(c) for c in np.asarray(topk_or)[:kk]]
+    if set(tg.tolist()) != set(sel_or):
+        rest = [c for c in range(k_eff) if c not in sel_or]
+        kth = min(sel_or, key=lambda c: (D_or[c], -c))
+        best_rest = max(rest, key=lambda c: (D_or[c], -c))
+        mg = topk_margin(D_or, topk_or, k_eff)
+        if tie(kth, best_rest):
+            log(f"    {tag}: top-k near-tie (oracle margin {mg:.2e}, clusters {kth}/{best_rest}), reported")
+            return False
+        raise AssertionError(f"{tag}: top-k {tg.tolist()} != oracle {sel_or} (margin {mg:.2e})")
     for a, b in zip(tg[:-1], tg[1:]):
-        assert D_or[a] >= D_or[b] * (1 - 1e-3) - 1e-12, f"{tag}: top-k order {tg.tolist()} vs oracle drift"
+        assert D_or[a] >= D_or[b] or tie(a, b), f"{tag}: top-k order {tg.tolist()} vs oracle drift"
     return True
 
 
@@ -171,7 +229,8 @@ class Dev:
                            vocab=self.vocab, dtype=B.BF16 if w.dtype == "bf16" else B.F32,
                            resid_fmt=B.RESID_BY_NAME[w.resid])
         self.params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist,
-                               mask_id=max(self.vocab - 1, 0), kmeans_iters=w.kmeans_iters)
+                               mask_id=max(self.vocab - 1, 0), kmeans_iters=w.kmeans_iters,
+                               proxy_support=B.PROXY_ACTIVE if w.proxy_support == "active" else B.PROXY_ALL)
         self.h = B.polestar_create(self.dims, self.params)
         self.ws_bytes = B.polestar_workspace_size(self.h)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)

@@ -20,7 +20,8 @@ import torch
 import synth
 from drift_driven_sparse_amd import binding as B
 from oracle import polestar_oracle as O
-from tests.harness import (Dev, assert_close, assert_stored, assert_traj, layer_struct, log, np64, oracle_weights,
+from tests import flips as FL
+from tests.harness import (LOGIT_FLOOR, Dev, assert_close, assert_derived, assert_stored, assert_traj, layer_struct, log, np64, oracle_weights,
                            packed_layer, weights)
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +32,8 @@ CASES = {
     "tiny_fp32_full_2layers": (TINY, 1, 2, True, 64),
     "tiny_fp32_window": (TINY, 1, 1, False, 160),
     "tiny_bf16_full_2layers_batch2": (synth.shrink(TINY, dtype="bf16"), 2, 2, True, 96),
+    "tiny_bf16_full_2layers_proxy_active": (synth.shrink(TINY, dtype="bf16", proxy_support="active"), 1, 2, True, 96),
+    "tiny_fp32_window_proxy_active": (synth.shrink(TINY, proxy_support="active"), 1, 1, False, 160),
     "tiny_bf16_window_at_start": (synth.shrink(TINY, dtype="bf16"), 1, 1, False, 0),
     "tiny_bf16_window_at_end": (synth.shrink(TINY, dtype="bf16"), 1, 1, False, 288),
     "tiny_bf16_nvfp4_full": (synth.shrink(TINY, dtype="bf16", resid="nvfp4"), 1, 1, True, 128),
@@ -128,33 +131,57 @@ def test_block_entry_parity(case):
                 assert np.allclose(obj[b].cpu().numpy(), ls["trace"], rtol=1e-12, atol=0), "k-means objective"
                 assert_stored(np64(z[b]), ls["Z"], w.dtype, "entry centroids")
                 if nv:
-                    c_or, s_or = O.residual_quantize(h_or[b][wpos], np64(z[b]), m[b, :nw].cpu().numpy(), w.resid)
-                    assert np.array_equal(codes[b, :nw].cpu().numpy(), c_or), f"entry {w.resid} codes differ"
-                    assert np.array_equal(scales[b, :nw, :sb].cpu().numpy(), s_or)
+                    assert np.array_equal(codes[b, :nw].cpu().numpy(), ls["codes"]), f"entry {w.resid} codes differ"
+                    assert np.array_equal(scales[b, :nw, :sb].cpu().numpy(), ls["scales"])
                 else:
                     assert torch.equal(win[b, :nw], h_in[b, wpos]), "window rows not stored as they are"
             else:
-                # inputs differ by storage roundings: compare the GPU's labels with k-means of its own rows
-                zg, mg, _ = O.spherical_kmeans(np64(h_in[b, wpos]), K, inits[b], w.kmeans_iters)
-                assert np.array_equal(m[b, :nw].cpu().numpy(), mg), "k-means labels differ (GPU input rows)"
-                assert_stored(np64(z[b]), st(zg), w.dtype, "entry centroids (GPU input rows)")
-            # proxy logits: from the GPU's stored centroids and cache by the oracle's definition, and
-            # (first layer) against the oracle's own state
-            zq = O.project(np64(z[b]), Wo["wq"], cfg.eps, st).reshape(K, hq, dh)
-            _, pl = O.attention(zq, kg.reshape(n, hkv, dh), vg.reshape(n, hkv, dh), hq, hkv)
-            assert_close(plog[b].cpu().numpy(), pl, f"layer {l} seq {b} proxy logits", dtype=w.dtype)
+                # each side clusters its own input rows, which differ where a storage rounding went
+                # the other way: labels must agree except at rows whose oracle cosine margin (best
+                # against second-best centroid) is below 1e-3, reported
+                xh = O.unit_rows(h_or[b][wpos])
+                cos = np.sort(xh @ O.unit_rows(ls["Z"][:min(K, nw)]).T, axis=1)
+                margin = cos[:, -1] - cos[:, -2] if cos.shape[1] > 1 else np.full(nw, np.inf)
+                diff = np.nonzero(m[b, :nw].cpu().numpy() != ls["M"])[0]
+                if len(diff):
+                    log(f"    layer {l} seq {b}: {len(diff)} labels differ at oracle margins {margin[diff]}")
+                assert np.all(margin[diff] < 1e-3), "k-means labels differ away from a near-tie"
+                if not len(diff):
+                    assert_derived(np64(z[b]), ls["Z"], w.dtype, f"layer {l} seq {b} entry centroids")
+            # proxy logits (over the proxy keys) and, last layer, the active block's logits over the
+            # fresh cache, against the oracle's own state: per-call rule on the first layer, whose
+            # inputs both sides share; later layers start from each side's own stored rows
+            pk = O.proxy_keys(cfg, blk_start)
+            jpos = O.active_positions(blk_start, w.block)
             if l == 0:
-                assert_close(plog[b].cpu().numpy(), ls["P"], f"seq {b} proxy logits (oracle state)", dtype=w.dtype)
+                # admissible deviations from the oracle alone: the K/V rows and centroids this call
+                # stores, and the rounded projection inputs
+                hr = h_or[b][rows]
+                dK, dV = np.zeros((n, hkv, dh)), np.zeros((n, hkv, dh))
+                dnr = FL.norm_in_dev(hr, cfg.eps, w.dtype)
+                for arr, wm in ((dK, Wo["wk"]), (dV, Wo["wv"])):
+                    arr[rows] = FL.stored_dev(O.project(hr, wm, cfg.eps, st), w.dtype,
+                                              FL.proj_dev(dnr, wm)).reshape(-1, hkv, dh)
+                z_pre, _, _ = O.spherical_kmeans(h_or[b][wpos], K, inits[b], w.kmeans_iters)
+                dz = FL.norm_in_dev(ls["Z"], cfg.eps, w.dtype, FL.stored_dev(z_pre, w.dtype))
+                q_px = O.project(ls["Z"], Wo["wq"], cfg.eps, st).reshape(K, hq, dh)
+                dlp = FL.attn_dev(q_px, Kb, Vb, FL.proj_dev(dz, Wo["wq"]).reshape(K, hq, dh), dK, dV, hq, hkv,
+                                  keys=pk)[0]
+                assert_close(plog[b].cpu().numpy()[..., pk], ls["P"][..., pk], f"layer {l} seq {b} proxy logits",
+                             dtype=w.dtype, allow=dlp, floor=LOGIT_FLOOR)
+            else:
+                assert_derived(plog[b].cpu().numpy()[..., pk], ls["P"][..., pk], w.dtype,
+                               f"layer {l} seq {b} proxy logits")
             if last:
-                # the active block's main-attention logits over the fresh cache: from the GPU's
-                # stored cache by the oracle's definition, and against the oracle's own state
-                jpos = O.active_positions(blk_start, w.block)
-                qg = O.project(np64(h_in[b, jpos]), Wo["wq"], cfg.eps, st).reshape(-1, hq, dh)
-                _, lg = O.attention(qg, kg.reshape(n, hkv, dh), vg.reshape(n, hkv, dh), hq, hkv)
-                assert_close(act[b].cpu().numpy(), lg, f"seq {b} active logits", dtype=w.dtype)
                 qa = O.project(h_or[b][jpos], Wo["wq"], cfg.eps, st).reshape(-1, hq, dh)
                 _, lo = O.attention(qa, Kb, Vb, hq, hkv)
-                assert_close(act[b].cpu().numpy(), lo, f"seq {b} active logits (oracle state)", dtype=w.dtype)
+                if l == 0:
+                    dqa = FL.proj_dev(FL.norm_in_dev(h_or[b][jpos], cfg.eps, w.dtype), Wo["wq"]).reshape(-1, hq, dh)
+                    dla = FL.attn_dev(qa, Kb, Vb, dqa, dK, dV, hq, hkv)[0]
+                    assert_close(act[b].cpu().numpy(), lo, f"seq {b} active logits", dtype=w.dtype, allow=dla,
+                                 floor=LOGIT_FLOOR)
+                else:
+                    assert_derived(act[b].cpu().numpy(), lo, w.dtype, f"seq {b} active logits")
             hn = h_or[b].copy()
             hn[rows] = out_or
             nxt[b] = hn

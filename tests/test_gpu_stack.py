@@ -164,7 +164,10 @@ def test_step_call_matches_layer_calls(refresh):
 def test_query_cache_matches_full_projection():
     """The window-row query cache (raw window rows: only patched rows projected after the first
     refresh of a block) against a stack that projects every window row: bit-identical outputs and
-    state over a block entry and five steps, refresh and active-only."""
+    state over a block entry and five steps, then a full and a window entry of the next block with
+    steps after each (the entry clears the cache: q_ok 0 after it, blk_start + 1 after the first
+    refresh), and a refresh at a later block position with no entry (a stale tag: every window row
+    is projected again)."""
     w = synth.shrink(synth.WORKLOADS[1], dtype="bf16")
     n_layers = 3
     dims = B.Dims(d=w.d, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn,
@@ -172,32 +175,54 @@ def test_query_cache_matches_full_projection():
                   n_clusters=w.n_clusters, top_k=w.top_k, vocab=0, dtype=B.BF16, resid_fmt=B.RESID_RAW)
     params = B.Params(rms_eps=w.rms_eps, tau_s=w.tau_s, tau_suf=w.tau_suf, alpha=w.alpha, hist=w.hist, mask_id=0,
                       kmeans_iters=w.kmeans_iters)
-    blk = w.prompt
+    blk0 = w.prompt
     nw = w.win_prefix + w.win_suffix
     stacks = [RefreshStack(dims, params, n_layers, q_cache=qc) for qc in (True, False)]
+    # (kind, block start, refresh): "e" full entry, "w" window entry, "s" step
+    plan = [("e", blk0, None)] + [("s", blk0, r) for r in (True, True, False, True, True)]
+    blk1, blk2 = blk0 + w.block, blk0 + 2 * w.block
+    plan += [("e", blk1, None), ("s", blk1, True), ("s", blk1, False), ("s", blk1, True)]
+    plan += [("w", blk1, None), ("s", blk1, True), ("s", blk1, True)]
+    plan += [("s", blk2, True), ("s", blk2, True)]
     try:
         h0 = torch.stack([synth.embeddings(w, 0, "cuda", b).to(torch.bfloat16) for b in range(2)]).contiguous()
         inits = [torch.stack([torch.tensor(synth.kmeans_init(w, nw, l, 0, 0, b), dtype=torch.int32)
                               for b in range(2)]).cuda() for l in range(n_layers)]
-        inputs = synth.tensor(w, (98,), (6, 2, w.block, w.d), 1.0, 0, "cuda", "bf16")
-        outs = []
-        for st in stacks:
+        inputs = synth.tensor(w, (98,), (len(plan), 2, w.block, w.d), 1.0, 0, "cuda", "bf16")
+        outs, tags = [], []
+        for si, st in enumerate(stacks):
             for l in range(n_layers):
                 st.set_layer_weights(l, synth.layer_weights(w, l, device="cuda"))
-            st.entry_forward(blk, h0, inits, full=True)
-            seq = []
-            for i, refresh in enumerate([True, True, False, True, True]):
-                out = st.step(blk, inputs[i], refresh=refresh)
-                torch.cuda.synchronize()
-                seq.append([out.clone(), st.D.clone(), st.topk.clone(), st.delta.clone()] +
-                           [L[k].clone() for L in st.layers for k in ("k_cache", "v_cache", "win_h", "win_z",
-                                                                         "proxy_logits")])
+            seq, tg = [], []
+            h_seq = h0
+            for i, (kind, blk, refresh) in enumerate(plan):
+                if kind in ("e", "w"):
+                    out = st.entry_forward(blk, h_seq, inits, full=kind == "e").clone()
+                    torch.cuda.synchronize()
+                    seq.append([out] + [L[k].clone() for L in st.layers for k in ("k_cache", "v_cache", "win_h",
+                                                                                     "win_z", "proxy_logits")])
+                else:
+                    out = st.step(blk, inputs[i], refresh=refresh)
+                    torch.cuda.synchronize()
+                    seq.append([out.clone(), st.D.clone(), st.topk.clone(), st.delta.clone()] +
+                               [L[k].clone() for L in st.layers for k in ("k_cache", "v_cache", "win_h", "win_z",
+                                                                             "proxy_logits")])
+                if si == 0:
+                    tg.append([int(L["q_ok"][b]) for L in st.layers for b in range(2)])
             outs.append(seq)
-        assert int(stacks[0].layers[0]["q_ok"][0]) == 1
+            tags = tags or tg
+        # the tag each layer's cache should carry after every item of the plan
+        cur = 0
+        for i, (kind, blk, refresh) in enumerate(plan):
+            if kind in ("e", "w"):
+                cur = 0
+            elif refresh:
+                cur = blk + 1
+            assert tags[i] == [cur] * (2 * n_layers), f"item {i} {plan[i]}: q_ok {tags[i]}, want {cur}"
         for i, (a, b_) in enumerate(zip(*outs)):
             bad = [j for j, (x, y) in enumerate(zip(a, b_)) if not torch.equal(x, y)]
-            log(f"[q-cache] step {i}: {len(a) - len(bad)}/{len(a)} tensors bit-identical")
-            assert not bad, f"step {i}: the query cache changes tensors {bad}"
+            log(f"[q-cache] {plan[i]}: {len(a) - len(bad)}/{len(a)} tensors bit-identical")
+            assert not bad, f"item {i} {plan[i]}: the query cache changes tensors {bad}"
     finally:
         for st in stacks:
             st.close()

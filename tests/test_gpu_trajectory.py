@@ -1,21 +1,32 @@
-"""GPU parity over a free-running trajectory: several denoising steps of a small
-layer stack, refresh steps (window update, drift, top-k, sparse forward,
-update packet to the next layer) interleaved with steps without a refresh
-(active rows only), and the last layer's active drift for the commit rule.
+"""GPU parity along a trajectory of a layer stack: denoising steps whose
+refresh / active-only kind is decided by the update schedule's trigger
+(polestar_should_refresh on the tokens decoded since the last refresh, the
+workload's unmask schedule supplying the counts), with the per-layer calls the
+benchmark issues (window update, drift, sparse forward, update packet to the
+next layer; the window-row query cache on for raw bf16 windows) and the last
+layer's active drift for the commit rule.
 
-Both sides start from the oracle's block-entry state (dense forward of all
-positions, k-means of the window rows, proxy logits).  Each step feeds the
-same seeded layer-0 active rows to both; every later value is each side's own.
-Per step and layer the top-k clusters and the selected rows must match; every
-floating-point tensor (drift values, active outputs, update packets, logits and
-the state below) must stay within 2e-3 normwise per tensor, and for bf16
-storage within one bf16 ulp normwise per row and a few ulps per element, since
-each side continues from its own stored values.  At the end of each step the state each side
-carries into the next one (K/V caches, window rows or NVFP4 codes, centroids,
-proxy logits, active logits) is compared, then the oracle's copy is written
-back to the device so that storage-rounding differences of one step do not
-compound into the next.  A top-k selection whose oracle margin is below 1e-3
-ends the comparison (both selections are then admissible).
+Both sides start from the same seeded block-entry state (stale K/V caches and
+window rows, k-means of the window rows and the first proxy logits by the
+oracle).  Each step unmasks the schedule's positions by adding seeded noise to
+their layer-0 rows on both sides.  Every call is checked against the oracle on
+shared inputs: the rows passed from one layer to the next (active rows, update
+packet) are the oracle's stored values on both sides, and the state carried to
+the next step (K/V caches, centroids, proxy and active logits) likewise.  The
+window rows are patched from those packets, so they, and the query cache built
+from them, evolve across steps as in the benchmark's stack.  Per call: S and its
+count bit-exact; drift D and delta within 2e-3 elementwise (floor 1e-3 max|b|)
+plus the oracle-derived effect of admissible tie roundings of the K/V rows the
+call stores; stored tensors (active outputs, update packet, caches, window
+rows, centroids) within the stored-value bounds, with the number of values a
+rounding tie moved reported.  A top-k selection may differ from the oracle's
+only where the oracle's gap between the two clusters lies within their
+admissible deviation: such a near-tie is reported, the GPU takes the oracle's
+selection, and the trajectory goes on.  (Without re-synchronisation, bf16
+storage ties decided differently by float32 and float64 arithmetic, about 0.4%
+of each layer's stored outputs, compound through the layers; the per-tensor
+distance then passes 2e-3 after three or four layers of these random-weight
+stacks, for any float32 implementation.)
 """
 from __future__ import annotations
 
@@ -26,21 +37,33 @@ import torch
 import synth
 from drift_driven_sparse_amd import binding as B
 from oracle import polestar_oracle as O
-from tests.harness import (Dev, assert_traj, check_topk, layer_struct, log, np64, packed_layer,
-                           packet, to_dev, weights)
+from tests import flips as FL
+from tests.harness import (Dev, assert_close, assert_stored, assert_traj, check_topk, layer_struct, log, np64,
+                           packed_layer, packet, to_dev, weights)
 
 pytestmark = pytest.mark.gpu
 
 CASES = {
     # name: (workload, layers, steps)
-    "tiny_fp32_2layers": (synth.WORKLOADS[1], 2, 8),
-    "tiny_bf16_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16"), 2, 8),
-    "tiny_bf16_nvfp4_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", resid="nvfp4"), 2, 6),
+    "tiny_fp32_2layers": (synth.WORKLOADS[1], 2, 10),
+    "tiny_bf16_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16"), 2, 10),
+    "tiny_bf16_nvfp4_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", resid="nvfp4"), 2, 8),
+    # the benchmark's stack shape (32 x 128 heads, FFN 12288, n 1024), first four layers
+    "llada8b_stack_4layers_n1024": (synth.shrink(synth.WORKLOADS[3], n_layers=4), 4, 8),
+    # the Dream-7B GQA stack shape (28 / 4 heads, FFN 18944, n 640), first four layers
+    "dream7b_gqa_stack_4layers": (synth.shrink(synth.WORKLOADS[4], n_layers=4), 4, 6),
 }
 
 
-def _refresh_at(t: int) -> bool:
-    return t % 3 != 2
+def _layer_state(w, l, blk_start, nw, cfg, Wq):
+    """Seeded stale caches and window rows of layer l, and the oracle's block-entry state."""
+    n, d, hkv, dh = w.n_pos, w.d, w.n_kv_heads, w.head_dim
+    t = lambda tag, shape, dtype=w.dtype: np64(synth.tensor(w, (l,) + tag, shape, 1.0, 0, "cpu", dtype))
+    H = np.zeros((n, d))
+    wpos = O.window_positions(blk_start, n, w.block, w.win_prefix, w.win_suffix)
+    H[wpos] = t((30,), (nw, d))
+    return O.block_entry_layer_state(H, t((31,), (n, hkv, dh)), t((32,), (n, hkv, dh)), Wq, cfg, blk_start,
+                                     synth.kmeans_init(w, nw, l, 0))
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -57,21 +80,20 @@ def test_trajectory_parity(case):
     wpos = O.window_positions(blk_start, n, Bk, w.win_prefix, w.win_suffix)
     nw, WM = len(wpos), dev.win_max
     keff = min(K, nw)
-    nv = w.resid == "nvfp4"
+    nv = w.resid != "raw"
+    qcache = w.dtype == "bf16" and not nv
+    sched = synth.unmask_schedule(w, steps=steps)
+    assert all(b == 0 for b, _ in sched), "the trajectory stays in the first block"
     try:
-        # ---- weights and the block-entry state (oracle)
-        Wd = [weights(w, l) for l in range(n_layers)]
-        Wo = [{k: np64(v) for k, v in W.items()} for W in Wd]
-        P = [packed_layer(dev, W) for W in Wd]
-        del Wd
-        h0 = st(np64(synth.embeddings(w)))
-        Hs, Ks, Vs, last_logits = O.full_forward(h0, Wo, cfg)
-        OL, L, Ls = [], [], []
+        # ---- weights and the block-entry state (seeded, oracle)
+        OL, L, Ls, Wo = [], [], [], []
         for l in range(n_layers):
-            init = synth.kmeans_init(w, nw, l, 0)
-            ls = O.block_entry_layer_state(Hs[l], Ks[l], Vs[l], Wo[l]["wq"], cfg, blk_start, init)
+            Wd = weights(w, l)
+            Wo.append({k: np64(v) for k, v in Wd.items()})
+            Ld = packed_layer(dev, Wd)
+            del Wd
+            ls = _layer_state(w, l, blk_start, nw, cfg, Wo[l]["wq"])
             OL.append(ls)
-            Ld = dict(P[l])
             Ld["k_cache"] = to_dev(ls["K"], w.dtype)[None].contiguous()
             Ld["v_cache"] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)[None].contiguous()
             Ld["win_z"] = to_dev(ls["Z"], w.dtype)[None].contiguous()
@@ -80,23 +102,29 @@ def test_trajectory_parity(case):
             Ld["win_m"] = m
             Ld["proxy_logits"] = torch.tensor(ls["P"], dtype=torch.float32, device="cuda")[None].contiguous()
             if nv:
-                c = torch.zeros(1, WM, d // 2, dtype=torch.uint8, device="cuda")
-                s = torch.zeros(1, WM, d // 16, dtype=torch.uint8, device="cuda")
+                cb, sb = B.polestar_resid_bytes(B.RESID_BY_NAME[w.resid], d)
+                c = torch.zeros(1, WM, cb, dtype=torch.uint8, device="cuda")
+                s = torch.zeros(1, WM, max(sb, 1), dtype=torch.uint8, device="cuda")
                 c[0, :nw] = torch.tensor(ls["codes"])
-                s[0, :nw] = torch.tensor(ls["scales"])
+                s[0, :nw, :sb] = torch.tensor(ls["scales"])
                 Ld["win_codes"], Ld["win_scales"] = c, s
             else:
                 hw = dev.zeros(1, WM, d)
                 hw[0, :nw] = to_dev(ls["H"], w.dtype)
                 Ld["win_h"] = hw
+            if qcache:   # the window-row query cache, as the benchmark's stack runs it
+                Ld["q_win"] = torch.zeros(1, WM, hq * dh, dtype=torch.float32, device="cuda")
+                Ld["q_ok"] = torch.zeros(1, dtype=torch.int32, device="cuda")
             L.append(Ld)
-            Ls.append(layer_struct(Ld))
-        # active drift reference: the entry forward's last-layer logits of the active rows
-        act_prev = O.round_f32(last_logits[blk_start: blk_start + Bk])
+            s_ = layer_struct(Ld)
+            if qcache:
+                s_.q_win, s_.q_ok = Ld["q_win"].data_ptr(), Ld["q_ok"].data_ptr()
+            Ls.append(s_)
+        x0 = np64(synth.tensor(w, (60,), (Bk, d), 1.0, 0, "cpu", w.dtype))     # layer-0 active rows
+        act_prev = O.round_f32(np64(synth.tensor(w, (61,), (Bk, hq, n), 1.0, 0, "cpu", "f32")))
         act_logits = torch.tensor(act_prev, dtype=torch.float32, device="cuda")[None].contiguous()
         log("[trajectory] entry state ready")
 
-        # ---- device step buffers
         h_act = [dev.zeros(1, Bk, d) for _ in range(2)]
         pk_rows = [dev.zeros(1, WM, d) for _ in range(2)]
         pk_idx = [torch.zeros(1, WM, dtype=torch.int32, device="cuda") for _ in range(2)]
@@ -106,17 +134,24 @@ def test_trajectory_parity(case):
         topk = torch.zeros(1, w.top_k, dtype=torch.int32, device="cuda")
         delta = torch.zeros(1, Bk, dtype=torch.float32, device="cuda")
 
+        decoded, kinds, ties = 0, [], 0
         for t in range(steps):
-            refresh = _refresh_at(t)
-            # layer-0 active rows: the entry input plus the step's unmasking noise
-            noise = np64(synth.tensor(w, (77, t), (Bk, d), np.sqrt(w.noise_var)))
-            x = st(h0[blk_start: blk_start + Bk] + noise)
-            h_act[0][0] = to_dev(x, w.dtype)
+            # decoding: the schedule's positions of the active block get their new layer-0 rows
+            _, offs = sched[t]
+            for o in offs:
+                x0[o] = st(x0[o] + np64(synth.unmask_noise(w, t, blk_start + o)))
+            decoded += len(offs)
+            refresh = bool(B.polestar_should_refresh(decoded, w.tau_upd))
+            if refresh:
+                decoded = 0
+            kinds.append(refresh)
+            h_act[0][0] = to_dev(x0, w.dtype)
+            x = x0.copy()
             cur, pk = 0, 0
             u_in, U_prev, S_prev = None, None, None
             for l in range(n_layers):
                 last = l == n_layers - 1
-                # device
+                tag = f"step {t} layer {l} ({'refresh' if refresh else 'active only'})"
                 if refresh:
                     B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls[l], blk_start, u_in, None, None, None, dev.ws,
                                        dev.ws_bytes)
@@ -124,66 +159,78 @@ def test_trajectory_parity(case):
                 B.polestar_drift(dev.h, B.DRIFT_REFRESH if refresh else B.DRIFT_ACTIVE_ONLY, Ls[l], blk_start,
                                  h_act[cur], u_in, D, topk, sel, act_logits if last else None,
                                  delta if last else None, dev.ws, dev.ws_bytes)
-                B.polestar_refresh(dev.h, Ls[l], blk_start, h_act[cur], sel, None, None, None, h_act[1 - cur],
-                                   pk_rows[pk], dev.ws, dev.ws_bytes)
                 torch.cuda.synchronize()
-                # oracle
                 ls = OL[l]
                 if refresh:
                     cu = O.cluster_update(ls, cfg, U_prev, S_prev)
                     h_win, patched = cu["h"], cu["patched"]
                 else:
                     h_win, patched = O.window_rows_now(ls, cfg), None
+                P_before = ls["P"].copy()
                 dr = O.drift_layer(ls, Wo[l], cfg, blk_start, x, h_win, patched, refresh,
                                    commit_prev=act_prev if last else None)
+                al = FL.drift_call_allow(O, cfg, Wo[l], blk_start, x, h_win, patched, ls["Z"], ls["K"], ls["V"],
+                                         dr.get("proxy_q"), dr.get("proxy_keys"), P_before,
+                                         act_prev=act_prev if last else None, refresh=refresh)
                 S = dr["S"] if refresh else np.zeros(0, dtype=np.int64)
-                rf = O.refresh_layer(Wo[l], cfg, x, h_win, dr["o"], S)
-                tag = f"step {t} layer {l} ({'refresh' if refresh else 'active only'})"
                 if refresh:
                     Dg = D[0].cpu().numpy()
-                    assert_traj(Dg, dr["D"], w.dtype, f"{tag}: cluster drift D")
-                    if not check_topk(topk[0].cpu().numpy(), Dg, dr["D"], dr["topk"], w.top_k, keff, tag):
-                        log(f"[trajectory] {tag}: trajectories part here")
-                        return
+                    assert_close(Dg, dr["D"], f"{tag}: cluster drift D", allow=al["D"])
+                    if not check_topk(topk[0].cpu().numpy(), Dg, dr["D"], dr["topk"], w.top_k, keff, tag,
+                                      D_allow=al["D"]):
+                        ties += 1
+                        log(f"[trajectory] {tag}: near-tie; the GPU continues with the oracle's selection")
+                        pk_idx[pk][0, : len(S)] = torch.tensor(S, dtype=torch.int32)
+                        pk_cnt[pk][0] = len(S)
                     cnt = int(pk_cnt[pk][0])
-                    assert np.array_equal(pk_idx[pk][0, :cnt].cpu().numpy(), dr["S"]), f"{tag}: rows S differ"
-                    assert_traj(np64(pk_rows[pk][0, :cnt]), rf["U"], w.dtype, f"{tag}: update packet U")
+                    assert np.array_equal(pk_idx[pk][0, :cnt].cpu().numpy(), S), f"{tag}: rows S differ"
                 else:
                     assert int(pk_cnt[pk][0]) == 0
-                assert_traj(np64(h_act[1 - cur][0]), rf["h_act_out"], w.dtype, f"{tag}: active outputs")
                 if last:
-                    assert_traj(delta[0].cpu().numpy(), dr["delta"], w.dtype, f"{tag}: active drift delta")
+                    assert_close(delta[0].cpu().numpy(), dr["delta"], f"{tag}: active drift delta", allow=al["delta"])
                     act_prev = dr["act_logits"]
-                # both sides continue from their own values
+                B.polestar_refresh(dev.h, Ls[l], blk_start, h_act[cur], sel, None, None, None, h_act[1 - cur],
+                                   pk_rows[pk], dev.ws, dev.ws_bytes)
+                torch.cuda.synchronize()
+                rf = O.refresh_layer(Wo[l], cfg, x, h_win, dr["o"], S)
+                if refresh:
+                    assert_stored(np64(pk_rows[pk][0, : len(S)]), rf["U"], w.dtype, f"{tag}: update packet U")
+                    pk_rows[pk][0, : len(S)] = to_dev(rf["U"], w.dtype)
+                assert_stored(np64(h_act[1 - cur][0]), rf["h_act_out"], w.dtype, f"{tag}: active outputs")
+                h_act[1 - cur][0] = to_dev(rf["h_act_out"], w.dtype)
                 x = rf["h_act_out"]
                 if refresh:
-                    u_in, U_prev, S_prev = pks[pk], rf["U"], dr["S"]
+                    u_in, U_prev, S_prev = pks[pk], rf["U"], S
                 cur, pk = 1 - cur, 1 - pk
-            # carried state: compare, then continue from the oracle's copy on both sides
+            # the state carried into the next step: compared, then both sides continue from the
+            # oracle's copy (window rows and labels are equal by construction: patched from the
+            # re-synchronised packets)
             for l in range(n_layers):
                 ls, Ld, tag = OL[l], L[l], f"step {t} layer {l} state"
-                assert_traj(np64(Ld["k_cache"][0]).reshape(n, -1), ls["K"].reshape(n, -1), w.dtype, f"{tag}: K")
-                assert_traj(np64(Ld["v_cache"][0].permute(2, 0, 1)).reshape(n, -1), ls["V"].reshape(n, -1),
+                assert_stored(np64(Ld["k_cache"][0]).reshape(n, -1), ls["K"].reshape(n, -1), w.dtype, f"{tag}: K")
+                assert_stored(np64(Ld["v_cache"][0].permute(2, 0, 1)).reshape(n, -1), ls["V"].reshape(n, -1),
                               w.dtype, f"{tag}: V")
-                assert_traj(np64(Ld["win_z"][0]), ls["Z"], w.dtype, f"{tag}: centroids")
+                assert_stored(np64(Ld["win_z"][0]), ls["Z"], w.dtype, f"{tag}: centroids")
                 assert np.array_equal(Ld["win_m"][0, :nw].cpu().numpy(), ls["M"]), f"{tag}: labels changed"
-                assert_traj(Ld["proxy_logits"][0].cpu().numpy(), ls["P"], w.dtype, f"{tag}: proxy logits")
+                pk_ = O.proxy_keys(cfg, blk_start)
+                assert_traj(Ld["proxy_logits"][0].cpu().numpy()[..., pk_], ls["P"][..., pk_], w.dtype,
+                            f"{tag}: proxy logits")
                 if nv:
-                    frac = float(np.mean(Ld["win_codes"][0, :nw].cpu().numpy() != ls["codes"]))
-                    log(f"    {tag}: {frac:.3%} NVFP4 code bytes differ")
-                    assert frac < 0.05, f"{tag}: NVFP4 codes differ in {frac:.2%} of bytes"
-                    Ld["win_codes"][0, :nw] = torch.tensor(ls["codes"])
-                    Ld["win_scales"][0, :nw] = torch.tensor(ls["scales"])
+                    same = np.array_equal(Ld["win_codes"][0, :nw].cpu().numpy(), ls["codes"])
+                    assert same, f"{tag}: residual codes differ"
                 else:
-                    assert_traj(np64(Ld["win_h"][0, :nw]), ls["H"], w.dtype, f"{tag}: window rows")
-                    Ld["win_h"][0, :nw] = to_dev(ls["H"], w.dtype)
+                    assert np.array_equal(np64(Ld["win_h"][0, :nw]), ls["H"]), f"{tag}: window rows differ"
+                if qcache and refresh:
+                    assert int(Ld["q_ok"][0]) == blk_start + 1, f"{tag}: query cache tag"
                 Ld["k_cache"][0] = to_dev(ls["K"], w.dtype)
                 Ld["v_cache"][0] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)
                 Ld["win_z"][0] = to_dev(ls["Z"], w.dtype)
                 Ld["proxy_logits"][0] = torch.tensor(ls["P"], dtype=torch.float32)
             assert_traj(act_logits[0].cpu().numpy(), act_prev, w.dtype, f"step {t}: active logits")
             act_logits[0] = torch.tensor(act_prev, dtype=torch.float32)
-            log(f"[trajectory] step {t} ok ({'refresh' if refresh else 'active only'})")
+            log(f"[trajectory] step {t} ok ({'refresh' if refresh else 'active only'}, {len(offs)} decoded)")
+        log(f"[trajectory] case={case} passed: {sum(kinds)} refresh and {len(kinds) - sum(kinds)} active-only "
+            f"steps, {ties} reported top-k near-ties")
+        assert any(kinds) and not all(kinds), "the trigger gave a trajectory of one step kind only"
     finally:
         dev.close()
-    log(f"[trajectory] case={case} passed")

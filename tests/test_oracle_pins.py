@@ -818,3 +818,35 @@ def test_residual_composition_exact_round_trip(fmt):
     c2, s2 = O.residual_quantize(h, z, wrong, fmt)
     assert not np.array_equal(O.residual_dequantize(c2, s2, z, wrong, O.round_bf16, fmt), h)
     assert not np.array_equal(O.residual_dequantize(codes, scales, np.zeros_like(z), m, O.round_bf16, fmt), h)
+
+
+def test_proxy_drift_over_the_active_block_keys():
+    """Proxy attention over the active block's keys only [§4.1 "Measuring Drift..."; Eq. 3, the
+    "active" reading of the key support]: the KL equals torch's kl_div between the softmaxes of
+    the J_b scores; keys outside J_b do not move D ("active") but do move it ("all")."""
+    rng = np.random.default_rng(3)
+    n, hq, dh, K, blk, Bk = 40, 2, 16, 3, 12, 8
+    common = dict(d=32, n_heads=hq, n_kv_heads=hq, head_dim=dh, ffn=48, n_pos=n, block=Bk, win_prefix=8,
+                  win_suffix=4, n_clusters=K, top_k=1, dtype="f64")
+    act = O.Cfg(proxy_support="active", **common)
+    full = O.Cfg(proxy_support="all", **common)
+    zq = rng.normal(size=(K, hq, dh))
+    Kc, Vc = rng.normal(size=(n, hq, dh)), rng.normal(size=(n, hq, dh))
+    P_prev = rng.normal(size=(K, hq, n)) * 2
+    plog, kl, keys = O.proxy_drift(zq, Kc, Vc, P_prev, act, blk)
+    assert np.array_equal(keys, np.arange(blk, blk + Bk))
+    qt = torch.tensor(zq).permute(1, 0, 2)                                  # [Hq, K, dh]
+    kt = torch.tensor(Kc[keys]).permute(1, 2, 0)                            # [Hq, dh, B]
+    scores = (qt @ kt / math.sqrt(dh)).permute(1, 0, 2)                      # [K, Hq, B]
+    assert np.allclose(plog, scores.numpy(), rtol=1e-12, atol=1e-12)
+    want = F.kl_div(torch.log_softmax(torch.tensor(P_prev[..., keys]), -1), torch.log_softmax(scores, -1),
+                    reduction="none", log_target=True).sum(-1)
+    assert np.allclose(kl, want.numpy(), rtol=1e-10, atol=1e-13)
+    # keys outside the active block: no effect on the "active" reading, an effect on "all"
+    K2, V2, P2 = Kc.copy(), Vc.copy(), P_prev.copy()
+    out = np.setdiff1d(np.arange(n), keys)
+    K2[out] = rng.normal(size=K2[out].shape)
+    V2[out] = rng.normal(size=V2[out].shape)
+    P2[..., out] = rng.normal(size=P2[..., out].shape)
+    assert np.array_equal(O.proxy_drift(zq, K2, V2, P2, act, blk)[1], kl)
+    assert not np.allclose(O.proxy_drift(zq, K2, V2, P2, full, blk)[1], O.proxy_drift(zq, Kc, Vc, P_prev, full, blk)[1])
