@@ -14,6 +14,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpolestar.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_ALIGN, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+E_SCRATCH = -9
+SCRATCH_BYTES = 192 << 20
 F32, BF16 = 0, 1
 RESID_RAW, RESID_NVFP4, RESID_FP8, RESID_MXINT8, RESID_MXFP4 = 0, 1, 2, 3, 4
 RESID_BY_NAME = {"raw": RESID_RAW, "nvfp4": RESID_NVFP4, "fp8": RESID_FP8, "mxint8": RESID_MXINT8,
@@ -30,7 +32,7 @@ EXPORTED = [
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
     "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
-    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit", "polestar_step",
+    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit", "polestar_step", "polestar_step_noalloc",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -93,6 +95,8 @@ def lib() -> C.CDLL:
         L.polestar_entry.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_step.argtypes = [vp, C.c_int, i32, C.POINTER(Layer), i32, vp, vp, C.POINTER(Packet),
                                     C.POINTER(Packet), vp, vp, vp, vp, vp, sz, vp]
+        L.polestar_step_noalloc.argtypes = [vp, C.c_int, i32, C.POINTER(Layer), i32, vp, vp, C.POINTER(Packet),
+                                            C.POINTER(Packet), vp, vp, vp, vp, vp]
         L.polestar_entry_commit.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.polestar_drift.argtypes = [vp, C.c_int, C.POINTER(Layer), i32, vp, C.POINTER(Packet), vp, vp,
                                      C.POINTER(Packet), vp, vp, vp, sz, vp]
@@ -220,6 +224,14 @@ def polestar_step(h, mode, layers, blk_start, h_act0, h_act1, pk0: Packet, pk1: 
     _ck(lib().polestar_step(h, mode, len(layers), arr, blk_start, ptr(h_act0), ptr(h_act1), C.byref(pk0),
                             C.byref(pk1), ptr(D), ptr(topk), ptr(act_logits), ptr(delta), ptr(ws), ws_bytes,
                             stream_ptr(stream)), "polestar_step")
+
+
+def polestar_step_noalloc(h, mode, layers, blk_start, h_act0, h_act1, pk0: Packet, pk1: Packet, D, topk, act_logits,
+                          delta, stream=None) -> None:
+    arr = (Layer * len(layers))(*layers)
+    _ck(lib().polestar_step_noalloc(h, mode, len(layers), arr, blk_start, ptr(h_act0), ptr(h_act1), C.byref(pk0),
+                                    C.byref(pk1), ptr(D), ptr(topk), ptr(act_logits), ptr(delta), stream_ptr(stream)),
+        "polestar_step_noalloc")
 
 
 def polestar_commit(h, blk_start, w_lm, h_final, u_final: Optional[Packet], delta, active_masked, suffix_masked,

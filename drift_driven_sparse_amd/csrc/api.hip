@@ -2,6 +2,7 @@
 // and the launch sequence of each call.  Every argument is checked before the
 // first launch, so a call that returns an error has enqueued nothing.
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string.h>
 #include <vector>
@@ -1049,6 +1050,8 @@ const char* polestar_strerror(int code) {
     case POLESTAR_E_ALIGN: return "device pointer misaligned";
     case POLESTAR_E_HIP: return "HIP runtime error while enqueueing";
     case POLESTAR_E_ARG: return "invalid mode or scalar argument";
+    case POLESTAR_E_SCRATCH:
+      return "workspace larger than the library's static scratch (192 MiB): use polestar_step with a caller workspace";
   }
   return "unknown error";
 }
@@ -1424,6 +1427,53 @@ int polestar_entry_commit(polestar_handle* h, int32_t blk_start, const void* w_l
              : do_commit<float>(h, blk_start, w_lm, nullptr, nullptr, nullptr, active_masked, suffix_masked, nullptr,
                                 nullptr, commit_active, commit_suffix, conf_active, yhat_active, nullptr,
                                 conf_suffix, ws, s, h_full);
+}
+
+}  // extern "C"
+
+// ---- the step for callers that cannot allocate ------------------------------------------------
+// The workspace of polestar_step_noalloc: one array per device, placed by the loader with the
+// code object.  In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[POLESTAR_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call there).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return POLESTAR_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return POLESTAR_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return POLESTAR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int polestar_step_noalloc(polestar_handle* h, int mode, int32_t n_layers, const polestar_layer* layers,
+                          int32_t blk_start, void* h_act0, void* h_act1, polestar_packet* pk0, polestar_packet* pk1,
+                          float* D, int32_t* topk, float* act_logits, float* delta, void* stream) {
+  if (!h) return POLESTAR_E_NULL;
+  if (h->ws.total > (size_t)POLESTAR_SCRATCH_BYTES) return POLESTAR_E_SCRATCH;
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc) return rc;
+  // no profiling events here: recording them creates host objects on demand
+  const bool prof_on = h->prof->on;
+  h->prof->on = false;
+  rc = polestar_step(h, mode, n_layers, layers, blk_start, h_act0, h_act1, pk0, pk1, D, topk, act_logits, delta, ws,
+                     POLESTAR_SCRATCH_BYTES, stream);
+  h->prof->on = prof_on;
+  return rc;
 }
 
 int polestar_should_refresh(int32_t decoded_since_refresh, int32_t tau_upd) {

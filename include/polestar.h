@@ -83,7 +83,8 @@ enum {
   POLESTAR_E_WORKSPACE = -5,   /* workspace smaller than polestar_workspace_size */
   POLESTAR_E_ALIGN = -6,       /* device pointer not 16-byte aligned */
   POLESTAR_E_HIP = -7,         /* HIP runtime error while enqueueing */
-  POLESTAR_E_ARG = -8          /* invalid mode or scalar argument */
+  POLESTAR_E_ARG = -8,         /* invalid mode or scalar argument */
+  POLESTAR_E_SCRATCH = -9      /* workspace larger than the library's static scratch (polestar_step_noalloc) */
 };
 
 enum { POLESTAR_F32 = 0, POLESTAR_BF16 = 1 };
@@ -305,6 +306,24 @@ int polestar_refresh(polestar_handle* h, const polestar_layer* L, int32_t blk_st
 int polestar_step(polestar_handle* h, int mode, int32_t n_layers, const polestar_layer* layers, int32_t blk_start,
                   void* h_act0, void* h_act1, polestar_packet* pk0, polestar_packet* pk1, float* D, int32_t* topk,
                   float* act_logits, float* delta, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * polestar_step_noalloc — polestar_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, same validation, same launches and results.
+ * The workspace is the library's own static device array of POLESTAR_SCRATCH_BYTES
+ * (192 MiB) per GPU, held until the process ends; its address is looked up once per device
+ * (the device current at the first call) and no call allocates or frees device memory.
+ * Returns POLESTAR_E_SCRATCH, before any HIP call, when the handle's workspace
+ * (polestar_workspace_size) is larger.  Every call on one GPU uses the same array, which
+ * keeps the last call's contents (no step reads workspace it has not written first, so
+ * nothing is cleared); calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  Per-kernel profiling events are not recorded.
+ */
+#define POLESTAR_SCRATCH_BYTES (192u << 20)
+int polestar_step_noalloc(polestar_handle* h, int mode, int32_t n_layers, const polestar_layer* layers,
+                          int32_t blk_start, void* h_act0, void* h_act1, polestar_packet* pk0, polestar_packet* pk1,
+                          float* D, int32_t* topk, float* act_logits, float* delta, void* stream);
 
 /*
  * polestar_entry — block-entry state of one layer [§4.1 "Update Schedule"

@@ -210,3 +210,27 @@ def test_residual_format_sizes_and_rejections():
     for fmt in (B.RESID_FP8, B.RESID_MXINT8, B.RESID_MXFP4):
         assert lib.polestar_create(C.byref(_dims(resid_fmt=fmt)), C.byref(_params()), C.byref(h)) == B.E_UNSUPPORTED
     assert lib.polestar_create(C.byref(_dims(resid_fmt=9)), C.byref(_params()), C.byref(h)) == B.E_DTYPE
+
+
+def test_step_noalloc_rejects_a_workspace_beyond_the_scratch():
+    """polestar_step_noalloc returns E_SCRATCH, before any HIP call, for a handle whose workspace
+    exceeds the static scratch (the batch-16 LLaDA-shaped workload needs about 1 GiB); the
+    LLaDA-shaped stack of one sequence fits."""
+    lib = B.lib()
+    big = B.polestar_create(_dims(d=4096, n_heads=32, n_kv_heads=32, head_dim=128, ffn=12288, n_pos=768, batch=16,
+                                  vocab=126464, dtype=B.BF16, resid_fmt=B.RESID_NVFP4), _params(mask_id=126463))
+    one = B.polestar_create(_dims(d=4096, n_heads=32, n_kv_heads=32, head_dim=128, ffn=12288, n_pos=1024,
+                                  dtype=B.BF16), _params())
+    try:
+        assert B.polestar_workspace_size(big) > B.SCRATCH_BYTES
+        assert B.polestar_workspace_size(one) <= B.SCRATCH_BYTES
+        L = (B.Layer * 1)()
+        pk = B.Packet(rows=4096, idx=4096, count=4096)
+        rc = lib.polestar_step_noalloc(big, B.DRIFT_REFRESH, 1, L, 512, 4096, 4096, C.byref(pk), C.byref(pk), None,
+                                       None, None, None, None)
+        assert rc == B.E_SCRATCH
+        assert "static scratch" in B.strerror(rc)
+        assert lib.polestar_step_noalloc(None, 0, 1, L, 0, 0, 0, None, None, None, None, None, None, None) == B.E_NULL
+    finally:
+        B.polestar_destroy(big)
+        B.polestar_destroy(one)
