@@ -136,7 +136,8 @@ template <typename T, int RT, int KIND>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e) {
   constexpr int NSUB = kNT / 16;
   __shared__ float tile[RT * 16 * kLDT];
-  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  // sequences fastest: one weight tile's workgroups of all sequences are dispatched together
+  const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
 template <int RT, int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) {
   __shared__ float tile[RT * 16 * kLDT];
-  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) 
 
 template <typename T, int RT, int KIND>
 hipError_t launch_one(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
-  dim3 grid(PS_CEIL_DIV(g.N, kNT), g.batch, g.ksplit);
+  dim3 grid(g.batch, PS_CEIL_DIV(g.N, kNT), g.ksplit);
   if constexpr (std::is_same<T, float>::value) {
     hipLaunchKernelGGL((gemm_f32_kernel<RT, KIND>), grid, dim3(256), 0, s, g, e);
   } else {

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     else if constexpr (I == 6) return b6;
     else return b7;
   };
-  const int nt = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  // sequences are the fastest grid dimension: the workgroups of all sequences that stream one
+  // weight tile are dispatched together, so the repeats of the tile come from L2 and the
+  // last-level cache rather than HBM
+  const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
   int rows_b = g.A.rows(b);
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
 template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
 hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
   using C = DlCfg<RTW, RG, CG, NSUB, PL>;
-  const dim3 grid(PS_CEIL_DIV(g.N, C::NCOL), g.batch, g.ksplit), block(64 * RG * CG);
+  const dim3 grid(g.batch, PS_CEIL_DIV(g.N, C::NCOL), g.ksplit), block(64 * RG * CG);
   // with split-K every kind writes raw partial sums; its epilogue runs in launch_dl_finish
   switch (g.ksplit > 1 ? (int)EPI_PARTIAL : g.e.kind) {
     case EPI_PARTIAL: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_PARTIAL>), grid, block, 0, s, g); break;

@@ -23,7 +23,7 @@ import re
 import sqlite3
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/gemm_dl.hip", "csrc/kernels.h", "csrc/common.h"]
+KERNEL_SOURCES = ["csrc/gemm_dl.hip", "csrc/gemm_dl_impl.h", "csrc/kernels.h", "csrc/common.h"]
 
 
 def short(name: str) -> str:

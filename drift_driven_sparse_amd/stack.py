@@ -131,6 +131,32 @@ class RefreshStack:
             cur = 1 - cur
         return self.h_seq[cur]
 
+    # ---- Polestar-Commit of the last layer's outputs ------------------------------------------
+    def set_lm_head(self, w_lm: torch.Tensor) -> None:
+        """W_lm [vocab, d] in the storage dtype; also allocates the commit state and outputs."""
+        d, bt, Bk, suf = self.dims, self.dims.batch, self.dims.block, self.dims.win_suffix
+        self.w_lm = self._pack(B.W_LM, w_lm)
+        H = max(self.params.hist, 1)
+        dev = self.device
+        self.hist_vals = torch.zeros(bt, Bk, H, dtype=torch.float32, device=dev)
+        self.hist_cnt = torch.zeros(bt, Bk, dtype=torch.int32, device=dev)
+        self.active_masked = torch.ones(bt, Bk, dtype=torch.uint8, device=dev)
+        self.suffix_masked = torch.ones(bt, max(suf, 1), dtype=torch.uint8, device=dev)
+        self.commit_active = torch.zeros(bt, Bk, dtype=torch.uint8, device=dev)
+        self.commit_suffix = torch.zeros(bt, max(suf, 1), dtype=torch.uint8, device=dev)
+        self.conf_active = torch.zeros(bt, Bk, dtype=torch.float32, device=dev)
+        self.yhat_active = torch.zeros(bt, Bk, dtype=torch.int32, device=dev)
+        self.spike = torch.zeros(bt, Bk, dtype=torch.float32, device=dev)
+        self.conf_suffix = torch.zeros(bt, max(suf, 1), dtype=torch.float32, device=dev)
+
+    def commit(self, blk_start: int, h_final: torch.Tensor) -> None:
+        """polestar_commit on the last step's outputs: its active rows h_final, its last layer's
+        update packet and active drift delta."""
+        B.polestar_commit(self.h, blk_start, self.w_lm, h_final, self.packets[self.last_packet], self.delta,
+                          self.active_masked, self.suffix_masked, self.hist_vals, self.hist_cnt,
+                          self.commit_active, self.commit_suffix, self.conf_active, self.yhat_active, self.spike,
+                          self.conf_suffix, self.ws, self.ws_bytes)
+
     # ---- one denoising step -----------------------------------------------------------------
     def step(self, blk_start: int, h_in: torch.Tensor, refresh: bool = True, commit_delta: bool = True) -> torch.Tensor:
         """Runs every layer on the active rows h_in [batch, B, d]; returns the last layer's active rows."""
