@@ -5,10 +5,14 @@ drift history, and the suffix commit rule.
 Inputs are seeded synthetic tensors.  Some rows are planted close to one
 LM-head row so that the confidences spread over (0, 1) and straddle tau_s; one
 row is planted on the mask token's row so that the argmax has to skip it.
-Confidences are compared with the oracle's float64 values; the decisions are
-checked bit-exactly by evaluating the oracle's rule on the GPU's confidences
-(the rule is a float32 comparison, taken in the same precision on both sides).
-The full-vocabulary case streams W_lm through the oracle in row chunks.
+Confidences are compared with the oracle's float64 values.  The decisions are
+checked end to end: the oracle takes them from its own confidences (the rule is
+a float32 comparison, taken in that precision on both sides) and the spikes and
+drift history, whose inputs both sides share, must be bit-identical; a commit
+mask may differ only where the oracle's confidence lies within the confidence
+tolerance (2e-3 relative) of its threshold, or its spike within the matching
+band around tau_d = alpha (tau_s - c)^2, and every such case is reported.  The
+full-vocabulary case streams W_lm through the oracle in row chunks.
 """
 from __future__ import annotations
 
@@ -36,6 +40,27 @@ CASES = {
 }
 
 CHUNK = 8192   # LM-head rows per oracle chunk
+C_TOL = 2e-3   # relative tolerance of a confidence
+
+
+def _check_masks(got, want, c, thr, tag, spike=None, alpha=None, spike_tol=0.0):
+    """Commit masks from the two sides' confidences: equal, except where the oracle's confidence c
+    is within C_TOL of its threshold (or, with spikes, the spike within the band of tau_d that the
+    confidence tolerance spans, widened by ``spike_tol``, the bound on the two sides' spike
+    difference when the drift itself comes from each side's own computation); such differences
+    are reported."""
+    got, want = np.asarray(got), np.asarray(want)
+    c = np.asarray(c, dtype=np.float64)
+    near = np.abs(c - thr) <= C_TOL * np.maximum(c, thr)
+    if spike is not None:
+        taud = alpha * (thr - c) ** 2
+        band = 2 * alpha * np.abs(thr - c) * C_TOL * c + 1e-6 * np.maximum(taud, 1e-30) + spike_tol
+        near |= np.abs(np.asarray(spike, np.float64) - taud) <= band
+    diff = np.nonzero(got != want)[0]
+    for i in diff:
+        log(f"    {tag}: row {i} decided differently at a threshold (c {c[i]:.6f}, threshold {thr})")
+    assert np.all(near[diff]), f"{tag}: commit masks differ away from a threshold at rows {diff[~near[diff]]}"
+    return len(diff)
 
 
 def _lm_logits(w, rows64: np.ndarray, eps: float) -> np.ndarray:
@@ -131,26 +156,27 @@ def test_commit_parity(case):
             assert np.array_equal(got["yhat"][b], ya), f"seq {b}: argmax ids differ"
             assert got["yhat"][b][Bk - 1] != mask_id
             assert (ca >= w.tau_s).any() and (ca < w.tau_s).any(), "planted rows should straddle tau_s"
-            # the rule on the GPU's confidences: bit-exact decisions, spikes and history
-            com, sp, _, hv, hc = O.commit_decide(np64(delta[b]), got["conf_active"][b], act_mask[b].numpy(),
+            # the rule on the oracle's own confidences: masks end to end; spikes and history, whose
+            # inputs both sides share, bit-identical
+            com, sp, _, hv, hc = O.commit_decide(np64(delta[b]), ca.astype(np.float32), act_mask[b].numpy(),
                                                  hv0[b], hc0[b], w.hist, w.alpha, w.tau_s)
-            assert np.array_equal(got["commit_active"][b], com), f"seq {b}: commit mask differs"
+            _check_masks(got["commit_active"][b], com, ca, w.tau_s, f"seq {b} active", sp, w.alpha)
             assert np.array_equal(got["spike"][b].astype(np.float32), sp), f"seq {b}: spike differs"
             assert np.array_equal(hist_cnt_d[b].cpu().numpy(), hc)
             assert np.array_equal(hist_vals[b].cpu().numpy().reshape(Bk, -1)[:, :w.hist],
                                   hv.reshape(Bk, -1)[:, :w.hist].astype(np.float32))
             # suffix rows
             cs = c[Bk:]
-            conf_suf = np.zeros(w.win_suffix, dtype=np.float32)
+            conf_suf = np.zeros(w.win_suffix, dtype=np.float64)
             elig = np.zeros(w.win_suffix, dtype=bool)
             for t, r in enumerate(suf_r):
                 slot = int(idx[r]) - n_pre
                 err = abs(got["conf_suffix"][b][slot] - cs[t]) / max(cs[t], 1e-30)
-                assert err <= 2e-3, f"seq {b}: suffix confidence rel err {err:.3e}"
-                conf_suf[slot] = got["conf_suffix"][b][slot]
+                assert err <= C_TOL, f"seq {b}: suffix confidence rel err {err:.3e}"
+                conf_suf[slot] = cs[t]
                 elig[slot] = suf_mask[b, slot] != 0
-            want = O.suffix_commit(conf_suf, elig, w.tau_suf)
-            assert np.array_equal(got["commit_suffix"][b], want), f"seq {b}: suffix commit differs"
+            want = O.suffix_commit(conf_suf.astype(np.float32), elig, w.tau_suf)
+            _check_masks(got["commit_suffix"][b], want, conf_suf, w.tau_suf, f"seq {b} suffix")
             log(f"    seq {b}: {int(com.sum())} active commits, {int(want.sum())} suffix commits, "
                 f"{len(suf_r)} suffix packet rows of {n_suf}")
     finally:
@@ -221,12 +247,12 @@ def test_entry_commit_parity(case):
             es = np.abs(got["conf_suffix"][b][:n_suf] - cs) / np.maximum(cs, 1e-30)
             assert es.size == 0 or es.max() <= 2e-3, f"seq {b}: suffix confidence rel err {es.max():.3e}"
             assert np.all(got["conf_suffix"][b][n_suf:] == 0) and np.all(got["commit_suffix"][b][n_suf:] == 0)
-            # the rule on the GPU's confidences, bit-exact
-            assert np.array_equal(got["commit_active"][b],
-                                  O.entry_commit(got["conf_active"][b], act_mask[b].numpy(), w.tau_s))
-            assert np.array_equal(got["commit_suffix"][b][:n_suf],
-                                  O.entry_commit(got["conf_suffix"][b][:n_suf], suf_mask[b, :n_suf].numpy(),
-                                                 w.tau_suf))
+            # the rule on the oracle's own confidences, masks end to end
+            _check_masks(got["commit_active"][b], O.entry_commit(ca.astype(np.float32), act_mask[b].numpy(), w.tau_s),
+                         ca, w.tau_s, f"seq {b} entry active")
+            _check_masks(got["commit_suffix"][b][:n_suf],
+                         O.entry_commit(cs.astype(np.float32), suf_mask[b, :n_suf].numpy(), w.tau_suf), cs, w.tau_suf,
+                         f"seq {b} entry suffix")
             log(f"    seq {b}: {int(got['commit_active'][b].sum())} active and "
                 f"{int(got['commit_suffix'][b].sum())} suffix commits of {Bk} + {n_suf} rows")
     finally:
