@@ -51,7 +51,7 @@ struct ProfScope {
 };
 #define PROF(id) ProfScope _prof_##__LINE__(h, s, id)
 
-constexpr int kMaxRows = 192;   // rows of one projection tile column (block + window + centroids)
+constexpr int kMaxRows = 192;   // rows of one projection launch (longer row lists take several)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -333,6 +333,8 @@ AttnArgs attn_base(polestar_handle* h, const polestar_layer* L, void* ws, int ca
 void set_row_groups(const polestar_handle* h, AttnArgs& a) {
   const int tiles = PS_CEIL_DIV(a.n_tok + a.n_proxy, 16);
   a.row_groups = tiles >= 2 * h->attn_rgroups ? h->attn_rgroups : 1;
+  // at most 12 row tiles (waves) per workgroup
+  a.row_groups = std::max(a.row_groups, PS_CEIL_DIV(tiles, 12));
   a.group_tiles = PS_CEIL_DIV(tiles, a.row_groups);
 }
 
@@ -1071,8 +1073,8 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   if (d.n_clusters > 16 || d.top_k > d.n_clusters) return POLESTAR_E_UNSUPPORTED;
   if (d.head_dim != 64 && d.head_dim != 128) return POLESTAR_E_UNSUPPORTED;
   if (d.block > 64 || d.win_prefix + d.win_suffix > 256) return POLESTAR_E_UNSUPPORTED;
-  if (d.block + d.win_prefix + d.win_suffix + d.n_clusters > kMaxRows) return POLESTAR_E_UNSUPPORTED;
-  if (d.n_pos > 1024) return POLESTAR_E_UNSUPPORTED;
+  if (d.n_pos > kMaxPos) return POLESTAR_E_UNSUPPORTED;
+  if (d.dtype == POLESTAR_F32 && d.n_pos > 1024) return POLESTAR_E_UNSUPPORTED;   // f32 attention keeps a row's scores in LDS
   if (d.d % 16 != 0) return POLESTAR_E_UNSUPPORTED;
   if (d.dtype == POLESTAR_BF16) {
     if (d.d % 128 || (d.n_heads * d.head_dim) % 128 || d.ffn % 128 || d.vocab % 16 || d.n_pos % 4 || d.n_pos < 8)
@@ -1103,7 +1105,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->nkv = d.n_kv_heads * d.head_dim;
   h->rq = 16 * PS_CEIL_DIV(h->mq, 16);
   h->rt = 16 * PS_CEIL_DIV(h->mt, 16);
-  h->ec = kMaxRows;   // >= rq: the rows of a sequence never exceed kMaxRows
+  h->ec = std::max(kMaxRows, h->rq);   // >= rq: every row list of a sequence fits one slab list
   h->rw = 16 * PS_CEIL_DIV(h->win_max, 16);
   const int ntiles = PS_CEIL_DIV(d.d, 64) * d.batch;
   int ks = PS_CEIL_DIV(256, ntiles);

@@ -454,7 +454,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-constexpr int kKlPer = 4;   // logits per thread of a 256-thread workgroup (n_pos <= 1024)
 
 // Block-wide max (fixed combination order); every thread gets the result.
 PS_DEV float block_max_f(float v, float* red) {
@@ -483,20 +482,21 @@ PS_DEV void block_sum2(float& x, float& y, float* red) {
   __syncthreads();
 }
 
-// KL(softmax(s) || softmax(p)) of one row held kKlPer values per thread across the workgroup,
+// KL(softmax(s) || softmax(p)) of one row held PER values per thread across the workgroup,
 // from the logit differences: with u = exp(p - max p), dbar the u-weighted mean of s - p and
 // e = s - p - dbar, KL = E_u[e^e e] / E_u[e^e] - log E_u[e^e], formed with expm1/log1p so that
 // small drifts keep their relative precision.
+template <int PER>
 PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
   float mp = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kKlPer; ++i)
+  for (int i = 0; i < PER; ++i)
     if (threadIdx.x + 256 * i < n) mp = fmaxf(mp, pv[i]);
   mp = block_max_f(mp, red);
-  float u[kKlPer];
+  float u[PER];
   float s0 = 0.f, sd = 0.f;
 #pragma unroll
-  for (int i = 0; i < kKlPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const bool ok = threadIdx.x + 256 * i < n;
     u[i] = ok ? expf(pv[i] - mp) : 0.f;
     s0 += u[i];
@@ -506,7 +506,7 @@ PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
   const float dbar = sd / s0;
   float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < kKlPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     if (threadIdx.x + 256 * i < n) {
       const float e = (sv[i] - pv[i]) - dbar;
       s1 += u[i] * expm1f(e);
@@ -520,6 +520,7 @@ PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
 
 // One 256-thread workgroup per (staged row, head): KL against the previous logits (when
 // wanted), then the staged logits replace them.  Staged rows: [proxies; active].
+template <int PER>
 PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   __shared__ float red[8];
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
@@ -545,19 +546,19 @@ PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
   }
   s += lo;
   prev += lo;
-  float sv[kKlPer], pv[kKlPer];
+  float sv[PER], pv[PER];
 #pragma unroll
-  for (int i = 0; i < kKlPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int j = threadIdx.x + 256 * i;
     sv[i] = j < n ? s[j] : 0.f;
     pv[i] = (do_kl && j < n) ? prev[j] : 0.f;
   }
   if (do_kl) {
-    const float kl = block_kl(sv, pv, n, red);
+    const float kl = block_kl<PER>(sv, pv, n, red);
     if (threadIdx.x == 0) *out = kl;
   }
 #pragma unroll
-  for (int i = 0; i < kKlPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int j = threadIdx.x + 256 * i;
     if (j < n) prev[j] = sv[i];
   }
@@ -566,11 +567,12 @@ PS_DEV void kl_item(const AttnArgs& a, int item, int b) {
 // One launch for the two consumers of the chunk kernel's outputs: workgroups below
 // merge_wgs merge token rows (four (row, head) pairs each, one per wave), the rest form one KL
 // item each.  Both only read what the attention kernel wrote and write disjoint outputs.
-template <int DH>
+// PER logits per thread: rows of up to 256 * PER positions.
+template <int DH, int PER>
 __global__ __launch_bounds__(256) void attn_merge_kl_kernel(AttnArgs a, int merge_wgs) {
   const int wave = threadIdx.x >> 6, b = blockIdx.y;
   if ((int)blockIdx.x < merge_wgs) attn_merge_pair<DH>(a, blockIdx.x * 4 + wave, b);
-  else kl_item(a, blockIdx.x - merge_wgs, b);
+  else kl_item<PER>(a, blockIdx.x - merge_wgs, b);
 }
 
 // Per sequence: D_c = sum_h max(0, KL_{c,h}); top-k clusters by (D desc, index asc), found by
@@ -687,13 +689,19 @@ hipError_t launch_merge_kl(const AttnArgs& a, bool merge, hipStream_t s) {
   merge = merge && a.n_chunks > 1 && a.n_tok > 0;
   if (merge && a.n_chunks > 64) return hipErrorInvalidValue;
   const int nst = a.n_proxy + (a.act_logits ? a.block : 0);
-  if (a.n_pos > 256 * kKlPer) return hipErrorInvalidValue;
+  if (a.n_pos > kMaxPos) return hipErrorInvalidValue;
   const int mw = merge ? PS_CEIL_DIV(a.n_tok * a.hq, 4) : 0, kw = nst * a.hq;
   if (mw + kw == 0) return hipSuccess;
   const dim3 grid(mw + kw, a.batch);
-  if (!merge || a.dh == 128) hipLaunchKernelGGL(attn_merge_kl_kernel<128>, grid, dim3(256), 0, s, a, mw);
-  else if (a.dh == 64) hipLaunchKernelGGL(attn_merge_kl_kernel<64>, grid, dim3(256), 0, s, a, mw);
-  else return hipErrorInvalidValue;
+  if (merge && a.dh != 128 && a.dh != 64) return hipErrorInvalidValue;
+  auto go = [&](auto PERc) {
+    constexpr int PER = decltype(PERc)::value;
+    if (!merge || a.dh == 128) hipLaunchKernelGGL((attn_merge_kl_kernel<128, PER>), grid, dim3(256), 0, s, a, mw);
+    else hipLaunchKernelGGL((attn_merge_kl_kernel<64, PER>), grid, dim3(256), 0, s, a, mw);
+  };
+  if (a.n_pos <= 1024) go(std::integral_constant<int, 4>{});
+  else if (a.n_pos <= 2048) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 16>{});
   return hipGetLastError();
 }
 

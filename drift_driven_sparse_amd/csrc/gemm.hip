@@ -66,16 +66,17 @@ template <typename T, int KIND>
 PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, int n0, int nt,
                      const float* tile) {
   const int tid = threadIdx.x, nthr = blockDim.x;
+  const int r0 = g.A.row0;   // tile row r is row r0 + r of the sequence
   if constexpr (KIND == EPI_PARTIAL) {
     float* out = g.part + (((int64_t)blockIdx.z * g.batch + b) * g.part_rows) * g.N;
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
       const int r = idx / kNT, c = idx % kNT, n = n0 + c;
-      if (n < g.N) out[(int64_t)r * g.N + n] = tile[r * kLDT + c];
+      if (n < g.N) out[(int64_t)(r0 + r) * g.N + n] = tile[r * kLDT + c];
     }
   } else if constexpr (KIND == EPI_QKV) {
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
       const int r = idx / kNT, c = idx % kNT, n = n0 + c;
-      if (n < g.N) epi_qkv_elem<T>(e, b, r, n, tile[r * kLDT + c]);
+      if (n < g.N) epi_qkv_elem<T>(e, b, r0 + r, n, tile[r * kLDT + c]);
     }
   } else if constexpr (KIND == EPI_SWIGLU) {
     // tile columns: [gate 16 | up 16] x 2 pairs -> 32 output columns starting at n0/2
@@ -86,12 +87,12 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
       if (oc >= e.ffn) continue;
       const float gv = tile[r * kLDT + (2 * p) * 16 + jj];
       const float uv = tile[r * kLDT + (2 * p + 1) * 16 + jj];
-      St<T>::store((T*)e.act, ((int64_t)b * e.act_rows + r) * e.ffn + oc, gv / (1.f + expf(-gv)) * uv);
+      St<T>::store((T*)e.act, ((int64_t)b * e.act_rows + r0 + r) * e.ffn + oc, gv / (1.f + expf(-gv)) * uv);
     }
   } else if constexpr (KIND == EPI_KV) {
     for (int idx = tid; idx < rows_b * kNT; idx += nthr) {
       const int r = idx / kNT, c = idx % kNT, n = n0 + c;
-      if (n < g.N) epi_kv_elem<T>(e, b, r, n, tile[r * kLDT + c]);
+      if (n < g.N) epi_kv_elem<T>(e, b, r0 + r, n, tile[r * kLDT + c]);
     }
   } else if constexpr (KIND == EPI_LMSTAT) {
     // Per row, over this tile's vocabulary ids: max logit, sum exp(logit - max), and the
@@ -108,7 +109,7 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
       const unsigned long long hit = __ballot(lb == bm && bm > -INFINITY);
       const int bid = hit ? n0 + __ffsll((long long)hit) - 1 : -1;
       if (lane == 0) {
-        float* st = e.lm_stats + (((int64_t)b * e.lm_rows + r) * e.lm_tiles + nt) * 4;
+        float* st = e.lm_stats + (((int64_t)b * e.lm_rows + r0 + r) * e.lm_tiles + nt) * 4;
         st[0] = m;
         st[1] = se;
         st[2] = bm;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
   __shared__ float tile[RT * 16 * kLDT];
   // sequences fastest: one weight tile's workgroups of all sequences are dispatched together
   const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
-  int rows_b = g.A.rows(b);
+  int rows_b = g.A.rows(b) - g.A.row0;   // this launch's slab of rows
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
   const int nrt = (rows_b + 15) >> 4;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e)
   for (int rt = 0; rt < RT; ++rt) {
     int r = rt * 16 + (lane & 15);
     if (r >= rows_b) r = 0;
-    arow[rt] = (const uint4*)(Ab + g.A.src_row(b, r) * g.A.lda + 8 * (lane >> 4));
+    arow[rt] = (const uint4*)(Ab + g.A.src_row(b, g.A.row0 + r) * g.A.lda + 8 * (lane >> 4));
   }
   const int n16_total = g.N >> 4;
   // per-subtile fragment stream; subtiles past N re-read the first one (their columns are never stored)
@@ -231,7 +232,7 @@ template <int RT, int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) {
   __shared__ float tile[RT * 16 * kLDT];
   const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
-  int rows_b = g.A.rows(b);
+  int rows_b = g.A.rows(b) - g.A.row0;   // this launch's slab of rows
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
   const int kc = g.K >> 2;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) 
     const int r = idx / kNT, c = idx % kNT, n = n0 + c;
     float acc = 0.f;
     if (n < g.N) {
-      const float4* a4 = (const float4*)(Ab + g.A.src_row(b, r) * g.A.lda);
+      const float4* a4 = (const float4*)(Ab + g.A.src_row(b, g.A.row0 + r) * g.A.lda);
       const float4* w4 = (const float4*)(W + (int64_t)n * g.K);
       for (int k = c0; k < c1; ++k) {
         const float4 x = a4[k], y = w4[k];
@@ -405,11 +406,20 @@ hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int G
 
 template <typename T>
 hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s) {
-  if (max_rows <= 32) return dispatch_kind<T, 2>(g, e, s);
-  if (max_rows <= 64) return dispatch_kind<T, 4>(g, e, s);
-  if (max_rows <= 144) return dispatch_kind<T, 9>(g, e, s);
-  if (max_rows <= 192) return dispatch_kind<T, 12>(g, e, s);
-  return hipErrorInvalidValue;
+  if (g.A.row0 != 0) return hipErrorInvalidValue;
+  // one launch per slab of at most kDlSlab rows
+  for (int r0 = 0; r0 < max_rows; r0 += kDlSlab) {
+    GemmArgs gs = g;
+    gs.A.row0 = r0;
+    const int mr = max_rows - r0 < kDlSlab ? max_rows - r0 : kDlSlab;
+    hipError_t err;
+    if (mr <= 32) err = dispatch_kind<T, 2>(gs, e, s);
+    else if (mr <= 64) err = dispatch_kind<T, 4>(gs, e, s);
+    else if (mr <= 144) err = dispatch_kind<T, 9>(gs, e, s);
+    else err = dispatch_kind<T, 12>(gs, e, s);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 template <typename T>

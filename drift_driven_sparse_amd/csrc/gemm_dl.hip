@@ -119,21 +119,30 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
     return hipErrorInvalidValue;
   } else {
     if (max_rows <= 0) return hipSuccess;
-    if (max_rows > 192) return hipErrorInvalidValue;
+    if (g.A.row0 != 0) return hipErrorInvalidValue;
     if (g.K % 32 || g.N % 16 || g.ksplit < 1 || g.ksplit > (g.K >> 5)) return hipErrorInvalidValue;
     if (g.wg < 1 || g.wg % (dl_tile_cols(shape) / 16) != 0) return hipErrorInvalidValue;
     const bool one_plane = shape == DL_NARROW || shape == DL_N192 || shape == DL_N96;
     if (g.planes != (one_plane ? 1 : 2)) return hipErrorInvalidValue;
-    switch (shape) {
-      case DL_NARROW: return dl_launch_narrow(g, max_rows, s);
-      case DL_N192: return dl_launch_n192(g, max_rows, s);
-      case DL_N96: return dl_launch_n96(g, max_rows, s);
-      case DL_WIDE: return dl_launch_wide(g, max_rows, s);
-      case DL_MID: return dl_launch_mid(g, max_rows, s);
-      case DL_W192: return dl_launch_w192(g, max_rows, s);
-      case DL_MID8: return dl_launch_mid8(g, max_rows, s);
-      default: return hipErrorInvalidValue;
+    // rows past one slab's 192 take further launches over the same weights, one per slab
+    for (int r0 = 0; r0 < max_rows; r0 += kDlSlab) {
+      DlArgs gs = g;
+      gs.A.row0 = r0;
+      const int mr = max_rows - r0 < kDlSlab ? max_rows - r0 : kDlSlab;
+      hipError_t e;
+      switch (shape) {
+        case DL_NARROW: e = dl_launch_narrow(gs, mr, s); break;
+        case DL_N192: e = dl_launch_n192(gs, mr, s); break;
+        case DL_N96: e = dl_launch_n96(gs, mr, s); break;
+        case DL_WIDE: e = dl_launch_wide(gs, mr, s); break;
+        case DL_MID: e = dl_launch_mid(gs, mr, s); break;
+        case DL_W192: e = dl_launch_w192(gs, mr, s); break;
+        case DL_MID8: e = dl_launch_mid8(gs, mr, s); break;
+        default: e = hipErrorInvalidValue;
+      }
+      if (e != hipSuccess) return e;
     }
+    return hipSuccess;
   }
 }
 

@@ -55,7 +55,9 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   // weight tile are dispatched together, so the repeats of the tile come from L2 and the
   // last-level cache rather than HBM
   const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
-  int rows_b = g.A.rows(b);
+  // this launch's slab: rows [row0, row0 + RT*16) of the sequence; r below is slab-local
+  const int row0 = g.A.row0;
+  int rows_b = g.A.rows(b) - row0;
   if (rows_b > RT * 16) rows_b = RT * 16;
   if (rows_b <= 0) return;
   const int nrt = (rows_b + 15) >> 4;
@@ -84,12 +86,12 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     if (f < FA) {
       const int p = f / RT, rt = f % RT;
       if (g.A.tiles > 0) {   // fragment-packed: step s, plane p, tile rt
-        src[i] = (const char*)(Ab + ((((int64_t)g0 * PL + p) * g.A.tiles + rt) * 64 + lane) * 8);
+        src[i] = (const char*)(Ab + ((((int64_t)g0 * PL + p) * g.A.tiles + (row0 >> 4) + rt) * 64 + lane) * 8);
         stride[i] = PL * g.A.tiles * 1024;
       } else {
         int r = rt * 16 + (lane & 15);
         if (r >= rows_b) r = 0;
-        src[i] = (const char*)(Ab + p * g.A.plane_stride + g.A.src_row(b, r) * g.A.lda + (int64_t)g0 * 32 +
+        src[i] = (const char*)(Ab + p * g.A.plane_stride + g.A.src_row(b, row0 + r) * g.A.lda + (int64_t)g0 * 32 +
                                8 * (lane >> 4));
         stride[i] = 64;
       }
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
 
   // accumulator element (rt, sb, i) of this lane: row r, column n
   const int col0 = (nt * CG + cg) * NSUB * 16 + (lane & 15);
-  const int row0 = rg * 16 + 4 * (lane >> 4);   // accumulator tile j holds rows of tile j*RG + rg
+  const int rrow0 = rg * 16 + 4 * (lane >> 4);   // accumulator tile j holds rows of tile j*RG + rg
   if (g.ksplit > 1 || KIND == EPI_PARTIAL) {
     float* out = g.part + ((int64_t)sp * g.batch + b) * g.part_rows * g.N;
 #pragma unroll
@@ -167,8 +169,8 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * RG * 16 + i, c = col0 + sb * 16;
-          if (r < rows_b && c < g.N) out[(int64_t)r * g.N + c] = acc[rt][sb][i];
+          const int r = rrow0 + rt * RG * 16 + i, c = col0 + sb * 16;
+          if (r < rows_b && c < g.N) out[(int64_t)(row0 + r) * g.N + c] = acc[rt][sb][i];
         }
     return;
   }
@@ -179,10 +181,10 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * RG * 16 + i, c = col0 + sb * 16;
+          const int r = rrow0 + rt * RG * 16 + i, c = col0 + sb * 16;
           if (r < rows_b && c < g.N) {
-            if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
-            else epi_kv_elem<T>(g.e, b, r, c, acc[rt][sb][i]);
+            if constexpr (KIND == EPI_QKV) epi_qkv_elem<T>(g.e, b, row0 + r, c, acc[rt][sb][i]);
+            else epi_kv_elem<T>(g.e, b, row0 + r, c, acc[rt][sb][i]);
           }
         }
   } else if constexpr (KIND == EPI_SWIGLU) {
@@ -196,15 +198,15 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
       for (int j = 0; j < NSUB / 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + rt * RG * 16 + i;
+          const int r = rrow0 + rt * RG * 16 + i;
           const int oc = ((nt * CG + cg) * NSUB / 2 + j) * 16 + (lane & 15);
           if (r < rows_b && oc < e.ffn) {
             const float gv = acc[rt][2 * j][i], uv = acc[rt][2 * j + 1][i];
             const float a = gv / (1.f + expf(-gv)) * uv;
             uint16_t hi, lo;
             split_bf16(a, hi, lo);
-            act[apack(r, oc, 0, 2, e.act_tiles)].bits = hi;
-            act[apack(r, oc, 1, 2, e.act_tiles)].bits = lo;
+            act[apack(row0 + r, oc, 0, 2, e.act_tiles)].bits = hi;
+            act[apack(row0 + r, oc, 1, 2, e.act_tiles)].bits = lo;
           }
         }
   }
@@ -232,7 +234,7 @@ hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
 
 
 // Launch of one workgroup shape (RG x CG waves of NSUB subtiles, PL planes) with the row-tile
-// count per wave that covers max_rows (at most 192 rows).
+// count per wave that covers max_rows (at most 192 rows: one slab).
 template <int RG, int CG, int NSUB, int PL>
 hipError_t launch_shape(const DlArgs& g, int max_rows, hipStream_t s) {
   constexpr int kMax = 192 / (16 * RG);

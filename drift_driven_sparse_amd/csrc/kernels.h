@@ -55,6 +55,7 @@ struct GemmA {
   int32_t map_bstride, map_from, map_off;
   const int32_t* rows_dev;   // rows of block b = min(rows_dev[b] + rows_add, rows_max), or rows_static
   int32_t rows_add, rows_static, rows_max;
+  int32_t row0;              // first row of this launch (a multiple of 16): launches cover row slabs
   PS_DEV int rows(int b) const {
     if (!rows_dev) return rows_static;
     int r = rows_dev[b] + rows_add;
@@ -189,6 +190,8 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 // A: bf16 planes (1 = bf16 rows, 2 = hi/lo of float32 rows), rows gathered per lane.
 // ksplit > 1: raw sums to part[((s*batch + b)*part_rows + r)*N + n], finished by
 // launch_dl_finish (QKV, gate/up, KV) or the row reduction (O, down).
+constexpr int kMaxPos = 4096;  // key positions per sequence at most (KL rows are held in registers)
+constexpr int kDlSlab = 192;   // rows per launch of the projection kernels (longer row lists take several)
 struct DlArgs {
   GemmA A;
   int32_t planes;

@@ -50,6 +50,11 @@ def test_create_accepts_the_five_workload_shapes():
         _dims(d=3584, n_heads=28, n_kv_heads=4, head_dim=128, ffn=18944, n_pos=640, dtype=B.BF16),
         _dims(d=4096, n_heads=32, n_kv_heads=32, head_dim=128, ffn=12288, n_pos=768, batch=16, vocab=126464,
               dtype=B.BF16, resid_fmt=B.RESID_NVFP4),
+        # sweep shapes past one 192-row projection slab and 1024 positions
+        _dims(d=256, n_heads=4, n_kv_heads=4, head_dim=64, ffn=512, n_pos=512, block=64, win_prefix=128,
+              win_suffix=64, dtype=B.BF16),
+        _dims(d=256, n_heads=4, n_kv_heads=4, head_dim=64, ffn=512, n_pos=4096, block=64, win_prefix=192,
+              win_suffix=64, n_clusters=16, top_k=8, dtype=B.BF16),
     ]
     for dm in shapes:
         h = B.polestar_create(dm, _params(mask_id=max(dm.vocab - 1, 0)))
@@ -67,7 +72,9 @@ def test_create_accepts_the_five_workload_shapes():
     (dict(resid_fmt=B.RESID_NVFP4), B.E_UNSUPPORTED),       # NVFP4 needs bf16 storage
     (dict(d=0), B.E_SHAPE),
     (dict(n_pos=16), B.E_SHAPE),
-    (dict(win_prefix=128, win_suffix=64), B.E_UNSUPPORTED),  # rows per tile column exceeded
+    (dict(win_prefix=224, win_suffix=64), B.E_UNSUPPORTED),  # window of more than 256 rows
+    (dict(dtype=B.BF16, n_pos=8192), B.E_UNSUPPORTED),        # more than 4096 positions
+    (dict(n_pos=2048), B.E_UNSUPPORTED),                      # float32 storage: at most 1024 positions
     (dict(dtype=B.BF16, d=200), B.E_UNSUPPORTED),
 ])
 def test_create_rejects_bad_dims(kw, code):

@@ -37,6 +37,13 @@ CASES = {
                                           alpha=2.5), 2, 64),
     "small_hist7_alpha40": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128, hist=7,
                                          alpha=40.0), 2, 64),
+    # the other points of the page's threshold and history sweeps
+    "small_hist1_taus0p7": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128, hist=1,
+                                         tau_s=0.7), 2, 64),
+    "small_hist3_tausuf0p85": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128,
+                                            hist=3, tau_suf=0.85), 2, 64),
+    "small_tausuf0p95": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", vocab=1008, prompt=64, gen=128,
+                                      tau_suf=0.95), 2, 64),
 }
 
 CHUNK = 8192   # LM-head rows per oracle chunk
@@ -92,10 +99,14 @@ def test_commit_parity(case):
         w_lm = dev.pack(B.W_LM, wlm)
         # active rows: random, with planted rows near W_lm rows (confidences spread over (0, 1))
         # x = sqrt(d) W_lm[v] + l g (g ~ N(0, 1) per element) gives the planted logit about
-        # sqrt(d) / sqrt(1 + l^2) against N(0, 1) logits elsewhere; l0 puts c near 0.9.
+        # sqrt(d) / sqrt(1 + l^2) against N(0, 1) logits elsewhere; noise_for(tau) puts c near tau.
         h_fin = synth.tensor(w, (90, 1), (batch, Bk, d), 1.0, device="cuda", dtype="f32")
-        target = np.log(V) + 0.5 + np.log(9.0)
-        l0 = np.sqrt(max((np.sqrt(d) / target) ** 2 - 1.0, 0.01))
+
+        def noise_for(tau):
+            target = np.log(V) + 0.5 + np.log(tau / (1.0 - tau))
+            return np.sqrt(max((np.sqrt(d) / target) ** 2 - 1.0, 0.01))
+
+        l0, l_suf = noise_for(w.tau_s), noise_for(w.tau_suf)
         for b in range(batch):
             for i, f in enumerate([0.6, 0.85, 0.94, 0.99, 1.04, 1.11, 1.33, 1.7]):
                 j = (3 * i + b) % (Bk - 1)
@@ -113,10 +124,11 @@ def test_commit_parity(case):
             pick = np.sort(rng.choice(n_win, size=min(n_win, 12 + 7 * b), replace=False))
             u_idx[b, :len(pick)] = torch.tensor(pick, dtype=torch.int32)
             u_cnt[b] = len(pick)
-            for t, wr in enumerate(pick[::3]):      # some confident suffix/prefix packet rows
+            for t, wr in enumerate(pick[::3]):      # suffix/prefix packet rows with c spread around tau_suf
                 v = int(synth.hash32_int(seed + 7 * b + t + 1000) % (V - 1))
                 r = int(np.nonzero(pick == wr)[0][0])
-                u_rows[b, r] = wlm[v].float() * np.sqrt(d) + 0.05 * u_rows[b, r]
+                f = (0.05, 0.8, 0.95, 1.05, 1.25)[t % 5]
+                u_rows[b, r] = wlm[v].float() * np.sqrt(d) + (l_suf * f) * u_rows[b, r]
         u_rows = u_rows.to(torch.bfloat16)
         u_idx_d, u_cnt_d = u_idx.cuda(), u_cnt.cuda()
         # drift, masks, history

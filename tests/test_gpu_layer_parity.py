@@ -56,6 +56,21 @@ CASES = {
     # 188 rows per sequence: the widest row tiling of every kernel
     "rows188_K4_k2_B64": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, n_clusters=4,
                                        top_k=2, block=64, win_prefix=96, win_suffix=24), 1, {}),
+    # windows (1,1)B and (2,2)B of the window ablation
+    "sweep_B32_w11": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, win_prefix=32,
+                                   win_suffix=32), 1, {}),
+    "sweep_B32_w22": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, win_prefix=64,
+                                   win_suffix=64), 1, {}),
+    # more rows per sequence than one 192-row projection slab: B = 64 at the default (2,1)B window
+    # (264 rows), and 336 rows with K = 16 at (3,1)B
+    "rows264_B64_w21": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=256, gen=256, block=64,
+                                     win_prefix=128, win_suffix=64), 1, {}),
+    "rows336_K16_k8_B64_w31": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=256, gen=256, block=64,
+                                            n_clusters=16, top_k=8, win_prefix=192, win_suffix=64), 1, {}),
+    "llada_layer_B64_w21": (synth.shrink(synth.WORKLOADS[2], block=64, win_prefix=128, win_suffix=64), 1, {}),
+    # more than 1024 positions (KL rows of 2048 and 4096 logits)
+    "npos2048_bf16": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=1024, gen=1024), 1, {}),
+    "npos4096_bf16": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=2048, gen=2048), 1, {}),
     # residual formats of the quantisation ablation
     "resid_fp8": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, resid="fp8"), 1, {}),
     "resid_mxint8": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=128, resid="mxint8"), 1, {}),

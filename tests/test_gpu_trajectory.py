@@ -48,6 +48,12 @@ CASES = {
     "tiny_fp32_2layers": (synth.WORKLOADS[1], 2, 10),
     "tiny_bf16_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16"), 2, 10),
     "tiny_bf16_nvfp4_2layers": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", resid="nvfp4"), 2, 8),
+    # the update trigger's sweep: refresh once more than tau_upd tokens were decoded since the
+    # last refresh (1, 2, 4), or never
+    "tiny_bf16_tau_upd1": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", tau_upd=1), 2, 8),
+    "tiny_bf16_tau_upd2": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", tau_upd=2), 2, 8),
+    "tiny_bf16_tau_upd4": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", tau_upd=4), 2, 8),
+    "tiny_bf16_tau_upd_never": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", tau_upd=-1), 2, 6),
     # the benchmark's stack shape (32 x 128 heads, FFN 12288, n 1024), first four layers
     "llada8b_stack_4layers_n1024": (synth.shrink(synth.WORKLOADS[3], n_layers=4), 4, 8),
     # the Dream-7B GQA stack shape (28 / 4 heads, FFN 18944, n 640), first four layers
@@ -231,6 +237,9 @@ def test_trajectory_parity(case):
             log(f"[trajectory] step {t} ok ({'refresh' if refresh else 'active only'}, {len(offs)} decoded)")
         log(f"[trajectory] case={case} passed: {sum(kinds)} refresh and {len(kinds) - sum(kinds)} active-only "
             f"steps, {ties} reported top-k near-ties")
-        assert any(kinds) and not all(kinds), "the trigger gave a trajectory of one step kind only"
+        if w.tau_upd < 0:
+            assert not any(kinds), "tau_upd < 0 never refreshes"
+        else:
+            assert any(kinds) and not all(kinds), "the trigger gave a trajectory of one step kind only"
     finally:
         dev.close()
