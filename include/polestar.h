@@ -120,11 +120,12 @@ typedef struct polestar_dims {
   int32_t n_kv_heads; /* key/value heads; n_heads % n_kv_heads == 0 */
   int32_t head_dim;   /* 64 or 128 */
   int32_t ffn;        /* SwiGLU width */
-  int32_t n_pos;      /* positions per sequence (prompt + generation); bf16: multiple of 4 */
+  int32_t n_pos;      /* positions per sequence (prompt + generation); bf16: multiple of 4, at
+                         most 4096; f32: at most 1024 */
   int32_t batch;      /* independent sequences processed together */
   int32_t block;      /* active block size B (<= 64) */
   int32_t win_prefix; /* |Omega_p| */
-  int32_t win_suffix; /* |Omega_s| */
+  int32_t win_suffix; /* |Omega_s|; win_prefix + win_suffix <= 256 */
   int32_t n_clusters; /* K (1..16) */
   int32_t top_k;      /* k (1..K) */
   int32_t vocab;      /* LM-head rows, 0 when polestar_commit is not used */
