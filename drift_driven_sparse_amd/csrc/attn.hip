@@ -483,9 +483,12 @@ PS_DEV void block_sum2(float& x, float& y, float* red) {
 }
 
 // KL(softmax(s) || softmax(p)) of one row held PER values per thread across the workgroup,
-// from the logit differences: with u = exp(p - max p), dbar the u-weighted mean of s - p and
-// e = s - p - dbar, KL = E_u[e^e e] / E_u[e^e] - log E_u[e^e], formed with expm1/log1p so that
-// small drifts keep their relative precision.
+// from the logit differences: with a = p - max p, u = exp(a), dbar the u-weighted mean of s - p
+// and e = s - p - dbar, KL = E_u[e^e e] / E_u[e^e] - log E_u[e^e], formed with expm1/log1p so
+// that small drifts keep their relative precision.  The products u e^e are taken as exp(a + e),
+// which stays bounded by the spread of s where e alone overflows (positions that p makes very
+// unlikely and s does not); when even a + e exceeds 60 somewhere (a drift of tens of nats),
+// the sums are scaled by exp(-max(a + e)) and the logarithm is taken directly.
 template <int PER>
 PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
   float mp = -INFINITY;
@@ -504,18 +507,39 @@ PS_DEV float block_kl(const float* sv, const float* pv, int n, float* red) {
   }
   block_sum2(s0, sd, red);
   const float dbar = sd / s0;
+  float e[PER], ae[PER];
+  float c = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    e[i] = (sv[i] - pv[i]) - dbar;
+    ae[i] = (pv[i] - mp) + e[i];
+    if (threadIdx.x + 256 * i < n) c = fmaxf(c, ae[i]);
+  }
+  c = block_max_f(c, red);   // uniform over the workgroup
   float s1 = 0.f, s2 = 0.f;
+  if (c <= 60.f) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (threadIdx.x + 256 * i < n) {
+        const float w = expf(ae[i]);
+        s1 += e[i] < 80.f ? u[i] * expm1f(e[i]) : w - u[i];
+        s2 += w * e[i];
+      }
+    }
+    block_sum2(s1, s2, red);
+    const float r1 = s1 / s0;
+    return (s2 / s0) / (1.f + r1) - log1pf(r1);
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (threadIdx.x + 256 * i < n) {
-      const float e = (sv[i] - pv[i]) - dbar;
-      s1 += u[i] * expm1f(e);
-      s2 += u[i] * expf(e) * e;
+      const float w = expf(ae[i] - c);
+      s1 += w;
+      s2 += w * e[i];
     }
   }
   block_sum2(s1, s2, red);
-  const float r1 = s1 / s0;
-  return (s2 / s0) / (1.f + r1) - log1pf(r1);
+  return s2 / s1 - (c + logf(s1 / s0));
 }
 
 // One 256-thread workgroup per (staged row, head): KL against the previous logits (when

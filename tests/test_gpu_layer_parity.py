@@ -56,6 +56,8 @@ CASES = {
     # 188 rows per sequence: the widest row tiling of every kernel
     "rows188_K4_k2_B64": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, n_clusters=4,
                                        top_k=2, block=64, win_prefix=96, win_suffix=24), 1, {}),
+    # fewer window rows than clusters (n_Omega = 4 < K = 8): block entry and top-k over 4 clusters
+    "tiny_bf16_nwin4_K8": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=4, gen=32), 1, {"blk_start": 4}),
     # windows (1,1)B and (2,2)B of the window ablation
     "sweep_B32_w11": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=128, gen=256, win_prefix=32,
                                    win_suffix=32), 1, {}),
