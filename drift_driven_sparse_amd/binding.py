@@ -32,7 +32,7 @@ EXPORTED = [
     "polestar_drift", "polestar_refresh", "polestar_commit", "polestar_should_refresh",
     "polestar_nvfp4_pack", "polestar_nvfp4_unpack", "polestar_nvfp4_pack_host", "polestar_profile",
     "polestar_profile_read", "polestar_resid_bytes", "polestar_resid_pack", "polestar_resid_unpack",
-    "polestar_kv_staleness", "polestar_entry", "polestar_entry_commit", "polestar_step", "polestar_step_noalloc",
+    "polestar_kv_staleness", "polestar_attended_change", "polestar_entry", "polestar_entry_commit", "polestar_step", "polestar_step_noalloc",
 ]
 KERNELS = ["cluster", "prep", "qkv", "attn", "topk", "oproj", "oreduce", "gu", "down", "dreduce", "kvnext",
            "lmprep", "lmhead", "decide", "kl"]
@@ -111,6 +111,7 @@ def lib() -> C.CDLL:
         L.polestar_resid_pack.argtypes = [i32, vp, i64, i32, vp, vp, vp]
         L.polestar_resid_unpack.argtypes = [i32, vp, vp, i64, i32, vp, vp]
         L.polestar_kv_staleness.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.polestar_attended_change.argtypes = [vp, vp, i32, i32, C.c_int64, vp, vp, vp, vp, vp]
         L.polestar_profile.argtypes = [vp, C.c_int]
         L.polestar_profile_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32)]
         for name in EXPORTED:
@@ -270,6 +271,12 @@ def polestar_resid_pack(fmt, x, rows, d, codes, scales, stream=None) -> None:
 def polestar_resid_unpack(fmt, codes, scales, rows, d, x, stream=None) -> None:
     _ck(lib().polestar_resid_unpack(fmt, ptr(codes), ptr(scales), rows, d, ptr(x), stream_ptr(stream)),
         "polestar_resid_unpack")
+
+
+def polestar_attended_change(h: int, q, rows: int, q_ld: int, q_bstride: int, k_cache, k_ref, top_pos, score,
+                             stream=None) -> None:
+    _ck(lib().polestar_attended_change(h, ptr(q), rows, q_ld, q_bstride, ptr(k_cache), ptr(k_ref), ptr(top_pos),
+                                       ptr(score), stream_ptr(stream)), "polestar_attended_change")
 
 
 def polestar_kv_staleness(h: int, k_cache, v_cache, k_ref, v_ref, stale, stream=None) -> None:

@@ -1539,6 +1539,34 @@ int polestar_kv_staleness(const polestar_handle* h, const void* k_cache, const v
   return hip_status(h->dm.dtype == POLESTAR_BF16 ? launch_kv_staleness<bf16_t>(a, s) : launch_kv_staleness<float>(a, s));
 }
 
+int polestar_attended_change(const polestar_handle* h, const float* q, int32_t rows, int32_t q_ld,
+                             int64_t q_bstride, const void* k_cache, const void* k_ref, int32_t* top_pos,
+                             float* score, void* stream) {
+  if (!h) return POLESTAR_E_NULL;
+  if (rows < 0) return POLESTAR_E_SHAPE;
+  if (rows == 0) return POLESTAR_OK;
+  if (!q || !k_cache || !k_ref || !top_pos || !score) return POLESTAR_E_NULL;
+  const polestar_dims& d = h->dm;
+  if (q_ld < d.n_heads * d.head_dim || q_bstride < (int64_t)(rows - 1) * q_ld + d.n_heads * d.head_dim)
+    return POLESTAR_E_SHAPE;
+  AttendArgs a;
+  a.q = q;
+  a.q_bstride = q_bstride;
+  a.q_ld = q_ld;
+  a.rows = rows;
+  a.k = k_cache;
+  a.k_ref = k_ref;
+  a.batch = d.batch;
+  a.n_pos = d.n_pos;
+  a.hq = d.n_heads;
+  a.hkv = d.n_kv_heads;
+  a.dh = d.head_dim;
+  a.top = top_pos;
+  a.score = score;
+  const hipStream_t s = (hipStream_t)stream;
+  return hip_status(d.dtype == POLESTAR_BF16 ? launch_attended_change<bf16_t>(a, s) : launch_attended_change<float>(a, s));
+}
+
 int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales) {
   if (!x || !codes || !scales) return POLESTAR_E_NULL;
   if (rows < 0 || d <= 0 || d % 16) return POLESTAR_E_SHAPE;

@@ -376,6 +376,18 @@ struct StaleArgs {
 template <typename T>
 hipError_t launch_kv_staleness(const StaleArgs& a, hipStream_t s);
 
+// Most-attended-token policy (measurement): per query row, the key position with the largest
+// head-mean attention probability over the cache k, and 1 - mean over KV heads of the cosine
+// between that position's rows in k and k_ref.
+struct AttendArgs {
+  const float* q; int64_t q_bstride; int32_t q_ld, rows;   // q[b*q_bstride + r*q_ld + h*dh + e]
+  const void* k; const void* k_ref;                        // K cache layout, storage dtype
+  int32_t batch, n_pos, hq, hkv, dh;
+  int32_t* top; float* score;                              // [batch][rows]
+};
+template <typename T>
+hipError_t launch_attended_change(const AttendArgs& a, hipStream_t s);
+
 hipError_t launch_resid_pack(int fmt, const float* x, int64_t rows, int32_t d, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
 hipError_t launch_resid_unpack(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d, float* x,

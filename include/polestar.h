@@ -443,6 +443,21 @@ int polestar_nvfp4_pack_host(const float* x, int64_t rows, int32_t d, uint8_t* c
 int polestar_kv_staleness(const polestar_handle* h, const void* k_cache, const void* v_cache, const void* k_ref,
                           const void* v_ref, float* stale, void* stream);
 
+/* The most-attended-token cosine policy that the drift ablation of §5 ("Drift Measurement
+ * Policy", Fig. 6(a)) compares the KL drift with: for each query row r of each sequence (a
+ * candidate window position), its most-attended token j*(r), the position whose attention
+ * probability averaged over the query heads is largest when q_r attends over every position
+ * of k_cache (softmax(q.k/sqrt(dh)) per head; the lowest position on ties), and the cosine
+ * change of that token's keys, score = 1 - mean over KV heads of cos(k_cache[j*], k_ref[j*])
+ * (a zero row has cosine 0).  Positions are ranked for refresh by score.
+ * q: float32 [batch] x [rows] x [Hq dh] (element (b, r, c) at q[b q_bstride + r q_ld + c],
+ * device); k_cache, k_ref: K caches [batch, n_pos, Hkv, dh] in the storage dtype (device);
+ * top_pos: int32 [batch, rows] (device), score: float32 [batch, rows] (device).  float32
+ * arithmetic.  E_NULL, E_SHAPE (q_ld < Hq dh, q_bstride too small); measurement only. */
+int polestar_attended_change(const polestar_handle* h, const float* q, int32_t rows, int32_t q_ld,
+                             int64_t q_bstride, const void* k_cache, const void* k_ref, int32_t* top_pos,
+                             float* score, void* stream);
+
 /* ---- residual formats [App. C.3; Table 11 ablation] ------------------------ */
 /* Bytes per row of d values of format fmt: codes and scales (0 for RAW; FP8 has
  * no scales).  E_DTYPE for an unknown format, E_SHAPE when d is not a positive

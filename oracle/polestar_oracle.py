@@ -463,6 +463,31 @@ def top_fraction(scores: np.ndarray, frac: float) -> np.ndarray:
     return np.asarray(sorted(order[:m]), dtype=np.int64)
 
 
+def attended_token_change(q: np.ndarray, K_now: np.ndarray, K_ref: np.ndarray, hq: int, hkv: int):
+    """The most-attended-token cosine policy that the drift ablation compares with [§5
+    "Drift Measurement Policy", Fig. 6(a): each candidate position is ranked by the cosine
+    change of its most-attended token].
+
+    q [rows, hq, dh] are the candidate positions' queries, K_now [n, hkv, dh] the cache they
+    attend over, K_ref [n, hkv, dh] the keys it is compared with.  Reading: a position's
+    most-attended token j* is the argmax over positions of the attention probability averaged
+    over the query heads (query head h reads KV head h * hkv // hq; lowest position on ties), and
+    its change is 1 - the mean over KV heads of cos(K_now[j*], K_ref[j*]) (0 for a zero row).
+    Returns (j_star [rows], score [rows], A [rows, n] head-mean probabilities).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K_now, dtype=np.float64)
+    Kr = np.asarray(K_ref, dtype=np.float64)
+    dh = q.shape[-1]
+    g = (np.arange(hq) * hkv) // hq
+    logits = np.einsum("rhd,jhd->rhj", q, K[:, g, :]) / math.sqrt(dh)
+    p = np.exp(logits - logsumexp(logits)[..., None])
+    A = p.mean(axis=1)
+    j_star = np.argmax(A, axis=1)               # first maximum: the lowest position
+    score = 1.0 - np.mean(cosine(K[j_star], Kr[j_star]), axis=-1)
+    return j_star.astype(np.int64), score, A
+
+
 def selection_accuracy(chosen, stale: np.ndarray, frac: float = 0.25) -> float:
     """Share of the true top-frac most stale positions that a policy's choice contains."""
     truth = set(int(i) for i in top_fraction(stale, frac))

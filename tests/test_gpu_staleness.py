@@ -55,6 +55,72 @@ def test_kv_staleness_kernel_matches_oracle(dtype):
         dev.close()
 
 
+ATTEND_CASES = {
+    # name: (workload, batch, rows, q row stride padding)
+    "tiny_f32_gqa": (synth.shrink(synth.WORKLOADS[1], n_heads=4, n_kv_heads=2), 2, 40, 0),
+    "tiny_bf16_padded_rows": (synth.shrink(synth.WORKLOADS[1], dtype="bf16"), 1, 96, 64),
+    "llada_bf16_n1024": (synth.shrink(synth.WORKLOADS[3], n_layers=1), 1, 96, 0),
+    "dream_gqa_bf16": (synth.shrink(synth.WORKLOADS[4], n_layers=1), 1, 64, 0),
+    "tiny_bf16_n2048": (synth.shrink(synth.WORKLOADS[1], dtype="bf16", prompt=1024, gen=1024), 1, 48, 0),
+}
+
+
+@pytest.mark.parametrize("case", list(ATTEND_CASES))
+def test_attended_change_kernel_matches_oracle(case):
+    """Most-attended token and its cosine change: the token exact where the oracle's head-mean
+    probabilities separate the top two positions by more than 1e-5 of the largest (else the
+    GPU's token must be one of the near-maximal ones), the score within 2e-3 of the oracle's
+    score of the GPU's token (floor 1e-4)."""
+    w, batch, rows, pad = ATTEND_CASES[case]
+    n, hq, hkv, dh = w.n_pos, w.n_heads, w.n_kv_heads, w.head_dim
+    log(f"[attended] case={case} n={n} heads={hq}/{hkv} dh={dh} rows={rows} batch={batch} dtype={w.dtype}")
+    dev = Dev(w, batch=batch, vocab=0)
+    try:
+        q_ld = hq * dh + pad
+        q = synth.tensor(w, (80, 1), (batch, rows, q_ld), 1.0, 0, "cuda", "f32")
+        k = synth.tensor(w, (80, 2), (batch, n, hkv, dh), 1.0, 0, "cuda", w.dtype)
+        # reference keys: unchanged, scaled, perturbed and fresh rows
+        kr = k.clone()
+        pert = synth.tensor(w, (80, 3), (batch, n, hkv, dh), 1.0, 0, "cuda", "f32")
+        sel = torch.arange(n, device="cuda") % 4
+        kr[:, sel == 1] = (k[:, sel == 1].float() * 2.0).to(k.dtype)
+        kr[:, sel == 2] = (k[:, sel == 2].float() + 0.3 * pert[:, sel == 2]).to(k.dtype)
+        kr[:, sel == 3] = pert[:, sel == 3].to(k.dtype)
+        # a few queries aimed at chosen keys, so that some rows have a dominant token
+        for b in range(batch):
+            for r in range(0, rows, 5):
+                j = int(synth.hash32_int(w.seed(0) + 13 * b + r) % n)
+                for h in range(hq):
+                    q[b, r, h * dh:(h + 1) * dh] = 3.0 * k[b, j, (h * hkv) // hq].float()
+        top = torch.zeros(batch, rows, dtype=torch.int32, device="cuda")
+        score = torch.zeros(batch, rows, dtype=torch.float32, device="cuda")
+        B.polestar_attended_change(dev.h, q, rows, q_ld, rows * q_ld, k, kr, top, score)
+        torch.cuda.synchronize()
+        near = 0
+        for b in range(batch):
+            qo = np64(q[b, :, : hq * dh]).reshape(rows, hq, dh)
+            ko, kro = np64(k[b]), np64(kr[b])
+            j_or, s_or, A = O.attended_token_change(qo, ko, kro, hq, hkv)
+            jg = top[b].cpu().numpy()
+            sg = score[b].cpu().numpy()
+            amax = A.max(axis=1)
+            srt = np.sort(A, axis=1)
+            gap = srt[:, -1] - srt[:, -2]
+            sep = gap > 1e-5 * amax
+            assert np.array_equal(jg[sep], j_or[sep]), f"seq {b}: most-attended tokens differ"
+            ok = A[np.arange(rows), jg] >= amax - 1e-5 * amax
+            assert ok.all(), f"seq {b}: GPU token not among the near-maximal positions"
+            near += int((~sep).sum())
+            s_at = 1.0 - np.mean(O.cosine(ko[jg], kro[jg]), axis=-1)   # oracle score of the GPU's token
+            err = np.abs(sg - s_at) / np.maximum(np.abs(s_at), 1e-4)
+            assert err.max() <= 2e-3, f"seq {b}: score rel err {err.max():.2e}"
+            log(f"    seq {b}: {int(sep.sum())} rows with a separated maximum, scores in "
+                f"[{sg.min():.3f}, {sg.max():.3f}], max rel err {err.max():.2e}")
+        log(f"[attended] case={case} passed ({near} near-tied rows checked as valid choices)")
+    finally:
+        dev.close()
+
+
 def test_staleness_and_selection_accuracy_of_the_drift_policy():
     w = synth.shrink(synth.WORKLOADS[1], dtype="bf16", top_k=2)     # k/K = 1/4: the page's top quarter
     n_layers, steps = 2, 6

@@ -850,3 +850,68 @@ def test_proxy_drift_over_the_active_block_keys():
     P2[..., out] = rng.normal(size=P2[..., out].shape)
     assert np.array_equal(O.proxy_drift(zq, K2, V2, P2, act, blk)[1], kl)
     assert not np.allclose(O.proxy_drift(zq, K2, V2, P2, full, blk)[1], O.proxy_drift(zq, Kc, Vc, P_prev, full, blk)[1])
+
+
+# ---- most-attended-token cosine policy [§5 "Drift Measurement Policy", Fig. 6(a)] ----------
+
+def test_attended_token_change_planted_tokens_and_scores():
+    """Queries aligned with one key recover that key as the most-attended token; the score is
+    0 for an unchanged or rescaled key, 2 for a negated one, 1 for an orthogonal or zero one."""
+    rng = np.random.default_rng(11)
+    n, hq, hkv, dh = 7, 4, 2, 8
+    K = rng.normal(size=(n, hkv, dh))
+    targets = [2, 5, 0, 6, 3]
+    q = np.zeros((len(targets), hq, dh))
+    for r, j in enumerate(targets):
+        for h in range(hq):
+            q[r, h] = 40.0 * K[j, (h * hkv) // hq]
+    Kref = K.copy()
+    Kref[5] = -K[5]                       # negated: cos -1
+    Kref[0] = 3.0 * K[0]                  # rescaled: cos 1
+    e = np.zeros(dh)
+    e[0] = 1.0
+    Kref[6, 0] = e * np.linalg.norm(K[6, 0])
+    Kref[6, 0] -= np.dot(Kref[6, 0], K[6, 0]) / np.dot(K[6, 0], K[6, 0]) * K[6, 0]   # orthogonal in head 0
+    Kref[6, 1] = 0.0                      # zero row in head 1: cosine 0
+    Kref[3] = -K[3]
+    Kref[3, 1] = K[3, 1]                  # head 0 negated, head 1 unchanged: mean cos 0
+    j, s, A = O.attended_token_change(q, K, Kref, hq, hkv)
+    assert j.tolist() == targets
+    assert np.allclose(A.sum(axis=1), 1.0)
+    assert s[0] == pytest.approx(0.0, abs=1e-12)          # position 2 unchanged
+    assert s[1] == pytest.approx(2.0, abs=1e-12)          # position 5 negated
+    assert s[2] == pytest.approx(0.0, abs=1e-12)          # position 0 rescaled
+    assert s[3] == pytest.approx(1.0, abs=1e-12)          # position 6: cos 0 and 0
+    assert s[4] == pytest.approx(1.0, abs=1e-12)          # position 3: cos -1 and 1
+
+
+def test_attended_token_change_ties_and_head_map():
+    """Equal keys at two positions tie exactly and the lower position wins; all-zero keys give a
+    uniform distribution (position 0); the query head -> KV head map is h * hkv // hq (grouped)."""
+    rng = np.random.default_rng(12)
+    n, hq, hkv, dh = 6, 4, 2, 4
+    K = rng.normal(size=(n, hkv, dh)) * 0.01
+    K[1] = rng.normal(size=(hkv, dh))
+    K[4] = K[1]
+    q = np.zeros((1, hq, dh))
+    for h in range(hq):
+        q[0, h] = 30.0 * K[1, (h * hkv) // hq] / np.linalg.norm(K[1, (h * hkv) // hq]) ** 2
+    j, _, A = O.attended_token_change(q, K, K, hq, hkv)
+    assert A[0, 1] == A[0, 4] and j[0] == 1
+    j0, _, A0 = O.attended_token_change(q, np.zeros_like(K), K, hq, hkv)
+    assert np.allclose(A0, 1.0 / n) and j0[0] == 0
+    # grouped map: heads 0, 1 read KV head 0 (which points at position 2), heads 2, 3 read KV
+    # head 1 (position 3, weaker); an interleaved map (h % hkv) would pair differently
+    K = np.zeros((n, hkv, dh))
+    K[2, 0, 0] = 1.0
+    K[3, 1, 1] = 1.0
+    q = np.zeros((1, hq, dh))
+    q[0, 0, 0] = q[0, 1, 0] = 20.0        # heads 0, 1: strongly on position 2 through KV head 0
+    q[0, 2, 1] = q[0, 3, 1] = 2.0         # heads 2, 3: weakly on position 3 through KV head 1
+    j, _, A = O.attended_token_change(q, K, K, hq, hkv)
+    assert j[0] == 2 and A[0, 2] > 0.49
+    # the interleaved reading: heads 0 and 2 on KV head 0, heads 1 and 3 on KV head 1
+    qi = q.copy()
+    qi[0, 1], qi[0, 2] = q[0, 2], q[0, 1]
+    ji, _, Ai = O.attended_token_change(qi, K, K, hq, hkv)
+    assert not np.allclose(Ai, A)
