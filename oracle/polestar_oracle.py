@@ -631,7 +631,7 @@ def drift_layer(ls: Dict, W: Dict, cfg: Cfg, blk_start: int, h_act: np.ndarray, 
         K[wpos[rows]] = kr[cfg.B + rows]
         V[wpos[rows]] = vr[cfg.B + rows]
     out, logits = attention(q, K, V, hq, hkv)
-    res = {"o": out.reshape(out.shape[0], hq * dh),
+    res = {"o": out.reshape(out.shape[0], hq * dh), "q": q,
            "act_logits": round_f32(logits[: cfg.B])}
     if commit_prev is not None:
         res["delta"] = head_summed_drift(logits[: cfg.B], commit_prev)

@@ -1,16 +1,12 @@
-"""KV-cache staleness on the GPU [App. C.2 of the Polestar page] and the
-selection-accuracy measurement of §3 / Fig. 6(a).
+"""KV-cache staleness on the GPU [App. C.2 of the Polestar page] and the selection-accuracy
+measurement of the drift ablation (§5 "Drift Measurement Policy", Fig. 6(a)).
 
-1. The staleness kernel against the oracle's E_i on random caches with fresh,
-   opposite and zero rows.
-2. A free-running bf16 trajectory (oracle block entry, then GPU steps): at every
-   refresh step and layer, right after the drift call picked S, the caches are
-   compared with a full recompute of the current sequence (the oracle's dense
-   forward): E_i of every position from the GPU kernel (checked against the
-   oracle), and the share of the true top-quarter most stale window positions
-   that S contains, beside a random choice of the same size.  With synthetic
-   weights the numbers say nothing about trained models; the test checks the
-   measurement and reports it.
+1. The staleness kernel against the oracle's E_i on random caches with fresh, opposite and
+   zero rows.
+2. The most-attended-token cosine policy kernel against the oracle on seeded queries and caches.
+3. One trajectory on which the KL drift policy, the most-attended-token cosine policy and a
+   random choice are scored against the true top quarter of stale window positions, at the
+   same refresh budget, from the GPU's values and the oracle's side by side.
 """
 from __future__ import annotations
 
@@ -21,7 +17,9 @@ import torch
 import synth
 from drift_driven_sparse_amd import binding as B
 from oracle import polestar_oracle as O
-from tests.harness import Dev, layer_struct, log, np64, packed_layer, packet, to_dev, weights
+from tests import flips as FL
+from tests.harness import (Dev, assert_close, assert_stored, check_topk, layer_struct, log, np64, packed_layer, packet,
+                           to_dev, weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,19 +119,45 @@ def test_attended_change_kernel_matches_oracle(case):
         dev.close()
 
 
-def test_staleness_and_selection_accuracy_of_the_drift_policy():
-    w = synth.shrink(synth.WORKLOADS[1], dtype="bf16", top_k=2)     # k/K = 1/4: the page's top quarter
-    n_layers, steps = 2, 6
-    log(f"[staleness] trajectory d={w.d} n={w.n_pos} layers={n_layers} steps={steps} K={w.n_clusters} k={w.top_k}")
+def _top_budget(scores, m):
+    """Indices of the m largest scores (lower index first on equal scores), ascending."""
+    order = sorted(range(len(scores)), key=lambda i: (-float(scores[i]), i))
+    return np.asarray(sorted(order[:m]), dtype=np.int64)
+
+
+def _boundary_gap(scores, m):
+    """Gap between the m-th and (m+1)-th largest score (inf when m covers every score)."""
+    v = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
+    return float(v[m - 1] - v[m]) if 0 < m < len(v) else np.inf
+
+
+def test_selection_accuracy_of_three_policies():
+    """Selection accuracy of the KL drift policy, the most-attended-token cosine policy and a
+    random choice, on one trajectory with the same refresh budget per (step, layer): |S|, the
+    rows the drift policy selects (k/K = 1/4 of the clusters, the page's top quarter).  Truth:
+    the top quarter of window positions by staleness E_i against a full recompute of the
+    current sequence.
+
+    Both sides run the same trajectory: every call starts from the oracle's state, the GPU's
+    selection S must equal the oracle's (near-ties reported, then the oracle's S is used), the
+    GPU's E_i and policy scores are taken on the oracle's caches and queries and must match the
+    oracle's, and the accuracies are computed from the GPU's values and the oracle's and
+    reported side by side.  With synthetic weights the numbers say nothing about trained
+    models; the test checks the measurement and reports it."""
+    w = synth.shrink(synth.WORKLOADS[1], dtype="bf16", top_k=2)
+    n_layers, steps = 3, 6
+    log(f"[policies] trajectory d={w.d} n={w.n_pos} layers={n_layers} steps={steps} K={w.n_clusters} k={w.top_k}")
     dev = Dev(w, batch=1, vocab=0)
     cfg = O.Cfg.from_workload(w, top_k=w.top_k)
     st = cfg.st
-    n, d, Bk, K = w.n_pos, w.d, w.block, w.n_clusters
-    blk_start = w.prompt
-    wpos = np.asarray(O.window_positions(blk_start, n, Bk, w.win_prefix, w.win_suffix))
+    n, d, Bk, K, hq, hkv, dh = w.n_pos, w.d, w.block, w.n_clusters, w.n_heads, w.n_kv_heads, w.head_dim
+    blk = w.prompt
+    wpos = np.asarray(O.window_positions(blk, n, Bk, w.win_prefix, w.win_suffix))
     nw, WM = len(wpos), dev.win_max
+    keff = min(K, nw)
     rng = np.random.default_rng(5)
-    acc_kl, acc_rand = [], []
+    acc = {k: [] for k in ("kl", "cos", "rand", "kl_or", "cos_or")}
+    ties, fresh, ambiguous = 0, 0, 0
     try:
         Wd = [weights(w, l) for l in range(n_layers)]
         Wo = [{k_: np64(v_) for k_, v_ in W.items()} for W in Wd]
@@ -141,23 +165,29 @@ def test_staleness_and_selection_accuracy_of_the_drift_policy():
         del Wd
         h0 = st(np64(synth.embeddings(w)))
         Hs, Ks, Vs, _ = O.full_forward(h0, Wo, cfg)
-        L, Ls = [], []
+        OL, L, Ls = [], [], []
         for l in range(n_layers):
-            ls = O.block_entry_layer_state(Hs[l], Ks[l], Vs[l], Wo[l]["wq"], cfg, blk_start,
-                                           synth.kmeans_init(w, nw, l, 0))
+            ls = O.block_entry_layer_state(Hs[l], Ks[l], Vs[l], Wo[l]["wq"], cfg, blk, synth.kmeans_init(w, nw, l, 0))
+            OL.append(ls)
             Ld = dict(P[l])
-            Ld["k_cache"] = to_dev(ls["K"], w.dtype)[None].contiguous()
-            Ld["v_cache"] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)[None].contiguous()
-            Ld["win_z"] = to_dev(ls["Z"], w.dtype)[None].contiguous()
-            m = torch.zeros(1, WM, dtype=torch.int32, device="cuda")
-            m[0, :nw] = torch.tensor(ls["M"], dtype=torch.int32)
-            Ld["win_m"] = m
-            Ld["proxy_logits"] = torch.tensor(ls["P"], dtype=torch.float32, device="cuda")[None].contiguous()
-            hw = dev.zeros(1, WM, d)
-            hw[0, :nw] = to_dev(ls["H"], w.dtype)
-            Ld["win_h"] = hw
+            Ld["k_cache"] = dev.zeros(1, n, hkv, dh)
+            Ld["v_cache"] = dev.zeros(1, hkv, dh, n)
+            Ld["win_z"] = dev.zeros(1, K, d)
+            Ld["win_m"] = torch.zeros(1, WM, dtype=torch.int32, device="cuda")
+            Ld["proxy_logits"] = torch.zeros(1, K, hq, n, dtype=torch.float32, device="cuda")
+            Ld["win_h"] = dev.zeros(1, WM, d)
             L.append(Ld)
             Ls.append(layer_struct(Ld))
+
+        def sync(l):   # the GPU layer state := the oracle's
+            ls, Ld = OL[l], L[l]
+            Ld["k_cache"][0] = to_dev(ls["K"], w.dtype)
+            Ld["v_cache"][0] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)
+            Ld["win_z"][0] = to_dev(ls["Z"], w.dtype)
+            Ld["win_m"][0, :nw] = torch.tensor(ls["M"], dtype=torch.int32)
+            Ld["proxy_logits"][0] = torch.tensor(ls["P"], dtype=torch.float32)
+            Ld["win_h"][0, :nw] = to_dev(ls["H"], w.dtype)
+
         h_act = [dev.zeros(1, Bk, d) for _ in range(2)]
         pk_rows = [dev.zeros(1, WM, d) for _ in range(2)]
         pk_idx = [torch.zeros(1, WM, dtype=torch.int32, device="cuda") for _ in range(2)]
@@ -166,46 +196,108 @@ def test_staleness_and_selection_accuracy_of_the_drift_policy():
         D = torch.zeros(1, K, dtype=torch.float32, device="cuda")
         topk = torch.zeros(1, w.top_k, dtype=torch.int32, device="cuda")
         E = torch.zeros(1, n, dtype=torch.float32, device="cuda")
+        top = torch.zeros(1, nw, dtype=torch.int32, device="cuda")
+        score = torch.zeros(1, nw, dtype=torch.float32, device="cuda")
         for t in range(steps):
             noise = np64(synth.tensor(w, (77, t), (Bk, d), np.sqrt(w.noise_var)))
-            x = st(h0[blk_start: blk_start + Bk] + noise)
-            h_act[0][0] = to_dev(x, w.dtype)
-            # the full recompute of the current sequence: the entry inputs with this step's block
+            x = st(h0[blk: blk + Bk] + noise)
             hcur = h0.copy()
-            hcur[blk_start: blk_start + Bk] = x
-            _, Kr, Vr, _ = O.full_forward(hcur, Wo, cfg)
-            cur, pk, u_in = 0, 0, None
+            hcur[blk: blk + Bk] = x
+            _, Kr, Vr, _ = O.full_forward(hcur, Wo, cfg)     # the full recompute of the current sequence
+            h_act[0][0] = to_dev(x, w.dtype)
+            cur, pk, u_in, U_prev, S_prev = 0, 0, None, None, None
             for l in range(n_layers):
-                B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls[l], blk_start, u_in, None, None, None, dev.ws,
-                                   dev.ws_bytes)
+                tag = f"step {t} layer {l}"
+                sync(l)
+                ls = OL[l]
+                B.polestar_cluster(dev.h, B.CLUSTER_UPDATE, Ls[l], blk, u_in, None, None, None, dev.ws, dev.ws_bytes)
                 sel = pks[pk]
-                B.polestar_drift(dev.h, B.DRIFT_REFRESH, Ls[l], blk_start, h_act[cur], u_in, D, topk, sel, None,
-                                 None, dev.ws, dev.ws_bytes)
-                # staleness of this layer's cache at the moment S is chosen
+                B.polestar_drift(dev.h, B.DRIFT_REFRESH, Ls[l], blk, h_act[cur], u_in, D, topk, sel, None, None,
+                                 dev.ws, dev.ws_bytes)
+                torch.cuda.synchronize()
+                cu = O.cluster_update(ls, cfg, U_prev, S_prev)
+                K_before = ls["K"].copy()
+                P_before = ls["P"].copy()
+                dr = O.drift_layer(ls, Wo[l], cfg, blk, x, cu["h"], cu["patched"], True)
+                al = FL.drift_call_allow(O, cfg, Wo[l], blk, x, cu["h"], cu["patched"], ls["Z"], ls["K"], ls["V"],
+                                         dr["proxy_q"], dr["proxy_keys"], P_before)
+                S = dr["S"]
+                Dg = D[0].cpu().numpy()
+                assert_close(Dg, dr["D"], f"{tag}: cluster drift D", allow=al["D"])
+                if not check_topk(topk[0].cpu().numpy(), Dg, dr["D"], dr["topk"], w.top_k, keff, tag, D_allow=al["D"]):
+                    ties += 1
+                    pk_idx[pk][0, : len(S)] = torch.tensor(S, dtype=torch.int32)
+                    pk_cnt[pk][0] = len(S)
+                cnt = int(pk_cnt[pk][0])
+                S_gpu = pk_idx[pk][0, :cnt].cpu().numpy()
+                assert np.array_equal(S_gpu, S), f"{tag}: rows S differ"
+                # measurements on the oracle's caches and queries (both sides on identical inputs)
+                kb = to_dev(K_before, w.dtype)[None].contiguous()
+                L[l]["k_cache"][0] = to_dev(ls["K"], w.dtype)
+                L[l]["v_cache"][0] = to_dev(ls["V"], w.dtype).permute(1, 2, 0)
                 kr = to_dev(Kr[l], w.dtype)[None].contiguous()
                 vr = to_dev(Vr[l], w.dtype).permute(1, 2, 0)[None].contiguous()
                 B.polestar_kv_staleness(dev.h, L[l]["k_cache"], L[l]["v_cache"], kr, vr, E)
+                qw = torch.tensor(dr["q"][Bk:].reshape(nw, hq * dh), dtype=torch.float32, device="cuda")[None].contiguous()
+                B.polestar_attended_change(dev.h, qw, nw, hq * dh, nw * hq * dh, L[l]["k_cache"], kb, top, score)
                 torch.cuda.synchronize()
+                Kc, Vc = np64(L[l]["k_cache"][0]), np64(L[l]["v_cache"][0].permute(2, 0, 1))
+                e_or = O.kv_staleness(Kc, Vc, np64(kr[0]), np64(vr[0].permute(2, 0, 1)))
                 e = E[0].cpu().numpy()
-                ref = O.kv_staleness(np64(L[l]["k_cache"][0]), np64(L[l]["v_cache"][0].permute(2, 0, 1)),
-                                     np64(kr[0]), np64(vr[0].permute(2, 0, 1)))
-                assert np.max(np.abs(e - ref)) < 1e-5
-                assert np.all(np.isfinite(e)) and e.min() > -1e-5 and e.max() < 2 + 1e-5
-                cnt = int(pk_cnt[pk][0])
-                S = pk_idx[pk][0, :cnt].cpu().numpy()
-                ew = e[wpos]
-                if cnt:
-                    acc_kl.append(O.selection_accuracy(S, ew))
-                    acc_rand.append(O.selection_accuracy(rng.choice(nw, size=cnt, replace=False), ew))
-                log(f"    step {t} layer {l}: |S| = {cnt}, window E mean {ew.mean():.4f} max {ew.max():.4f}, "
-                    f"drift-policy accuracy {acc_kl[-1] if cnt else float('nan'):.2f}")
-                B.polestar_refresh(dev.h, Ls[l], blk_start, h_act[cur], sel, None, None, None, h_act[1 - cur],
-                                   pk_rows[pk], dev.ws, dev.ws_bytes)
-                u_in = sel
+                e_err = float(np.max(np.abs(e - e_or)))
+                assert e_err < 1e-6, f"{tag}: staleness E_i differs by {e_err:.2e}"
+                j_or, s_or, A = O.attended_token_change(dr["q"][Bk:], Kc, np64(kb[0]), hq, hkv)
+                jg, sg = top[0].cpu().numpy(), score[0].cpu().numpy()
+                srt = np.sort(A, axis=1)
+                sep = srt[:, -1] - srt[:, -2] > 1e-5 * srt[:, -1]
+                assert np.array_equal(jg[sep], j_or[sep]), f"{tag}: most-attended tokens differ"
+                assert np.all(A[np.arange(nw), jg] >= srt[:, -1] * (1 - 1e-5)), f"{tag}: GPU token not near-maximal"
+                s_at = 1.0 - np.mean(O.cosine(Kc[jg], np64(kb[0])[jg]), axis=-1)
+                assert np.all(np.abs(sg - s_at) <= 2e-3 * np.maximum(np.abs(s_at), 1e-4)), f"{tag}: policy scores"
+                # the three policies at the drift policy's budget |S|; points whose window holds no
+                # stale row (E = 0 everywhere: layer 0's window rows are the unchanged inputs) rank
+                # nothing and are left out
+                ew, ew_or = e[wpos], e_or[wpos]
+                if cnt and ew_or.max() > 1e-9:
+                    a = (O.selection_accuracy(S_gpu, ew), O.selection_accuracy(_top_budget(sg, cnt), ew),
+                         O.selection_accuracy(rng.choice(nw, size=cnt, replace=False), ew),
+                         O.selection_accuracy(S, ew_or), O.selection_accuracy(_top_budget(s_or, cnt), ew_or))
+                    for k_, v_ in zip(("kl", "cos", "rand", "kl_or", "cos_or"), a):
+                        acc[k_].append(v_)
+                    # both sides rank the same positions, except across a boundary closer than their
+                    # values' agreement (E within 1e-6, scores within 2e-3)
+                    m_true = int(np.ceil(0.25 * nw))
+                    same_truth = np.array_equal(O.top_fraction(ew, 0.25), O.top_fraction(ew_or, 0.25))
+                    same_cos = np.array_equal(_top_budget(sg, cnt), _top_budget(s_or, cnt))
+                    assert same_truth or _boundary_gap(ew_or, m_true) <= 2e-6, f"{tag}: stale top quarter differs"
+                    assert same_cos or _boundary_gap(s_or, cnt) <= 4e-3 * float(np.max(np.abs(s_or))), \
+                        f"{tag}: attended-cosine selection differs"
+                    if same_truth and same_cos:
+                        assert a[0] == a[3] and a[1] == a[4]
+                    else:
+                        ambiguous += 1
+                    log(f"    {tag}: |S| = {cnt}, window E mean {ew.mean():.2e} max {ew.max():.2e}; accuracy KL "
+                        f"{a[0]:.2f} (oracle {a[3]:.2f}), attended-cosine {a[1]:.2f} (oracle {a[4]:.2f}), random "
+                        f"{a[2]:.2f}")
+                elif cnt:
+                    fresh += 1
+                # sparse forward, then both sides continue from the oracle's outputs
+                B.polestar_refresh(dev.h, Ls[l], blk, h_act[cur], sel, None, None, None, h_act[1 - cur], pk_rows[pk],
+                                   dev.ws, dev.ws_bytes)
+                torch.cuda.synchronize()
+                rf = O.refresh_layer(Wo[l], cfg, x, cu["h"], dr["o"], S)
+                assert_stored(np64(pk_rows[pk][0, : len(S)]), rf["U"], w.dtype, f"{tag}: update packet U")
+                assert_stored(np64(h_act[1 - cur][0]), rf["h_act_out"], w.dtype, f"{tag}: active outputs")
+                pk_rows[pk][0, : len(S)] = to_dev(rf["U"], w.dtype)
+                h_act[1 - cur][0] = to_dev(rf["h_act_out"], w.dtype)
+                x = rf["h_act_out"]
+                u_in, U_prev, S_prev = pks[pk], rf["U"], S
                 cur, pk = 1 - cur, 1 - pk
-        torch.cuda.synchronize()
-        assert acc_kl, "no refresh selected any row"
-        log(f"[staleness] top-quarter selection accuracy over {len(acc_kl)} (step, layer) points: "
-            f"KL drift {np.mean(acc_kl):.3f}, random {np.mean(acc_rand):.3f}")
+        assert acc["kl"], "no point with stale window rows"
+        log(f"[policies] top-quarter selection accuracy over {len(acc['kl'])} (step, layer) points at the drift "
+            f"policy's budget: KL drift {np.mean(acc['kl']):.3f} (oracle {np.mean(acc['kl_or']):.3f}), "
+            f"most-attended-token cosine {np.mean(acc['cos']):.3f} (oracle {np.mean(acc['cos_or']):.3f}), random "
+            f"{np.mean(acc['rand']):.3f}; {fresh} points without stale rows left out, {ambiguous} points with a "
+            f"ranking boundary inside the value agreement, {ties} top-k near-ties")
     finally:
         dev.close()
