@@ -96,8 +96,9 @@ void layout(polestar_handle* h) {
     w.lm_a = take(Bt * lm_rows * d.d * T);
     w.lm_stats = take(Bt * lm_rows * (size_t)h->lm_tiles * 4 * 4);
     w.lm_meta = take(Bt * 2 * 4);
+    w.lm_conf = take(Bt * lm_rows * 8);
   } else {
-    w.lm_a = w.lm_stats = w.lm_meta = 0;
+    w.lm_a = w.lm_stats = w.lm_meta = w.lm_conf = 0;
   }
   w.q_all = take(Bt * d.n_pos * (size_t)h->nq * 4);   // block entry: queries of every position
   w.qmap = take(Bt * (h->win_max + 1) * 4);           // query cache: staged window rows, count
@@ -1019,6 +1020,8 @@ int do_commit(polestar_handle* h, int32_t blk_start, const void* w_lm, const voi
   da.tau_suf = h->pr.tau_suf;
   da.alpha = h->pr.alpha;
   da.lm_stats = ep.lm_stats;
+  da.lm_conf = at<float>(ws, h->ws.lm_conf);
+  da.lm_yhat = (int32_t*)(da.lm_conf + (size_t)d.batch * lm_rows);
   da.meta = lp.meta;
   da.u_idx = lp.u_idx;
   da.delta = delta;

@@ -40,30 +40,70 @@ __global__ __launch_bounds__(256) void lm_prep_kernel(LmPrepArgs a, int32_t* met
   rmsnorm_row<T>(src, d, a.eps, red, [&](int n, const float* x) { Quad<T>::store(dst + n, x); });
 }
 
-// Combine per-tile (max, sum exp, best non-mask logit, its id) in tile order.
-PS_DEV void combine_stats(const float* st, int tiles, float* conf, int* yhat) {
-  float M = -INFINITY;
-  for (int t = 0; t < tiles; ++t) M = fmaxf(M, st[t * 4 + 0]);
-  float Z = 0.f, best = -INFINITY;
+// Confidence and argmax of one staged row from the LM head's per-tile statistics (max, sum of
+// exp(logit - max), best non-mask logit, its id): one workgroup per (row, sequence), thread t
+// combines tiles t, t + 256, ... in order, then the threads' partials are combined in thread
+// order (the maximum first, then the rescaled sums; the best logit with the lowest id on ties).
+__global__ __launch_bounds__(256) void lm_conf_kernel(DecideArgs a, const int32_t* meta_rows) {
+  __shared__ float rm[4], rz[4], rb[4];
+  __shared__ int ri[4];
+  const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (r >= meta_rows[b]) return;   // uniform: rows staged for this sequence
+  const float* st = a.lm_stats + ((int64_t)b * a.lm_rows + r) * a.lm_tiles * 4;
+  float m = -INFINITY;
+  for (int t = tid; t < a.lm_tiles; t += 256) m = fmaxf(m, st[t * 4 + 0]);
+  m = wave_max(m);
+  if (lane == 0) rm[wid] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  float z = 0.f, best = -INFINITY;
   int bid = -1;
-  for (int t = 0; t < tiles; ++t) {
-    Z += st[t * 4 + 1] * expf(st[t * 4 + 0] - M);
-    if (st[t * 4 + 2] > best) {
-      best = st[t * 4 + 2];
-      bid = __float_as_int(st[t * 4 + 3]);
+  for (int t = tid; t < a.lm_tiles; t += 256) {
+    const float4 v = *(const float4*)(st + t * 4);
+    z += v.y * expf(v.x - M);
+    if (v.z > best) {   // tiles ascend: the first maximum has the lowest id
+      best = v.z;
+      bid = __float_as_int(v.w);
     }
   }
-  *conf = expf(best - M) / Z;
-  *yhat = bid;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    z += __shfl_xor(z, o, 64);
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bid, o, 64);
+    if (ob > best || (ob == best && oi >= 0 && (bid < 0 || oi < bid))) {
+      best = ob;
+      bid = oi;
+    }
+  }
+  if (lane == 0) {
+    rz[wid] = z;
+    rb[wid] = best;
+    ri[wid] = bid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Z = 0.f, B = -INFINITY;
+    int I = -1;
+    for (int w = 0; w < 4; ++w) {
+      Z += rz[w];
+      if (rb[w] > B || (rb[w] == B && ri[w] >= 0 && (I < 0 || ri[w] < I))) {
+        B = rb[w];
+        I = ri[w];
+      }
+    }
+    const int64_t o = (int64_t)b * a.lm_rows + r;
+    a.lm_conf[o] = expf(B - M) / Z;
+    a.lm_yhat[o] = I;
+  }
 }
 
 __global__ __launch_bounds__(64) void decide_kernel(DecideArgs a, const int32_t* meta_rows, const int32_t* meta_p0) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int H = a.hist > 0 ? a.hist : 1;
   for (int j = lane; j < a.block; j += 64) {
-    float c;
-    int y;
-    combine_stats(a.lm_stats + ((int64_t)b * a.lm_rows + j) * a.lm_tiles * 4, a.lm_tiles, &c, &y);
+    const float c = a.lm_conf[(int64_t)b * a.lm_rows + j];
+    const int y = a.lm_yhat[(int64_t)b * a.lm_rows + j];
     const int64_t row = (int64_t)b * a.block + j;
     if (a.entry) {   // no drift at block entry: the confidence alone decides
       a.commit_active[row] = (a.active_masked[row] != 0 && c >= a.tau_s) ? 1 : 0;
@@ -105,9 +145,7 @@ __global__ __launch_bounds__(64) void decide_kernel(DecideArgs a, const int32_t*
   __syncthreads();
   const int nsuf = meta_rows[b] - a.block, p0 = meta_p0[b];
   for (int i = lane; i < nsuf; i += 64) {
-    float c;
-    int y;
-    combine_stats(a.lm_stats + ((int64_t)b * a.lm_rows + a.block + i) * a.lm_tiles * 4, a.lm_tiles, &c, &y);
+    const float c = a.lm_conf[(int64_t)b * a.lm_rows + a.block + i];
     const int slot = a.entry ? i : a.u_idx[(int64_t)b * a.win_max + p0 + i] - a.n_pre;
     if (slot < 0 || slot >= a.win_suffix) continue;
     const int64_t o = (int64_t)b * a.win_suffix + slot;
@@ -127,6 +165,7 @@ hipError_t launch_lm_prep(const LmPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decide(const DecideArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(lm_conf_kernel, dim3(a.lm_rows, a.batch), dim3(256), 0, s, a, a.meta);
   hipLaunchKernelGGL(decide_kernel, dim3(a.batch), dim3(64), 0, s, a, a.meta, a.meta + a.batch);
   return hipGetLastError();
 }

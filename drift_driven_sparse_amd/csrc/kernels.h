@@ -5,7 +5,7 @@
 // Handle contents (host only).
 struct WsLayout {
   size_t win_rows, flags, a_qkv, q, o, kl, akl, lg, part, hp, a_gu, act, a_kv, xhat, z64, wstat, attn_part, lm_a,
-      lm_stats, lm_meta, q_all, qmap, km_lab, km_cnt, km_sum, total;
+      lm_stats, lm_meta, lm_conf, q_all, qmap, km_lab, km_cnt, km_sum, total;
 };
 
 struct ProfState;   // per-kernel event records (api.hip)
@@ -356,6 +356,7 @@ struct DecideArgs {
   int32_t batch, block, win_suffix, win_max, n_pre, lm_rows, lm_tiles, hist, mask_id;
   float tau_s, tau_suf, alpha;
   const float* lm_stats; const int32_t* meta; const int32_t* u_idx;
+  float* lm_conf; int32_t* lm_yhat;   // [batch][lm_rows] confidence and argmax of each staged row
   const float* delta; const uint8_t* active_masked; const uint8_t* suffix_masked;
   float* hist_vals; int32_t* hist_cnt;
   uint8_t* commit_active; uint8_t* commit_suffix; float* conf_active; int32_t* yhat_active;
