@@ -96,13 +96,21 @@ def counter_traffic():
 
 
 def host_info() -> dict:
-    """CPU model and the BLAS thread count the oracle runs with."""
+    """CPU model (name, family/model/stepping, clock) and the BLAS thread count the oracle runs with."""
     model = "unknown"
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k in ("model name", "cpu family", "model", "stepping", "cpu MHz", "cache size") and k not in fields:
+                fields[k] = v
+            if not line.strip() and fields:
                 break
+        if "model name" in fields:
+            model = (f"{fields['model name']} (family {fields.get('cpu family', '?')}, model "
+                     f"{fields.get('model', '?')}, stepping {fields.get('stepping', '?')}, "
+                     f"{fields.get('cpu MHz', '?')} MHz, cache {fields.get('cache size', '?')})")
     except OSError:
         pass
     try:
@@ -169,6 +177,45 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "kind": "oracle", "cpu_model": info["cpu_model"], "host_cpus": info["host_cpus"],
             "sample": f"{layers} of {w.n_layers} layers of one sequence's refresh step ({what}), "
                       f"{t_total:.1f} s of CPU time, scaled to {w.n_layers} layers x {w.batch} sequence(s)"}
+
+
+def oracle_step_timing(names=("tiny_fp32_layer", "llada8b_layer"), reps: int = 3) -> dict:
+    """Single-thread CPU oracle time of one refresh step of the single-layer workloads (window
+    update, drift, sparse forward, and the next layer's K/V of the packet), median of reps."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import polestar_oracle as O
+    out = {}
+    with threadpool_limits(limits=1):
+        for w in synth.WORKLOADS.values():
+            if w.name not in names:
+                continue
+            cfg = O.Cfg.from_workload(w)
+            blk = w.prompt
+            nw = len(O.window_positions(blk, w.n_pos, w.block, w.win_prefix, w.win_suffix))
+            W = {k: v.double().numpy() for k, v in synth.layer_weights(w, 0).items()}
+            W1 = {k: v.double().numpy() for k, v in synth.layer_weights(w, 1).items()}
+            t = lambda tag, shape, dt=w.dtype: synth.tensor(w, (0,) + tag, shape, 1.0, 0, "cpu", dt).double().numpy()
+            H = t((1,), (nw, w.d))
+            times = []
+            for _ in range(reps):
+                ls = {"K": t((2,), (w.n_pos, w.n_kv_heads, w.head_dim)),
+                      "V": t((3,), (w.n_pos, w.n_kv_heads, w.head_dim)),
+                      "P": t((4,), (w.n_clusters, w.n_heads, w.n_pos), "f32")}
+                z, m, _ = O.spherical_kmeans(H, w.n_clusters, synth.kmeans_init(w, nw, 0, 0), w.kmeans_iters)
+                ls.update(Z=cfg.st(z), M=m, H=H.copy())
+                h_act = t((5,), (w.block, w.d))
+                t0 = time.perf_counter()
+                cu = O.cluster_update(ls, cfg)
+                dr = O.drift_layer(ls, W, cfg, blk, h_act, cu["h"], cu["patched"], True)
+                rf = O.refresh_layer(W, cfg, h_act, cu["h"], dr["o"], dr["S"])
+                O.kv_rows(rf["U"], W1["wk"], W1["wv"], cfg)
+                times.append(time.perf_counter() - t0)
+            out[w.name] = {"seconds_per_step": float(np.median(times)), "reps": reps, "threads": 1,
+                           "selected_rows": int(len(dr["S"]))}
+    return {"oracle_single_thread": out, **host_info()}
 
 
 def entry_cpu_baseline(w, blk: int, full: bool, budget_s: float = 20.0):
@@ -293,7 +340,12 @@ def main():
                     help="time the block entry (polestar_entry, full and window kinds) instead of the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="also run one element-wise copy of MB MiB (reference for hardware byte counters)")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="(CPU only) single-thread oracle time per refresh step of the single-layer workloads")
     args = ap.parse_args()
+    if args.oracle_timing:
+        print(json.dumps(oracle_step_timing()), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this refresh path runs on a single MI355X and uses no "
               "collectives; run it without --gpus or with --gpus 1.", file=sys.stderr)
@@ -478,13 +530,13 @@ def main():
     if commit:
         gu_flops = 2 * w.d * 2 * w.ffn * (w.block + n_sel) * bt
         achieved = gu_flops / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "gate/up projection (split-K bf16 GEMM + SwiGLU finish), all sequences",
+        roof = {"bound": "mfma", "kernel": "gate/up projection (bf16 GEMM with the SwiGLU product; split-K finish where split), all sequences",
                 "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5), "launches": gu_n, "timing": timing}
     else:
         achieved = lb["gu_launch"] / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "gate/up projection (split-K bf16 GEMM + SwiGLU finish)",
+        roof = {"bound": "hbm", "kernel": "gate/up projection (bf16 GEMM with the SwiGLU product; split-K finish where split)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic() if args.workload == "llada8b_stack32" else None,

@@ -10,6 +10,10 @@
       runs, each scaled by the counter's reading for an element-wise copy kernel that
       reads and writes B bytes (the run's last float add kernel); ends with a JSON line
       of the figures and a hash of the projection sources they were taken from.
+      --pick every:offset selects dispatches of a kernel that serves several units.
+  python -m drift_driven_sparse_amd.prof_summary mfma <counters.csv> --kernels NAME [NAME ...]
+      [--pick every:offset ...] [--labels L ...]
+      MfmaUtil (MFMA busy %) and bf16 MFMA FLOPs per dispatch of the named kernels.
 """
 from __future__ import annotations
 
@@ -63,16 +67,32 @@ def trace(a):
     print(f"| (other kernels: input generation, copies) | {other[0]} | {other[1] / 1e3:.3f} | |")
 
 
-def _per_kernel(path):
+def _per_kernel(path, counter=None):
+    """Per kernel name, the counter values of its dispatches in dispatch order (rows of other
+    counters skipped when ``counter`` is given), and the copy probe's value."""
+    rows = list(csv.DictReader(open(path)))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else None
+    if key:
+        rows.sort(key=lambda r: int(r[key]))
     agg = collections.defaultdict(list)
     probe = None
-    for r in csv.DictReader(open(path)):
+    for r in rows:
+        if counter and r.get("Counter_Name") != counter:
+            continue
         n = short(r["Kernel_Name"])
         v = float(r["Counter_Value"])
         agg[n].append(v)
         if "CUDAFunctorOnSelf_add<float>" in n:
             probe = v
     return agg, probe
+
+
+def _pick(vals, spec):
+    """Dispatches selected by 'every:offset' (e.g. 2:1 = the odd ones), or all."""
+    if not spec:
+        return vals
+    every, off = (int(x) for x in spec.split(":"))
+    return vals[off::every]
 
 
 def pmc(a):
@@ -89,8 +109,9 @@ def pmc(a):
     print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |")
     print("|---|---:|---:|---:|---:|---:|")
     total = 0.0
-    for k in a.kernels:
-        fv, wv = fetch.get(k), write.get(k)
+    picks = a.pick or [""] * len(a.kernels)
+    for k, pk in zip(a.kernels, picks):
+        fv, wv = _pick(fetch.get(k, []), pk), _pick(write.get(k, []), pk)
         if not fv or not wv:
             raise SystemExit(f"kernel {k} not in both runs")
         fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
@@ -101,6 +122,26 @@ def pmc(a):
     print("```json")
     print(json.dumps({"traffic_bytes": round(total * 1e6), "kernels": a.kernels, "source_hash": source_hash()}))
     print("```")
+
+
+def mfma(a):
+    """Per kernel: mean MfmaUtil (% of the MFMA units' cycles busy while the GPU was active) and
+    bf16 MFMA FLOPs per dispatch, from one counter run."""
+    util, _ = _per_kernel(a.csv, "MfmaUtil")
+    flops, _ = _per_kernel(a.csv, "MfmaFlopsBF16")
+    print(f"# {a.title}\n")
+    if a.command:
+        print(f"Command (from the repository root on the GPU box):\n\n```\n{a.command}\n```\n")
+    print("| unit | kernel | dispatches | MFMA busy % | bf16 MFMA GFLOP per dispatch |")
+    print("|---|---|---:|---:|---:|")
+    picks = a.pick or [""] * len(a.kernels)
+    labels = a.labels or a.kernels
+    for k, pk, lab in zip(a.kernels, picks, labels):
+        u, f = _pick(util.get(k, []), pk), _pick(flops.get(k, []), pk)
+        if not u:
+            raise SystemExit(f"kernel {k} not in the run")
+        fl = sum(f) / len(f) / 1e9 if f else float("nan")
+        print(f"| {lab} | `{k}` | {len(u)} | {sum(u) / len(u):.1f} | {fl:.2f} |")
 
 
 def main():
@@ -115,10 +156,19 @@ def main():
     p.add_argument("--write", required=True)
     p.add_argument("--kernels", nargs="+", required=True)
     p.add_argument("--probe-bytes", type=int, required=True)
+    p.add_argument("--pick", nargs="*", default=None,
+                   help="per kernel, 'every:offset' to select dispatches (kernels launched for several units)")
     p.add_argument("--title", default="rocprofv3 memory counters")
     p.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--kernels", nargs="+", required=True)
+    m.add_argument("--pick", nargs="*", default=None)
+    m.add_argument("--labels", nargs="*", default=None)
+    m.add_argument("--title", default="rocprofv3 MFMA counters")
+    m.add_argument("--command", default="")
     a = ap.parse_args()
-    trace(a) if a.cmd == "trace" else pmc(a)
+    {"trace": trace, "pmc": pmc, "mfma": mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
