@@ -51,10 +51,20 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     else if constexpr (I == 6) return b6;
     else return b7;
   };
-  // sequences are the fastest grid dimension: the workgroups of all sequences that stream one
-  // weight tile are dispatched together, so the repeats of the tile come from L2 and the
-  // last-level cache rather than HBM
-  const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
+  // Workgroup -> (sequence b, column tile nt, split sp).  Workgroups are handed to the 8 XCDs
+  // in turn (id % 8), each XCD with its own L2: the ids of one XCD take one (tile, split) for
+  // all sequences in a row, so that a weight tile's repeats for the other sequences come from
+  // that XCD's L2.  With one sequence this is the identity (tile-major, split outer).
+  int b, nt, sp;
+  {
+    const int id = blockIdx.x, q = id >> 3;
+    const int t = (q / g.batch) * 8 + (id & 7);
+    const int ntiles = PS_CEIL_DIV(g.N, C::NCOL);
+    if (t >= ntiles * g.ksplit) return;
+    b = q % g.batch;
+    nt = t % ntiles;
+    sp = t / ntiles;
+  }
   // this launch's slab: rows [row0, row0 + RT*16) of the sequence; r below is slab-local
   const int row0 = g.A.row0;
   int rows_b = g.A.rows(b) - row0;
@@ -174,7 +184,61 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
         }
     return;
   }
-  if constexpr (KIND == EPI_QKV || KIND == EPI_KV) {
+  if constexpr (KIND == EPI_LMSTAT) {
+    // LM-head statistics of this workgroup's NCOL vocabulary ids per row: max logit, sum of
+    // exp(logit - max), best logit among ids != mask_id with its id (lowest on ties).  Each lane
+    // combines its subtiles (ascending ids), the 16 lanes of a row group by an xor tree, the
+    // column waves of a row in order through LDS.
+    static_assert(PL == 1, "LM head: one bf16 plane");
+    __shared__ float lmst[CG][RT * 16][4];
+    const EpiParams& e = g.e;
+    auto comb = [](float& m, float& s, float& v, int& id, float m2, float s2, float v2, int id2) {
+      const float M = fmaxf(m, m2);
+      s = M == -INFINITY ? 0.f : s * expf(m - M) + s2 * expf(m2 - M);
+      m = M;
+      if (v2 > v || (v2 == v && id2 < id)) {
+        v = v2;
+        id = id2;
+      }
+    };
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = -INFINITY, s = 0.f, v = -INFINITY;
+        int id = 0x7fffffff;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+          const int c = col0 + sb * 16;
+          const bool ok = c < e.vocab;
+          const float l = ok ? acc[rt][sb][i] : -INFINITY;
+          comb(m, s, v, id, l, ok ? 1.f : 0.f, (ok && c != e.mask_id) ? l : -INFINITY, c);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1)
+          comb(m, s, v, id, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64), __shfl_xor(v, o, 64), __shfl_xor(id, o, 64));
+        if ((lane & 15) == 0) {
+          const int rl = (rt * RG + rg) * 16 + 4 * (lane >> 4) + i;
+          lmst[cg][rl][0] = m;
+          lmst[cg][rl][1] = s;
+          lmst[cg][rl][2] = v;
+          lmst[cg][rl][3] = __int_as_float(id);
+        }
+      }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < RT * 16; rl += blockDim.x) {
+      if (rl >= rows_b) continue;
+      float m = lmst[0][rl][0], s = lmst[0][rl][1], v = lmst[0][rl][2];
+      int id = __float_as_int(lmst[0][rl][3]);
+      for (int c2 = 1; c2 < CG; ++c2)
+        comb(m, s, v, id, lmst[c2][rl][0], lmst[c2][rl][1], lmst[c2][rl][2], __float_as_int(lmst[c2][rl][3]));
+      float* st = e.lm_stats + (((int64_t)b * e.lm_rows + row0 + rl) * e.lm_tiles + nt) * 4;
+      st[0] = m;
+      st[1] = s;
+      st[2] = v;
+      st[3] = __int_as_float(v == -INFINITY ? -1 : id);
+    }
+  } else if constexpr (KIND == EPI_QKV || KIND == EPI_KV) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -215,12 +279,19 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
 template <typename T, int RTW, int RG, int CG, int NSUB, int PL>
 hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
   using C = DlCfg<RTW, RG, CG, NSUB, PL>;
-  const dim3 grid(g.batch, PS_CEIL_DIV(g.N, C::NCOL), g.ksplit), block(64 * RG * CG);
+  const int tiles = PS_CEIL_DIV(g.N, C::NCOL) * g.ksplit;
+  const dim3 grid(8 * g.batch * PS_CEIL_DIV(tiles, 8)), block(64 * RG * CG);
   // with split-K every kind writes raw partial sums; its epilogue runs in launch_dl_finish
   switch (g.ksplit > 1 ? (int)EPI_PARTIAL : g.e.kind) {
     case EPI_PARTIAL: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_PARTIAL>), grid, block, 0, s, g); break;
     case EPI_QKV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_QKV>), grid, block, 0, s, g); break;
     case EPI_KV: hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_KV>), grid, block, 0, s, g); break;
+    case EPI_LMSTAT:
+      if constexpr (PL == 1) {
+        hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_LMSTAT>), grid, block, 0, s, g);
+        break;
+      }
+      return hipErrorInvalidValue;
     case EPI_SWIGLU:
       if constexpr (PL == 2 && NSUB % 2 == 0) {
         hipLaunchKernelGGL((dl_kernel<T, RTW, RG, CG, NSUB, PL, EPI_SWIGLU>), grid, block, 0, s, g);

@@ -26,7 +26,8 @@ struct polestar_handle {
                         // token-row buffers of the workspace hold this many rows per sequence
   int32_t attn_chunk, attn_nchunks;             // bf16 attention: keys per workgroup, workgroups per head
   int32_t attn_rgroups;                         // bf16 attention: workgroups along the query rows
-  int32_t lm_tiles;  // vocab / 64 rounded up
+  int32_t lm_tiles;  // LM-head vocabulary tiles: vocab / tile width of sh_lm (bf16) or 64 (f32), rounded up
+  int32_t sh_lm;     // LM-head workgroup shape (bf16)
   WsLayout ws;
   polestar_check chk;
 };
