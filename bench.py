@@ -415,8 +415,8 @@ def main():
     inputs = synth.tensor(w, (99,), (n_in, bt, w.block, w.d), 1.0, 0, "cuda", "bf16")
     h_in = torch.zeros(bt, w.block, w.d, dtype=torch.bfloat16, device="cuda")
 
-    def step():
-        out = st.step(blk, h_in)
+    def step(refresh=True):
+        out = st.step(blk, h_in, refresh=refresh)
         if commit:
             st.commit(blk, out)
 
@@ -437,7 +437,11 @@ def main():
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        log("[bench] step captured in a HIP graph")
+        graph_a = torch.cuda.CUDAGraph()   # the active-only step (no refresh) of the trajectory
+        with torch.cuda.graph(graph_a):
+            step(False)
+        torch.cuda.synchronize()
+        log("[bench] refresh and active-only steps captured in HIP graphs")
 
     def run_step(i, eager=False):
         h_in.copy_(inputs[i])
@@ -576,6 +580,38 @@ def main():
         log(f"[bench] copy probe: one element-wise kernel reading {src.numel() * 4} B and writing "
             f"{dst.numel() * 4} B")
         del src, dst
+    # the workload's own trajectory: its unmask schedule over its step count, each step a refresh
+    # or an active-only step as the update trigger decides (tau_upd), one event between steps
+    sched = synth.unmask_schedule(w, steps=w.steps)
+    tin = synth.tensor(w, (98,), (len(sched), bt, w.block, w.d), 1.0, 0, "cuda", "bf16")
+    kinds, decoded = [], 0
+    for _, offs in sched:
+        decoded += len(offs)
+        r = bool(B.polestar_should_refresh(decoded, w.tau_upd))
+        decoded = 0 if r else decoded
+        kinds.append(r)
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
+    torch.cuda.synchronize()
+    tev[0].record()
+    for t, r in enumerate(kinds):
+        h_in.copy_(tin[t])
+        if graph is not None:
+            (graph if r else graph_a).replay()
+        else:
+            step(r)
+        tev[t + 1].record()
+    torch.cuda.synchronize()
+    tper = np.array([tev[t].elapsed_time(tev[t + 1]) for t in range(len(kinds))])
+    kr = np.array(kinds)
+    out["trajectory"] = {
+        "steps": len(kinds), "refresh_steps": int(kr.sum()), "active_only_steps": int((~kr).sum()),
+        "tau_upd": w.tau_upd, "ms_total": round(float(tper.sum()), 3),
+        "steps_per_s": round(1000.0 * len(kinds) / float(tper.sum()), 2),
+        "refresh_ms_median": round(float(np.median(tper[kr])), 4) if kr.any() else None,
+        "refresh_ms_mean": round(float(np.mean(tper[kr])), 4) if kr.any() else None,
+        "active_only_ms_median": round(float(np.median(tper[~kr])), 4) if (~kr).any() else None,
+        "active_only_ms_mean": round(float(np.mean(tper[~kr])), 4) if (~kr).any() else None}
+    log(f"[bench] trajectory of {len(kinds)} steps ({int(kr.sum())} refresh): {tper.sum():.2f} ms")
     st.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
