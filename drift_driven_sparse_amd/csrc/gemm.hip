@@ -1,20 +1,18 @@
-// Projection kernels for the gathered rows of a refresh step.
+// Weight packing, the float32 projections and the split-K row reduction.
 //
-// The rows the method needs per layer and sequence are few (active block,
-// window rows, centroids: <= 144) while the weights are large, so every
-// projection here is a skinny GEMM that streams the weight once from HBM.
+// Weight packing: bf16 weights are repacked once into MFMA 16x16x32 B-operand
+// fragments in lane order, grouped so that a workgroup's weights for one K step
+// are contiguous (gemm_dl.hip streams them); float32 weights stay row-major.
 //
-// bf16 path: weights are repacked once into MFMA 16x16x32 B-operand fragments
-// stored in lane order, so every wave load is one contiguous 1 KiB from HBM.
-// A workgroup (4 waves) owns 64 output columns (4 fragments) of one sequence
-// and a range of K; its waves split that range and stream their A rows
-// (activations, L2-resident) straight into registers.  Wave partial sums are
-// combined in LDS in a fixed order, then a fused epilogue writes the result.
-// N = d projections use a split-K grid whose partial sums are reduced (in a
-// fixed order) by a row kernel that also adds the residual.
+// float32 path (small models): a workgroup owns 64 output columns of one
+// sequence and a range of K; a plain FMA inner product per (row, column) into an
+// LDS tile, then the fused epilogue (QKV, SwiGLU, next-layer K/V, LM-head
+// statistics, or raw split-K partial sums).  Every bf16 projection runs on the
+// weight-streaming kernel of gemm_dl.hip instead.
 //
-// float32 path (small models): the same grid and epilogues with a plain FMA
-// inner product.
+// Row reduction: the partial sums of the N = d projections (added in split
+// order) plus the residual, and RMSNorm of the stored row for the next
+// projection.
 #include "kernels.h"
 
 namespace {
@@ -119,114 +117,6 @@ PS_DEV void epilogue(const GemmArgs& g, const EpiParams& e, int b, int rows_b, i
   }
 }
 
-// ---- bf16 MFMA main loop -----------------------------------------------------------------
-// bf16 x bf16 -> f32 MFMA of one 16x16 tile step
-PS_DEV floatx4_t mfma(uint4 a, uint4 w, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, w), c,
-                                                 0, 0, 0);
-}
-
-// Each wave walks its K range in 32-wide steps.  Weight fragments are kept in a
-// ring of kDW steps and the activation fragments of the next step are loaded
-// while the current one is multiplied, so a wave always has several KiB of
-// HBM reads in flight.  Loads past the wave's range re-read its last step
-// (valid addresses, results unused) so the loop body has no load branches.
-constexpr int kDW = 4;   // weight prefetch depth in 32-wide K steps
-
-template <typename T, int RT, int KIND>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, EpiParams e) {
-  constexpr int NSUB = kNT / 16;
-  __shared__ float tile[RT * 16 * kLDT];
-  // sequences fastest: one weight tile's workgroups of all sequences are dispatched together
-  const int b = blockIdx.x, nt = blockIdx.y, sp = blockIdx.z;
-  int rows_b = g.A.rows(b) - g.A.row0;   // this launch's slab of rows
-  if (rows_b > RT * 16) rows_b = RT * 16;
-  if (rows_b <= 0) return;
-  const int nrt = (rows_b + 15) >> 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int k32n = g.K >> 5;
-  const int s0 = (int)((int64_t)k32n * sp / g.ksplit), s1 = (int)((int64_t)k32n * (sp + 1) / g.ksplit);
-  const int w0 = s0 + (s1 - s0) * wave / 4, w1 = s0 + (s1 - s0) * (wave + 1) / 4;
-  const int wlast = w1 > 0 ? w1 - 1 : 0;
-
-  const uint16_t* Ab = (const uint16_t*)g.A.base + (int64_t)b * g.A.bstride;
-  const uint4* arow[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    int r = rt * 16 + (lane & 15);
-    if (r >= rows_b) r = 0;
-    arow[rt] = (const uint4*)(Ab + g.A.src_row(b, g.A.row0 + r) * g.A.lda + 8 * (lane >> 4));
-  }
-  const int n16_total = g.N >> 4;
-  // per-subtile fragment stream; subtiles past N re-read the first one (their columns are never stored)
-  const uint4* Wsub[NSUB];
-#pragma unroll
-  for (int sb = 0; sb < NSUB; ++sb) {
-    int n16 = nt * NSUB + sb;
-    if (n16 >= n16_total) n16 = nt * NSUB;
-    Wsub[sb] = (const uint4*)g.W + ((int64_t)n16 * k32n) * 64 + lane;
-  }
-
-  floatx4_t acc[RT][NSUB];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wr[kDW][NSUB];
-  uint4 ar[2][RT];
-  auto load_w = [&](uint4 (&w)[NSUB], int st) {
-    st = st < wlast ? st : wlast;
-#pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) w[sb] = Wsub[sb][(int64_t)st * 64];
-  };
-  auto load_a = [&](uint4 (&a)[RT], int st) {
-    st = st < wlast ? st : wlast;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) a[rt] = arow[rt][st * 4];
-  };
-  auto compute = [&](const uint4 (&w)[NSUB], const uint4 (&a)[RT]) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (rt < nrt) {
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) acc[rt][sb] = mfma(a[rt], w[sb], acc[rt][sb]);
-      }
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kDW; ++u) load_w(wr[u], w0 + u);
-  load_a(ar[0], w0);
-  load_a(ar[1], w0 + 1);
-  for (int t = w0; t < w1; t += kDW) {
-#pragma unroll
-    for (int u = 0; u < kDW; ++u) {
-      if (t + u < w1) compute(wr[u], ar[u & 1]);
-      load_w(wr[u], t + u + kDW);
-      load_a(ar[u & 1], t + u + 2);
-    }
-  }
-  // Combine the four waves' partial sums in LDS, wave 0 first.
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if (rt < nrt) {
-#pragma unroll
-          for (int sb = 0; sb < NSUB; ++sb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float* t = &tile[(rt * 16 + 4 * (lane >> 4) + i) * kLDT + sb * 16 + (lane & 15)];
-              *t = (w == 0 ? 0.f : *t) + acc[rt][sb][i];
-            }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  epilogue<T, KIND>(g, e, b, rows_b, nt * kNT, nt, tile);
-}
-
 // ---- float32 main loop ----------------------------------------------------------------------
 template <int RT, int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) {
@@ -263,11 +153,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams e) 
 template <typename T, int RT, int KIND>
 hipError_t launch_one(const GemmArgs& g, const EpiParams& e, hipStream_t s) {
   dim3 grid(g.batch, PS_CEIL_DIV(g.N, kNT), g.ksplit);
-  if constexpr (std::is_same<T, float>::value) {
-    hipLaunchKernelGGL((gemm_f32_kernel<RT, KIND>), grid, dim3(256), 0, s, g, e);
-  } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<T, RT, KIND>), grid, dim3(256), 0, s, g, e);
-  }
+  hipLaunchKernelGGL((gemm_f32_kernel<RT, KIND>), grid, dim3(256), 0, s, g, e);
   return hipGetLastError();
 }
 
@@ -406,6 +292,8 @@ hipError_t launch_pack(int kind, const void* src, void* dst, int N, int K, int G
 
 template <typename T>
 hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipStream_t s) {
+  // float32 storage only: every bf16 projection runs on the weight-streaming kernel (gemm_dl)
+  if constexpr (!std::is_same<T, float>::value) return hipErrorInvalidValue;
   if (g.A.row0 != 0) return hipErrorInvalidValue;
   // one launch per slab of at most kDlSlab rows
   for (int r0 = 0; r0 < max_rows; r0 += kDlSlab) {
