@@ -327,6 +327,41 @@ def copy_bandwidth(torch, mib: int = 1024) -> float:
     return 2 * (mib << 20) / (best * 1e-3) / 1e9
 
 
+def trajectory(w, bt, h_in, graph, graph_a, step, out):
+    """The workload's own trajectory: its unmask schedule over its step count, each step a refresh
+    or an active-only step as the update trigger decides (tau_upd), one event between steps."""
+    sched = synth.unmask_schedule(w, steps=w.steps)
+    tin = synth.tensor(w, (98,), (len(sched), bt, w.block, w.d), 1.0, 0, "cuda", "bf16")
+    kinds, decoded = [], 0
+    for _, offs in sched:
+        decoded += len(offs)
+        r = bool(B.polestar_should_refresh(decoded, w.tau_upd))
+        decoded = 0 if r else decoded
+        kinds.append(r)
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
+    torch.cuda.synchronize()
+    tev[0].record()
+    for t, r in enumerate(kinds):
+        h_in.copy_(tin[t])
+        if graph is not None:
+            (graph if r else graph_a).replay()
+        else:
+            step(r)
+        tev[t + 1].record()
+    torch.cuda.synchronize()
+    tper = np.array([tev[t].elapsed_time(tev[t + 1]) for t in range(len(kinds))])
+    kr = np.array(kinds)
+    out["trajectory"] = {
+        "steps": len(kinds), "refresh_steps": int(kr.sum()), "active_only_steps": int((~kr).sum()),
+        "tau_upd": w.tau_upd, "ms_total": round(float(tper.sum()), 3),
+        "steps_per_s": round(1000.0 * len(kinds) / float(tper.sum()), 2),
+        "refresh_ms_median": round(float(np.median(tper[kr])), 4) if kr.any() else None,
+        "refresh_ms_mean": round(float(np.mean(tper[kr])), 4) if kr.any() else None,
+        "active_only_ms_median": round(float(np.median(tper[~kr])), 4) if (~kr).any() else None,
+        "active_only_ms_mean": round(float(np.mean(tper[~kr])), 4) if (~kr).any() else None}
+    log(f"[bench] trajectory of {len(kinds)} steps ({int(kr.sum())} refresh): {tper.sum():.2f} ms")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +375,8 @@ def main():
                     help="time the block entry (polestar_entry, full and window kinds) instead of the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="also run one element-wise copy of MB MiB (reference for hardware byte counters)")
+    ap.add_argument("--no-trajectory", action="store_true",
+                    help="(diagnostics) skip the trajectory, so that a kernel trace holds refresh steps only")
     ap.add_argument("--oracle-timing", action="store_true",
                     help="(CPU only) single-thread oracle time per refresh step of the single-layer workloads")
     args = ap.parse_args()
@@ -425,7 +462,7 @@ def main():
     step()
     torch.cuda.synchronize()
 
-    graph = None
+    graph = graph_a = None
     if not args.no_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -580,38 +617,10 @@ def main():
         log(f"[bench] copy probe: one element-wise kernel reading {src.numel() * 4} B and writing "
             f"{dst.numel() * 4} B")
         del src, dst
-    # the workload's own trajectory: its unmask schedule over its step count, each step a refresh
-    # or an active-only step as the update trigger decides (tau_upd), one event between steps
-    sched = synth.unmask_schedule(w, steps=w.steps)
-    tin = synth.tensor(w, (98,), (len(sched), bt, w.block, w.d), 1.0, 0, "cuda", "bf16")
-    kinds, decoded = [], 0
-    for _, offs in sched:
-        decoded += len(offs)
-        r = bool(B.polestar_should_refresh(decoded, w.tau_upd))
-        decoded = 0 if r else decoded
-        kinds.append(r)
-    tev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
-    torch.cuda.synchronize()
-    tev[0].record()
-    for t, r in enumerate(kinds):
-        h_in.copy_(tin[t])
-        if graph is not None:
-            (graph if r else graph_a).replay()
-        else:
-            step(r)
-        tev[t + 1].record()
-    torch.cuda.synchronize()
-    tper = np.array([tev[t].elapsed_time(tev[t + 1]) for t in range(len(kinds))])
-    kr = np.array(kinds)
-    out["trajectory"] = {
-        "steps": len(kinds), "refresh_steps": int(kr.sum()), "active_only_steps": int((~kr).sum()),
-        "tau_upd": w.tau_upd, "ms_total": round(float(tper.sum()), 3),
-        "steps_per_s": round(1000.0 * len(kinds) / float(tper.sum()), 2),
-        "refresh_ms_median": round(float(np.median(tper[kr])), 4) if kr.any() else None,
-        "refresh_ms_mean": round(float(np.mean(tper[kr])), 4) if kr.any() else None,
-        "active_only_ms_median": round(float(np.median(tper[~kr])), 4) if (~kr).any() else None,
-        "active_only_ms_mean": round(float(np.mean(tper[~kr])), 4) if (~kr).any() else None}
-    log(f"[bench] trajectory of {len(kinds)} steps ({int(kr.sum())} refresh): {tper.sum():.2f} ms")
+    if args.no_trajectory:
+        out["trajectory"] = None
+    else:
+        trajectory(w, bt, h_in, graph, graph_a, step, out)
     st.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
