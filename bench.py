@@ -330,6 +330,11 @@ def copy_bandwidth(torch, mib: int = 1024) -> float:
 def trajectory(w, bt, h_in, graph, graph_a, step, out):
     """The workload's own trajectory: its unmask schedule over its step count, each step a refresh
     or an active-only step as the update trigger decides (tau_upd), one event between steps."""
+    import numpy as np
+    import torch
+
+    import synth
+    from drift_driven_sparse_amd import binding as B
     sched = synth.unmask_schedule(w, steps=w.steps)
     tin = synth.tensor(w, (98,), (len(sched), bt, w.block, w.d), 1.0, 0, "cuda", "bf16")
     kinds, decoded = [], 0

@@ -59,6 +59,9 @@ PS_DEV int stage_row(const AttnArgs& a, int row) {   // staging buffer row: [pro
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 #define AT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// ... and every LDS access of the wave complete (lgkmcnt 0): taken before the ring barrier, after
+// which loads into the stage read last may land
+#define AT_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4))
 
 PS_DEV uint4 frag_hi(const float* x) {
   uint32_t w[4];
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   for (int s = 0; s < nst; s += 4) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
       ([&] {
-        AT_VMCNT(LPW * 2);
+        AT_WAIT(LPW * 2);
         __builtin_amdgcn_s_barrier();
         issue(bp(std::integral_constant<int, (U + 3) % 4>{}), s + U + 3);
         if (s + U < nst) compute(bp(std::integral_constant<int, U>{}), s + U);

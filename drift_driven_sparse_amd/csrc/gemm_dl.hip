@@ -4,9 +4,9 @@
 // the kernel is organised around moving bytes: every 32-wide K step is one
 // pipeline stage that holds the A fragments of all row tiles and the weight
 // fragments of the workgroup.  Stages are filled by direct global -> LDS loads
-// (global_load_lds_dwordx4, no VGPR staging) in a ring of P buffers; stage s is
-// consumed after a wait that leaves the P-2 younger stages in flight and one
-// workgroup barrier.  Each ring buffer is its own LDS object, which lets the
+// (global_load_lds_dwordx4, no VGPR staging) in a ring of P buffers (P = 4, or 3
+// where four do not fit); stage s is consumed after a wait that leaves the P-2
+// younger stages in flight and one workgroup barrier.  Each ring buffer is its own LDS object, which lets the
 // compiler see that reads of one stage do not alias the loads still landing in
 // the others.
 //

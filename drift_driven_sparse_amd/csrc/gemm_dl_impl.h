@@ -12,6 +12,10 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define DL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// The same with every LDS read of the wave complete as well (lgkmcnt 0).  Taken before each ring
+// barrier: the barrier releases the stage read last for the loads issued after it, and a read
+// still queued in the LDS unit could otherwise return data those loads already wrote.
+#define DL_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4))
 
 PS_DEV floatx4_t mfma_bf16(uint4 a, uint4 w, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, w), c,
@@ -26,8 +30,10 @@ struct DlCfg {
   static constexpr int F = FA + CG * NSUB;         // fragments per stage
   static constexpr int LPW = (F + NWV - 1) / NWV;  // direct loads per wave per stage
   static constexpr int STAGE = F * 1024;           // bytes
+  // ring depth: four stages where they fit (three in flight while one is read).  The weight
+  // stream is already saturated at that depth, and deeper rings only unroll more code.
   static constexpr int P0 = (150 * 1024 - 1024) / STAGE;
-  static constexpr int P = P0 > 8 ? 8 : P0;        // ring depth
+  static constexpr int P = P0 > 4 ? 4 : P0;
   static constexpr int NCOL = CG * NSUB * 16;      // columns per workgroup
   static_assert(P >= 3, "pipeline needs three stages");
   static_assert(LPW * (P - 2) < 64, "vmcnt range");
@@ -39,17 +45,12 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
   constexpr int NWV = C::NWV, RT = C::RT, FA = C::FA, F = C::F, LPW = C::LPW, P = C::P;
   // ring stages (only the first P are referenced) and one slot that the padding loads of the
   // waves with fewer than LPW fragments write to and nothing reads
-  __shared__ uint4 b0[F * 64], b1[F * 64], b2[F * 64], b3[F * 64], b4[F * 64], b5[F * 64], b6[F * 64],
-      b7[F * 64], bd[64];
+  __shared__ uint4 b0[F * 64], b1[F * 64], b2[F * 64], b3[F * 64], bd[64];
   auto bp = [&](auto I) -> uint4* {
     if constexpr (I == 0) return b0;
     else if constexpr (I == 1) return b1;
     else if constexpr (I == 2) return b2;
-    else if constexpr (I == 3) return b3;
-    else if constexpr (I == 4) return b4;
-    else if constexpr (I == 5) return b5;
-    else if constexpr (I == 6) return b6;
-    else return b7;
+    else return b3;
   };
   // Workgroup -> (sequence b, column tile nt, split sp).  Workgroups are handed to the 8 XCDs
   // in turn (id % 8), each XCD with its own L2: the ids of one XCD take one (tile, split) for
@@ -155,8 +156,9 @@ __global__ __launch_bounds__(64 * RG * CG) void dl_kernel(DlArgs g) {
     for (int s = 0; s < n; s += P) {
       [&]<int... U>(std::integer_sequence<int, U...>) {
         ([&] {
-          DL_VMCNT(LPW * (P - 2));          // this wave's loads of stage s+U have landed
-          __builtin_amdgcn_s_barrier();     // ... and everyone's; stage s+U-1 is fully consumed
+          DL_WAIT(LPW * (P - 2));           // this wave's loads of stage s+U have landed, its
+          __builtin_amdgcn_s_barrier();     // reads of s+U-1 are done; after the barrier both
+                                            // hold for every wave
           issue(bp(std::integral_constant<int, (U + P - 1) % P>{}), s + U + P - 1);
           if (NT > 0 && s + U < n) compute(bp(std::integral_constant<int, U>{}));
         }(), ...);
