@@ -6,8 +6,9 @@
 // [batch][Hkv][dh][n] so that V^T fragments are contiguous along keys.
 //
 // bf16 path (attn_chunk_kernel): workgroups over (key chunk, head); MFMA 16x16x32 with the
-// float32 queries and the probabilities as three-term bf16 splits (float32 precision), online
-// softmax per chunk.  Logits
+// float32 queries as three-term bf16 splits (float32 precision: the logits feed the KL drift)
+// and the probabilities as two-term splits (relative error below 2^-16, far inside what the
+// outputs need), online softmax per chunk.  Logits
 // of proxy rows and (when requested) active rows go to a staging buffer.  One following launch
 // (attn_merge_kl_kernel) combines the chunks of the token rows and forms the KL drift of the
 // staged rows against the previous logits, which the staged logits then replace.
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = 0.f;
       }
-      const Split3 pv = frag_split3(v);
+      const Split3 pv = frag_split3(v);   // the third term is not used
       if (rescale) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[t][dt] *= corr;
@@ -264,7 +265,6 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint4 vf = buf[(FK + dt) * 64 + lane];
-        o[t][dt] = mfma(vf, pv.t[2], o[t][dt]);
         o[t][dt] = mfma(vf, pv.t[1], o[t][dt]);
         o[t][dt] = mfma(vf, pv.t[0], o[t][dt]);
       }
