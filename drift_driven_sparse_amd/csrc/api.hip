@@ -1130,11 +1130,11 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
   // bf16 projections: tile width and split-K so that about 256 workgroups are busy
   {
-    const int one[] = {DL_NARROW, DL_N192, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8, DL_P96};
+    const int one[] = {DL_NARROW, DL_N192, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8, DL_P96, DL_P160};
     plan_projection(h->nq + 2 * h->nkv, d.d, d.batch, one, 3, 8, false, &h->sh_qkv, &h->ks_qkv);
-    plan_projection(d.d, h->nq, d.batch, two, 4, 16, false, &h->sh_o, &h->ks_o);
-    plan_projection(2 * d.ffn, d.d, d.batch, two, 4, 4, true, &h->sh_gu, &h->ks_gu);
-    plan_projection(d.d, d.ffn, d.batch, two, 4, 16, false, &h->sh_down, &h->ks_down);
+    plan_projection(d.d, h->nq, d.batch, two, 5, 16, false, &h->sh_o, &h->ks_o);
+    plan_projection(2 * d.ffn, d.d, d.batch, two, 5, 4, true, &h->sh_gu, &h->ks_gu);
+    plan_projection(d.d, d.ffn, d.batch, two, 5, 16, false, &h->sh_down, &h->ks_down);
     plan_projection(2 * h->nkv, d.d, d.batch, one, 3, 16, false, &h->sh_kv, &h->ks_kv);
   }
   // bf16 attention: query rows in two groups when there are enough of them, and the keys split

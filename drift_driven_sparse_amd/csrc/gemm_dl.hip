@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void dl_finish_swiglu_kernel(DlArgs g) {
 int dl_subtiles_per_wave(int shape) {
   switch (shape) {
     case DL_N192: case DL_W192: case DL_N96: return 3;
-    case DL_MID8: case DL_P96: return 2;
+    case DL_MID8: case DL_P96: case DL_P160: return 2;
     default: return 4;
   }
 }
@@ -109,6 +109,7 @@ int dl_tile_cols(int shape) {
     case DL_WIDE: return 256;
     case DL_N192: case DL_W192: return 192;
     case DL_N96: case DL_P96: return 96;
+    case DL_P160: return 160;
     default: return 128;
   }
 }
@@ -139,6 +140,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
         case DL_W192: e = dl_launch_w192(gs, mr, s); break;
         case DL_MID8: e = dl_launch_mid8(gs, mr, s); break;
         case DL_P96: e = dl_launch_p96(gs, mr, s); break;
+        case DL_P160: e = dl_launch_p160(gs, mr, s); break;
         default: e = hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;

@@ -204,7 +204,7 @@ struct DlArgs {
   EpiParams e;
 };
 // Workgroup shapes: row groups x column groups (waves), columns per wave.  One bf16 plane:
-// NARROW, N192, N96; hi/lo planes: WIDE, MID, W192, MID8, P96.
+// NARROW, N192, N96; hi/lo planes: WIDE, MID, W192, MID8, P96, P160.
 enum DlShape { DL_NARROW = 0,   // 3 x 2 waves of 64 columns: 128-column tiles
                DL_WIDE = 1,     // 2 x 4 waves of 64 columns: 256-column tiles
                DL_MID = 2,      // 2 x 2 waves of 64 columns: 128-column tiles
@@ -212,7 +212,8 @@ enum DlShape { DL_NARROW = 0,   // 3 x 2 waves of 64 columns: 128-column tiles
                DL_W192 = 4,     // 2 x 4 waves of 48 columns: 192-column tiles
                DL_N96 = 5,      // 4 x 2 waves of 48 columns: 96-column tiles
                DL_MID8 = 6,     // 2 x 4 waves of 32 columns: 128-column tiles
-               DL_P96 = 7 };    // 4 x 3 waves of 32 columns: 96-column tiles
+               DL_P96 = 7,      // 4 x 3 waves of 32 columns: 96-column tiles
+               DL_P160 = 8 };   // 2 x 5 waves of 32 columns: 160-column tiles
 int dl_tile_cols(int shape);
 // 16-column subtiles per wave; the in-kernel SwiGLU epilogue needs an even count (gate/up pairs)
 int dl_subtiles_per_wave(int shape);
