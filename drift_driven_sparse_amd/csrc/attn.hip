@@ -6,9 +6,9 @@
 // [batch][Hkv][dh][n] so that V^T fragments are contiguous along keys.
 //
 // bf16 path (attn_chunk_kernel): workgroups over (key chunk, head); MFMA 16x16x32 with the
-// float32 queries as three-term bf16 splits (float32 precision: the logits feed the KL drift)
-// and the probabilities as two-term splits (relative error below 2^-16, far inside what the
-// outputs need), online softmax per chunk.  Logits
+// float32 queries as three-term bf16 splits where the logits feed the KL drift (float32
+// precision), two-term splits elsewhere, and the probabilities as two-term splits (relative
+// error below 2^-16, far inside what the outputs need), online softmax per chunk.  Logits
 // of proxy rows and (when requested) active rows go to a staging buffer.  One following launch
 // (attn_merge_kl_kernel) combines the chunks of the token rows and forms the KL drift of the
 // staged rows against the previous logits, which the staged logits then replace.
@@ -151,13 +151,18 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
   // query fragments (B operand of S^T): lane holds row c16 of each tile, dh [32 ks + 8 g4, +8)
   // (loaded before the first K/V stages are issued and converted after, so that the query
   // loads overlap the K/V loads)
+  // Tiles holding a row whose logits are kept for the KL drift (centroid rows; active rows
+  // when their logits are kept) multiply all three query terms: the drift of nearly equal
+  // distributions needs float32 logits.  The other tiles' logits only weight the outputs, and
+  // two terms (relative error below 2^-16) are far inside what those need.
   Split3 qs[RTW][KS];
   float4 qraw[RTW][KS][2];
-  bool tile_on[RTW], q_valid[RTW];
+  bool tile_on[RTW], q_valid[RTW], q3[RTW];
   auto load_q = [&](auto Tc) __attribute__((always_inline)) {
     constexpr int t = decltype(Tc)::value;
     const int tile = tile0 + wave * RTW + t;
     tile_on[t] = tile * 16 < nrows && wave * RTW + t < a.group_tiles;
+    q3[t] = tile * 16 + 15 >= a.n_tok || (a.act_logits != nullptr && tile * 16 < a.block);
     const int row = tile * 16 + c16;
     q_valid[t] = row < nrows;
     const int qrow = q_valid[t] ? row : 0;
@@ -203,17 +208,31 @@ __global__ __launch_bounds__(64 * NWV) void attn_chunk_kernel(AttnArgs a) {
       constexpr int t = decltype(Tc)::value;
       if (!tile_on[t]) return;
       floatx4_t sacc[2];
+      if (q3[t]) {   // wave-uniform
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 2; ++kt) {
+          floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 kf = buf[(kt * KS + ks) * 64 + lane];
-          acc = mfma(kf, qs[t][ks].t[2], acc);   // smallest terms first
-          acc = mfma(kf, qs[t][ks].t[1], acc);
-          acc = mfma(kf, qs[t][ks].t[0], acc);
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 kf = buf[(kt * KS + ks) * 64 + lane];
+            acc = mfma(kf, qs[t][ks].t[2], acc);   // smallest terms first
+            acc = mfma(kf, qs[t][ks].t[1], acc);
+            acc = mfma(kf, qs[t][ks].t[0], acc);
+          }
+          sacc[kt] = acc;
         }
-        sacc[kt] = acc;
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 kf = buf[(kt * KS + ks) * 64 + lane];
+            acc = mfma(kf, qs[t][ks].t[1], acc);
+            acc = mfma(kf, qs[t][ks].t[0], acc);
+          }
+          sacc[kt] = acc;
+        }
       }
       float v[8];
 #pragma unroll
