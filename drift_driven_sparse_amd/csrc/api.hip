@@ -1137,10 +1137,12 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
     plan_projection(d.d, d.ffn, d.batch, two, 5, 16, false, &h->sh_down, &h->ks_down);
     plan_projection(2 * h->nkv, d.d, d.batch, one, 3, 16, false, &h->sh_kv, &h->ks_kv);
   }
-  // bf16 attention: query rows in two groups when there are enough of them, and the keys split
-  // so that about 256 workgroups run, at least 128 keys each
+  // bf16 attention: query rows in two groups when there are enough of them and one group per
+  // (head, sequence) would leave compute units idle (a second group reads the keys and values
+  // again, which at 16 sequences doubles the attention's traffic), and the keys split so that
+  // about 256 workgroups run, at least 128 keys each
   {
-    h->attn_rgroups = PS_CEIL_DIV(h->mq, 16) >= 6 ? 2 : 1;
+    h->attn_rgroups = PS_CEIL_DIV(h->mq, 16) >= 6 && d.n_heads * d.batch * 2 <= 256 ? 2 : 1;
     const int blocks32 = PS_CEIL_DIV(d.n_pos, 32);
     int want = 256 / (d.n_heads * d.batch * h->attn_rgroups);
     want = want < 1 ? 1 : want;
