@@ -143,7 +143,9 @@ int weight_group(const polestar_handle* h, int which) {
 // Shape and split-K factor of one bf16 projection (n_cols x k weight, batch sequences): the
 // candidate that keeps the largest share of the 256 compute units streaming weights, counting
 // the columns a partial last tile wastes and the rounds of workgroups past the first; ties go
-// to the smaller split (less partial-sum traffic), then to the earlier shape.  With pairs set
+// to the smaller split (less partial-sum traffic), then to the earlier shape (the lists put
+// the widest tiles first: with several sequences the projections are bound by the per-step
+// work of a workgroup, which wider tiles spread over more columns).  With pairs set
 // (gate/up), a shape whose waves hold an odd number of subtiles is only taken with split-K,
 // whose finish kernel forms the SwiGLU product.
 void plan_projection(int n_cols, int k, int batch, const int* shapes, int n_shapes, int cap, bool pairs,
@@ -1130,7 +1132,7 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
   // bf16 projections: tile width and split-K so that about 256 workgroups are busy
   {
-    const int one[] = {DL_NARROW, DL_N192, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8, DL_P96, DL_P160};
+    const int one[] = {DL_N192, DL_NARROW, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8, DL_P96, DL_P160};
     plan_projection(h->nq + 2 * h->nkv, d.d, d.batch, one, 3, 8, false, &h->sh_qkv, &h->ks_qkv);
     plan_projection(d.d, h->nq, d.batch, two, 5, 16, false, &h->sh_o, &h->ks_o);
     plan_projection(2 * d.ffn, d.d, d.batch, two, 5, 4, true, &h->sh_gu, &h->ks_gu);
