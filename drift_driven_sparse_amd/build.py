@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpolestar.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "gemm.hip", "gemm_dl.hip", "gemm_dl_narrow.hip", "gemm_dl_n192.hip", "gemm_dl_n96.hip",
-           "gemm_dl_wide.hip", "gemm_dl_mid.hip", "gemm_dl_w192.hip", "gemm_dl_mid8.hip", "gemm_dl_p96.hip", "gemm_dl_p160.hip", "attn.hip", "cluster.hip", "commit.hip", "staleness.hip"]
+           "gemm_dl_wide.hip", "gemm_dl_mid.hip", "gemm_dl_w192.hip", "gemm_dl_mid8.hip", "gemm_dl_p96.hip", "gemm_dl_p160.hip", "gemm_dl_x512.hip", "attn.hip", "cluster.hip", "commit.hip", "staleness.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

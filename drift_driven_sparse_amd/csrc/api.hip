@@ -145,7 +145,8 @@ int weight_group(const polestar_handle* h, int which) {
 // the columns a partial last tile wastes and the rounds of workgroups past the first; ties go
 // to the smaller split (less partial-sum traffic), then to the earlier shape (the lists put
 // the widest tiles first: with several sequences the projections are bound by the per-step
-// work of a workgroup, which wider tiles spread over more columns).  With pairs set
+// work of a workgroup, which wider tiles spread over more columns, so from 8 sequences on a
+// tie keeps the earlier shape at split 2 or less).  With pairs set
 // (gate/up), a shape whose waves hold an odd number of subtiles is only taken with split-K,
 // whose finish kernel forms the SwiGLU product.
 void plan_projection(int n_cols, int k, int batch, const int* shapes, int n_shapes, int cap, bool pairs,
@@ -161,7 +162,10 @@ void plan_projection(int n_cols, int k, int batch, const int* shapes, int n_shap
       const int wgs = tiles * v;
       const int rounds = PS_CEIL_DIV(wgs, 256);
       const double use = (double)n_cols * batch / ((double)tiles * tc) * wgs / (256.0 * rounds);
-      if (use > best + 1e-9 || (use > best - 1e-9 && v < *ks)) {
+      // a tie takes the smaller split; from 8 sequences on only over a split above 2, so that
+      // the wider (earlier) shape keeps a tie at split 2 or less
+      const bool smaller = batch >= 8 ? v < *ks && *ks > 2 : v < *ks;
+      if (use > best + 1e-9 || (use > best - 1e-9 && smaller)) {
         best = use;
         *shape = shapes[i];
         *ks = v;
@@ -1132,11 +1136,11 @@ int polestar_create(const polestar_dims* dims, const polestar_params* params, po
   h->ksplit = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
   // bf16 projections: tile width and split-K so that about 256 workgroups are busy
   {
-    const int one[] = {DL_N192, DL_NARROW, DL_N96}, two[] = {DL_WIDE, DL_W192, DL_MID8, DL_P96, DL_P160};
+    const int one[] = {DL_N192, DL_NARROW, DL_N96}, two[] = {DL_X512, DL_WIDE, DL_W192, DL_MID8, DL_P96, DL_P160};
     plan_projection(h->nq + 2 * h->nkv, d.d, d.batch, one, 3, 8, false, &h->sh_qkv, &h->ks_qkv);
-    plan_projection(d.d, h->nq, d.batch, two, 5, 16, false, &h->sh_o, &h->ks_o);
-    plan_projection(2 * d.ffn, d.d, d.batch, two, 5, 4, true, &h->sh_gu, &h->ks_gu);
-    plan_projection(d.d, d.ffn, d.batch, two, 5, 16, false, &h->sh_down, &h->ks_down);
+    plan_projection(d.d, h->nq, d.batch, two, 6, 16, false, &h->sh_o, &h->ks_o);
+    plan_projection(2 * d.ffn, d.d, d.batch, two, 6, 4, true, &h->sh_gu, &h->ks_gu);
+    plan_projection(d.d, d.ffn, d.batch, two, 6, 16, false, &h->sh_down, &h->ks_down);
     plan_projection(2 * h->nkv, d.d, d.batch, one, 3, 16, false, &h->sh_kv, &h->ks_kv);
   }
   // bf16 attention: query rows in two groups when there are enough of them and one group per

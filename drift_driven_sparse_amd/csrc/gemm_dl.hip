@@ -107,6 +107,7 @@ int dl_subtiles_per_wave(int shape) {
 int dl_tile_cols(int shape) {
   switch (shape) {
     case DL_WIDE: return 256;
+    case DL_X512: return 512;
     case DL_N192: case DL_W192: return 192;
     case DL_N96: case DL_P96: return 96;
     case DL_P160: return 160;
@@ -125,11 +126,13 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
     if (g.wg < 1 || g.wg % (dl_tile_cols(shape) / 16) != 0) return hipErrorInvalidValue;
     const bool one_plane = shape == DL_NARROW || shape == DL_N192 || shape == DL_N96;
     if (g.planes != (one_plane ? 1 : 2)) return hipErrorInvalidValue;
-    // rows past one slab's 192 take further launches over the same weights, one per slab
-    for (int r0 = 0; r0 < max_rows; r0 += kDlSlab) {
+    // rows past one slab (192 rows, 128 for the 512-column shape) take further launches over
+    // the same weights, one per slab
+    const int slab = shape == DL_X512 ? kDlSlabX512 : kDlSlab;
+    for (int r0 = 0; r0 < max_rows; r0 += slab) {
       DlArgs gs = g;
       gs.A.row0 = r0;
-      const int mr = max_rows - r0 < kDlSlab ? max_rows - r0 : kDlSlab;
+      const int mr = max_rows - r0 < slab ? max_rows - r0 : slab;
       hipError_t e;
       switch (shape) {
         case DL_NARROW: e = dl_launch_narrow(gs, mr, s); break;
@@ -141,6 +144,7 @@ hipError_t launch_dl(const DlArgs& g, int shape, int max_rows, hipStream_t s) {
         case DL_MID8: e = dl_launch_mid8(gs, mr, s); break;
         case DL_P96: e = dl_launch_p96(gs, mr, s); break;
         case DL_P160: e = dl_launch_p160(gs, mr, s); break;
+        case DL_X512: e = dl_launch_x512(gs, mr, s); break;
         default: e = hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;

@@ -331,3 +331,4 @@ hipError_t dl_launch_w192(const DlArgs& g, int max_rows, hipStream_t s);
 hipError_t dl_launch_mid8(const DlArgs& g, int max_rows, hipStream_t s);
 hipError_t dl_launch_p96(const DlArgs& g, int max_rows, hipStream_t s);
 hipError_t dl_launch_p160(const DlArgs& g, int max_rows, hipStream_t s);
+hipError_t dl_launch_x512(const DlArgs& g, int max_rows, hipStream_t s);

@@ -192,7 +192,8 @@ hipError_t launch_gemm(const GemmArgs& g, const EpiParams& e, int max_rows, hipS
 // ksplit > 1: raw sums to part[((s*batch + b)*part_rows + r)*N + n], finished by
 // launch_dl_finish (QKV, gate/up, KV) or the row reduction (O, down).
 constexpr int kMaxPos = 4096;  // key positions per sequence at most (KL rows are held in registers)
-constexpr int kDlSlab = 192;   // rows per launch of the projection kernels (longer row lists take several)
+constexpr int kDlSlab = 192;       // rows per launch of the projection kernels (longer row lists take several)
+constexpr int kDlSlabX512 = 128;   // rows per launch of the 512-column shape
 struct DlArgs {
   GemmA A;
   int32_t planes;
@@ -204,7 +205,7 @@ struct DlArgs {
   EpiParams e;
 };
 // Workgroup shapes: row groups x column groups (waves), columns per wave.  One bf16 plane:
-// NARROW, N192, N96; hi/lo planes: WIDE, MID, W192, MID8, P96, P160.
+// NARROW, N192, N96; hi/lo planes: X512, WIDE, MID, W192, MID8, P96, P160.
 enum DlShape { DL_NARROW = 0,   // 3 x 2 waves of 64 columns: 128-column tiles
                DL_WIDE = 1,     // 2 x 4 waves of 64 columns: 256-column tiles
                DL_MID = 2,      // 2 x 2 waves of 64 columns: 128-column tiles
@@ -213,7 +214,8 @@ enum DlShape { DL_NARROW = 0,   // 3 x 2 waves of 64 columns: 128-column tiles
                DL_N96 = 5,      // 4 x 2 waves of 48 columns: 96-column tiles
                DL_MID8 = 6,     // 2 x 4 waves of 32 columns: 128-column tiles
                DL_P96 = 7,      // 4 x 3 waves of 32 columns: 96-column tiles
-               DL_P160 = 8 };   // 2 x 5 waves of 32 columns: 160-column tiles
+               DL_P160 = 8,     // 2 x 5 waves of 32 columns: 160-column tiles
+               DL_X512 = 9 };   // 1 x 8 waves of 64 columns: 512-column tiles, 128-row launches
 int dl_tile_cols(int shape);
 // 16-column subtiles per wave; the in-kernel SwiGLU epilogue needs an even count (gate/up pairs)
 int dl_subtiles_per_wave(int shape);
