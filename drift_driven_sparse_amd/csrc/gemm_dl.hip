@@ -12,11 +12,12 @@
 //
 // Waves form RG row groups x CG column groups: the CG waves of a row group read
 // the same A fragments, the RG waves of a column group the same weight
-// fragments.  Row tiles are dealt to the row groups in turn and the shapes used
-// have RG = 2 and CG = 4 where it matters, so each SIMD holds one wave of each row
-// group and carries the same number of matrix products: with hi/lo planes and
-// real data the products are what the projection's time depends on once the
-// stream is fed.  Fragments are 16x16x32 MFMA operands in lane order.  Weights are
+// fragments.  Row tiles are dealt to the row groups in turn.  Shapes with RG = 2
+// and CG = 4 give each SIMD one wave of each row group and the same number of
+// matrix products; the 512-column shape (RG = 1, CG = 8) gives every wave all row
+// tiles, for many sequences, where a stage's fixed cost is best spread over more
+// products.  With hi/lo planes and real data the products are what the
+// projection's time depends on once the stream is fed.  Fragments are 16x16x32 MFMA operands in lane order.  Weights are
 // pre-packed in groups of subtiles so that a workgroup's weights for one step are
 // one contiguous block and its whole range one contiguous stream.  A operands are
 // fragment-packed by their producers (one contiguous block per step), except the

@@ -307,7 +307,8 @@ hipError_t launch_cfg(const DlArgs& g, hipStream_t s) {
 
 
 // Launch of one workgroup shape (RG x CG waves of NSUB subtiles, PL planes) with the row-tile
-// count per wave that covers max_rows (at most 192 rows: one slab).
+// count per wave that covers max_rows (at most 192 rows: one slab; the 512-column shapes have
+// launchers of their own with 128-row slabs).
 template <int RG, int CG, int NSUB, int PL>
 hipError_t launch_shape(const DlArgs& g, int max_rows, hipStream_t s) {
   constexpr int kMax = 192 / (16 * RG);
