@@ -14,6 +14,11 @@
   python -m drift_driven_sparse_amd.prof_summary mfma <counters.csv> --kernels NAME [NAME ...]
       [--pick every:offset ...] [--labels L ...]
       MfmaUtil (MFMA busy %) and bf16 MFMA FLOPs per dispatch of the named kernels.
+  python -m drift_driven_sparse_amd.prof_summary stall <counters.csv> [<counters.csv> ...]
+      --kernels NAME [NAME ...] [--pick every:offset ...] [--labels L ...]
+      where the waves of the named kernels spend their time (SQ wait and issue counters),
+      LDS bank conflicts, average vector-memory latency and MFMA busy cycles per SIMD, from
+      counter runs that together hold the counters listed in STALL_COUNTERS.
 """
 from __future__ import annotations
 
@@ -149,6 +154,48 @@ def mfma(a):
         print(f"| {lab} | `{k}` | {len(u)} | {sum(u) / len(u):.1f} | {fl:.2f} |")
 
 
+STALL_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                  "SQ_WAIT_INST_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "VmemLatency",
+                  "SQ_VALU_MFMA_BUSY_CYCLES", "TA_TA_BUSY", "TA_ADDR_STALLED_BY_TC_CYCLES"]
+
+
+def stall(a):
+    """Per kernel, means over its dispatches.  SQ_WAVE_CYCLES, SQ_WAIT_ANY and SQ_WAIT_INST_ANY
+    count wave-cycles in units of 4 cycles; SQ_BUSY_CYCLES counts, per shader engine, the cycles
+    with a wave present (32 shader engines, 4 SIMDs per compute unit, 8 compute units per engine);
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs, TA_* over the 256 texture-address
+    units; VmemLatency is the average cycles from issue to return of a vector-memory instruction."""
+    vals = {}
+    for path in a.csv:
+        for c in STALL_COUNTERS:
+            per, _ = _per_kernel(path, c)
+            for k, v in per.items():
+                if v:
+                    vals[(k, c)] = v
+    print(f"# {a.title}\n")
+    if a.command:
+        print(f"Commands (from the repository root on the GPU box, one counter set per run):\n\n```\n{a.command}\n```\n")
+    print("| unit | kernel | waves | cycles per wave | waiting (waitcnt, barrier) % | waiting for issue % | "
+          "LDS-issue wait % | LDS bank-conflict cycles per LDS cycle | vector-memory latency (cycles) | "
+          "MFMA busy % of SIMD time | TA stalled by L1 % of TA busy |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    picks = a.pick or [""] * len(a.kernels)
+    labels = a.labels or a.kernels
+    for k, pk, lab in zip(a.kernels, picks, labels):
+        def m(c):
+            v = _pick(vals.get((k, c), []), pk)
+            if not v:
+                raise SystemExit(f"counter {c} of kernel {k} not in the runs")
+            return sum(v) / len(v)
+        waves, wc = m("SQ_WAVES"), m("SQ_WAVE_CYCLES")
+        se_cycles = m("SQ_BUSY_CYCLES") / 32
+        print(f"| {lab} | `{k}` | {waves:.0f} | {4 * wc / waves:.0f} | {100 * m('SQ_WAIT_ANY') / wc:.0f} | "
+              f"{100 * m('SQ_WAIT_INST_ANY') / wc:.0f} | {100 * m('SQ_WAIT_INST_LDS') / wc:.1f} | "
+              f"{m('SQ_LDS_BANK_CONFLICT') / max(m('SQ_LDS_IDX_ACTIVE'), 1):.3f} | {m('VmemLatency'):.0f} | "
+              f"{100 * m('SQ_VALU_MFMA_BUSY_CYCLES') / 1024 / se_cycles:.0f} | "
+              f"{100 * m('TA_ADDR_STALLED_BY_TC_CYCLES') / max(m('TA_TA_BUSY'), 1):.0f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -172,8 +219,15 @@ def main():
     m.add_argument("--labels", nargs="*", default=None)
     m.add_argument("--title", default="rocprofv3 MFMA counters")
     m.add_argument("--command", default="")
+    st = sub.add_parser("stall")
+    st.add_argument("csv", nargs="+")
+    st.add_argument("--kernels", nargs="+", required=True)
+    st.add_argument("--pick", nargs="*", default=None)
+    st.add_argument("--labels", nargs="*", default=None)
+    st.add_argument("--title", default="rocprofv3 wave-state counters")
+    st.add_argument("--command", default="")
     a = ap.parse_args()
-    {"trace": trace, "pmc": pmc, "mfma": mfma}[a.cmd](a)
+    {"trace": trace, "pmc": pmc, "mfma": mfma, "stall": stall}[a.cmd](a)
 
 
 if __name__ == "__main__":
