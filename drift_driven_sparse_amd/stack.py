@@ -158,13 +158,23 @@ class RefreshStack:
                           self.conf_suffix, self.ws, self.ws_bytes)
 
     # ---- one denoising step -----------------------------------------------------------------
-    def step(self, blk_start: int, h_in: torch.Tensor, refresh: bool = True, commit_delta: bool = True) -> torch.Tensor:
-        """Runs every layer on the active rows h_in [batch, B, d]; returns the last layer's active rows."""
-        cur_h = 0
+    def step(self, blk_start: int, h_in: torch.Tensor, refresh: bool = True, commit_delta: bool = True,
+             per_layer: bool = False) -> torch.Tensor:
+        """Runs every layer on the active rows h_in [batch, B, d]; returns the last layer's active rows.
+        One polestar_step call for the whole stack, or with per_layer the cluster / drift / refresh
+        calls of each layer (the same launches)."""
         self.h_act[0].copy_(h_in)
+        mode = B.DRIFT_REFRESH if refresh else B.DRIFT_ACTIVE_ONLY
+        if not per_layer:
+            B.polestar_step(self.h, mode, [self.struct(l) for l in range(self.n_layers)], blk_start, self.h_act[0],
+                            self.h_act[1], self.packets[0], self.packets[1], self.D, self.topk,
+                            self.act_logits if commit_delta else None, self.delta if commit_delta else None,
+                            self.ws, self.ws_bytes)
+            self.last_packet = (self.n_layers - 1) % 2
+            return self.h_act[self.n_layers % 2]
+        cur_h = 0
         pk = 0
         u_in = None
-        mode = B.DRIFT_REFRESH if refresh else B.DRIFT_ACTIVE_ONLY
         for l in range(self.n_layers):
             Ls = self.struct(l)
             last = l == self.n_layers - 1

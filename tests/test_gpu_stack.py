@@ -144,7 +144,7 @@ def test_step_call_matches_layer_calls(refresh):
         st.step(blk, inputs[0])                 # drift references
         torch.cuda.synchronize()
         snap = _snapshot(st)
-        out = st.step(blk, inputs[1], refresh=refresh)
+        out = st.step(blk, inputs[1], refresh=refresh, per_layer=True)
         torch.cuda.synchronize()
         want = _outputs(st, out)
         _restore(st, snap)
