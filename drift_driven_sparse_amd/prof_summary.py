@@ -63,7 +63,7 @@ def trace(a):
     rows = list(db.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
     print(f"# {a.title}\n")
     if a.command:
-        print(f"Command (from the repository root on the GPU box):\n\n```\n{a.command}\n```\n")
+        print(f"Command (from the repository root on the MI355X machine):\n\n```\n{a.command}\n```\n")
     print("| kernel | calls | total ms | avg us |")
     print("|---|---:|---:|---:|")
     other = [0, 0.0]
@@ -113,7 +113,7 @@ def pmc(a):
     w_scale = a.probe_bytes / (pw * kib)
     print(f"# {a.title}\n")
     if a.command:
-        print(f"Commands (from the repository root on the GPU box, one counter per run):\n\n```\n{a.command}\n```\n")
+        print(f"Commands (from the repository root on the MI355X machine, one counter per run):\n\n```\n{a.command}\n```\n")
     print(f"Calibration: the element-wise copy reads and writes {a.probe_bytes} B; FETCH_SIZE reads "
           f"{pf:.0f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads {pw:.0f} KiB (scale {w_scale:.3f}).\n")
     print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |")
@@ -141,7 +141,7 @@ def mfma(a):
     flops, _ = _per_kernel(a.csv, "MfmaFlopsBF16")
     print(f"# {a.title}\n")
     if a.command:
-        print(f"Command (from the repository root on the GPU box):\n\n```\n{a.command}\n```\n")
+        print(f"Command (from the repository root on the MI355X machine):\n\n```\n{a.command}\n```\n")
     print("| unit | kernel | dispatches | MFMA busy % | bf16 MFMA GFLOP per dispatch |")
     print("|---|---|---:|---:|---:|")
     picks = a.pick or [""] * len(a.kernels)
@@ -174,7 +174,7 @@ def stall(a):
                     vals[(k, c)] = v
     print(f"# {a.title}\n")
     if a.command:
-        print(f"Commands (from the repository root on the GPU box, one counter set per run):\n\n```\n{a.command}\n```\n")
+        print(f"Commands (from the repository root on the MI355X machine, one counter set per run):\n\n```\n{a.command}\n```\n")
     print("| unit | kernel | waves | cycles per wave | waiting (waitcnt, barrier) % | waiting for issue % | "
           "LDS-issue wait % | LDS bank-conflict cycles per LDS cycle | vector-memory latency (cycles) | "
           "MFMA busy % of SIMD time | TA stalled by L1 % of TA busy |")

@@ -1,7 +1,7 @@
 """The page's printed defaults and sweep ranges (tests/golden/table5_defaults.json, copied from
 the page's §5.1 and Table 5) against the synthetic workloads and the parity cases: the
 workloads use the defaults, and every swept value a parity case uses lies in the page's range
-(block size 8 aside: the survey adds it for the short-generation benchmark)."""
+(block size 8 aside: the page's short-generation benchmark setting, outside Table 5)."""
 import json
 import os
 
